@@ -1,0 +1,249 @@
+"""Benchmark of the TensorGRaD optimizer step on one MI355X.
+
+Workload: the bf16 3-D FNO spectral-weight gradient of shape (64, 64, 48, 48, 25)
+(235,929,600 elements), Tucker ranks (32, 32, 24, 24, 13), 5% top-k sparse part
+(11,796,480 COO entries), Adam lr 1e-3, betas (0.9, 0.999), eps 1e-8, refresh every
+T = 200 steps; synthetic seeded inputs (Tucker low-rank signal + N(0, 0.01) noise + 1%
+Laplace(5) outliers, see synth/gen.py).
+
+A timed step is one tgrad_step on a fresh gradient buffer already resident in HBM
+(every buffer is staged before timing starts; the step writes the residual into its
+gradient). The refresh (top-k + Gram + eigensolver) runs before step 1 during warm-up
+and is timed on its own with tgrad_refresh. Per-kernel durations come from HIP events
+that the library records on the launch stream around every launch in the timed region.
+
+Prints ONE JSON line. --gpus N with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP32_MFMA_PEAK_TFS = 157.3     # MI355X dense fp32 matrix
+WORKLOAD = 4
+
+
+def esize(dtype):
+    return {"f32": 4, "f16": 2, "bf16": 2, "c64": 8}[dtype]
+
+
+def kernel_bytes(wl):
+    """Algorithmic HBM bytes per launch of every step kernel, keyed by kernel name.
+    Mode products: the input tile read once and the output written once (the operand
+    matrix is negligible); apply: + W read and written, membership bitmask (N/8 B),
+    per-word ranks (N/16 B) and the k sparse updates. Gather: k indices, k gradient
+    values read, k fp32 values written, k zeros written. Adam: g, m, v read and m, v, u
+    written, 4 B each, over core + k values."""
+    P = 2 if wl.dtype == "c64" else 1
+    es = esize(wl.dtype)
+    N, k = wl.numel, wl.k
+    fmodes = [n for n, (I, r) in enumerate(zip(wl.shape, wl.ranks)) if r < I]
+    cur = list(wl.shape)
+    proj, rec = [], []
+    size = N
+    for j, n in enumerate(reversed(fmodes)):
+        out = size // cur[n] * wl.ranks[n]
+        inb = size * P * (es if j == 0 else 4)
+        proj.append(inb + out * P * 4)
+        cur[n] = wl.ranks[n]
+        size = out
+    ncore = size
+    for j, n in enumerate(fmodes):
+        out = size // cur[n] * wl.shape[n]
+        b = size * P * 4
+        if j + 1 == len(fmodes):
+            b += 2 * N * es + N // 8 + N // 16 + k * P * 4
+        else:
+            b += out * P * 4
+        rec.append(b)
+        cur[n] = wl.shape[n]
+        size = out
+    flops_proj = []
+    size = N
+    cur = list(wl.shape)
+    for n in reversed(fmodes):
+        flops_proj.append(2 * size * P * wl.ranks[n] * P)
+        size = size // cur[n] * wl.ranks[n]
+        cur[n] = wl.ranks[n]
+    return {
+        "gather_residual": [k * (4 + es + 4 * P + es)],
+        "modeprod_project_first": proj[:1],
+        "modeprod_project": proj[1:],
+        "adam_fused": [(ncore + k) * P * 24],
+        "modeprod_reconstruct": rec[:-1],
+        "modeprod_reconstruct_apply": rec[-1:],
+        "_flops_project": flops_proj,
+        "_ncore": ncore,
+    }
+
+
+def cpu_baseline(wl, seed=0):
+    """The oracle (numpy, fp64 contractions) timed on this host on a bounded sample: one
+    non-refresh step of the full workload, with Omega a seeded random index set of size
+    k and seeded random orthonormal factors (the step's cost does not depend on which
+    indices or which subspace it uses). The refresh (a 236M-key sort and fp64 Grams)
+    is left out of the sample."""
+    import oracle as O
+    from synth import GradStream, init_weights
+    g = GradStream(wl, seed=seed).next()
+    W = init_weights(wl, seed=seed)
+    orc = O.TGradOracle(wl.shape, wl.ranks, wl.dtype, wl.sparse_ratio, wl.T, wl.lr, *wl.betas, wl.eps)
+    rng = np.random.default_rng(seed + 99)
+    orc.omega = np.sort(rng.choice(wl.numel, wl.k, replace=False)).astype(np.uint32)
+    orc.factors = [np.linalg.qr(rng.standard_normal((I, r)))[0].astype(np.float32) if r < I else None
+                   for I, r in zip(wl.shape, wl.ranks)]
+    orc.t = 1
+    orc.refreshed_for = 2
+    t0 = time.perf_counter()
+    orc.step(W, g)
+    dt = time.perf_counter() - t0
+    threads = len(os.sched_getaffinity(0))
+    return {"value": wl.numel / dt, "unit": "grad elems/s", "cores": threads, "kind": "oracle",
+            "sample": f"1 non-refresh step of the full workload ({wl.numel} elements), "
+                      f"{dt:.1f} s; numpy BLAS threads = available cores; refresh excluded",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--refresh-reps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import tensor_gradient_compression_amd as tg
+    from synth import CONFIGS, GradStream, init_weights
+
+    wl = CONFIGS[WORKLOAD]
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    K, Wm = args.steps, args.warmup
+
+    # inputs: two distinct synthetic gradients, staged into one buffer per step
+    gs = GradStream(wl, seed=0)
+    bases = [tg.to_device(gs.next(), wl.dtype, dev) for _ in range(2)]
+    W = tg.to_device(init_weights(wl, seed=0), wl.dtype, dev)
+    nbuf = K + Wm
+    grads = [bases[i % 2].clone() for i in range(nbuf)]
+    pristine = bases[0]
+    torch.cuda.synchronize()
+
+    lib = tg.TGrad(wl.shape, wl.ranks, wl.dtype, wl.sparse_ratio, wl.T, wl.lr, wl.betas, wl.eps)
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    for i in range(Wm):                      # step 1 refreshes (t = 1)
+        lib.step(W, grads[i], stream)
+    torch.cuda.synchronize()
+
+    lib.timing_enable(True, 100000)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        lib.step(W, grads[Wm + i], stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rec = lib.timing_read()
+    ms_step = (t1 - t0) * 1e3 / K
+
+    # refresh timed alone (reads the gradient only)
+    rt = []
+    lib.timing_enable(True, 100000)
+    for _ in range(args.refresh_reps):
+        torch.cuda.synchronize()
+        r0 = time.perf_counter()
+        lib.refresh(pristine, stream)
+        torch.cuda.synchronize()
+        rt.append((time.perf_counter() - r0) * 1e3)
+    rrec = lib.timing_read()
+    lib.timing_enable(False, 0)
+    refresh_ms = float(np.median(rt))
+
+    kb = kernel_bytes(wl)
+    kernels = {}
+    for name, (n, ms) in rec.items():
+        per_step = n // K if n % K == 0 else n / K
+        avg_ms = ms / n
+        entry = {"launches_per_step": per_step, "avg_ms": round(avg_ms, 5),
+                 "ms_per_step": round(ms / K, 5)}
+        if name in kb and kb[name]:
+            byts = sum(kb[name]) / len(kb[name])           # mean algorithmic bytes per launch
+            gbs = byts / (avg_ms * 1e-3) / 1e9
+            entry.update({"alg_bytes_per_launch": int(byts), "achieved_GBs": round(gbs, 1),
+                          "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+        kernels[name] = entry
+    refresh_kernels = {name: {"launches": n, "ms": round(ms / args.refresh_reps, 4)}
+                       for name, (n, ms) in rrec.items()}
+
+    # dominant kernel with a single launch per step (unique symbol for the profiler)
+    single = {k: v for k, v in kernels.items() if v.get("launches_per_step") == 1 and "achieved_GBs" in v}
+    dom = max(single, key=lambda k: single[k]["ms_per_step"])
+    d = kernels[dom]
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": d["achieved_GBs"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(d["achieved_GBs"] / HBM_PEAK_GBS, 4), "traffic": None}
+    step_bytes = sum(sum(v) for k2, v in kb.items() if not k2.startswith("_"))
+    step_frac = step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        del grads
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline(wl)
+
+    out = {
+        "metric": "TensorGRaD step ms + grad elems/s, % of HBM/MFMA roofline; refresh ms",
+        "value": wl.numel / (ms_step * 1e-3),
+        "unit": "grad elems/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bf16 FNO spectral-weight gradient (64,64,48,48,25), Tucker ranks "
+                               "(32,32,24,24,13), 5% top-k sparse, T=200",
+                   "numel": wl.numel, "k": wl.k, "core_numel": kb["_ncore"],
+                   "parallelism": "single GPU"},
+        "refresh_ms": round(refresh_ms, 3),
+        "step_alg_bytes": int(step_bytes),
+        "step_hbm_frac": round(step_frac, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+        "refresh_kernels": refresh_kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,165 @@
+/*
+ * tgrad.h - C ABI of the TensorGRaD optimizer step on AMD MI355X (gfx950).
+ *
+ * One handle optimises one weight tensor W of shape (I_1, ..., I_d) with the
+ * TensorGRaD step: the gradient G is split into a sparse part S on an index set
+ * Omega (the k = floor(rho * N) largest |G| entries, extracted first) and a Tucker
+ * low-rank part of the residual R = G - scatter(S); Adam runs on the Tucker core and
+ * on the sparse values; the update is reconstructed by mode-wise products with the
+ * sparse update scatter-added into the same buffer, and W is updated in place.
+ * Omega and the Tucker factors are refreshed every T steps (top-k by magnitude,
+ * HOSVD from mode-n Gram matrices).
+ *
+ * Sources (no code exists on them): the nullthought.net summary of "TensorGRaD:
+ * Tensor Gradient Robust Decomposition for Memory-Efficient Neural Operator
+ * Training", sections 2-3 (G = L + S, sparse part extracted first, Tucker on the
+ * residual, separate Adam updates, scatter-add after reconstruction, half-precision
+ * weights with fp32 optimizer state, re-selection every T steps); the pith.science
+ * review of arXiv 2501.02379, "What carries the argument" (factors reused for T
+ * steps, projection to a core, Adam moments on the core, mode-wise reconstruction,
+ * COO sparse set by top-k magnitude) and its appendix M excerpt of Theorem 2
+ * (project, update optimizer states, project back).
+ *
+ * Conventions for every call:
+ *   - Tensors are dense, contiguous, row-major (last index fastest). complex64 is
+ *     interleaved (re, im) fp32 pairs. Element (linear) indices count complex
+ *     elements, not floats.
+ *   - Device pointers are HIP device addresses on the device that was current at
+ *     tgrad_init; `stream` is a hipStream_t (NULL = the default stream). Every call
+ *     that takes a stream only enqueues work on it and returns without waiting;
+ *     device faults surface at the caller's next synchronisation.
+ *   - Host pointers (marked host) are ordinary CPU memory; calls taking them
+ *     synchronise the device before returning.
+ *   - Return value: TGRAD_OK or an error code below; no call throws. After
+ *     TGRAD_EHIP, tgrad_last_error() gives the HIP error string.
+ *   - One handle is used by one host thread and one stream at a time. Separate
+ *     handles are independent.
+ */
+#ifndef TGRAD_H
+#define TGRAD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tgrad_handle tgrad_t;
+
+/* Storage dtype of the weight and the gradient. Optimizer state is always fp32. */
+enum tgrad_dtype { TGRAD_F32 = 0, TGRAD_F16 = 1, TGRAD_BF16 = 2, TGRAD_C64 = 3 };
+
+enum tgrad_status {
+  TGRAD_OK = 0,
+  TGRAD_EINVAL = 1,   /* invalid argument (null pointer, size or range) */
+  TGRAD_ENOMEM = 2,   /* device allocation failed */
+  TGRAD_EHIP = 3,     /* a HIP call or kernel launch failed */
+  TGRAD_ESTATE = 4    /* call not valid in the handle's current state */
+};
+
+#define TGRAD_MAX_NDIM 8
+#define TGRAD_MAX_FACTOR_DIM 64   /* largest I_n of a mode with r_n < I_n */
+
+/*
+ * Create a handle on the current HIP device and allocate all optimizer state.
+ *   ndim            number of modes d, 1..8
+ *   shape[d]        I_n >= 1; N = prod I_n must be < 2^32
+ *   tucker_ranks[d] r_n in [1, I_n]. r_n == I_n keeps mode n uncompressed (identity
+ *                   factor, no mode product); r_n < I_n needs I_n <= 64.
+ *   dtype           enum tgrad_dtype of W and G
+ *   sparse_ratio    rho in [0, 1]; k = floor(rho * N) computed in IEEE double
+ *   T               refresh period >= 1: a refresh runs before every step t with
+ *                   (t - 1) mod T == 0, t = 1, 2, ... (pith.science: factors and
+ *                   Omega reused for T steps; nullthought section 3)
+ *   lr, beta1, beta2, eps   Adam: lr >= 0, beta in [0, 1), eps >= 0
+ * Moments start at zero, t = 0. The handle owns every device buffer it allocates.
+ * Errors: TGRAD_EINVAL, TGRAD_ENOMEM, TGRAD_EHIP. *out is NULL on error.
+ */
+int tgrad_init(tgrad_t **out, int ndim, const int64_t *shape, const int64_t *tucker_ranks,
+               int dtype, double sparse_ratio, int64_t T, double lr, double beta1,
+               double beta2, double eps);
+
+/*
+ * One optimizer step on device buffers `weight` (W, updated in place) and `grad`
+ * (G, caller-owned, N elements of dtype).
+ *   t <- t + 1; if a refresh is due for t and tgrad_refresh was not already called
+ *   for it, refresh from `grad` first. Then: S = G[Omega] (fp32) and G[Omega] <- 0
+ *   (grad becomes the residual R in place and stays so on return); core C = R x_1
+ *   U1^H ... x_d Ud^H; Adam on C and on S (fp32 moments); Delta = N_C x_1 U1 ...
+ *   x_d Ud with N_S added at Omega (sparse scale 1); W <- round(W - lr * Delta), one
+ *   rounding per element (nullthought section 3 step order; pith.science Theorem 2).
+ * Both buffers must stay valid until the work on `stream` completes.
+ * Errors: TGRAD_EINVAL (null handle/pointer), TGRAD_EHIP.
+ */
+int tgrad_step(tgrad_t *h, void *weight, void *grad, void *stream);
+
+/*
+ * Refresh Omega and the Tucker factors from `grad` (device, N elements of dtype):
+ * Omega = the k largest magnitudes (ties to the lowest linear index), stored
+ * ascending; each U(n) (r_n < I_n) = the r_n leading eigenvectors of the mode-n Gram
+ * matrix of the residual, descending eigenvalue order, each column scaled so its
+ * largest-magnitude entry (lowest row on ties) is real positive. `grad` is only
+ * read. Moments and t are untouched; the refresh serves step t + 1.
+ * (nullthought section 3: re-select sparse indices and low-rank subspace every T
+ * steps; pith.science: top-k magnitude, Tucker/HOSVD factors.)
+ * Errors: TGRAD_EINVAL, TGRAD_EHIP.
+ */
+int tgrad_refresh(tgrad_t *h, const void *grad, void *stream);
+
+/* Free every buffer of the handle. The caller synchronises first. NULL is a no-op. */
+int tgrad_destroy(tgrad_t *h);
+
+/* Static description of an error code; never NULL. */
+const char *tgrad_status_string(int status);
+/* Last HIP error message recorded on the handle (empty string if none). */
+const char *tgrad_last_error(const tgrad_t *h);
+
+/* ---------------------------------------------------------------- introspection.
+ * Not on the hot path. Host buffers; each call synchronises the device. */
+
+typedef struct tgrad_info {
+  int64_t ndim, dtype, numel, k, core_numel, T, t;
+  int64_t shape[TGRAD_MAX_NDIM];
+  int64_t ranks[TGRAD_MAX_NDIM];
+  int64_t state_bytes;      /* moments, core, factors, Omega (optimizer state) */
+  int64_t workspace_bytes;  /* transient buffers owned by the handle */
+} tgrad_info;
+
+int tgrad_get_info(const tgrad_t *h, tgrad_info *out);
+
+/* Omega, k uint32 linear indices ascending. cap = capacity of out (elements). */
+int tgrad_get_omega(tgrad_t *h, uint32_t *out, int64_t cap);
+
+/* U(n) as I_n x r_n row-major fp32 (complex: interleaved pairs, 2 I_n r_n floats).
+ * TGRAD_EINVAL for an identity mode (r_n == I_n) or too small cap (floats). */
+int tgrad_get_factor(tgrad_t *h, int mode, float *out, int64_t cap);
+
+/* Gram-matrix eigenvalues of mode n from the last refresh, I_n doubles, descending. */
+int tgrad_get_eigvals(tgrad_t *h, int mode, double *out, int64_t cap);
+
+/* Adam moments (fp32; complex = pairs): core m, v (core_numel*P each) and sparse m,
+ * v (k*P each). Any pointer may be NULL to skip it. */
+int tgrad_get_moments(tgrad_t *h, float *m_core, float *v_core, float *m_sparse,
+                      float *v_sparse);
+
+/* Test hooks: replace Omega (k ascending unique indices < N) or U(n) (layout as
+ * tgrad_get_factor) from host memory, and mark the handle refreshed for step t + 1
+ * so the next step uses them. */
+int tgrad_set_omega(tgrad_t *h, const uint32_t *omega, int64_t k);
+int tgrad_set_factor(tgrad_t *h, int mode, const float *U, int64_t n_floats);
+int tgrad_mark_refreshed(tgrad_t *h);
+
+/* ---------------------------------------------------------------- timing.
+ * When enabled, every kernel launch of step/refresh is bracketed by HIP events on
+ * the launch stream (at most max_records launches are kept). tgrad_timing_read
+ * synchronises, then returns per-kernel-id totals: launches[id] and ms[id] for
+ * id < n_ids (n_ids <= TGRAD_MAX_KERNEL_IDS) and resets the records. */
+#define TGRAD_MAX_KERNEL_IDS 32
+int tgrad_timing_enable(tgrad_t *h, int enable, int max_records);
+int tgrad_timing_read(tgrad_t *h, int64_t *launches, double *ms, int n_ids);
+const char *tgrad_kernel_name(int id);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TGRAD_H */

@@ -1,0 +1,252 @@
+"""TensorGRaD optimizer step on AMD MI355X: Python binding of libtgrad.so.
+
+Argument marshalling only: every step of the optimizer runs in the HIP kernels of
+libtgrad.so (built in-tree by tensor_gradient_compression_amd.build). PyTorch supplies
+device memory and the current stream. Loading fails loudly when the library is
+missing; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtgrad.so")
+
+F32, F16, BF16, C64 = 0, 1, 2, 3
+DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "c64": C64}
+OK, EINVAL, ENOMEM, EHIP, ESTATE = 0, 1, 2, 3, 4
+MAX_NDIM = 8
+MAX_KERNEL_IDS = 32
+
+_lib = None
+
+
+class TGradError(RuntimeError):
+    pass
+
+
+class Info(ctypes.Structure):
+    _fields_ = [("ndim", ctypes.c_int64), ("dtype", ctypes.c_int64), ("numel", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("core_numel", ctypes.c_int64), ("T", ctypes.c_int64),
+                ("t", ctypes.c_int64), ("shape", ctypes.c_int64 * MAX_NDIM),
+                ("ranks", ctypes.c_int64 * MAX_NDIM), ("state_bytes", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_int64)]
+
+
+# (name, restype, argtypes) of every exported symbol declared in include/tgrad.h
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+SIGNATURES = [
+    ("tgrad_init", ctypes.c_int, [ctypes.POINTER(_P), ctypes.c_int, ctypes.POINTER(_I64),
+                                  ctypes.POINTER(_I64), ctypes.c_int, ctypes.c_double, _I64,
+                                  ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                  ctypes.c_double]),
+    ("tgrad_step", ctypes.c_int, [_P, _P, _P, _P]),
+    ("tgrad_refresh", ctypes.c_int, [_P, _P, _P]),
+    ("tgrad_destroy", ctypes.c_int, [_P]),
+    ("tgrad_status_string", ctypes.c_char_p, [ctypes.c_int]),
+    ("tgrad_last_error", ctypes.c_char_p, [_P]),
+    ("tgrad_get_info", ctypes.c_int, [_P, ctypes.POINTER(Info)]),
+    ("tgrad_get_omega", ctypes.c_int, [_P, _P, _I64]),
+    ("tgrad_get_factor", ctypes.c_int, [_P, ctypes.c_int, _P, _I64]),
+    ("tgrad_get_eigvals", ctypes.c_int, [_P, ctypes.c_int, _P, _I64]),
+    ("tgrad_get_moments", ctypes.c_int, [_P, _P, _P, _P, _P]),
+    ("tgrad_set_omega", ctypes.c_int, [_P, _P, _I64]),
+    ("tgrad_set_factor", ctypes.c_int, [_P, ctypes.c_int, _P, _I64]),
+    ("tgrad_mark_refreshed", ctypes.c_int, [_P]),
+    ("tgrad_timing_enable", ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int]),
+    ("tgrad_timing_read", ctypes.c_int, [_P, _P, _P, ctypes.c_int]),
+    ("tgrad_kernel_name", ctypes.c_char_p, [ctypes.c_int]),
+]
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libtgrad.so and declare its signatures. Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise TGradError(f"{path} is not built; run `python -m tensor_gradient_compression_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, res, args in SIGNATURES:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def kernel_name(i: int) -> str:
+    return load_library().tgrad_kernel_name(i).decode()
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None else None
+
+
+class TGrad:
+    """One TensorGRaD-optimised tensor (see include/tgrad.h for the exact semantics).
+
+    weight and grad are device tensors (torch, contiguous) of the given shape; complex64
+    for "c64", torch.bfloat16 for "bf16", float16 for "f16", float32 for "f32"."""
+
+    def __init__(self, shape: Sequence[int], tucker_ranks: Sequence[int], dtype: str,
+                 sparse_ratio: float, T: int, lr: float = 1e-3,
+                 betas=(0.9, 0.999), eps: float = 1e-8):
+        self._lib = load_library()
+        self.shape = tuple(int(s) for s in shape)
+        self.ranks = tuple(int(r) for r in tucker_ranks)
+        self.dtype = dtype
+        self.P = 2 if dtype == "c64" else 1
+        nd = len(self.shape)
+        if len(self.ranks) != nd:
+            raise ValueError("shape and tucker_ranks differ in length")
+        sh = (ctypes.c_int64 * nd)(*self.shape)
+        rk = (ctypes.c_int64 * nd)(*self.ranks)
+        h = ctypes.c_void_p()
+        rc = self._lib.tgrad_init(ctypes.byref(h), nd, sh, rk, DTYPE_CODES[dtype],
+                                  float(sparse_ratio), int(T), float(lr), float(betas[0]),
+                                  float(betas[1]), float(eps))
+        if rc != OK:
+            raise TGradError(f"tgrad_init: {self._lib.tgrad_status_string(rc).decode()}")
+        self._h = h
+        self.info = self.get_info()
+
+    # ---------------------------------------------------------------- lifecycle
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.tgrad_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _check(self, rc: int, what: str):
+        if rc != OK:
+            msg = self._lib.tgrad_status_string(rc).decode()
+            detail = self._lib.tgrad_last_error(self._h).decode() if self._h else ""
+            raise TGradError(f"{what}: {msg} {detail}".strip())
+
+    @staticmethod
+    def _stream(stream):
+        if stream is None:
+            import torch
+            return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if isinstance(stream, int):
+            return ctypes.c_void_p(stream)
+        return ctypes.c_void_p(stream.cuda_stream)
+
+    # ---------------------------------------------------------------- hot path
+    def step(self, weight, grad, stream=None):
+        self._check(self._lib.tgrad_step(self._h, ctypes.c_void_p(weight.data_ptr()),
+                                         ctypes.c_void_p(grad.data_ptr()), self._stream(stream)),
+                    "tgrad_step")
+
+    def refresh(self, grad, stream=None):
+        self._check(self._lib.tgrad_refresh(self._h, ctypes.c_void_p(grad.data_ptr()),
+                                            self._stream(stream)), "tgrad_refresh")
+
+    # ---------------------------------------------------------------- introspection
+    def get_info(self) -> Info:
+        info = Info()
+        self._check(self._lib.tgrad_get_info(self._h, ctypes.byref(info)), "tgrad_get_info")
+        return info
+
+    @property
+    def k(self) -> int:
+        return int(self.info.k)
+
+    @property
+    def t(self) -> int:
+        return int(self.get_info().t)
+
+    def get_omega(self) -> np.ndarray:
+        out = np.zeros(max(self.k, 1), np.uint32)
+        self._check(self._lib.tgrad_get_omega(self._h, _ptr(out), out.size), "tgrad_get_omega")
+        return out[:self.k]
+
+    def get_factor(self, mode: int) -> np.ndarray:
+        I, r = self.shape[mode], self.ranks[mode]
+        out = np.zeros(I * r * self.P, np.float32)
+        self._check(self._lib.tgrad_get_factor(self._h, mode, _ptr(out), out.size), "tgrad_get_factor")
+        if self.P == 2:
+            return out.view(np.complex64).reshape(I, r)
+        return out.reshape(I, r)
+
+    def get_eigvals(self, mode: int) -> np.ndarray:
+        out = np.zeros(self.shape[mode], np.float64)
+        self._check(self._lib.tgrad_get_eigvals(self._h, mode, _ptr(out), out.size), "tgrad_get_eigvals")
+        return out
+
+    def get_moments(self):
+        nc = int(self.info.core_numel) * self.P
+        ns = self.k * self.P
+        mc, vc = np.zeros(nc, np.float32), np.zeros(nc, np.float32)
+        ms, vs = np.zeros(max(ns, 1), np.float32), np.zeros(max(ns, 1), np.float32)
+        self._check(self._lib.tgrad_get_moments(self._h, _ptr(mc), _ptr(vc), _ptr(ms), _ptr(vs)),
+                    "tgrad_get_moments")
+        return mc, vc, ms[:ns], vs[:ns]
+
+    def set_omega(self, omega: np.ndarray):
+        om = np.ascontiguousarray(omega, dtype=np.uint32)
+        buf = om if om.size else np.zeros(1, np.uint32)
+        self._check(self._lib.tgrad_set_omega(self._h, _ptr(buf), om.size), "tgrad_set_omega")
+
+    def set_factor(self, mode: int, U: np.ndarray):
+        if self.P == 2:
+            flat = np.ascontiguousarray(U, dtype=np.complex64).reshape(-1).view(np.float32)
+        else:
+            flat = np.ascontiguousarray(U, dtype=np.float32).reshape(-1)
+        self._check(self._lib.tgrad_set_factor(self._h, mode, _ptr(flat), flat.size), "tgrad_set_factor")
+
+    def mark_refreshed(self):
+        self._check(self._lib.tgrad_mark_refreshed(self._h), "tgrad_mark_refreshed")
+
+    # ---------------------------------------------------------------- timing
+    def timing_enable(self, enable: bool = True, max_records: int = 100000):
+        self._check(self._lib.tgrad_timing_enable(self._h, int(enable), int(max_records)),
+                    "tgrad_timing_enable")
+
+    def timing_read(self):
+        """{kernel name: (launches, total ms)} since the last read."""
+        n = np.zeros(MAX_KERNEL_IDS, np.int64)
+        ms = np.zeros(MAX_KERNEL_IDS, np.float64)
+        self._check(self._lib.tgrad_timing_read(self._h, _ptr(n), _ptr(ms), MAX_KERNEL_IDS),
+                    "tgrad_timing_read")
+        out = {}
+        for i in range(MAX_KERNEL_IDS):
+            if n[i]:
+                out[kernel_name(i)] = (int(n[i]), float(ms[i]))
+        return out
+
+
+def torch_dtype(dtype: str):
+    import torch
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+            "c64": torch.complex64}[dtype]
+
+
+def to_device(x: np.ndarray, dtype: str, device="cuda"):
+    """Storage-convention numpy array (see synth) -> contiguous device tensor."""
+    import torch
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to(device).contiguous()
+
+
+def to_host(t, dtype: str) -> np.ndarray:
+    """Device tensor -> storage-convention numpy array."""
+    import torch
+    c = t.detach().cpu().contiguous()
+    if dtype == "bf16":
+        return c.view(torch.int16).numpy().view(np.uint16).copy()
+    return c.numpy().copy()

@@ -1,0 +1,296 @@
+// Small symmetric / Hermitian eigensolver for the HOSVD factors, on device.
+//
+// U(n) = the r_n leading eigenvectors of the mode-n Gram matrix of the residual
+// (pith.science "What carries the argument": Tucker / higher-order SVD factors U^(n);
+// its appendix M excerpt: the factors are orthonormal, P^T P = I). One workgroup
+// diagonalises one I x I matrix (I <= 64) held in LDS in fp64 with the parallel cyclic
+// Jacobi method: each sweep visits every (p, q) pair once, in I - 1 rounds of disjoint
+// pairs (round-robin order); within a round every rotation is computed from the same
+// matrix, then all column updates (A <- A J, V <- V J) and all row updates
+// (A <- J^H A) are applied. Hermitian rotations first turn a_pq real with a phase on
+// column q, then apply the real rotation. Sweeps stop when the off-diagonal energy is
+// below 1e-26 of the total, or after 40 sweeps.
+//
+// Outputs (pages silent on eigenvector order, sign and phase): eigenvalues descending
+// (equal values keep index order); each selected column scaled by a unit scalar so its
+// largest-magnitude entry (lowest row on ties) is real positive; U stored fp32, and
+// from those fp32 values the two MFMA operand matrices of the mode products: Mproj
+// ((r*P) x (I*P), the real form of U^H) and Mrec ((I*P) x (r*P), the real form of U).
+#include "tg_common.h"
+
+namespace tg {
+
+namespace {
+
+constexpr int NTH = 256;
+
+struct EK {
+  const double* gram;
+  float* U;
+  float* Mproj;
+  float* Mrec;
+  double* eigvals;
+  uint32_t n, r;
+};
+
+__device__ __forceinline__ double block_sum(double v, double* red) {
+  const int tid = threadIdx.x;
+  red[tid] = v;
+  __syncthreads();
+  for (int off = NTH / 2; off > 0; off >>= 1) {
+    if (tid < off) red[tid] += red[tid + off];
+    __syncthreads();
+  }
+  const double s = red[0];
+  __syncthreads();
+  return s;
+}
+
+template <bool CPLX>
+__global__ void __launch_bounds__(NTH) k_eig(EK k) {
+  extern __shared__ double sm[];
+  const int tid = threadIdx.x;
+  const uint32_t n = k.n;
+  const uint32_t nn = n * n;
+  double* Ar = sm;
+  double* Ai = CPLX ? Ar + nn : nullptr;
+  double* Vr = CPLX ? Ai + nn : Ar + nn;
+  double* Vi = CPLX ? Vr + nn : nullptr;
+  double* tail = (CPLX ? Vi : Vr) + nn;
+  double* rc = tail;          // 32 pairs max
+  double* rs = rc + 32;
+  double* rpc = rs + 32;      // cos(phi)
+  double* rps = rpc + 32;     // sin(phi)
+  double* red = rps + 32;     // NTH
+  int* rp = (int*)(red + NTH);
+  int* rq = rp + 32;
+  int* order = rq + 32;       // 64
+
+  // Hermitian (or symmetric) matrix from the stacked real Gram, symmetrised.
+  const uint32_t K = CPLX ? 2 * n : n;
+  for (uint32_t idx = tid; idx < nn; idx += NTH) {
+    const uint32_t i = idx / n, j = idx - i * n;
+    if (CPLX) {
+      auto G = [&](uint32_t a, uint32_t b) { return k.gram[(uint64_t)a * K + b]; };
+      const double re1 = G(2 * i, 2 * j) + G(2 * i + 1, 2 * j + 1);
+      const double im1 = G(2 * i + 1, 2 * j) - G(2 * i, 2 * j + 1);
+      const double re2 = G(2 * j, 2 * i) + G(2 * j + 1, 2 * i + 1);
+      const double im2 = G(2 * j + 1, 2 * i) - G(2 * j, 2 * i + 1);
+      Ar[idx] = 0.5 * (re1 + re2);
+      Ai[idx] = 0.5 * (im1 - im2);
+      Vi[idx] = 0.0;
+    } else {
+      Ar[idx] = 0.5 * (k.gram[(uint64_t)i * K + j] + k.gram[(uint64_t)j * K + i]);
+    }
+    Vr[idx] = (i == j) ? 1.0 : 0.0;
+  }
+  __syncthreads();
+
+  const uint32_t m = n + (n & 1u);   // even number of players; player n is a bye
+  const uint32_t half = m / 2;
+  for (int sweep = 0; sweep < 40; ++sweep) {
+    double off = 0.0, tot = 0.0;
+    for (uint32_t idx = tid; idx < nn; idx += NTH) {
+      const uint32_t i = idx / n, j = idx - i * n;
+      const double a2 = Ar[idx] * Ar[idx] + (CPLX ? Ai[idx] * Ai[idx] : 0.0);
+      tot += a2;
+      if (i != j) off += a2;
+    }
+    off = block_sum(off, red);
+    tot = block_sum(tot, red);
+    if (!(off > 1e-26 * tot)) break;
+
+    for (uint32_t round = 0; round + 1 < m; ++round) {
+      if ((uint32_t)tid < half) {
+        auto player = [&](uint32_t pos) -> uint32_t {
+          return pos == 0 ? 0u : 1u + (pos - 1u + round) % (m - 1u);
+        };
+        uint32_t p = player(tid), q = player(m - 1 - tid);
+        if (p > q) { uint32_t t = p; p = q; q = t; }
+        double c = 1.0, s = 0.0, pc = 1.0, ps = 0.0;
+        if (q < n) {
+          const double app = Ar[p * n + p], aqq = Ar[q * n + q];
+          const double xr = Ar[p * n + q], xi = CPLX ? Ai[p * n + q] : 0.0;
+          const double rr = CPLX ? sqrt(xr * xr + xi * xi) : fabs(xr);
+          if (rr > 0.0) {
+            const double theta = (aqq - app) / (2.0 * rr);
+            double t;
+            if (fabs(theta) > 1e100) {
+              t = 0.5 / theta;
+            } else {
+              t = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+            }
+            c = 1.0 / sqrt(t * t + 1.0);
+            s = t * c;
+            if (CPLX) {
+              pc = xr / rr;
+              ps = xi / rr;
+            } else {
+              pc = xr >= 0.0 ? 1.0 : -1.0;
+            }
+          }
+        }
+        rc[tid] = c;
+        rs[tid] = s;
+        rpc[tid] = pc;
+        rps[tid] = ps;
+        rp[tid] = (int)p;
+        rq[tid] = (q < n) ? (int)q : -1;
+      }
+      __syncthreads();
+      // Real case: the phase is the sign of a_pq; folding it into s gives the usual
+      // real rotation (c, s*sign) for the symmetric 2x2 problem.
+      // Column updates: A[:, p], A[:, q] and V[:, p], V[:, q].
+      for (uint32_t idx = tid; idx < n * half; idx += NTH) {
+        const uint32_t j = idx / n, i = idx - j * n;
+        const int q = rq[j];
+        if (q < 0 || rs[j] == 0.0) continue;
+        const int p = rp[j];
+        const double c = rc[j], s = rs[j], pc = rpc[j], ps = rps[j];
+        if (CPLX) {
+          // y' = e^{-i phi} * y
+          {
+            const double xr = Ar[i * n + p], xi = Ai[i * n + p];
+            const double yr0 = Ar[i * n + q], yi0 = Ai[i * n + q];
+            const double yr = pc * yr0 + ps * yi0, yi = pc * yi0 - ps * yr0;
+            Ar[i * n + p] = c * xr - s * yr;
+            Ai[i * n + p] = c * xi - s * yi;
+            Ar[i * n + q] = s * xr + c * yr;
+            Ai[i * n + q] = s * xi + c * yi;
+          }
+          {
+            const double xr = Vr[i * n + p], xi = Vi[i * n + p];
+            const double yr0 = Vr[i * n + q], yi0 = Vi[i * n + q];
+            const double yr = pc * yr0 + ps * yi0, yi = pc * yi0 - ps * yr0;
+            Vr[i * n + p] = c * xr - s * yr;
+            Vi[i * n + p] = c * xi - s * yi;
+            Vr[i * n + q] = s * xr + c * yr;
+            Vi[i * n + q] = s * xi + c * yi;
+          }
+        } else {
+          const double ss = s * pc;
+          const double x = Ar[i * n + p], y = Ar[i * n + q];
+          Ar[i * n + p] = c * x - ss * y;
+          Ar[i * n + q] = ss * x + c * y;
+          const double vx = Vr[i * n + p], vy = Vr[i * n + q];
+          Vr[i * n + p] = c * vx - ss * vy;
+          Vr[i * n + q] = ss * vx + c * vy;
+        }
+      }
+      __syncthreads();
+      // Row updates: A[p, :], A[q, :] <- J^H A.
+      for (uint32_t idx = tid; idx < n * half; idx += NTH) {
+        const uint32_t j = idx / n, col = idx - j * n;
+        const int q = rq[j];
+        if (q < 0 || rs[j] == 0.0) continue;
+        const int p = rp[j];
+        const double c = rc[j], s = rs[j], pc = rpc[j], ps = rps[j];
+        if (CPLX) {
+          // y' = e^{+i phi} * y
+          const double xr = Ar[p * n + col], xi = Ai[p * n + col];
+          const double yr0 = Ar[q * n + col], yi0 = Ai[q * n + col];
+          const double yr = pc * yr0 - ps * yi0, yi = pc * yi0 + ps * yr0;
+          Ar[p * n + col] = c * xr - s * yr;
+          Ai[p * n + col] = c * xi - s * yi;
+          Ar[q * n + col] = s * xr + c * yr;
+          Ai[q * n + col] = s * xi + c * yi;
+        } else {
+          const double ss = s * pc;
+          const double x = Ar[p * n + col], y = Ar[q * n + col];
+          Ar[p * n + col] = c * x - ss * y;
+          Ar[q * n + col] = ss * x + c * y;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // Descending order of the diagonal, equal values in index order.
+  if (tid == 0) {
+    uint64_t used = 0;
+    for (uint32_t pos = 0; pos < n; ++pos) {
+      int best = -1;
+      double bv = 0.0;
+      for (uint32_t i = 0; i < n; ++i) {
+        if ((used >> i) & 1ull) continue;
+        const double d = Ar[i * n + i];
+        if (best < 0 || d > bv) { best = (int)i; bv = d; }
+      }
+      used |= 1ull << best;
+      order[pos] = best;
+    }
+  }
+  __syncthreads();
+  for (uint32_t i = tid; i < n; i += NTH) k.eigvals[i] = Ar[order[i] * n + order[i]];
+
+  const uint32_t r = k.r;
+  const uint32_t P = CPLX ? 2 : 1;
+  for (uint32_t c = tid; c < r; c += NTH) {
+    const uint32_t src = (uint32_t)order[c];
+    uint32_t imax = 0;
+    double best = -1.0;
+    for (uint32_t i = 0; i < n; ++i) {
+      const double vr = Vr[i * n + src], vi = CPLX ? Vi[i * n + src] : 0.0;
+      const double a2 = vr * vr + vi * vi;
+      if (a2 > best) { best = a2; imax = i; }
+    }
+    const double vr = Vr[imax * n + src], vi = CPLX ? Vi[imax * n + src] : 0.0;
+    const double mag = sqrt(vr * vr + vi * vi);
+    const double sr = mag > 0.0 ? vr / mag : 1.0;     // scale = conj(phase)
+    const double si = mag > 0.0 ? -vi / mag : 0.0;
+    for (uint32_t i = 0; i < n; ++i) {
+      const double xr = Vr[i * n + src], xi = CPLX ? Vi[i * n + src] : 0.0;
+      const float ur = (float)(xr * sr - xi * si);
+      const float ui = (float)(xr * si + xi * sr);
+      if (CPLX) {
+        k.U[((uint64_t)i * r + c) * 2] = ur;
+        k.U[((uint64_t)i * r + c) * 2 + 1] = ui;
+        const uint64_t KP = 2ull * n, RP = 2ull * r;
+        k.Mproj[(2 * c) * KP + 2 * i] = ur;
+        k.Mproj[(2 * c) * KP + 2 * i + 1] = ui;
+        k.Mproj[(2 * c + 1) * KP + 2 * i] = -ui;
+        k.Mproj[(2 * c + 1) * KP + 2 * i + 1] = ur;
+        k.Mrec[(2 * i) * RP + 2 * c] = ur;
+        k.Mrec[(2 * i) * RP + 2 * c + 1] = -ui;
+        k.Mrec[(2 * i + 1) * RP + 2 * c] = ui;
+        k.Mrec[(2 * i + 1) * RP + 2 * c + 1] = ur;
+      } else {
+        k.U[(uint64_t)i * r + c] = ur;
+        k.Mproj[(uint64_t)c * n + i] = ur;
+        k.Mrec[(uint64_t)i * r + c] = ur;
+      }
+    }
+    (void)P;
+  }
+}
+
+}  // namespace
+
+size_t eig_lds_bytes(uint32_t I, uint32_t P) {
+  const size_t nn = (size_t)I * I;
+  const size_t mats = (P == 2 ? 4 : 2) * nn;
+  return (mats + 4 * 32 + NTH) * sizeof(double) + (32 + 32 + 64) * sizeof(int);
+}
+
+hipError_t launch_eig(const EigArgs& e, hipStream_t s) {
+  if (e.I > 64 || e.r > e.I || e.r < 1) return hipErrorInvalidValue;
+  EK k;
+  k.gram = e.gram;
+  k.U = e.U;
+  k.Mproj = e.Mproj;
+  k.Mrec = e.Mrec;
+  k.eigvals = e.eigvals;
+  k.n = e.I;
+  k.r = e.r;
+  const size_t lds = eig_lds_bytes(e.I, e.P);
+  auto fn = (e.P == 2) ? k_eig<true> : k_eig<false>;
+  if (lds > 64 * 1024) {
+    hipError_t err = hipFuncSetAttribute((const void*)fn,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(fn, dim3(1), dim3(NTH), lds, s, k);
+  return hipGetLastError();
+}
+
+}  // namespace tg

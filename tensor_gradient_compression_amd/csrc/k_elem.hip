@@ -1,0 +1,166 @@
+// Element-wise kernels of the TensorGRaD step:
+//   gather:       S = G[Omega] in fp32 and G[Omega] <- 0, so G becomes the residual in
+//                 place (nullthought summary section 3: the sparse part is extracted
+//                 first and the remainder is the residual).
+//   adam:         fp32 Adam on the core and on the sparse values in one launch
+//                 (nullthought section 3: each part gets its own Adam update; section 3
+//                 mixed precision: optimizer state stays fp32; pith.science: Adam
+//                 moments live on the core). Operation order, each rounded to fp32:
+//                 m = b1*m + (1-b1)*g; v = b2*v + (1-b2)*(g*g);
+//                 u = (m/bc1) / (sqrt(v/bc2) + eps). The library is built without
+//                 floating-point contraction, so no step is fused into an FMA.
+//   apply_dense:  the update when no mode is compressed (every r_n = I_n): Delta =
+//                 N_C, plus N_S at Omega, W <- round(W - lr * Delta).
+#include "tg_common.h"
+
+namespace tg {
+
+namespace {
+
+unsigned grid_for(uint64_t n, unsigned per_block, unsigned cap) {
+  uint64_t b = (n + per_block - 1) / per_block;
+  if (b > cap) b = cap;
+  return b ? (unsigned)b : 1u;
+}
+
+template <typename ST, int P>
+__global__ void __launch_bounds__(256) k_gather(ST* __restrict__ G,
+                                                const uint32_t* __restrict__ omega, uint32_t k,
+                                                float* __restrict__ S) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < k; j += stride) {
+    const uint64_t e = omega[j];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      S[j * P + p] = to_f32(G[e * P + p]);
+      G[e * P + p] = zero_of<ST>();
+    }
+  }
+}
+
+__device__ __forceinline__ float adam_one(float g, float& m, float& v, const AdamK& a) {
+  m = a.b1 * m + a.c1 * g;
+  v = a.b2 * v + a.c2 * (g * g);
+  return (m / a.bc1) / (sqrtf(v / a.bc2) + a.eps);
+}
+
+template <typename CT>
+__global__ void __launch_bounds__(256) k_adam(const CT* __restrict__ gc, float* __restrict__ uc,
+                                              float* __restrict__ mc, float* __restrict__ vc,
+                                              uint64_t nc, float* __restrict__ S,
+                                              float* __restrict__ ms, float* __restrict__ vs,
+                                              uint64_t ns, AdamK a) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  const uint64_t n = nc + ns;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    if (i < nc) {
+      float m = mc[i], v = vc[i];
+      uc[i] = adam_one(to_f32(gc[i]), m, v, a);
+      mc[i] = m;
+      vc[i] = v;
+    } else {
+      const uint64_t j = i - nc;
+      float m = ms[j], v = vs[j];
+      S[j] = adam_one(S[j], m, v, a);
+      ms[j] = m;
+      vs[j] = v;
+    }
+  }
+}
+
+template <typename WT, int P>
+__global__ void __launch_bounds__(256) k_apply_dense(WT* __restrict__ W,
+                                                     const float* __restrict__ uc,
+                                                     const uint64_t* __restrict__ mask,
+                                                     const uint32_t* __restrict__ rank,
+                                                     const float* __restrict__ us, uint64_t N,
+                                                     float lr, int has_sparse) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; e < N; e += stride) {
+    float d[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) d[p] = uc[e * P + p];
+    if (has_sparse) {
+      const uint64_t word = mask[e >> 6];
+      if ((word >> (e & 63)) & 1ull) {
+        const uint64_t j = omega_rank(mask, rank, e, word);
+#pragma unroll
+        for (int p = 0; p < P; ++p) d[p] = d[p] + us[j * P + p];
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const float w = to_f32(W[e * P + p]);
+      W[e * P + p] = from_f32<WT>(w - lr * d[p]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gather(int dt, void* G, const uint32_t* omega, uint32_t k, float* S,
+                         hipStream_t s) {
+  if (!k) return hipSuccess;
+  const unsigned b = grid_for(k, 256, 8192);
+  switch (dt) {
+    case DT_F32: k_gather<float, 1><<<b, 256, 0, s>>>((float*)G, omega, k, S); break;
+    case DT_F16: k_gather<_Float16, 1><<<b, 256, 0, s>>>((_Float16*)G, omega, k, S); break;
+    case DT_BF16: k_gather<bf16_t, 1><<<b, 256, 0, s>>>((bf16_t*)G, omega, k, S); break;
+    case DT_C64: k_gather<float, 2><<<b, 256, 0, s>>>((float*)G, omega, k, S); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_adam(int core_dt, const void* g_core, float* u_core, float* m_core,
+                       float* v_core, uint64_t n_core, float* S, float* m_s, float* v_s,
+                       uint64_t n_s, AdamK a, hipStream_t s) {
+  const uint64_t n = n_core + n_s;
+  if (!n) return hipSuccess;
+  const unsigned b = grid_for(n, 256, 8192);
+  switch (core_dt) {
+    case DT_F32:
+    case DT_C64:
+      k_adam<float><<<b, 256, 0, s>>>((const float*)g_core, u_core, m_core, v_core, n_core, S,
+                                      m_s, v_s, n_s, a);
+      break;
+    case DT_F16:
+      k_adam<_Float16><<<b, 256, 0, s>>>((const _Float16*)g_core, u_core, m_core, v_core,
+                                         n_core, S, m_s, v_s, n_s, a);
+      break;
+    case DT_BF16:
+      k_adam<bf16_t><<<b, 256, 0, s>>>((const bf16_t*)g_core, u_core, m_core, v_core, n_core,
+                                       S, m_s, v_s, n_s, a);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_apply_dense(int dt, void* W, const float* u_core, const uint64_t* mask,
+                              const uint32_t* rank, const float* u_s, uint64_t N, float lr,
+                              int has_sparse, hipStream_t s) {
+  const unsigned b = grid_for(N, 256, 8192);
+  switch (dt) {
+    case DT_F32:
+      k_apply_dense<float, 1><<<b, 256, 0, s>>>((float*)W, u_core, mask, rank, u_s, N, lr,
+                                                has_sparse);
+      break;
+    case DT_F16:
+      k_apply_dense<_Float16, 1><<<b, 256, 0, s>>>((_Float16*)W, u_core, mask, rank, u_s, N, lr,
+                                                   has_sparse);
+      break;
+    case DT_BF16:
+      k_apply_dense<bf16_t, 1><<<b, 256, 0, s>>>((bf16_t*)W, u_core, mask, rank, u_s, N, lr,
+                                                 has_sparse);
+      break;
+    case DT_C64:
+      k_apply_dense<float, 2><<<b, 256, 0, s>>>((float*)W, u_core, mask, rank, u_s, N, lr,
+                                                has_sparse);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tg

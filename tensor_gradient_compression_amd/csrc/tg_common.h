@@ -1,0 +1,131 @@
+// Internal declarations shared by the HIP sources of libtgrad (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tg {
+
+enum Dt { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_C64 = 3 };
+
+// bf16 held as its 16-bit pattern.
+struct bf16_t { uint16_t b; };
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(_Float16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(((uint32_t)x.b) << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return (_Float16)x; }
+// Round to nearest even; a NaN keeps its upper bits and is made quiet.
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+  uint32_t u = __float_as_uint(x);
+  bf16_t r;
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) {
+    r.b = (uint16_t)((u >> 16) | 0x40u);
+  } else {
+    r.b = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+  }
+  return r;
+}
+template <typename T> __device__ __forceinline__ T zero_of();
+template <> __device__ __forceinline__ float zero_of<float>() { return 0.0f; }
+template <> __device__ __forceinline__ _Float16 zero_of<_Float16>() { return (_Float16)0.0f; }
+template <> __device__ __forceinline__ bf16_t zero_of<bf16_t>() { bf16_t z; z.b = 0; return z; }
+
+// Position of element e in Omega given the membership bitmask and per-word ranks.
+__device__ __forceinline__ uint32_t omega_rank(const uint64_t* mask, const uint32_t* rank,
+                                               uint64_t e, uint64_t word) {
+  uint32_t bit = (uint32_t)(e & 63u);
+  return rank[e >> 6] + (uint32_t)__popcll(word & ((1ull << bit) - 1ull));
+}
+
+struct AdamK {
+  float b1, c1, b2, c2, eps, bc1, bc2;
+};
+
+// Kernel ids for per-launch timing (names in tgrad_kernel_name).
+enum KernelId {
+  KID_TOPK_INIT = 0, KID_TOPK_HIST, KID_TOPK_SELECT, KID_TOPK_COUNT, KID_TOPK_SCAN,
+  KID_TOPK_COMPACT, KID_MASK_FROM_OMEGA, KID_GATHER, KID_PROJECT, KID_ADAM,
+  KID_RECONSTRUCT, KID_RECON_APPLY, KID_APPLY_DENSE, KID_GRAM, KID_GRAM_REDUCE,
+  KID_EIG, KID_FILL, KID_PROJECT_FIRST, KID_COUNT_
+};
+
+// ---------------------------------------------------------------- launchers
+// Every launcher enqueues on `s` and returns hipGetLastError().
+
+struct TopkWs {
+  uint32_t* hist;       // 2048 bins
+  uint64_t* state;      // TopkState (4 x u64)
+  uint32_t* ucount;     // 2 per unit
+  uint32_t* uoff;       // 2 per unit
+};
+uint64_t topk_units(uint64_t N);
+hipError_t launch_topk(int dt, const void* G, uint64_t N, uint32_t k, const TopkWs& ws,
+                       uint32_t* omega, uint64_t* mask, uint32_t* rank, hipStream_t s,
+                       void (*mark)(void*, int, bool), void* mctx);
+hipError_t launch_mask_from_omega(const uint32_t* omega, uint32_t k, uint64_t* mask,
+                                  uint32_t* rank, uint64_t nwords, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, uint64_t n, uint32_t v, hipStream_t s);
+hipError_t launch_fill_u64(uint64_t* p, uint64_t n, uint64_t v, hipStream_t s);
+
+hipError_t launch_gather(int dt, void* G, const uint32_t* omega, uint32_t k, float* S,
+                         hipStream_t s);
+
+// core input dtype: DT_F32 for an fp32 buffer (complex: pairs, P folded into n_core)
+hipError_t launch_adam(int core_dt, const void* g_core, float* u_core, float* m_core,
+                       float* v_core, uint64_t n_core, float* S, float* m_s, float* v_s,
+                       uint64_t n_s, AdamK a, hipStream_t s);
+hipError_t launch_apply_dense(int dt, void* W, const float* u_core, const uint64_t* mask,
+                              const uint32_t* rank, const float* u_s, uint64_t N, float lr,
+                              int has_sparse, hipStream_t s);
+
+// Mode product Y[a, jj, b] = sum_kk M[jj, kk] X[a, kk, b] over the (A, I, B, P) view.
+struct ModeProd {
+  const void* X;   // input, dtype in_dt (P == 2 only with fp32)
+  int in_dt;
+  const float* M;  // (R*P) x (I*P) row-major
+  uint32_t A, I, B, R, P;
+  // epilogue: apply == 0 -> store fp32 to Y; apply == 1 -> W <- round(W - lr*(acc + uS@Omega))
+  int apply;
+  float* Y;
+  void* W;
+  int w_dt;
+  const uint64_t* mask;
+  const uint32_t* rank;
+  const float* uS;
+  float lr;
+  int has_sparse;
+};
+size_t modeprod_lds_bytes(const ModeProd& mp);
+hipError_t launch_modeprod(const ModeProd& mp, int num_cu, hipStream_t s);
+
+// Gram of the (A, I, B, P) view with Omega entries treated as zero:
+// out[x, y] (fp64, (I*P) x (I*P)) = sum over (a, b) of X[a, x, b] X[a, y, b].
+struct GramArgs {
+  const void* X;
+  int dt;
+  uint32_t A, I, B, P;
+  const uint64_t* mask;  // NULL -> no masking
+  double* partial;       // nblk * (I*P)^2
+  double* out;           // (I*P)^2
+};
+uint32_t gram_blocks(const GramArgs& g, int num_cu);
+size_t gram_lds_bytes(const GramArgs& g);
+hipError_t launch_gram(const GramArgs& g, int num_cu, hipStream_t s,
+                       void (*mark)(void*, int, bool), void* mctx);
+
+// Eigen-decomposition of the Gram (stacked real (I*P)^2 fp64) and factor outputs.
+struct EigArgs {
+  const double* gram;
+  uint32_t I, r, P;
+  float* U;      // I x r (x P)
+  float* Mproj;  // (r*P) x (I*P)
+  float* Mrec;   // (I*P) x (r*P)
+  double* eigvals;  // I
+};
+size_t eig_lds_bytes(uint32_t I, uint32_t P);
+hipError_t launch_eig(const EigArgs& e, hipStream_t s);
+
+}  // namespace tg

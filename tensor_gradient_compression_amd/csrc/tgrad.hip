@@ -1,0 +1,635 @@
+// Host side of libtgrad: the handle, state allocation, and the order of launches for
+// one TensorGRaD step and refresh. Every launch goes onto the caller's stream; no host
+// synchronisation happens inside tgrad_step or tgrad_refresh.
+//
+// Step order (nullthought summary section 3; pith.science "What carries the argument"
+// and its appendix M excerpt of Theorem 2):
+//   [refresh when due] -> gather S = G[Omega], zero G[Omega] -> projection, one mode
+//   product per compressed mode (last mode first) -> fused Adam on core and S ->
+//   reconstruction, one mode product per compressed mode (first mode first), the last
+//   one applying W <- round(W - lr * (Delta_L + N_S at Omega)).
+// Refresh: top-k -> Omega (+ bitmask, ranks) -> per compressed mode: Gram of the
+//   residual (Omega masked on load) -> Jacobi eigensolver -> U(n) and operand matrices.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "tg_common.h"
+#include "tgrad.h"
+
+using namespace tg;
+
+namespace {
+
+struct Rec {
+  int id;
+  hipEvent_t a, b;
+};
+
+}  // namespace
+
+struct tgrad_handle {
+  int device = 0;
+  int num_cu = 256;
+  int d = 0;
+  int64_t shape[TGRAD_MAX_NDIM] = {0};
+  int64_t ranks[TGRAD_MAX_NDIM] = {0};
+  int dtype = 0;
+  uint32_t P = 1;
+  uint64_t N = 0, k = 0, ncore = 0, nwords = 0;
+  int64_t T = 1;
+  double lr = 0, b1 = 0, b2 = 0, eps = 0;
+  int64_t t = 0, refreshed_for = 0;
+  std::vector<int> fmodes;   // compressed modes, ascending
+
+  uint32_t* omega = nullptr;
+  uint64_t* mask = nullptr;
+  uint32_t* rank = nullptr;
+  float *S = nullptr, *mS = nullptr, *vS = nullptr;
+  float *core = nullptr, *ucore = nullptr, *mC = nullptr, *vC = nullptr;
+  float* buf[2] = {nullptr, nullptr};
+  float* U[TGRAD_MAX_NDIM] = {nullptr};
+  float* Mp[TGRAD_MAX_NDIM] = {nullptr};
+  float* Mr[TGRAD_MAX_NDIM] = {nullptr};
+  double* eig[TGRAD_MAX_NDIM] = {nullptr};
+  double* gram_part = nullptr;
+  double* gram = nullptr;
+  TopkWs tw{};
+
+  std::vector<void*> allocs;
+  int64_t state_bytes = 0, ws_bytes = 0;
+  std::string err;
+
+  bool timing = false;
+  int max_rec = 0;
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+  hipStream_t cur_stream = nullptr;
+};
+
+namespace {
+
+struct DevGuard {
+  int prev = -1;
+  explicit DevGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) (void)hipSetDevice(dev);
+  }
+  ~DevGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+int fail_hip(tgrad_t* h, hipError_t e, const char* what) {
+  if (h) {
+    h->err = std::string(what) + ": " + hipGetErrorString(e);
+  }
+  return TGRAD_EHIP;
+}
+
+#define HIPCHK(h, expr)                                  \
+  do {                                                   \
+    hipError_t _e = (expr);                              \
+    if (_e != hipSuccess) return fail_hip((h), _e, #expr); \
+  } while (0)
+
+template <typename T>
+bool dalloc(tgrad_t* h, T** p, uint64_t n, bool state) {
+  *p = nullptr;
+  if (n == 0) return true;
+  void* q = nullptr;
+  const size_t bytes = (size_t)n * sizeof(T);
+  if (hipMalloc(&q, bytes) != hipSuccess) return false;
+  h->allocs.push_back(q);
+  (state ? h->state_bytes : h->ws_bytes) += (int64_t)bytes;
+  *p = (T*)q;
+  return true;
+}
+
+void free_all(tgrad_t* h) {
+  for (void* p : h->allocs) (void)hipFree(p);
+  h->allocs.clear();
+  for (auto& r : h->recs) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  h->recs.clear();
+  for (auto e : h->pool) (void)hipEventDestroy(e);
+  h->pool.clear();
+}
+
+// (A, I, B) view of mode n of a tensor with the given current sizes.
+void view(const int64_t* sz, int d, int n, uint32_t* A, uint32_t* I, uint32_t* B) {
+  uint64_t a = 1, b = 1;
+  for (int i = 0; i < n; ++i) a *= (uint64_t)sz[i];
+  for (int i = n + 1; i < d; ++i) b *= (uint64_t)sz[i];
+  *A = (uint32_t)a;
+  *I = (uint32_t)sz[n];
+  *B = (uint32_t)b;
+}
+
+hipEvent_t take_event(tgrad_t* h) {
+  if (!h->pool.empty()) {
+    hipEvent_t e = h->pool.back();
+    h->pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void mark_cb(void* ctx, int id, bool begin) {
+  tgrad_t* h = (tgrad_t*)ctx;
+  if (!h->timing) return;
+  if (begin) {
+    if ((int)h->recs.size() >= h->max_rec) return;
+    Rec r;
+    r.id = id;
+    r.a = take_event(h);
+    r.b = take_event(h);
+    if (!r.a || !r.b) return;
+    (void)hipEventRecord(r.a, h->cur_stream);
+    h->recs.push_back(r);
+  } else {
+    if (h->recs.empty() || h->recs.back().id != id) return;
+    Rec& r = h->recs.back();
+    if (r.b == nullptr) return;
+    (void)hipEventRecord(r.b, h->cur_stream);
+  }
+}
+
+struct Mark {
+  tgrad_t* h;
+  int id;
+  Mark(tgrad_t* hh, int i) : h(hh), id(i) { mark_cb(h, id, true); }
+  ~Mark() { mark_cb(h, id, false); }
+};
+
+void host_operands(uint32_t I, uint32_t r, uint32_t P, const float* U, float* Mp, float* Mr) {
+  if (P == 1) {
+    for (uint32_t i = 0; i < I; ++i)
+      for (uint32_t c = 0; c < r; ++c) {
+        Mp[(size_t)c * I + i] = U[(size_t)i * r + c];
+        Mr[(size_t)i * r + c] = U[(size_t)i * r + c];
+      }
+    return;
+  }
+  const size_t KP = 2 * (size_t)I, RP = 2 * (size_t)r;
+  for (uint32_t i = 0; i < I; ++i)
+    for (uint32_t c = 0; c < r; ++c) {
+      const float ur = U[((size_t)i * r + c) * 2], ui = U[((size_t)i * r + c) * 2 + 1];
+      Mp[(2 * c) * KP + 2 * i] = ur;
+      Mp[(2 * c) * KP + 2 * i + 1] = ui;
+      Mp[(2 * c + 1) * KP + 2 * i] = -ui;
+      Mp[(2 * c + 1) * KP + 2 * i + 1] = ur;
+      Mr[(2 * i) * RP + 2 * c] = ur;
+      Mr[(2 * i) * RP + 2 * c + 1] = -ui;
+      Mr[(2 * i + 1) * RP + 2 * c] = ui;
+      Mr[(2 * i + 1) * RP + 2 * c + 1] = ur;
+    }
+}
+
+int do_refresh(tgrad_t* h, const void* grad, hipStream_t s) {
+  if (h->k > 0) {
+    HIPCHK(h, launch_topk(h->dtype, grad, h->N, (uint32_t)h->k, h->tw, h->omega, h->mask,
+                          h->rank, s, mark_cb, h));
+  }
+  const int gdt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
+  for (int n : h->fmodes) {
+    GramArgs g;
+    g.X = grad;
+    g.dt = gdt;
+    view(h->shape, h->d, n, &g.A, &g.I, &g.B);
+    g.P = h->P;
+    g.mask = h->k > 0 ? h->mask : nullptr;
+    g.partial = h->gram_part;
+    g.out = h->gram;
+    HIPCHK(h, launch_gram(g, h->num_cu, s, mark_cb, h));
+    EigArgs e;
+    e.gram = h->gram;
+    e.I = (uint32_t)h->shape[n];
+    e.r = (uint32_t)h->ranks[n];
+    e.P = h->P;
+    e.U = h->U[n];
+    e.Mproj = h->Mp[n];
+    e.Mrec = h->Mr[n];
+    e.eigvals = h->eig[n];
+    {
+      Mark m(h, KID_EIG);
+      HIPCHK(h, launch_eig(e, s));
+    }
+  }
+  h->refreshed_for = h->t + 1;
+  return TGRAD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tgrad_status_string(int status) {
+  switch (status) {
+    case TGRAD_OK: return "ok";
+    case TGRAD_EINVAL: return "invalid argument";
+    case TGRAD_ENOMEM: return "device allocation failed";
+    case TGRAD_EHIP: return "HIP call failed";
+    case TGRAD_ESTATE: return "invalid state";
+  }
+  return "unknown status";
+}
+
+const char* tgrad_last_error(const tgrad_t* h) { return h ? h->err.c_str() : ""; }
+
+const char* tgrad_kernel_name(int id) {
+  static const char* names[KID_COUNT_] = {
+      "topk_init", "topk_hist", "topk_select", "topk_count", "topk_scan", "topk_compact",
+      "mask_from_omega", "gather_residual", "modeprod_project", "adam_fused",
+      "modeprod_reconstruct", "modeprod_reconstruct_apply", "apply_dense", "gram",
+      "gram_reduce", "eig_jacobi", "fill", "modeprod_project_first"};
+  if (id < 0 || id >= KID_COUNT_) return "";
+  return names[id];
+}
+
+int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tucker_ranks,
+               int dtype, double sparse_ratio, int64_t T, double lr, double beta1, double beta2,
+               double eps) {
+  if (!out) return TGRAD_EINVAL;
+  *out = nullptr;
+  if (ndim < 1 || ndim > TGRAD_MAX_NDIM || !shape || !tucker_ranks) return TGRAD_EINVAL;
+  if (dtype < TGRAD_F32 || dtype > TGRAD_C64) return TGRAD_EINVAL;
+  if (!(sparse_ratio >= 0.0 && sparse_ratio <= 1.0) || T < 1) return TGRAD_EINVAL;
+  if (!(lr >= 0.0) || !(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) ||
+      !(eps >= 0.0))
+    return TGRAD_EINVAL;
+  uint64_t N = 1, ncore = 1;
+  for (int i = 0; i < ndim; ++i) {
+    if (shape[i] < 1 || tucker_ranks[i] < 1 || tucker_ranks[i] > shape[i]) return TGRAD_EINVAL;
+    if (tucker_ranks[i] < shape[i] && shape[i] > TGRAD_MAX_FACTOR_DIM) return TGRAD_EINVAL;
+    N *= (uint64_t)shape[i];
+    ncore *= (uint64_t)tucker_ranks[i];
+    if (N >= (1ull << 32)) return TGRAD_EINVAL;
+  }
+  tgrad_t* h = new (std::nothrow) tgrad_t();
+  if (!h) return TGRAD_ENOMEM;
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    delete h;
+    return TGRAD_EHIP;
+  }
+  int cu = 0;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, h->device) == hipSuccess &&
+      cu > 0)
+    h->num_cu = cu;
+  h->d = ndim;
+  for (int i = 0; i < ndim; ++i) {
+    h->shape[i] = shape[i];
+    h->ranks[i] = tucker_ranks[i];
+    if (tucker_ranks[i] < shape[i]) h->fmodes.push_back(i);
+  }
+  h->dtype = dtype;
+  h->P = dtype == TGRAD_C64 ? 2 : 1;
+  h->N = N;
+  h->k = (uint64_t)std::floor(sparse_ratio * (double)N);
+  if (h->k > N) h->k = N;
+  h->ncore = ncore;
+  h->nwords = (N + 63) / 64;
+  h->T = T;
+  h->lr = lr;
+  h->b1 = beta1;
+  h->b2 = beta2;
+  h->eps = eps;
+  const uint64_t P = h->P;
+
+  // Intermediate sizes of the projection and reconstruction chains.
+  uint64_t inter = 0;
+  {
+    int64_t cur[TGRAD_MAX_NDIM];
+    for (int i = 0; i < ndim; ++i) cur[i] = shape[i];
+    uint64_t size = N;
+    const size_t nf = h->fmodes.size();
+    for (size_t j = 0; j < nf; ++j) {       // projection: last mode first
+      const int n = h->fmodes[nf - 1 - j];
+      size = size / (uint64_t)cur[n] * (uint64_t)h->ranks[n];
+      cur[n] = h->ranks[n];
+      if (j + 1 < nf && size > inter) inter = size;   // not the core
+    }
+    size = ncore;
+    for (size_t j = 0; j < nf; ++j) {       // reconstruction: first mode first
+      const int n = h->fmodes[j];
+      size = size / (uint64_t)cur[n] * (uint64_t)shape[n];
+      cur[n] = shape[n];
+      if (j + 1 < nf && size > inter) inter = size;   // not the weight
+    }
+  }
+
+  bool ok = true;
+  ok = ok && dalloc(h, &h->omega, h->k, true);
+  ok = ok && dalloc(h, &h->mask, h->nwords, false);
+  ok = ok && dalloc(h, &h->rank, h->nwords, false);
+  ok = ok && dalloc(h, &h->S, h->k * P, false);
+  ok = ok && dalloc(h, &h->mS, h->k * P, true);
+  ok = ok && dalloc(h, &h->vS, h->k * P, true);
+  ok = ok && dalloc(h, &h->mC, ncore * P, true);
+  ok = ok && dalloc(h, &h->vC, ncore * P, true);
+  ok = ok && dalloc(h, &h->ucore, ncore * P, false);
+  if (!h->fmodes.empty()) ok = ok && dalloc(h, &h->core, ncore * P, false);
+  ok = ok && dalloc(h, &h->buf[0], inter * P, false);
+  ok = ok && dalloc(h, &h->buf[1], inter * P, false);
+  uint64_t gpart = 0, gmax = 0;
+  for (int n : h->fmodes) {
+    const uint64_t I = (uint64_t)shape[n], r = (uint64_t)tucker_ranks[n];
+    ok = ok && dalloc(h, &h->U[n], I * r * P, true);
+    ok = ok && dalloc(h, &h->Mp[n], I * r * P * P, false);
+    ok = ok && dalloc(h, &h->Mr[n], I * r * P * P, false);
+    ok = ok && dalloc(h, &h->eig[n], I, false);
+    GramArgs g{};
+    view(shape, ndim, n, &g.A, &g.I, &g.B);
+    g.P = (uint32_t)P;
+    const uint64_t K2 = (I * P) * (I * P);
+    const uint64_t nb = gram_blocks(g, h->num_cu);
+    if (nb * K2 > gpart) gpart = nb * K2;
+    if (K2 > gmax) gmax = K2;
+  }
+  ok = ok && dalloc(h, &h->gram_part, gpart, false);
+  ok = ok && dalloc(h, &h->gram, gmax, false);
+  const uint64_t units = topk_units(N);
+  ok = ok && dalloc(h, &h->tw.hist, 2048, false);
+  ok = ok && dalloc(h, &h->tw.state, 4, false);
+  ok = ok && dalloc(h, &h->tw.ucount, 2 * units, false);
+  ok = ok && dalloc(h, &h->tw.uoff, 2 * units, false);
+  if (!ok) {
+    free_all(h);
+    delete h;
+    return TGRAD_ENOMEM;
+  }
+  hipError_t e = hipSuccess;
+  auto zero = [&](void* p, uint64_t bytes) {
+    if (p && bytes && e == hipSuccess) e = hipMemset(p, 0, bytes);
+  };
+  zero(h->mS, h->k * P * 4);
+  zero(h->vS, h->k * P * 4);
+  zero(h->mC, ncore * P * 4);
+  zero(h->vC, ncore * P * 4);
+  zero(h->mask, h->nwords * 8);
+  zero(h->rank, h->nwords * 4);
+  zero(h->omega, h->k * 4);
+  for (int n : h->fmodes) {
+    const uint64_t I = (uint64_t)shape[n], r = (uint64_t)tucker_ranks[n];
+    zero(h->U[n], I * r * P * 4);
+    zero(h->Mp[n], I * r * P * P * 4);
+    zero(h->Mr[n], I * r * P * P * 4);
+    zero(h->eig[n], I * 8);
+  }
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    free_all(h);
+    delete h;
+    return TGRAD_EHIP;
+  }
+  *out = h;
+  return TGRAD_OK;
+}
+
+int tgrad_destroy(tgrad_t* h) {
+  if (!h) return TGRAD_OK;
+  {
+    DevGuard g(h->device);
+    free_all(h);
+  }
+  delete h;
+  return TGRAD_OK;
+}
+
+int tgrad_refresh(tgrad_t* h, const void* grad, void* stream) {
+  if (!h || !grad) return TGRAD_EINVAL;
+  DevGuard g(h->device);
+  h->cur_stream = (hipStream_t)stream;
+  return do_refresh(h, grad, (hipStream_t)stream);
+}
+
+int tgrad_step(tgrad_t* h, void* weight, void* grad, void* stream) {
+  if (!h || !weight || !grad) return TGRAD_EINVAL;
+  DevGuard gd(h->device);
+  hipStream_t s = (hipStream_t)stream;
+  h->cur_stream = s;
+  h->t += 1;
+  const int64_t t = h->t;
+  if ((t - 1) % h->T == 0 && h->refreshed_for != t) {
+    h->t -= 1;                       // the refresh serves step t = (current t) + 1
+    int rc = do_refresh(h, grad, s);
+    h->t += 1;
+    if (rc != TGRAD_OK) return rc;
+  }
+  const uint32_t P = h->P;
+  if (h->k > 0) {
+    Mark m(h, KID_GATHER);
+    HIPCHK(h, launch_gather(h->dtype, grad, h->omega, (uint32_t)h->k, h->S, s));
+  }
+  // projection, last compressed mode first
+  int64_t cur[TGRAD_MAX_NDIM];
+  for (int i = 0; i < h->d; ++i) cur[i] = h->shape[i];
+  const void* X = grad;
+  int xdt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
+  int which = 0;
+  const size_t nf = h->fmodes.size();
+  for (size_t j = 0; j < nf; ++j) {
+    const int n = h->fmodes[nf - 1 - j];
+    ModeProd mp{};
+    mp.X = X;
+    mp.in_dt = xdt;
+    mp.M = h->Mp[n];
+    view(cur, h->d, n, &mp.A, &mp.I, &mp.B);
+    mp.R = (uint32_t)h->ranks[n];
+    mp.P = P;
+    mp.apply = 0;
+    mp.Y = (j + 1 == nf) ? h->core : h->buf[which];
+    {
+      Mark m(h, j == 0 ? KID_PROJECT_FIRST : KID_PROJECT);
+      HIPCHK(h, launch_modeprod(mp, h->num_cu, s));
+    }
+    X = mp.Y;
+    xdt = DT_F32;
+    which ^= 1;
+    cur[n] = h->ranks[n];
+  }
+  AdamK a;
+  a.b1 = (float)h->b1;
+  a.c1 = (float)(1.0 - h->b1);
+  a.b2 = (float)h->b2;
+  a.c2 = (float)(1.0 - h->b2);
+  a.eps = (float)h->eps;
+  a.bc1 = (float)(1.0 - std::pow(h->b1, (double)t));
+  a.bc2 = (float)(1.0 - std::pow(h->b2, (double)t));
+  {
+    Mark m(h, KID_ADAM);
+    const void* gcore = nf ? (const void*)h->core : (const void*)grad;
+    const int cdt = nf ? DT_F32 : h->dtype;
+    HIPCHK(h, launch_adam(cdt, gcore, h->ucore, h->mC, h->vC, h->ncore * P, h->S, h->mS, h->vS,
+                          h->k * P, a, s));
+  }
+  const float lr = (float)h->lr;
+  if (nf == 0) {
+    Mark m(h, KID_APPLY_DENSE);
+    HIPCHK(h, launch_apply_dense(h->dtype, weight, h->ucore, h->mask, h->rank, h->S, h->N, lr,
+                                 h->k > 0, s));
+    return TGRAD_OK;
+  }
+  X = h->ucore;
+  which = 0;
+  for (size_t j = 0; j < nf; ++j) {
+    const int n = h->fmodes[j];
+    ModeProd mp{};
+    mp.X = X;
+    mp.in_dt = DT_F32;
+    mp.M = h->Mr[n];
+    view(cur, h->d, n, &mp.A, &mp.I, &mp.B);
+    mp.R = (uint32_t)h->shape[n];
+    mp.P = P;
+    const bool last = (j + 1 == nf);
+    mp.apply = last ? 1 : 0;
+    mp.Y = last ? nullptr : h->buf[which];
+    mp.W = weight;
+    mp.w_dt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
+    mp.mask = h->mask;
+    mp.rank = h->rank;
+    mp.uS = h->S;
+    mp.lr = lr;
+    mp.has_sparse = h->k > 0;
+    {
+      Mark m(h, last ? KID_RECON_APPLY : KID_RECONSTRUCT);
+      HIPCHK(h, launch_modeprod(mp, h->num_cu, s));
+    }
+    X = mp.Y;
+    which ^= 1;
+    cur[n] = h->shape[n];
+  }
+  return TGRAD_OK;
+}
+
+int tgrad_get_info(const tgrad_t* h, tgrad_info* out) {
+  if (!h || !out) return TGRAD_EINVAL;
+  std::memset(out, 0, sizeof(*out));
+  out->ndim = h->d;
+  out->dtype = h->dtype;
+  out->numel = (int64_t)h->N;
+  out->k = (int64_t)h->k;
+  out->core_numel = (int64_t)h->ncore;
+  out->T = h->T;
+  out->t = h->t;
+  for (int i = 0; i < h->d; ++i) {
+    out->shape[i] = h->shape[i];
+    out->ranks[i] = h->ranks[i];
+  }
+  out->state_bytes = h->state_bytes;
+  out->workspace_bytes = h->ws_bytes;
+  return TGRAD_OK;
+}
+
+int tgrad_get_omega(tgrad_t* h, uint32_t* out, int64_t cap) {
+  if (!h || (!out && h->k) || cap < (int64_t)h->k) return TGRAD_EINVAL;
+  DevGuard g(h->device);
+  HIPCHK(h, hipDeviceSynchronize());
+  if (h->k) HIPCHK(h, hipMemcpy(out, h->omega, h->k * 4, hipMemcpyDeviceToHost));
+  return TGRAD_OK;
+}
+
+int tgrad_get_factor(tgrad_t* h, int mode, float* out, int64_t cap) {
+  if (!h || !out || mode < 0 || mode >= h->d || !h->U[mode]) return TGRAD_EINVAL;
+  const uint64_t n = (uint64_t)h->shape[mode] * h->ranks[mode] * h->P;
+  if (cap < (int64_t)n) return TGRAD_EINVAL;
+  DevGuard g(h->device);
+  HIPCHK(h, hipDeviceSynchronize());
+  HIPCHK(h, hipMemcpy(out, h->U[mode], n * 4, hipMemcpyDeviceToHost));
+  return TGRAD_OK;
+}
+
+int tgrad_get_eigvals(tgrad_t* h, int mode, double* out, int64_t cap) {
+  if (!h || !out || mode < 0 || mode >= h->d || !h->eig[mode]) return TGRAD_EINVAL;
+  if (cap < h->shape[mode]) return TGRAD_EINVAL;
+  DevGuard g(h->device);
+  HIPCHK(h, hipDeviceSynchronize());
+  HIPCHK(h, hipMemcpy(out, h->eig[mode], (size_t)h->shape[mode] * 8, hipMemcpyDeviceToHost));
+  return TGRAD_OK;
+}
+
+int tgrad_get_moments(tgrad_t* h, float* m_core, float* v_core, float* m_sparse,
+                      float* v_sparse) {
+  if (!h) return TGRAD_EINVAL;
+  DevGuard g(h->device);
+  HIPCHK(h, hipDeviceSynchronize());
+  const size_t nc = h->ncore * h->P * 4, ns = h->k * h->P * 4;
+  if (m_core && nc) HIPCHK(h, hipMemcpy(m_core, h->mC, nc, hipMemcpyDeviceToHost));
+  if (v_core && nc) HIPCHK(h, hipMemcpy(v_core, h->vC, nc, hipMemcpyDeviceToHost));
+  if (m_sparse && ns) HIPCHK(h, hipMemcpy(m_sparse, h->mS, ns, hipMemcpyDeviceToHost));
+  if (v_sparse && ns) HIPCHK(h, hipMemcpy(v_sparse, h->vS, ns, hipMemcpyDeviceToHost));
+  return TGRAD_OK;
+}
+
+int tgrad_set_omega(tgrad_t* h, const uint32_t* omega, int64_t k) {
+  if (!h || k != (int64_t)h->k || (k && !omega)) return TGRAD_EINVAL;
+  for (int64_t j = 0; j < k; ++j) {
+    if ((uint64_t)omega[j] >= h->N) return TGRAD_EINVAL;
+    if (j && omega[j] <= omega[j - 1]) return TGRAD_EINVAL;
+  }
+  DevGuard g(h->device);
+  HIPCHK(h, hipDeviceSynchronize());
+  if (k) HIPCHK(h, hipMemcpy(h->omega, omega, (size_t)k * 4, hipMemcpyHostToDevice));
+  HIPCHK(h, launch_mask_from_omega(h->omega, (uint32_t)k, h->mask, h->rank, h->nwords, nullptr));
+  HIPCHK(h, hipDeviceSynchronize());
+  return TGRAD_OK;
+}
+
+int tgrad_set_factor(tgrad_t* h, int mode, const float* U, int64_t n_floats) {
+  if (!h || !U || mode < 0 || mode >= h->d || !h->U[mode]) return TGRAD_EINVAL;
+  const uint32_t I = (uint32_t)h->shape[mode], r = (uint32_t)h->ranks[mode];
+  const uint64_t n = (uint64_t)I * r * h->P;
+  if (n_floats != (int64_t)n) return TGRAD_EINVAL;
+  std::vector<float> mp(n * h->P), mr(n * h->P);
+  host_operands(I, r, h->P, U, mp.data(), mr.data());
+  DevGuard g(h->device);
+  HIPCHK(h, hipDeviceSynchronize());
+  HIPCHK(h, hipMemcpy(h->U[mode], U, n * 4, hipMemcpyHostToDevice));
+  HIPCHK(h, hipMemcpy(h->Mp[mode], mp.data(), mp.size() * 4, hipMemcpyHostToDevice));
+  HIPCHK(h, hipMemcpy(h->Mr[mode], mr.data(), mr.size() * 4, hipMemcpyHostToDevice));
+  return TGRAD_OK;
+}
+
+int tgrad_mark_refreshed(tgrad_t* h) {
+  if (!h) return TGRAD_EINVAL;
+  h->refreshed_for = h->t + 1;
+  return TGRAD_OK;
+}
+
+int tgrad_timing_enable(tgrad_t* h, int enable, int max_records) {
+  if (!h || max_records < 0) return TGRAD_EINVAL;
+  h->timing = enable != 0;
+  h->max_rec = max_records;
+  return TGRAD_OK;
+}
+
+int tgrad_timing_read(tgrad_t* h, int64_t* launches, double* ms, int n_ids) {
+  if (!h || n_ids < 0 || n_ids > TGRAD_MAX_KERNEL_IDS) return TGRAD_EINVAL;
+  DevGuard g(h->device);
+  HIPCHK(h, hipDeviceSynchronize());
+  for (int i = 0; i < n_ids; ++i) {
+    if (launches) launches[i] = 0;
+    if (ms) ms[i] = 0.0;
+  }
+  for (auto& r : h->recs) {
+    float el = 0.0f;
+    if (r.a && r.b && hipEventElapsedTime(&el, r.a, r.b) == hipSuccess && r.id < n_ids) {
+      if (launches) launches[r.id] += 1;
+      if (ms) ms[r.id] += el;
+    }
+    h->pool.push_back(r.a);
+    h->pool.push_back(r.b);
+  }
+  h->recs.clear();
+  return TGRAD_OK;
+}
+
+}  // extern "C"

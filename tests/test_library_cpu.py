@@ -1,0 +1,92 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function that
+include/tgrad.h declares, and rejects invalid arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tensor_gradient_compression_amd as tg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tgrad.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tgrad_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tg.LIB_PATH):
+        from tensor_gradient_compression_amd import build
+        build.build(verbose=False)
+    return tg.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for required in ("tgrad_init", "tgrad_step", "tgrad_refresh", "tgrad_destroy"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_binding_covers_every_declared_symbol():
+    bound = {name for name, _, _ in tg.SIGNATURES}
+    assert set(_declared()) == bound
+
+
+def test_status_strings_and_kernel_names(lib):
+    for code in range(5):
+        assert lib.tgrad_status_string(code)
+    assert lib.tgrad_status_string(99) == b"unknown status"
+    assert tg.kernel_name(0) == "topk_init"
+    assert tg.kernel_name(1000) == ""
+
+
+def test_destroy_null_is_noop(lib):
+    assert lib.tgrad_destroy(None) == tg.OK
+
+
+def _init(lib, shape, ranks, dtype=0, rho=0.05, T=10, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8):
+    h = ctypes.c_void_p()
+    nd = len(shape)
+    sh = (ctypes.c_int64 * max(nd, 1))(*shape)
+    rk = (ctypes.c_int64 * max(nd, 1))(*ranks)
+    rc = lib.tgrad_init(ctypes.byref(h), nd, sh, rk, dtype, rho, T, lr, b1, b2, eps)
+    return rc, h
+
+
+@pytest.mark.parametrize("kw", [
+    dict(shape=(), ranks=()),                               # ndim 0
+    dict(shape=(2,) * 9, ranks=(1,) * 9),                   # ndim 9
+    dict(shape=(4, 4), ranks=(5, 4)),                       # rank > size
+    dict(shape=(4, 4), ranks=(0, 4)),                       # rank 0
+    dict(shape=(65, 4), ranks=(8, 4)),                      # factor mode too large
+    dict(shape=(4, 4), ranks=(2, 2), dtype=7),              # dtype
+    dict(shape=(4, 4), ranks=(2, 2), rho=1.5),              # rho > 1
+    dict(shape=(4, 4), ranks=(2, 2), rho=-0.1),
+    dict(shape=(4, 4), ranks=(2, 2), T=0),                  # T < 1
+    dict(shape=(4, 4), ranks=(2, 2), b1=1.0),               # beta1 = 1
+    dict(shape=(4, 4), ranks=(2, 2), eps=-1.0),
+    dict(shape=(4, 4), ranks=(2, 2), lr=-1.0),
+    dict(shape=(65536, 65536), ranks=(65536, 65536)),       # N = 2^32
+])
+def test_init_rejects_invalid_arguments(lib, kw):
+    rc, h = _init(lib, **kw)
+    assert rc == tg.EINVAL
+    assert not h.value
+
+
+def test_null_handle_calls_are_einval(lib):
+    assert lib.tgrad_step(None, None, None, None) == tg.EINVAL
+    assert lib.tgrad_refresh(None, None, None) == tg.EINVAL
+    assert lib.tgrad_get_omega(None, None, 0) == tg.EINVAL
+    assert lib.tgrad_mark_refreshed(None) == tg.EINVAL
+    assert lib.tgrad_timing_enable(None, 1, 10) == tg.EINVAL
