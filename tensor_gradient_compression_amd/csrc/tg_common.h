@@ -95,8 +95,11 @@ struct ModeProd {
   const uint64_t* mask;
   const uint32_t* rank;
   const float* uS;
+  const uint32_t* omega;   // Omega ascending, |Omega| = kS (apply)
+  uint64_t kS;
   float lr;
   int has_sparse;
+  int force_ncb;           // 0: choose the tile width automatically
 };
 size_t modeprod_lds_bytes(const ModeProd& mp);
 hipError_t launch_modeprod(const ModeProd& mp, int num_cu, hipStream_t s);

@@ -497,6 +497,8 @@ int tgrad_step(tgrad_t* h, void* weight, void* grad, void* stream) {
     mp.mask = h->mask;
     mp.rank = h->rank;
     mp.uS = h->S;
+    mp.omega = h->omega;
+    mp.kS = h->k;
     mp.lr = lr;
     mp.has_sparse = h->k > 0;
     {
