@@ -63,7 +63,9 @@ def kernel_bytes(wl):
         out = size // cur[n] * wl.shape[n]
         b = size * P * 4
         if j + 1 == len(fmodes):
-            b += 2 * N * es + N // 8 + N // 16 + k * P * 4
+            # W read + written, membership mask, per-word ranks, the k sparse updates and
+            # (contiguous output tiles) their k Omega indices
+            b += 2 * N * es + N // 8 + N // 16 + k * P * 4 + k * 4
         else:
             b += out * P * 4
         rec.append(b)
@@ -86,6 +88,26 @@ def kernel_bytes(wl):
         "_flops_project": flops_proj,
         "_ncore": ncore,
     }
+
+
+def counter_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE passes (scaled by the plain-copy calibration), or None when the kernel's
+    source has changed since the counters were taken."""
+    import glob
+    import hashlib
+    for f in glob.glob(os.path.join(ROOT, "profiles", "counters_*.json")):
+        with open(f) as fh:
+            rec = json.load(fh)
+        if rec.get("kernel") != kernel:
+            continue
+        src = os.path.join(ROOT, rec["source"])
+        if not os.path.exists(src):
+            return None
+        with open(src, "rb") as fh:
+            sha = hashlib.sha256(fh.read()).hexdigest()
+        return rec["traffic_bytes"] if sha.startswith(rec["source_sha256_prefix"]) else None
+    return None
 
 
 def cpu_baseline(wl, seed=0):
@@ -207,7 +229,8 @@ def main():
     dom = max(single, key=lambda k: single[k]["ms_per_step"])
     d = kernels[dom]
     roofline = {"kernel": dom, "bound": "hbm", "achieved": d["achieved_GBs"], "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(d["achieved_GBs"] / HBM_PEAK_GBS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(d["achieved_GBs"] / HBM_PEAK_GBS, 4),
+                "traffic": counter_traffic(dom)}
     step_bytes = sum(sum(v) for k2, v in kb.items() if not k2.startswith("_"))
     step_frac = step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS
 
