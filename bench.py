@@ -71,6 +71,12 @@ def kernel_bytes(wl):
         rec.append(b)
         cur[n] = wl.shape[n]
         size = out
+    # two trailing modes per launch: input read once, output written once
+    d = len(wl.shape)
+    I1, I2, R1, R2 = wl.shape[d - 2], wl.shape[d - 1], wl.ranks[d - 2], wl.ranks[d - 1]
+    A = N // (I1 * I2)
+    proj2 = A * I1 * I2 * P * es + A * R1 * R2 * P * 4
+    rec2 = A * R1 * R2 * P * 4 + 2 * N * es + N // 8 + N // 16 + k * P * 4 + k * 4
     flops_proj = []
     size = N
     cur = list(wl.shape)
@@ -85,6 +91,8 @@ def kernel_bytes(wl):
         "adam_fused": [(ncore + k) * P * 24],
         "modeprod_reconstruct": rec[:-1],
         "modeprod_reconstruct_apply": rec[-1:],
+        "modeprod2_project_first": [proj2],
+        "modeprod2_reconstruct_apply": [rec2],
         "_flops_project": flops_proj,
         "_ncore": ncore,
     }
@@ -231,7 +239,8 @@ def main():
     roofline = {"kernel": dom, "bound": "hbm", "achieved": d["achieved_GBs"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(d["achieved_GBs"] / HBM_PEAK_GBS, 4),
                 "traffic": counter_traffic(dom)}
-    step_bytes = sum(sum(v) for k2, v in kb.items() if not k2.startswith("_"))
+    step_bytes = sum(sum(kb[name]) / len(kb[name]) * v["launches_per_step"]
+                     for name, v in kernels.items() if name in kb and kb[name])
     step_frac = step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS
 
     cpu = None

@@ -149,6 +149,13 @@ int tgrad_set_omega(tgrad_t *h, const uint32_t *omega, int64_t k);
 int tgrad_set_factor(tgrad_t *h, int mode, const float *U, int64_t n_floats);
 int tgrad_mark_refreshed(tgrad_t *h);
 
+/* Test / benchmark hook: when the last two modes are both compressed and a slab of
+ * them fits in LDS, the projection's first two mode products and the reconstruction's
+ * last two run as one launch each (the default). enable = 0 selects one launch per
+ * mode; enable = 1 returns TGRAD_EINVAL where the fused form does not apply. Results
+ * agree to fp32 rounding; takes effect at the next step. */
+int tgrad_set_fusion(tgrad_t *h, int enable);
+
 /* ---------------------------------------------------------------- timing.
  * When enabled, every kernel launch of step/refresh is bracketed by HIP events on
  * the launch stream (at most max_records launches are kept). tgrad_timing_read

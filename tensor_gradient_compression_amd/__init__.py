@@ -58,6 +58,7 @@ SIGNATURES = [
     ("tgrad_set_omega", ctypes.c_int, [_P, _P, _I64]),
     ("tgrad_set_factor", ctypes.c_int, [_P, ctypes.c_int, _P, _I64]),
     ("tgrad_mark_refreshed", ctypes.c_int, [_P]),
+    ("tgrad_set_fusion", ctypes.c_int, [_P, ctypes.c_int]),
     ("tgrad_timing_enable", ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int]),
     ("tgrad_timing_read", ctypes.c_int, [_P, _P, _P, ctypes.c_int]),
     ("tgrad_kernel_name", ctypes.c_char_p, [ctypes.c_int]),
@@ -205,6 +206,15 @@ class TGrad:
         else:
             flat = np.ascontiguousarray(U, dtype=np.float32).reshape(-1)
         self._check(self._lib.tgrad_set_factor(self._h, mode, _ptr(flat), flat.size), "tgrad_set_factor")
+
+    def set_fusion(self, enable: bool) -> bool:
+        """Select fused two-mode launches (True) or one launch per mode; returns False
+        when the fused form does not apply to this shape."""
+        rc = self._lib.tgrad_set_fusion(self._h, int(enable))
+        if rc == EINVAL and enable:
+            return False
+        self._check(rc, "tgrad_set_fusion")
+        return True
 
     def mark_refreshed(self):
         self._check(self._lib.tgrad_mark_refreshed(self._h), "tgrad_mark_refreshed")

@@ -24,13 +24,17 @@ namespace {
 
 constexpr int NTH = 256;
 
-struct EK {
+struct EK1 {
   const double* gram;
   float* U;
   float* Mproj;
   float* Mrec;
   double* eigvals;
   uint32_t n, r;
+};
+// One workgroup per matrix; up to 8 matrices (one per compressed mode) per launch.
+struct EK {
+  EK1 m[8];
 };
 
 __device__ __forceinline__ double block_sum(double v, double* red) {
@@ -47,11 +51,13 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
 }
 
 template <bool CPLX>
-__global__ void __launch_bounds__(NTH) k_eig(EK k) {
+__global__ void __launch_bounds__(NTH) k_eig(EK kk) {
   extern __shared__ double sm[];
+  const EK1& k = kk.m[blockIdx.x];
   const int tid = threadIdx.x;
   const uint32_t n = k.n;
-  const uint32_t nn = n * n;
+  const uint32_t LD = n + 1;          // odd row stride: column walks hit distinct banks
+  const uint32_t nn = n * LD;
   double* Ar = sm;
   double* Ai = CPLX ? Ar + nn : nullptr;
   double* Vr = CPLX ? Ai + nn : Ar + nn;
@@ -68,8 +74,9 @@ __global__ void __launch_bounds__(NTH) k_eig(EK k) {
 
   // Hermitian (or symmetric) matrix from the stacked real Gram, symmetrised.
   const uint32_t K = CPLX ? 2 * n : n;
-  for (uint32_t idx = tid; idx < nn; idx += NTH) {
-    const uint32_t i = idx / n, j = idx - i * n;
+  for (uint32_t idx0 = tid; idx0 < n * n; idx0 += NTH) {
+    const uint32_t i = idx0 / n, j = idx0 - i * n;
+    const uint32_t idx = i * LD + j;
     if (CPLX) {
       auto G = [&](uint32_t a, uint32_t b) { return k.gram[(uint64_t)a * K + b]; };
       const double re1 = G(2 * i, 2 * j) + G(2 * i + 1, 2 * j + 1);
@@ -90,8 +97,9 @@ __global__ void __launch_bounds__(NTH) k_eig(EK k) {
   const uint32_t half = m / 2;
   for (int sweep = 0; sweep < 40; ++sweep) {
     double off = 0.0, tot = 0.0;
-    for (uint32_t idx = tid; idx < nn; idx += NTH) {
-      const uint32_t i = idx / n, j = idx - i * n;
+    for (uint32_t idx0 = tid; idx0 < n * n; idx0 += NTH) {
+      const uint32_t i = idx0 / n, j = idx0 - i * n;
+      const uint32_t idx = i * LD + j;
       const double a2 = Ar[idx] * Ar[idx] + (CPLX ? Ai[idx] * Ai[idx] : 0.0);
       tot += a2;
       if (i != j) off += a2;
@@ -109,8 +117,8 @@ __global__ void __launch_bounds__(NTH) k_eig(EK k) {
         if (p > q) { uint32_t t = p; p = q; q = t; }
         double c = 1.0, s = 0.0, pc = 1.0, ps = 0.0;
         if (q < n) {
-          const double app = Ar[p * n + p], aqq = Ar[q * n + q];
-          const double xr = Ar[p * n + q], xi = CPLX ? Ai[p * n + q] : 0.0;
+          const double app = Ar[p * LD + p], aqq = Ar[q * LD + q];
+          const double xr = Ar[p * LD + q], xi = CPLX ? Ai[p * LD + q] : 0.0;
           const double rr = CPLX ? sqrt(xr * xr + xi * xi) : fabs(xr);
           if (rr > 0.0) {
             const double theta = (aqq - app) / (2.0 * rr);
@@ -150,31 +158,31 @@ __global__ void __launch_bounds__(NTH) k_eig(EK k) {
         if (CPLX) {
           // y' = e^{-i phi} * y
           {
-            const double xr = Ar[i * n + p], xi = Ai[i * n + p];
-            const double yr0 = Ar[i * n + q], yi0 = Ai[i * n + q];
+            const double xr = Ar[i * LD + p], xi = Ai[i * LD + p];
+            const double yr0 = Ar[i * LD + q], yi0 = Ai[i * LD + q];
             const double yr = pc * yr0 + ps * yi0, yi = pc * yi0 - ps * yr0;
-            Ar[i * n + p] = c * xr - s * yr;
-            Ai[i * n + p] = c * xi - s * yi;
-            Ar[i * n + q] = s * xr + c * yr;
-            Ai[i * n + q] = s * xi + c * yi;
+            Ar[i * LD + p] = c * xr - s * yr;
+            Ai[i * LD + p] = c * xi - s * yi;
+            Ar[i * LD + q] = s * xr + c * yr;
+            Ai[i * LD + q] = s * xi + c * yi;
           }
           {
-            const double xr = Vr[i * n + p], xi = Vi[i * n + p];
-            const double yr0 = Vr[i * n + q], yi0 = Vi[i * n + q];
+            const double xr = Vr[i * LD + p], xi = Vi[i * LD + p];
+            const double yr0 = Vr[i * LD + q], yi0 = Vi[i * LD + q];
             const double yr = pc * yr0 + ps * yi0, yi = pc * yi0 - ps * yr0;
-            Vr[i * n + p] = c * xr - s * yr;
-            Vi[i * n + p] = c * xi - s * yi;
-            Vr[i * n + q] = s * xr + c * yr;
-            Vi[i * n + q] = s * xi + c * yi;
+            Vr[i * LD + p] = c * xr - s * yr;
+            Vi[i * LD + p] = c * xi - s * yi;
+            Vr[i * LD + q] = s * xr + c * yr;
+            Vi[i * LD + q] = s * xi + c * yi;
           }
         } else {
           const double ss = s * pc;
-          const double x = Ar[i * n + p], y = Ar[i * n + q];
-          Ar[i * n + p] = c * x - ss * y;
-          Ar[i * n + q] = ss * x + c * y;
-          const double vx = Vr[i * n + p], vy = Vr[i * n + q];
-          Vr[i * n + p] = c * vx - ss * vy;
-          Vr[i * n + q] = ss * vx + c * vy;
+          const double x = Ar[i * LD + p], y = Ar[i * LD + q];
+          Ar[i * LD + p] = c * x - ss * y;
+          Ar[i * LD + q] = ss * x + c * y;
+          const double vx = Vr[i * LD + p], vy = Vr[i * LD + q];
+          Vr[i * LD + p] = c * vx - ss * vy;
+          Vr[i * LD + q] = ss * vx + c * vy;
         }
       }
       __syncthreads();
@@ -187,18 +195,18 @@ __global__ void __launch_bounds__(NTH) k_eig(EK k) {
         const double c = rc[j], s = rs[j], pc = rpc[j], ps = rps[j];
         if (CPLX) {
           // y' = e^{+i phi} * y
-          const double xr = Ar[p * n + col], xi = Ai[p * n + col];
-          const double yr0 = Ar[q * n + col], yi0 = Ai[q * n + col];
+          const double xr = Ar[p * LD + col], xi = Ai[p * LD + col];
+          const double yr0 = Ar[q * LD + col], yi0 = Ai[q * LD + col];
           const double yr = pc * yr0 - ps * yi0, yi = pc * yi0 + ps * yr0;
-          Ar[p * n + col] = c * xr - s * yr;
-          Ai[p * n + col] = c * xi - s * yi;
-          Ar[q * n + col] = s * xr + c * yr;
-          Ai[q * n + col] = s * xi + c * yi;
+          Ar[p * LD + col] = c * xr - s * yr;
+          Ai[p * LD + col] = c * xi - s * yi;
+          Ar[q * LD + col] = s * xr + c * yr;
+          Ai[q * LD + col] = s * xi + c * yi;
         } else {
           const double ss = s * pc;
-          const double x = Ar[p * n + col], y = Ar[q * n + col];
-          Ar[p * n + col] = c * x - ss * y;
-          Ar[q * n + col] = ss * x + c * y;
+          const double x = Ar[p * LD + col], y = Ar[q * LD + col];
+          Ar[p * LD + col] = c * x - ss * y;
+          Ar[q * LD + col] = ss * x + c * y;
         }
       }
       __syncthreads();
@@ -213,7 +221,7 @@ __global__ void __launch_bounds__(NTH) k_eig(EK k) {
       double bv = 0.0;
       for (uint32_t i = 0; i < n; ++i) {
         if ((used >> i) & 1ull) continue;
-        const double d = Ar[i * n + i];
+        const double d = Ar[i * LD + i];
         if (best < 0 || d > bv) { best = (int)i; bv = d; }
       }
       used |= 1ull << best;
@@ -221,7 +229,7 @@ __global__ void __launch_bounds__(NTH) k_eig(EK k) {
     }
   }
   __syncthreads();
-  for (uint32_t i = tid; i < n; i += NTH) k.eigvals[i] = Ar[order[i] * n + order[i]];
+  for (uint32_t i = tid; i < n; i += NTH) k.eigvals[i] = Ar[order[i] * LD + order[i]];
 
   const uint32_t r = k.r;
   const uint32_t P = CPLX ? 2 : 1;
@@ -230,16 +238,16 @@ __global__ void __launch_bounds__(NTH) k_eig(EK k) {
     uint32_t imax = 0;
     double best = -1.0;
     for (uint32_t i = 0; i < n; ++i) {
-      const double vr = Vr[i * n + src], vi = CPLX ? Vi[i * n + src] : 0.0;
+      const double vr = Vr[i * LD + src], vi = CPLX ? Vi[i * LD + src] : 0.0;
       const double a2 = vr * vr + vi * vi;
       if (a2 > best) { best = a2; imax = i; }
     }
-    const double vr = Vr[imax * n + src], vi = CPLX ? Vi[imax * n + src] : 0.0;
+    const double vr = Vr[imax * LD + src], vi = CPLX ? Vi[imax * LD + src] : 0.0;
     const double mag = sqrt(vr * vr + vi * vi);
     const double sr = mag > 0.0 ? vr / mag : 1.0;     // scale = conj(phase)
     const double si = mag > 0.0 ? -vi / mag : 0.0;
     for (uint32_t i = 0; i < n; ++i) {
-      const double xr = Vr[i * n + src], xi = CPLX ? Vi[i * n + src] : 0.0;
+      const double xr = Vr[i * LD + src], xi = CPLX ? Vi[i * LD + src] : 0.0;
       const float ur = (float)(xr * sr - xi * si);
       const float ui = (float)(xr * si + xi * sr);
       if (CPLX) {
@@ -267,29 +275,34 @@ __global__ void __launch_bounds__(NTH) k_eig(EK k) {
 }  // namespace
 
 size_t eig_lds_bytes(uint32_t I, uint32_t P) {
-  const size_t nn = (size_t)I * I;
+  const size_t nn = (size_t)I * (I + 1);
   const size_t mats = (P == 2 ? 4 : 2) * nn;
   return (mats + 4 * 32 + NTH) * sizeof(double) + (32 + 32 + 64) * sizeof(int);
 }
 
-hipError_t launch_eig(const EigArgs& e, hipStream_t s) {
-  if (e.I > 64 || e.r > e.I || e.r < 1) return hipErrorInvalidValue;
+hipError_t launch_eig(const EigArgs* e, int count, hipStream_t s) {
+  if (count < 1 || count > 8) return hipErrorInvalidValue;
   EK k;
-  k.gram = e.gram;
-  k.U = e.U;
-  k.Mproj = e.Mproj;
-  k.Mrec = e.Mrec;
-  k.eigvals = e.eigvals;
-  k.n = e.I;
-  k.r = e.r;
-  const size_t lds = eig_lds_bytes(e.I, e.P);
-  auto fn = (e.P == 2) ? k_eig<true> : k_eig<false>;
+  size_t lds = 0;
+  for (int i = 0; i < count; ++i) {
+    if (e[i].I > 64 || e[i].r > e[i].I || e[i].r < 1 || e[i].P != e[0].P) return hipErrorInvalidValue;
+    k.m[i].gram = e[i].gram;
+    k.m[i].U = e[i].U;
+    k.m[i].Mproj = e[i].Mproj;
+    k.m[i].Mrec = e[i].Mrec;
+    k.m[i].eigvals = e[i].eigvals;
+    k.m[i].n = e[i].I;
+    k.m[i].r = e[i].r;
+    const size_t b = eig_lds_bytes(e[i].I, e[i].P);
+    if (b > lds) lds = b;
+  }
+  auto fn = (e[0].P == 2) ? k_eig<true> : k_eig<false>;
   if (lds > 64 * 1024) {
     hipError_t err = hipFuncSetAttribute((const void*)fn,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(fn, dim3(1), dim3(NTH), lds, s, k);
+  hipLaunchKernelGGL(fn, dim3(count), dim3(NTH), lds, s, k);
   return hipGetLastError();
 }
 

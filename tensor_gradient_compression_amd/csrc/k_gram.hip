@@ -153,12 +153,26 @@ __global__ void __launch_bounds__(NTH) k_gram(GK k) {
   }
 }
 
-__global__ void k_gram_reduce(const double* __restrict__ partial, uint32_t nblk, uint32_t n2,
-                              double* __restrict__ out) {
+// Fixed-order two-stage sum of the workgroup partials: stage 1 sums group g's
+// contiguous range of partials for every entry, stage 2 sums the groups in order.
+constexpr uint32_t RGROUPS = 32;
+__global__ void k_gram_reduce1(const double* __restrict__ partial, uint32_t nblk, uint32_t n2,
+                               double* __restrict__ stage) {
+  const uint32_t x = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t g = blockIdx.y;
+  if (x >= n2) return;
+  const uint32_t per = (nblk + RGROUPS - 1) / RGROUPS;
+  const uint32_t w0 = g * per, w1 = w0 + per < nblk ? w0 + per : nblk;
+  double s = 0.0;
+  for (uint32_t w = w0; w < w1; ++w) s += partial[(uint64_t)w * n2 + x];
+  stage[(uint64_t)g * n2 + x] = s;
+}
+__global__ void k_gram_reduce2(const double* __restrict__ stage, uint32_t n2,
+                               double* __restrict__ out) {
   const uint32_t x = blockIdx.x * blockDim.x + threadIdx.x;
   if (x >= n2) return;
   double s = 0.0;
-  for (uint32_t w = 0; w < nblk; ++w) s += partial[(uint64_t)w * n2 + x];
+  for (uint32_t g = 0; g < RGROUPS; ++g) s += stage[(uint64_t)g * n2 + x];
   out[x] = s;
 }
 
@@ -210,6 +224,8 @@ hipError_t pick_nob(const GK& k, size_t lds, unsigned grid, hipStream_t s) {
 
 }  // namespace
 
+uint32_t gram_reduce_groups() { return RGROUPS; }
+
 uint32_t gram_blocks(const GramArgs& g, int num_cu) {
   const GGeo r = ggeo(g);
   uint64_t nb = (uint64_t)(num_cu > 0 ? num_cu : 256) * 4;
@@ -256,8 +272,10 @@ hipError_t launch_gram(const GramArgs& g, int num_cu, hipStream_t s,
   if (mark) mark(mctx, KID_GRAM, false);
   if (e != hipSuccess) return e;
   const uint32_t n2 = r.Kin * r.Kin;
+  double* stage = g.partial + (uint64_t)nblk * n2;
   if (mark) mark(mctx, KID_GRAM_REDUCE, true);
-  k_gram_reduce<<<(n2 + 255) / 256, 256, 0, s>>>(g.partial, nblk, n2, g.out);
+  k_gram_reduce1<<<dim3((n2 + 255) / 256, RGROUPS), 256, 0, s>>>(g.partial, nblk, n2, stage);
+  k_gram_reduce2<<<(n2 + 255) / 256, 256, 0, s>>>(stage, n2, g.out);
   if (mark) mark(mctx, KID_GRAM_REDUCE, false);
   return hipGetLastError();
 }

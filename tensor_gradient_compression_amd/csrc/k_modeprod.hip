@@ -213,9 +213,12 @@ __global__ void __launch_bounds__(NTH) k_modeprod(MPK k) {
     }
   }
 
+  // vmcnt counts both the transfers and the stores of this thread. Waiting right
+  // before the stream-out (not at the top of the loop) lets the next tile's transfer
+  // overlap the multiply and lets this tile's stores drain during the next iteration.
+  __builtin_amdgcn_s_waitcnt(0);
   for (; tile < k.ntiles; tile += gridDim.x) {
     const uint64_t next = tile + gridDim.x;
-    __builtin_amdgcn_s_waitcnt(0);   // this thread's transfers (and stores) completed
     __syncthreads();                 // every thread's transfers visible; buffers free
     const TileGeo gc = g;
     unsigned char* bx = lds + (cur ? k.off_x1 : k.off_x0);
@@ -341,6 +344,10 @@ __global__ void __launch_bounds__(NTH) k_modeprod(MPK k) {
       }
       __syncthreads();
     }
+
+    // this thread's transfer of the next tile has landed (it is read after the next
+    // barrier), and the previous tile's stores have completed
+    __builtin_amdgcn_s_waitcnt(0);
 
     // stream the output tile out in memory order
     auto finish = [&](uint64_t gi, float d, float w) -> float {

@@ -1,0 +1,444 @@
+// Two trailing mode products in one pass: the projection's first two products
+// (modes d, then d-1) and the reconstruction's last two (modes d-1, then d, fused with
+// the weight update).
+//
+// Same mathematics as the one-mode kernel (pith.science "What carries the argument":
+// projection to the core and reconstruction by mode-wise products; appendix M
+// Theorem 2: project, update, project back), reorganised so the intermediate between
+// the two products never leaves LDS. The tensor is viewed as A slabs of the last two
+// modes, (A, I1, I2, P); a slab is contiguous in memory, so a tile of TA slabs is one
+// contiguous block in and one contiguous block out.
+//   projection:     Y[a, i1, j2] = sum_i2 M2[j2, i2] X[a, i1, i2]       (mode d)
+//                   Z[a, j1, j2] = sum_i1 M1[j1, i1] Y[a, i1, j2]       (mode d-1)
+//   reconstruction: Y[a, i1, j2] = sum_j1 M1[i1, j1] Z[a, j1, j2]       (mode d-1)
+//                   O[a, i1, i2] = sum_j2 M2[i2, j2] Y[a, i1, j2]       (mode d)
+//                   W <- round(W - lr * (O + N_S at Omega))
+// (indices include the complex part p, as in the one-mode kernel). Each product is an
+// MFMA GEMM over LDS operands (v_mfma_f32_16x16x4_f32, fp32 accumulation). Input tiles
+// (and W tiles) move HBM -> LDS with 16-byte global_load_lds transfers, double
+// buffered; outputs leave with 16-byte stores. Versus two one-mode launches this skips
+// writing and re-reading the fp32 intermediate between the two products (nullthought
+// summary section 3: no second full tensor).
+#include <algorithm>
+
+#include "tg_common.h"
+
+namespace tg {
+
+namespace {
+
+constexpr int NTH = 256;
+constexpr int NRBMAX = 8;   // up to 128 output rows per product (16 per block)
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+struct MP2K {
+  const void* X;
+  const float* M1;
+  const float* M2;
+  float* Y;
+  void* W;
+  const uint64_t* mask;
+  const uint32_t* rank;
+  const float* uS;
+  const uint32_t* omega;
+  uint64_t kS, N;
+  uint64_t ntiles;
+  uint32_t A, TA;
+  uint32_t I1, I2, R1, R2;          // input and output slab sizes (elements)
+  uint32_t recon;                   // 0 projection, 1 reconstruction
+  // GEMM shapes of the two passes (values, complex parts included)
+  uint32_t k1, kp1, m1, mp1, k2, kp2, m2, mp2;
+  uint32_t dma_in, dma_w, vout;
+  uint32_t off_m2, off_x0, off_x1, off_y, off_o, off_w0, off_w1;
+  float lr;
+  int has_sparse;
+};
+
+// One mode product between LDS buffers over the (A', I, B, P) view: ncols = A' * B
+// GEMM columns; dst[a', jj, b] = sum_kk sM[jj, kk] src[a', kk, b]. Each wave takes
+// 16-column blocks in turn and one 16-row output block at a time. The inner loop is one
+// A read at a fixed stride, one B read from a strength-reduced pointer and the MFMA:
+// only the last k-step can hold rows >= Kin (zeroed there), and lanes of columns past
+// ncols read a real column whose result is dropped.
+template <typename ST, int P>
+__device__ __forceinline__ void lds_gemm(const ST* src, uint32_t ncols, uint32_t B, uint32_t I,
+                                         uint32_t R, const float* sM, uint32_t Kin,
+                                         uint32_t Kpad, uint32_t Mout, uint32_t Mpad,
+                                         float* dst) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave = threadIdx.x >> 6;
+  const uint32_t g = lane >> 4, li = lane & 15;
+  const uint32_t LDM = Kpad + 1;
+  const uint32_t rs = B * P;
+  const uint32_t blk_in = I * B * P, blk_out = R * B * P;
+  const uint32_t ncb = (ncols + 15) / 16;
+  const uint32_t nks = Kpad >> 2;
+  // row kk = 4*ks + g of a column sits at (kk / P) * rs + kk % P
+  const uint32_t goff = (P == 1) ? g * rs : (g >> 1) * rs + (g & 1);
+  const uint32_t kstep = (P == 1) ? 4 * rs : 2 * rs;
+  const bool last_ok = 4 * (nks - 1) + g < Kin;
+  for (uint32_t cb = wave; cb < ncb; cb += 4) {
+    const uint32_t c0 = cb * 16 + li;
+    const bool valid = c0 < ncols;
+    const uint32_t col = valid ? c0 : ncols - 1;
+    const uint32_t ca = col / B, cbb = col - ca * B;
+    const ST* bp = src + ca * blk_in + cbb * P + goff;
+    const uint32_t cout = ca * blk_out + cbb * P;
+    for (uint32_t r0 = 0; r0 < Mpad; r0 += 16) {
+      const float* ap = sM + (r0 + li) * LDM + g;
+      f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+      const ST* b = bp;
+      for (uint32_t ks = 0; ks + 1 < nks; ++ks) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ap[4 * ks], to_f32(*b), acc, 0, 0, 0);
+        b += kstep;
+      }
+      const float bl = last_ok ? to_f32(*b) : 0.0f;
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ap[4 * (nks - 1)], bl, acc, 0, 0, 0);
+      if (valid) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t jj = r0 + 4 * g + v;
+          if (jj < Mout) dst[cout + (jj / P) * rs + (jj % P)] = acc[v];
+        }
+      }
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void dma_block(const T* src, uint32_t nvals, unsigned char* dst) {
+  constexpr uint32_t V = 16 / sizeof(T);
+  const uint32_t total = nvals / V;
+  const int tid = threadIdx.x;
+  const uint32_t wave_base = (uint32_t)(tid & ~63);
+  for (uint32_t q0 = 0; q0 < total; q0 += NTH) {
+    const uint32_t q = q0 + tid;
+    unsigned char* lds = dst + (size_t)(q0 + wave_base) * 16;   // wave-uniform
+    if (q < total)
+      __builtin_amdgcn_global_load_lds((const void*)(src + (uint64_t)q * V), (lds_void*)lds, 16, 0, 0);
+  }
+}
+
+template <typename XT, int P, int EPI, typename WT>
+__global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
+  constexpr int VO = (EPI == 0) ? 4 : 16 / (int)sizeof(WT);
+  extern __shared__ float smem[];
+  unsigned char* lds = (unsigned char*)smem;
+  const int tid = threadIdx.x;
+  float* sM1 = smem;
+  float* sM2 = (float*)(lds + k.off_m2);
+  float* sYm = (float*)(lds + k.off_y);
+  float* sO = (float*)(lds + k.off_o);
+  const XT* __restrict__ X = (const XT*)k.X;
+
+  for (uint32_t idx = tid; idx < k.mp1 * k.kp1; idx += NTH) {
+    const uint32_t jj = idx / k.kp1, kk = idx - jj * k.kp1;
+    sM1[jj * (k.kp1 + 1) + kk] = (jj < k.m1 && kk < k.k1) ? k.M1[(uint64_t)jj * k.k1 + kk] : 0.0f;
+  }
+  for (uint32_t idx = tid; idx < k.mp2 * k.kp2; idx += NTH) {
+    const uint32_t jj = idx / k.kp2, kk = idx - jj * k.kp2;
+    sM2[jj * (k.kp2 + 1) + kk] = (jj < k.m2 && kk < k.k2) ? k.M2[(uint64_t)jj * k.k2 + kk] : 0.0f;
+  }
+
+  const uint32_t slab_in = k.I1 * k.I2 * P, slab_out = k.R1 * k.R2 * P;
+  // projection: pass 1 is mode d (M = M2), pass 2 mode d-1 (M = M1);
+  // reconstruction: pass 1 is mode d-1 (M = M1), pass 2 mode d (M = M2).
+  const float* sA = k.recon ? sM1 : sM2;
+  const float* sB = k.recon ? sM2 : sM1;
+  const uint32_t ka = k.recon ? k.k1 : k.k2, kpa = k.recon ? k.kp1 : k.kp2;
+  const uint32_t ma = k.recon ? k.m1 : k.m2, mpa = k.recon ? k.mp1 : k.mp2;
+  const uint32_t kb = k.recon ? k.k2 : k.k1, kpb = k.recon ? k.kp2 : k.kp1;
+  const uint32_t mb = k.recon ? k.m2 : k.m1, mpb = k.recon ? k.mp2 : k.mp1;
+
+  auto can_dma_in = [&](uint32_t nta) { return k.dma_in && (nta * slab_in * sizeof(XT)) % 16 == 0; };
+  auto can_dma_w = [&](uint32_t nta) {
+    return EPI == 1 && k.dma_w && (nta * slab_out * sizeof(WT)) % 16 == 0;
+  };
+  auto nta_of = [&](uint64_t tile) -> uint32_t {
+    const uint64_t a0 = tile * k.TA;
+    return (uint64_t)k.A - a0 < k.TA ? (uint32_t)((uint64_t)k.A - a0) : k.TA;
+  };
+  auto issue = [&](uint64_t tile, int buf) {
+    const uint32_t nta = nta_of(tile);
+    const uint64_t a0 = tile * k.TA;
+    if (can_dma_in(nta))
+      dma_block<XT>(X + a0 * slab_in, nta * slab_in, lds + (buf ? k.off_x1 : k.off_x0));
+    if (EPI == 1 && can_dma_w(nta))
+      dma_block<WT>((const WT*)k.W + a0 * slab_out, nta * slab_out,
+                    lds + (buf ? k.off_w1 : k.off_w0));
+  };
+  auto rank_of = [&](uint64_t e) -> uint64_t {
+    if (e >= k.N) return k.kS;
+    const uint64_t word = k.mask[e >> 6];
+    return k.rank[e >> 6] + (uint64_t)__popcll(word & ((1ull << (e & 63)) - 1ull));
+  };
+  const bool merged = (EPI == 1) && k.has_sparse;
+  constexpr int NSR = 2;
+  uint64_t jc0 = 0, jc1 = 0, jn0 = 0, jn1 = 0;
+
+  uint64_t tile = blockIdx.x;
+  int cur = 0;
+  if (tile < k.ntiles) {
+    issue(tile, cur);
+    if (merged) {
+      const uint64_t a0 = tile * k.TA;
+      jc0 = rank_of(a0 * slab_out / P);
+      jc1 = rank_of((a0 + nta_of(tile)) * slab_out / P);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  for (; tile < k.ntiles; tile += gridDim.x) {
+    const uint64_t next = tile + gridDim.x;
+    __syncthreads();
+    const uint32_t nta = nta_of(tile);
+    const uint64_t a0 = tile * k.TA;
+    unsigned char* bx = lds + (cur ? k.off_x1 : k.off_x0);
+    unsigned char* bw = lds + (cur ? k.off_w1 : k.off_w0);
+    if (next < k.ntiles) {
+      issue(next, cur ^ 1);
+      if (merged) {
+        const uint64_t an = next * k.TA;
+        jn0 = rank_of(an * slab_out / P);
+        jn1 = rank_of((an + nta_of(next)) * slab_out / P);
+      }
+    }
+    uint32_t om_r[NSR];
+    float us_r[NSR][P];
+    if (merged) {
+#pragma unroll
+      for (int i = 0; i < NSR; ++i) {
+        const uint64_t j = jc0 + tid + (uint64_t)NTH * i;
+        if (j < jc1) {
+          om_r[i] = k.omega[j];
+#pragma unroll
+          for (int p = 0; p < P; ++p) us_r[i][p] = k.uS[j * P + p];
+        }
+      }
+    }
+    bool filled = false;
+    if (!can_dma_in(nta)) {
+      XT* d = (XT*)bx;
+      for (uint32_t idx = tid; idx < nta * slab_in; idx += NTH) d[idx] = X[a0 * slab_in + idx];
+      filled = true;
+    }
+    if (EPI == 1 && !can_dma_w(nta)) {
+      WT* d = (WT*)bw;
+      const WT* W = (const WT*)k.W;
+      for (uint32_t idx = tid; idx < nta * slab_out; idx += NTH) d[idx] = W[a0 * slab_out + idx];
+      filled = true;
+    }
+    if (filled) __syncthreads();
+
+    if (!k.recon) {
+      // mode d: (A' = nta*I1, I = I2, B = 1) -> (nta*I1, R2, 1)
+      lds_gemm<XT, P>((const XT*)bx, nta * k.I1, 1, k.I2, k.R2, sA, ka, kpa, ma, mpa, sYm);
+      __syncthreads();
+      // mode d-1: (A' = nta, I = I1, B = R2) -> (nta, R1, R2)
+      lds_gemm<float, P>(sYm, nta * k.R2, k.R2, k.I1, k.R1, sB, kb, kpb, mb, mpb, sO);
+    } else {
+      // mode d-1: (A' = nta, I = I1, B = I2) -> (nta, R1, I2)
+      lds_gemm<XT, P>((const XT*)bx, nta * k.I2, k.I2, k.I1, k.R1, sA, ka, kpa, ma, mpa, sYm);
+      __syncthreads();
+      // mode d: (A' = nta*R1, I = I2, B = 1) -> (nta*R1, R2, 1)
+      lds_gemm<float, P>(sYm, nta * k.R1, 1, k.I2, k.R2, sB, kb, kpb, mb, mpb, sO);
+    }
+    __syncthreads();
+    if (merged) {
+      const uint64_t e_lo = a0 * slab_out / P;
+#pragma unroll
+      for (int i = 0; i < NSR; ++i) {
+        const uint64_t j = jc0 + tid + (uint64_t)NTH * i;
+        if (j < jc1) {
+          const uint32_t loc = (uint32_t)(om_r[i] - e_lo) * P;
+#pragma unroll
+          for (int p = 0; p < P; ++p) sO[loc + p] = sO[loc + p] + us_r[i][p];
+        }
+      }
+      for (uint64_t j = jc0 + (uint64_t)NTH * NSR + tid; j < jc1; j += NTH) {
+        const uint32_t loc = (uint32_t)(k.omega[j] - e_lo) * P;
+#pragma unroll
+        for (int p = 0; p < P; ++p) sO[loc + p] = sO[loc + p] + k.uS[j * P + p];
+      }
+      __syncthreads();
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // next tile's transfer landed; previous stores done
+
+    const uint32_t len = nta * slab_out;
+    const uint64_t gbase = a0 * slab_out;
+    if (k.vout && len % VO == 0) {
+      for (uint32_t q = tid; q < len / VO; q += NTH) {
+        const uint32_t off = q * VO;
+        float d[VO];
+#pragma unroll
+        for (int e = 0; e < VO; e += 4) {
+          const float4 t = *(const float4*)(sO + off + e);
+          d[e] = t.x; d[e + 1] = t.y; d[e + 2] = t.z; d[e + 3] = t.w;
+        }
+        if (EPI == 0) {
+          *(float4*)&k.Y[gbase + off] = make_float4(d[0], d[1], d[2], d[3]);
+        } else {
+          const uint4 wraw = *(const uint4*)(bw + (size_t)off * sizeof(WT));
+          const WT* ws = (const WT*)&wraw;
+          WT wv[VO];
+#pragma unroll
+          for (int e = 0; e < VO; ++e) wv[e] = from_f32<WT>(to_f32(ws[e]) - k.lr * d[e]);
+          *(uint4*)((WT*)k.W + gbase + off) = *(const uint4*)wv;
+        }
+      }
+    } else {
+      for (uint32_t q = tid; q < len; q += NTH) {
+        if (EPI == 0) {
+          k.Y[gbase + q] = sO[q];
+        } else {
+          const float w = to_f32(((const WT*)bw)[q]);
+          ((WT*)k.W)[gbase + q] = from_f32<WT>(w - k.lr * sO[q]);
+        }
+      }
+    }
+    cur ^= 1;
+    jc0 = jn0;
+    jc1 = jn1;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+size_t esz(int dt) { return dt == DT_F32 ? 4 : 2; }
+
+struct Geo2 {
+  MP2K k;
+  size_t lds;
+  bool ok;
+};
+
+Geo2 plan(const ModeProd2& mp, uint32_t TA) {
+  Geo2 g{};
+  MP2K& k = g.k;
+  const uint32_t P = mp.P;
+  k.I1 = mp.I1;
+  k.I2 = mp.I2;
+  k.R1 = mp.R1;
+  k.R2 = mp.R2;
+  k.recon = mp.recon;
+  // pass shapes: M1 is (R1*P) x (I1*P), M2 is (R2*P) x (I2*P)
+  k.k1 = mp.I1 * P; k.m1 = mp.R1 * P;
+  k.k2 = mp.I2 * P; k.m2 = mp.R2 * P;
+  k.kp1 = (k.k1 + 3) & ~3u; k.mp1 = (k.m1 + 15) & ~15u;
+  k.kp2 = (k.k2 + 3) & ~3u; k.mp2 = (k.m2 + 15) & ~15u;
+  g.ok = k.mp1 <= 16 * NRBMAX && k.mp2 <= 16 * NRBMAX && k.kp1 <= 128 && k.kp2 <= 128;
+  k.A = mp.A;
+  k.TA = TA;
+  k.ntiles = ((uint64_t)mp.A + TA - 1) / TA;
+  const size_t esx = P == 2 ? 4 : esz(mp.in_dt);
+  const size_t esw = mp.apply ? (P == 2 ? 4 : esz(mp.w_dt)) : 4;
+  const size_t slab_in = (size_t)mp.I1 * mp.I2 * P, slab_out = (size_t)mp.R1 * mp.R2 * P;
+  const size_t slab_mid = mp.recon ? (size_t)mp.R1 * mp.I2 * P : (size_t)mp.I1 * mp.R2 * P;
+  auto al = [](size_t x) { return (x + 15) & ~(size_t)15; };
+  size_t off = al((size_t)k.mp1 * (k.kp1 + 1) * 4);
+  k.off_m2 = (uint32_t)off; off += al((size_t)k.mp2 * (k.kp2 + 1) * 4);
+  k.off_x0 = (uint32_t)off; off += al(TA * slab_in * esx);
+  k.off_x1 = (uint32_t)off; off += al(TA * slab_in * esx);
+  k.off_y = (uint32_t)off; off += al(TA * slab_mid * 4);
+  k.off_o = (uint32_t)off; off += al(TA * slab_out * 4);
+  k.off_w0 = (uint32_t)off; off += mp.apply ? al(TA * slab_out * esw) : 0;
+  k.off_w1 = (uint32_t)off; off += mp.apply ? al(TA * slab_out * esw) : 0;
+  g.lds = off;
+  const auto a16 = [](const void* p) { return ((uintptr_t)p) % 16 == 0; };
+  k.dma_in = a16(mp.X) && (TA * slab_in * esx) % 16 == 0;
+  k.dma_w = mp.apply && a16(mp.W) && (TA * slab_out * esw) % 16 == 0;
+  k.vout = a16(mp.apply ? mp.W : (const void*)mp.Y) && (TA * slab_out * esw) % 16 == 0;
+  return g;
+}
+
+template <typename XT, int P, int EPI, typename WT>
+hipError_t go2(const MP2K& k, size_t lds, unsigned grid, hipStream_t s) {
+  auto fn = k_modeprod2<XT, P, EPI, WT>;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)fn,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(NTH), lds, s, k);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// MFMA k-steps the busiest wave spends on one pass of a tile, as lds_gemm splits it:
+// 16-column blocks dealt round-robin to the 4 waves, each running every 16-row block.
+static uint64_t pass_steps(uint64_t ncols, uint32_t kpad, uint32_t mpad) {
+  const uint64_t ncb = (ncols + 15) / 16;
+  return ((ncb + 3) / 4) * (mpad / 16) * (kpad / 4);
+}
+
+// Tile (whole slabs) with LDS <= 52 KB (three or more workgroups per CU) that minimises
+// the busiest wave's MFMA k-steps per slab over both passes (larger tile on ties); 0
+// when not even one slab fits (or a product is too large): the caller then uses two
+// one-mode launches.
+uint32_t modeprod2_tile(const ModeProd2& mp) {
+  uint32_t best = 0;
+  double best_cost = 0.0;
+  for (uint32_t TA = 1; TA <= 64; ++TA) {
+    const Geo2 g = plan(mp, TA);
+    if (!g.ok || g.lds > 52 * 1024) break;
+    const MP2K& k = g.k;
+    const uint64_t steps =
+        mp.recon ? pass_steps((uint64_t)TA * mp.I2, k.kp1, k.mp1) +
+                       pass_steps((uint64_t)TA * mp.R1, k.kp2, k.mp2)
+                 : pass_steps((uint64_t)TA * mp.I1, k.kp2, k.mp2) +
+                       pass_steps((uint64_t)TA * mp.R2, k.kp1, k.mp1);
+    const double cost = (double)steps / TA;
+    if (!best || cost <= best_cost) {
+      best = TA;
+      best_cost = cost;
+    }
+    if ((uint64_t)TA >= mp.A) break;
+  }
+  return best;
+}
+
+hipError_t launch_modeprod2(const ModeProd2& mp, int num_cu, hipStream_t s) {
+  const uint32_t TA = mp.force_ta ? mp.force_ta : modeprod2_tile(mp);
+  if (!TA) return hipErrorInvalidValue;
+  Geo2 g = plan(mp, TA);
+  if (!g.ok || g.lds > 160 * 1024) return hipErrorInvalidValue;
+  MP2K& k = g.k;
+  k.X = mp.X;
+  k.M1 = mp.M1;
+  k.M2 = mp.M2;
+  k.Y = mp.Y;
+  k.W = mp.W;
+  k.mask = mp.mask;
+  k.rank = mp.rank;
+  k.uS = mp.uS;
+  k.omega = mp.omega;
+  k.kS = mp.kS;
+  k.N = (uint64_t)mp.A * mp.R1 * mp.R2;
+  k.lr = mp.lr;
+  k.has_sparse = mp.has_sparse;
+  const size_t per_cu = g.lds ? (160 * 1024) / g.lds : 8;
+  uint64_t occ = per_cu < 1 ? 1 : (per_cu > 8 ? 8 : per_cu);
+  uint64_t grid = (uint64_t)(num_cu > 0 ? num_cu : 256) * occ;
+  if (grid > k.ntiles) grid = k.ntiles;
+  if (grid < 1) grid = 1;
+  const unsigned gr = (unsigned)grid;
+  if (!mp.apply) {
+    if (mp.P == 2) return go2<float, 2, 0, float>(k, g.lds, gr, s);
+    switch (mp.in_dt) {
+      case DT_F32: return go2<float, 1, 0, float>(k, g.lds, gr, s);
+      case DT_F16: return go2<_Float16, 1, 0, float>(k, g.lds, gr, s);
+      case DT_BF16: return go2<bf16_t, 1, 0, float>(k, g.lds, gr, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (mp.P == 2) return go2<float, 2, 1, float>(k, g.lds, gr, s);
+  switch (mp.w_dt) {
+    case DT_F32: return go2<float, 1, 1, float>(k, g.lds, gr, s);
+    case DT_F16: return go2<float, 1, 1, _Float16>(k, g.lds, gr, s);
+    case DT_BF16: return go2<float, 1, 1, bf16_t>(k, g.lds, gr, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tg

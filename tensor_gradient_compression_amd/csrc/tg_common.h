@@ -17,15 +17,11 @@ __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(((uin
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return (_Float16)x; }
-// Round to nearest even; a NaN keeps its upper bits and is made quiet.
+// Round to nearest even (gfx950's v_cvt_pk_bf16_f32); a NaN stays a NaN.
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
-  uint32_t u = __float_as_uint(x);
+  const __bf16 h = (__bf16)x;
   bf16_t r;
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) {
-    r.b = (uint16_t)((u >> 16) | 0x40u);
-  } else {
-    r.b = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-  }
+  __builtin_memcpy(&r.b, &h, 2);
   return r;
 }
 template <typename T> __device__ __forceinline__ T zero_of();
@@ -49,7 +45,8 @@ enum KernelId {
   KID_TOPK_INIT = 0, KID_TOPK_HIST, KID_TOPK_SELECT, KID_TOPK_COUNT, KID_TOPK_SCAN,
   KID_TOPK_COMPACT, KID_MASK_FROM_OMEGA, KID_GATHER, KID_PROJECT, KID_ADAM,
   KID_RECONSTRUCT, KID_RECON_APPLY, KID_APPLY_DENSE, KID_GRAM, KID_GRAM_REDUCE,
-  KID_EIG, KID_FILL, KID_PROJECT_FIRST, KID_COUNT_
+  KID_EIG, KID_FILL, KID_PROJECT_FIRST, KID_PROJECT_FUSED2, KID_RECON_FUSED2_APPLY,
+  KID_RECON_FUSED2, KID_COUNT_
 };
 
 // ---------------------------------------------------------------- launchers
@@ -104,6 +101,32 @@ struct ModeProd {
 size_t modeprod_lds_bytes(const ModeProd& mp);
 hipError_t launch_modeprod(const ModeProd& mp, int num_cu, hipStream_t s);
 
+// Two trailing mode products in one launch over slabs (A, I1, I2, P) -> (A, R1, R2, P).
+// M1 is (R1*P) x (I1*P) (mode d-1), M2 is (R2*P) x (I2*P) (mode d). recon = 0: mode d
+// first (projection); recon = 1: mode d-1 first (reconstruction), optionally applying.
+struct ModeProd2 {
+  const void* X;
+  int in_dt;
+  uint32_t P, A, I1, I2, R1, R2;
+  int recon;
+  const float* M1;
+  const float* M2;
+  int apply;
+  float* Y;
+  void* W;
+  int w_dt;
+  const uint64_t* mask;
+  const uint32_t* rank;
+  const float* uS;
+  const uint32_t* omega;
+  uint64_t kS;
+  float lr;
+  int has_sparse;
+  uint32_t force_ta;       // 0: choose the slabs per tile automatically
+};
+uint32_t modeprod2_tile(const ModeProd2& mp);   // 0: does not fit
+hipError_t launch_modeprod2(const ModeProd2& mp, int num_cu, hipStream_t s);
+
 // Gram of the (A, I, B, P) view with Omega entries treated as zero:
 // out[x, y] (fp64, (I*P) x (I*P)) = sum over (a, b) of X[a, x, b] X[a, y, b].
 struct GramArgs {
@@ -115,6 +138,7 @@ struct GramArgs {
   double* out;           // (I*P)^2
 };
 uint32_t gram_blocks(const GramArgs& g, int num_cu);
+uint32_t gram_reduce_groups();   // partial buffer holds (blocks + groups) * (I*P)^2
 size_t gram_lds_bytes(const GramArgs& g);
 hipError_t launch_gram(const GramArgs& g, int num_cu, hipStream_t s,
                        void (*mark)(void*, int, bool), void* mctx);
@@ -129,6 +153,6 @@ struct EigArgs {
   double* eigvals;  // I
 };
 size_t eig_lds_bytes(uint32_t I, uint32_t P);
-hipError_t launch_eig(const EigArgs& e, hipStream_t s);
+hipError_t launch_eig(const EigArgs* e, int count, hipStream_t s);   // one workgroup each
 
 }  // namespace tg

@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
+#include <utility>
 #include <string>
 #include <vector>
 
@@ -44,6 +45,8 @@ struct tgrad_handle {
   double lr = 0, b1 = 0, b2 = 0, eps = 0;
   int64_t t = 0, refreshed_for = 0;
   std::vector<int> fmodes;   // compressed modes, ascending
+  bool can_fuse = false;     // last two modes compressed and a slab fits in LDS
+  bool fuse = false;         // use the two-mode launches
 
   uint32_t* omega = nullptr;
   uint64_t* mask = nullptr;
@@ -56,7 +59,8 @@ struct tgrad_handle {
   float* Mr[TGRAD_MAX_NDIM] = {nullptr};
   double* eig[TGRAD_MAX_NDIM] = {nullptr};
   double* gram_part = nullptr;
-  double* gram = nullptr;
+  double* gram = nullptr;        // one (I*P)^2 matrix per compressed mode
+  uint64_t gram_stride = 0;
   TopkWs tw{};
 
   std::vector<void*> allocs;
@@ -194,12 +198,36 @@ void host_operands(uint32_t I, uint32_t r, uint32_t P, const float* U, float* Mp
     }
 }
 
+// Launch groups of the projection (applied in order) and the reconstruction: each group
+// is one launch, one mode or the two trailing modes together.
+void build_chain(const tgrad_t* h, bool fuse, std::vector<std::vector<int>>& proj,
+                 std::vector<std::vector<int>>& rec) {
+  proj.clear();
+  rec.clear();
+  const int nf = (int)h->fmodes.size();
+  const int d = h->d;
+  if (fuse) proj.push_back({d - 1, d - 2});
+  for (int j = nf - 1; j >= 0; --j) {
+    const int n = h->fmodes[j];
+    if (fuse && n >= d - 2) continue;
+    proj.push_back({n});
+  }
+  for (int j = 0; j < nf; ++j) {
+    const int n = h->fmodes[j];
+    if (fuse && n >= d - 2) continue;
+    rec.push_back({n});
+  }
+  if (fuse) rec.push_back({d - 2, d - 1});
+}
+
 int do_refresh(tgrad_t* h, const void* grad, hipStream_t s) {
   if (h->k > 0) {
     HIPCHK(h, launch_topk(h->dtype, grad, h->N, (uint32_t)h->k, h->tw, h->omega, h->mask,
                           h->rank, s, mark_cb, h));
   }
   const int gdt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
+  EigArgs eig[TGRAD_MAX_NDIM];
+  int ne = 0;
   for (int n : h->fmodes) {
     GramArgs g;
     g.X = grad;
@@ -208,10 +236,10 @@ int do_refresh(tgrad_t* h, const void* grad, hipStream_t s) {
     g.P = h->P;
     g.mask = h->k > 0 ? h->mask : nullptr;
     g.partial = h->gram_part;
-    g.out = h->gram;
+    g.out = h->gram + (size_t)ne * h->gram_stride;
     HIPCHK(h, launch_gram(g, h->num_cu, s, mark_cb, h));
-    EigArgs e;
-    e.gram = h->gram;
+    EigArgs& e = eig[ne++];
+    e.gram = g.out;
     e.I = (uint32_t)h->shape[n];
     e.r = (uint32_t)h->ranks[n];
     e.P = h->P;
@@ -219,10 +247,10 @@ int do_refresh(tgrad_t* h, const void* grad, hipStream_t s) {
     e.Mproj = h->Mp[n];
     e.Mrec = h->Mr[n];
     e.eigvals = h->eig[n];
-    {
-      Mark m(h, KID_EIG);
-      HIPCHK(h, launch_eig(e, s));
-    }
+  }
+  if (ne) {
+    Mark m(h, KID_EIG);
+    HIPCHK(h, launch_eig(eig, ne, s));
   }
   h->refreshed_for = h->t + 1;
   return TGRAD_OK;
@@ -250,7 +278,8 @@ const char* tgrad_kernel_name(int id) {
       "topk_init", "topk_hist", "topk_select", "topk_count", "topk_scan", "topk_compact",
       "mask_from_omega", "gather_residual", "modeprod_project", "adam_fused",
       "modeprod_reconstruct", "modeprod_reconstruct_apply", "apply_dense", "gram",
-      "gram_reduce", "eig_jacobi", "fill", "modeprod_project_first"};
+      "gram_reduce", "eig_jacobi", "fill", "modeprod_project_first",
+      "modeprod2_project_first", "modeprod2_reconstruct_apply", "modeprod2_reconstruct"};
   if (id < 0 || id >= KID_COUNT_) return "";
   return names[id];
 }
@@ -304,25 +333,54 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
   h->eps = eps;
   const uint64_t P = h->P;
 
-  // Intermediate sizes of the projection and reconstruction chains.
-  uint64_t inter = 0;
+  // Two trailing compressed modes can run as one launch in each direction.
   {
+    const int d = ndim;
+    if (d >= 2 && tucker_ranks[d - 2] < shape[d - 2] && tucker_ranks[d - 1] < shape[d - 1]) {
+      uint64_t A = 1;
+      for (int i = 0; i < d - 2; ++i) A *= (uint64_t)shape[i];
+      ModeProd2 pp{};
+      pp.in_dt = dtype == TGRAD_C64 ? DT_F32 : dtype;
+      pp.P = h->P;
+      pp.A = (uint32_t)A;
+      pp.I1 = (uint32_t)shape[d - 2];
+      pp.I2 = (uint32_t)shape[d - 1];
+      pp.R1 = (uint32_t)tucker_ranks[d - 2];
+      pp.R2 = (uint32_t)tucker_ranks[d - 1];
+      ModeProd2 rr = pp;
+      rr.recon = 1;
+      rr.in_dt = DT_F32;
+      rr.apply = 1;
+      rr.w_dt = pp.in_dt;
+      std::swap(rr.I1, rr.R1);
+      std::swap(rr.I2, rr.R2);
+      h->can_fuse = modeprod2_tile(pp) > 0 && modeprod2_tile(rr) > 0;
+      h->fuse = h->can_fuse;
+    }
+  }
+  // Largest intermediate of the projection and reconstruction chains (either plan).
+  uint64_t inter = 0;
+  for (int plan = 0; plan < 2; ++plan) {
+    const bool fz = plan == 1;
+    if (fz && !h->can_fuse) continue;
     int64_t cur[TGRAD_MAX_NDIM];
     for (int i = 0; i < ndim; ++i) cur[i] = shape[i];
+    std::vector<std::vector<int>> proj, rec;
+    build_chain(h, fz, proj, rec);
     uint64_t size = N;
-    const size_t nf = h->fmodes.size();
-    for (size_t j = 0; j < nf; ++j) {       // projection: last mode first
-      const int n = h->fmodes[nf - 1 - j];
-      size = size / (uint64_t)cur[n] * (uint64_t)h->ranks[n];
-      cur[n] = h->ranks[n];
-      if (j + 1 < nf && size > inter) inter = size;   // not the core
+    for (size_t j = 0; j < proj.size(); ++j) {
+      for (int n : proj[j]) {
+        size = size / (uint64_t)cur[n] * (uint64_t)h->ranks[n];
+        cur[n] = h->ranks[n];
+      }
+      if (j + 1 < proj.size() && size > inter) inter = size;    // not the core
     }
-    size = ncore;
-    for (size_t j = 0; j < nf; ++j) {       // reconstruction: first mode first
-      const int n = h->fmodes[j];
-      size = size / (uint64_t)cur[n] * (uint64_t)shape[n];
-      cur[n] = shape[n];
-      if (j + 1 < nf && size > inter) inter = size;   // not the weight
+    for (size_t j = 0; j < rec.size(); ++j) {
+      for (int n : rec[j]) {
+        size = size / (uint64_t)cur[n] * (uint64_t)shape[n];
+        cur[n] = shape[n];
+      }
+      if (j + 1 < rec.size() && size > inter) inter = size;     // not the weight
     }
   }
 
@@ -350,12 +408,13 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
     view(shape, ndim, n, &g.A, &g.I, &g.B);
     g.P = (uint32_t)P;
     const uint64_t K2 = (I * P) * (I * P);
-    const uint64_t nb = gram_blocks(g, h->num_cu);
+    const uint64_t nb = gram_blocks(g, h->num_cu) + gram_reduce_groups();
     if (nb * K2 > gpart) gpart = nb * K2;
     if (K2 > gmax) gmax = K2;
   }
   ok = ok && dalloc(h, &h->gram_part, gpart, false);
-  ok = ok && dalloc(h, &h->gram, gmax, false);
+  h->gram_stride = gmax;
+  ok = ok && dalloc(h, &h->gram, gmax * h->fmodes.size(), false);
   const uint64_t units = topk_units(N);
   ok = ok && dalloc(h, &h->tw.hist, 2048, false);
   ok = ok && dalloc(h, &h->tw.state, 4, false);
@@ -429,32 +488,60 @@ int tgrad_step(tgrad_t* h, void* weight, void* grad, void* stream) {
     Mark m(h, KID_GATHER);
     HIPCHK(h, launch_gather(h->dtype, grad, h->omega, (uint32_t)h->k, h->S, s));
   }
-  // projection, last compressed mode first
+  // projection: one launch per group, last compressed mode first
+  std::vector<std::vector<int>> proj, rec;
+  build_chain(h, h->fuse, proj, rec);
   int64_t cur[TGRAD_MAX_NDIM];
   for (int i = 0; i < h->d; ++i) cur[i] = h->shape[i];
   const void* X = grad;
   int xdt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
   int which = 0;
   const size_t nf = h->fmodes.size();
-  for (size_t j = 0; j < nf; ++j) {
-    const int n = h->fmodes[nf - 1 - j];
-    ModeProd mp{};
-    mp.X = X;
-    mp.in_dt = xdt;
-    mp.M = h->Mp[n];
-    view(cur, h->d, n, &mp.A, &mp.I, &mp.B);
-    mp.R = (uint32_t)h->ranks[n];
-    mp.P = P;
-    mp.apply = 0;
-    mp.Y = (j + 1 == nf) ? h->core : h->buf[which];
-    {
-      Mark m(h, j == 0 ? KID_PROJECT_FIRST : KID_PROJECT);
-      HIPCHK(h, launch_modeprod(mp, h->num_cu, s));
+  for (size_t j = 0; j < proj.size(); ++j) {
+    float* Y = (j + 1 == proj.size()) ? h->core : h->buf[which];
+    if (proj[j].size() == 2) {
+      const int d = h->d;
+      ModeProd2 mp{};
+      mp.X = X;
+      mp.in_dt = xdt;
+      mp.P = P;
+      uint32_t A, I, B;
+      view(cur, d, d - 2, &A, &I, &B);
+      mp.A = A;
+      mp.I1 = (uint32_t)cur[d - 2];
+      mp.I2 = (uint32_t)cur[d - 1];
+      mp.R1 = (uint32_t)h->ranks[d - 2];
+      mp.R2 = (uint32_t)h->ranks[d - 1];
+      mp.recon = 0;
+      mp.M1 = h->Mp[d - 2];
+      mp.M2 = h->Mp[d - 1];
+      mp.Y = Y;
+      {
+        Mark m(h, KID_PROJECT_FUSED2);
+        HIPCHK(h, launch_modeprod2(mp, h->num_cu, s));
+      }
+      cur[d - 2] = h->ranks[d - 2];
+      cur[d - 1] = h->ranks[d - 1];
+    } else {
+      const int n = proj[j][0];
+      ModeProd mp{};
+      mp.X = X;
+      mp.in_dt = xdt;
+      mp.M = h->Mp[n];
+      view(cur, h->d, n, &mp.A, &mp.I, &mp.B);
+      mp.R = (uint32_t)h->ranks[n];
+      mp.P = P;
+      mp.apply = 0;
+      mp.Y = Y;
+      {
+        Mark m(h, j == 0 ? KID_PROJECT_FIRST : KID_PROJECT);
+        HIPCHK(h, launch_modeprod(mp, h->num_cu, s));
+      }
+      cur[n] = h->ranks[n];
     }
-    X = mp.Y;
+    X = Y;
     xdt = DT_F32;
     which ^= 1;
-    cur[n] = h->ranks[n];
   }
   AdamK a;
   a.b1 = (float)h->b1;
@@ -480,34 +567,70 @@ int tgrad_step(tgrad_t* h, void* weight, void* grad, void* stream) {
   }
   X = h->ucore;
   which = 0;
-  for (size_t j = 0; j < nf; ++j) {
-    const int n = h->fmodes[j];
-    ModeProd mp{};
-    mp.X = X;
-    mp.in_dt = DT_F32;
-    mp.M = h->Mr[n];
-    view(cur, h->d, n, &mp.A, &mp.I, &mp.B);
-    mp.R = (uint32_t)h->shape[n];
-    mp.P = P;
-    const bool last = (j + 1 == nf);
-    mp.apply = last ? 1 : 0;
-    mp.Y = last ? nullptr : h->buf[which];
-    mp.W = weight;
-    mp.w_dt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
-    mp.mask = h->mask;
-    mp.rank = h->rank;
-    mp.uS = h->S;
-    mp.omega = h->omega;
-    mp.kS = h->k;
-    mp.lr = lr;
-    mp.has_sparse = h->k > 0;
-    {
-      Mark m(h, last ? KID_RECON_APPLY : KID_RECONSTRUCT);
-      HIPCHK(h, launch_modeprod(mp, h->num_cu, s));
+  for (size_t j = 0; j < rec.size(); ++j) {
+    const bool last = (j + 1 == rec.size());
+    float* Y = last ? nullptr : h->buf[which];
+    if (rec[j].size() == 2) {
+      const int d = h->d;
+      ModeProd2 mp{};
+      mp.X = X;
+      mp.in_dt = DT_F32;
+      mp.P = P;
+      uint32_t A, I, B;
+      view(cur, d, d - 2, &A, &I, &B);
+      mp.A = A;
+      mp.I1 = (uint32_t)cur[d - 2];
+      mp.I2 = (uint32_t)cur[d - 1];
+      mp.R1 = (uint32_t)h->shape[d - 2];
+      mp.R2 = (uint32_t)h->shape[d - 1];
+      mp.recon = 1;
+      mp.M1 = h->Mr[d - 2];
+      mp.M2 = h->Mr[d - 1];
+      mp.apply = last ? 1 : 0;
+      mp.Y = Y;
+      mp.W = weight;
+      mp.w_dt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
+      mp.mask = h->mask;
+      mp.rank = h->rank;
+      mp.uS = h->S;
+      mp.omega = h->omega;
+      mp.kS = h->k;
+      mp.lr = lr;
+      mp.has_sparse = h->k > 0;
+      {
+        Mark m(h, last ? KID_RECON_FUSED2_APPLY : KID_RECON_FUSED2);
+        HIPCHK(h, launch_modeprod2(mp, h->num_cu, s));
+      }
+      cur[d - 2] = h->shape[d - 2];
+      cur[d - 1] = h->shape[d - 1];
+    } else {
+      const int n = rec[j][0];
+      ModeProd mp{};
+      mp.X = X;
+      mp.in_dt = DT_F32;
+      mp.M = h->Mr[n];
+      view(cur, h->d, n, &mp.A, &mp.I, &mp.B);
+      mp.R = (uint32_t)h->shape[n];
+      mp.P = P;
+      mp.apply = last ? 1 : 0;
+      mp.Y = Y;
+      mp.W = weight;
+      mp.w_dt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
+      mp.mask = h->mask;
+      mp.rank = h->rank;
+      mp.uS = h->S;
+      mp.omega = h->omega;
+      mp.kS = h->k;
+      mp.lr = lr;
+      mp.has_sparse = h->k > 0;
+      {
+        Mark m(h, last ? KID_RECON_APPLY : KID_RECONSTRUCT);
+        HIPCHK(h, launch_modeprod(mp, h->num_cu, s));
+      }
+      cur[n] = h->shape[n];
     }
-    X = mp.Y;
+    X = Y;
     which ^= 1;
-    cur[n] = h->shape[n];
   }
   return TGRAD_OK;
 }
@@ -597,6 +720,13 @@ int tgrad_set_factor(tgrad_t* h, int mode, const float* U, int64_t n_floats) {
   HIPCHK(h, hipMemcpy(h->U[mode], U, n * 4, hipMemcpyHostToDevice));
   HIPCHK(h, hipMemcpy(h->Mp[mode], mp.data(), mp.size() * 4, hipMemcpyHostToDevice));
   HIPCHK(h, hipMemcpy(h->Mr[mode], mr.data(), mr.size() * 4, hipMemcpyHostToDevice));
+  return TGRAD_OK;
+}
+
+int tgrad_set_fusion(tgrad_t* h, int enable) {
+  if (!h) return TGRAD_EINVAL;
+  if (enable && !h->can_fuse) return TGRAD_EINVAL;
+  h->fuse = enable != 0;
   return TGRAD_OK;
 }
 

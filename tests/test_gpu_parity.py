@@ -133,13 +133,17 @@ STEP_CASES = FACTOR_CASES + [
 ]
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "one-mode"])
 @pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: c[0])
-def test_steps_with_pinned_omega_and_factors(case):
-    """Omega and U(n) injected from the oracle, so only the step kernels are compared."""
+def test_steps_with_pinned_omega_and_factors(case, fused):
+    """Omega and U(n) injected from the oracle, so only the step kernels are compared;
+    both launch plans (two trailing modes per launch, one mode per launch)."""
     name, wl = case
     gs = GradStream(wl, seed=8)
     W0 = init_weights(wl, seed=8)
     lib, orc = make_lib(wl, T=10 ** 6), make_oracle(wl, T=10 ** 6)
+    if not lib.set_fusion(fused):
+        pytest.skip("the two trailing modes are not both compressed")
     g1 = gs.next()
     orc.refresh(g1)
     lib.set_omega(orc.omega)
@@ -266,13 +270,17 @@ def test_timing_records_every_kernel():
     for _ in range(3):
         lib.step(W, dev(gs.next(), wl.dtype))
     rec = lib.timing_read()
-    for name in ("topk_hist", "topk_compact", "gather_residual", "modeprod_project_first",
-                 "modeprod_project", "adam_fused",
-                 "modeprod_reconstruct", "modeprod_reconstruct_apply", "gram", "eig_jacobi"):
+    for name in ("topk_hist", "topk_compact", "gather_residual", "modeprod2_project_first",
+                 "modeprod_project", "adam_fused", "modeprod_reconstruct",
+                 "modeprod2_reconstruct_apply", "gram", "eig_jacobi"):
         assert name in rec, name
     assert rec["adam_fused"][0] == 3
-    assert rec["modeprod_project_first"][0] == 3
-    assert rec["modeprod_project"][0] == 9
+    assert rec["modeprod2_project_first"][0] == 3
+    assert rec["modeprod_project"][0] == 6
+    assert lib.set_fusion(False)
+    lib.step(W, dev(gs.next(), wl.dtype))
+    rec = lib.timing_read()
+    assert rec["modeprod_project_first"][0] == 1 and rec["modeprod_reconstruct_apply"][0] == 1
 
 
 # --------------------------------------------------------------------------- full size, config 4
