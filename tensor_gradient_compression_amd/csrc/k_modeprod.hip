@@ -195,10 +195,16 @@ __global__ void __launch_bounds__(NTH) k_modeprod(MPK k) {
   // update) pairs are loaded into registers before the multiply.
   const bool merged = (EPI == 1) && k.has_sparse && !k.wide;
   constexpr int NSR = 2;                         // Omega entries per thread in registers
+  // Omega rank of element e (how many Omega entries lie below e). e is uniform over the
+  // workgroup and mask/rank are read-only here, so the words come in by scalar loads:
+  // those retire on lgkmcnt, whereas a vector load would retire on vmcnt behind the
+  // next tile's transfer and make the double buffering synchronous.
   auto rank_of = [&](uint64_t e) -> uint64_t {
     if (e >= k.N) return k.kS;
-    const uint64_t word = k.mask[e >> 6];
-    return k.rank[e >> 6] + (uint64_t)__popcll(word & ((1ull << (e & 63)) - 1ull));
+    const uint64_t w = e >> 6;
+    const uint64_t word = ((const __attribute__((address_space(4))) uint64_t*)k.mask)[w];
+    const uint32_t base = ((const __attribute__((address_space(4))) uint32_t*)k.rank)[w];
+    return base + (uint64_t)__popcll(word & ((1ull << (e & 63)) - 1ull));
   };
   uint64_t jc0 = 0, jc1 = 0, jn0 = 0, jn1 = 0;
 
@@ -219,7 +225,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod(MPK k) {
   __builtin_amdgcn_s_waitcnt(0);
   for (; tile < k.ntiles; tile += gridDim.x) {
     const uint64_t next = tile + gridDim.x;
-    __syncthreads();                 // every thread's transfers visible; buffers free
+    lds_barrier();                 // every thread's transfers visible; buffers free
     const TileGeo gc = g;
     unsigned char* bx = lds + (cur ? k.off_x1 : k.off_x0);
     unsigned char* bw = lds + (cur ? k.off_w1 : k.off_w0);
@@ -271,7 +277,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod(MPK k) {
       }
       filled = true;
     }
-    if (filled) __syncthreads();
+    if (filled) lds_barrier();
 
     f4 acc[NCB][NRB];
     uint32_t cb_in[NCB], cb_y[NCB];
@@ -325,7 +331,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod(MPK k) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (merged) {
       const uint64_t e_lo = gc.base_out / P;
 #pragma unroll
@@ -342,7 +348,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod(MPK k) {
 #pragma unroll
         for (int p = 0; p < P; ++p) sY[loc + p] = sY[loc + p] + k.uS[j * P + p];
       }
-      __syncthreads();
+      lds_barrier();
     }
 
     // this thread's transfer of the next tile has landed (it is read after the next

@@ -27,7 +27,8 @@ namespace tg {
 
 namespace {
 
-constexpr int NTH = 256;
+constexpr int NTH = 512;
+constexpr int NW = NTH / 64;   // waves per workgroup
 constexpr int NRBMAX = 8;   // up to 128 output rows per product (16 per block)
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -47,62 +48,93 @@ struct MP2K {
   uint64_t ntiles;
   uint32_t A, TA;
   uint32_t I1, I2, R1, R2;          // input and output slab sizes (elements)
-  uint32_t recon;                   // 0 projection, 1 reconstruction
+  float inv_b;                      // 1/B of the pass whose B > 1 (fp32-rounded)
   // GEMM shapes of the two passes (values, complex parts included)
   uint32_t k1, kp1, m1, mp1, k2, kp2, m2, mp2;
   uint32_t dma_in, dma_w, vout;
-  uint32_t off_m2, off_x0, off_x1, off_y, off_o, off_w0, off_w1;
+  uint32_t off_m2, off_x0, off_x1, off_y, off_o, off_w0, off_w1, off_r0, off_r1;
   float lr;
   int has_sparse;
 };
 
 // One mode product between LDS buffers over the (A', I, B, P) view: ncols = A' * B
-// GEMM columns; dst[a', jj, b] = sum_kk sM[jj, kk] src[a', kk, b]. Each wave takes
-// 16-column blocks in turn and one 16-row output block at a time. The inner loop is one
+// GEMM columns; dst[a', jj, b] = sum_kk sM[jj, kk] src[a', kk, b]. The (16-column block,
+// 16-row block) items are dealt to the waves in turn. The inner loop is one
 // A read at a fixed stride, one B read from a strength-reduced pointer and the MFMA:
-// only the last k-step can hold rows >= Kin (zeroed there), and lanes of columns past
-// ncols read a real column whose result is dropped.
-template <typename ST, int P>
-__device__ __forceinline__ void lds_gemm(const ST* src, uint32_t ncols, uint32_t B, uint32_t I,
-                                         uint32_t R, const float* sM, uint32_t Kin,
+// sM is zero past Kin, and only the last k-step can hold source rows >= Kin (zeroed
+// there). Lanes of columns past ncols read a real column whose result is dropped.
+// B1: B == 1 (columns are whole fibres). Otherwise a column splits as col = a' B + b
+// with a' = floor((col + 1/2) * invB) in fp32: with col < 2^16 and B <= 128 the
+// product is within 2^-10 of (col + 1/2) / B, whose distance to an integer is at
+// least 1/(2B), so the floor is exact.
+template <typename ST, int P, bool B1>
+__device__ __forceinline__ void lds_gemm(const ST* src, uint32_t ncols, uint32_t B, float invB,
+                                         uint32_t I, uint32_t R, const float* sM, uint32_t Kin,
                                          uint32_t Kpad, uint32_t Mout, uint32_t Mpad,
                                          float* dst) {
   const uint32_t lane = threadIdx.x & 63;
-  const uint32_t wave = threadIdx.x >> 6;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t g = lane >> 4, li = lane & 15;
   const uint32_t LDM = Kpad + 1;
-  const uint32_t rs = B * P;
-  const uint32_t blk_in = I * B * P, blk_out = R * B * P;
+  const uint32_t rs = B1 ? P : B * P;
+  const uint32_t blk_in = I * rs, blk_out = R * rs;
   const uint32_t ncb = (ncols + 15) / 16;
   const uint32_t nks = Kpad >> 2;
   // row kk = 4*ks + g of a column sits at (kk / P) * rs + kk % P
   const uint32_t goff = (P == 1) ? g * rs : (g >> 1) * rs + (g & 1);
   const uint32_t kstep = (P == 1) ? 4 * rs : 2 * rs;
   const bool last_ok = 4 * (nks - 1) + g < Kin;
-  for (uint32_t cb = wave; cb < ncb; cb += 4) {
+  // output rows r0 + 4g + v, v = 0..3, sit at (r0 + 4g) / P * rs + vo(v)
+  const uint32_t vo1 = (P == 1) ? rs : 1, vo2 = (P == 1) ? 2 * rs : rs;
+  const uint32_t vo3 = (P == 1) ? 3 * rs : rs + 1;
+  const uint32_t nrb = Mpad >> 4;
+  // item = rb * ncb + cb, this wave's first one: cb = wave mod ncb, rb = wave / ncb
+  uint32_t cb = wave, rb = 0;
+  while (cb >= ncb) {
+    cb -= ncb;
+    ++rb;
+  }
+  while (rb < nrb) {
     const uint32_t c0 = cb * 16 + li;
     const bool valid = c0 < ncols;
     const uint32_t col = valid ? c0 : ncols - 1;
-    const uint32_t ca = col / B, cbb = col - ca * B;
-    const ST* bp = src + ca * blk_in + cbb * P + goff;
-    const uint32_t cout = ca * blk_out + cbb * P;
-    for (uint32_t r0 = 0; r0 < Mpad; r0 += 16) {
-      const float* ap = sM + (r0 + li) * LDM + g;
-      f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-      const ST* b = bp;
-      for (uint32_t ks = 0; ks + 1 < nks; ++ks) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ap[4 * ks], to_f32(*b), acc, 0, 0, 0);
-        b += kstep;
-      }
-      const float bl = last_ok ? to_f32(*b) : 0.0f;
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ap[4 * (nks - 1)], bl, acc, 0, 0, 0);
+    uint32_t ca, cbb;
+    if (B1) {
+      ca = col;
+      cbb = 0;
+    } else {
+      ca = (uint32_t)(((float)col + 0.5f) * invB);
+      cbb = col - ca * B;
+    }
+    const uint32_t r0 = rb * 16;
+    const ST* b = src + ca * blk_in + cbb * P + goff;
+    const float* ap = sM + (r0 + li) * LDM + g;
+    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+    for (uint32_t ks = 0; ks + 1 < nks; ++ks) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ap[4 * ks], to_f32(*b), acc, 0, 0, 0);
+      b += kstep;
+    }
+    const float bl = last_ok ? to_f32(*b) : 0.0f;
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ap[4 * (nks - 1)], bl, acc, 0, 0, 0);
+    float* d = dst + ca * blk_out + cbb * P + ((r0 + 4 * g) / P) * rs;
+    if (r0 + 16 <= Mout) {
       if (valid) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint32_t jj = r0 + 4 * g + v;
-          if (jj < Mout) dst[cout + (jj / P) * rs + (jj % P)] = acc[v];
-        }
+        d[0] = acc[0];
+        d[vo1] = acc[1];
+        d[vo2] = acc[2];
+        d[vo3] = acc[3];
       }
+    } else if (valid) {
+      const uint32_t j0 = r0 + 4 * g;
+      if (j0 < Mout) d[0] = acc[0];
+      if (j0 + 1 < Mout) d[vo1] = acc[1];
+      if (j0 + 2 < Mout) d[vo2] = acc[2];
+      if (j0 + 3 < Mout) d[vo3] = acc[3];
+    }
+    cb += NW;
+    while (cb >= ncb) {
+      cb -= ncb;
+      ++rb;
     }
   }
 }
@@ -121,7 +153,7 @@ __device__ __forceinline__ void dma_block(const T* src, uint32_t nvals, unsigned
   }
 }
 
-template <typename XT, int P, int EPI, typename WT>
+template <typename XT, int P, int REC, int EPI, typename WT>
 __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
   constexpr int VO = (EPI == 0) ? 4 : 16 / (int)sizeof(WT);
   extern __shared__ float smem[];
@@ -145,12 +177,12 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
   const uint32_t slab_in = k.I1 * k.I2 * P, slab_out = k.R1 * k.R2 * P;
   // projection: pass 1 is mode d (M = M2), pass 2 mode d-1 (M = M1);
   // reconstruction: pass 1 is mode d-1 (M = M1), pass 2 mode d (M = M2).
-  const float* sA = k.recon ? sM1 : sM2;
-  const float* sB = k.recon ? sM2 : sM1;
-  const uint32_t ka = k.recon ? k.k1 : k.k2, kpa = k.recon ? k.kp1 : k.kp2;
-  const uint32_t ma = k.recon ? k.m1 : k.m2, mpa = k.recon ? k.mp1 : k.mp2;
-  const uint32_t kb = k.recon ? k.k2 : k.k1, kpb = k.recon ? k.kp2 : k.kp1;
-  const uint32_t mb = k.recon ? k.m2 : k.m1, mpb = k.recon ? k.mp2 : k.mp1;
+  const float* sA = REC ? sM1 : sM2;
+  const float* sB = REC ? sM2 : sM1;
+  const uint32_t ka = REC ? k.k1 : k.k2, kpa = REC ? k.kp1 : k.kp2;
+  const uint32_t ma = REC ? k.m1 : k.m2, mpa = REC ? k.mp1 : k.mp2;
+  const uint32_t kb = REC ? k.k2 : k.k1, kpb = REC ? k.kp2 : k.kp1;
+  const uint32_t mb = REC ? k.m2 : k.m1, mpb = REC ? k.mp2 : k.mp1;
 
   auto can_dma_in = [&](uint32_t nta) { return k.dma_in && (nta * slab_in * sizeof(XT)) % 16 == 0; };
   auto can_dma_w = [&](uint32_t nta) {
@@ -169,40 +201,57 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
       dma_block<WT>((const WT*)k.W + a0 * slab_out, nta * slab_out,
                     lds + (buf ? k.off_w1 : k.off_w0));
   };
-  auto rank_of = [&](uint64_t e) -> uint64_t {
+  // The tile's Omega entries are the contiguous range [rank(e_lo), rank(e_hi)) of the
+  // sorted list, rank(e) = rank[e / 64] + popcount(mask[e / 64] below bit e % 64). The
+  // two boundary words and ranks travel with the tile's transfer: lanes 0-5 of wave 0
+  // bring mask[lo] (2 dwords), rank[lo], mask[hi] (2 dwords), rank[hi] into a 24-byte
+  // LDS slot of the same buffer, read after the barrier that publishes the tile.
+  auto tile_lo = [&](uint64_t tile) -> uint64_t { return tile * k.TA * slab_out / P; };
+  auto tile_hi = [&](uint64_t tile) -> uint64_t {
+    return (tile * k.TA + nta_of(tile)) * slab_out / P;
+  };
+  auto issue_rank = [&](uint64_t tile, int buf) {
+    if (tid < 6) {
+      const uint64_t e = tid < 3 ? tile_lo(tile) : tile_hi(tile);
+      const uint32_t part = tid % 3;
+      const uint64_t w = e < k.N ? e >> 6 : 0;
+      const void* src = part < 2 ? (const void*)((const uint32_t*)(k.mask + w) + part)
+                                 : (const void*)(k.rank + w);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + (buf ? k.off_r1 : k.off_r0)), 4,
+                                       0, 0);
+    }
+  };
+  auto rank_from = [&](const uint32_t* r, uint64_t e) -> uint64_t {
     if (e >= k.N) return k.kS;
-    const uint64_t word = k.mask[e >> 6];
-    return k.rank[e >> 6] + (uint64_t)__popcll(word & ((1ull << (e & 63)) - 1ull));
+    const uint64_t word = (uint64_t)r[0] | ((uint64_t)r[1] << 32);
+    return r[2] + (uint64_t)__popcll(word & ((1ull << (e & 63)) - 1ull));
   };
   const bool merged = (EPI == 1) && k.has_sparse;
   constexpr int NSR = 2;
-  uint64_t jc0 = 0, jc1 = 0, jn0 = 0, jn1 = 0;
+  uint64_t jc0 = 0, jc1 = 0;
 
   uint64_t tile = blockIdx.x;
   int cur = 0;
   if (tile < k.ntiles) {
     issue(tile, cur);
-    if (merged) {
-      const uint64_t a0 = tile * k.TA;
-      jc0 = rank_of(a0 * slab_out / P);
-      jc1 = rank_of((a0 + nta_of(tile)) * slab_out / P);
-    }
+    if (merged) issue_rank(tile, cur);
   }
   __builtin_amdgcn_s_waitcnt(0);
   for (; tile < k.ntiles; tile += gridDim.x) {
     const uint64_t next = tile + gridDim.x;
-    __syncthreads();
+    lds_barrier();
     const uint32_t nta = nta_of(tile);
     const uint64_t a0 = tile * k.TA;
     unsigned char* bx = lds + (cur ? k.off_x1 : k.off_x0);
     unsigned char* bw = lds + (cur ? k.off_w1 : k.off_w0);
+    if (merged) {
+      const uint32_t* r = (const uint32_t*)(lds + (cur ? k.off_r1 : k.off_r0));
+      jc0 = rank_from(r, tile_lo(tile));
+      jc1 = rank_from(r + 3, tile_hi(tile));
+    }
     if (next < k.ntiles) {
       issue(next, cur ^ 1);
-      if (merged) {
-        const uint64_t an = next * k.TA;
-        jn0 = rank_of(an * slab_out / P);
-        jn1 = rank_of((an + nta_of(next)) * slab_out / P);
-      }
+      if (merged) issue_rank(next, cur ^ 1);
     }
     uint32_t om_r[NSR];
     float us_r[NSR][P];
@@ -229,22 +278,26 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
       for (uint32_t idx = tid; idx < nta * slab_out; idx += NTH) d[idx] = W[a0 * slab_out + idx];
       filled = true;
     }
-    if (filled) __syncthreads();
+    if (filled) lds_barrier();
 
-    if (!k.recon) {
+    if (!REC) {
       // mode d: (A' = nta*I1, I = I2, B = 1) -> (nta*I1, R2, 1)
-      lds_gemm<XT, P>((const XT*)bx, nta * k.I1, 1, k.I2, k.R2, sA, ka, kpa, ma, mpa, sYm);
-      __syncthreads();
+      lds_gemm<XT, P, true>((const XT*)bx, nta * k.I1, 1, 1.0f, k.I2, k.R2, sA, ka, kpa, ma,
+                            mpa, sYm);
+      lds_barrier();
       // mode d-1: (A' = nta, I = I1, B = R2) -> (nta, R1, R2)
-      lds_gemm<float, P>(sYm, nta * k.R2, k.R2, k.I1, k.R1, sB, kb, kpb, mb, mpb, sO);
+      lds_gemm<float, P, false>(sYm, nta * k.R2, k.R2, k.inv_b, k.I1, k.R1, sB, kb, kpb, mb,
+                                mpb, sO);
     } else {
       // mode d-1: (A' = nta, I = I1, B = I2) -> (nta, R1, I2)
-      lds_gemm<XT, P>((const XT*)bx, nta * k.I2, k.I2, k.I1, k.R1, sA, ka, kpa, ma, mpa, sYm);
-      __syncthreads();
+      lds_gemm<XT, P, false>((const XT*)bx, nta * k.I2, k.I2, k.inv_b, k.I1, k.R1, sA, ka, kpa,
+                             ma, mpa, sYm);
+      lds_barrier();
       // mode d: (A' = nta*R1, I = I2, B = 1) -> (nta*R1, R2, 1)
-      lds_gemm<float, P>(sYm, nta * k.R1, 1, k.I2, k.R2, sB, kb, kpb, mb, mpb, sO);
+      lds_gemm<float, P, true>(sYm, nta * k.R1, 1, 1.0f, k.I2, k.R2, sB, kb, kpb, mb, mpb,
+                               sO);
     }
-    __syncthreads();
+    lds_barrier();
     if (merged) {
       const uint64_t e_lo = a0 * slab_out / P;
 #pragma unroll
@@ -261,7 +314,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
 #pragma unroll
         for (int p = 0; p < P; ++p) sO[loc + p] = sO[loc + p] + k.uS[j * P + p];
       }
-      __syncthreads();
+      lds_barrier();
     }
     __builtin_amdgcn_s_waitcnt(0);   // next tile's transfer landed; previous stores done
 
@@ -298,8 +351,6 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
       }
     }
     cur ^= 1;
-    jc0 = jn0;
-    jc1 = jn1;
   }
   __builtin_amdgcn_s_waitcnt(0);
 }
@@ -320,13 +371,16 @@ Geo2 plan(const ModeProd2& mp, uint32_t TA) {
   k.I2 = mp.I2;
   k.R1 = mp.R1;
   k.R2 = mp.R2;
-  k.recon = mp.recon;
+  k.inv_b = 1.0f / (float)(mp.recon ? mp.I2 : mp.R2);
   // pass shapes: M1 is (R1*P) x (I1*P), M2 is (R2*P) x (I2*P)
   k.k1 = mp.I1 * P; k.m1 = mp.R1 * P;
   k.k2 = mp.I2 * P; k.m2 = mp.R2 * P;
   k.kp1 = (k.k1 + 3) & ~3u; k.mp1 = (k.m1 + 15) & ~15u;
   k.kp2 = (k.k2 + 3) & ~3u; k.mp2 = (k.m2 + 15) & ~15u;
   g.ok = k.mp1 <= 16 * NRBMAX && k.mp2 <= 16 * NRBMAX && k.kp1 <= 128 && k.kp2 <= 128;
+  // the fp32 column split in lds_gemm needs ncols < 2^16 and B <= 128
+  const uint32_t dmax = std::max(std::max(mp.I1, mp.I2), std::max(mp.R1, mp.R2));
+  g.ok = g.ok && dmax <= 128 && (uint64_t)TA * dmax * dmax < 65536;
   k.A = mp.A;
   k.TA = TA;
   k.ntiles = ((uint64_t)mp.A + TA - 1) / TA;
@@ -343,6 +397,8 @@ Geo2 plan(const ModeProd2& mp, uint32_t TA) {
   k.off_o = (uint32_t)off; off += al(TA * slab_out * 4);
   k.off_w0 = (uint32_t)off; off += mp.apply ? al(TA * slab_out * esw) : 0;
   k.off_w1 = (uint32_t)off; off += mp.apply ? al(TA * slab_out * esw) : 0;
+  k.off_r0 = (uint32_t)off; off += mp.apply ? 32 : 0;
+  k.off_r1 = (uint32_t)off; off += mp.apply ? 32 : 0;
   g.lds = off;
   const auto a16 = [](const void* p) { return ((uintptr_t)p) % 16 == 0; };
   k.dma_in = a16(mp.X) && (TA * slab_in * esx) % 16 == 0;
@@ -351,9 +407,9 @@ Geo2 plan(const ModeProd2& mp, uint32_t TA) {
   return g;
 }
 
-template <typename XT, int P, int EPI, typename WT>
+template <typename XT, int P, int REC, int EPI, typename WT>
 hipError_t go2(const MP2K& k, size_t lds, unsigned grid, hipStream_t s) {
-  auto fn = k_modeprod2<XT, P, EPI, WT>;
+  auto fn = k_modeprod2<XT, P, REC, EPI, WT>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)fn,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -366,14 +422,15 @@ hipError_t go2(const MP2K& k, size_t lds, unsigned grid, hipStream_t s) {
 }  // namespace
 
 // MFMA k-steps the busiest wave spends on one pass of a tile, as lds_gemm splits it:
-// 16-column blocks dealt round-robin to the 4 waves, each running every 16-row block.
+// (16-column block, 16-row block) items dealt round-robin to the NW waves.
 static uint64_t pass_steps(uint64_t ncols, uint32_t kpad, uint32_t mpad) {
-  const uint64_t ncb = (ncols + 15) / 16;
-  return ((ncb + 3) / 4) * (mpad / 16) * (kpad / 4);
+  const uint64_t items = (ncols + 15) / 16 * (mpad / 16);
+  return (items + NW - 1) / NW * (kpad / 4);
 }
 
 // Tile (whole slabs) with LDS <= 52 KB (three or more workgroups per CU) that minimises
-// the busiest wave's MFMA k-steps per slab over both passes (larger tile on ties); 0
+// the busiest wave's MFMA k-steps per slab over both passes plus a per-tile fixed cost
+// (larger tile on ties); 0
 // when not even one slab fits (or a product is too large): the caller then uses two
 // one-mode launches.
 uint32_t modeprod2_tile(const ModeProd2& mp) {
@@ -388,7 +445,9 @@ uint32_t modeprod2_tile(const ModeProd2& mp) {
                        pass_steps((uint64_t)TA * mp.R1, k.kp2, k.mp2)
                  : pass_steps((uint64_t)TA * mp.I1, k.kp2, k.mp2) +
                        pass_steps((uint64_t)TA * mp.R2, k.kp1, k.mp1);
-    const double cost = (double)steps / TA;
+    // + 16: a tile's fixed work (barriers, transfer issue, stream-out) costs about as
+    // much as 16 k-steps on this GEMM shape class (measured on bf16 48x25 -> 24x13)
+    const double cost = (double)(steps + 16) / TA;
     if (!best || cost <= best_cost) {
       best = TA;
       best_cost = cost;
@@ -423,20 +482,24 @@ hipError_t launch_modeprod2(const ModeProd2& mp, int num_cu, hipStream_t s) {
   if (grid > k.ntiles) grid = k.ntiles;
   if (grid < 1) grid = 1;
   const unsigned gr = (unsigned)grid;
-  if (!mp.apply) {
-    if (mp.P == 2) return go2<float, 2, 0, float>(k, g.lds, gr, s);
+  if (!mp.recon) {
+    if (mp.P == 2) return go2<float, 2, 0, 0, float>(k, g.lds, gr, s);
     switch (mp.in_dt) {
-      case DT_F32: return go2<float, 1, 0, float>(k, g.lds, gr, s);
-      case DT_F16: return go2<_Float16, 1, 0, float>(k, g.lds, gr, s);
-      case DT_BF16: return go2<bf16_t, 1, 0, float>(k, g.lds, gr, s);
+      case DT_F32: return go2<float, 1, 0, 0, float>(k, g.lds, gr, s);
+      case DT_F16: return go2<_Float16, 1, 0, 0, float>(k, g.lds, gr, s);
+      case DT_BF16: return go2<bf16_t, 1, 0, 0, float>(k, g.lds, gr, s);
     }
     return hipErrorInvalidValue;
   }
-  if (mp.P == 2) return go2<float, 2, 1, float>(k, g.lds, gr, s);
+  if (mp.in_dt != DT_F32) return hipErrorInvalidValue;
+  if (!mp.apply)
+    return mp.P == 2 ? go2<float, 2, 1, 0, float>(k, g.lds, gr, s)
+                     : go2<float, 1, 1, 0, float>(k, g.lds, gr, s);
+  if (mp.P == 2) return go2<float, 2, 1, 1, float>(k, g.lds, gr, s);
   switch (mp.w_dt) {
-    case DT_F32: return go2<float, 1, 1, float>(k, g.lds, gr, s);
-    case DT_F16: return go2<float, 1, 1, _Float16>(k, g.lds, gr, s);
-    case DT_BF16: return go2<float, 1, 1, bf16_t>(k, g.lds, gr, s);
+    case DT_F32: return go2<float, 1, 1, 1, float>(k, g.lds, gr, s);
+    case DT_F16: return go2<float, 1, 1, 1, _Float16>(k, g.lds, gr, s);
+    case DT_BF16: return go2<float, 1, 1, 1, bf16_t>(k, g.lds, gr, s);
   }
   return hipErrorInvalidValue;
 }

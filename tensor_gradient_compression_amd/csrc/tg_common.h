@@ -29,6 +29,19 @@ template <> __device__ __forceinline__ float zero_of<float>() { return 0.0f; }
 template <> __device__ __forceinline__ _Float16 zero_of<_Float16>() { return (_Float16)0.0f; }
 template <> __device__ __forceinline__ bf16_t zero_of<bf16_t>() { bf16_t z; z.b = 0; return z; }
 
+// Workgroup barrier that orders LDS traffic only: waits for this wave's LDS operations
+// (lgkmcnt) and not for its global loads, stores or global->LDS transfers (vmcnt), which
+// __syncthreads() would also wait for. Kernels that double-buffer with global_load_lds
+// publish a transfer with an explicit s_waitcnt before the barrier that precedes its
+// first read. The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 // Position of element e in Omega given the membership bitmask and per-word ranks.
 __device__ __forceinline__ uint32_t omega_rank(const uint64_t* mask, const uint32_t* rank,
                                                uint64_t e, uint64_t word) {
