@@ -16,6 +16,8 @@
 // 64-term sums in fp32, and every tile result is added to fp64 accumulators. Each
 // workgroup writes its fp64 partial; a second kernel sums the partials in a fixed
 // order, so the result is deterministic run to run.
+#include <algorithm>
+
 #include "tg_common.h"
 
 namespace tg {
@@ -222,11 +224,403 @@ hipError_t pick_nob(const GK& k, size_t lds, unsigned grid, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------- 16-bit real data
+// bf16 and fp16 products are exact in fp32, so for these the Gram runs on the
+// 16x16x32 MFMAs (v_mfma_f32_16x16x32_bf16 / _f16): lane l supplies row l % 16 of a
+// 16-row block at the 8 consecutive k = 8 (l / 16) .. + 7, as both the A and the B
+// operand, and block (rb, cb) of the Gram is mfma(fragment rb, fragment cb). Only the
+// blocks with rb <= cb are formed; the partial is written symmetric.
+//
+// Tiles move HBM -> LDS with 16-byte global_load_lds transfers, double buffered, in
+// a persistent grid (tile = blockIdx.x, + gridDim.x, ...). Two tile forms:
+//   wide   (B % 8 == 0, B >= 32): one a, 128 consecutive b, all I rows. The K index is
+//          b. Row r's 16-byte chunk c sits at LDS chunk r * 16 + (c ^ (r % 16)), so the
+//          transfer stays contiguous in LDS (each lane fetches the chunk that belongs
+//          in its slot) and the 16 rows a fragment read touches fall in distinct banks.
+//   narrow (I * B small): TA whole slabs, contiguous. K runs over (a, b), element
+//          offset a * I * B + r * B + b; fragments are read 16 bits at a time.
+// Each wave sums 8 k-steps in fp32 (at most 256 exact products per sum) before adding
+// into fp64; at the end the waves' fp64 sums are combined in wave order, so results are
+// deterministic run to run.
+constexpr int G16_NTH = 256;
+constexpr uint32_t G16_TB = 128;           // wide tiles: columns (b) per tile
+constexpr uint32_t G16_NARROW = 16384;     // narrow tiles: at most this many elements
+constexpr uint32_t G16_FLUSH = 8;          // k-steps per fp32 partial sum
+constexpr int G16_WGS_PER_CU = 3;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+struct G16K {
+  const uint16_t* X;
+  double* partial;
+  uint64_t ntiles;
+  uint32_t A, I, B;
+  uint32_t wide;
+  uint32_t tiles_per_a;   // wide
+  uint32_t TA;            // narrow: slabs per tile
+  uint32_t buf_bytes;     // one LDS tile buffer (multiple of 16)
+  float invB;             // narrow: 1/B rounded to fp32
+};
+
+template <bool BF>
+__device__ __forceinline__ f4 mfma32(const u16x8& a, const u16x8& b, const f4& c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Upper-triangle block q (row-major: (0,0), (0,1), ..., (1,1), ...) of an NB x NB grid.
+__host__ __device__ constexpr int blk_rb(int NB, int q) {
+  int rb = 0;
+  while (q >= NB - rb) {
+    q -= NB - rb;
+    ++rb;
+  }
+  return rb;
+}
+__host__ __device__ constexpr int blk_cb(int NB, int q) {
+  int rb = 0;
+  while (q >= NB - rb) {
+    q -= NB - rb;
+    ++rb;
+  }
+  return rb + q;
+}
+
+// Work split of the four waves: with at most 3 blocks (NB <= 2) every wave forms all
+// blocks over every fourth k-step; otherwise wave W forms blocks W, W + 4, ... (at most
+// 3) over every k-step. Either way a wave holds at most 3 fp32 and 3 fp64 block sums.
+template <int NB>
+struct G16Split {
+  static constexpr int NBLK = NB * (NB + 1) / 2;
+  static constexpr bool KSPLIT = NB <= 2;
+  static constexpr int MAXB = KSPLIT ? NBLK : (NBLK + 3) / 4;
+  __host__ __device__ static constexpr int count(int W) {
+    return KSPLIT ? NBLK : (NBLK > W ? (NBLK - W + 3) / 4 : 0);
+  }
+  __host__ __device__ static constexpr int q(int W, int m) { return KSPLIT ? m : W + 4 * m; }
+};
+
+template <int NB>
+__host__ __device__ constexpr bool row_used(int W, int rb) {
+  using S = G16Split<NB>;
+  for (int m = 0; m < S::count(W); ++m)
+    if (blk_rb(NB, S::q(W, m)) == rb || blk_cb(NB, S::q(W, m)) == rb) return true;
+  return false;
+}
+
+// One k-step of wave W: read the fragments its blocks use, then one MFMA per block.
+// Template recursion keeps every block and fragment index a compile-time constant.
+template <int NB, int W, int RB, class LD>
+__device__ __forceinline__ void g16_load(u16x8* fr, LD& ld) {
+  if constexpr (RB < NB) {
+    if constexpr (row_used<NB>(W, RB)) fr[RB] = ld(RB);
+    g16_load<NB, W, RB + 1>(fr, ld);
+  }
+}
+template <bool BF, int NB, int W, int M>
+__device__ __forceinline__ void g16_mfma(f4* acc, const u16x8* fr) {
+  if constexpr (M < G16Split<NB>::count(W)) {
+    constexpr int qq = G16Split<NB>::q(W, M);
+    constexpr int rb = blk_rb(NB, qq), cb = blk_cb(NB, qq);
+    acc[M] = mfma32<BF>(fr[rb], fr[cb], acc[M]);
+    g16_mfma<BF, NB, W, M + 1>(acc, fr);
+  }
+}
+template <bool BF, int NB, int W, class LD>
+__device__ __forceinline__ void g16_step(f4* acc, LD&& ld) {
+  u16x8 fr[NB];
+  g16_load<NB, W, 0>(fr, ld);
+  g16_mfma<BF, NB, W, 0>(acc, fr);
+}
+
+template <bool BF, int NB>
+__global__ void __launch_bounds__(G16_NTH) k_gram16(G16K k) {
+  extern __shared__ uint4 smem16[];
+  unsigned char* lds = (unsigned char*)smem16;
+  using S = G16Split<NB>;
+  constexpr int NBLK = S::NBLK, MAXB = S::MAXB;
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t li = lane & 15, kg = lane >> 4;
+  const uint32_t IB = k.I * k.B;
+  const uint32_t st0 = S::KSPLIT ? wave : 0, dst_ = S::KSPLIT ? 4 : 1;
+
+  f4 acc[MAXB];
+  double dacc[MAXB][4];
+#pragma unroll
+  for (int m = 0; m < MAXB; ++m) {
+    acc[m] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) dacc[m][v] = 0.0;
+  }
+  auto flush = [&]() {
+#pragma unroll
+    for (int m = 0; m < MAXB; ++m) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dacc[m][v] += (double)acc[m][v];
+      acc[m] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto step = [&](auto&& ld) {
+    if (S::KSPLIT) {
+      g16_step<BF, NB, 0>(acc, ld);
+    } else {
+      switch (wave) {
+        case 0: g16_step<BF, NB, 0>(acc, ld); break;
+        case 1: g16_step<BF, NB, 1>(acc, ld); break;
+        case 2: g16_step<BF, NB, 2>(acc, ld); break;
+        default: g16_step<BF, NB, 3>(acc, ld); break;
+      }
+    }
+  };
+
+  auto issue = [&](uint64_t tile, int buf) {
+    unsigned char* dst = lds + (size_t)buf * k.buf_bytes;
+    if (k.wide) {
+      const uint64_t a = tile / k.tiles_per_a;
+      const uint32_t b0 = (uint32_t)(tile - a * k.tiles_per_a) * G16_TB;
+      const uint32_t lenc = (k.B - b0 < G16_TB ? k.B - b0 : G16_TB) / 8;
+      const uint32_t nchunk = k.I * (G16_TB / 8);
+      for (uint32_t q0 = wave * 64; q0 < nchunk; q0 += G16_NTH) {
+        const uint32_t p = q0 + lane;
+        const uint32_t r = p >> 4, c = (p & 15) ^ (r & 15);
+        if (p < nchunk && c < lenc)
+          __builtin_amdgcn_global_load_lds(
+              (const void*)(k.X + ((a * k.I + r) * k.B + b0 + c * 8)),
+              (lds_void_t*)(dst + (size_t)q0 * 16), 16, 0, 0);
+      }
+    } else {
+      const uint64_t a0 = tile * k.TA;
+      const uint32_t nta = (uint64_t)k.A - a0 < k.TA ? (uint32_t)((uint64_t)k.A - a0) : k.TA;
+      const uint32_t len = nta * IB;
+      const uint32_t n16 = len / 8;
+      const uint16_t* src = k.X + a0 * IB;
+      for (uint32_t q0 = wave * 64; q0 < n16; q0 += G16_NTH) {
+        if (q0 + lane < n16)
+          __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)(q0 + lane) * 8),
+                                           (lds_void_t*)(dst + (size_t)q0 * 16), 16, 0, 0);
+      }
+      // the last tile may end inside a 16-byte piece
+      if (tid < len - n16 * 8) ((uint16_t*)dst)[n16 * 8 + tid] = src[n16 * 8 + tid];
+    }
+  };
+
+  uint32_t since = 0;
+  uint64_t tile = blockIdx.x;
+  int cur = 0;
+  if (tile < k.ntiles) issue(tile, cur);
+  __builtin_amdgcn_s_waitcnt(0);
+  for (; tile < k.ntiles; tile += gridDim.x) {
+    const uint64_t next = tile + gridDim.x;
+    lds_barrier();                  // tile `cur` landed everywhere; `cur ^ 1` free
+    if (next < k.ntiles) issue(next, cur ^ 1);
+    const unsigned char* buf = lds + (size_t)cur * k.buf_bytes;
+    if (k.wide) {
+      const uint64_t a = tile / k.tiles_per_a;
+      const uint32_t b0 = (uint32_t)(tile - a * k.tiles_per_a) * G16_TB;
+      const uint32_t lenc = (k.B - b0 < G16_TB ? k.B - b0 : G16_TB) / 8;
+      const uint32_t nsteps = (lenc + 3) / 4;
+      for (uint32_t st = st0; st < nsteps; st += dst_) {
+        const uint32_t c = st * 4 + kg;
+        const bool cok = c < lenc;
+        const uint32_t cc = cok ? c : 0;
+        step([&](int rb) -> u16x8 {
+          // rows >= I only reach Gram entries that are dropped: read row I - 1 instead
+          const uint32_t r = rb * 16 + li < k.I ? rb * 16 + li : k.I - 1;
+          const u16x8 f = *(const u16x8*)(buf + (size_t)(r * 16 + (cc ^ (r & 15))) * 16);
+          return cok ? f : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        });
+        if (++since == G16_FLUSH) {
+          flush();
+          since = 0;
+        }
+      }
+    } else {
+      const uint64_t a0 = tile * k.TA;
+      const uint32_t nta = (uint64_t)k.A - a0 < k.TA ? (uint32_t)((uint64_t)k.A - a0) : k.TA;
+      const uint32_t K = nta * k.B;
+      const uint32_t nsteps = (K + 31) / 32;
+      const uint16_t* b16 = (const uint16_t*)buf;
+      for (uint32_t st = st0; st < nsteps; st += dst_) {
+        const uint32_t kk0 = st * 32 + kg * 8;
+        uint32_t off[8];
+        bool ok[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t kk = kk0 + j;
+          ok[j] = kk < K;
+          // a = floor(kk / B): exact in fp32 for kk < 2^22 (error 2^-23 kk / B < 1 / (2B))
+          const uint32_t a = (uint32_t)(((float)kk + 0.5f) * k.invB);
+          off[j] = a * (IB - k.B) + kk;
+        }
+        step([&](int rb) -> u16x8 {
+          // rows >= I only reach Gram entries that are dropped: read row I - 1 instead;
+          // k past the tile reads row start and is zeroed, so every read is in bounds
+          const uint32_t r = rb * 16 + li < k.I ? rb * 16 + li : k.I - 1;
+          const uint32_t ro = r * k.B;
+          u16x8 f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint16_t x = b16[ok[j] ? off[j] + ro : ro];
+            f[j] = ok[j] ? x : (uint16_t)0;
+          }
+          return f;
+        });
+        if (++since == G16_FLUSH) {
+          flush();
+          since = 0;
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's part of the next tile landed
+    cur ^= 1;
+  }
+  flush();
+
+  // block sums to LDS (k-split: added in wave order), then the symmetric partial
+  double* red = (double*)lds;
+  lds_barrier();
+  if (S::KSPLIT) {
+    for (uint32_t w = 0; w < 4; ++w) {
+      if (wave == w) {
+#pragma unroll
+        for (int m = 0; m < MAXB; ++m)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const uint32_t idx = (m * 4 + v) * 64 + lane;
+            red[idx] = (w == 0 ? 0.0 : red[idx]) + dacc[m][v];
+          }
+      }
+      lds_barrier();
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < MAXB; ++m) {
+      const uint32_t q = wave + 4 * m;
+      if (q < (uint32_t)NBLK) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[(q * 4 + v) * 64 + lane] = dacc[m][v];
+      }
+    }
+    lds_barrier();
+  }
+  double* out = k.partial + (uint64_t)blockIdx.x * k.I * k.I;
+  for (int q = 0; q < NBLK; ++q) {
+    if (wave != (uint32_t)(q & 3)) continue;
+    const int rb = blk_rb(NB, q), cb = blk_cb(NB, q);
+    const uint32_t col = cb * 16 + li;
+    for (int v = 0; v < 4; ++v) {
+      const uint32_t row = rb * 16 + 4 * kg + v;
+      if (row < k.I && col < k.I) {
+        const double x = red[(q * 4 + v) * 64 + lane];
+        out[(size_t)row * k.I + col] = x;
+        if (rb != cb) out[(size_t)col * k.I + row] = x;
+      }
+    }
+  }
+}
+
+struct G16Geo {
+  bool ok;
+  G16K k;
+  size_t lds;
+  uint32_t grid;
+};
+
+G16Geo g16geo(const GramArgs& g, int num_cu) {
+  G16Geo r{};
+  r.ok = false;
+  if (g.P != 1 || (g.dt != DT_BF16 && g.dt != DT_F16) || g.I > 64 || g.I == 0) return r;
+  if (((uintptr_t)g.X) % 16 != 0 || g.mask) return r;
+  G16K& k = r.k;
+  k.X = (const uint16_t*)g.X;
+  k.A = g.A;
+  k.I = g.I;
+  k.B = g.B;
+  const uint64_t IB = (uint64_t)g.I * g.B;
+  if (g.B >= 32 && g.B % 8 == 0) {
+    k.wide = 1;
+    k.tiles_per_a = (g.B + G16_TB - 1) / G16_TB;
+    k.ntiles = (uint64_t)g.A * k.tiles_per_a;
+    k.buf_bytes = g.I * G16_TB * 2;
+  } else {
+    if (IB > G16_NARROW) return r;
+    // tiles start on 16-byte boundaries: TA * I * B a multiple of 8
+    uint32_t TA = (uint32_t)(G16_NARROW / IB);
+    uint32_t step = 8;
+    for (uint32_t t = 1; t <= 8; t <<= 1)
+      if ((IB * t) % 8 == 0) {
+        step = t;
+        break;
+      }
+    TA -= TA % step;
+    if (TA == 0) return r;
+    if ((uint64_t)TA > g.A) TA = g.A;   // a single tile; its start is the buffer start
+    k.wide = 0;
+    k.TA = TA;
+    k.ntiles = ((uint64_t)g.A + TA - 1) / TA;
+    k.buf_bytes = (uint32_t)((TA * IB * 2 + 15) & ~15ull);
+    k.invB = 1.0f / (float)g.B;
+  }
+  const uint32_t nb = (g.I + 15) / 16;
+  const size_t red = (size_t)nb * (nb + 1) / 2 * 4 * 64 * sizeof(double);   // block sums
+  r.lds = std::max((size_t)2 * k.buf_bytes, red);
+  uint64_t grid = (uint64_t)(num_cu > 0 ? num_cu : 256) * G16_WGS_PER_CU;
+  if (grid > k.ntiles) grid = k.ntiles;
+  if (grid < 1) grid = 1;
+  r.grid = (uint32_t)grid;
+  r.ok = true;
+  return r;
+}
+
+template <bool BF, int NB>
+hipError_t go16(const G16Geo& g, hipStream_t s) {
+  auto fn = k_gram16<BF, NB>;
+  if (g.lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)fn,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)g.lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(fn, dim3(g.grid), dim3(G16_NTH), g.lds, s, g.k);
+  return hipGetLastError();
+}
+
+template <bool BF>
+hipError_t pick16(const G16Geo& g, hipStream_t s) {
+  switch ((g.k.I + 15) / 16) {
+    case 1: return go16<BF, 1>(g, s);
+    case 2: return go16<BF, 2>(g, s);
+    case 3: return go16<BF, 3>(g, s);
+    case 4: return go16<BF, 4>(g, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+// Sum nblk partials of n2 values (stored after them: RGROUPS stage rows) into out.
+static hipError_t reduce_partials(double* partial, uint32_t nblk, uint32_t n2, double* out,
+                           hipStream_t s, void (*mark)(void*, int, bool), void* mctx) {
+  double* stage = partial + (uint64_t)nblk * n2;
+  if (mark) mark(mctx, KID_GRAM_REDUCE, true);
+  k_gram_reduce1<<<dim3((n2 + 255) / 256, RGROUPS), 256, 0, s>>>(partial, nblk, n2, stage);
+  k_gram_reduce2<<<(n2 + 255) / 256, 256, 0, s>>>(stage, n2, out);
+  if (mark) mark(mctx, KID_GRAM_REDUCE, false);
+  return hipGetLastError();
+}
 
 uint32_t gram_reduce_groups() { return RGROUPS; }
 
 uint32_t gram_blocks(const GramArgs& g, int num_cu) {
+  const G16Geo f = g16geo(g, num_cu);
+  if (f.ok) return f.grid;
   const GGeo r = ggeo(g);
   uint64_t nb = (uint64_t)(num_cu > 0 ? num_cu : 256) * 4;
   if (nb > r.ntiles) nb = r.ntiles;
@@ -243,6 +637,16 @@ hipError_t launch_gram(const GramArgs& g, int num_cu, hipStream_t s,
   const GGeo r = ggeo(g);
   if (r.Kin > 128) return hipErrorInvalidValue;
   const uint32_t nblk = gram_blocks(g, num_cu);
+  const G16Geo f = g16geo(g, num_cu);
+  if (f.ok) {
+    G16Geo ff = f;
+    ff.k.partial = g.partial;
+    if (mark) mark(mctx, KID_GRAM, true);
+    const hipError_t e = g.dt == DT_BF16 ? pick16<true>(ff, s) : pick16<false>(ff, s);
+    if (mark) mark(mctx, KID_GRAM, false);
+    if (e != hipSuccess) return e;
+    return reduce_partials(g.partial, nblk, r.Kin * r.Kin, g.out, s, mark, mctx);
+  }
   GK k;
   k.X = g.X;
   k.mask = g.mask;
@@ -271,13 +675,7 @@ hipError_t launch_gram(const GramArgs& g, int num_cu, hipStream_t s,
   }
   if (mark) mark(mctx, KID_GRAM, false);
   if (e != hipSuccess) return e;
-  const uint32_t n2 = r.Kin * r.Kin;
-  double* stage = g.partial + (uint64_t)nblk * n2;
-  if (mark) mark(mctx, KID_GRAM_REDUCE, true);
-  k_gram_reduce1<<<dim3((n2 + 255) / 256, RGROUPS), 256, 0, s>>>(g.partial, nblk, n2, stage);
-  k_gram_reduce2<<<(n2 + 255) / 256, 256, 0, s>>>(stage, n2, g.out);
-  if (mark) mark(mctx, KID_GRAM_REDUCE, false);
-  return hipGetLastError();
+  return reduce_partials(g.partial, nblk, r.Kin * r.Kin, g.out, s, mark, mctx);
 }
 
 }  // namespace tg

@@ -22,7 +22,8 @@
 //   4. compaction: each wave walks its unit 64 elements at a time; ballots give the
 //      in-order rank of every selected element, so Omega comes out ascending. The
 //      selection ballot of an aligned 64-element group is also the Omega membership
-//      bitmask word, and the running offset its rank word.
+//      bitmask word, and the running offset its rank word. Optionally the same pass
+//      writes the residual (G with Omega zeroed) to a separate buffer.
 #include "tg_common.h"
 
 namespace tg {
@@ -35,27 +36,38 @@ constexpr int UNIT_ITERS = 16;               // 16 x 64 = 1024 elements per wave
 constexpr uint64_t UNIT = 64ull * UNIT_ITERS;
 
 // state[0] = prefix, state[1] = remaining (ties still to take), state[2] = k
+// Per storage type: load the raw element, its key, and store a raw element.
 struct KeyF32 {
   static constexpr int BITS = 31;
-  __device__ static uint64_t key(const void* G, uint64_t e) {
-    return (uint64_t)(((const uint32_t*)G)[e] & 0x7FFFFFFFu);
-  }
+  typedef uint32_t Raw;
+  __device__ static Raw load(const void* G, uint64_t e) { return ((const uint32_t*)G)[e]; }
+  __device__ static uint64_t key_of(Raw x) { return (uint64_t)(x & 0x7FFFFFFFu); }
+  __device__ static void store(void* R, uint64_t e, Raw x) { ((uint32_t*)R)[e] = x; }
+  __device__ static Raw zero() { return 0u; }
+  __device__ static uint64_t key(const void* G, uint64_t e) { return key_of(load(G, e)); }
 };
 struct KeyH16 {
   static constexpr int BITS = 15;
-  __device__ static uint64_t key(const void* G, uint64_t e) {
-    return (uint64_t)(((const uint16_t*)G)[e] & 0x7FFFu);
-  }
+  typedef uint16_t Raw;
+  __device__ static Raw load(const void* G, uint64_t e) { return ((const uint16_t*)G)[e]; }
+  __device__ static uint64_t key_of(Raw x) { return (uint64_t)(x & 0x7FFFu); }
+  __device__ static void store(void* R, uint64_t e, Raw x) { ((uint16_t*)R)[e] = x; }
+  __device__ static Raw zero() { return (uint16_t)0; }
+  __device__ static uint64_t key(const void* G, uint64_t e) { return key_of(load(G, e)); }
 };
 struct KeyC64 {
   static constexpr int BITS = 63;
-  __device__ static uint64_t key(const void* G, uint64_t e) {
-    const float2 z = ((const float2*)G)[e];
+  typedef float2 Raw;
+  __device__ static Raw load(const void* G, uint64_t e) { return ((const float2*)G)[e]; }
+  __device__ static uint64_t key_of(Raw z) {
     const double re = (double)z.x, im = (double)z.y;
     const double s = re * re + im * im;
     if (s != s) return 0x7FF8000000000000ull;
     return (uint64_t)__double_as_longlong(s) & 0x7FFFFFFFFFFFFFFFull;
   }
+  __device__ static void store(void* R, uint64_t e, Raw x) { ((float2*)R)[e] = x; }
+  __device__ static Raw zero() { return make_float2(0.0f, 0.0f); }
+  __device__ static uint64_t key(const void* G, uint64_t e) { return key_of(load(G, e)); }
 };
 
 __global__ void k_topk_init(uint64_t* state, uint32_t* hist, uint32_t k) {
@@ -120,8 +132,10 @@ __global__ void __launch_bounds__(256) k_topk_count(const void* __restrict__ G, 
   for (int it = 0; it < UNIT_ITERS; ++it) {
     const uint64_t e = unit * UNIT + (uint64_t)it * 64 + lane;
     bool pg = false, pe = false;
+    typename K::Raw x = K::zero();
     if (e < N) {
-      const uint64_t key = K::key(G, e);
+      x = K::load(G, e);
+      const uint64_t key = K::key_of(x);
       pg = key > tau;
       pe = key == tau;
     }
@@ -180,7 +194,8 @@ __global__ void __launch_bounds__(256) k_topk_compact(const void* __restrict__ G
                                                       uint64_t nunits, uint64_t k,
                                                       uint32_t* __restrict__ omega,
                                                       uint64_t* __restrict__ mask,
-                                                      uint32_t* __restrict__ rank) {
+                                                      uint32_t* __restrict__ rank,
+                                                      void* __restrict__ resid) {
   const uint64_t unit = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
   if (unit >= nunits) return;
@@ -194,8 +209,10 @@ __global__ void __launch_bounds__(256) k_topk_compact(const void* __restrict__ G
     const uint64_t w = unit * UNIT_ITERS + it;
     const uint64_t e = w * 64 + lane;
     bool pg = false, pe = false;
+    typename K::Raw x = K::zero();
     if (e < N) {
-      const uint64_t key = K::key(G, e);
+      x = K::load(G, e);
+      const uint64_t key = K::key_of(x);
       pg = key > tau;
       pe = key == tau;
     }
@@ -205,6 +222,7 @@ __global__ void __launch_bounds__(256) k_topk_compact(const void* __restrict__ G
     const uint64_t selb = __ballot(sel);
     const uint64_t at = pos + (uint64_t)__popcll(selb & lt);
     if (sel && at < k) omega[at] = (uint32_t)e;
+    if (resid && e < N) K::store(resid, e, sel ? K::zero() : x);
     if (lane == 0 && w < nwords) {
       mask[w] = selb;
       rank[w] = (uint32_t)pos;
@@ -216,7 +234,7 @@ __global__ void __launch_bounds__(256) k_topk_compact(const void* __restrict__ G
 
 template <class K>
 hipError_t run_topk(const void* G, uint64_t N, uint32_t k, const TopkWs& ws, uint32_t* omega,
-                    uint64_t* mask, uint32_t* rank, hipStream_t s,
+                    uint64_t* mask, uint32_t* rank, void* resid, hipStream_t s,
                     void (*mark)(void*, int, bool), void* mctx) {
   auto M = [&](int id, bool b) { if (mark) mark(mctx, id, b); };
   hipError_t err;
@@ -252,7 +270,8 @@ hipError_t run_topk(const void* G, uint64_t N, uint32_t k, const TopkWs& ws, uin
   M(KID_TOPK_SCAN, false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   M(KID_TOPK_COMPACT, true);
-  k_topk_compact<K><<<ub, 256, 0, s>>>(G, N, ws.state, ws.uoff, nunits, k, omega, mask, rank);
+  k_topk_compact<K><<<ub, 256, 0, s>>>(G, N, ws.state, ws.uoff, nunits, k, omega, mask, rank,
+                                       resid);
   M(KID_TOPK_COMPACT, false);
   return hipGetLastError();
 }
@@ -295,13 +314,13 @@ unsigned fill_blocks(uint64_t n) {
 uint64_t topk_units(uint64_t N) { return (N + UNIT - 1) / UNIT; }
 
 hipError_t launch_topk(int dt, const void* G, uint64_t N, uint32_t k, const TopkWs& ws,
-                       uint32_t* omega, uint64_t* mask, uint32_t* rank, hipStream_t s,
-                       void (*mark)(void*, int, bool), void* mctx) {
+                       uint32_t* omega, uint64_t* mask, uint32_t* rank, void* resid,
+                       hipStream_t s, void (*mark)(void*, int, bool), void* mctx) {
   switch (dt) {
-    case DT_F32: return run_topk<KeyF32>(G, N, k, ws, omega, mask, rank, s, mark, mctx);
+    case DT_F32: return run_topk<KeyF32>(G, N, k, ws, omega, mask, rank, resid, s, mark, mctx);
     case DT_F16:
-    case DT_BF16: return run_topk<KeyH16>(G, N, k, ws, omega, mask, rank, s, mark, mctx);
-    case DT_C64: return run_topk<KeyC64>(G, N, k, ws, omega, mask, rank, s, mark, mctx);
+    case DT_BF16: return run_topk<KeyH16>(G, N, k, ws, omega, mask, rank, resid, s, mark, mctx);
+    case DT_C64: return run_topk<KeyC64>(G, N, k, ws, omega, mask, rank, resid, s, mark, mctx);
   }
   return hipErrorInvalidValue;
 }

@@ -73,8 +73,8 @@ struct TopkWs {
 };
 uint64_t topk_units(uint64_t N);
 hipError_t launch_topk(int dt, const void* G, uint64_t N, uint32_t k, const TopkWs& ws,
-                       uint32_t* omega, uint64_t* mask, uint32_t* rank, hipStream_t s,
-                       void (*mark)(void*, int, bool), void* mctx);
+                       uint32_t* omega, uint64_t* mask, uint32_t* rank, void* resid,
+                       hipStream_t s, void (*mark)(void*, int, bool), void* mctx);
 hipError_t launch_mask_from_omega(const uint32_t* omega, uint32_t k, uint64_t* mask,
                                   uint32_t* rank, uint64_t nwords, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint64_t n, uint32_t v, hipStream_t s);

@@ -10,6 +10,7 @@
 //   one applying W <- round(W - lr * (Delta_L + N_S at Omega)).
 // Refresh: top-k -> Omega (+ bitmask, ranks) -> per compressed mode: Gram of the
 //   residual (Omega masked on load) -> Jacobi eigensolver -> U(n) and operand matrices.
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -54,6 +55,7 @@ struct tgrad_handle {
   float *S = nullptr, *mS = nullptr, *vS = nullptr;
   float *core = nullptr, *ucore = nullptr, *mC = nullptr, *vC = nullptr;
   float* buf[2] = {nullptr, nullptr};
+  void* resid = nullptr;         // refresh: G with Omega zeroed (shares buf's memory)
   float* U[TGRAD_MAX_NDIM] = {nullptr};
   float* Mp[TGRAD_MAX_NDIM] = {nullptr};
   float* Mr[TGRAD_MAX_NDIM] = {nullptr};
@@ -221,20 +223,25 @@ void build_chain(const tgrad_t* h, bool fuse, std::vector<std::vector<int>>& pro
 }
 
 int do_refresh(tgrad_t* h, const void* grad, hipStream_t s) {
+  // the Grams read the residual: G itself when k = 0, else the copy with Omega zeroed
+  // that the top-k compaction writes
+  const void* R = grad;
   if (h->k > 0) {
+    void* rw = h->fmodes.empty() ? nullptr : h->resid;
     HIPCHK(h, launch_topk(h->dtype, grad, h->N, (uint32_t)h->k, h->tw, h->omega, h->mask,
-                          h->rank, s, mark_cb, h));
+                          h->rank, rw, s, mark_cb, h));
+    if (rw) R = rw;
   }
   const int gdt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
   EigArgs eig[TGRAD_MAX_NDIM];
   int ne = 0;
   for (int n : h->fmodes) {
     GramArgs g;
-    g.X = grad;
+    g.X = R;
     g.dt = gdt;
     view(h->shape, h->d, n, &g.A, &g.I, &g.B);
     g.P = h->P;
-    g.mask = h->k > 0 ? h->mask : nullptr;
+    g.mask = nullptr;
     g.partial = h->gram_part;
     g.out = h->gram + (size_t)ne * h->gram_stride;
     HIPCHK(h, launch_gram(g, h->num_cu, s, mark_cb, h));
@@ -395,8 +402,20 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
   ok = ok && dalloc(h, &h->vC, ncore * P, true);
   ok = ok && dalloc(h, &h->ucore, ncore * P, false);
   if (!h->fmodes.empty()) ok = ok && dalloc(h, &h->core, ncore * P, false);
-  ok = ok && dalloc(h, &h->buf[0], inter * P, false);
-  ok = ok && dalloc(h, &h->buf[1], inter * P, false);
+  // One block holds the two chain intermediates and, during a refresh (when they are
+  // idle), the residual G with Omega zeroed that the Gram kernels read.
+  {
+    const uint64_t esz = dtype == TGRAD_C64 ? 8 : (dtype == TGRAD_F32 ? 4 : 2);
+    const uint64_t rbytes = (h->k > 0 && !h->fmodes.empty()) ? N * esz : 0;
+    const uint64_t ib = (inter * P * sizeof(float) + 255) & ~255ull;
+    unsigned char* blk = nullptr;
+    ok = ok && dalloc(h, &blk, std::max(2 * ib, rbytes), false);
+    if (ok && inter) {
+      h->buf[0] = (float*)blk;
+      h->buf[1] = (float*)(blk + ib);
+    }
+    if (ok && rbytes) h->resid = blk;
+  }
   uint64_t gpart = 0, gmax = 0;
   for (int n : h->fmodes) {
     const uint64_t I = (uint64_t)shape[n], r = (uint64_t)tucker_ranks[n];
@@ -408,7 +427,12 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
     view(shape, ndim, n, &g.A, &g.I, &g.B);
     g.P = (uint32_t)P;
     const uint64_t K2 = (I * P) * (I * P);
-    const uint64_t nb = gram_blocks(g, h->num_cu) + gram_reduce_groups();
+    // partials for whichever Gram path a refresh takes (the 16-bit one needs an
+    // aligned input; the general one takes any)
+    g.dt = DT_F32;
+    uint64_t nb = gram_blocks(g, h->num_cu);
+    g.dt = dtype == TGRAD_C64 ? DT_F32 : dtype;
+    nb = std::max<uint64_t>(nb, gram_blocks(g, h->num_cu)) + gram_reduce_groups();
     if (nb * K2 > gpart) gpart = nb * K2;
     if (K2 > gmax) gmax = K2;
   }
