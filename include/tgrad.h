@@ -81,7 +81,7 @@ int tgrad_init(tgrad_t **out, int ndim, const int64_t *shape, const int64_t *tuc
 
 /*
  * One optimizer step on device buffers `weight` (W, updated in place) and `grad`
- * (G, caller-owned, N elements of dtype).
+ * (G, caller-owned, N elements of dtype, 16-byte aligned).
  *   t <- t + 1; if a refresh is due for t and tgrad_refresh was not already called
  *   for it, refresh from `grad` first. Then: S = G[Omega] (fp32) and G[Omega] <- 0
  *   (grad becomes the residual R in place and stays so on return); core C = R x_1
@@ -89,12 +89,13 @@ int tgrad_init(tgrad_t **out, int ndim, const int64_t *shape, const int64_t *tuc
  *   x_d Ud with N_S added at Omega (sparse scale 1); W <- round(W - lr * Delta), one
  *   rounding per element (nullthought section 3 step order; pith.science Theorem 2).
  * Both buffers must stay valid until the work on `stream` completes.
- * Errors: TGRAD_EINVAL (null handle/pointer), TGRAD_EHIP.
+ * Errors: TGRAD_EINVAL (null handle/pointer, grad not 16-byte aligned), TGRAD_EHIP.
  */
 int tgrad_step(tgrad_t *h, void *weight, void *grad, void *stream);
 
 /*
- * Refresh Omega and the Tucker factors from `grad` (device, N elements of dtype):
+ * Refresh Omega and the Tucker factors from `grad` (device, N elements of dtype,
+ * 16-byte aligned):
  * Omega = the k largest magnitudes (ties to the lowest linear index), stored
  * ascending; each U(n) (r_n < I_n) = the r_n leading eigenvectors of the mode-n Gram
  * matrix of the residual, descending eigenvalue order, each column scaled so its
@@ -102,7 +103,7 @@ int tgrad_step(tgrad_t *h, void *weight, void *grad, void *stream);
  * read. Moments and t are untouched; the refresh serves step t + 1.
  * (nullthought section 3: re-select sparse indices and low-rank subspace every T
  * steps; pith.science: top-k magnitude, Tucker/HOSVD factors.)
- * Errors: TGRAD_EINVAL, TGRAD_EHIP.
+ * Errors: TGRAD_EINVAL (null handle/pointer, grad not 16-byte aligned), TGRAD_EHIP.
  */
 int tgrad_refresh(tgrad_t *h, const void *grad, void *stream);
 

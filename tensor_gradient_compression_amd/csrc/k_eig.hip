@@ -272,6 +272,182 @@ __global__ void __launch_bounds__(NTH) k_eig(EK kk) {
   }
 }
 
+// ---------------------------------------------------------------- real symmetric case
+// Same method and arithmetic as above (parallel cyclic Jacobi in fp64, round-robin
+// pairs, each rotation from the same matrix, A <- J^T A J as the column rotation then
+// the row rotation), organised for one 1024-thread workgroup per matrix: per round, the
+// rotations are formed, then one pass applies the two-sided update to every 2 x 2 block
+// (pair a rows, pair b columns) of A and the column rotation to V. Every element sees
+// the same operations in the same order as a column pass followed by a row pass.
+constexpr int NTS = 1024;
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
+  extern __shared__ double sm[];
+  const EK1& k = kk.m[blockIdx.x];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t n = k.n;
+  const uint32_t LD = n + 1;          // odd row stride: column walks hit distinct banks
+  const uint32_t nn = n * LD;
+  double* A = sm;
+  double* V = A + nn;
+  double* rc = V + nn;        // 32 rotations: cos, sin (sign of a_pq folded in)
+  double* rs = rc + 32;
+  double* red = rs + 32;      // 2 x 16 wave partials
+  int* rp = (int*)(red + 32);
+  int* rq = rp + 32;
+  int* order = rq + 32;       // 64
+
+  for (uint32_t idx0 = tid; idx0 < n * n; idx0 += NTS) {
+    const uint32_t i = idx0 / n, j = idx0 - i * n;
+    A[i * LD + j] = 0.5 * (k.gram[(uint64_t)i * n + j] + k.gram[(uint64_t)j * n + i]);
+    V[i * LD + j] = (i == j) ? 1.0 : 0.0;
+  }
+  __syncthreads();
+
+  const uint32_t m = n + (n & 1u);   // even number of players; player n is a bye
+  const uint32_t half = m / 2;
+  for (int sweep = 0; sweep < 40; ++sweep) {
+    double off = 0.0, tot = 0.0;
+    for (uint32_t idx0 = tid; idx0 < n * n; idx0 += NTS) {
+      const uint32_t i = idx0 / n, j = idx0 - i * n;
+      const double a = A[i * LD + j];
+      tot += a * a;
+      if (i != j) off += a * a;
+    }
+    off = wave_sum(off);
+    tot = wave_sum(tot);
+    if (lane == 0) {
+      red[wave] = off;
+      red[16 + wave] = tot;
+    }
+    __syncthreads();
+    off = 0.0;
+    tot = 0.0;
+    for (int w = 0; w < NTS / 64; ++w) {
+      off += red[w];
+      tot += red[16 + w];
+    }
+    if (!(off > 1e-26 * tot)) break;
+
+    for (uint32_t round = 0; round + 1 < m; ++round) {
+      if (tid < half) {
+        auto player = [&](uint32_t pos) -> uint32_t {
+          return pos == 0 ? 0u : 1u + (pos - 1u + round) % (m - 1u);
+        };
+        uint32_t p = player(tid), q = player(m - 1 - tid);
+        if (p > q) { uint32_t t = p; p = q; q = t; }
+        double c = 1.0, ss = 0.0;
+        if (q < n) {
+          const double app = A[p * LD + p], aqq = A[q * LD + q];
+          const double xr = A[p * LD + q];
+          const double rr = fabs(xr);
+          if (rr > 0.0) {
+            const double theta = (aqq - app) / (2.0 * rr);
+            double t;
+            if (fabs(theta) > 1e100) {
+              t = 0.5 / theta;
+            } else {
+              t = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+            }
+            c = 1.0 / sqrt(t * t + 1.0);
+            ss = (t * c) * (xr >= 0.0 ? 1.0 : -1.0);
+          }
+        }
+        rc[tid] = c;
+        rs[tid] = ss;
+        rp[tid] = (int)p;
+        rq[tid] = (q < n) ? (int)q : -1;
+      }
+      __syncthreads();
+      // A: block (pair a rows) x (pair b columns); a bye or an unrotated pair acts as
+      // the identity on its index
+      for (uint32_t t = tid; t < half * half; t += NTS) {
+        const uint32_t a = t / half, b = t - a * half;
+        const int qa = rq[a], qb = rq[b];
+        const bool ra = qa >= 0 && rs[a] != 0.0, rb = qb >= 0 && rs[b] != 0.0;
+        if (!ra && !rb) continue;
+        const int pa = rp[a], pb = rp[b];
+        const double ca = rc[a], sa = rs[a], cb = rc[b], sb = rs[b];
+        double x00 = A[pa * LD + pb];
+        double x01 = qb >= 0 ? A[pa * LD + qb] : 0.0;
+        double x10 = qa >= 0 ? A[qa * LD + pb] : 0.0;
+        double x11 = (qa >= 0 && qb >= 0) ? A[qa * LD + qb] : 0.0;
+        if (rb) {   // columns pb, qb
+          const double y00 = cb * x00 - sb * x01, y01 = sb * x00 + cb * x01;
+          const double y10 = cb * x10 - sb * x11, y11 = sb * x10 + cb * x11;
+          x00 = y00; x01 = y01; x10 = y10; x11 = y11;
+        }
+        if (ra) {   // rows pa, qa
+          const double z00 = ca * x00 - sa * x10, z10 = sa * x00 + ca * x10;
+          const double z01 = ca * x01 - sa * x11, z11 = sa * x01 + ca * x11;
+          x00 = z00; x10 = z10; x01 = z01; x11 = z11;
+        }
+        A[pa * LD + pb] = x00;
+        if (qb >= 0) A[pa * LD + qb] = x01;
+        if (qa >= 0) A[qa * LD + pb] = x10;
+        if (qa >= 0 && qb >= 0) A[qa * LD + qb] = x11;
+      }
+      // V <- V J (columns)
+      for (uint32_t t = tid; t < n * half; t += NTS) {
+        const uint32_t b = t / n, i = t - b * n;
+        const int qb = rq[b];
+        if (qb < 0 || rs[b] == 0.0) continue;
+        const int pb = rp[b];
+        const double cb = rc[b], sb = rs[b];
+        const double vx = V[i * LD + pb], vy = V[i * LD + qb];
+        V[i * LD + pb] = cb * vx - sb * vy;
+        V[i * LD + qb] = sb * vx + cb * vy;
+      }
+      __syncthreads();
+    }
+  }
+
+  // Descending order of the diagonal, equal values in index order: rank of each entry.
+  if (tid < n) {
+    const double d = A[tid * LD + tid];
+    uint32_t rank = 0;
+    for (uint32_t j = 0; j < n; ++j) {
+      const double e = A[j * LD + j];
+      rank += (e > d || (e == d && j < tid)) ? 1u : 0u;
+    }
+    order[rank] = (int)tid;
+  }
+  __syncthreads();
+  if (tid < n) k.eigvals[tid] = A[order[tid] * LD + order[tid]];
+
+  // one wave per selected column: largest |entry| (lowest row on ties) made positive
+  const uint32_t r = k.r;
+  for (uint32_t c = wave; c < r; c += NTS / 64) {
+    const uint32_t src = (uint32_t)order[c];
+    const double x = lane < n ? V[lane * LD + src] : 0.0;
+    double best = lane < n ? x * x : -1.0;
+    uint32_t bi = lane;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const double ob = __shfl_xor(best, off, 64);
+      const uint32_t oi = __shfl_xor(bi, off, 64);
+      if (ob > best || (ob == best && oi < bi)) {
+        best = ob;
+        bi = oi;
+      }
+    }
+    const double vmax = __shfl(x, bi, 64);
+    const double sr = vmax != 0.0 ? (vmax > 0.0 ? 1.0 : -1.0) : 1.0;
+    if (lane < n) {
+      const float u = (float)(x * sr);
+      k.U[(uint64_t)lane * r + c] = u;
+      k.Mproj[(uint64_t)c * n + lane] = u;
+      k.Mrec[(uint64_t)lane * r + c] = u;
+    }
+  }
+}
+
 }  // namespace
 
 size_t eig_lds_bytes(uint32_t I, uint32_t P) {
@@ -296,13 +472,14 @@ hipError_t launch_eig(const EigArgs* e, int count, hipStream_t s) {
     const size_t b = eig_lds_bytes(e[i].I, e[i].P);
     if (b > lds) lds = b;
   }
-  auto fn = (e[0].P == 2) ? k_eig<true> : k_eig<false>;
+  const bool cplx = e[0].P == 2;
+  auto fn = cplx ? k_eig<true> : k_eig_sym;
   if (lds > 64 * 1024) {
     hipError_t err = hipFuncSetAttribute((const void*)fn,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(fn, dim3(count), dim3(NTH), lds, s, k);
+  hipLaunchKernelGGL(fn, dim3(count), dim3(cplx ? NTH : NTS), lds, s, k);
   return hipGetLastError();
 }
 

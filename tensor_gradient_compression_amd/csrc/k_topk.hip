@@ -9,21 +9,24 @@
 // the bits of fl64(re^2 + im^2) (both squares exact in fp64, so one rounding), any
 // NaN mapped to the canonical quiet NaN.
 //
-// Algorithm (all passes re-read G; no key array is stored):
+// Algorithm (all passes re-read G; no key array is stored). Every pass reads G as groups
+// of 8 consecutive elements per lane (16 bytes for 16-bit data):
 //   1. radix select, most significant 11-bit digit first: per pass, each workgroup
 //      builds an LDS histogram of the digit over the elements whose higher digits
 //      equal the prefix found so far, and adds it to a global histogram; a one-block
 //      kernel walks the bins from the top and fixes the next digit. After the last
 //      digit: tau = the k-th largest key, need = how many keys equal to tau are taken.
-//   2. count pass: each wave64 counts (key > tau, key == tau) over a unit of 1024
+//   2. count pass: each wave counts (key > tau, key == tau) over a unit of 1024
 //      consecutive elements.
 //   3. scan: one block turns unit counts into each unit's output offset and its
-//      number of preceding ties.
-//   4. compaction: each wave walks its unit 64 elements at a time; ballots give the
-//      in-order rank of every selected element, so Omega comes out ascending. The
-//      selection ballot of an aligned 64-element group is also the Omega membership
-//      bitmask word, and the running offset its rank word. Optionally the same pass
-//      writes the residual (G with Omega zeroed) to a separate buffer.
+//      number of preceding ties, a chunk of units at a time.
+//   4. compaction: each wave walks its unit 512 elements at a time; prefix sums of the
+//      lanes' counts give the in-order rank of every selected element (ties taken in
+//      index order), so Omega comes out ascending. Each lane writes its 8 membership
+//      bits as one byte of the bitmask, the lane that starts a 64-element word writes
+//      that word's rank, and optionally the residual (G with Omega zeroed) goes to a
+//      separate buffer.
+// G must be 16-byte aligned.
 #include "tg_common.h"
 
 namespace tg {
@@ -32,8 +35,8 @@ namespace {
 
 constexpr int DIGIT = 11;
 constexpr int NBINS = 1 << DIGIT;
-constexpr int UNIT_ITERS = 16;               // 16 x 64 = 1024 elements per wave unit
-constexpr uint64_t UNIT = 64ull * UNIT_ITERS;
+constexpr int UNIT_ITERS = 2;                // 2 x 64 lanes x 8 = 1024 elements per wave unit
+constexpr uint64_t UNIT = 512ull * UNIT_ITERS;
 
 // state[0] = prefix, state[1] = remaining (ties still to take), state[2] = k
 // Per storage type: load the raw element, its key, and store a raw element.
@@ -45,6 +48,16 @@ struct KeyF32 {
   __device__ static void store(void* R, uint64_t e, Raw x) { ((uint32_t*)R)[e] = x; }
   __device__ static Raw zero() { return 0u; }
   __device__ static uint64_t key(const void* G, uint64_t e) { return key_of(load(G, e)); }
+  __device__ static void load8(const void* G, uint64_t e0, Raw* x) {
+    const uint4 a = ((const uint4*)((const uint32_t*)G + e0))[0];
+    const uint4 b = ((const uint4*)((const uint32_t*)G + e0))[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+  __device__ static void store8(void* R, uint64_t e0, const Raw* x) {
+    ((uint4*)((uint32_t*)R + e0))[0] = make_uint4(x[0], x[1], x[2], x[3]);
+    ((uint4*)((uint32_t*)R + e0))[1] = make_uint4(x[4], x[5], x[6], x[7]);
+  }
 };
 struct KeyH16 {
   static constexpr int BITS = 15;
@@ -54,6 +67,21 @@ struct KeyH16 {
   __device__ static void store(void* R, uint64_t e, Raw x) { ((uint16_t*)R)[e] = x; }
   __device__ static Raw zero() { return (uint16_t)0; }
   __device__ static uint64_t key(const void* G, uint64_t e) { return key_of(load(G, e)); }
+  __device__ static void load8(const void* G, uint64_t e0, Raw* x) {
+    const uint4 a = *(const uint4*)((const uint16_t*)G + e0);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = (uint16_t)(w[j] & 0xFFFFu);
+      x[2 * j + 1] = (uint16_t)(w[j] >> 16);
+    }
+  }
+  __device__ static void store8(void* R, uint64_t e0, const Raw* x) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = (uint32_t)x[2 * j] | ((uint32_t)x[2 * j + 1] << 16);
+    *(uint4*)((uint16_t*)R + e0) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
 };
 struct KeyC64 {
   static constexpr int BITS = 63;
@@ -68,7 +96,34 @@ struct KeyC64 {
   __device__ static void store(void* R, uint64_t e, Raw x) { ((float2*)R)[e] = x; }
   __device__ static Raw zero() { return make_float2(0.0f, 0.0f); }
   __device__ static uint64_t key(const void* G, uint64_t e) { return key_of(load(G, e)); }
+  __device__ static void load8(const void* G, uint64_t e0, Raw* x) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = ((const float4*)((const float2*)G + e0))[j];
+      x[2 * j] = make_float2(v.x, v.y);
+      x[2 * j + 1] = make_float2(v.z, v.w);
+    }
+  }
+  __device__ static void store8(void* R, uint64_t e0, const Raw* x) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      ((float4*)((float2*)R + e0))[j] =
+          make_float4(x[2 * j].x, x[2 * j].y, x[2 * j + 1].x, x[2 * j + 1].y);
+  }
 };
+
+// The 8 consecutive elements e0 .. e0 + 7 (e0 a multiple of 8, G 16-byte aligned);
+// past N they read as zero keys and are never selected.
+template <class K>
+__device__ __forceinline__ void load_group(const void* G, uint64_t N, uint64_t e0,
+                                           typename K::Raw* x) {
+  if (e0 + 8 <= N) {
+    K::load8(G, e0, x);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = e0 + j < N ? K::load(G, e0 + j) : K::zero();
+  }
+}
 
 __global__ void k_topk_init(uint64_t* state, uint32_t* hist, uint32_t k) {
   for (int i = threadIdx.x; i < NBINS; i += blockDim.x) hist[i] = 0;
@@ -92,31 +147,82 @@ __global__ void __launch_bounds__(256) k_topk_hist(const void* __restrict__ G, u
   const uint64_t want = state[0] >> hi;
   const uint64_t dmask = (1ull << width) - 1ull;
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  for (uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; e < N; e += stride) {
-    const uint64_t key = K::key(G, e);
-    if ((key >> hi) == want) atomicAdd(&h[(key >> shift) & dmask], 1u);
+  const uint64_t ngroups = (N + 7) / 8;
+  for (uint64_t gi = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < ngroups;
+       gi += stride) {
+    typename K::Raw x[8];
+    load_group<K>(G, N, gi * 8, x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint64_t key = K::key_of(x[j]);
+      if (gi * 8 + j < N && (key >> hi) == want) atomicAdd(&h[(key >> shift) & dmask], 1u);
+    }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < (1 << width); i += blockDim.x)
     if (h[i]) atomicAdd(&ghist[i], h[i]);
 }
 
-// Fix the next digit; clears the histogram for the next pass.
-__global__ void k_topk_select(uint32_t* hist, int shift, int width, uint64_t* state) {
-  if (threadIdx.x == 0) {
-    const uint64_t rem = state[1];
-    uint64_t cum = 0;
-    int b = (1 << width) - 1;
-    for (; b > 0; --b) {
-      const uint64_t c = hist[b];
-      if (cum + c >= rem) break;
-      cum += c;
+// Fix the next digit and clear the histogram for the next pass. The digit is the
+// highest bin b whose count, added to the counts of all higher bins, reaches the number
+// of keys still to take (bin 0 if none does); 256 threads own 8 consecutive bins each
+// and a suffix scan over the threads locates that bin.
+__global__ void __launch_bounds__(256) k_topk_select(uint32_t* hist, int shift, int width,
+                                                     uint64_t* state) {
+  __shared__ uint64_t suf[257];
+  __shared__ int found_b;
+  __shared__ uint64_t found_cum;
+  const int t = threadIdx.x;
+  const int nb = 1 << width;
+  constexpr int PER = NBINS / 256;
+  const int b0 = t * PER;
+  uint32_t c[PER];
+  uint64_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    c[i] = b0 + i < nb ? hist[b0 + i] : 0u;
+    mine += c[i];
+  }
+  suf[t] = mine;
+  if (t == 0) {
+    suf[256] = 0;
+    found_b = -1;
+  }
+  __syncthreads();
+  // inclusive suffix sums: suf[t] = sum over threads >= t
+  for (int off = 1; off < 256; off <<= 1) {
+    const uint64_t y = t + off < 256 ? suf[t + off] : 0;
+    __syncthreads();
+    suf[t] += y;
+    __syncthreads();
+  }
+  const uint64_t rem = state[1];
+  const uint64_t above = suf[t + 1];        // bins owned by higher threads
+  if (above < rem && above + mine >= rem) {
+    uint64_t cum = above;
+    for (int i = PER - 1; i >= 0; --i) {
+      const int b = b0 + i;
+      if (b == 0 || cum + c[i] >= rem) {
+        found_b = b;
+        found_cum = cum;
+        break;
+      }
+      cum += c[i];
+    }
+  }
+  __syncthreads();
+  if (t == 0) {
+    int b = found_b;
+    uint64_t cum = found_cum;
+    if (b < 0) {             // never reached: bin 0, with every higher bin counted
+      b = 0;
+      cum = suf[0] - (nb > 0 ? (uint64_t)hist[0] : 0);
     }
     state[0] |= ((uint64_t)b) << shift;
     state[1] = rem - cum;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < NBINS; i += blockDim.x) hist[i] = 0;
+  for (int i = t; i < NBINS; i += blockDim.x) hist[i] = 0;
 }
 
 template <class K>
@@ -130,17 +236,21 @@ __global__ void __launch_bounds__(256) k_topk_count(const void* __restrict__ G, 
   const uint64_t tau = state[0];
   uint32_t gt = 0, eq = 0;
   for (int it = 0; it < UNIT_ITERS; ++it) {
-    const uint64_t e = unit * UNIT + (uint64_t)it * 64 + lane;
-    bool pg = false, pe = false;
-    typename K::Raw x = K::zero();
-    if (e < N) {
-      x = K::load(G, e);
-      const uint64_t key = K::key_of(x);
-      pg = key > tau;
-      pe = key == tau;
+    const uint64_t e0 = unit * UNIT + (uint64_t)it * 512 + (uint64_t)lane * 8;
+    typename K::Raw x[8];
+    load_group<K>(G, N, e0, x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint64_t key = K::key_of(x[j]);
+      const bool in = e0 + j < N;
+      gt += (in && key > tau) ? 1u : 0u;
+      eq += (in && key == tau) ? 1u : 0u;
     }
-    gt += (uint32_t)__popcll(__ballot(pg));
-    eq += (uint32_t)__popcll(__ballot(pe));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    gt += __shfl_xor(gt, off, 64);
+    eq += __shfl_xor(eq, off, 64);
   }
   if (lane == 0) {
     ucount[2 * unit] = gt;
@@ -148,42 +258,91 @@ __global__ void __launch_bounds__(256) k_topk_count(const void* __restrict__ G, 
   }
 }
 
-// One block of 1024 threads: exclusive scan of (gt, eq) unit counts.
+// One block of 1024 threads: exclusive scan of the (gt, eq) unit counts, in chunks of
+// 1024 x SCAN_V consecutive units (each thread SCAN_V of them, loaded as 16-byte
+// pieces); the next chunk's counts are loaded before the current chunk is scanned.
+// uoff[2u] = selected elements before unit u = gt before + min(eq before, need);
+// uoff[2u + 1] = ties before unit u. (N < 2^32, so every count fits in 32 bits.)
+constexpr int SCAN_V = 8;
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sw, uint32_t& total) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sw[wave] = x;
+  __syncthreads();
+  uint32_t before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const uint32_t y = sw[w];
+    before += w < wave ? y : 0u;
+    total += y;
+  }
+  __syncthreads();
+  return before + x - v;
+}
+
 __global__ void __launch_bounds__(1024) k_topk_scan(const uint32_t* __restrict__ ucount,
                                                     uint64_t nunits,
                                                     const uint64_t* __restrict__ state,
                                                     uint32_t* __restrict__ uoff) {
-  __shared__ uint64_t sg[1024], se[1024];
+  __shared__ uint32_t sw[16];
   const int t = threadIdx.x;
-  const uint64_t per = (nunits + 1023) / 1024;
-  const uint64_t lo = per * t < nunits ? per * t : nunits;
-  const uint64_t hi = lo + per < nunits ? lo + per : nunits;
-  uint64_t g = 0, q = 0;
-  for (uint64_t u = lo; u < hi; ++u) {
-    g += ucount[2 * u];
-    q += ucount[2 * u + 1];
-  }
-  sg[t] = g;
-  se[t] = q;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    uint64_t ag = 0, aq = 0;
-    if (t >= off) {
-      ag = sg[t - off];
-      aq = se[t - off];
+  const uint32_t need = (uint32_t)state[1];
+  const uint32_t nu = (uint32_t)nunits;
+  constexpr uint32_t CH = 1024u * SCAN_V;
+  auto load = [&](uint32_t c0, uint4* v) {
+    const uint32_t u0 = c0 + (uint32_t)t * SCAN_V;
+#pragma unroll
+    for (int q = 0; q < SCAN_V / 2; ++q) {
+      const uint32_t u = u0 + 2 * q;
+      if (u + 2 <= nu) {
+        v[q] = *(const uint4*)(ucount + 2 * (uint64_t)u);
+      } else {
+        v[q] = make_uint4(u < nu ? ucount[2 * (uint64_t)u] : 0u,
+                          u < nu ? ucount[2 * (uint64_t)u + 1] : 0u, 0u, 0u);
+      }
     }
-    __syncthreads();
-    sg[t] += ag;
-    se[t] += aq;
-    __syncthreads();
-  }
-  uint64_t gp = sg[t] - g, qp = se[t] - q;   // exclusive prefixes
-  const uint64_t need = state[1];
-  for (uint64_t u = lo; u < hi; ++u) {
-    uoff[2 * u] = (uint32_t)(gp + (qp < need ? qp : need));
-    uoff[2 * u + 1] = (uint32_t)qp;
-    gp += ucount[2 * u];
-    qp += ucount[2 * u + 1];
+  };
+  uint4 cur[SCAN_V / 2], nxt[SCAN_V / 2];
+  load(0, cur);
+  uint32_t gbase = 0, qbase = 0;
+  for (uint32_t c0 = 0; c0 < nu; c0 += CH) {
+    if (c0 + CH < nu) load(c0 + CH, nxt);
+    uint32_t g = 0, q = 0;
+#pragma unroll
+    for (int i = 0; i < SCAN_V / 2; ++i) {
+      g += cur[i].x + cur[i].z;
+      q += cur[i].y + cur[i].w;
+    }
+    uint32_t gt_tot, eq_tot;
+    uint32_t gp = gbase + block_excl_scan(g, sw, gt_tot);
+    uint32_t qp = qbase + block_excl_scan(q, sw, eq_tot);
+    const uint32_t u0 = c0 + (uint32_t)t * SCAN_V;
+#pragma unroll
+    for (int i = 0; i < SCAN_V / 2; ++i) {
+      const uint32_t u = u0 + 2 * i;
+      const uint32_t o0 = gp + (qp < need ? qp : need), e0 = qp;
+      gp += cur[i].x;
+      qp += cur[i].y;
+      const uint32_t o1 = gp + (qp < need ? qp : need), e1 = qp;
+      gp += cur[i].z;
+      qp += cur[i].w;
+      if (u + 2 <= nu) {
+        *(uint4*)(uoff + 2 * (uint64_t)u) = make_uint4(o0, e0, o1, e1);
+      } else if (u < nu) {
+        uoff[2 * (uint64_t)u] = o0;
+        uoff[2 * (uint64_t)u + 1] = e0;
+      }
+    }
+    gbase += gt_tot;
+    qbase += eq_tot;
+#pragma unroll
+    for (int i = 0; i < SCAN_V / 2; ++i) cur[i] = nxt[i];
   }
 }
 
@@ -202,33 +361,71 @@ __global__ void __launch_bounds__(256) k_topk_compact(const void* __restrict__ G
   const uint64_t tau = state[0];
   const uint64_t need = state[1];
   const uint64_t nwords = (N + 63) >> 6;
-  const uint64_t lt = (1ull << lane) - 1ull;
-  uint64_t pos = uoff[2 * unit];
-  uint64_t eqrun = uoff[2 * unit + 1];
+  uint64_t pos = uoff[2 * unit];        // selected elements before this group of 512
+  uint64_t eqrun = uoff[2 * unit + 1];  // ties before it
   for (int it = 0; it < UNIT_ITERS; ++it) {
-    const uint64_t w = unit * UNIT_ITERS + it;
-    const uint64_t e = w * 64 + lane;
-    bool pg = false, pe = false;
-    typename K::Raw x = K::zero();
-    if (e < N) {
-      x = K::load(G, e);
-      const uint64_t key = K::key_of(x);
-      pg = key > tau;
-      pe = key == tau;
+    const uint64_t e0 = unit * UNIT + (uint64_t)it * 512 + (uint64_t)lane * 8;
+    typename K::Raw x[8];
+    load_group<K>(G, N, e0, x);
+    uint32_t pg = 0, pe = 0;   // bit j: element e0 + j is > tau / == tau
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint64_t key = K::key_of(x[j]);
+      if (e0 + j < N) {
+        pg |= (key > tau ? 1u : 0u) << j;
+        pe |= (key == tau ? 1u : 0u) << j;
+      }
     }
-    const uint64_t eqb = __ballot(pe);
-    const bool take_eq = pe && (eqrun + (uint64_t)__popcll(eqb & lt) < need);
-    const bool sel = pg || take_eq;
-    const uint64_t selb = __ballot(sel);
-    const uint64_t at = pos + (uint64_t)__popcll(selb & lt);
-    if (sel && at < k) omega[at] = (uint32_t)e;
-    if (resid && e < N) K::store(resid, e, sel ? K::zero() : x);
-    if (lane == 0 && w < nwords) {
-      mask[w] = selb;
-      rank[w] = (uint32_t)pos;
+    // ties and strict selections before this lane's group, in element order
+    uint32_t ce = (uint32_t)__popc(pe), cg = (uint32_t)__popc(pg);
+    uint32_t xe = ce, xg = cg;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t ye = __shfl_up(xe, off, 64), yg = __shfl_up(xg, off, 64);
+      if (lane >= off) {
+        xe += ye;
+        xg += yg;
+      }
     }
-    pos += (uint64_t)__popcll(selb);
-    eqrun += (uint64_t)__popcll(eqb);
+    const uint32_t te = __shfl(xe, 63, 64), tg = __shfl(xg, 63, 64);
+    uint64_t eqb = eqrun + (xe - ce);              // ties before this lane's group
+    // selected before this lane's group: strict ones plus the ties taken so far
+    const uint64_t taken0 = eqrun < need ? eqrun : need;
+    const uint64_t takenb = eqb < need ? eqb : need;
+    uint64_t at = pos + (xg - cg) + (takenb - taken0);
+    uint32_t sel = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      bool sj = (pg >> j) & 1u;
+      if ((pe >> j) & 1u) {
+        sj = eqb < need;
+        ++eqb;
+      }
+      if (sj) {
+        if (at < k) omega[at] = (uint32_t)(e0 + j);
+        ++at;
+        sel |= 1u << j;
+      }
+    }
+    if (e0 < nwords * 64) {
+      ((uint8_t*)mask)[e0 >> 3] = (uint8_t)sel;
+      if ((lane & 7) == 0) rank[e0 >> 6] = (uint32_t)(pos + (xg - cg) + (takenb - taken0));
+    }
+    if (resid && e0 < N) {
+      if (e0 + 8 <= N) {
+        typename K::Raw y[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = ((sel >> j) & 1u) ? K::zero() : x[j];
+        K::store8(resid, e0, y);
+      } else {
+        for (int j = 0; j < 8 && e0 + j < N; ++j)
+          K::store(resid, e0 + j, ((sel >> j) & 1u) ? K::zero() : x[j]);
+      }
+    }
+    // the group of 512 after this one
+    const uint64_t taken1 = (eqrun + te) < need ? (eqrun + te) : need;
+    pos += tg + (taken1 - taken0);
+    eqrun += te;
   }
 }
 

@@ -488,14 +488,14 @@ int tgrad_destroy(tgrad_t* h) {
 }
 
 int tgrad_refresh(tgrad_t* h, const void* grad, void* stream) {
-  if (!h || !grad) return TGRAD_EINVAL;
+  if (!h || !grad || ((uintptr_t)grad & 15u) != 0) return TGRAD_EINVAL;
   DevGuard g(h->device);
   h->cur_stream = (hipStream_t)stream;
   return do_refresh(h, grad, (hipStream_t)stream);
 }
 
 int tgrad_step(tgrad_t* h, void* weight, void* grad, void* stream) {
-  if (!h || !weight || !grad) return TGRAD_EINVAL;
+  if (!h || !weight || !grad || ((uintptr_t)grad & 15u) != 0) return TGRAD_EINVAL;
   DevGuard gd(h->device);
   hipStream_t s = (hipStream_t)stream;
   h->cur_stream = s;
