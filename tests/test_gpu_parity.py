@@ -261,6 +261,26 @@ def test_deterministic_rerun():
     assert np.array_equal(outs[0][2], outs[1][2])
 
 
+def test_misaligned_grad_is_rejected():
+    """grad is read in 16-byte pieces: a view 2 bytes off is refused with EINVAL before
+    any work, and the handle still steps afterwards."""
+    wl = custom((8, 6, 5), "bf16", (4, 3, 5), 0.1, T=2)
+    lib = make_lib(wl)
+    G = dev(GradStream(wl, seed=1).next(), "bf16")
+    W = dev(init_weights(wl, seed=1), "bf16")
+    buf = torch.zeros(G.numel() + 8, dtype=torch.bfloat16, device="cuda")
+    bad = buf[1:1 + G.numel()]
+    assert bad.data_ptr() % 16 != 0
+    with pytest.raises(tg.TGradError, match="invalid argument"):
+        lib.step(W, bad)
+    with pytest.raises(tg.TGradError, match="invalid argument"):
+        lib.refresh(bad)
+    assert lib.t == 0
+    lib.step(W, G)
+    torch.cuda.synchronize()
+    assert lib.t == 1
+
+
 def test_timing_records_every_kernel():
     wl = CONFIGS[1]
     lib = make_lib(wl)
