@@ -55,6 +55,7 @@ struct MP2K {
   uint32_t off_m2, off_x0, off_x1, off_y, off_o, off_w0, off_w1, off_r0, off_r1;
   float lr;
   int has_sparse;
+  float* gS;              // projection with the COO gather folded in (else null)
 };
 
 // One mode product between LDS buffers over the (A', I, B, P) view: ncols = A' * B
@@ -202,13 +203,15 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
                     lds + (buf ? k.off_w1 : k.off_w0));
   };
   // The tile's Omega entries are the contiguous range [rank(e_lo), rank(e_hi)) of the
-  // sorted list, rank(e) = rank[e / 64] + popcount(mask[e / 64] below bit e % 64). The
+  // sorted list, rank(e) = rank[e / 64] + popcount(mask[e / 64] below bit e % 64), over
+  // the tile's output elements (reconstruction) or input elements (projection). The
   // two boundary words and ranks travel with the tile's transfer: lanes 0-5 of wave 0
   // bring mask[lo] (2 dwords), rank[lo], mask[hi] (2 dwords), rank[hi] into a 24-byte
   // LDS slot of the same buffer, read after the barrier that publishes the tile.
-  auto tile_lo = [&](uint64_t tile) -> uint64_t { return tile * k.TA * slab_out / P; };
+  const uint32_t slab_e = REC ? slab_out : slab_in;
+  auto tile_lo = [&](uint64_t tile) -> uint64_t { return tile * k.TA * slab_e / P; };
   auto tile_hi = [&](uint64_t tile) -> uint64_t {
-    return (tile * k.TA + nta_of(tile)) * slab_out / P;
+    return (tile * k.TA + nta_of(tile)) * slab_e / P;
   };
   auto issue_rank = [&](uint64_t tile, int buf) {
     if (tid < 6) {
@@ -227,6 +230,9 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
     return r[2] + (uint64_t)__popcll(word & ((1ull << (e & 63)) - 1ull));
   };
   const bool merged = (EPI == 1) && k.has_sparse;
+  // projection: the sparse part leaves the staged input before the first product
+  const bool gath = !REC && k.gS != nullptr;
+  const bool ranged = merged || gath;
   constexpr int NSR = 2;
   uint64_t jc0 = 0, jc1 = 0;
 
@@ -234,7 +240,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
   int cur = 0;
   if (tile < k.ntiles) {
     issue(tile, cur);
-    if (merged) issue_rank(tile, cur);
+    if (ranged) issue_rank(tile, cur);
   }
   __builtin_amdgcn_s_waitcnt(0);
   for (; tile < k.ntiles; tile += gridDim.x) {
@@ -244,25 +250,27 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
     const uint64_t a0 = tile * k.TA;
     unsigned char* bx = lds + (cur ? k.off_x1 : k.off_x0);
     unsigned char* bw = lds + (cur ? k.off_w1 : k.off_w0);
-    if (merged) {
+    if (ranged) {
       const uint32_t* r = (const uint32_t*)(lds + (cur ? k.off_r1 : k.off_r0));
       jc0 = rank_from(r, tile_lo(tile));
       jc1 = rank_from(r + 3, tile_hi(tile));
     }
     if (next < k.ntiles) {
       issue(next, cur ^ 1);
-      if (merged) issue_rank(next, cur ^ 1);
+      if (ranged) issue_rank(next, cur ^ 1);
     }
     uint32_t om_r[NSR];
     float us_r[NSR][P];
-    if (merged) {
+    if (ranged) {
 #pragma unroll
       for (int i = 0; i < NSR; ++i) {
         const uint64_t j = jc0 + tid + (uint64_t)NTH * i;
         if (j < jc1) {
           om_r[i] = k.omega[j];
+          if (merged) {
 #pragma unroll
-          for (int p = 0; p < P; ++p) us_r[i][p] = k.uS[j * P + p];
+            for (int p = 0; p < P; ++p) us_r[i][p] = k.uS[j * P + p];
+          }
         }
       }
     }
@@ -279,6 +287,31 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
       filled = true;
     }
     if (filled) lds_barrier();
+
+    if (gath) {
+      // S[j] = X[omega[j]] (fp32), then X[omega[j]] <- 0 in the staged tile and in HBM:
+      // the projection runs on the residual, which the gradient buffer keeps
+      const uint64_t e_lo = a0 * slab_in / P;
+      XT* xs = (XT*)bx;
+      XT* xg = (XT*)const_cast<void*>(k.X);
+      const XT z = zero_of<XT>();
+      auto take = [&](uint64_t j, uint32_t om) {
+        const uint32_t loc = (uint32_t)(om - e_lo) * P;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          k.gS[j * P + p] = to_f32(xs[loc + p]);
+          xs[loc + p] = z;
+          xg[(uint64_t)om * P + p] = z;
+        }
+      };
+#pragma unroll
+      for (int i = 0; i < NSR; ++i) {
+        const uint64_t j = jc0 + tid + (uint64_t)NTH * i;
+        if (j < jc1) take(j, om_r[i]);
+      }
+      for (uint64_t j = jc0 + (uint64_t)NTH * NSR + tid; j < jc1; j += NTH) take(j, k.omega[j]);
+      lds_barrier();
+    }
 
     if (!REC) {
       // mode d: (A' = nta*I1, I = I2, B = 1) -> (nta*I1, R2, 1)
@@ -397,8 +430,9 @@ Geo2 plan(const ModeProd2& mp, uint32_t TA) {
   k.off_o = (uint32_t)off; off += al(TA * slab_out * 4);
   k.off_w0 = (uint32_t)off; off += mp.apply ? al(TA * slab_out * esw) : 0;
   k.off_w1 = (uint32_t)off; off += mp.apply ? al(TA * slab_out * esw) : 0;
-  k.off_r0 = (uint32_t)off; off += mp.apply ? 32 : 0;
-  k.off_r1 = (uint32_t)off; off += mp.apply ? 32 : 0;
+  const bool ranged = mp.apply || mp.gather_S;
+  k.off_r0 = (uint32_t)off; off += ranged ? 32 : 0;
+  k.off_r1 = (uint32_t)off; off += ranged ? 32 : 0;
   g.lds = off;
   const auto a16 = [](const void* p) { return ((uintptr_t)p) % 16 == 0; };
   k.dma_in = a16(mp.X) && (TA * slab_in * esx) % 16 == 0;
@@ -473,9 +507,11 @@ hipError_t launch_modeprod2(const ModeProd2& mp, int num_cu, hipStream_t s) {
   k.uS = mp.uS;
   k.omega = mp.omega;
   k.kS = mp.kS;
-  k.N = (uint64_t)mp.A * mp.R1 * mp.R2;
+  // elements the Omega ranks count over: the output (reconstruction), the input (projection)
+  k.N = (uint64_t)mp.A * (mp.recon ? (uint64_t)mp.R1 * mp.R2 : (uint64_t)mp.I1 * mp.I2);
   k.lr = mp.lr;
   k.has_sparse = mp.has_sparse;
+  k.gS = mp.recon ? nullptr : mp.gather_S;
   const size_t per_cu = g.lds ? (160 * 1024) / g.lds : 8;
   uint64_t occ = per_cu < 1 ? 1 : (per_cu > 8 ? 8 : per_cu);
   uint64_t grid = (uint64_t)(num_cu > 0 ? num_cu : 256) * occ;

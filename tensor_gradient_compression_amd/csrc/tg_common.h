@@ -136,6 +136,9 @@ struct ModeProd2 {
   float lr;
   int has_sparse;
   uint32_t force_ta;       // 0: choose the slabs per tile automatically
+  // projection only: also perform the COO gather on the staged input, S[j] = X[omega[j]]
+  // (fp32) and X[omega[j]] <- 0 in place (X is then the caller's writable gradient)
+  float* gather_S;
 };
 uint32_t modeprod2_tile(const ModeProd2& mp);   // 0: does not fit
 hipError_t launch_modeprod2(const ModeProd2& mp, int num_cu, hipStream_t s);

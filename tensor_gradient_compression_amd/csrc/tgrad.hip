@@ -508,13 +508,16 @@ int tgrad_step(tgrad_t* h, void* weight, void* grad, void* stream) {
     if (rc != TGRAD_OK) return rc;
   }
   const uint32_t P = h->P;
-  if (h->k > 0) {
-    Mark m(h, KID_GATHER);
-    HIPCHK(h, launch_gather(h->dtype, grad, h->omega, (uint32_t)h->k, h->S, s));
-  }
   // projection: one launch per group, last compressed mode first
   std::vector<std::vector<int>> proj, rec;
   build_chain(h, h->fuse, proj, rec);
+  // the COO gather runs on its own unless the first projection launch is the fused
+  // two-mode one, which takes S and zeroes Omega on its staged input
+  const bool gather_fused = h->k > 0 && !proj.empty() && proj[0].size() == 2;
+  if (h->k > 0 && !gather_fused) {
+    Mark m(h, KID_GATHER);
+    HIPCHK(h, launch_gather(h->dtype, grad, h->omega, (uint32_t)h->k, h->S, s));
+  }
   int64_t cur[TGRAD_MAX_NDIM];
   for (int i = 0; i < h->d; ++i) cur[i] = h->shape[i];
   const void* X = grad;
@@ -540,6 +543,14 @@ int tgrad_step(tgrad_t* h, void* weight, void* grad, void* stream) {
       mp.M1 = h->Mp[d - 2];
       mp.M2 = h->Mp[d - 1];
       mp.Y = Y;
+      if (j == 0 && gather_fused) {
+        mp.gather_S = h->S;
+        mp.mask = h->mask;
+        mp.rank = h->rank;
+        mp.omega = h->omega;
+        mp.kS = h->k;
+        mp.has_sparse = 1;
+      }
       {
         Mark m(h, KID_PROJECT_FUSED2);
         HIPCHK(h, launch_modeprod2(mp, h->num_cu, s));

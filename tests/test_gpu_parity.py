@@ -290,10 +290,11 @@ def test_timing_records_every_kernel():
     for _ in range(3):
         lib.step(W, dev(gs.next(), wl.dtype))
     rec = lib.timing_read()
-    for name in ("topk_hist", "topk_compact", "gather_residual", "modeprod2_project_first",
+    for name in ("topk_hist", "topk_compact", "modeprod2_project_first",
                  "modeprod_project", "adam_fused", "modeprod_reconstruct",
                  "modeprod2_reconstruct_apply", "gram", "eig_jacobi"):
         assert name in rec, name
+    assert "gather_residual" not in rec        # folded into the fused first projection
     assert rec["adam_fused"][0] == 3
     assert rec["modeprod2_project_first"][0] == 3
     assert rec["modeprod_project"][0] == 6
@@ -301,6 +302,7 @@ def test_timing_records_every_kernel():
     lib.step(W, dev(gs.next(), wl.dtype))
     rec = lib.timing_read()
     assert rec["modeprod_project_first"][0] == 1 and rec["modeprod_reconstruct_apply"][0] == 1
+    assert rec["gather_residual"][0] == 1
 
 
 # --------------------------------------------------------------------------- full size, config 4
