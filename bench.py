@@ -97,6 +97,10 @@ def kernel_bytes(wl):
         "modeprod2_reconstruct_apply": [rec2],
         "_flops_project": flops_proj,
         "_ncore": ncore,
+        # the step's work as one launch per kernel of the path, fp32 intermediates and no
+        # fusion: gather, projection chain, Adam, reconstruction chain with the apply
+        "_unfused_step": k * (4 + es + 4 * P + es) * (1 if k else 0) + sum(proj)
+                         + (ncore + k) * P * 24 + sum(rec),
     }
 
 
@@ -241,9 +245,14 @@ def main():
     roofline = {"kernel": dom, "bound": "hbm", "achieved": d["achieved_GBs"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(d["achieved_GBs"] / HBM_PEAK_GBS, 4),
                 "traffic": counter_traffic(dom)}
-    step_bytes = sum(sum(kb[name]) / len(kb[name]) * v["launches_per_step"]
-                     for name, v in kernels.items() if name in kb and kb[name])
+    # whole-step roofline: the step's algorithmic bytes counted kernel by kernel without
+    # fusion, over the measured step time; the bytes the launched (fused) kernels move
+    # are reported beside it
+    moved_bytes = sum(sum(kb[name]) / len(kb[name]) * v["launches_per_step"]
+                      for name, v in kernels.items() if name in kb and kb[name])
+    step_bytes = kb["_unfused_step"]
     step_frac = step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS
+    moved_frac = moved_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -271,6 +280,8 @@ def main():
         "refresh_ms": round(refresh_ms, 3),
         "step_alg_bytes": int(step_bytes),
         "step_hbm_frac": round(step_frac, 4),
+        "step_moved_bytes": int(moved_bytes),
+        "step_moved_hbm_frac": round(moved_frac, 4),
         "roofline": roofline,
         "kernels": kernels,
         "refresh_kernels": refresh_kernels,

@@ -157,6 +157,20 @@ int tgrad_mark_refreshed(tgrad_t *h);
  * agree to fp32 rounding; takes effect at the next step. */
 int tgrad_set_fusion(tgrad_t *h, int enable);
 
+/* ---------------------------------------------------------------- checkpoint.
+ * The optimizer state as one host byte string, to stop and resume training: the step
+ * count and refresh mark, Omega, every U(n) with its Gram eigenvalues, and the core and
+ * sparse Adam moments. tgrad_state_size gives its length (-1 for a NULL handle).
+ * tgrad_save_state writes it into `buf` (cap >= that size, host memory).
+ * tgrad_load_state restores it into a handle created with the same shape, Tucker ranks,
+ * dtype and sparse_ratio (hyper-parameters lr, betas, eps, T are the new handle's), after
+ * which steps continue exactly as they would have in the saved handle.
+ * Both synchronise the device. Errors: TGRAD_EINVAL (NULL, too small a buffer, a size,
+ * header, shape or Omega that does not match), TGRAD_EHIP. */
+int64_t tgrad_state_size(tgrad_t *h);
+int tgrad_save_state(tgrad_t *h, void *buf, int64_t cap);
+int tgrad_load_state(tgrad_t *h, const void *buf, int64_t size);
+
 /* ---------------------------------------------------------------- timing.
  * When enabled, every kernel launch of step/refresh is bracketed by HIP events on
  * the launch stream (at most max_records launches are kept). tgrad_timing_read

@@ -59,6 +59,9 @@ SIGNATURES = [
     ("tgrad_set_factor", ctypes.c_int, [_P, ctypes.c_int, _P, _I64]),
     ("tgrad_mark_refreshed", ctypes.c_int, [_P]),
     ("tgrad_set_fusion", ctypes.c_int, [_P, ctypes.c_int]),
+    ("tgrad_state_size", _I64, [_P]),
+    ("tgrad_save_state", ctypes.c_int, [_P, _P, _I64]),
+    ("tgrad_load_state", ctypes.c_int, [_P, _P, _I64]),
     ("tgrad_timing_enable", ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int]),
     ("tgrad_timing_read", ctypes.c_int, [_P, _P, _P, ctypes.c_int]),
     ("tgrad_kernel_name", ctypes.c_char_p, [ctypes.c_int]),
@@ -215,6 +218,18 @@ class TGrad:
             return False
         self._check(rc, "tgrad_set_fusion")
         return True
+
+    def save_state(self) -> bytes:
+        """The optimizer state as bytes (see tgrad_save_state)."""
+        n = int(self._lib.tgrad_state_size(self._h))
+        buf = np.zeros(max(n, 1), np.uint8)
+        self._check(self._lib.tgrad_save_state(self._h, _ptr(buf), n), "tgrad_save_state")
+        return buf[:n].tobytes()
+
+    def load_state(self, state: bytes):
+        """Restore a state written by save_state of a handle of the same shape."""
+        buf = np.frombuffer(state, np.uint8).copy()
+        self._check(self._lib.tgrad_load_state(self._h, _ptr(buf), buf.size), "tgrad_load_state")
 
     def mark_refreshed(self):
         self._check(self._lib.tgrad_mark_refreshed(self._h), "tgrad_mark_refreshed")

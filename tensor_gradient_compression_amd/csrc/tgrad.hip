@@ -758,6 +758,121 @@ int tgrad_set_factor(tgrad_t* h, int mode, const float* U, int64_t n_floats) {
   return TGRAD_OK;
 }
 
+// ---------------------------------------------------------------- checkpoint / resume
+// Layout: header, then Omega (k u32), per compressed mode (ascending) U(n) (I r P fp32)
+// and its eigenvalues (I fp64), then m_C, v_C (core P fp32 each), m_S, v_S (k P fp32
+// each). Membership mask, ranks and the MFMA operand matrices are rebuilt on load.
+namespace {
+struct CkptHeader {
+  char magic[8];
+  uint32_t version, dtype;
+  int64_t ndim;
+  int64_t shape[TGRAD_MAX_NDIM];
+  int64_t ranks[TGRAD_MAX_NDIM];
+  uint64_t k, ncore;
+  int64_t t, refreshed_for;
+};
+constexpr char kCkptMagic[8] = {'T', 'G', 'R', 'A', 'D', 'C', 'K', '1'};
+
+void ckpt_header(const tgrad_t* h, CkptHeader* c) {
+  std::memset(c, 0, sizeof(*c));
+  std::memcpy(c->magic, kCkptMagic, 8);
+  c->version = 1;
+  c->dtype = (uint32_t)h->dtype;
+  c->ndim = h->d;
+  for (int i = 0; i < h->d; ++i) {
+    c->shape[i] = h->shape[i];
+    c->ranks[i] = h->ranks[i];
+  }
+  c->k = h->k;
+  c->ncore = h->ncore;
+  c->t = h->t;
+  c->refreshed_for = h->refreshed_for;
+}
+
+// (device pointer, bytes) of every state array in checkpoint order
+std::vector<std::pair<void*, size_t>> ckpt_arrays(tgrad_t* h) {
+  std::vector<std::pair<void*, size_t>> a;
+  a.push_back({h->omega, (size_t)h->k * 4});
+  for (int n : h->fmodes) {
+    const size_t I = (size_t)h->shape[n], r = (size_t)h->ranks[n];
+    a.push_back({h->U[n], I * r * h->P * 4});
+    a.push_back({h->eig[n], I * 8});
+  }
+  const size_t nc = (size_t)h->ncore * h->P * 4, ns = (size_t)h->k * h->P * 4;
+  a.push_back({h->mC, nc});
+  a.push_back({h->vC, nc});
+  a.push_back({h->mS, ns});
+  a.push_back({h->vS, ns});
+  return a;
+}
+}  // namespace
+
+int64_t tgrad_state_size(tgrad_t* h) {
+  if (!h) return -1;
+  int64_t n = (int64_t)sizeof(CkptHeader);
+  for (auto& a : ckpt_arrays(h)) n += (int64_t)a.second;
+  return n;
+}
+
+int tgrad_save_state(tgrad_t* h, void* buf, int64_t cap) {
+  if (!h || !buf || cap < tgrad_state_size(h)) return TGRAD_EINVAL;
+  DevGuard g(h->device);
+  HIPCHK(h, hipDeviceSynchronize());
+  unsigned char* p = (unsigned char*)buf;
+  ckpt_header(h, (CkptHeader*)p);
+  p += sizeof(CkptHeader);
+  for (auto& a : ckpt_arrays(h)) {
+    if (a.second) HIPCHK(h, hipMemcpy(p, a.first, a.second, hipMemcpyDeviceToHost));
+    p += a.second;
+  }
+  return TGRAD_OK;
+}
+
+int tgrad_load_state(tgrad_t* h, const void* buf, int64_t size) {
+  if (!h || !buf || size != tgrad_state_size(h)) return TGRAD_EINVAL;
+  CkptHeader mine, theirs;
+  ckpt_header(h, &mine);
+  std::memcpy(&theirs, buf, sizeof(theirs));
+  if (std::memcmp(theirs.magic, mine.magic, 8) != 0 || theirs.version != mine.version ||
+      theirs.dtype != mine.dtype || theirs.ndim != mine.ndim || theirs.k != mine.k ||
+      theirs.ncore != mine.ncore ||
+      std::memcmp(theirs.shape, mine.shape, sizeof(mine.shape)) != 0 ||
+      std::memcmp(theirs.ranks, mine.ranks, sizeof(mine.ranks)) != 0 || theirs.t < 0)
+    return TGRAD_EINVAL;
+  const unsigned char* p = (const unsigned char*)buf + sizeof(CkptHeader);
+  // Omega must be ascending and in range, as tgrad_set_omega requires
+  const uint32_t* om = (const uint32_t*)p;
+  for (uint64_t j = 0; j < h->k; ++j) {
+    uint32_t x;
+    std::memcpy(&x, om + j, 4);
+    uint32_t prev = 0;
+    if (j) std::memcpy(&prev, om + j - 1, 4);
+    if ((uint64_t)x >= h->N || (j && x <= prev)) return TGRAD_EINVAL;
+  }
+  DevGuard g(h->device);
+  HIPCHK(h, hipDeviceSynchronize());
+  for (auto& a : ckpt_arrays(h)) {
+    if (a.second) HIPCHK(h, hipMemcpy(a.first, p, a.second, hipMemcpyHostToDevice));
+    p += a.second;
+  }
+  HIPCHK(h, launch_mask_from_omega(h->omega, (uint32_t)h->k, h->mask, h->rank, h->nwords,
+                                   nullptr));
+  for (int n : h->fmodes) {
+    const uint32_t I = (uint32_t)h->shape[n], r = (uint32_t)h->ranks[n];
+    const size_t nu = (size_t)I * r * h->P;
+    std::vector<float> U(nu), mp(nu * h->P), mr(nu * h->P);
+    HIPCHK(h, hipMemcpy(U.data(), h->U[n], nu * 4, hipMemcpyDeviceToHost));
+    host_operands(I, r, h->P, U.data(), mp.data(), mr.data());
+    HIPCHK(h, hipMemcpy(h->Mp[n], mp.data(), mp.size() * 4, hipMemcpyHostToDevice));
+    HIPCHK(h, hipMemcpy(h->Mr[n], mr.data(), mr.size() * 4, hipMemcpyHostToDevice));
+  }
+  HIPCHK(h, hipDeviceSynchronize());
+  h->t = theirs.t;
+  h->refreshed_for = theirs.refreshed_for;
+  return TGRAD_OK;
+}
+
 int tgrad_set_fusion(tgrad_t* h, int enable) {
   if (!h) return TGRAD_EINVAL;
   if (enable && !h->can_fuse) return TGRAD_EINVAL;

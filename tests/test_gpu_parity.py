@@ -281,6 +281,46 @@ def test_misaligned_grad_is_rejected():
     assert lib.t == 1
 
 
+@pytest.mark.parametrize("name,wl", [("config1", CONFIGS[1]),
+                                     ("c64-small", custom((12, 10, 9), "c64", (5, 4, 3), 0.05, T=3, steps=7))],
+                         ids=lambda x: x if isinstance(x, str) else "")
+def test_checkpoint_resume_is_exact(name, wl):
+    """Save after n1 steps, restore into a fresh handle, continue across a refresh:
+    weights, moments, Omega, factors and the step count match an uninterrupted run bit
+    for bit. A state for another shape is refused."""
+    n1, n2 = 4, 5
+    gs = GradStream(wl, seed=5)
+    grads = [gs.next() for _ in range(n1 + n2)]
+    W0 = init_weights(wl, seed=5)
+    a = make_lib(wl, T=4)
+    Wa = dev(W0, wl.dtype)
+    for g in grads:
+        a.step(Wa, dev(g, wl.dtype))
+    b = make_lib(wl, T=4)
+    Wb = dev(W0, wl.dtype)
+    for g in grads[:n1]:
+        b.step(Wb, dev(g, wl.dtype))
+    state = b.save_state()
+    b.close()
+    c = make_lib(wl, T=4)
+    c.load_state(state)
+    assert c.t == n1
+    for g in grads[n1:]:
+        c.step(Wb, dev(g, wl.dtype))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(Wa, wl.dtype).view(np.uint8), host(Wb, wl.dtype).view(np.uint8))
+    for x, y in zip(a.get_moments(), c.get_moments()):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    assert np.array_equal(a.get_omega(), c.get_omega())
+    for n, (I, r) in enumerate(zip(wl.shape, wl.ranks)):
+        if r < I:
+            assert np.array_equal(a.get_factor(n).view(np.uint32), c.get_factor(n).view(np.uint32))
+    assert a.t == c.t == n1 + n2
+    other = tg.TGrad(tuple(x + 1 for x in wl.shape), wl.ranks, wl.dtype, wl.sparse_ratio, 4)
+    with pytest.raises(tg.TGradError, match="invalid argument"):
+        other.load_state(state)
+
+
 def test_timing_records_every_kernel():
     wl = CONFIGS[1]
     lib = make_lib(wl)
