@@ -136,6 +136,46 @@ def select_omega(keys: np.ndarray, k: int) -> np.ndarray:
     return np.sort(order[:k]).astype(np.uint32)
 
 
+SPLITMIX_GAMMA = 0x9E3779B97F4A7C15
+
+
+def splitmix64(z: np.ndarray) -> np.ndarray:
+    """The SplitMix64 output function (Steele, Lea and Flood, "Fast splittable
+    pseudorandom number generators", 2014; the 64-bit finaliser of Stafford's Mix13)
+    applied to states z (uint64, arithmetic modulo 2^64)."""
+    z = np.asarray(z, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+    return z ^ (z >> np.uint64(31))
+
+
+def randk_keys(N: int, seed: int, t: int) -> np.ndarray:
+    """Random-sampling keys for Omega (pith.science "What carries the argument": Omega is
+    re-selected by top-k magnitude or by random sampling). Element e of the refresh that
+    serves step t gets the top 31 bits of the SplitMix64 output for the state
+    seed + gamma * (t * 2^32 + e + 1); Omega is then the k largest keys with ties to the
+    lowest index, exactly as for magnitudes, i.e. a uniformly random k-subset."""
+    e = np.arange(N, dtype=np.uint64)
+    ctr = (np.uint64(t) << np.uint64(32)) + e + np.uint64(1)
+    with np.errstate(over="ignore"):
+        z = np.uint64(seed) + np.uint64(SPLITMIX_GAMMA) * ctr
+    return splitmix64(z) >> np.uint64(33)
+
+
+def remap_moments(omega_old: np.ndarray, omega_new: np.ndarray, m: np.ndarray, P: int) -> np.ndarray:
+    """Sparse moments after a refresh when they follow their index: entry j of the new
+    Omega takes the moments of the same element in the old Omega, or zero if it was not
+    there (the alternative to keeping them by position)."""
+    out = np.zeros(len(omega_new) * P, np.float32)
+    pos = {int(x): i for i, x in enumerate(omega_old)}
+    for j, x in enumerate(omega_new):
+        i = pos.get(int(x))
+        if i is not None:
+            out[j * P:(j + 1) * P] = m[i * P:(i + 1) * P]
+    return out
+
+
 def gather(G32: np.ndarray, omega: np.ndarray) -> np.ndarray:
     """S = G restricted to Omega, in Omega's order [NT 三: sparse part first]."""
     return np.ascontiguousarray(G32).reshape(-1)[omega.astype(np.int64)].copy()
@@ -271,7 +311,8 @@ class TGradOracle:
     steps, Omega re-selected every T steps].
     step(W, G): returns the new W (storage dtype) [NT 三 step order; PITH Theorem 2]."""
 
-    def __init__(self, shape, ranks, dtype, sparse_ratio, T, lr, beta1, beta2, eps):
+    def __init__(self, shape, ranks, dtype, sparse_ratio, T, lr, beta1, beta2, eps,
+                 weight_decay=0.0, sparse_scale=1.0, selection="topk", remap=False, seed=0):
         self.shape = tuple(int(s) for s in shape)
         self.ranks = tuple(int(r) for r in ranks)
         if dtype not in DTYPES:
@@ -295,14 +336,33 @@ class TGradOracle:
         self.t = 0
         self.refreshed_for = 0
         self.last = {}
+        # variants (defaults reproduce the plain method bit for bit)
+        self.weight_decay = float(weight_decay)   # decoupled, AdamW style
+        self.sparse_scale = float(sparse_scale)   # lambda in Delta[Omega] += lambda N_S
+        if selection not in ("topk", "randk"):
+            raise ValueError(selection)
+        self.selection = selection
+        self.remap = bool(remap)
+        self.seed = int(seed)
 
     def refresh_due(self, t: int) -> bool:
         return (t - 1) % self.T == 0
 
-    def refresh(self, G: np.ndarray):
-        """Sparse first, then HOSVD of the residual [NT 三; PITH "Core claim"]."""
+    def refresh(self, G: np.ndarray, serves: int = None):
+        """Sparse first, then HOSVD of the residual [NT 三; PITH "Core claim"]. `serves` is
+        the step the new Omega and factors are first used in (default: the next one)."""
+        if serves is None:
+            serves = self.t + 1
         G = np.asarray(G).reshape(self.shape)
-        self.omega = select_omega(topk_keys(G, self.dtype), self.k)
+        old = self.omega
+        if self.selection == "topk":
+            keys = topk_keys(G, self.dtype)
+        else:
+            keys = randk_keys(self.N, self.seed, serves)
+        self.omega = select_omega(keys, self.k)
+        if self.remap:
+            self.mS = remap_moments(old, self.omega, self.mS, self.P)
+            self.vS = remap_moments(old, self.omega, self.vS, self.P)
         R = residual(decode(G, self.dtype), self.omega)
         for n, (I, r) in enumerate(zip(self.shape, self.ranks)):
             if r >= I:
@@ -312,7 +372,7 @@ class TGradOracle:
             else:
                 U, w, gap = hosvd_factor(R, n, r)
                 self.factors[n], self.eigvals[n], self.gaps[n] = U, w, gap
-        self.refreshed_for = self.t + 1
+        self.refreshed_for = serves
 
     def step(self, W: np.ndarray, G: np.ndarray) -> np.ndarray:
         W = np.asarray(W).reshape(self.shape)
@@ -320,7 +380,7 @@ class TGradOracle:
         self.t += 1
         t = self.t
         if self.refresh_due(t) and self.refreshed_for != t:
-            self.refresh(G)
+            self.refresh(G, t)
         G32 = decode(G, self.dtype)
         S = gather(G32, self.omega)
         R = residual(G32, self.omega)
@@ -336,9 +396,12 @@ class TGradOracle:
         Dr = real_view(D).copy()                        # fp32 (re, im interleaved)
         if self.k:
             Dr2 = Dr.reshape(-1, self.P)
-            Dr2[self.omega.astype(np.int64)] += uS.reshape(-1, self.P)   # lambda = 1
+            Dr2[self.omega.astype(np.int64)] += np.float32(self.sparse_scale) * uS.reshape(-1, self.P)
         W32 = real_view(decode(W, self.dtype)).copy()
-        W32 = W32 - np.float32(self.lr) * Dr
+        # decoupled weight decay folded into the one rounding: W (1 - lr wd) - lr Delta, the
+        # factor formed in fp64 and rounded to fp32 (exactly 1 without decay)
+        decay = np.float32(1.0 - self.lr * self.weight_decay)
+        W32 = W32 * decay - np.float32(self.lr) * Dr
         if self.P == 2:
             Wn = encode(W32.view(np.complex64), self.dtype)
         else:

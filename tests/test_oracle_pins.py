@@ -442,9 +442,9 @@ def test_refresh_schedule_every_T():
     calls = []
     orig = o.refresh
 
-    def spy(G):
+    def spy(G, serves=None):
         calls.append(o.t)
-        orig(G)
+        orig(G, serves)
     o.refresh = spy
     gs, W = GradStream(wl), init_weights(wl)
     for _ in range(10):
@@ -461,3 +461,186 @@ def test_moments_persist_across_refresh():
     m_before = o.mC.copy()
     o.refresh(gs.next())
     assert np.array_equal(o.mC, m_before) and o.t == 2
+
+
+# --------------------------------------------------------------------------- variants
+
+def test_splitmix64_reference_outputs():
+    """The rand-k keys at step counter 0 are the published SplitMix64 stream >> 33."""
+    with open(os.path.join(GOLDEN, "splitmix64.json")) as f:
+        fx = json.load(f)
+    ref = np.array([int(x) for x in fx["outputs"]], np.uint64)
+    keys = O.randk_keys(len(ref), fx["seed"], 0)
+    assert np.array_equal(keys, ref >> np.uint64(33))
+
+
+def test_randk_is_a_uniform_subset_independent_of_g():
+    """Random-sampling Omega: k distinct ascending indices, the same for any gradient,
+    different per refresh step and seed, and every element equally likely (chi-square
+    over 400 draws of 100 out of 1000, far inside the 1e-6 tail)."""
+    N, k = 1000, 100
+    o1 = O.TGradOracle((10, 10, 10), (10, 10, 10), "f32", k / N, 1, 1e-3, 0.9, 0.999, 1e-8,
+                       selection="randk", seed=7)
+    o2 = O.TGradOracle((10, 10, 10), (10, 10, 10), "f32", k / N, 1, 1e-3, 0.9, 0.999, 1e-8,
+                       selection="randk", seed=7)
+    r = rng(50)
+    o1.refresh(r.standard_normal((10, 10, 10)).astype(np.float32))
+    o2.refresh(np.zeros((10, 10, 10), np.float32))
+    assert np.array_equal(o1.omega, o2.omega)
+    assert len(o1.omega) == k and np.all(np.diff(o1.omega.astype(np.int64)) > 0)
+    counts = np.zeros(N)
+    seen = set()
+    for t in range(400):
+        om = O.select_omega(O.randk_keys(N, 3 + (t % 2), t // 2), k)
+        seen.add(om.tobytes())
+        counts[om.astype(np.int64)] += 1
+    assert len(seen) == 400
+    expect = 400 * k / N
+    chi2 = float(((counts - expect) ** 2 / expect).sum())
+    # chi-square with 999 dof: mean 999, sd ~ 44.7; hypergeometric draws shrink it by 0.9
+    assert 600 < chi2 < 1300, chi2
+
+
+def test_randk_ties_go_to_the_lowest_index():
+    """31-bit keys can collide; select_omega breaks ties by index, checked by brute force
+    on keys forced to collide (N = 2^16 elements, keys reduced to 4 bits)."""
+    keys = O.randk_keys(1 << 16, 11, 3) >> np.uint64(27)
+    k = 5000
+    om = O.select_omega(keys, k)
+    order = sorted(range(len(keys)), key=lambda e: (-int(keys[e]), e))[:k]
+    assert np.array_equal(om, np.array(sorted(order), np.uint32))
+
+
+def _torch_adamw_run(W0, grads, wl, wd):
+    p = torch.nn.Parameter(torch.from_numpy(O.decode(W0, wl.dtype).copy()))
+    opt = torch.optim.AdamW([p], lr=wl.lr, betas=wl.betas, eps=wl.eps, weight_decay=wd,
+                            foreach=False)
+    for g in grads:
+        p.grad = torch.from_numpy(O.decode(g, wl.dtype).copy())
+        opt.step()
+    return p.detach().numpy()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "c64"])
+def test_weight_decay_reduces_to_adamw(dtype):
+    """With full ranks and k = 0 the decayed method is AdamW (decoupled decay,
+    W <- W (1 - lr wd) - lr u), checked against torch.optim.AdamW over 10 steps."""
+    shape = (6, 5, 4, 3)
+    wl = custom(shape, dtype, shape, 0.0, T=5, steps=10, lr=3e-2)
+    gs = GradStream(wl, seed=22)
+    W = init_weights(wl, seed=22) * 10
+    grads = [gs.next() for _ in range(10)]
+    o = O.TGradOracle(shape, shape, dtype, 0.0, 5, wl.lr, *wl.betas, wl.eps, weight_decay=0.5)
+    Wo = W
+    for g in grads:
+        Wo = o.step(Wo, g)
+    ref = _torch_adamw_run(W, grads, wl, 0.5)
+    ref0 = _torch_adam_run(W, grads, wl)
+    got = O.decode(Wo, dtype)
+    assert np.abs(ref - ref0).max() > 100 * np.abs(got - ref).max()   # decay is visible
+    rel = np.abs(got - ref).max() / np.abs(ref).max()
+    assert rel <= 1e-6, rel
+
+
+def test_sparse_scale_is_a_learning_rate_on_the_sparse_part():
+    """rho = 1 puts the whole gradient in the sparse part, so the update is lambda * lr
+    times Adam's: the oracle with lambda = 0.25 matches torch.optim.Adam at lr / 4, and
+    lambda = 0 leaves W unchanged."""
+    shape = (6, 5, 4)
+    wl = custom(shape, "f32", shape, 1.0, T=3, steps=8, lr=4e-3)
+    gs = GradStream(wl, seed=23)
+    W = init_weights(wl, seed=23)
+    grads = [gs.next() for _ in range(8)]
+    o = O.TGradOracle(shape, (3, 2, 2), "f32", 1.0, 3, wl.lr, *wl.betas, wl.eps,
+                      sparse_scale=0.25)
+    z = O.TGradOracle(shape, (3, 2, 2), "f32", 1.0, 3, wl.lr, *wl.betas, wl.eps,
+                      sparse_scale=0.0)
+    Wo, Wz = W, W
+    for g in grads:
+        Wo, Wz = o.step(Wo, g), z.step(Wz, g)
+    assert np.array_equal(Wz, W)
+    ref = _torch_adam_run(W, grads, custom(shape, "f32", shape, 1.0, lr=1e-3))
+    rel = np.abs(O.decode(Wo, "f32") - ref).max() / np.abs(ref - W).max()
+    assert rel <= 1e-5, rel
+
+
+def test_remapped_moments_follow_their_element():
+    """With remapped sparse moments, an element that stays in Omega across refreshes keeps
+    the Adam moments of its own gradient sequence (torch.optim.Adam on that element
+    alone), while Omega's other members change and shift its position; keeping moments
+    by position instead gives it another element's history. Elements new to Omega start
+    from zero."""
+    shape = (8, 8, 8)
+    N = 512
+    r = rng(60)
+    stay = np.array([40, 300, 301], np.int64)
+    T, steps = 3, 10
+    grads = []
+    for t in range(steps):
+        g = 1e-3 * r.standard_normal(N).astype(np.float32)
+        g[stay] = 5.0 + r.standard_normal(3).astype(np.float32)
+        # three more outliers, moved every refresh period
+        mv = np.random.default_rng(100 + t // T).choice(np.setdiff1d(np.arange(N), stay), 3,
+                                                        replace=False)
+        g[mv] = 4.0 + r.standard_normal(3).astype(np.float32)
+        grads.append(g.reshape(shape))
+    rho = 6 / N
+    kw = dict(selection="topk")
+    on = O.TGradOracle(shape, (4, 4, 4), "f32", rho, T, 1e-3, 0.9, 0.999, 1e-8, remap=True, **kw)
+    off = O.TGradOracle(shape, (4, 4, 4), "f32", rho, T, 1e-3, 0.9, 0.999, 1e-8, **kw)
+    W = np.zeros(shape, np.float32)
+    Wa, Wb = W, W
+    p = torch.nn.Parameter(torch.zeros(3))
+    opt = torch.optim.Adam([p], lr=1e-3, betas=(0.9, 0.999), eps=1e-8, foreach=False)
+    moved_new = 0
+    for t, g in enumerate(grads, 1):
+        old = on.omega.copy()
+        Wa, Wb = on.step(Wa, g), off.step(Wb, g)
+        if (t - 1) % T == 0 and t > 1:
+            new_pos = [j for j, e in enumerate(on.omega) if e not in set(old.tolist())]
+            moved_new += len(new_pos)
+            # an element new to Omega had zero moments before this step's update: its
+            # first moment is now exactly (1 - beta1) g
+            for j in new_pos:
+                e = int(on.omega[j])
+                assert on.mS[j] == np.float32(1.0 - 0.9) * g.reshape(-1)[e]
+        p.grad = torch.from_numpy(g.reshape(-1)[stay].copy())
+        opt.step()
+        st = opt.state[p]
+        pos = np.searchsorted(on.omega, stay)
+        assert np.array_equal(on.omega[pos], stay.astype(np.uint32))
+        np.testing.assert_allclose(on.mS[pos], st["exp_avg"].numpy(), rtol=1e-6)
+        np.testing.assert_allclose(on.vS[pos], st["exp_avg_sq"].numpy(), rtol=1e-6)
+    assert moved_new > 0
+    pos = np.searchsorted(off.omega, stay)
+    assert not np.allclose(off.mS[pos], opt.state[p]["exp_avg"].numpy(), rtol=1e-3)
+
+
+def test_variant_defaults_are_the_plain_method():
+    wl = custom((8, 7, 6), "bf16", (4, 3, 3), 0.05, T=2)
+    a = O.TGradOracle(wl.shape, wl.ranks, "bf16", 0.05, 2, wl.lr, *wl.betas, wl.eps)
+    b = O.TGradOracle(wl.shape, wl.ranks, "bf16", 0.05, 2, wl.lr, *wl.betas, wl.eps,
+                      weight_decay=0.0, sparse_scale=1.0, selection="topk", remap=False, seed=9)
+    gs, W = GradStream(wl, seed=4), init_weights(wl, seed=4)
+    Wa, Wb = W, W
+    for _ in range(5):
+        g = gs.next()
+        Wa, Wb = a.step(Wa, g), b.step(Wb, g)
+        assert np.array_equal(Wa, Wb)
+
+
+def test_refresh_every_step_when_T_is_one():
+    """T = 1: Omega and the factors are recomputed at every step."""
+    wl = custom((6, 5, 4), "f32", (3, 3, 2), 0.05, T=1)
+    o = O.TGradOracle(wl.shape, wl.ranks, "f32", 0.05, 1, wl.lr, *wl.betas, wl.eps)
+    calls = []
+    orig = o.refresh
+
+    def spy(G, serves=None):
+        calls.append(serves)
+        orig(G, serves)
+    o.refresh = spy
+    gs, W = GradStream(wl), init_weights(wl)
+    for _ in range(4):
+        W = o.step(W, gs.next())
+    assert calls == [1, 2, 3, 4]
