@@ -157,6 +157,42 @@ int tgrad_mark_refreshed(tgrad_t *h);
  * agree to fp32 rounding; takes effect at the next step. */
 int tgrad_set_fusion(tgrad_t *h, int enable);
 
+/* ---------------------------------------------------------------- variants.
+ * Choices the method leaves open, as options of a handle (defaults: the plain method,
+ * bit for bit):
+ *   weight_decay   decoupled decay as in AdamW (the nullthought summary trains L and S
+ *                  with AdamW; the pith.science page's experiment settings use weight
+ *                  decay 1e-4 and 2e-6): W <- round(fp32(W) * decay - lr * Delta) with
+ *                  decay = fp32(1 - lr * weight_decay) formed in fp64. >= 0; default 0.
+ *   sparse_scale   lambda, the sparse scale factor the pith.science page lists among the
+ *                  method's hyper-parameters (its value is not reported): Delta at Omega
+ *                  gets fp32(lambda) * N_S instead of N_S. Finite; default 1.
+ *   selection      how a refresh picks Omega (pith.science "What carries the argument":
+ *                  top-k magnitude or random sampling): TGRAD_SELECT_TOPK, or
+ *                  TGRAD_SELECT_RANDK = a uniformly random k-subset: element e gets the top
+ *                  31 bits of SplitMix64's output for the state
+ *                  seed + 0x9E3779B97F4A7C15 * (t * 2^32 + e + 1), t the step the refresh
+ *                  serves, and the k largest keys (ties to the lowest index) are taken.
+ *   remap_moments  0 (default): the sparse Adam moments stay with their position in
+ *                  Omega across a refresh; 1: they follow their element, and an element
+ *                  new to Omega starts from zero moments. Enabling it allocates two more
+ *                  k*P fp32 buffers and a second bitmask (synchronises the device).
+ *   seed           rand-k base seed.
+ * Options take effect at the next step or refresh. Errors: TGRAD_EINVAL (NULL, a
+ * negative or non-finite weight_decay, a non-finite sparse_scale, an unknown selection or
+ * remap value), TGRAD_ENOMEM, TGRAD_EHIP. */
+enum tgrad_selection { TGRAD_SELECT_TOPK = 0, TGRAD_SELECT_RANDK = 1 };
+typedef struct tgrad_options {
+  double weight_decay;
+  double sparse_scale;
+  int32_t selection;
+  int32_t remap_moments;
+  uint64_t seed;
+} tgrad_options;
+void tgrad_default_options(tgrad_options *out);
+int tgrad_set_options(tgrad_t *h, const tgrad_options *opt);
+int tgrad_get_options(const tgrad_t *h, tgrad_options *out);
+
 /* ---------------------------------------------------------------- checkpoint.
  * The optimizer state as one host byte string, to stop and resume training: the step
  * count and refresh mark, Omega, every U(n) with its Gram eigenvalues, and the core and

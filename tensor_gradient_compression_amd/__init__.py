@@ -37,6 +37,16 @@ class Info(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_int64)]
 
 
+SELECT_TOPK, SELECT_RANDK = 0, 1
+SELECTIONS = {"topk": SELECT_TOPK, "randk": SELECT_RANDK}
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("weight_decay", ctypes.c_double), ("sparse_scale", ctypes.c_double),
+                ("selection", ctypes.c_int32), ("remap_moments", ctypes.c_int32),
+                ("seed", ctypes.c_uint64)]
+
+
 # (name, restype, argtypes) of every exported symbol declared in include/tgrad.h
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -59,6 +69,9 @@ SIGNATURES = [
     ("tgrad_set_factor", ctypes.c_int, [_P, ctypes.c_int, _P, _I64]),
     ("tgrad_mark_refreshed", ctypes.c_int, [_P]),
     ("tgrad_set_fusion", ctypes.c_int, [_P, ctypes.c_int]),
+    ("tgrad_default_options", None, [ctypes.POINTER(Options)]),
+    ("tgrad_set_options", ctypes.c_int, [_P, ctypes.POINTER(Options)]),
+    ("tgrad_get_options", ctypes.c_int, [_P, ctypes.POINTER(Options)]),
     ("tgrad_state_size", _I64, [_P]),
     ("tgrad_save_state", ctypes.c_int, [_P, _P, _I64]),
     ("tgrad_load_state", ctypes.c_int, [_P, _P, _I64]),
@@ -209,6 +222,22 @@ class TGrad:
         else:
             flat = np.ascontiguousarray(U, dtype=np.float32).reshape(-1)
         self._check(self._lib.tgrad_set_factor(self._h, mode, _ptr(flat), flat.size), "tgrad_set_factor")
+
+    def set_options(self, weight_decay: float = 0.0, sparse_scale: float = 1.0,
+                    selection: str = "topk", remap_moments: bool = False, seed: int = 0):
+        """Variants of the method (include/tgrad.h, tgrad_options): decoupled weight decay,
+        the sparse scale factor lambda, rand-k selection of Omega, and sparse moments that
+        follow their element across a refresh. The defaults are the plain method."""
+        o = Options(float(weight_decay), float(sparse_scale), SELECTIONS[selection],
+                    int(bool(remap_moments)), int(seed) & 0xFFFFFFFFFFFFFFFF)
+        self._check(self._lib.tgrad_set_options(self._h, ctypes.byref(o)), "tgrad_set_options")
+
+    def get_options(self) -> dict:
+        o = Options()
+        self._check(self._lib.tgrad_get_options(self._h, ctypes.byref(o)), "tgrad_get_options")
+        sel = {v: k for k, v in SELECTIONS.items()}[o.selection]
+        return dict(weight_decay=o.weight_decay, sparse_scale=o.sparse_scale, selection=sel,
+                    remap_moments=bool(o.remap_moments), seed=o.seed)
 
     def set_fusion(self, enable: bool) -> bool:
         """Select fused two-mode launches (True) or one launch per mode; returns False

@@ -7,10 +7,12 @@
 //                 mixed precision: optimizer state stays fp32; pith.science: Adam
 //                 moments live on the core). Operation order, each rounded to fp32:
 //                 m = b1*m + (1-b1)*g; v = b2*v + (1-b2)*(g*g);
-//                 u = (m/bc1) / (sqrt(v/bc2) + eps). The library is built without
+//                 u = (m/bc1) / (sqrt(v/bc2) + eps); the sparse output is then scaled
+//                 by lambda (1 for the plain method, an exact identity). The library is built without
 //                 floating-point contraction, so no step is fused into an FMA.
 //   apply_dense:  the update when no mode is compressed (every r_n = I_n): Delta =
-//                 N_C, plus N_S at Omega, W <- round(W - lr * Delta).
+//                 N_C, plus N_S at Omega, W <- round(W * decay - lr * Delta), decay =
+//                 fp32(1 - lr * weight_decay) (decoupled decay, exactly 1 without it).
 #include "tg_common.h"
 
 namespace tg {
@@ -61,7 +63,7 @@ __global__ void __launch_bounds__(256) k_adam(const CT* __restrict__ gc, float* 
     } else {
       const uint64_t j = i - nc;
       float m = ms[j], v = vs[j];
-      S[j] = adam_one(S[j], m, v, a);
+      S[j] = a.lam * adam_one(S[j], m, v, a);
       ms[j] = m;
       vs[j] = v;
     }
@@ -74,7 +76,8 @@ __global__ void __launch_bounds__(256) k_apply_dense(WT* __restrict__ W,
                                                      const uint64_t* __restrict__ mask,
                                                      const uint32_t* __restrict__ rank,
                                                      const float* __restrict__ us, uint64_t N,
-                                                     float lr, int has_sparse) {
+                                                     float lr, float decay,
+                                                     int has_sparse) {
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   for (uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; e < N; e += stride) {
     float d[P];
@@ -91,7 +94,7 @@ __global__ void __launch_bounds__(256) k_apply_dense(WT* __restrict__ W,
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const float w = to_f32(W[e * P + p]);
-      W[e * P + p] = from_f32<WT>(w - lr * d[p]);
+      W[e * P + p] = from_f32<WT>(w * decay - lr * d[p]);
     }
   }
 }
@@ -139,24 +142,24 @@ hipError_t launch_adam(int core_dt, const void* g_core, float* u_core, float* m_
 
 hipError_t launch_apply_dense(int dt, void* W, const float* u_core, const uint64_t* mask,
                               const uint32_t* rank, const float* u_s, uint64_t N, float lr,
-                              int has_sparse, hipStream_t s) {
+                              float decay, int has_sparse, hipStream_t s) {
   const unsigned b = grid_for(N, 256, 8192);
   switch (dt) {
     case DT_F32:
       k_apply_dense<float, 1><<<b, 256, 0, s>>>((float*)W, u_core, mask, rank, u_s, N, lr,
-                                                has_sparse);
+                                                decay, has_sparse);
       break;
     case DT_F16:
       k_apply_dense<_Float16, 1><<<b, 256, 0, s>>>((_Float16*)W, u_core, mask, rank, u_s, N, lr,
-                                                   has_sparse);
+                                                   decay, has_sparse);
       break;
     case DT_BF16:
       k_apply_dense<bf16_t, 1><<<b, 256, 0, s>>>((bf16_t*)W, u_core, mask, rank, u_s, N, lr,
-                                                 has_sparse);
+                                                 decay, has_sparse);
       break;
     case DT_C64:
       k_apply_dense<float, 2><<<b, 256, 0, s>>>((float*)W, u_core, mask, rank, u_s, N, lr,
-                                                has_sparse);
+                                                decay, has_sparse);
       break;
     default: return hipErrorInvalidValue;
   }

@@ -25,7 +25,7 @@
 //  * the output tile is staged in LDS (fp32) and written out in memory order with
 //    16-byte stores.
 // Epilogues: store (fp32 intermediate or core) or apply (last reconstruction):
-// W <- round(W - lr * (acc + N_S at Omega)); the W tile is transferred with the input
+// W <- round(W * decay - lr * (acc + N_S at Omega)); the W tile is transferred with the input
 // tile. When the output tile is one contiguous element range its Omega entries are one
 // contiguous range of the sorted Omega list, added into the staged tile; otherwise each
 // output looks up its membership bit and rank (nullthought summary section 3: the
@@ -67,6 +67,7 @@ struct MPK {
   uint32_t vout;           // 16-byte output stores usable
   uint32_t off_x0, off_x1, off_y, off_w0, off_w1;   // LDS byte offsets of the buffers
   float lr;
+  float decay;   // fp32(1 - lr * weight_decay): 1 exactly without decay
   int has_sparse;
 };
 
@@ -365,7 +366,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod(MPK k) {
           d = d + k.uS[jpos * P + (gi % P)];
         }
       }
-      return w - k.lr * d;
+      return w * k.decay - k.lr * d;
     };
     const uint32_t nseg_o = k.wide ? k.R : 1u;
     const uint32_t seg_o = k.wide ? TW : gc.len_out;          // values per segment slot
@@ -562,6 +563,7 @@ hipError_t launch_modeprod(const ModeProd& mp, int num_cu, hipStream_t s) {
   k.off_w0 = g.off_w0;
   k.off_w1 = g.off_w1;
   k.lr = mp.lr;
+  k.decay = mp.decay;
   k.has_sparse = mp.has_sparse;
   // persistent grid: every CU filled several times over
   const size_t per_cu = g.lds ? (160 * 1024) / g.lds : 8;

@@ -12,7 +12,7 @@
 //                   Z[a, j1, j2] = sum_i1 M1[j1, i1] Y[a, i1, j2]       (mode d-1)
 //   reconstruction: Y[a, i1, j2] = sum_j1 M1[i1, j1] Z[a, j1, j2]       (mode d-1)
 //                   O[a, i1, i2] = sum_j2 M2[i2, j2] Y[a, i1, j2]       (mode d)
-//                   W <- round(W - lr * (O + N_S at Omega))
+//                   W <- round(W * decay - lr * (O + N_S at Omega))
 // (indices include the complex part p, as in the one-mode kernel). Each product is an
 // MFMA GEMM over LDS operands (v_mfma_f32_16x16x4_f32, fp32 accumulation). Input tiles
 // (and W tiles) move HBM -> LDS with 16-byte global_load_lds transfers, double
@@ -54,6 +54,7 @@ struct MP2K {
   uint32_t dma_in, dma_w, vout;
   uint32_t off_m2, off_x0, off_x1, off_y, off_o, off_w0, off_w1, off_r0, off_r1;
   float lr;
+  float decay;            // fp32(1 - lr * weight_decay): 1 exactly without decay
   int has_sparse;
   float* gS;              // projection with the COO gather folded in (else null)
 };
@@ -369,7 +370,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
           const WT* ws = (const WT*)&wraw;
           WT wv[VO];
 #pragma unroll
-          for (int e = 0; e < VO; ++e) wv[e] = from_f32<WT>(to_f32(ws[e]) - k.lr * d[e]);
+          for (int e = 0; e < VO; ++e) wv[e] = from_f32<WT>(to_f32(ws[e]) * k.decay - k.lr * d[e]);
           *(uint4*)((WT*)k.W + gbase + off) = *(const uint4*)wv;
         }
       }
@@ -379,7 +380,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
           k.Y[gbase + q] = sO[q];
         } else {
           const float w = to_f32(((const WT*)bw)[q]);
-          ((WT*)k.W)[gbase + q] = from_f32<WT>(w - k.lr * sO[q]);
+          ((WT*)k.W)[gbase + q] = from_f32<WT>(w * k.decay - k.lr * sO[q]);
         }
       }
     }
@@ -510,6 +511,7 @@ hipError_t launch_modeprod2(const ModeProd2& mp, int num_cu, hipStream_t s) {
   // elements the Omega ranks count over: the output (reconstruction), the input (projection)
   k.N = (uint64_t)mp.A * (mp.recon ? (uint64_t)mp.R1 * mp.R2 : (uint64_t)mp.I1 * mp.I2);
   k.lr = mp.lr;
+  k.decay = mp.decay;
   k.has_sparse = mp.has_sparse;
   k.gS = mp.recon ? nullptr : mp.gather_S;
   const size_t per_cu = g.lds ? (160 * 1024) / g.lds : 8;

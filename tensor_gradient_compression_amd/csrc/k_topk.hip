@@ -4,6 +4,13 @@
 // (nullthought summary section 2: top-k gradient elements in COO form; pith.science
 // "What carries the argument": Omega chosen by top-k magnitude).
 //
+// Random sampling, the other choice pith.science names, runs the same selection on
+// per-element random keys instead of magnitudes: element e's key is the top 31 bits of
+// SplitMix64's output function (Steele, Lea and Flood, OOPSLA 2014) applied to the state
+// base + 0x9E3779B97F4A7C15 * e, so the k largest keys are a uniform k-subset, and a
+// refresh needs no generator state beyond the base (the host derives it from the seed and
+// the step). G is then read only to write the residual.
+//
 // Keys: the storage bit pattern with the sign cleared (an order-preserving integer
 // form of |x| for IEEE formats, subnormals kept distinct, NaN above Inf); complex:
 // the bits of fl64(re^2 + im^2) (both squares exact in fp64, so one rounding), any
@@ -112,6 +119,14 @@ struct KeyC64 {
   }
 };
 
+__device__ __forceinline__ uint64_t rand_key(uint64_t base, uint64_t e) {
+  uint64_t z = base + 0x9E3779B97F4A7C15ull * e;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return z >> 33;
+}
+
 // The 8 consecutive elements e0 .. e0 + 7 (e0 a multiple of 8, G 16-byte aligned);
 // past N they read as zero keys and are never selected.
 template <class K>
@@ -135,11 +150,12 @@ __global__ void k_topk_init(uint64_t* state, uint32_t* hist, uint32_t k) {
   }
 }
 
-template <class K>
+template <class K, bool RK>
 __global__ void __launch_bounds__(256) k_topk_hist(const void* __restrict__ G, uint64_t N,
                                                    int shift, int width,
                                                    const uint64_t* __restrict__ state,
-                                                   uint32_t* __restrict__ ghist) {
+                                                   uint32_t* __restrict__ ghist,
+                                                   uint64_t rk_base) {
   __shared__ uint32_t h[NBINS];
   for (int i = threadIdx.x; i < NBINS; i += blockDim.x) h[i] = 0;
   __syncthreads();
@@ -151,10 +167,12 @@ __global__ void __launch_bounds__(256) k_topk_hist(const void* __restrict__ G, u
   for (uint64_t gi = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < ngroups;
        gi += stride) {
     typename K::Raw x[8];
-    load_group<K>(G, N, gi * 8, x);
+    if constexpr (!RK) load_group<K>(G, N, gi * 8, x);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint64_t key = K::key_of(x[j]);
+      uint64_t key;
+      if constexpr (RK) key = rand_key(rk_base, gi * 8 + j);
+      else key = K::key_of(x[j]);
       if (gi * 8 + j < N && (key >> hi) == want) atomicAdd(&h[(key >> shift) & dmask], 1u);
     }
   }
@@ -225,11 +243,11 @@ __global__ void __launch_bounds__(256) k_topk_select(uint32_t* hist, int shift, 
   for (int i = t; i < NBINS; i += blockDim.x) hist[i] = 0;
 }
 
-template <class K>
+template <class K, bool RK>
 __global__ void __launch_bounds__(256) k_topk_count(const void* __restrict__ G, uint64_t N,
                                                     const uint64_t* __restrict__ state,
                                                     uint32_t* __restrict__ ucount,
-                                                    uint64_t nunits) {
+                                                    uint64_t nunits, uint64_t rk_base) {
   const uint64_t unit = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
   if (unit >= nunits) return;   // whole wave exits together
@@ -238,10 +256,12 @@ __global__ void __launch_bounds__(256) k_topk_count(const void* __restrict__ G, 
   for (int it = 0; it < UNIT_ITERS; ++it) {
     const uint64_t e0 = unit * UNIT + (uint64_t)it * 512 + (uint64_t)lane * 8;
     typename K::Raw x[8];
-    load_group<K>(G, N, e0, x);
+    if constexpr (!RK) load_group<K>(G, N, e0, x);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint64_t key = K::key_of(x[j]);
+      uint64_t key;
+      if constexpr (RK) key = rand_key(rk_base, e0 + j);
+      else key = K::key_of(x[j]);
       const bool in = e0 + j < N;
       gt += (in && key > tau) ? 1u : 0u;
       eq += (in && key == tau) ? 1u : 0u;
@@ -346,7 +366,7 @@ __global__ void __launch_bounds__(1024) k_topk_scan(const uint32_t* __restrict__
   }
 }
 
-template <class K>
+template <class K, bool RK>
 __global__ void __launch_bounds__(256) k_topk_compact(const void* __restrict__ G, uint64_t N,
                                                       const uint64_t* __restrict__ state,
                                                       const uint32_t* __restrict__ uoff,
@@ -354,7 +374,8 @@ __global__ void __launch_bounds__(256) k_topk_compact(const void* __restrict__ G
                                                       uint32_t* __restrict__ omega,
                                                       uint64_t* __restrict__ mask,
                                                       uint32_t* __restrict__ rank,
-                                                      void* __restrict__ resid) {
+                                                      void* __restrict__ resid,
+                                                      uint64_t rk_base) {
   const uint64_t unit = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
   if (unit >= nunits) return;
@@ -366,11 +387,13 @@ __global__ void __launch_bounds__(256) k_topk_compact(const void* __restrict__ G
   for (int it = 0; it < UNIT_ITERS; ++it) {
     const uint64_t e0 = unit * UNIT + (uint64_t)it * 512 + (uint64_t)lane * 8;
     typename K::Raw x[8];
-    load_group<K>(G, N, e0, x);
+    if (!RK || resid) load_group<K>(G, N, e0, x);   // rand-k reads G only for the residual
     uint32_t pg = 0, pe = 0;   // bit j: element e0 + j is > tau / == tau
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint64_t key = K::key_of(x[j]);
+      uint64_t key;
+      if constexpr (RK) key = rand_key(rk_base, e0 + j);
+      else key = K::key_of(x[j]);
       if (e0 + j < N) {
         pg |= (key > tau ? 1u : 0u) << j;
         pe |= (key == tau ? 1u : 0u) << j;
@@ -429,10 +452,10 @@ __global__ void __launch_bounds__(256) k_topk_compact(const void* __restrict__ G
   }
 }
 
-template <class K>
+template <class K, bool RK>
 hipError_t run_topk(const void* G, uint64_t N, uint32_t k, const TopkWs& ws, uint32_t* omega,
-                    uint64_t* mask, uint32_t* rank, void* resid, hipStream_t s,
-                    void (*mark)(void*, int, bool), void* mctx) {
+                    uint64_t* mask, uint32_t* rank, void* resid, uint64_t rk_base,
+                    hipStream_t s, void (*mark)(void*, int, bool), void* mctx) {
   auto M = [&](int id, bool b) { if (mark) mark(mctx, id, b); };
   hipError_t err;
   M(KID_TOPK_INIT, true);
@@ -443,12 +466,14 @@ hipError_t run_topk(const void* G, uint64_t N, uint32_t k, const TopkWs& ws, uin
   if (hb > 4096) hb = 4096;
   if (hb < 1) hb = 1;
   for (int pass = 0;; ++pass) {
-    int top = K::BITS - DIGIT * pass;         // bits above this digit already fixed
+    constexpr int BITS = RK ? 31 : K::BITS;
+    int top = BITS - DIGIT * pass;            // bits above this digit already fixed
     if (top <= 0) break;
     int width = top < DIGIT ? top : DIGIT;
     int shift = top - width;
     M(KID_TOPK_HIST, true);
-    k_topk_hist<K><<<(unsigned)hb, 256, 0, s>>>(G, N, shift, width, ws.state, ws.hist);
+    k_topk_hist<K, RK><<<(unsigned)hb, 256, 0, s>>>(G, N, shift, width, ws.state, ws.hist,
+                                                    rk_base);
     M(KID_TOPK_HIST, false);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     M(KID_TOPK_SELECT, true);
@@ -459,7 +484,7 @@ hipError_t run_topk(const void* G, uint64_t N, uint32_t k, const TopkWs& ws, uin
   const uint64_t nunits = topk_units(N);
   const unsigned ub = (unsigned)((nunits + 3) / 4);
   M(KID_TOPK_COUNT, true);
-  k_topk_count<K><<<ub, 256, 0, s>>>(G, N, ws.state, ws.ucount, nunits);
+  k_topk_count<K, RK><<<ub, 256, 0, s>>>(G, N, ws.state, ws.ucount, nunits, rk_base);
   M(KID_TOPK_COUNT, false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   M(KID_TOPK_SCAN, true);
@@ -467,8 +492,8 @@ hipError_t run_topk(const void* G, uint64_t N, uint32_t k, const TopkWs& ws, uin
   M(KID_TOPK_SCAN, false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   M(KID_TOPK_COMPACT, true);
-  k_topk_compact<K><<<ub, 256, 0, s>>>(G, N, ws.state, ws.uoff, nunits, k, omega, mask, rank,
-                                       resid);
+  k_topk_compact<K, RK><<<ub, 256, 0, s>>>(G, N, ws.state, ws.uoff, nunits, k, omega, mask,
+                                           rank, resid, rk_base);
   M(KID_TOPK_COMPACT, false);
   return hipGetLastError();
 }
@@ -491,6 +516,29 @@ __global__ void k_mask_from_omega(const uint32_t* __restrict__ omega, uint32_t k
   mask[w] = bits;
 }
 
+template <int P>
+__global__ void __launch_bounds__(256) k_remap_moments(const uint64_t* __restrict__ mask_old,
+                                                       const uint32_t* __restrict__ rank_old,
+                                                       const uint32_t* __restrict__ om_new,
+                                                       uint32_t k,
+                                                       const float* __restrict__ m_old,
+                                                       const float* __restrict__ v_old,
+                                                       float* __restrict__ m_new,
+                                                       float* __restrict__ v_new) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < k; j += stride) {
+    const uint64_t e = om_new[j];
+    const uint64_t word = mask_old[e >> 6];
+    const bool kept = (word >> (e & 63)) & 1ull;
+    const uint64_t i = kept ? omega_rank(mask_old, rank_old, e, word) : 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      m_new[j * P + p] = kept ? m_old[i * P + p] : 0.0f;
+      v_new[j * P + p] = kept ? v_old[i * P + p] : 0.0f;
+    }
+  }
+}
+
 __global__ void k_fill_u32(uint32_t* p, uint64_t n, uint32_t v) {
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
@@ -510,16 +558,48 @@ unsigned fill_blocks(uint64_t n) {
 
 uint64_t topk_units(uint64_t N) { return (N + UNIT - 1) / UNIT; }
 
+template <class K>
+hipError_t topk_dispatch(const void* G, uint64_t N, uint32_t k, const TopkWs& ws,
+                         uint32_t* omega, uint64_t* mask, uint32_t* rank, void* resid,
+                         int randk, uint64_t rk_base, hipStream_t s,
+                         void (*mark)(void*, int, bool), void* mctx) {
+  if (randk) return run_topk<K, true>(G, N, k, ws, omega, mask, rank, resid, rk_base, s, mark, mctx);
+  return run_topk<K, false>(G, N, k, ws, omega, mask, rank, resid, 0, s, mark, mctx);
+}
+
 hipError_t launch_topk(int dt, const void* G, uint64_t N, uint32_t k, const TopkWs& ws,
                        uint32_t* omega, uint64_t* mask, uint32_t* rank, void* resid,
-                       hipStream_t s, void (*mark)(void*, int, bool), void* mctx) {
+                       int randk, uint64_t rk_base, hipStream_t s,
+                       void (*mark)(void*, int, bool), void* mctx) {
   switch (dt) {
-    case DT_F32: return run_topk<KeyF32>(G, N, k, ws, omega, mask, rank, resid, s, mark, mctx);
+    case DT_F32:
+      return topk_dispatch<KeyF32>(G, N, k, ws, omega, mask, rank, resid, randk, rk_base, s,
+                                   mark, mctx);
     case DT_F16:
-    case DT_BF16: return run_topk<KeyH16>(G, N, k, ws, omega, mask, rank, resid, s, mark, mctx);
-    case DT_C64: return run_topk<KeyC64>(G, N, k, ws, omega, mask, rank, resid, s, mark, mctx);
+    case DT_BF16:
+      return topk_dispatch<KeyH16>(G, N, k, ws, omega, mask, rank, resid, randk, rk_base, s,
+                                   mark, mctx);
+    case DT_C64:
+      return topk_dispatch<KeyC64>(G, N, k, ws, omega, mask, rank, resid, randk, rk_base, s,
+                                   mark, mctx);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_remap_moments(const uint64_t* mask_old, const uint32_t* rank_old,
+                                const uint32_t* omega_new, uint32_t k, uint32_t P,
+                                const float* m_old, const float* v_old, float* m_new,
+                                float* v_new, hipStream_t s) {
+  if (!k) return hipSuccess;
+  uint64_t b = ((uint64_t)k + 255) / 256;
+  if (b > 8192) b = 8192;
+  if (P == 2)
+    k_remap_moments<2><<<(unsigned)b, 256, 0, s>>>(mask_old, rank_old, omega_new, k, m_old,
+                                                   v_old, m_new, v_new);
+  else
+    k_remap_moments<1><<<(unsigned)b, 256, 0, s>>>(mask_old, rank_old, omega_new, k, m_old,
+                                                   v_old, m_new, v_new);
+  return hipGetLastError();
 }
 
 hipError_t launch_mask_from_omega(const uint32_t* omega, uint32_t k, uint64_t* mask,

@@ -51,6 +51,7 @@ __device__ __forceinline__ uint32_t omega_rank(const uint64_t* mask, const uint3
 
 struct AdamK {
   float b1, c1, b2, c2, eps, bc1, bc2;
+  float lam;   // sparse scale: N_S = lam * (Adam update of S); 1 for the plain method
 };
 
 // Kernel ids for per-launch timing (names in tgrad_kernel_name).
@@ -59,7 +60,7 @@ enum KernelId {
   KID_TOPK_COMPACT, KID_MASK_FROM_OMEGA, KID_GATHER, KID_PROJECT, KID_ADAM,
   KID_RECONSTRUCT, KID_RECON_APPLY, KID_APPLY_DENSE, KID_GRAM, KID_GRAM_REDUCE,
   KID_EIG, KID_FILL, KID_PROJECT_FIRST, KID_PROJECT_FUSED2, KID_RECON_FUSED2_APPLY,
-  KID_RECON_FUSED2, KID_COUNT_
+  KID_RECON_FUSED2, KID_REMAP, KID_COUNT_
 };
 
 // ---------------------------------------------------------------- launchers
@@ -72,9 +73,20 @@ struct TopkWs {
   uint32_t* uoff;       // 2 per unit
 };
 uint64_t topk_units(uint64_t N);
+// Omega = the k largest keys, ties to the lowest index. randk == 0: magnitude keys of G;
+// randk != 0: element e's key is the top 31 bits of SplitMix64's output for the state
+// rk_base + 0x9E3779B97F4A7C15 * e (G is then read only for the residual).
 hipError_t launch_topk(int dt, const void* G, uint64_t N, uint32_t k, const TopkWs& ws,
                        uint32_t* omega, uint64_t* mask, uint32_t* rank, void* resid,
-                       hipStream_t s, void (*mark)(void*, int, bool), void* mctx);
+                       int randk, uint64_t rk_base, hipStream_t s,
+                       void (*mark)(void*, int, bool), void* mctx);
+// Sparse moments that follow their element across a refresh: for each j < k with
+// e = omega_new[j], (m, v)_new[j] = (m, v)_old[i] if e is in the old Omega (bitmask and
+// word ranks of the old Omega give its position i), else 0 (P floats each).
+hipError_t launch_remap_moments(const uint64_t* mask_old, const uint32_t* rank_old,
+                                const uint32_t* omega_new, uint32_t k, uint32_t P,
+                                const float* m_old, const float* v_old, float* m_new,
+                                float* v_new, hipStream_t s);
 hipError_t launch_mask_from_omega(const uint32_t* omega, uint32_t k, uint64_t* mask,
                                   uint32_t* rank, uint64_t nwords, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint64_t n, uint32_t v, hipStream_t s);
@@ -87,9 +99,11 @@ hipError_t launch_gather(int dt, void* G, const uint32_t* omega, uint32_t k, flo
 hipError_t launch_adam(int core_dt, const void* g_core, float* u_core, float* m_core,
                        float* v_core, uint64_t n_core, float* S, float* m_s, float* v_s,
                        uint64_t n_s, AdamK a, hipStream_t s);
+// W <- round(fp32(W) * decay - lr * Delta) (decay = fp32(1 - lr * weight_decay); 1 exactly
+// without decay)
 hipError_t launch_apply_dense(int dt, void* W, const float* u_core, const uint64_t* mask,
                               const uint32_t* rank, const float* u_s, uint64_t N, float lr,
-                              int has_sparse, hipStream_t s);
+                              float decay, int has_sparse, hipStream_t s);
 
 // Mode product Y[a, jj, b] = sum_kk M[jj, kk] X[a, kk, b] over the (A, I, B, P) view.
 struct ModeProd {
@@ -97,7 +111,8 @@ struct ModeProd {
   int in_dt;
   const float* M;  // (R*P) x (I*P) row-major
   uint32_t A, I, B, R, P;
-  // epilogue: apply == 0 -> store fp32 to Y; apply == 1 -> W <- round(W - lr*(acc + uS@Omega))
+  // epilogue: apply == 0 -> store fp32 to Y;
+  // apply == 1 -> W <- round(W * decay - lr*(acc + uS@Omega))
   int apply;
   float* Y;
   void* W;
@@ -108,6 +123,7 @@ struct ModeProd {
   const uint32_t* omega;   // Omega ascending, |Omega| = kS (apply)
   uint64_t kS;
   float lr;
+  float decay;
   int has_sparse;
   int force_ncb;           // 0: choose the tile width automatically
 };
@@ -134,6 +150,7 @@ struct ModeProd2 {
   const uint32_t* omega;
   uint64_t kS;
   float lr;
+  float decay;
   int has_sparse;
   uint32_t force_ta;       // 0: choose the slabs per tile automatically
   // projection only: also perform the COO gather on the staged input, S[j] = X[omega[j]]

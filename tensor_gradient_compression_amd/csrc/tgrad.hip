@@ -7,7 +7,7 @@
 //   [refresh when due] -> gather S = G[Omega], zero G[Omega] -> projection, one mode
 //   product per compressed mode (last mode first) -> fused Adam on core and S ->
 //   reconstruction, one mode product per compressed mode (first mode first), the last
-//   one applying W <- round(W - lr * (Delta_L + N_S at Omega)).
+//   one applying W <- round(W * decay - lr * (Delta_L + lambda N_S at Omega)).
 // Refresh: top-k -> Omega (+ bitmask, ranks) -> per compressed mode: Gram of the
 //   residual (Omega masked on load) -> Jacobi eigensolver -> U(n) and operand matrices.
 #include <algorithm>
@@ -64,6 +64,17 @@ struct tgrad_handle {
   double* gram = nullptr;        // one (I*P)^2 matrix per compressed mode
   uint64_t gram_stride = 0;
   TopkWs tw{};
+
+  // variants (tgrad_options); the defaults are the plain method
+  double wd = 0.0, lam = 1.0;
+  int selection = TGRAD_SELECT_TOPK;
+  bool remap = false;
+  uint64_t seed = 0;
+  // remapped sparse moments: the previous Omega's bitmask and ranks, and the second
+  // moment buffers (allocated when remapping is first enabled)
+  uint64_t* mask_prev = nullptr;
+  uint32_t* rank_prev = nullptr;
+  float *mS_alt = nullptr, *vS_alt = nullptr;
 
   std::vector<void*> allocs;
   int64_t state_bytes = 0, ws_bytes = 0;
@@ -228,8 +239,25 @@ int do_refresh(tgrad_t* h, const void* grad, hipStream_t s) {
   const void* R = grad;
   if (h->k > 0) {
     void* rw = h->fmodes.empty() ? nullptr : h->resid;
+    // with remapped moments the new Omega's bitmask goes to the other buffer, so the old
+    // one still locates each element's previous moments
+    if (h->remap) {
+      std::swap(h->mask, h->mask_prev);
+      std::swap(h->rank, h->rank_prev);
+    }
+    const uint64_t gamma = 0x9E3779B97F4A7C15ull;
+    const uint64_t serves = (uint64_t)(h->t + 1);
+    const uint64_t rk_base = h->seed + gamma * ((serves << 32) + 1ull);
     HIPCHK(h, launch_topk(h->dtype, grad, h->N, (uint32_t)h->k, h->tw, h->omega, h->mask,
-                          h->rank, rw, s, mark_cb, h));
+                          h->rank, rw, h->selection == TGRAD_SELECT_RANDK, rk_base, s,
+                          mark_cb, h));
+    if (h->remap) {
+      Mark m(h, KID_REMAP);
+      HIPCHK(h, launch_remap_moments(h->mask_prev, h->rank_prev, h->omega, (uint32_t)h->k,
+                                     h->P, h->mS, h->vS, h->mS_alt, h->vS_alt, s));
+      std::swap(h->mS, h->mS_alt);
+      std::swap(h->vS, h->vS_alt);
+    }
     if (rw) R = rw;
   }
   const int gdt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
@@ -286,7 +314,8 @@ const char* tgrad_kernel_name(int id) {
       "mask_from_omega", "gather_residual", "modeprod_project", "adam_fused",
       "modeprod_reconstruct", "modeprod_reconstruct_apply", "apply_dense", "gram",
       "gram_reduce", "eig_jacobi", "fill", "modeprod_project_first",
-      "modeprod2_project_first", "modeprod2_reconstruct_apply", "modeprod2_reconstruct"};
+      "modeprod2_project_first", "modeprod2_reconstruct_apply", "modeprod2_reconstruct",
+      "remap_moments"};
   if (id < 0 || id >= KID_COUNT_) return "";
   return names[id];
 }
@@ -586,6 +615,7 @@ int tgrad_step(tgrad_t* h, void* weight, void* grad, void* stream) {
   a.eps = (float)h->eps;
   a.bc1 = (float)(1.0 - std::pow(h->b1, (double)t));
   a.bc2 = (float)(1.0 - std::pow(h->b2, (double)t));
+  a.lam = (float)h->lam;
   {
     Mark m(h, KID_ADAM);
     const void* gcore = nf ? (const void*)h->core : (const void*)grad;
@@ -594,10 +624,11 @@ int tgrad_step(tgrad_t* h, void* weight, void* grad, void* stream) {
                           h->k * P, a, s));
   }
   const float lr = (float)h->lr;
+  const float decay = (float)(1.0 - h->lr * h->wd);
   if (nf == 0) {
     Mark m(h, KID_APPLY_DENSE);
     HIPCHK(h, launch_apply_dense(h->dtype, weight, h->ucore, h->mask, h->rank, h->S, h->N, lr,
-                                 h->k > 0, s));
+                                 decay, h->k > 0, s));
     return TGRAD_OK;
   }
   X = h->ucore;
@@ -631,6 +662,7 @@ int tgrad_step(tgrad_t* h, void* weight, void* grad, void* stream) {
       mp.omega = h->omega;
       mp.kS = h->k;
       mp.lr = lr;
+      mp.decay = decay;
       mp.has_sparse = h->k > 0;
       {
         Mark m(h, last ? KID_RECON_FUSED2_APPLY : KID_RECON_FUSED2);
@@ -657,6 +689,7 @@ int tgrad_step(tgrad_t* h, void* weight, void* grad, void* stream) {
       mp.omega = h->omega;
       mp.kS = h->k;
       mp.lr = lr;
+      mp.decay = decay;
       mp.has_sparse = h->k > 0;
       {
         Mark m(h, last ? KID_RECON_APPLY : KID_RECONSTRUCT);
@@ -762,6 +795,7 @@ int tgrad_set_factor(tgrad_t* h, int mode, const float* U, int64_t n_floats) {
 // Layout: header, then Omega (k u32), per compressed mode (ascending) U(n) (I r P fp32)
 // and its eigenvalues (I fp64), then m_C, v_C (core P fp32 each), m_S, v_S (k P fp32
 // each). Membership mask, ranks and the MFMA operand matrices are rebuilt on load.
+}  // extern "C"
 namespace {
 struct CkptHeader {
   char magic[8];
@@ -807,6 +841,7 @@ std::vector<std::pair<void*, size_t>> ckpt_arrays(tgrad_t* h) {
   return a;
 }
 }  // namespace
+extern "C" {
 
 int64_t tgrad_state_size(tgrad_t* h) {
   if (!h) return -1;
@@ -870,6 +905,70 @@ int tgrad_load_state(tgrad_t* h, const void* buf, int64_t size) {
   HIPCHK(h, hipDeviceSynchronize());
   h->t = theirs.t;
   h->refreshed_for = theirs.refreshed_for;
+  return TGRAD_OK;
+}
+
+void tgrad_default_options(tgrad_options* out) {
+  if (!out) return;
+  std::memset(out, 0, sizeof(*out));
+  out->weight_decay = 0.0;
+  out->sparse_scale = 1.0;
+  out->selection = TGRAD_SELECT_TOPK;
+  out->remap_moments = 0;
+  out->seed = 0;
+}
+
+int tgrad_get_options(const tgrad_t* h, tgrad_options* out) {
+  if (!h || !out) return TGRAD_EINVAL;
+  tgrad_default_options(out);
+  out->weight_decay = h->wd;
+  out->sparse_scale = h->lam;
+  out->selection = h->selection;
+  out->remap_moments = h->remap ? 1 : 0;
+  out->seed = h->seed;
+  return TGRAD_OK;
+}
+
+int tgrad_set_options(tgrad_t* h, const tgrad_options* o) {
+  if (!h || !o) return TGRAD_EINVAL;
+  if (!std::isfinite(o->weight_decay) || o->weight_decay < 0.0 || !std::isfinite(o->sparse_scale))
+    return TGRAD_EINVAL;
+  if (o->selection != TGRAD_SELECT_TOPK && o->selection != TGRAD_SELECT_RANDK) return TGRAD_EINVAL;
+  if (o->remap_moments != 0 && o->remap_moments != 1) return TGRAD_EINVAL;
+  if (o->remap_moments && h->k > 0 && !h->mask_prev) {
+    DevGuard g(h->device);
+    const uint64_t ns = h->k * h->P;
+    bool ok = dalloc(h, &h->mask_prev, h->nwords, false);
+    ok = ok && dalloc(h, &h->rank_prev, h->nwords, false);
+    ok = ok && dalloc(h, &h->mS_alt, ns, true);
+    ok = ok && dalloc(h, &h->vS_alt, ns, true);
+    if (!ok) {
+      // keep the handle usable: release what this call got
+      struct Part { void** p; int64_t bytes; bool state; };
+      const Part parts[4] = {{(void**)&h->mask_prev, (int64_t)h->nwords * 8, false},
+                             {(void**)&h->rank_prev, (int64_t)h->nwords * 4, false},
+                             {(void**)&h->mS_alt, (int64_t)ns * 4, true},
+                             {(void**)&h->vS_alt, (int64_t)ns * 4, true}};
+      for (const Part& q : parts) {
+        if (!*q.p) continue;
+        auto it = std::find(h->allocs.begin(), h->allocs.end(), *q.p);
+        if (it != h->allocs.end()) h->allocs.erase(it);
+        (void)hipFree(*q.p);
+        *q.p = nullptr;
+        (q.state ? h->state_bytes : h->ws_bytes) -= q.bytes;
+      }
+      return TGRAD_ENOMEM;
+    }
+    HIPCHK(h, hipDeviceSynchronize());
+    HIPCHK(h, hipMemset(h->mask_prev, 0, h->nwords * 8));
+    HIPCHK(h, hipMemset(h->rank_prev, 0, h->nwords * 4));
+    HIPCHK(h, hipDeviceSynchronize());
+  }
+  h->wd = o->weight_decay;
+  h->lam = o->sparse_scale;
+  h->selection = o->selection;
+  h->remap = o->remap_moments != 0;
+  h->seed = o->seed;
   return TGRAD_OK;
 }
 

@@ -1,0 +1,241 @@
+"""GPU parity of the method's variants (tgrad_set_options) against the CPU oracle:
+rand-k selection of Omega, decoupled weight decay, the sparse scale factor lambda, and
+sparse Adam moments remapped by element at a refresh.
+
+Omega bit for bit; weights within gpu_helpers.weight_check's bar; where every step is
+element-wise (k = 0 with full ranks, rho = 1) W bit for bit, since both sides take the
+same fp32 operations in the same order."""
+import numpy as np
+import pytest
+
+import oracle as O
+import tensor_gradient_compression_amd as tg
+from gpu_helpers import factor_check, make_lib, weight_check
+from synth import CONFIGS, GradStream, init_weights
+from synth.gen import custom
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    tg.load_library()
+
+
+def dev(x, dtype):
+    return tg.to_device(x, dtype)
+
+
+def host(t, dtype):
+    return tg.to_host(t, dtype)
+
+
+def oracle_for(wl, T=None, rho=None, **opts):
+    if "remap_moments" in opts:
+        opts["remap"] = opts.pop("remap_moments")
+    return O.TGradOracle(wl.shape, wl.ranks, wl.dtype, wl.sparse_ratio if rho is None else rho,
+                         T or wl.T, wl.lr, *wl.betas, wl.eps, **opts)
+
+
+def lib_for(wl, T=None, rho=None, **opts):
+    lib = make_lib(wl, T=T, rho=rho)
+    lib.set_options(**opts)
+    return lib
+
+
+# --------------------------------------------------------------------------- rand-k
+
+RANDK_CASES = [
+    ("f32-tiny-k0", custom((7, 5, 3), "f32", (7, 5, 3), 0.0), 3),
+    ("f32-tiny-k1", custom((7, 5, 3), "f32", (7, 5, 3), 1 / 105 + 1e-12), 3),
+    ("f32-tiny-all", custom((7, 5, 3), "f32", (7, 5, 3), 1.0), 3),
+    ("bf16-ragged", custom((33, 17, 61), "bf16", (33, 17, 61), 0.05), 12345),
+    ("c64-small", custom((12, 10, 9), "c64", (12, 10, 9), 0.2), 2 ** 64 - 1),
+    ("f32-ragged-4M", custom((4099, 1031), "f32", (4099, 1031), 0.05, signal_ranks=(2, 2)), 99),
+]
+
+
+@pytest.mark.parametrize("case", RANDK_CASES, ids=lambda c: c[0])
+def test_randk_omega_bit_exact(case):
+    """Rand-k Omega for the refresh that serves step 1 and, after three steps, step 4:
+    bit-exact against the oracle's keys, whatever the gradient."""
+    name, wl, seed = case
+    lib = lib_for(wl, T=3, selection="randk", seed=seed)
+    orc = oracle_for(wl, T=3, selection="randk", seed=seed)
+    gs = GradStream(wl, seed=1)
+    W0 = init_weights(wl, seed=1)
+    W, Wo = dev(W0, wl.dtype), W0
+    for t in range(1, 5):
+        g = gs.next()
+        lib.step(W, dev(g, wl.dtype))
+        Wo = orc.step(Wo, g)
+        if t in (1, 4):
+            torch.cuda.synchronize()
+            om = lib.get_omega()
+            assert np.array_equal(om, orc.omega), f"{name}: Omega differs at t={t}"
+            if 0 < orc.k < orc.N:
+                keys = O.randk_keys(orc.N, seed, t)
+                assert keys[om.astype(np.int64)].min() >= np.delete(keys, om.astype(np.int64)).max()
+    torch.cuda.synchronize()
+    weight_check(host(W, wl.dtype), Wo, wl.dtype, name)
+
+
+def test_randk_factors_are_those_of_its_residual():
+    """The Gram after a rand-k selection is taken over G with the random Omega zeroed."""
+    wl = CONFIGS[1]
+    lib = lib_for(wl, selection="randk", seed=5)
+    orc = oracle_for(wl, selection="randk", seed=5)
+    g = GradStream(wl, seed=3).next()
+    lib.refresh(dev(g, wl.dtype))
+    orc.refresh(g)
+    torch.cuda.synchronize()
+    assert np.array_equal(lib.get_omega(), orc.omega)
+    factor_check(lib, orc)
+
+
+# --------------------------------------------------------------------------- full runs
+
+VARIANTS = [
+    ("decay", dict(weight_decay=0.5)),
+    ("lambda", dict(sparse_scale=0.25)),
+    ("randk", dict(selection="randk", seed=17)),
+    ("remap", dict(remap_moments=True)),
+    ("all", dict(weight_decay=0.3, sparse_scale=2.0, selection="randk", seed=3,
+                 remap_moments=True)),
+]
+RUNS = [
+    ("config1", CONFIGS[1], 12),
+    ("bf16-odd", custom((33, 17, 60), "bf16", (13, 8, 31), 0.05, T=4, steps=9), 9),
+    ("c64-small", custom((12, 10, 9), "c64", (5, 4, 3), 0.05, T=3, steps=7), 7),
+]
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "one-mode"])
+@pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: v[0])
+@pytest.mark.parametrize("run", RUNS, ids=lambda r: r[0])
+def test_variant_runs_match_oracle(run, variant, fused):
+    """Independent runs across several refreshes: Omega bit-exact at every refresh,
+    factors within the projector bar, sparse moments to fp32 rounding, weights within
+    the weight bar, with each variant on both launch plans."""
+    name, wl, nsteps = run
+    vname, opts = variant
+    T = 4 if name == "config1" else wl.T
+    lib, orc = lib_for(wl, T=T, **opts), oracle_for(wl, T=T, **opts)
+    if not lib.set_fusion(fused):
+        pytest.skip("the two trailing modes are not both compressed")
+    gs = GradStream(wl, seed=6)
+    W0 = init_weights(wl, seed=6)
+    W, Wo = dev(W0, wl.dtype), W0
+    for t in range(1, nsteps + 1):
+        g = gs.next()
+        lib.step(W, dev(g, wl.dtype))
+        Wo = orc.step(Wo, g)
+        if (t - 1) % T == 0:
+            torch.cuda.synchronize()
+            assert np.array_equal(lib.get_omega(), orc.omega), f"{name}/{vname}: Omega at t={t}"
+            factor_check(lib, orc)
+    torch.cuda.synchronize()
+    weight_check(host(W, wl.dtype), Wo, wl.dtype, f"{name}/{vname}")
+    _, _, ms, vs = lib.get_moments()
+    np.testing.assert_allclose(ms, orc.mS, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(vs, orc.vS, rtol=1e-6, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "c64", "bf16", "f16"])
+def test_decay_full_rank_k0_is_bitwise_oracle(dtype):
+    """Full ranks and k = 0 make the step dense AdamW: W bit for bit."""
+    shape = (6, 5, 4, 3)
+    wl = custom(shape, dtype, shape, 0.0, T=5, steps=8, lr=3e-2)
+    gs = GradStream(wl, seed=21)
+    W0 = init_weights(wl, seed=21)
+    lib, orc = lib_for(wl, weight_decay=0.7), oracle_for(wl, weight_decay=0.7)
+    W, Wo = dev(W0, dtype), W0
+    for _ in range(8):
+        g = gs.next()
+        lib.step(W, dev(g, dtype))
+        Wo = orc.step(Wo, g)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(W, dtype).view(np.uint8), np.ascontiguousarray(Wo).view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("selection", ["topk", "randk"])
+def test_rho_one_lambda_decay_is_bitwise_oracle(dtype, selection):
+    """rho = 1: W <- W decay - lr lambda N_S element-wise, bit for bit."""
+    shape = (6, 5, 4, 3)
+    wl = custom(shape, dtype, (3, 2, 2, 1), 1.0, T=3, steps=8, signal_ranks=(2, 2, 2, 1), lr=1e-2)
+    opts = dict(weight_decay=0.2, sparse_scale=0.375, selection=selection, seed=4,
+                remap_moments=True)
+    gs = GradStream(wl, seed=4)
+    W0 = init_weights(wl, seed=4)
+    lib, orc = lib_for(wl, **opts), oracle_for(wl, **opts)
+    W, Wo = dev(W0, dtype), W0
+    for _ in range(8):
+        g = gs.next()
+        lib.step(W, dev(g, dtype))
+        Wo = orc.step(Wo, g)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(W, dtype).view(np.uint8), np.ascontiguousarray(Wo).view(np.uint8))
+
+
+def test_default_options_leave_the_step_unchanged():
+    wl = CONFIGS[1]
+    outs = []
+    for set_defaults in (False, True):
+        lib = make_lib(wl, T=4)
+        if set_defaults:
+            lib.set_options(weight_decay=0.9, sparse_scale=3.0, selection="randk",
+                            remap_moments=True, seed=8)
+            lib.set_options()
+            assert lib.get_options() == dict(weight_decay=0.0, sparse_scale=1.0,
+                                             selection="topk", remap_moments=False, seed=0)
+        gs = GradStream(wl, seed=2)
+        W = dev(init_weights(wl, seed=2), wl.dtype)
+        for _ in range(6):
+            lib.step(W, dev(gs.next(), wl.dtype))
+        torch.cuda.synchronize()
+        outs.append(host(W, wl.dtype))
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+def test_invalid_options_are_rejected():
+    wl = CONFIGS[0]
+    lib = make_lib(wl)
+    for bad in (dict(weight_decay=-1e-3), dict(weight_decay=float("nan")),
+                dict(sparse_scale=float("inf"))):
+        with pytest.raises(tg.TGradError, match="invalid argument"):
+            lib.set_options(**bad)
+    import ctypes
+    o = tg.Options(0.0, 1.0, 2, 0, 0)
+    assert lib._lib.tgrad_set_options(lib._h, ctypes.byref(o)) == tg.EINVAL
+    o = tg.Options(0.0, 1.0, 0, 2, 0)
+    assert lib._lib.tgrad_set_options(lib._h, ctypes.byref(o)) == tg.EINVAL
+    assert lib.get_options()["selection"] == "topk"
+
+
+def test_remap_checkpoint_resume_is_exact():
+    """Remapped moments survive a checkpoint: resume before a refresh and continue."""
+    wl = custom((12, 10, 9), "c64", (5, 4, 3), 0.05, T=3, steps=7)
+    opts = dict(remap_moments=True, selection="randk", seed=11, weight_decay=0.1)
+    gs = GradStream(wl, seed=5)
+    grads = [gs.next() for _ in range(8)]
+    W0 = init_weights(wl, seed=5)
+    a = lib_for(wl, T=3, **opts)
+    Wa = dev(W0, wl.dtype)
+    for g in grads:
+        a.step(Wa, dev(g, wl.dtype))
+    b = lib_for(wl, T=3, **opts)
+    Wb = dev(W0, wl.dtype)
+    for g in grads[:5]:
+        b.step(Wb, dev(g, wl.dtype))
+    state = b.save_state()
+    c = lib_for(wl, T=3, **opts)
+    c.load_state(state)
+    for g in grads[5:]:
+        c.step(Wb, dev(g, wl.dtype))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(Wa, wl.dtype).view(np.uint8), host(Wb, wl.dtype).view(np.uint8))
+    for x, y in zip(a.get_moments(), c.get_moments()):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))

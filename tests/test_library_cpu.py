@@ -90,3 +90,15 @@ def test_null_handle_calls_are_einval(lib):
     assert lib.tgrad_get_omega(None, None, 0) == tg.EINVAL
     assert lib.tgrad_mark_refreshed(None) == tg.EINVAL
     assert lib.tgrad_timing_enable(None, 1, 10) == tg.EINVAL
+
+
+def test_default_options_are_the_plain_method(lib):
+    """tgrad_default_options is host-only; the ctypes layout matches the C struct
+    (two doubles, two int32, one uint64: 32 bytes)."""
+    assert ctypes.sizeof(tg.Options) == 32
+    o = tg.Options(7.0, 7.0, 5, 5, 5)
+    lib.tgrad_default_options(ctypes.byref(o))
+    assert (o.weight_decay, o.sparse_scale, o.selection, o.remap_moments, o.seed) == \
+        (0.0, 1.0, tg.SELECT_TOPK, 0, 0)
+    assert lib.tgrad_set_options(None, ctypes.byref(o)) == tg.EINVAL
+    assert lib.tgrad_get_options(None, ctypes.byref(o)) == tg.EINVAL
