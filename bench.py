@@ -72,12 +72,13 @@ def kernel_bytes(wl):
         cur[n] = wl.shape[n]
         size = out
     # two trailing modes per launch: input read once, output written once; the first
-    # projection launch also performs the COO gather (k indices read, k fp32 values and
-    # k zeros written; the gradient values come with the input tile)
+    # projection launch also performs the COO gather (k indices read and k fp32 values
+    # written; the gradient values come with the input tile, which is zeroed at Omega in
+    # LDS only)
     d = len(wl.shape)
     I1, I2, R1, R2 = wl.shape[d - 2], wl.shape[d - 1], wl.ranks[d - 2], wl.ranks[d - 1]
     A = N // (I1 * I2)
-    proj2 = A * I1 * I2 * P * es + A * R1 * R2 * P * 4 + k * (4 + 4 * P + es)
+    proj2 = A * I1 * I2 * P * es + A * R1 * R2 * P * 4 + k * (4 + 4 * P)
     rec2 = A * R1 * R2 * P * 4 + 2 * N * es + N // 8 + N // 16 + k * P * 4 + k * 4
     flops_proj = []
     size = N

@@ -81,17 +81,18 @@ int tgrad_init(tgrad_t **out, int ndim, const int64_t *shape, const int64_t *tuc
 
 /*
  * One optimizer step on device buffers `weight` (W, updated in place) and `grad`
- * (G, caller-owned, N elements of dtype, 16-byte aligned).
+ * (G, caller-owned, N elements of dtype, 16-byte aligned, only read).
  *   t <- t + 1; if a refresh is due for t and tgrad_refresh was not already called
- *   for it, refresh from `grad` first. Then: S = G[Omega] (fp32) and G[Omega] <- 0
- *   (grad becomes the residual R in place and stays so on return); core C = R x_1
- *   U1^H ... x_d Ud^H; Adam on C and on S (fp32 moments); Delta = N_C x_1 U1 ...
- *   x_d Ud with N_S added at Omega (sparse scale 1); W <- round(W - lr * Delta), one
- *   rounding per element (nullthought section 3 step order; pith.science Theorem 2).
+ *   for it, refresh from `grad` first. Then: S = G[Omega] (fp32) and R = G with
+ *   Omega zeroed; core C = R x_1 U1^H ... x_d Ud^H; Adam on C and on S (fp32
+ *   moments); Delta = N_C x_1 U1 ... x_d Ud with lambda N_S added at Omega;
+ *   W <- round(W * decay - lr * Delta), one rounding per element (lambda = 1 and
+ *   decay = 1 unless tgrad_set_options says otherwise; nullthought section 3 step
+ *   order; pith.science Theorem 2).
  * Both buffers must stay valid until the work on `stream` completes.
  * Errors: TGRAD_EINVAL (null handle/pointer, grad not 16-byte aligned), TGRAD_EHIP.
  */
-int tgrad_step(tgrad_t *h, void *weight, void *grad, void *stream);
+int tgrad_step(tgrad_t *h, void *weight, const void *grad, void *stream);
 
 /*
  * Refresh Omega and the Tucker factors from `grad` (device, N elements of dtype,
@@ -152,8 +153,13 @@ int tgrad_mark_refreshed(tgrad_t *h);
 
 /* Test / benchmark hook: when the last two modes are both compressed and a slab of
  * them fits in LDS, the projection's first two mode products and the reconstruction's
- * last two run as one launch each (the default). enable = 0 selects one launch per
- * mode; enable = 1 returns TGRAD_EINVAL where the fused form does not apply. Results
+ * last two run as one launch each (the default). For bf16/fp16 tensors with small
+ * enough slabs those launches use one wave per slab on bf16 MFMAs (exact bf16 splits of
+ * the fp32 operands), otherwise workgroup-wide fp32 MFMA tiles. enable = 0 selects one
+ * launch per mode; 1 the fused form (default choice of kernel); 2 the fused form with
+ * the workgroup-tile kernel only. enable = 1 or 2 returns TGRAD_EINVAL where the fused
+ * form does not apply. The unfused plan projects a residual copy of grad, so enable = 0
+ * allocates an N-element workspace the first time (TGRAD_ENOMEM if that fails). Results
  * agree to fp32 rounding; takes effect at the next step. */
 int tgrad_set_fusion(tgrad_t *h, int enable);
 

@@ -239,9 +239,10 @@ class TGrad:
         return dict(weight_decay=o.weight_decay, sparse_scale=o.sparse_scale, selection=sel,
                     remap_moments=bool(o.remap_moments), seed=o.seed)
 
-    def set_fusion(self, enable: bool) -> bool:
-        """Select fused two-mode launches (True) or one launch per mode; returns False
-        when the fused form does not apply to this shape."""
+    def set_fusion(self, enable) -> bool:
+        """Select fused two-mode launches (True or 1: default kernel choice; 2: workgroup
+        tiles only) or one launch per mode (False or 0); returns False when the fused form
+        does not apply to this shape."""
         rc = self._lib.tgrad_set_fusion(self._h, int(enable))
         if rc == EINVAL and enable:
             return False

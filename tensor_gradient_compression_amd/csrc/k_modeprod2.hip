@@ -290,11 +290,10 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
     if (filled) lds_barrier();
 
     if (gath) {
-      // S[j] = X[omega[j]] (fp32), then X[omega[j]] <- 0 in the staged tile and in HBM:
-      // the projection runs on the residual, which the gradient buffer keeps
+      // S[j] = X[omega[j]] (fp32), then X[omega[j]] <- 0 in the staged tile: the
+      // projection runs on the residual; the gradient in HBM is only read
       const uint64_t e_lo = a0 * slab_in / P;
       XT* xs = (XT*)bx;
-      XT* xg = (XT*)const_cast<void*>(k.X);
       const XT z = zero_of<XT>();
       auto take = [&](uint64_t j, uint32_t om) {
         const uint32_t loc = (uint32_t)(om - e_lo) * P;
@@ -302,7 +301,6 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
         for (int p = 0; p < P; ++p) {
           k.gS[j * P + p] = to_f32(xs[loc + p]);
           xs[loc + p] = z;
-          xg[(uint64_t)om * P + p] = z;
         }
       };
 #pragma unroll

@@ -1,0 +1,705 @@
+// Two trailing mode products of a 16-bit tensor, one wave per slab, on MFMAs.
+//
+// Same mathematics as the two-mode kernel in k_modeprod2.hip (pith.science "What
+// carries the argument": projection to the core and reconstruction by mode-wise
+// products; appendix M Theorem 2), with the COO gather folded into the projection and
+// the sparse merge plus weight update folded into the reconstruction (nullthought
+// summary section 3). The tensor is A slabs of the last two modes, (A, I1, I2).
+//   projection:     Y[i1, r2] = sum_i2 X[i1, i2] M2[r2, i2]     (mode d)
+//                   Z[j1, r2] = sum_i1 M1[j1, i1] Y[i1, r2]     (mode d-1)
+//   reconstruction: Y[i1, j2] = sum_j1 M1[i1, j1] Z[j1, j2]     (mode d-1)
+//                   O[i1, i2] = sum_j2 Y[i1, j2] M2[i2, j2]     (mode d)
+//                   W <- round(W * decay - lr * (O + N_S at Omega))
+//
+// Organisation. Every wave owns a contiguous run of slabs and a private slice of LDS;
+// no workgroup barrier is used. While a wave computes slab n, the DMA engine brings the
+// input of slab n + 1 (global_load_lds, 16-byte pieces; the reconstruction also brings
+// the weights of slab n), and the Omega indices (and N_S) of slab n + 1 and the bitmask
+// word that bounds slab n + 2's Omega range arrive in registers. The output of slab n
+// leaves at the start of slab n + 1, before that slab's transfers are issued, and is
+// waited for only after slab n + 1 has been computed. A wave's LDS operations execute
+// in issue order, so data passed between its lanes through LDS needs no barrier.
+//
+// Arithmetic. The first product of each direction runs on v_mfma_f32_16x16x32_bf16:
+// every fp32 operand there (the factor matrices, the reconstruction's input) is split
+// into three bf16 parts, x = x0 + x1 + x2 with |x - x0 - x1 - x2| <= 2^-27 |x| (bf16
+// keeps fp32's exponent range, so each part takes the next 8 significand bits); bf16
+// data are exact as they are and fp16 data split exactly into two bf16 parts. Every
+// part product is exact in fp32; those whose parts' orders sum above 2 (each below
+// 2^-24 of the full product) are dropped, so the result agrees with an fp32 GEMM to the
+// level of fp32 rounding. The second product takes the fp32 intermediate as it is, on
+// v_mfma_f32_16x16x4_f32. Accumulation is fp32 throughout.
+#include "tg_common.h"
+
+namespace tg {
+
+namespace {
+
+constexpr int WPB = 4;            // waves per workgroup
+constexpr int NT = WPB * 64;
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+// LDS-qualified pointers: accesses through them compile to ds_* instructions (a
+// generic pointer would give flat accesses, which also count against vmcnt)
+#define LDS __attribute__((address_space(3)))
+
+struct S2K {
+  const void* X;        // projection: the gradient (A, I1, I2), only read
+  const float* Zin;     // reconstruction: fp32 input (A, R1, R2)
+  void* W;              // reconstruction: weights (A, I1, I2)
+  float* Y;             // projection: fp32 output (A, R1, R2)
+  const float* M1;      // projection: R1 x I1; reconstruction: I1 x R1 (row-major fp32)
+  const float* M2;      // projection: R2 x I2; reconstruction: I2 x R2
+  const uint64_t* mask;
+  const uint32_t* rank;
+  const uint32_t* omega;
+  float* S;             // projection: gathered S (written); reconstruction: N_S (read)
+  uint64_t kS;          // |Omega|; 0: no sparse part
+  uint32_t A, I1, I2, R1, R2;
+  uint32_t slab_e;      // I1 * I2
+  uint32_t spw_q, spw_r;   // slabs per wave: spw_q, plus one for the first spw_r waves
+  uint32_t lds_wave;       // LDS bytes per wave
+  uint32_t off_b1, off_y, off_o;   // per-wave byte offsets (second input buffer, Y, output)
+  uint32_t off_w0;      // reconstruction: the W buffer
+  uint32_t ly;          // row stride (floats) of the fp32 intermediate in LDS
+  uint32_t ydelta;      // reconstruction: float offset of Y inside the output region
+  float lr, decay;
+};
+
+__device__ __forceinline__ unsigned short bf_bits(float x) {
+  return __builtin_bit_cast(unsigned short, (__bf16)x);
+}
+__device__ __forceinline__ float bf_val(unsigned short b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+__device__ __forceinline__ void split3(float x, unsigned short& a, unsigned short& b,
+                                       unsigned short& c) {
+  a = bf_bits(x);
+  const float r = x - bf_val(a);
+  b = bf_bits(r);
+  c = bf_bits(r - bf_val(b));
+}
+__device__ __forceinline__ void split2(float x, unsigned short& a, unsigned short& b) {
+  a = bf_bits(x);
+  b = bf_bits(x - bf_val(a));
+}
+__device__ __forceinline__ f4 mma(const u16x8& a, const u16x8& b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+// sum over the kept part products of (a0 + a1 + a2)(b0 + b1 + b2): the six with
+// i + j <= 2, small terms first
+__device__ __forceinline__ f4 mma_3x3(const u16x8* a, const u16x8* b, f4 c) {
+  c = mma(a[2], b[0], c);
+  c = mma(a[1], b[1], c);
+  c = mma(a[0], b[2], c);
+  c = mma(a[1], b[0], c);
+  c = mma(a[0], b[1], c);
+  return mma(a[0], b[0], c);
+}
+// (a0 + a1)(b0 + b1 + b2) for exact two-part data: the five with i + j <= 2
+__device__ __forceinline__ f4 mma_2x3(const u16x8& a0, const u16x8& a1, const u16x8* b, f4 c) {
+  c = mma(a0, b[2], c);
+  c = mma(a1, b[1], c);
+  c = mma(a0, b[1], c);
+  c = mma(a1, b[0], c);
+  return mma(a0, b[0], c);
+}
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ void wave_fence() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// nchunks 16-byte pieces from src to dst (wave-uniform), one per lane per instruction
+__device__ __forceinline__ void wave_dma(const void* src, uint32_t nchunks, LDS unsigned char* dst,
+                                        uint32_t lane) {
+  for (uint32_t q0 = 0; q0 < nchunks; q0 += 64)
+    if (q0 + lane < nchunks)
+      __builtin_amdgcn_global_load_lds((const unsigned char*)src + (size_t)(q0 + lane) * 16,
+                                       (lds_void*)(dst + (size_t)q0 * 16), 16, 0, 0);
+}
+
+// Omega rank of element e from its bitmask word and word rank; kS past the end
+__device__ __forceinline__ uint64_t rank_at(uint64_t word, uint32_t wr, uint64_t e, uint64_t N,
+                                            uint64_t kS) {
+  if (e >= N) return kS;
+  return wr + (uint64_t)__popcll(word & ((1ull << (e & 63)) - 1ull));
+}
+
+// 16-bit storage types seen as their bit patterns (LDS holds raw 16-bit words)
+template <typename T> struct Bits16;
+template <> struct Bits16<bf16_t> {
+  // x as bf16 parts: exact in one
+  static constexpr int NP = 1;
+  __device__ static void parts(unsigned short raw, unsigned short* p) { p[0] = raw; }
+  __device__ static float value(unsigned short raw) { return bf_val(raw); }
+};
+template <> struct Bits16<_Float16> {
+  static constexpr int NP = 2;
+  __device__ static void parts(unsigned short raw, unsigned short* p) {
+    const float x = (float)__builtin_bit_cast(_Float16, raw);
+    split2(x, p[0], p[1]);   // 11 significand bits: exact in two bf16 parts
+  }
+  __device__ static float value(unsigned short raw) {
+    return (float)__builtin_bit_cast(_Float16, raw);
+  }
+};
+
+// Omega range of a slab: J(s) = Omega rank of element s * slab_e. A wave keeps J(n) and
+// J(n + 1), the first NOM * 64 indices (and N_S) of slab n + 1's range in registers,
+// and the bitmask word and rank that give J(n + 2); entries past NOM * 64 in one slab
+// are read directly.
+constexpr int NOM = 3;
+
+struct OmegaPipe {
+  uint64_t jn = 0, jn1 = 0;
+  uint64_t wnext = 0;
+  uint32_t rnext = 0;
+  uint32_t om_c[NOM], om_n[NOM];
+  float us_c[NOM], us_n[NOM];
+};
+
+// ------------------------------------------------------------------ projection
+// NRB1: 16-row blocks of I1 (I1 <= 16 NRB1 <= 64); NRB2: 16-row blocks of R1 (<= 32).
+// I2 <= 32 and R2 <= 16 (one k chunk and one column block in pass 1).
+// Pass 1 (mode d) runs on bf16 MFMAs: X exact (bf16) or in two exact parts (fp16),
+// M2 in three parts. Pass 2 (mode d-1) runs on v_mfma_f32_16x16x4_f32 directly on the
+// fp32 intermediate: its k index i1 = 4 NRB1 * (lane / 16) + step, so every lane reads
+// its part of a column of Y as consecutive 16-byte pieces.
+template <typename XT, int NRB1, int NRB2>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8))) k_proj2s(S2K k) {
+  constexpr int KS2 = 4 * NRB1;   // fp32 MFMA k-steps of pass 2
+  extern __shared__ float smem[];
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t gw = blockIdx.x * WPB + wv;
+  const uint32_t s0 = gw * k.spw_q + (gw < k.spw_r ? gw : k.spw_r);
+  const uint32_t s1 = s0 + k.spw_q + (gw < k.spw_r ? 1u : 0u);
+  if (s0 >= s1) return;
+  LDS unsigned char* const base = (LDS unsigned char*)smem + wv * k.lds_wave;
+  LDS unsigned char* const xb0 = base;
+  LDS unsigned char* const xb1 = base + k.off_b1;
+  LDS float* const Y1 = (LDS float*)(base + k.off_y);   // [r2 < 16][i1 < 16 NRB1], stride ly
+  LDS float* const So = (LDS float*)(base + k.off_o);   // [R1][R2]
+  const uint32_t li = lane & 15, lg = lane >> 4;
+  const uint32_t I1 = k.I1, I2 = k.I2, R1 = k.R1, R2 = k.R2, LY = k.ly;
+  const uint32_t slab_e = k.slab_e;
+  const uint64_t N = (uint64_t)k.A * slab_e;
+  const uint64_t kS = k.kS;
+  const bool sparse = kS > 0;
+
+  // pass 1 B[k = i2][col = r2] = M2[r2][i2] in three bf16 parts
+  u16x8 b1[3];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t i2 = 8 * lg + e;
+    const float v = (li < R2 && i2 < I2) ? k.M2[li * I2 + i2] : 0.0f;
+    unsigned short a, b, c;
+    split3(v, a, b, c);
+    b1[0][e] = a; b1[1][e] = b; b1[2][e] = c;
+  }
+  // pass 2 A[row = j1][k = i1] = M1[j1][i1], i1 = KS2 * lg + step
+  float a2[NRB2][KS2];
+#pragma unroll
+  for (int rb = 0; rb < NRB2; ++rb)
+#pragma unroll
+    for (int t = 0; t < KS2; ++t) {
+      const uint32_t j1 = 16 * rb + li, i1 = KS2 * lg + t;
+      a2[rb][t] = (j1 < R1 && i1 < I1) ? k.M1[j1 * I1 + i1] : 0.0f;
+    }
+
+  const XT* X = (const XT*)k.X;
+  const uint32_t xchunks = slab_e * 2 / 16;
+  auto bound_word = [&](uint32_t s) -> uint64_t {
+    const uint64_t e = (uint64_t)s * slab_e;
+    return e < N ? e >> 6 : 0;
+  };
+  OmegaPipe op;
+  if (sparse) {
+    const uint64_t w0 = bound_word(s0), w1 = bound_word(s0 + 1);
+    op.jn = rank_at(k.mask[w0], k.rank[w0], (uint64_t)s0 * slab_e, N, kS);
+    op.jn1 = rank_at(k.mask[w1], k.rank[w1], (uint64_t)(s0 + 1) * slab_e, N, kS);
+#pragma unroll
+    for (int i = 0; i < NOM; ++i) {
+      const uint64_t j = op.jn + lane + 64 * i;
+      op.om_c[i] = k.omega[j < kS ? j : kS - 1];
+    }
+    if (s0 + 2 <= s1) {
+      const uint64_t w2 = bound_word(s0 + 2);
+      op.wnext = k.mask[w2];
+      op.rnext = k.rank[w2];
+    }
+  }
+  wave_dma(X + (uint64_t)s0 * slab_e, xchunks, xb0, lane);
+
+  uint32_t nq_prev = 0;
+  uint64_t out_prev = 0;
+  for (uint32_t n = s0; n < s1; ++n) {
+    const int cur = (n - s0) & 1;
+    wait_vm0();   // slab n, its Omega indices and the next bound have landed
+    wave_fence();
+    uint64_t jn2 = 0;
+    if (sparse && n + 2 <= s1) jn2 = rank_at(op.wnext, op.rnext, (uint64_t)(n + 2) * slab_e, N, kS);
+    // the previous slab's output leaves (waited for at the next slab)
+    for (uint32_t q = lane; q < nq_prev; q += 64)
+      *(f4*)(k.Y + out_prev + 4 * q) = *(const LDS f4*)(So + 4 * q);
+    wait_lgkm0();
+    wave_fence();
+    // next slab's transfer, Omega indices and range bound
+    if (n + 1 < s1) {
+      wave_dma(X + (uint64_t)(n + 1) * slab_e, xchunks, cur ? xb0 : xb1, lane);
+      if (sparse) {
+#pragma unroll
+        for (int i = 0; i < NOM; ++i) {
+          const uint64_t j = op.jn1 + lane + 64 * i;
+          op.om_n[i] = k.omega[j < kS ? j : kS - 1];
+        }
+        if (n + 3 <= s1) {
+          const uint64_t w3 = bound_word(n + 3);
+          op.wnext = k.mask[w3];
+          op.rnext = k.rank[w3];
+        }
+      }
+    }
+
+    LDS unsigned short* const xs = (LDS unsigned short*)(cur ? xb1 : xb0);
+    const uint64_t e_lo = (uint64_t)n * slab_e;
+    if (sparse) {
+      // S[j] = X[omega[j]] and X[omega[j]] <- 0 in the LDS copy (+0 is the zero bit
+      // pattern of both 16-bit formats); the gradient in HBM is only read
+      auto take = [&](uint64_t j, uint32_t om) {
+        const uint32_t loc = (uint32_t)(om - e_lo);
+        k.S[j] = Bits16<XT>::value(xs[loc]);
+        xs[loc] = 0;
+      };
+      // the prefetched entries: every value read before any is cleared
+      float sv[NOM];
+#pragma unroll
+      for (int i = 0; i < NOM; ++i) {
+        const uint64_t j = op.jn + lane + 64 * i;
+        sv[i] = j < op.jn1 ? Bits16<XT>::value(xs[(uint32_t)(op.om_c[i] - e_lo)]) : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < NOM; ++i) {
+        const uint64_t j = op.jn + lane + 64 * i;
+        if (j < op.jn1) {
+          k.S[j] = sv[i];
+          xs[(uint32_t)(op.om_c[i] - e_lo)] = 0;
+        }
+      }
+      for (uint64_t j = op.jn + 64 * NOM + lane; j < op.jn1; j += 64) take(j, k.omega[j]);
+      wave_fence();
+    }
+
+    // pass 1 (mode d): rows i1, k = i2, columns r2
+#pragma unroll
+    for (int rb = 0; rb < NRB1; ++rb) {
+      const uint32_t i1 = 16 * rb + li;
+      u16x8 xp[Bits16<XT>::NP];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t i2 = 8 * lg + e;
+        const unsigned short raw =
+            (i1 < I1 && i2 < I2) ? xs[i1 * I2 + i2]
+                                 : (unsigned short)0;
+        unsigned short p[2];
+        Bits16<XT>::parts(raw, p);
+#pragma unroll
+        for (int h = 0; h < Bits16<XT>::NP; ++h) xp[h][e] = p[h];
+      }
+      f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (Bits16<XT>::NP == 1) {
+        acc = mma(xp[0], b1[2], acc);
+        acc = mma(xp[0], b1[1], acc);
+        acc = mma(xp[0], b1[0], acc);
+      } else {
+        acc = mma_2x3(xp[0], xp[1], b1, acc);
+      }
+      *(LDS f4*)(Y1 + li * LY + 16 * rb + 4 * lg) = acc;
+    }
+    wave_fence();
+    // pass 2 (mode d-1): rows j1, k = i1, columns r2
+    f4 acc2[NRB2];
+#pragma unroll
+    for (int rb = 0; rb < NRB2; ++rb) acc2[rb] = f4{0.f, 0.f, 0.f, 0.f};
+    const LDS float* yc = Y1 + li * LY + KS2 * lg;
+#pragma unroll
+    for (int q = 0; q < KS2 / 4; ++q) {
+      const f4 y = *(const LDS f4*)(yc + 4 * q);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int rb = 0; rb < NRB2; ++rb)
+          acc2[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[rb][4 * q + t], y[t], acc2[rb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int rb = 0; rb < NRB2; ++rb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t j1 = 16 * rb + 4 * lg + v;
+        if (j1 < R1 && li < R2) So[j1 * R2 + li] = acc2[rb][v];
+      }
+    wave_fence();
+    nq_prev = R1 * R2 / 4;
+    out_prev = (uint64_t)n * R1 * R2;
+    op.jn = op.jn1;
+    op.jn1 = jn2;
+#pragma unroll
+    for (int i = 0; i < NOM; ++i) op.om_c[i] = op.om_n[i];
+  }
+  // the last slab's output
+  wait_lgkm0();
+  for (uint32_t q = lane; q < nq_prev; q += 64)
+    *(f4*)(k.Y + out_prev + 4 * q) = *(const LDS f4*)(So + 4 * q);
+}
+
+// ------------------------------------------------------------------ reconstruction
+// NRB1: 16-row blocks of I1 (<= 64); NCB2: 16-column blocks of I2 (<= 32); R1 <= 32,
+// R2 <= 16. Pass 1 (mode d-1) on bf16 MFMAs with Z and M1 in three parts each; pass 2
+// (mode d) on v_mfma_f32_16x16x4_f32 with k index j2 = 4 (lane / 16) + step.
+template <typename WT, int NRB1, int NCB2>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8))) k_rec2s(S2K k) {
+  extern __shared__ float smem[];
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t gw = blockIdx.x * WPB + wv;
+  const uint32_t s0 = gw * k.spw_q + (gw < k.spw_r ? gw : k.spw_r);
+  const uint32_t s1 = s0 + k.spw_q + (gw < k.spw_r ? 1u : 0u);
+  if (s0 >= s1) return;
+  LDS unsigned char* const base = (LDS unsigned char*)smem + wv * k.lds_wave;
+  LDS unsigned char* const zb0 = base;
+  LDS unsigned char* const zb1 = base + k.off_b1;
+  LDS unsigned char* const wb = base + k.off_w0;
+  LDS float* const Ob = (LDS float*)(base + k.off_o);   // [I1][I2]; Y [i1][ly] at Ob + ydelta
+  LDS float* const Yb = Ob + k.ydelta;
+  const uint32_t li = lane & 15, lg = lane >> 4;
+  const uint32_t I1 = k.I1, I2 = k.I2, R1 = k.R1, R2 = k.R2, LY = k.ly;
+  const uint32_t slab_e = k.slab_e, slab_z = R1 * R2;
+  const uint64_t N = (uint64_t)k.A * slab_e;
+  const uint64_t kS = k.kS;
+  const bool sparse = kS > 0;
+  const float lr = k.lr, decay = k.decay;
+  const bool decayed = decay != 1.0f;
+
+  // pass 1 A[row = i1][k = j1] = M1[i1][j1] in three bf16 parts
+  u16x8 a1[NRB1][3];
+#pragma unroll
+  for (int rb = 0; rb < NRB1; ++rb)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t i1 = 16 * rb + li, j1 = 8 * lg + e;
+      const float v = (i1 < I1 && j1 < R1) ? k.M1[i1 * R1 + j1] : 0.0f;
+      unsigned short a, b, c;
+      split3(v, a, b, c);
+      a1[rb][0][e] = a; a1[rb][1][e] = b; a1[rb][2][e] = c;
+    }
+  // pass 2 B[k = j2][col = i2] = M2[i2][j2], j2 = 4 lg + step
+  float b2[NCB2][4];
+#pragma unroll
+  for (int cb = 0; cb < NCB2; ++cb)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t i2 = 16 * cb + li, j2 = 4 * lg + t;
+      b2[cb][t] = (i2 < I2 && j2 < R2) ? k.M2[i2 * R2 + j2] : 0.0f;
+    }
+
+  const WT* Wg = (const WT*)k.W;
+  const uint32_t zchunks = slab_z * 4 / 16, wchunks = slab_e * 2 / 16;
+  auto bound_word = [&](uint32_t s) -> uint64_t {
+    const uint64_t e = (uint64_t)s * slab_e;
+    return e < N ? e >> 6 : 0;
+  };
+  OmegaPipe op;
+  if (sparse) {
+    const uint64_t w0 = bound_word(s0), w1 = bound_word(s0 + 1);
+    op.jn = rank_at(k.mask[w0], k.rank[w0], (uint64_t)s0 * slab_e, N, kS);
+    op.jn1 = rank_at(k.mask[w1], k.rank[w1], (uint64_t)(s0 + 1) * slab_e, N, kS);
+#pragma unroll
+    for (int i = 0; i < NOM; ++i) {
+      const uint64_t j = op.jn + lane + 64 * i;
+      const uint64_t jc = j < kS ? j : kS - 1;
+      op.om_c[i] = k.omega[jc];
+      op.us_c[i] = k.S[jc];
+    }
+    if (s0 + 2 <= s1) {
+      const uint64_t w2 = bound_word(s0 + 2);
+      op.wnext = k.mask[w2];
+      op.rnext = k.rank[w2];
+    }
+  }
+  wave_dma(k.Zin + (uint64_t)s0 * slab_z, zchunks, zb0, lane);
+
+  uint32_t nq_prev = 0;
+  uint64_t out_prev = 0;
+  for (uint32_t n = s0; n <= s1; ++n) {
+    const int cur = (n - s0) & 1;
+    wait_vm0();   // Z of slab n, W of slab n - 1, Omega data; the stores of slab n - 2
+    wave_fence();
+    uint64_t jn2 = 0;
+    if (sparse && n + 2 <= s1) jn2 = rank_at(op.wnext, op.rnext, (uint64_t)(n + 2) * slab_e, N, kS);
+    // the previous slab: W <- round(W * decay - lr * O), 16-byte pieces (the stores are
+    // waited for at the next slab)
+    for (uint32_t q = lane; q < nq_prev; q += 64) {
+      const f4 o0 = *(const LDS f4*)(Ob + 8 * q);
+      const f4 o1 = *(const LDS f4*)(Ob + 8 * q + 4);
+      typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+      const u4v wraw = *(const LDS u4v*)(wb + 16 * q);
+      const WT* ws = (const WT*)&wraw;
+      WT o[8];
+      if (decayed) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] = from_f32<WT>(to_f32(ws[e]) * decay - lr * o0[e]);
+          o[4 + e] = from_f32<WT>(to_f32(ws[4 + e]) * decay - lr * o1[e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] = from_f32<WT>(to_f32(ws[e]) - lr * o0[e]);
+          o[4 + e] = from_f32<WT>(to_f32(ws[4 + e]) - lr * o1[e]);
+        }
+      }
+      *(uint4*)((WT*)k.W + out_prev + 8 * q) = *(const uint4*)o;
+    }
+    if (n == s1) break;
+    wait_lgkm0();
+    wave_fence();
+    // this slab's W (used at the next slab), the next slab's Z and Omega data
+    wave_dma(Wg + (uint64_t)n * slab_e, wchunks, wb, lane);
+    if (n + 1 < s1) {
+      wave_dma(k.Zin + (uint64_t)(n + 1) * slab_z, zchunks, cur ? zb0 : zb1, lane);
+      if (sparse) {
+#pragma unroll
+        for (int i = 0; i < NOM; ++i) {
+          const uint64_t j = op.jn1 + lane + 64 * i;
+          const uint64_t jc = j < kS ? j : kS - 1;
+          op.om_n[i] = k.omega[jc];
+          op.us_n[i] = k.S[jc];
+        }
+        if (n + 3 <= s1) {
+          const uint64_t w3 = bound_word(n + 3);
+          op.wnext = k.mask[w3];
+          op.rnext = k.rank[w3];
+        }
+      }
+    }
+
+    const LDS float* const zs = (const LDS float*)(cur ? zb1 : zb0);
+    // pass 1 (mode d-1): rows i1, k = j1, columns j2
+    u16x8 zp[3];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t j1 = 8 * lg + e;
+      const float v = (j1 < R1 && li < R2) ? zs[j1 * R2 + li] : 0.0f;
+      unsigned short a, b, c;
+      split3(v, a, b, c);
+      zp[0][e] = a; zp[1][e] = b; zp[2][e] = c;
+    }
+#pragma unroll
+    for (int rb = 0; rb < NRB1; ++rb) {
+      const f4 acc = mma_3x3(a1[rb], zp, f4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Yb[(16 * rb + 4 * lg + v) * LY + li] = acc[v];
+    }
+    wave_fence();
+    // pass 2 (mode d): rows i1, k = j2, columns i2; Y's block rb is read before O's
+    // block rb is written over it (their placement keeps block rb + 1 intact)
+#pragma unroll
+    for (int rb = 0; rb < NRB1; ++rb) {
+      const f4 y = *(const LDS f4*)(Yb + (16 * rb + li) * LY + 4 * lg);
+      f4 acc[NCB2];
+#pragma unroll
+      for (int cb = 0; cb < NCB2; ++cb) acc[cb] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int cb = 0; cb < NCB2; ++cb)
+          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(y[t], b2[cb][t], acc[cb], 0, 0, 0);
+      wave_fence();
+#pragma unroll
+      for (int cb = 0; cb < NCB2; ++cb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t i1 = 16 * rb + 4 * lg + v, i2 = 16 * cb + li;
+          if (i1 < I1 && i2 < I2) Ob[i1 * I2 + i2] = acc[cb][v];
+        }
+    }
+    wave_fence();
+    if (sparse) {
+      const uint64_t e_lo = (uint64_t)n * slab_e;
+#pragma unroll
+      for (int i = 0; i < NOM; ++i) {
+        const uint64_t j = op.jn + lane + 64 * i;
+        if (j < op.jn1) {
+          const uint32_t loc = (uint32_t)(op.om_c[i] - e_lo);
+          Ob[loc] = Ob[loc] + op.us_c[i];
+        }
+      }
+      for (uint64_t j = op.jn + 64 * NOM + lane; j < op.jn1; j += 64) {
+        const uint32_t loc = (uint32_t)(k.omega[j] - e_lo);
+        Ob[loc] = Ob[loc] + k.S[j];
+      }
+      wave_fence();
+    }
+    nq_prev = slab_e / 8;
+    out_prev = (uint64_t)n * slab_e;
+    op.jn = op.jn1;
+    op.jn1 = jn2;
+#pragma unroll
+    for (int i = 0; i < NOM; ++i) {
+      op.om_c[i] = op.om_n[i];
+      op.us_c[i] = op.us_n[i];
+    }
+  }
+}
+
+struct Plan2s {
+  S2K k;
+  int num_cu;
+  size_t lds;
+  int nrb1, nrb2;   // projection: (NRB1, NRB2); reconstruction: (NRB1, NCB2)
+  bool ok;
+};
+
+uint32_t al16(uint32_t x) { return (x + 15u) & ~15u; }
+
+Plan2s plan2s(const ModeProd2& mp, int num_cu) {
+  Plan2s p{};
+  S2K& k = p.k;
+  p.ok = false;
+  if (mp.P != 1) return p;
+  const bool rec = mp.recon != 0;
+  const int dt16 = rec ? mp.w_dt : mp.in_dt;
+  if (dt16 != DT_BF16 && dt16 != DT_F16) return p;
+  if (rec && (!mp.apply || mp.in_dt != DT_F32)) return p;
+  // sizes in the kernels' names: I = the full-size side, R = the core side
+  const uint32_t I1 = rec ? mp.R1 : mp.I1, I2 = rec ? mp.R2 : mp.I2;
+  const uint32_t R1 = rec ? mp.I1 : mp.R1, R2 = rec ? mp.I2 : mp.R2;
+  if (I1 > 64 || I2 > 32 || R1 > 32 || R2 > 16 || I1 == 0 || I2 == 0 || R1 == 0 || R2 == 0)
+    return p;
+  const uint32_t slab_e = I1 * I2;
+  if (slab_e % 8 != 0 || (R1 * R2) % 4 != 0) return p;
+  const uintptr_t big = (uintptr_t)(rec ? mp.W : mp.X);
+  const uintptr_t small = (uintptr_t)(rec ? mp.X : (const void*)mp.Y);
+  if (big % 16 || small % 16) return p;
+  k.I1 = I1; k.I2 = I2; k.R1 = R1; k.R2 = R2;
+  k.slab_e = slab_e;
+  k.A = mp.A;
+  p.nrb1 = (int)((I1 + 15) / 16);
+  if (!rec) {
+    p.nrb2 = (int)((R1 + 15) / 16);
+    k.ly = 16u * p.nrb1 + 4;
+    uint32_t off = al16(slab_e * 2);
+    k.off_b1 = off; off += al16(slab_e * 2);
+    k.off_y = off; off += al16(16 * k.ly * 4);
+    k.off_o = off; off += al16(R1 * R2 * 4);
+    k.lds_wave = off;
+  } else {
+    p.nrb2 = (int)((I2 + 15) / 16);
+    k.ly = 20;   // Y rows hold j2 < 16 (R2 <= 16), 16-byte aligned
+    const uint32_t i1p = 16u * p.nrb1;
+    // O rows of block rb must end before Y's block rb + 1 starts
+    int64_t d = 0;
+    for (int rb = 0; rb + 1 < p.nrb1; ++rb) {
+      const int64_t need = 16ll * (rb + 1) * I2 - 16ll * (rb + 1) * k.ly;
+      if (need > d) d = need;
+    }
+    k.ydelta = (uint32_t)((d + 3) & ~3ll);
+    const uint32_t ofl = std::max(slab_e, k.ydelta + i1p * k.ly);
+    uint32_t off = al16(R1 * R2 * 4);
+    k.off_b1 = off; off += al16(R1 * R2 * 4);
+    k.off_w0 = off; off += al16(slab_e * 2);
+    k.off_o = off; off += al16(ofl * 4);
+    k.lds_wave = off;
+  }
+  p.lds = (size_t)k.lds_wave * WPB;
+  p.num_cu = num_cu > 0 ? num_cu : 256;
+  p.ok = p.lds <= 64 * 1024;
+  return p;
+}
+
+// One resident round of workgroups (as many as the kernel's registers and LDS let a CU
+// hold), each wave taking a contiguous run of slabs.
+template <typename F>
+hipError_t launch2s(F fn, Plan2s p, hipStream_t s) {
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, p.lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidValue;
+  uint64_t grid = (uint64_t)p.num_cu * (uint64_t)per_cu;
+  const uint64_t need = ((uint64_t)p.k.A + WPB - 1) / WPB;
+  if (grid > need) grid = need;
+  if (grid < 1) grid = 1;
+  const uint64_t waves = grid * WPB;
+  p.k.spw_q = (uint32_t)(p.k.A / waves);
+  p.k.spw_r = (uint32_t)(p.k.A % waves);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(NT), p.lds, s, p.k);
+  return hipGetLastError();
+}
+
+template <typename XT, int NRB1>
+hipError_t proj_nrb2(const Plan2s& p, hipStream_t s) {
+  if (p.nrb2 == 1) return launch2s(k_proj2s<XT, NRB1, 1>, p, s);
+  return launch2s(k_proj2s<XT, NRB1, 2>, p, s);
+}
+template <typename XT>
+hipError_t proj_go(const Plan2s& p, hipStream_t s) {
+  switch (p.nrb1) {
+    case 1: return proj_nrb2<XT, 1>(p, s);
+    case 2: return proj_nrb2<XT, 2>(p, s);
+    case 3: return proj_nrb2<XT, 3>(p, s);
+    default: return proj_nrb2<XT, 4>(p, s);
+  }
+}
+template <typename WT, int NRB1>
+hipError_t rec_ncb(const Plan2s& p, hipStream_t s) {
+  if (p.nrb2 == 1) return launch2s(k_rec2s<WT, NRB1, 1>, p, s);
+  return launch2s(k_rec2s<WT, NRB1, 2>, p, s);
+}
+template <typename WT>
+hipError_t rec_go(const Plan2s& p, hipStream_t s) {
+  switch (p.nrb1) {
+    case 1: return rec_ncb<WT, 1>(p, s);
+    case 2: return rec_ncb<WT, 2>(p, s);
+    case 3: return rec_ncb<WT, 3>(p, s);
+    default: return rec_ncb<WT, 4>(p, s);
+  }
+}
+
+}  // namespace
+
+bool slab2_supported(const ModeProd2& mp, int num_cu) { return plan2s(mp, num_cu).ok; }
+
+hipError_t launch_slab2(const ModeProd2& mp, int num_cu, hipStream_t s) {
+  Plan2s p = plan2s(mp, num_cu);
+  if (!p.ok) return hipErrorInvalidValue;
+  S2K& k = p.k;
+  const bool rec = mp.recon != 0;
+  k.M1 = mp.M1;
+  k.M2 = mp.M2;
+  k.mask = mp.mask;
+  k.rank = mp.rank;
+  k.omega = mp.omega;
+  k.lr = mp.lr;
+  k.decay = mp.decay;
+  if (!rec) {
+    k.X = mp.X;
+    k.Y = mp.Y;
+    k.S = mp.gather_S;
+    k.kS = mp.gather_S ? mp.kS : 0;
+    return mp.in_dt == DT_BF16 ? proj_go<bf16_t>(p, s) : proj_go<_Float16>(p, s);
+  }
+  k.Zin = (const float*)mp.X;
+  k.W = mp.W;
+  k.S = const_cast<float*>(mp.uS);
+  k.kS = mp.has_sparse ? mp.kS : 0;
+  return mp.w_dt == DT_BF16 ? rec_go<bf16_t>(p, s) : rec_go<_Float16>(p, s);
+}
+
+}  // namespace tg

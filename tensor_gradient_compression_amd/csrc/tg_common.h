@@ -154,11 +154,17 @@ struct ModeProd2 {
   int has_sparse;
   uint32_t force_ta;       // 0: choose the slabs per tile automatically
   // projection only: also perform the COO gather on the staged input, S[j] = X[omega[j]]
-  // (fp32) and X[omega[j]] <- 0 in place (X is then the caller's writable gradient)
+  // (fp32), and project the staged input with Omega zeroed (X itself is only read)
   float* gather_S;
 };
 uint32_t modeprod2_tile(const ModeProd2& mp);   // 0: does not fit
 hipError_t launch_modeprod2(const ModeProd2& mp, int num_cu, hipStream_t s);
+// The same two products for 16-bit data, one wave per slab on bf16 MFMAs (projection
+// with the gather folded in, or reconstruction with merge and apply); supported when
+// P == 1, the slab sizes are small enough (full-size side I1 <= 64, I2 <= 32; core side
+// R1 <= 32, R2 <= 16) and the buffers are 16-byte aligned.
+bool slab2_supported(const ModeProd2& mp, int num_cu);
+hipError_t launch_slab2(const ModeProd2& mp, int num_cu, hipStream_t s);
 
 // Gram of the (A, I, B, P) view with Omega entries treated as zero:
 // out[x, y] (fp64, (I*P) x (I*P)) = sum over (a, b) of X[a, x, b] X[a, y, b].

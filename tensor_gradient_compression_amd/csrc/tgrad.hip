@@ -48,6 +48,7 @@ struct tgrad_handle {
   std::vector<int> fmodes;   // compressed modes, ascending
   bool can_fuse = false;     // last two modes compressed and a slab fits in LDS
   bool fuse = false;         // use the two-mode launches
+  bool slab2 = true;         // 16-bit data: the wave-per-slab two-mode kernels where they fit
 
   uint32_t* omega = nullptr;
   uint64_t* mask = nullptr;
@@ -56,6 +57,7 @@ struct tgrad_handle {
   float *core = nullptr, *ucore = nullptr, *mC = nullptr, *vC = nullptr;
   float* buf[2] = {nullptr, nullptr};
   void* resid = nullptr;         // refresh: G with Omega zeroed (shares buf's memory)
+  void* gcopy = nullptr;         // step without the folded gather: the residual (N elements)
   float* U[TGRAD_MAX_NDIM] = {nullptr};
   float* Mp[TGRAD_MAX_NDIM] = {nullptr};
   float* Mr[TGRAD_MAX_NDIM] = {nullptr};
@@ -137,6 +139,10 @@ void free_all(tgrad_t* h) {
   h->recs.clear();
   for (auto e : h->pool) (void)hipEventDestroy(e);
   h->pool.clear();
+}
+
+uint64_t dt_bytes(int dtype) {
+  return dtype == TGRAD_C64 ? 8 : (dtype == TGRAD_F32 ? 4 : 2);
 }
 
 // (A, I, B) view of mode n of a tensor with the given current sizes.
@@ -466,6 +472,13 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
     if (K2 > gmax) gmax = K2;
   }
   ok = ok && dalloc(h, &h->gram_part, gpart, false);
+  // the unfused launch plan projects a residual copy of grad (the fused one zeroes Omega
+  // in its staged tiles)
+  if (h->k > 0 && !h->can_fuse) {
+    unsigned char* gc = nullptr;
+    ok = ok && dalloc(h, &gc, N * dt_bytes(dtype), false);
+    h->gcopy = gc;
+  }
   h->gram_stride = gmax;
   ok = ok && dalloc(h, &h->gram, gmax * h->fmodes.size(), false);
   const uint64_t units = topk_units(N);
@@ -523,7 +536,7 @@ int tgrad_refresh(tgrad_t* h, const void* grad, void* stream) {
   return do_refresh(h, grad, (hipStream_t)stream);
 }
 
-int tgrad_step(tgrad_t* h, void* weight, void* grad, void* stream) {
+int tgrad_step(tgrad_t* h, void* weight, const void* grad, void* stream) {
   if (!h || !weight || !grad || ((uintptr_t)grad & 15u) != 0) return TGRAD_EINVAL;
   DevGuard gd(h->device);
   hipStream_t s = (hipStream_t)stream;
@@ -543,13 +556,23 @@ int tgrad_step(tgrad_t* h, void* weight, void* grad, void* stream) {
   // the COO gather runs on its own unless the first projection launch is the fused
   // two-mode one, which takes S and zeroes Omega on its staged input
   const bool gather_fused = h->k > 0 && !proj.empty() && proj[0].size() == 2;
+  // the first projection's input: grad itself, or (when the gather is not folded into
+  // it) a copy of grad that the gather turns into the residual; grad is only read
+  const void* G0 = grad;
   if (h->k > 0 && !gather_fused) {
+    if (!h->gcopy) {
+      h->err = "no residual workspace for the unfused launch plan";
+      return TGRAD_EHIP;
+    }
+    HIPCHK(h, hipMemcpyAsync(h->gcopy, grad, (size_t)h->N * dt_bytes(h->dtype),
+                             hipMemcpyDeviceToDevice, s));
     Mark m(h, KID_GATHER);
-    HIPCHK(h, launch_gather(h->dtype, grad, h->omega, (uint32_t)h->k, h->S, s));
+    HIPCHK(h, launch_gather(h->dtype, h->gcopy, h->omega, (uint32_t)h->k, h->S, s));
+    G0 = h->gcopy;
   }
   int64_t cur[TGRAD_MAX_NDIM];
   for (int i = 0; i < h->d; ++i) cur[i] = h->shape[i];
-  const void* X = grad;
+  const void* X = G0;
   int xdt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
   int which = 0;
   const size_t nf = h->fmodes.size();
@@ -582,7 +605,10 @@ int tgrad_step(tgrad_t* h, void* weight, void* grad, void* stream) {
       }
       {
         Mark m(h, KID_PROJECT_FUSED2);
-        HIPCHK(h, launch_modeprod2(mp, h->num_cu, s));
+        if (h->slab2 && slab2_supported(mp, h->num_cu))
+          HIPCHK(h, launch_slab2(mp, h->num_cu, s));
+        else
+          HIPCHK(h, launch_modeprod2(mp, h->num_cu, s));
       }
       cur[d - 2] = h->ranks[d - 2];
       cur[d - 1] = h->ranks[d - 1];
@@ -618,7 +644,7 @@ int tgrad_step(tgrad_t* h, void* weight, void* grad, void* stream) {
   a.lam = (float)h->lam;
   {
     Mark m(h, KID_ADAM);
-    const void* gcore = nf ? (const void*)h->core : (const void*)grad;
+    const void* gcore = nf ? (const void*)h->core : G0;
     const int cdt = nf ? DT_F32 : h->dtype;
     HIPCHK(h, launch_adam(cdt, gcore, h->ucore, h->mC, h->vC, h->ncore * P, h->S, h->mS, h->vS,
                           h->k * P, a, s));
@@ -666,7 +692,10 @@ int tgrad_step(tgrad_t* h, void* weight, void* grad, void* stream) {
       mp.has_sparse = h->k > 0;
       {
         Mark m(h, last ? KID_RECON_FUSED2_APPLY : KID_RECON_FUSED2);
-        HIPCHK(h, launch_modeprod2(mp, h->num_cu, s));
+        if (h->slab2 && slab2_supported(mp, h->num_cu))
+          HIPCHK(h, launch_slab2(mp, h->num_cu, s));
+        else
+          HIPCHK(h, launch_modeprod2(mp, h->num_cu, s));
       }
       cur[d - 2] = h->shape[d - 2];
       cur[d - 1] = h->shape[d - 1];
@@ -973,9 +1002,16 @@ int tgrad_set_options(tgrad_t* h, const tgrad_options* o) {
 }
 
 int tgrad_set_fusion(tgrad_t* h, int enable) {
-  if (!h) return TGRAD_EINVAL;
+  if (!h || enable < 0 || enable > 2) return TGRAD_EINVAL;
   if (enable && !h->can_fuse) return TGRAD_EINVAL;
+  if (!enable && h->k > 0 && !h->gcopy) {
+    DevGuard g(h->device);
+    unsigned char* gc = nullptr;
+    if (!dalloc(h, &gc, h->N * dt_bytes(h->dtype), false)) return TGRAD_ENOMEM;
+    h->gcopy = gc;
+  }
   h->fuse = enable != 0;
+  h->slab2 = enable != 2;
   return TGRAD_OK;
 }
 

@@ -1,8 +1,7 @@
 """GPU parity: the HIP library (through its C ABI) against the CPU oracle.
 
 Omega must match bit for bit; factor subspaces within 1e-4 (projector max-abs); weights
-within the bar of gpu_helpers.weight_check; the residual left in the gradient bit for
-bit. Inputs come from the seeded generator in synth/."""
+within the bar of gpu_helpers.weight_check; the gradient left untouched by a step. Inputs come from the seeded generator in synth/."""
 import numpy as np
 import pytest
 
@@ -98,6 +97,11 @@ FACTOR_CASES = [
     ("odd-5mode", custom((9, 7, 5, 11, 3), "f32", (4, 3, 5, 2, 1), 0.05)),
     ("narrow-lastmode-64", custom((3, 5, 64), "f32", (2, 5, 12), 0.1)),
     ("bf16-odd", custom((33, 17, 60), "bf16", (13, 8, 31), 0.05)),
+    # 16-bit tensors whose two trailing modes take the wave-per-slab kernels
+    ("bf16-slab-48x25", custom((6, 5, 48, 25), "bf16", (3, 3, 24, 13), 0.05)),
+    ("f16-slab-40x17", custom((9, 40, 17), "f16", (5, 20, 9), 0.05)),
+    ("bf16-slab-ragged", custom((7, 33, 24), "bf16", (4, 17, 12), 0.05)),
+    ("bf16-slab-k0", custom((5, 16, 8), "bf16", (3, 8, 4), 0.0)),
     ("f16-64", custom((64, 20, 9), "f16", (32, 7, 4), 0.05)),
     ("c64-small", custom((12, 10, 9), "c64", (5, 4, 3), 0.05)),
     ("c64-64", custom((64, 6, 33), "c64", (32, 6, 16), 0.05)),
@@ -133,11 +137,13 @@ STEP_CASES = FACTOR_CASES + [
 ]
 
 
-@pytest.mark.parametrize("fused", [True, False], ids=["fused", "one-mode"])
+@pytest.mark.parametrize("fused", [1, 2, 0], ids=["fused", "fused-tiles", "one-mode"])
 @pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: c[0])
 def test_steps_with_pinned_omega_and_factors(case, fused):
     """Omega and U(n) injected from the oracle, so only the step kernels are compared;
-    both launch plans (two trailing modes per launch, one mode per launch)."""
+    every launch plan (two trailing modes per launch with the default kernel choice, which
+    is one wave per slab for small 16-bit slabs; the same with workgroup tiles only; one
+    mode per launch)."""
     name, wl = case
     gs = GradStream(wl, seed=8)
     W0 = init_weights(wl, seed=8)
@@ -159,10 +165,9 @@ def test_steps_with_pinned_omega_and_factors(case, fused):
         lib.step(W, G)
         Wo = orc.step(Wo, g)
         torch.cuda.synchronize()
-        # the gradient buffer holds the residual, bit for bit
-        R = O.encode(orc.last["R"], wl.dtype) if wl.dtype != "c64" else orc.last["R"].astype(np.complex64)
-        assert np.array_equal(host(G, wl.dtype).view(np.uint8), np.ascontiguousarray(R).view(np.uint8)), \
-            f"{name}: residual differs at step {step + 1}"
+        # the gradient is only read
+        assert np.array_equal(host(G, wl.dtype).view(np.uint8), np.ascontiguousarray(g).view(np.uint8)), \
+            f"{name}: the step wrote to grad at step {step + 1}"
         weight_check(host(W, wl.dtype), Wo, wl.dtype, f"{name} step {step + 1}")
         g = gs.next()
     mc, vc, ms, vs = lib.get_moments()
@@ -365,12 +370,11 @@ def test_config4_full_size_refresh_and_step():
     om = lib.get_omega()
     keys = O.topk_keys(g, wl.dtype)
     omega_properties(keys, om, wl.k)
-    Rg = host(G, wl.dtype)
+    assert np.array_equal(host(G, wl.dtype).view(np.uint8), g.view(np.uint8))   # only read
     R32 = O.decode(g, wl.dtype).reshape(-1).copy()
     R32[om] = 0
-    assert np.array_equal(O.decode(Rg, wl.dtype).reshape(-1), R32)
     R = R32.reshape(wl.shape)
-    del R32, Rg
+    del R32
     Us = []
     for n in range(5):
         Ug = lib.get_factor(n)
