@@ -7,8 +7,8 @@ T = 200 steps; synthetic seeded inputs (Tucker low-rank signal + N(0, 0.01) nois
 Laplace(5) outliers, see synth/gen.py).
 
 A timed step is one tgrad_step on a fresh gradient buffer already resident in HBM
-(every buffer is staged before timing starts; the step writes the residual into its
-gradient). The refresh (top-k + Gram + eigensolver) runs before step 1 during warm-up
+(every buffer is staged before timing starts, so no step re-reads a gradient another
+step has left in the caches; the step only reads its gradient). The refresh (top-k + Gram + eigensolver) runs before step 1 during warm-up
 and is timed on its own with tgrad_refresh. Per-kernel durations come from HIP events
 that the library records on the launch stream around every launch in the timed region.
 
