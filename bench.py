@@ -12,6 +12,9 @@ step has left in the caches; the step only reads its gradient). The refresh (top
 and is timed on its own with tgrad_refresh. Per-kernel durations come from HIP events
 that the library records on the launch stream around every launch in the timed region.
 
+Beside the headline it reports, in "multi_tensor", the 4-layer fp16 (64,64,64,64)
+workload stepped layer after layer and as one tgrad_step_many call.
+
 Prints ONE JSON line. --gpus N with N > 1 exits: this build runs on one GPU.
 """
 from __future__ import annotations
@@ -125,6 +128,43 @@ def counter_traffic(kernel):
     return None
 
 
+def multi_tensor(dev, stream, steps=10, warmup=3):
+    """The 4-layer fp16 (64,64,64,64) workload: one optimizer step of all four layers,
+    issued layer after layer with tgrad_step on one stream, and as one tgrad_step_many
+    call (the layers' kernels overlap on internal streams). Milliseconds per 4-layer
+    step, after the warm-up steps (step 1 refreshes every layer)."""
+    import torch
+    import tensor_gradient_compression_amd as tg
+    from synth import CONFIGS, GradStream, init_weights
+    wl = CONFIGS[2]
+    L = wl.layers
+    out = {"workload": f"fp16 {L} x (64,64,64,64), Tucker ranks (32,32,32,32), 5% sparse"}
+    for mode in ("sequential", "step_many"):
+        libs = [tg.TGrad(wl.shape, wl.ranks, wl.dtype, wl.sparse_ratio, wl.T, wl.lr, wl.betas,
+                         wl.eps) for _ in range(L)]
+        G = [tg.to_device(GradStream(wl, seed=0, layer=l).next(), wl.dtype, dev) for l in range(L)]
+        W = [tg.to_device(init_weights(wl, seed=0, layer=l), wl.dtype, dev) for l in range(L)]
+
+        def one():
+            if mode == "sequential":
+                for l in range(L):
+                    libs[l].step(W[l], G[l], stream)
+            else:
+                tg.step_many(libs, W, G, stream)
+        for _ in range(warmup):
+            one()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            one()
+        torch.cuda.synchronize()
+        out[mode + "_ms"] = round((time.perf_counter() - t0) * 1e3 / steps, 4)
+        for lib in libs:
+            lib.close()
+        del G, W
+    return out
+
+
 def cpu_baseline(wl, seed=0):
     """The oracle (numpy, fp64 contractions) timed on this host on a bounded sample: one
     non-refresh step of the full workload, with Omega a seeded random index set of size
@@ -159,6 +199,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--refresh-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-multi-tensor", action="store_true",
+                    help="skip the 4-layer fp16 sequential vs tgrad_step_many measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -255,9 +297,12 @@ def main():
     step_frac = step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS
     moved_frac = moved_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS
 
+    del grads
+    torch.cuda.empty_cache()
+    multi = None if args.no_multi_tensor else multi_tensor(dev, stream)
+
     cpu = None
     if not args.no_cpu_baseline:
-        del grads
         torch.cuda.empty_cache()
         cpu = cpu_baseline(wl)
 
@@ -286,6 +331,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "refresh_kernels": refresh_kernels,
+        "multi_tensor": multi,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

@@ -95,6 +95,21 @@ int tgrad_init(tgrad_t **out, int ndim, const int64_t *shape, const int64_t *tuc
 int tgrad_step(tgrad_t *h, void *weight, const void *grad, void *stream);
 
 /*
+ * Several tensors' steps as one call (many small FNO layers per optimizer step):
+ * tgrad_step(hs[i], weights[i], grads[i], .) for i < n, issued on up to four internal
+ * streams (per device, created on first use, default priority) that start after the
+ * work already queued on `stream`; `stream` then waits for all of them, so later work
+ * on it sees every update. The tensors' kernels overlap on the device, filling the
+ * tail of each launch with another tensor's work; each handle's results are bit for
+ * bit those of tgrad_step. The handles must be distinct and on one device; calls are
+ * serialised by an internal mutex. Errors: TGRAD_EINVAL (n < 0, a NULL array or entry,
+ * a grad not 16-byte aligned, a repeated handle, handles on different devices), or the
+ * first failing step's status (the steps before it are issued and joined).
+ */
+int tgrad_step_many(tgrad_t *const *hs, void *const *weights, const void *const *grads, int n,
+                    void *stream);
+
+/*
  * Refresh Omega and the Tucker factors from `grad` (device, N elements of dtype,
  * 16-byte aligned):
  * Omega = the k largest magnitudes (ties to the lowest linear index), stored

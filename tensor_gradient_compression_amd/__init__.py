@@ -57,6 +57,8 @@ SIGNATURES = [
                                   ctypes.c_double]),
     ("tgrad_step", ctypes.c_int, [_P, _P, _P, _P]),
     ("tgrad_refresh", ctypes.c_int, [_P, _P, _P]),
+    ("tgrad_step_many", ctypes.c_int, [ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P),
+                                       ctypes.c_int, _P]),
     ("tgrad_destroy", ctypes.c_int, [_P]),
     ("tgrad_status_string", ctypes.c_char_p, [ctypes.c_int]),
     ("tgrad_last_error", ctypes.c_char_p, [_P]),
@@ -103,6 +105,24 @@ def kernel_name(i: int) -> str:
 
 def _ptr(a: np.ndarray):
     return ctypes.c_void_p(a.ctypes.data) if a is not None else None
+
+
+def step_many(handles, weights, grads, stream=None):
+    """One step of each (handle, weight, grad) triple in one call (tgrad_step_many): the
+    tensors' kernels overlap on internal streams joined back to `stream`."""
+    n = len(handles)
+    if len(weights) != n or len(grads) != n:
+        raise ValueError("handles, weights and grads differ in length")
+    lib = load_library()
+    hs = (_P * max(n, 1))(*[h._h.value for h in handles])
+    ws = (_P * max(n, 1))(*[w.data_ptr() for w in weights])
+    gs = (_P * max(n, 1))(*[g.data_ptr() for g in grads])
+    rc = lib.tgrad_step_many(hs, ws, gs, n, TGrad._stream(stream))
+    if rc != OK:
+        msg = lib.tgrad_status_string(rc).decode()
+        if n:
+            msg += ": " + lib.tgrad_last_error(handles[0]._h).decode()
+        raise TGradError(f"tgrad_step_many: {msg}")
 
 
 class TGrad:

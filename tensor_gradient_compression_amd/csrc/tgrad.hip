@@ -12,6 +12,7 @@
 //   residual (Omega masked on load) -> Jacobi eigensolver -> U(n) and operand matrices.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -102,6 +103,34 @@ struct DevGuard {
     if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
   }
 };
+
+// Streams and events for tgrad_step_many: per device, created on first use and kept for
+// the life of the process; default priority. One mutex serialises the calls.
+constexpr int kManyStreams = 4;
+struct ManyPool {
+  bool ready = false;
+  hipStream_t st[kManyStreams] = {};
+  hipEvent_t fork = nullptr;
+  hipEvent_t join[kManyStreams] = {};
+};
+std::mutex g_many_mu;
+std::vector<ManyPool> g_many;
+
+hipError_t many_pool(int dev, ManyPool** out) {
+  if ((int)g_many.size() <= dev) g_many.resize(dev + 1);
+  ManyPool& p = g_many[dev];
+  if (!p.ready) {
+    hipError_t e;
+    for (int i = 0; i < kManyStreams; ++i)
+      if ((e = hipStreamCreateWithFlags(&p.st[i], hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&p.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    for (int i = 0; i < kManyStreams; ++i)
+      if ((e = hipEventCreateWithFlags(&p.join[i], hipEventDisableTiming)) != hipSuccess) return e;
+    p.ready = true;
+  }
+  *out = &p;
+  return hipSuccess;
+}
 
 int fail_hip(tgrad_t* h, hipError_t e, const char* what) {
   if (h) {
@@ -527,6 +556,40 @@ int tgrad_destroy(tgrad_t* h) {
   }
   delete h;
   return TGRAD_OK;
+}
+
+int tgrad_step_many(tgrad_t* const* hs, void* const* weights, const void* const* grads, int n,
+                    void* stream) {
+  if (n < 0 || (n > 0 && (!hs || !weights || !grads))) return TGRAD_EINVAL;
+  if (n == 0) return TGRAD_OK;
+  for (int i = 0; i < n; ++i) {
+    if (!hs[i] || !weights[i] || !grads[i] || ((uintptr_t)grads[i] & 15u) != 0)
+      return TGRAD_EINVAL;
+    if (hs[i]->device != hs[0]->device) return TGRAD_EINVAL;
+    for (int j = 0; j < i; ++j)
+      if (hs[j] == hs[i]) return TGRAD_EINVAL;   // one handle's steps must stay ordered
+  }
+  std::lock_guard<std::mutex> lock(g_many_mu);
+  tgrad_t* h0 = hs[0];
+  DevGuard gd(h0->device);
+  ManyPool* p = nullptr;
+  HIPCHK(h0, many_pool(h0->device, &p));
+  const hipStream_t s = (hipStream_t)stream;
+  const int ns = n < kManyStreams ? n : kManyStreams;
+  // fork: every pool stream starts after the work already on the caller's stream
+  HIPCHK(h0, hipEventRecord(p->fork, s));
+  for (int i = 0; i < ns; ++i) HIPCHK(h0, hipStreamWaitEvent(p->st[i], p->fork, 0));
+  int rc = TGRAD_OK;
+  int launched = 0;
+  for (int i = 0; i < n && rc == TGRAD_OK; ++i, ++launched)
+    rc = tgrad_step(hs[i], weights[i], grads[i], p->st[i % ns]);
+  // join: the caller's stream waits for every pool stream that received work
+  const int used = launched < ns ? launched : ns;
+  for (int i = 0; i < used; ++i) {
+    HIPCHK(h0, hipEventRecord(p->join[i], p->st[i]));
+    HIPCHK(h0, hipStreamWaitEvent(s, p->join[i], 0));
+  }
+  return rc;
 }
 
 int tgrad_refresh(tgrad_t* h, const void* grad, void* stream) {

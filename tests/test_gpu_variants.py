@@ -239,3 +239,53 @@ def test_remap_checkpoint_resume_is_exact():
     assert np.array_equal(host(Wa, wl.dtype).view(np.uint8), host(Wb, wl.dtype).view(np.uint8))
     for x, y in zip(a.get_moments(), c.get_moments()):
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+# --------------------------------------------------------------------------- many tensors
+
+def test_step_many_matches_separate_steps():
+    """Three tensors of different shapes and dtypes stepped together on internal streams
+    across a refresh give, per tensor, bit for bit the weights, moments, Omega and
+    factors of stepping each alone; the caller's stream sees the updates."""
+    wls = [custom((6, 5, 48, 25), "bf16", (3, 3, 24, 13), 0.05, T=3),
+           CONFIGS[1],
+           custom((12, 10, 9), "c64", (5, 4, 3), 0.05, T=3)]
+    nsteps = 5
+    grads = []
+    for wl in wls:
+        gs = GradStream(wl, seed=9)
+        grads.append([dev(gs.next(), wl.dtype) for _ in range(nsteps)])
+    solo, many = [], []
+    Ws, Wm = [], []
+    for wl in wls:
+        solo.append(make_lib(wl, T=3))
+        many.append(make_lib(wl, T=3))
+        W0 = init_weights(wl, seed=9)
+        Ws.append(dev(W0, wl.dtype))
+        Wm.append(dev(W0, wl.dtype))
+    for t in range(nsteps):
+        for i in range(len(wls)):
+            solo[i].step(Ws[i], grads[i][t])
+        tg.step_many(many, Wm, [grads[i][t] for i in range(len(wls))])
+    # work queued on the caller's stream after the call sees the updated weights
+    sums = [w.float().sum() if w.dtype != torch.complex64 else torch.view_as_real(w).sum() for w in Wm]
+    torch.cuda.synchronize()
+    for i, wl in enumerate(wls):
+        a, b = host(Ws[i], wl.dtype), host(Wm[i], wl.dtype)
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), wl.name
+        ref = O.real_view(O.decode(b, wl.dtype)).astype(np.float64).sum()
+        assert abs(float(sums[i]) - ref) <= 1e-3 * max(1.0, abs(ref))
+        for x, y in zip(solo[i].get_moments(), many[i].get_moments()):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+        assert np.array_equal(solo[i].get_omega(), many[i].get_omega())
+        assert solo[i].t == many[i].t == nsteps
+
+
+def test_step_many_rejects_a_repeated_handle():
+    wl = CONFIGS[0]
+    lib = make_lib(wl)
+    W = dev(init_weights(wl), wl.dtype)
+    G = dev(GradStream(wl).next(), wl.dtype)
+    with pytest.raises(tg.TGradError, match="invalid argument"):
+        tg.step_many([lib, lib], [W, W], [G, G])
+    assert lib.t == 0

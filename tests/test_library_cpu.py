@@ -102,3 +102,14 @@ def test_default_options_are_the_plain_method(lib):
         (0.0, 1.0, tg.SELECT_TOPK, 0, 0)
     assert lib.tgrad_set_options(None, ctypes.byref(o)) == tg.EINVAL
     assert lib.tgrad_get_options(None, ctypes.byref(o)) == tg.EINVAL
+
+
+def test_step_many_argument_checks_need_no_device(lib):
+    """tgrad_step_many validates its arguments before any device work: n = 0 is a no-op,
+    a negative count or NULL arrays are EINVAL."""
+    P = ctypes.c_void_p
+    assert lib.tgrad_step_many(None, None, None, 0, None) == tg.OK
+    assert lib.tgrad_step_many(None, None, None, -1, None) == tg.EINVAL
+    assert lib.tgrad_step_many(None, None, None, 2, None) == tg.EINVAL
+    hs = (P * 1)(None)
+    assert lib.tgrad_step_many(hs, hs, hs, 1, None) == tg.EINVAL
