@@ -11,24 +11,25 @@
 //                   O[i1, i2] = sum_j2 Y[i1, j2] M2[i2, j2]     (mode d)
 //                   W <- round(W * decay - lr * (O + N_S at Omega))
 //
-// Organisation. Every wave owns a contiguous run of slabs and a private slice of LDS;
-// no workgroup barrier is used. While a wave computes slab n, the DMA engine brings the
-// input of slab n + 1 (global_load_lds, 16-byte pieces; the reconstruction also brings
-// the weights of slab n), and the Omega indices (and N_S) of slab n + 1 and the bitmask
-// word that bounds slab n + 2's Omega range arrive in registers. The output of slab n
-// leaves at the start of slab n + 1, before that slab's transfers are issued, and is
-// waited for only after slab n + 1 has been computed. A wave's LDS operations execute
-// in issue order, so data passed between its lanes through LDS needs no barrier.
+// Organisation. Wave w of a grid of TW waves takes slabs w, w + TW, w + 2 TW, ... (the
+// grid moves through the tensor as one window) and owns a private slice of LDS; no
+// workgroup barrier is used. While a wave computes a slab, the DMA engine brings the
+// input of its next slab (global_load_lds, 16-byte pieces; the reconstruction also
+// brings the weights of the current slab), and the Omega indices (and N_S) of the next
+// slab and the bitmask words that bound the slab after it arrive in registers. A slab's
+// output leaves at the start of the wave's next slab, before that slab's transfers are
+// issued, and is waited for only after that slab has been computed. A wave's LDS
+// operations execute in issue order, so data passed between its lanes through LDS
+// needs no barrier.
 //
-// Arithmetic. The first product of each direction runs on v_mfma_f32_16x16x32_bf16:
-// every fp32 operand there (the factor matrices, the reconstruction's input) is split
-// into three bf16 parts, x = x0 + x1 + x2 with |x - x0 - x1 - x2| <= 2^-27 |x| (bf16
-// keeps fp32's exponent range, so each part takes the next 8 significand bits); bf16
-// data are exact as they are and fp16 data split exactly into two bf16 parts. Every
-// part product is exact in fp32; those whose parts' orders sum above 2 (each below
-// 2^-24 of the full product) are dropped, so the result agrees with an fp32 GEMM to the
-// level of fp32 rounding. The second product takes the fp32 intermediate as it is, on
-// v_mfma_f32_16x16x4_f32. Accumulation is fp32 throughout.
+// Arithmetic. The projection's first product (mode d) runs on v_mfma_f32_16x16x32_bf16:
+// the factor matrix is split into three bf16 parts, x = x0 + x1 + x2 with
+// |x - x0 - x1 - x2| <= 2^-27 |x| (bf16 keeps fp32's exponent range, so each part takes
+// the next 8 significand bits); bf16 data are exact as they are and fp16 data split
+// exactly into two bf16 parts. Every part product is exact in fp32; those whose parts'
+// orders sum above 2 (each below 2^-24 of the full product) are dropped, so the result
+// agrees with an fp32 GEMM to the level of fp32 rounding. Every other product takes fp32
+// operands as they are, on v_mfma_f32_16x16x4_f32. Accumulation is fp32 throughout.
 #include "tg_common.h"
 
 namespace tg {
@@ -60,12 +61,13 @@ struct S2K {
   uint64_t kS;          // |Omega|; 0: no sparse part
   uint32_t A, I1, I2, R1, R2;
   uint32_t slab_e;      // I1 * I2
-  uint32_t spw_q, spw_r;   // slabs per wave: spw_q, plus one for the first spw_r waves
   uint32_t lds_wave;       // LDS bytes per wave
   uint32_t off_b1, off_y, off_o;   // per-wave byte offsets (second input buffer, Y, output)
   uint32_t off_w0;      // reconstruction: the W buffer
   uint32_t ly;          // row stride (floats) of the fp32 intermediate in LDS
   uint32_t ydelta;      // reconstruction: float offset of Y inside the output region
+  uint32_t trash;       // float offset (in the output region) of 64 per-lane slots that
+                        // take the writes of padding lanes, so no write needs a branch
   float lr, decay;
 };
 
@@ -89,16 +91,6 @@ __device__ __forceinline__ void split2(float x, unsigned short& a, unsigned shor
 __device__ __forceinline__ f4 mma(const u16x8& a, const u16x8& b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-// sum over the kept part products of (a0 + a1 + a2)(b0 + b1 + b2): the six with
-// i + j <= 2, small terms first
-__device__ __forceinline__ f4 mma_3x3(const u16x8* a, const u16x8* b, f4 c) {
-  c = mma(a[2], b[0], c);
-  c = mma(a[1], b[1], c);
-  c = mma(a[0], b[2], c);
-  c = mma(a[1], b[0], c);
-  c = mma(a[0], b[1], c);
-  return mma(a[0], b[0], c);
 }
 // (a0 + a1)(b0 + b1 + b2) for exact two-part data: the five with i + j <= 2
 __device__ __forceinline__ f4 mma_2x3(const u16x8& a0, const u16x8& a1, const u16x8* b, f4 c) {
@@ -124,6 +116,10 @@ __device__ __forceinline__ void wave_dma(const void* src, uint32_t nchunks, LDS 
       __builtin_amdgcn_global_load_lds((const unsigned char*)src + (size_t)(q0 + lane) * 16,
                                        (lds_void*)(dst + (size_t)q0 * 16), 16, 0, 0);
 }
+
+// Wave w takes slabs w, w + TW, w + 2 TW, ... (TW = waves in the grid), so the whole
+// grid streams through one moving window of the tensor.
+__device__ __forceinline__ uint32_t total_waves() { return gridDim.x * (uint32_t)WPB; }
 
 // Omega rank of element e from its bitmask word and word rank; kS past the end
 __device__ __forceinline__ uint64_t rank_at(uint64_t word, uint32_t wr, uint64_t e, uint64_t N,
@@ -151,16 +147,16 @@ template <> struct Bits16<_Float16> {
   }
 };
 
-// Omega range of a slab: J(s) = Omega rank of element s * slab_e. A wave keeps J(n) and
-// J(n + 1), the first NOM * 64 indices (and N_S) of slab n + 1's range in registers,
-// and the bitmask word and rank that give J(n + 2); entries past NOM * 64 in one slab
-// are read directly.
+// Omega range of slab s: [J(s), J(s + 1)) with J(s) = Omega rank of element s * slab_e.
+// A wave keeps the current slab's range, the next slab's range, the first NOM * 64
+// indices (and N_S) of the next slab's range, and the bitmask words and ranks that
+// bound the slab after it; entries past NOM * 64 in one slab are read directly.
 constexpr int NOM = 3;
 
 struct OmegaPipe {
-  uint64_t jn = 0, jn1 = 0;
-  uint64_t wnext = 0;
-  uint32_t rnext = 0;
+  uint64_t jlo = 0, jhi = 0;      // current slab
+  uint64_t nlo = 0, nhi = 0;      // next slab
+  uint64_t bw[4] = {0, 0, 0, 0};  // the slab after: mask, rank at its start; mask, rank at its end
   uint32_t om_c[NOM], om_n[NOM];
   float us_c[NOM], us_n[NOM];
 };
@@ -179,9 +175,9 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t gw = blockIdx.x * WPB + wv;
-  const uint32_t s0 = gw * k.spw_q + (gw < k.spw_r ? gw : k.spw_r);
-  const uint32_t s1 = s0 + k.spw_q + (gw < k.spw_r ? 1u : 0u);
-  if (s0 >= s1) return;
+  if (gw >= k.A) return;
+  const uint32_t TW = total_waves();
+  const uint32_t cnt = (k.A - 1 - gw) / TW + 1;   // slabs of this wave
   LDS unsigned char* const base = (LDS unsigned char*)smem + wv * k.lds_wave;
   LDS unsigned char* const xb0 = base;
   LDS unsigned char* const xb1 = base + k.off_b1;
@@ -216,55 +212,62 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
 
   const XT* X = (const XT*)k.X;
   const uint32_t xchunks = slab_e * 2 / 16;
-  auto bound_word = [&](uint32_t s) -> uint64_t {
-    const uint64_t e = (uint64_t)s * slab_e;
-    return e < N ? e >> 6 : 0;
+  // bitmask words and ranks at the start and the end of slab s, and its Omega range
+  // (uniform over the wave and read-only here: scalar loads, which retire on lgkmcnt and
+  // leave the vector memory queue to the slab transfers)
+  auto bounds = [&](uint32_t s, uint64_t* w) {
+    const uint64_t elo = (uint64_t)s * slab_e, ehi = elo + slab_e;
+    const uint64_t wl = elo >> 6, wh = ehi < N ? ehi >> 6 : 0;
+    const __attribute__((address_space(4))) uint64_t* m =
+        (const __attribute__((address_space(4))) uint64_t*)k.mask;
+    const __attribute__((address_space(4))) uint32_t* r =
+        (const __attribute__((address_space(4))) uint32_t*)k.rank;
+    w[0] = m[wl];
+    w[1] = r[wl];
+    w[2] = m[wh];
+    w[3] = r[wh];
+  };
+  auto range = [&](uint32_t s, const uint64_t* w, uint64_t& lo, uint64_t& hi) {
+    lo = rank_at(w[0], (uint32_t)w[1], (uint64_t)s * slab_e, N, kS);
+    hi = rank_at(w[2], (uint32_t)w[3], (uint64_t)(s + 1) * slab_e, N, kS);
   };
   OmegaPipe op;
   if (sparse) {
-    const uint64_t w0 = bound_word(s0), w1 = bound_word(s0 + 1);
-    op.jn = rank_at(k.mask[w0], k.rank[w0], (uint64_t)s0 * slab_e, N, kS);
-    op.jn1 = rank_at(k.mask[w1], k.rank[w1], (uint64_t)(s0 + 1) * slab_e, N, kS);
+    uint64_t w[4];
+    bounds(gw, w);
+    range(gw, w, op.jlo, op.jhi);
 #pragma unroll
     for (int i = 0; i < NOM; ++i) {
-      const uint64_t j = op.jn + lane + 64 * i;
+      const uint64_t j = op.jlo + lane + 64 * i;
       op.om_c[i] = k.omega[j < kS ? j : kS - 1];
     }
-    if (s0 + 2 <= s1) {
-      const uint64_t w2 = bound_word(s0 + 2);
-      op.wnext = k.mask[w2];
-      op.rnext = k.rank[w2];
-    }
+    if (cnt > 1) bounds(gw + TW, op.bw);
   }
-  wave_dma(X + (uint64_t)s0 * slab_e, xchunks, xb0, lane);
+  wave_dma(X + (uint64_t)gw * slab_e, xchunks, xb0, lane);
 
   uint32_t nq_prev = 0;
   uint64_t out_prev = 0;
-  for (uint32_t n = s0; n < s1; ++n) {
-    const int cur = (n - s0) & 1;
-    wait_vm0();   // slab n, its Omega indices and the next bound have landed
+  for (uint32_t i = 0; i < cnt; ++i) {
+    const uint32_t n = gw + i * TW;   // this slab
+    const int cur = i & 1;
+    wait_vm0();   // slab n, its Omega indices and the next slab's bounds have landed
     wave_fence();
-    uint64_t jn2 = 0;
-    if (sparse && n + 2 <= s1) jn2 = rank_at(op.wnext, op.rnext, (uint64_t)(n + 2) * slab_e, N, kS);
+    if (sparse && i + 1 < cnt) range(n + TW, op.bw, op.nlo, op.nhi);
     // the previous slab's output leaves (waited for at the next slab)
     for (uint32_t q = lane; q < nq_prev; q += 64)
       *(f4*)(k.Y + out_prev + 4 * q) = *(const LDS f4*)(So + 4 * q);
     wait_lgkm0();
     wave_fence();
     // next slab's transfer, Omega indices and range bound
-    if (n + 1 < s1) {
-      wave_dma(X + (uint64_t)(n + 1) * slab_e, xchunks, cur ? xb0 : xb1, lane);
+    if (i + 1 < cnt) {
+      wave_dma(X + (uint64_t)(n + TW) * slab_e, xchunks, cur ? xb0 : xb1, lane);
       if (sparse) {
 #pragma unroll
-        for (int i = 0; i < NOM; ++i) {
-          const uint64_t j = op.jn1 + lane + 64 * i;
-          op.om_n[i] = k.omega[j < kS ? j : kS - 1];
+        for (int q = 0; q < NOM; ++q) {
+          const uint64_t j = op.nlo + lane + 64 * q;
+          op.om_n[q] = k.omega[j < kS ? j : kS - 1];
         }
-        if (n + 3 <= s1) {
-          const uint64_t w3 = bound_word(n + 3);
-          op.wnext = k.mask[w3];
-          op.rnext = k.rank[w3];
-        }
+        if (i + 2 < cnt) bounds(n + 2 * TW, op.bw);
       }
     }
 
@@ -282,18 +285,18 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
       float sv[NOM];
 #pragma unroll
       for (int i = 0; i < NOM; ++i) {
-        const uint64_t j = op.jn + lane + 64 * i;
-        sv[i] = j < op.jn1 ? Bits16<XT>::value(xs[(uint32_t)(op.om_c[i] - e_lo)]) : 0.0f;
+        const uint64_t j = op.jlo + lane + 64 * i;
+        sv[i] = j < op.jhi ? Bits16<XT>::value(xs[(uint32_t)(op.om_c[i] - e_lo)]) : 0.0f;
       }
 #pragma unroll
       for (int i = 0; i < NOM; ++i) {
-        const uint64_t j = op.jn + lane + 64 * i;
-        if (j < op.jn1) {
+        const uint64_t j = op.jlo + lane + 64 * i;
+        if (j < op.jhi) {
           k.S[j] = sv[i];
           xs[(uint32_t)(op.om_c[i] - e_lo)] = 0;
         }
       }
-      for (uint64_t j = op.jn + 64 * NOM + lane; j < op.jn1; j += 64) take(j, k.omega[j]);
+      for (uint64_t j = op.jlo + 64 * NOM + lane; j < op.jhi; j += 64) take(j, k.omega[j]);
       wave_fence();
     }
 
@@ -343,15 +346,15 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const uint32_t j1 = 16 * rb + 4 * lg + v;
-        if (j1 < R1 && li < R2) So[j1 * R2 + li] = acc2[rb][v];
+        So[(j1 < R1 && li < R2) ? j1 * R2 + li : k.trash + lane] = acc2[rb][v];
       }
     wave_fence();
     nq_prev = R1 * R2 / 4;
     out_prev = (uint64_t)n * R1 * R2;
-    op.jn = op.jn1;
-    op.jn1 = jn2;
+    op.jlo = op.nlo;
+    op.jhi = op.nhi;
 #pragma unroll
-    for (int i = 0; i < NOM; ++i) op.om_c[i] = op.om_n[i];
+    for (int q = 0; q < NOM; ++q) op.om_c[q] = op.om_n[q];
   }
   // the last slab's output
   wait_lgkm0();
@@ -360,18 +363,21 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
 }
 
 // ------------------------------------------------------------------ reconstruction
-// NRB1: 16-row blocks of I1 (<= 64); NCB2: 16-column blocks of I2 (<= 32); R1 <= 32,
-// R2 <= 16. Pass 1 (mode d-1) on bf16 MFMAs with Z and M1 in three parts each; pass 2
-// (mode d) on v_mfma_f32_16x16x4_f32 with k index j2 = 4 (lane / 16) + step.
-template <typename WT, int NRB1, int NCB2>
+// NRB1: 16-row blocks of I1 (<= 64); NCB2: 16-column blocks of I2 (<= 32); KS1: fp32
+// MFMA k-steps of pass 1 (R1 <= 4 KS1 <= 32); R2 <= 16. Both products run on
+// v_mfma_f32_16x16x4_f32 straight from fp32 data: pass 1 (mode d-1) with k index
+// j1 = KS1 (lane / 16) + step, pass 2 (mode d) with j2 = 4 (lane / 16) + step; the factor
+// operands stay in registers, and pass 1's row blocks are independent accumulation
+// chains interleaved step by step.
+template <typename WT, int NRB1, int NCB2, int KS1>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8))) k_rec2s(S2K k) {
   extern __shared__ float smem[];
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t gw = blockIdx.x * WPB + wv;
-  const uint32_t s0 = gw * k.spw_q + (gw < k.spw_r ? gw : k.spw_r);
-  const uint32_t s1 = s0 + k.spw_q + (gw < k.spw_r ? 1u : 0u);
-  if (s0 >= s1) return;
+  if (gw >= k.A) return;
+  const uint32_t TW = total_waves();
+  const uint32_t cnt = (k.A - 1 - gw) / TW + 1;   // slabs of this wave
   LDS unsigned char* const base = (LDS unsigned char*)smem + wv * k.lds_wave;
   LDS unsigned char* const zb0 = base;
   LDS unsigned char* const zb1 = base + k.off_b1;
@@ -387,17 +393,14 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
   const float lr = k.lr, decay = k.decay;
   const bool decayed = decay != 1.0f;
 
-  // pass 1 A[row = i1][k = j1] = M1[i1][j1] in three bf16 parts
-  u16x8 a1[NRB1][3];
+  // pass 1 A[row = i1][k = j1] = M1[i1][j1], j1 = KS1 lg + step
+  float a1[NRB1][KS1];
 #pragma unroll
   for (int rb = 0; rb < NRB1; ++rb)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t i1 = 16 * rb + li, j1 = 8 * lg + e;
-      const float v = (i1 < I1 && j1 < R1) ? k.M1[i1 * R1 + j1] : 0.0f;
-      unsigned short a, b, c;
-      split3(v, a, b, c);
-      a1[rb][0][e] = a; a1[rb][1][e] = b; a1[rb][2][e] = c;
+    for (int t = 0; t < KS1; ++t) {
+      const uint32_t i1 = 16 * rb + li, j1 = KS1 * lg + t;
+      a1[rb][t] = (i1 < I1 && j1 < R1) ? k.M1[i1 * R1 + j1] : 0.0f;
     }
   // pass 2 B[k = j2][col = i2] = M2[i2][j2], j2 = 4 lg + step
   float b2[NCB2][4];
@@ -411,38 +414,49 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
 
   const WT* Wg = (const WT*)k.W;
   const uint32_t zchunks = slab_z * 4 / 16, wchunks = slab_e * 2 / 16;
-  auto bound_word = [&](uint32_t s) -> uint64_t {
-    const uint64_t e = (uint64_t)s * slab_e;
-    return e < N ? e >> 6 : 0;
+  // bitmask words and ranks at the start and the end of slab s, and its Omega range
+  // (uniform over the wave and read-only here: scalar loads, which retire on lgkmcnt and
+  // leave the vector memory queue to the slab transfers)
+  auto bounds = [&](uint32_t s, uint64_t* w) {
+    const uint64_t elo = (uint64_t)s * slab_e, ehi = elo + slab_e;
+    const uint64_t wl = elo >> 6, wh = ehi < N ? ehi >> 6 : 0;
+    const __attribute__((address_space(4))) uint64_t* m =
+        (const __attribute__((address_space(4))) uint64_t*)k.mask;
+    const __attribute__((address_space(4))) uint32_t* r =
+        (const __attribute__((address_space(4))) uint32_t*)k.rank;
+    w[0] = m[wl];
+    w[1] = r[wl];
+    w[2] = m[wh];
+    w[3] = r[wh];
+  };
+  auto range = [&](uint32_t s, const uint64_t* w, uint64_t& lo, uint64_t& hi) {
+    lo = rank_at(w[0], (uint32_t)w[1], (uint64_t)s * slab_e, N, kS);
+    hi = rank_at(w[2], (uint32_t)w[3], (uint64_t)(s + 1) * slab_e, N, kS);
   };
   OmegaPipe op;
   if (sparse) {
-    const uint64_t w0 = bound_word(s0), w1 = bound_word(s0 + 1);
-    op.jn = rank_at(k.mask[w0], k.rank[w0], (uint64_t)s0 * slab_e, N, kS);
-    op.jn1 = rank_at(k.mask[w1], k.rank[w1], (uint64_t)(s0 + 1) * slab_e, N, kS);
+    uint64_t w[4];
+    bounds(gw, w);
+    range(gw, w, op.jlo, op.jhi);
 #pragma unroll
     for (int i = 0; i < NOM; ++i) {
-      const uint64_t j = op.jn + lane + 64 * i;
+      const uint64_t j = op.jlo + lane + 64 * i;
       const uint64_t jc = j < kS ? j : kS - 1;
       op.om_c[i] = k.omega[jc];
       op.us_c[i] = k.S[jc];
     }
-    if (s0 + 2 <= s1) {
-      const uint64_t w2 = bound_word(s0 + 2);
-      op.wnext = k.mask[w2];
-      op.rnext = k.rank[w2];
-    }
+    if (cnt > 1) bounds(gw + TW, op.bw);
   }
-  wave_dma(k.Zin + (uint64_t)s0 * slab_z, zchunks, zb0, lane);
+  wave_dma(k.Zin + (uint64_t)gw * slab_z, zchunks, zb0, lane);
 
   uint32_t nq_prev = 0;
   uint64_t out_prev = 0;
-  for (uint32_t n = s0; n <= s1; ++n) {
-    const int cur = (n - s0) & 1;
-    wait_vm0();   // Z of slab n, W of slab n - 1, Omega data; the stores of slab n - 2
+  for (uint32_t i = 0; i <= cnt; ++i) {
+    const uint32_t n = gw + i * TW;   // this slab (i < cnt)
+    const int cur = i & 1;
+    wait_vm0();   // Z of this slab, W of the previous one, Omega data; older stores
     wave_fence();
-    uint64_t jn2 = 0;
-    if (sparse && n + 2 <= s1) jn2 = rank_at(op.wnext, op.rnext, (uint64_t)(n + 2) * slab_e, N, kS);
+    if (sparse && i + 1 < cnt) range(n + TW, op.bw, op.nlo, op.nhi);
     // the previous slab: W <- round(W * decay - lr * O), 16-byte pieces (the stores are
     // waited for at the next slab)
     for (uint32_t q = lane; q < nq_prev; q += 64) {
@@ -467,46 +481,45 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
       }
       *(uint4*)((WT*)k.W + out_prev + 8 * q) = *(const uint4*)o;
     }
-    if (n == s1) break;
+    if (i == cnt) break;
     wait_lgkm0();
     wave_fence();
     // this slab's W (used at the next slab), the next slab's Z and Omega data
     wave_dma(Wg + (uint64_t)n * slab_e, wchunks, wb, lane);
-    if (n + 1 < s1) {
-      wave_dma(k.Zin + (uint64_t)(n + 1) * slab_z, zchunks, cur ? zb0 : zb1, lane);
+    if (i + 1 < cnt) {
+      wave_dma(k.Zin + (uint64_t)(n + TW) * slab_z, zchunks, cur ? zb0 : zb1, lane);
       if (sparse) {
 #pragma unroll
-        for (int i = 0; i < NOM; ++i) {
-          const uint64_t j = op.jn1 + lane + 64 * i;
+        for (int q = 0; q < NOM; ++q) {
+          const uint64_t j = op.nlo + lane + 64 * q;
           const uint64_t jc = j < kS ? j : kS - 1;
-          op.om_n[i] = k.omega[jc];
-          op.us_n[i] = k.S[jc];
+          op.om_n[q] = k.omega[jc];
+          op.us_n[q] = k.S[jc];
         }
-        if (n + 3 <= s1) {
-          const uint64_t w3 = bound_word(n + 3);
-          op.wnext = k.mask[w3];
-          op.rnext = k.rank[w3];
-        }
+        if (i + 2 < cnt) bounds(n + 2 * TW, op.bw);
       }
     }
 
     const LDS float* const zs = (const LDS float*)(cur ? zb1 : zb0);
     // pass 1 (mode d-1): rows i1, k = j1, columns j2
-    u16x8 zp[3];
+    float zv[KS1];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t j1 = 8 * lg + e;
-      const float v = (j1 < R1 && li < R2) ? zs[j1 * R2 + li] : 0.0f;
-      unsigned short a, b, c;
-      split3(v, a, b, c);
-      zp[0][e] = a; zp[1][e] = b; zp[2][e] = c;
+    for (int t = 0; t < KS1; ++t) {
+      const uint32_t j1 = KS1 * lg + t;
+      zv[t] = (j1 < R1 && li < R2) ? zs[j1 * R2 + li] : 0.0f;
     }
+    f4 acc1[NRB1];
 #pragma unroll
-    for (int rb = 0; rb < NRB1; ++rb) {
-      const f4 acc = mma_3x3(a1[rb], zp, f4{0.f, 0.f, 0.f, 0.f});
+    for (int rb = 0; rb < NRB1; ++rb) acc1[rb] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int v = 0; v < 4; ++v) Yb[(16 * rb + 4 * lg + v) * LY + li] = acc[v];
-    }
+    for (int t = 0; t < KS1; ++t)
+#pragma unroll
+      for (int rb = 0; rb < NRB1; ++rb)
+        acc1[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[rb][t], zv[t], acc1[rb], 0, 0, 0);
+#pragma unroll
+    for (int rb = 0; rb < NRB1; ++rb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Yb[(16 * rb + 4 * lg + v) * LY + li] = acc1[rb][v];
     wave_fence();
     // pass 2 (mode d): rows i1, k = j2, columns i2; Y's block rb is read before O's
     // block rb is written over it (their placement keeps block rb + 1 intact)
@@ -527,21 +540,26 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const uint32_t i1 = 16 * rb + 4 * lg + v, i2 = 16 * cb + li;
-          if (i1 < I1 && i2 < I2) Ob[i1 * I2 + i2] = acc[cb][v];
+          Ob[(i1 < I1 && i2 < I2) ? i1 * I2 + i2 : k.trash + lane] = acc[cb][v];
         }
     }
     wave_fence();
     if (sparse) {
       const uint64_t e_lo = (uint64_t)n * slab_e;
+      // the prefetched entries: all reads, then all writes (distinct elements; lanes
+      // past the range use their trash slot)
+      uint32_t loc[NOM];
+      float cv[NOM];
 #pragma unroll
       for (int i = 0; i < NOM; ++i) {
-        const uint64_t j = op.jn + lane + 64 * i;
-        if (j < op.jn1) {
-          const uint32_t loc = (uint32_t)(op.om_c[i] - e_lo);
-          Ob[loc] = Ob[loc] + op.us_c[i];
-        }
+        const uint64_t j = op.jlo + lane + 64 * i;
+        loc[i] = j < op.jhi ? (uint32_t)(op.om_c[i] - e_lo) : k.trash + lane;
       }
-      for (uint64_t j = op.jn + 64 * NOM + lane; j < op.jn1; j += 64) {
+#pragma unroll
+      for (int i = 0; i < NOM; ++i) cv[i] = Ob[loc[i]];
+#pragma unroll
+      for (int i = 0; i < NOM; ++i) Ob[loc[i]] = cv[i] + op.us_c[i];
+      for (uint64_t j = op.jlo + 64 * NOM + lane; j < op.jhi; j += 64) {
         const uint32_t loc = (uint32_t)(k.omega[j] - e_lo);
         Ob[loc] = Ob[loc] + k.S[j];
       }
@@ -549,12 +567,12 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
     }
     nq_prev = slab_e / 8;
     out_prev = (uint64_t)n * slab_e;
-    op.jn = op.jn1;
-    op.jn1 = jn2;
+    op.jlo = op.nlo;
+    op.jhi = op.nhi;
 #pragma unroll
-    for (int i = 0; i < NOM; ++i) {
-      op.om_c[i] = op.om_n[i];
-      op.us_c[i] = op.us_n[i];
+    for (int q = 0; q < NOM; ++q) {
+      op.om_c[q] = op.om_n[q];
+      op.us_c[q] = op.us_n[q];
     }
   }
 }
@@ -598,7 +616,8 @@ Plan2s plan2s(const ModeProd2& mp, int num_cu) {
     uint32_t off = al16(slab_e * 2);
     k.off_b1 = off; off += al16(slab_e * 2);
     k.off_y = off; off += al16(16 * k.ly * 4);
-    k.off_o = off; off += al16(R1 * R2 * 4);
+    k.off_o = off; off += al16((R1 * R2 + 64) * 4);
+    k.trash = R1 * R2;
     k.lds_wave = off;
   } else {
     p.nrb2 = (int)((I2 + 15) / 16);
@@ -615,7 +634,8 @@ Plan2s plan2s(const ModeProd2& mp, int num_cu) {
     uint32_t off = al16(R1 * R2 * 4);
     k.off_b1 = off; off += al16(R1 * R2 * 4);
     k.off_w0 = off; off += al16(slab_e * 2);
-    k.off_o = off; off += al16(ofl * 4);
+    k.off_o = off; off += al16((ofl + 64) * 4);
+    k.trash = ofl;
     k.lds_wave = off;
   }
   p.lds = (size_t)k.lds_wave * WPB;
@@ -625,7 +645,7 @@ Plan2s plan2s(const ModeProd2& mp, int num_cu) {
 }
 
 // One resident round of workgroups (as many as the kernel's registers and LDS let a CU
-// hold), each wave taking a contiguous run of slabs.
+// hold); wave w takes every TW-th slab from slab w.
 template <typename F>
 hipError_t launch2s(F fn, Plan2s p, hipStream_t s) {
   int per_cu = 0;
@@ -636,9 +656,6 @@ hipError_t launch2s(F fn, Plan2s p, hipStream_t s) {
   const uint64_t need = ((uint64_t)p.k.A + WPB - 1) / WPB;
   if (grid > need) grid = need;
   if (grid < 1) grid = 1;
-  const uint64_t waves = grid * WPB;
-  p.k.spw_q = (uint32_t)(p.k.A / waves);
-  p.k.spw_r = (uint32_t)(p.k.A % waves);
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(NT), p.lds, s, p.k);
   return hipGetLastError();
 }
@@ -657,10 +674,22 @@ hipError_t proj_go(const Plan2s& p, hipStream_t s) {
     default: return proj_nrb2<XT, 4>(p, s);
   }
 }
+template <typename WT, int NRB1, int NCB2>
+hipError_t rec_ks(const Plan2s& p, hipStream_t s) {
+  switch ((p.k.R1 + 3) / 4) {
+    case 1:
+    case 2: return launch2s(k_rec2s<WT, NRB1, NCB2, 2>, p, s);
+    case 3:
+    case 4: return launch2s(k_rec2s<WT, NRB1, NCB2, 4>, p, s);
+    case 5:
+    case 6: return launch2s(k_rec2s<WT, NRB1, NCB2, 6>, p, s);
+    default: return launch2s(k_rec2s<WT, NRB1, NCB2, 8>, p, s);
+  }
+}
 template <typename WT, int NRB1>
 hipError_t rec_ncb(const Plan2s& p, hipStream_t s) {
-  if (p.nrb2 == 1) return launch2s(k_rec2s<WT, NRB1, 1>, p, s);
-  return launch2s(k_rec2s<WT, NRB1, 2>, p, s);
+  if (p.nrb2 == 1) return rec_ks<WT, NRB1, 1>(p, s);
+  return rec_ks<WT, NRB1, 2>(p, s);
 }
 template <typename WT>
 hipError_t rec_go(const Plan2s& p, hipStream_t s) {
