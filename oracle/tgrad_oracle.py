@@ -312,7 +312,8 @@ class TGradOracle:
     step(W, G): returns the new W (storage dtype) [NT 三 step order; PITH Theorem 2]."""
 
     def __init__(self, shape, ranks, dtype, sparse_ratio, T, lr, beta1, beta2, eps,
-                 weight_decay=0.0, sparse_scale=1.0, selection="topk", remap=False, seed=0):
+                 weight_decay=0.0, sparse_scale=1.0, selection="topk", remap=False, seed=0,
+                 order="sparse_first"):
         self.shape = tuple(int(s) for s in shape)
         self.ranks = tuple(int(r) for r in ranks)
         if dtype not in DTYPES:
@@ -344,6 +345,11 @@ class TGradOracle:
         self.selection = selection
         self.remap = bool(remap)
         self.seed = int(seed)
+        # decomposition order ([PITH] free parameters: "US -> LR", sparse then low-rank,
+        # chosen by ablation; the reverse is the alternative it is compared with)
+        if order not in ("sparse_first", "lowrank_first"):
+            raise ValueError(order)
+        self.order = order
 
     def refresh_due(self, t: int) -> bool:
         return (t - 1) % self.T == 0
@@ -355,6 +361,9 @@ class TGradOracle:
             serves = self.t + 1
         G = np.asarray(G).reshape(self.shape)
         old = self.omega
+        if self.order == "lowrank_first":
+            self._refresh_lowrank_first(G, serves, old)
+            return
         if self.selection == "topk":
             keys = topk_keys(G, self.dtype)
         else:
@@ -364,6 +373,10 @@ class TGradOracle:
             self.mS = remap_moments(old, self.omega, self.mS, self.P)
             self.vS = remap_moments(old, self.omega, self.vS, self.P)
         R = residual(decode(G, self.dtype), self.omega)
+        self._factors_from(R)
+        self.refreshed_for = serves
+
+    def _factors_from(self, R: np.ndarray):
         for n, (I, r) in enumerate(zip(self.shape, self.ranks)):
             if r >= I:
                 self.factors[n] = None
@@ -372,6 +385,28 @@ class TGradOracle:
             else:
                 U, w, gap = hosvd_factor(R, n, r)
                 self.factors[n], self.eigvals[n], self.gaps[n] = U, w, gap
+
+    def lowrank_part(self, G32: np.ndarray) -> np.ndarray:
+        """L = (G x_n Un^H ...) x_n Un ... with the core rounded to fp32 in between, as
+        the optimizer state keeps it, and L rounded to fp32."""
+        C32 = project(G32, self.factors).astype(np.complex64 if self.P == 2 else np.float32)
+        return reconstruct(C32, self.factors).astype(C32.dtype)
+
+    def _refresh_lowrank_first(self, G: np.ndarray, serves: int, old: np.ndarray):
+        """Low-rank first: the Tucker factors from the HOSVD of the whole gradient, then
+        Omega = the k largest entries of the fp32 residual G - L (by the same keys and tie
+        rule as the sparse-first order; random sampling ignores the residual)."""
+        G32 = decode(G, self.dtype)
+        self._factors_from(G32)
+        if self.selection == "topk":
+            R32 = G32 - self.lowrank_part(G32)
+            keys = topk_keys(R32, "c64" if self.P == 2 else "f32")
+        else:
+            keys = randk_keys(self.N, self.seed, serves)
+        self.omega = select_omega(keys, self.k)
+        if self.remap:
+            self.mS = remap_moments(old, self.omega, self.mS, self.P)
+            self.vS = remap_moments(old, self.omega, self.vS, self.P)
         self.refreshed_for = serves
 
     def step(self, W: np.ndarray, G: np.ndarray) -> np.ndarray:
@@ -382,8 +417,15 @@ class TGradOracle:
         if self.refresh_due(t) and self.refreshed_for != t:
             self.refresh(G, t)
         G32 = decode(G, self.dtype)
-        S = gather(G32, self.omega)
-        R = residual(G32, self.omega)
+        if self.order == "lowrank_first":
+            # the low-rank part of the whole gradient, then the sparse part of what it
+            # leaves: S = (G - L)[Omega] in fp32
+            R = G32
+            L32 = self.lowrank_part(G32)
+            S = gather(G32 - L32, self.omega)
+        else:
+            S = gather(G32, self.omega)
+            R = residual(G32, self.omega)
         C = project(R, self.factors)
         C32 = C.astype(np.complex64 if self.P == 2 else np.float32)
         uC, self.mC, self.vC = adam(real_view(C32), self.mC, self.vC, t,

@@ -644,3 +644,79 @@ def test_refresh_every_step_when_T_is_one():
     for _ in range(4):
         W = o.step(W, gs.next())
     assert calls == [1, 2, 3, 4]
+
+
+# --------------------------------------------------------------------------- low-rank-first order
+
+def test_lowrank_first_with_k0_is_the_sparse_first_method():
+    """With no sparse part the two orders are the same method: weights bit for bit."""
+    wl = custom((8, 7, 6), "bf16", (4, 3, 3), 0.0, T=2)
+    a = O.TGradOracle(wl.shape, wl.ranks, "bf16", 0.0, 2, wl.lr, *wl.betas, wl.eps)
+    b = O.TGradOracle(wl.shape, wl.ranks, "bf16", 0.0, 2, wl.lr, *wl.betas, wl.eps,
+                      order="lowrank_first")
+    gs, W = GradStream(wl, seed=4), init_weights(wl, seed=4)
+    Wa, Wb = W, W
+    for _ in range(5):
+        g = gs.next()
+        Wa, Wb = a.step(Wa, g), b.step(Wb, g)
+        assert np.array_equal(Wa, Wb)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "c64"])
+def test_lowrank_first_with_full_ranks_is_dense_adam(dtype):
+    """Full ranks: the low-rank part is the whole gradient, so the residual is exactly
+    zero, Omega is the first k indices (all keys tie), S = 0 contributes nothing, and
+    the step is dense Adam: checked against torch.optim.Adam over 10 steps."""
+    shape = (6, 5, 4, 3)
+    wl = custom(shape, dtype, shape, 0.2, T=5, steps=10, signal_ranks=(2, 2, 2, 2))
+    gs = GradStream(wl, seed=21)
+    W = init_weights(wl, seed=21)
+    grads = [gs.next() for _ in range(10)]
+    o = O.TGradOracle(shape, shape, dtype, 0.2, 5, wl.lr, *wl.betas, wl.eps, order="lowrank_first")
+    Wo = W
+    for g in grads:
+        Wo = o.step(Wo, g)
+        assert np.array_equal(o.omega, np.arange(o.k, dtype=np.uint32))
+        assert not np.any(o.last["S"])
+    ref = _torch_adam_run(W, grads, wl)
+    got = O.decode(Wo, dtype)
+    assert np.abs(got - ref).max() / np.abs(ref).max() <= 1e-6
+
+
+def test_sparse_first_approximates_better_than_lowrank_first():
+    """The pages' ablation direction (pith.science free parameters: the order is chosen
+    by ablation; nullthought summary section 5: sparse first beats low-rank first): with
+    1% Laplace outliers in the gradient, ||G - (L + S)|| / ||G|| after a refresh is at
+    least twice as large when the Tucker factors are fitted before the outliers are
+    removed."""
+    wl = custom((16, 16, 8, 8), "f32", (8, 8, 4, 4), 0.05, signal_ranks=(4, 4, 2, 2))
+    G = O.decode(GradStream(wl, seed=8).next(), "f32")
+    err = {}
+    for order in ("sparse_first", "lowrank_first"):
+        o = O.TGradOracle(wl.shape, wl.ranks, "f32", 0.05, 1, 1e-3, 0.9, 0.999, 1e-8, order=order)
+        o.refresh(G)
+        om = o.omega.astype(np.int64)
+        base = O.residual(G, o.omega) if order == "sparse_first" else G
+        L = O.reconstruct(O.project(base, o.factors), o.factors)
+        S = (G if order == "sparse_first" else G - L).reshape(-1)[om]
+        approx = L.reshape(-1).copy()
+        approx[om] += S
+        err[order] = np.linalg.norm(G.reshape(-1) - approx) / np.linalg.norm(G)
+    assert err["lowrank_first"] >= 2 * err["sparse_first"], err
+
+
+def test_lowrank_first_omega_is_topk_of_its_residual():
+    """After a low-rank-first refresh, Omega is the k largest |G - L| (brute force by
+    sorting on a small tensor), L the projection of G onto the refreshed factors."""
+    wl = custom((9, 8, 7), "f32", (4, 4, 3), 0.1)
+    G = O.decode(GradStream(wl, seed=2).next(), "f32")
+    o = O.TGradOracle(wl.shape, wl.ranks, "f32", 0.1, 1, 1e-3, 0.9, 0.999, 1e-8, order="lowrank_first")
+    o.refresh(G)
+    L = O.reconstruct(O.project(G, o.factors).astype(np.float32), o.factors).astype(np.float32)
+    mag = np.abs((G - L).reshape(-1)).astype(np.float64)
+    order = sorted(range(mag.size), key=lambda e: (-mag[e], e))[:o.k]
+    assert np.array_equal(o.omega, np.array(sorted(order), np.uint32))
+    # and the factors are the HOSVD of G itself
+    for n, U in enumerate(o.factors):
+        Ug = O.hosvd_factor(G, n, wl.ranks[n])[0]
+        assert np.allclose(U @ U.T, Ug @ Ug.T, atol=1e-6)
