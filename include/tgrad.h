@@ -199,16 +199,27 @@ int tgrad_set_fusion(tgrad_t *h, int enable);
  *                  new to Omega starts from zero moments. Enabling it allocates two more
  *                  k*P fp32 buffers and a second bitmask (synchronises the device).
  *   seed           rand-k base seed.
+ *   order          the decomposition order (pith.science lists "sparse then low-rank" as
+ *                  the tuned choice; the nullthought summary reports the reverse as
+ *                  worse): TGRAD_ORDER_SPARSE_FIRST (default), or
+ *                  TGRAD_ORDER_LOWRANK_FIRST: a refresh takes the Tucker factors from the
+ *                  HOSVD of G itself and Omega as the top-k of the fp32 residual G - L,
+ *                  L = (G x_n Un^H ...) x_n Un ... with the core in fp32; a step projects
+ *                  the whole G to the core, reconstructs L and takes S = (G - L)[Omega].
+ *                  Enabling it allocates an N-element fp32 workspace (complex: 2N).
  * Options take effect at the next step or refresh. Errors: TGRAD_EINVAL (NULL, a
- * negative or non-finite weight_decay, a non-finite sparse_scale, an unknown selection or
- * remap value), TGRAD_ENOMEM, TGRAD_EHIP. */
+ * negative or non-finite weight_decay, a non-finite sparse_scale, an unknown selection,
+ * remap or order value), TGRAD_ENOMEM, TGRAD_EHIP. */
 enum tgrad_selection { TGRAD_SELECT_TOPK = 0, TGRAD_SELECT_RANDK = 1 };
+enum tgrad_order { TGRAD_ORDER_SPARSE_FIRST = 0, TGRAD_ORDER_LOWRANK_FIRST = 1 };
 typedef struct tgrad_options {
   double weight_decay;
   double sparse_scale;
   int32_t selection;
   int32_t remap_moments;
   uint64_t seed;
+  int32_t order;
+  int32_t reserved;   /* 0 */
 } tgrad_options;
 void tgrad_default_options(tgrad_options *out);
 int tgrad_set_options(tgrad_t *h, const tgrad_options *opt);

@@ -41,10 +41,13 @@ SELECT_TOPK, SELECT_RANDK = 0, 1
 SELECTIONS = {"topk": SELECT_TOPK, "randk": SELECT_RANDK}
 
 
+ORDERS = {"sparse_first": 0, "lowrank_first": 1}
+
+
 class Options(ctypes.Structure):
     _fields_ = [("weight_decay", ctypes.c_double), ("sparse_scale", ctypes.c_double),
                 ("selection", ctypes.c_int32), ("remap_moments", ctypes.c_int32),
-                ("seed", ctypes.c_uint64)]
+                ("seed", ctypes.c_uint64), ("order", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 # (name, restype, argtypes) of every exported symbol declared in include/tgrad.h
@@ -244,20 +247,23 @@ class TGrad:
         self._check(self._lib.tgrad_set_factor(self._h, mode, _ptr(flat), flat.size), "tgrad_set_factor")
 
     def set_options(self, weight_decay: float = 0.0, sparse_scale: float = 1.0,
-                    selection: str = "topk", remap_moments: bool = False, seed: int = 0):
+                    selection: str = "topk", remap_moments: bool = False, seed: int = 0,
+                    order: str = "sparse_first"):
         """Variants of the method (include/tgrad.h, tgrad_options): decoupled weight decay,
-        the sparse scale factor lambda, rand-k selection of Omega, and sparse moments that
-        follow their element across a refresh. The defaults are the plain method."""
+        the sparse scale factor lambda, rand-k selection of Omega, sparse moments that
+        follow their element across a refresh, and the low-rank-first decomposition
+        order. The defaults are the plain method."""
         o = Options(float(weight_decay), float(sparse_scale), SELECTIONS[selection],
-                    int(bool(remap_moments)), int(seed) & 0xFFFFFFFFFFFFFFFF)
+                    int(bool(remap_moments)), int(seed) & 0xFFFFFFFFFFFFFFFF, ORDERS[order], 0)
         self._check(self._lib.tgrad_set_options(self._h, ctypes.byref(o)), "tgrad_set_options")
 
     def get_options(self) -> dict:
         o = Options()
         self._check(self._lib.tgrad_get_options(self._h, ctypes.byref(o)), "tgrad_get_options")
         sel = {v: k for k, v in SELECTIONS.items()}[o.selection]
+        order = {v: k for k, v in ORDERS.items()}[o.order]
         return dict(weight_decay=o.weight_decay, sparse_scale=o.sparse_scale, selection=sel,
-                    remap_moments=bool(o.remap_moments), seed=o.seed)
+                    remap_moments=bool(o.remap_moments), seed=o.seed, order=order)
 
     def set_fusion(self, enable) -> bool:
         """Select fused two-mode launches (True or 1: default kernel choice; 2: workgroup

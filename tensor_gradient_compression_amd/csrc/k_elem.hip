@@ -10,6 +10,9 @@
 //                 u = (m/bc1) / (sqrt(v/bc2) + eps); the sparse output is then scaled
 //                 by lambda (1 for the plain method, an exact identity). The library is built without
 //                 floating-point contraction, so no step is fused into an FMA.
+//   gather_sub,   low-rank first: S = G[Omega] - L[Omega], and the residual G - L that
+//   resid_sub:    its refresh selects Omega from (nullthought summary section 5 and
+//                 pith.science free parameters: the decomposition order is a choice).
 //   apply_dense:  the update when no mode is compressed (every r_n = I_n): Delta =
 //                 N_C, plus N_S at Omega, W <- round(W * decay - lr * Delta), decay =
 //                 fp32(1 - lr * weight_decay) (decoupled decay, exactly 1 without it).
@@ -36,6 +39,38 @@ __global__ void __launch_bounds__(256) k_gather(ST* __restrict__ G,
     for (int p = 0; p < P; ++p) {
       S[j * P + p] = to_f32(G[e * P + p]);
       G[e * P + p] = zero_of<ST>();
+    }
+  }
+}
+
+template <typename ST, int P>
+__global__ void __launch_bounds__(256) k_gather_sub(const ST* __restrict__ G,
+                                                    const float* __restrict__ L,
+                                                    const uint32_t* __restrict__ omega,
+                                                    uint32_t k, float* __restrict__ S) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < k; j += stride) {
+    const uint64_t e = omega[j];
+#pragma unroll
+    for (int p = 0; p < P; ++p) S[j * P + p] = to_f32(G[e * P + p]) - L[e * P + p];
+  }
+}
+
+// four values per thread per pass (16-byte L accesses when the tail allows)
+template <typename ST>
+__global__ void __launch_bounds__(256) k_resid_sub(const ST* __restrict__ G, float* __restrict__ L,
+                                                   uint64_t n) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x * 4;
+  for (uint64_t i = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 4 <= n) {
+      float4 l = *(const float4*)(L + i);
+      l.x = to_f32(G[i]) - l.x;
+      l.y = to_f32(G[i + 1]) - l.y;
+      l.z = to_f32(G[i + 2]) - l.z;
+      l.w = to_f32(G[i + 3]) - l.w;
+      *(float4*)(L + i) = l;
+    } else {
+      for (uint64_t q = i; q < n; ++q) L[q] = to_f32(G[q]) - L[q];
     }
   }
 }
@@ -110,6 +145,33 @@ hipError_t launch_gather(int dt, void* G, const uint32_t* omega, uint32_t k, flo
     case DT_F16: k_gather<_Float16, 1><<<b, 256, 0, s>>>((_Float16*)G, omega, k, S); break;
     case DT_BF16: k_gather<bf16_t, 1><<<b, 256, 0, s>>>((bf16_t*)G, omega, k, S); break;
     case DT_C64: k_gather<float, 2><<<b, 256, 0, s>>>((float*)G, omega, k, S); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_sub(int dt, const void* G, const float* L, const uint32_t* omega,
+                             uint32_t k, float* S, hipStream_t s) {
+  if (!k) return hipSuccess;
+  const unsigned b = grid_for(k, 256, 8192);
+  switch (dt) {
+    case DT_F32: k_gather_sub<float, 1><<<b, 256, 0, s>>>((const float*)G, L, omega, k, S); break;
+    case DT_F16: k_gather_sub<_Float16, 1><<<b, 256, 0, s>>>((const _Float16*)G, L, omega, k, S); break;
+    case DT_BF16: k_gather_sub<bf16_t, 1><<<b, 256, 0, s>>>((const bf16_t*)G, L, omega, k, S); break;
+    case DT_C64: k_gather_sub<float, 2><<<b, 256, 0, s>>>((const float*)G, L, omega, k, S); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_resid_sub(int dt, const void* G, float* L, uint64_t n, hipStream_t s) {
+  if (!n) return hipSuccess;
+  const unsigned b = grid_for((n + 3) / 4, 256, 16384);
+  switch (dt) {
+    case DT_F32:
+    case DT_C64: k_resid_sub<float><<<b, 256, 0, s>>>((const float*)G, L, n); break;
+    case DT_F16: k_resid_sub<_Float16><<<b, 256, 0, s>>>((const _Float16*)G, L, n); break;
+    case DT_BF16: k_resid_sub<bf16_t><<<b, 256, 0, s>>>((const bf16_t*)G, L, n); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

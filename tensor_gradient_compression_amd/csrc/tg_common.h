@@ -94,6 +94,11 @@ hipError_t launch_fill_u64(uint64_t* p, uint64_t n, uint64_t v, hipStream_t s);
 
 hipError_t launch_gather(int dt, void* G, const uint32_t* omega, uint32_t k, float* S,
                          hipStream_t s);
+// Low-rank first: S[j] = fp32(G[omega[j]]) - L[omega[j]] (L fp32, P values per element)
+hipError_t launch_gather_sub(int dt, const void* G, const float* L, const uint32_t* omega,
+                             uint32_t k, float* S, hipStream_t s);
+// L[i] <- fp32(G[i]) - L[i] for the n fp32 values of L (complex: re, im pairs)
+hipError_t launch_resid_sub(int dt, const void* G, float* L, uint64_t n, hipStream_t s);
 
 // core input dtype: DT_F32 for an fp32 buffer (complex: pairs, P folded into n_core)
 hipError_t launch_adam(int core_dt, const void* g_core, float* u_core, float* m_core,

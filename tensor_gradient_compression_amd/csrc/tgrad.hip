@@ -73,6 +73,8 @@ struct tgrad_handle {
   int selection = TGRAD_SELECT_TOPK;
   bool remap = false;
   uint64_t seed = 0;
+  int order = TGRAD_ORDER_SPARSE_FIRST;
+  float* lbuf = nullptr;         // low-rank first: L, then G - L (N * P fp32)
   // remapped sparse moments: the previous Omega's bitmask and ranks, and the second
   // moment buffers (allocated when remapping is first enabled)
   uint64_t* mask_prev = nullptr;
@@ -268,31 +270,45 @@ void build_chain(const tgrad_t* h, bool fuse, std::vector<std::vector<int>>& pro
   if (fuse) rec.push_back({d - 2, d - 1});
 }
 
+int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s);
+int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, float* out,
+                       hipStream_t s);
+
+// Omega (+ bitmask, ranks) as the k largest keys of `src` (storage type dt), or a random
+// k-subset; optionally the residual (src with Omega zeroed) written to `resid`. With
+// remapped moments the new bitmask goes to the other buffer, so the old one still
+// locates each element's previous moments, which then follow their element.
+int select_omega(tgrad_t* h, const void* src, int dt, void* resid, hipStream_t s) {
+  if (h->remap) {
+    std::swap(h->mask, h->mask_prev);
+    std::swap(h->rank, h->rank_prev);
+  }
+  const uint64_t gamma = 0x9E3779B97F4A7C15ull;
+  const uint64_t serves = (uint64_t)(h->t + 1);
+  const uint64_t rk_base = h->seed + gamma * ((serves << 32) + 1ull);
+  HIPCHK(h, launch_topk(dt, src, h->N, (uint32_t)h->k, h->tw, h->omega, h->mask, h->rank, resid,
+                        h->selection == TGRAD_SELECT_RANDK, rk_base, s, mark_cb, h));
+  if (h->remap) {
+    Mark m(h, KID_REMAP);
+    HIPCHK(h, launch_remap_moments(h->mask_prev, h->rank_prev, h->omega, (uint32_t)h->k,
+                                   h->P, h->mS, h->vS, h->mS_alt, h->vS_alt, s));
+    std::swap(h->mS, h->mS_alt);
+    std::swap(h->vS, h->vS_alt);
+  }
+  return TGRAD_OK;
+}
+
 int do_refresh(tgrad_t* h, const void* grad, hipStream_t s) {
-  // the Grams read the residual: G itself when k = 0, else the copy with Omega zeroed
-  // that the top-k compaction writes
+  // sparse first: Omega from G, then the Grams of the residual (G itself when k = 0,
+  // else the copy with Omega zeroed that the top-k compaction writes). Low-rank first:
+  // the Grams of G, then Omega from the residual G - L of the new factors.
+  const bool lowrank_first =
+      h->order == TGRAD_ORDER_LOWRANK_FIRST && h->k > 0 && !h->fmodes.empty();
   const void* R = grad;
-  if (h->k > 0) {
+  int rc;
+  if (h->k > 0 && !lowrank_first) {
     void* rw = h->fmodes.empty() ? nullptr : h->resid;
-    // with remapped moments the new Omega's bitmask goes to the other buffer, so the old
-    // one still locates each element's previous moments
-    if (h->remap) {
-      std::swap(h->mask, h->mask_prev);
-      std::swap(h->rank, h->rank_prev);
-    }
-    const uint64_t gamma = 0x9E3779B97F4A7C15ull;
-    const uint64_t serves = (uint64_t)(h->t + 1);
-    const uint64_t rk_base = h->seed + gamma * ((serves << 32) + 1ull);
-    HIPCHK(h, launch_topk(h->dtype, grad, h->N, (uint32_t)h->k, h->tw, h->omega, h->mask,
-                          h->rank, rw, h->selection == TGRAD_SELECT_RANDK, rk_base, s,
-                          mark_cb, h));
-    if (h->remap) {
-      Mark m(h, KID_REMAP);
-      HIPCHK(h, launch_remap_moments(h->mask_prev, h->rank_prev, h->omega, (uint32_t)h->k,
-                                     h->P, h->mS, h->vS, h->mS_alt, h->vS_alt, s));
-      std::swap(h->mS, h->mS_alt);
-      std::swap(h->vS, h->vS_alt);
-    }
+    if ((rc = select_omega(h, grad, h->dtype, rw, s)) != TGRAD_OK) return rc;
     if (rw) R = rw;
   }
   const int gdt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
@@ -322,10 +338,24 @@ int do_refresh(tgrad_t* h, const void* grad, hipStream_t s) {
     Mark m(h, KID_EIG);
     HIPCHK(h, launch_eig(eig, ne, s));
   }
+  if (lowrank_first) {
+    if (h->selection == TGRAD_SELECT_RANDK) {
+      if ((rc = select_omega(h, grad, h->dtype, nullptr, s)) != TGRAD_OK) return rc;
+    } else {
+      // R = G - (G x_n Un^H ...) x_n Un ... in fp32, then its k largest entries
+      if ((rc = run_projection(h, grad, false, s)) != TGRAD_OK) return rc;
+      if ((rc = run_reconstruction(h, h->core, false, nullptr, h->lbuf, s)) != TGRAD_OK) return rc;
+      {
+        Mark m(h, KID_GATHER);
+        HIPCHK(h, launch_resid_sub(h->dtype, grad, h->lbuf, h->N * h->P, s));
+      }
+      if ((rc = select_omega(h, h->lbuf, h->P == 2 ? DT_C64 : DT_F32, nullptr, s)) != TGRAD_OK)
+        return rc;
+    }
+  }
   h->refreshed_for = h->t + 1;
   return TGRAD_OK;
 }
-
 }  // namespace
 
 extern "C" {
@@ -599,46 +629,22 @@ int tgrad_refresh(tgrad_t* h, const void* grad, void* stream) {
   return do_refresh(h, grad, (hipStream_t)stream);
 }
 
-int tgrad_step(tgrad_t* h, void* weight, const void* grad, void* stream) {
-  if (!h || !weight || !grad || ((uintptr_t)grad & 15u) != 0) return TGRAD_EINVAL;
-  DevGuard gd(h->device);
-  hipStream_t s = (hipStream_t)stream;
-  h->cur_stream = s;
-  h->t += 1;
-  const int64_t t = h->t;
-  if ((t - 1) % h->T == 0 && h->refreshed_for != t) {
-    h->t -= 1;                       // the refresh serves step t = (current t) + 1
-    int rc = do_refresh(h, grad, s);
-    h->t += 1;
-    if (rc != TGRAD_OK) return rc;
-  }
+}  // extern "C"
+
+namespace {
+
+// Projection chain C = X x_n Un^H ... (last compressed mode first) into h->core. X has
+// the handle's storage dtype. gather: the first launch is a two-mode one that also takes
+// S = X[Omega] and projects its staged tiles with Omega zeroed.
+int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s) {
   const uint32_t P = h->P;
-  // projection: one launch per group, last compressed mode first
   std::vector<std::vector<int>> proj, rec;
   build_chain(h, h->fuse, proj, rec);
-  // the COO gather runs on its own unless the first projection launch is the fused
-  // two-mode one, which takes S and zeroes Omega on its staged input
-  const bool gather_fused = h->k > 0 && !proj.empty() && proj[0].size() == 2;
-  // the first projection's input: grad itself, or (when the gather is not folded into
-  // it) a copy of grad that the gather turns into the residual; grad is only read
-  const void* G0 = grad;
-  if (h->k > 0 && !gather_fused) {
-    if (!h->gcopy) {
-      h->err = "no residual workspace for the unfused launch plan";
-      return TGRAD_EHIP;
-    }
-    HIPCHK(h, hipMemcpyAsync(h->gcopy, grad, (size_t)h->N * dt_bytes(h->dtype),
-                             hipMemcpyDeviceToDevice, s));
-    Mark m(h, KID_GATHER);
-    HIPCHK(h, launch_gather(h->dtype, h->gcopy, h->omega, (uint32_t)h->k, h->S, s));
-    G0 = h->gcopy;
-  }
   int64_t cur[TGRAD_MAX_NDIM];
   for (int i = 0; i < h->d; ++i) cur[i] = h->shape[i];
-  const void* X = G0;
+  const void* X = X0;
   int xdt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
   int which = 0;
-  const size_t nf = h->fmodes.size();
   for (size_t j = 0; j < proj.size(); ++j) {
     float* Y = (j + 1 == proj.size()) ? h->core : h->buf[which];
     if (proj[j].size() == 2) {
@@ -658,7 +664,7 @@ int tgrad_step(tgrad_t* h, void* weight, const void* grad, void* stream) {
       mp.M1 = h->Mp[d - 2];
       mp.M2 = h->Mp[d - 1];
       mp.Y = Y;
-      if (j == 0 && gather_fused) {
+      if (j == 0 && gather) {
         mp.gather_S = h->S;
         mp.mask = h->mask;
         mp.rank = h->rank;
@@ -666,13 +672,11 @@ int tgrad_step(tgrad_t* h, void* weight, const void* grad, void* stream) {
         mp.kS = h->k;
         mp.has_sparse = 1;
       }
-      {
-        Mark m(h, KID_PROJECT_FUSED2);
-        if (h->slab2 && slab2_supported(mp, h->num_cu))
-          HIPCHK(h, launch_slab2(mp, h->num_cu, s));
-        else
-          HIPCHK(h, launch_modeprod2(mp, h->num_cu, s));
-      }
+      Mark m(h, KID_PROJECT_FUSED2);
+      if (h->slab2 && slab2_supported(mp, h->num_cu))
+        HIPCHK(h, launch_slab2(mp, h->num_cu, s));
+      else
+        HIPCHK(h, launch_modeprod2(mp, h->num_cu, s));
       cur[d - 2] = h->ranks[d - 2];
       cur[d - 1] = h->ranks[d - 1];
     } else {
@@ -686,15 +690,156 @@ int tgrad_step(tgrad_t* h, void* weight, const void* grad, void* stream) {
       mp.P = P;
       mp.apply = 0;
       mp.Y = Y;
-      {
-        Mark m(h, j == 0 ? KID_PROJECT_FIRST : KID_PROJECT);
-        HIPCHK(h, launch_modeprod(mp, h->num_cu, s));
-      }
+      Mark m(h, j == 0 ? KID_PROJECT_FIRST : KID_PROJECT);
+      HIPCHK(h, launch_modeprod(mp, h->num_cu, s));
       cur[n] = h->ranks[n];
     }
     X = Y;
     xdt = DT_F32;
     which ^= 1;
+  }
+  return TGRAD_OK;
+}
+
+// Reconstruction chain X x_1 U1 ... (first compressed mode first) from the core-sized
+// fp32 X. apply: the last launch merges N_S at Omega and updates W; otherwise it
+// writes the full fp32 tensor to out.
+int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, float* out,
+                       hipStream_t s) {
+  const uint32_t P = h->P;
+  std::vector<std::vector<int>> proj, rec;
+  build_chain(h, h->fuse, proj, rec);
+  int64_t cur[TGRAD_MAX_NDIM];
+  for (int i = 0; i < h->d; ++i) cur[i] = h->shape[i];
+  for (int n : h->fmodes) cur[n] = h->ranks[n];
+  const float lr = (float)h->lr;
+  const float decay = (float)(1.0 - h->lr * h->wd);
+  const void* X = X0;
+  int which = 0;
+  for (size_t j = 0; j < rec.size(); ++j) {
+    const bool last = (j + 1 == rec.size());
+    const bool app = last && apply;
+    float* Y = last ? (apply ? nullptr : out) : h->buf[which];
+    if (rec[j].size() == 2) {
+      const int d = h->d;
+      ModeProd2 mp{};
+      mp.X = X;
+      mp.in_dt = DT_F32;
+      mp.P = P;
+      uint32_t A, I, B;
+      view(cur, d, d - 2, &A, &I, &B);
+      mp.A = A;
+      mp.I1 = (uint32_t)cur[d - 2];
+      mp.I2 = (uint32_t)cur[d - 1];
+      mp.R1 = (uint32_t)h->shape[d - 2];
+      mp.R2 = (uint32_t)h->shape[d - 1];
+      mp.recon = 1;
+      mp.M1 = h->Mr[d - 2];
+      mp.M2 = h->Mr[d - 1];
+      mp.apply = app ? 1 : 0;
+      mp.Y = Y;
+      mp.W = weight;
+      mp.w_dt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
+      mp.mask = h->mask;
+      mp.rank = h->rank;
+      mp.uS = h->S;
+      mp.omega = h->omega;
+      mp.kS = h->k;
+      mp.lr = lr;
+      mp.decay = decay;
+      mp.has_sparse = app && h->k > 0;
+      Mark m(h, app ? KID_RECON_FUSED2_APPLY : KID_RECON_FUSED2);
+      if (h->slab2 && slab2_supported(mp, h->num_cu))
+        HIPCHK(h, launch_slab2(mp, h->num_cu, s));
+      else
+        HIPCHK(h, launch_modeprod2(mp, h->num_cu, s));
+      cur[d - 2] = h->shape[d - 2];
+      cur[d - 1] = h->shape[d - 1];
+    } else {
+      const int n = rec[j][0];
+      ModeProd mp{};
+      mp.X = X;
+      mp.in_dt = DT_F32;
+      mp.M = h->Mr[n];
+      view(cur, h->d, n, &mp.A, &mp.I, &mp.B);
+      mp.R = (uint32_t)h->shape[n];
+      mp.P = P;
+      mp.apply = app ? 1 : 0;
+      mp.Y = Y;
+      mp.W = weight;
+      mp.w_dt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
+      mp.mask = h->mask;
+      mp.rank = h->rank;
+      mp.uS = h->S;
+      mp.omega = h->omega;
+      mp.kS = h->k;
+      mp.lr = lr;
+      mp.decay = decay;
+      mp.has_sparse = app && h->k > 0;
+      Mark m(h, app ? KID_RECON_APPLY : KID_RECONSTRUCT);
+      HIPCHK(h, launch_modeprod(mp, h->num_cu, s));
+      cur[n] = h->shape[n];
+    }
+    X = Y;
+    which ^= 1;
+  }
+  return TGRAD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tgrad_step(tgrad_t* h, void* weight, const void* grad, void* stream) {
+  if (!h || !weight || !grad || ((uintptr_t)grad & 15u) != 0) return TGRAD_EINVAL;
+  DevGuard gd(h->device);
+  hipStream_t s = (hipStream_t)stream;
+  h->cur_stream = s;
+  h->t += 1;
+  const int64_t t = h->t;
+  if ((t - 1) % h->T == 0 && h->refreshed_for != t) {
+    h->t -= 1;                       // the refresh serves step t = (current t) + 1
+    int rc = do_refresh(h, grad, s);
+    h->t += 1;
+    if (rc != TGRAD_OK) return rc;
+  }
+  const uint32_t P = h->P;
+  const size_t nf = h->fmodes.size();
+  const bool lowrank_first = h->order == TGRAD_ORDER_LOWRANK_FIRST && h->k > 0;
+  const void* G0 = grad;             // the gradient the projection and dense Adam see
+  int rc;
+  if (lowrank_first) {
+    // the low-rank part of the whole gradient, then the sparse part of what it leaves:
+    // S = (G - L)[Omega] with L = C x_n Un ... in fp32
+    if (nf) {
+      if ((rc = run_projection(h, grad, false, s)) != TGRAD_OK) return rc;
+      if ((rc = run_reconstruction(h, h->core, false, nullptr, h->lbuf, s)) != TGRAD_OK) return rc;
+      Mark m(h, KID_GATHER);
+      HIPCHK(h, launch_gather_sub(h->dtype, grad, h->lbuf, h->omega, (uint32_t)h->k, h->S, s));
+    } else {
+      // every mode full rank: L = G, so S = 0
+      HIPCHK(h, launch_fill_u32((uint32_t*)h->S, h->k * P, 0u, s));
+    }
+  } else {
+    std::vector<std::vector<int>> proj, rec;
+    build_chain(h, h->fuse, proj, rec);
+    // the COO gather runs on its own unless the first projection launch is the fused
+    // two-mode one, which takes S and zeroes Omega on its staged input
+    const bool gather_fused = h->k > 0 && !proj.empty() && proj[0].size() == 2;
+    // the first projection's input: grad itself, or (when the gather is not folded into
+    // it) a copy of grad that the gather turns into the residual; grad is only read
+    if (h->k > 0 && !gather_fused) {
+      if (!h->gcopy) {
+        h->err = "no residual workspace for the unfused launch plan";
+        return TGRAD_EHIP;
+      }
+      HIPCHK(h, hipMemcpyAsync(h->gcopy, grad, (size_t)h->N * dt_bytes(h->dtype),
+                               hipMemcpyDeviceToDevice, s));
+      Mark m(h, KID_GATHER);
+      HIPCHK(h, launch_gather(h->dtype, h->gcopy, h->omega, (uint32_t)h->k, h->S, s));
+      G0 = h->gcopy;
+    }
+    if (nf && (rc = run_projection(h, G0, gather_fused, s)) != TGRAD_OK) return rc;
   }
   AdamK a;
   a.b1 = (float)h->b1;
@@ -712,87 +857,15 @@ int tgrad_step(tgrad_t* h, void* weight, const void* grad, void* stream) {
     HIPCHK(h, launch_adam(cdt, gcore, h->ucore, h->mC, h->vC, h->ncore * P, h->S, h->mS, h->vS,
                           h->k * P, a, s));
   }
-  const float lr = (float)h->lr;
-  const float decay = (float)(1.0 - h->lr * h->wd);
   if (nf == 0) {
+    const float lr = (float)h->lr;
+    const float decay = (float)(1.0 - h->lr * h->wd);
     Mark m(h, KID_APPLY_DENSE);
     HIPCHK(h, launch_apply_dense(h->dtype, weight, h->ucore, h->mask, h->rank, h->S, h->N, lr,
                                  decay, h->k > 0, s));
     return TGRAD_OK;
   }
-  X = h->ucore;
-  which = 0;
-  for (size_t j = 0; j < rec.size(); ++j) {
-    const bool last = (j + 1 == rec.size());
-    float* Y = last ? nullptr : h->buf[which];
-    if (rec[j].size() == 2) {
-      const int d = h->d;
-      ModeProd2 mp{};
-      mp.X = X;
-      mp.in_dt = DT_F32;
-      mp.P = P;
-      uint32_t A, I, B;
-      view(cur, d, d - 2, &A, &I, &B);
-      mp.A = A;
-      mp.I1 = (uint32_t)cur[d - 2];
-      mp.I2 = (uint32_t)cur[d - 1];
-      mp.R1 = (uint32_t)h->shape[d - 2];
-      mp.R2 = (uint32_t)h->shape[d - 1];
-      mp.recon = 1;
-      mp.M1 = h->Mr[d - 2];
-      mp.M2 = h->Mr[d - 1];
-      mp.apply = last ? 1 : 0;
-      mp.Y = Y;
-      mp.W = weight;
-      mp.w_dt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
-      mp.mask = h->mask;
-      mp.rank = h->rank;
-      mp.uS = h->S;
-      mp.omega = h->omega;
-      mp.kS = h->k;
-      mp.lr = lr;
-      mp.decay = decay;
-      mp.has_sparse = h->k > 0;
-      {
-        Mark m(h, last ? KID_RECON_FUSED2_APPLY : KID_RECON_FUSED2);
-        if (h->slab2 && slab2_supported(mp, h->num_cu))
-          HIPCHK(h, launch_slab2(mp, h->num_cu, s));
-        else
-          HIPCHK(h, launch_modeprod2(mp, h->num_cu, s));
-      }
-      cur[d - 2] = h->shape[d - 2];
-      cur[d - 1] = h->shape[d - 1];
-    } else {
-      const int n = rec[j][0];
-      ModeProd mp{};
-      mp.X = X;
-      mp.in_dt = DT_F32;
-      mp.M = h->Mr[n];
-      view(cur, h->d, n, &mp.A, &mp.I, &mp.B);
-      mp.R = (uint32_t)h->shape[n];
-      mp.P = P;
-      mp.apply = last ? 1 : 0;
-      mp.Y = Y;
-      mp.W = weight;
-      mp.w_dt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
-      mp.mask = h->mask;
-      mp.rank = h->rank;
-      mp.uS = h->S;
-      mp.omega = h->omega;
-      mp.kS = h->k;
-      mp.lr = lr;
-      mp.decay = decay;
-      mp.has_sparse = h->k > 0;
-      {
-        Mark m(h, last ? KID_RECON_APPLY : KID_RECONSTRUCT);
-        HIPCHK(h, launch_modeprod(mp, h->num_cu, s));
-      }
-      cur[n] = h->shape[n];
-    }
-    X = Y;
-    which ^= 1;
-  }
-  return TGRAD_OK;
+  return run_reconstruction(h, h->ucore, true, weight, nullptr, s);
 }
 
 int tgrad_get_info(const tgrad_t* h, tgrad_info* out) {
@@ -1008,6 +1081,7 @@ void tgrad_default_options(tgrad_options* out) {
   out->selection = TGRAD_SELECT_TOPK;
   out->remap_moments = 0;
   out->seed = 0;
+  out->order = TGRAD_ORDER_SPARSE_FIRST;
 }
 
 int tgrad_get_options(const tgrad_t* h, tgrad_options* out) {
@@ -1018,6 +1092,7 @@ int tgrad_get_options(const tgrad_t* h, tgrad_options* out) {
   out->selection = h->selection;
   out->remap_moments = h->remap ? 1 : 0;
   out->seed = h->seed;
+  out->order = h->order;
   return TGRAD_OK;
 }
 
@@ -1027,6 +1102,12 @@ int tgrad_set_options(tgrad_t* h, const tgrad_options* o) {
     return TGRAD_EINVAL;
   if (o->selection != TGRAD_SELECT_TOPK && o->selection != TGRAD_SELECT_RANDK) return TGRAD_EINVAL;
   if (o->remap_moments != 0 && o->remap_moments != 1) return TGRAD_EINVAL;
+  if (o->order != TGRAD_ORDER_SPARSE_FIRST && o->order != TGRAD_ORDER_LOWRANK_FIRST)
+    return TGRAD_EINVAL;
+  if (o->order == TGRAD_ORDER_LOWRANK_FIRST && h->k > 0 && !h->fmodes.empty() && !h->lbuf) {
+    DevGuard g(h->device);
+    if (!dalloc(h, &h->lbuf, h->N * h->P, false)) return TGRAD_ENOMEM;
+  }
   if (o->remap_moments && h->k > 0 && !h->mask_prev) {
     DevGuard g(h->device);
     const uint64_t ns = h->k * h->P;
@@ -1061,6 +1142,7 @@ int tgrad_set_options(tgrad_t* h, const tgrad_options* o) {
   h->selection = o->selection;
   h->remap = o->remap_moments != 0;
   h->seed = o->seed;
+  h->order = o->order;
   return TGRAD_OK;
 }
 

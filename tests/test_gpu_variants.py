@@ -187,10 +187,11 @@ def test_default_options_leave_the_step_unchanged():
         lib = make_lib(wl, T=4)
         if set_defaults:
             lib.set_options(weight_decay=0.9, sparse_scale=3.0, selection="randk",
-                            remap_moments=True, seed=8)
+                            remap_moments=True, seed=8, order="lowrank_first")
             lib.set_options()
             assert lib.get_options() == dict(weight_decay=0.0, sparse_scale=1.0,
-                                             selection="topk", remap_moments=False, seed=0)
+                                             selection="topk", remap_moments=False, seed=0,
+                                             order="sparse_first")
         gs = GradStream(wl, seed=2)
         W = dev(init_weights(wl, seed=2), wl.dtype)
         for _ in range(6):
@@ -208,9 +209,11 @@ def test_invalid_options_are_rejected():
         with pytest.raises(tg.TGradError, match="invalid argument"):
             lib.set_options(**bad)
     import ctypes
-    o = tg.Options(0.0, 1.0, 2, 0, 0)
+    o = tg.Options(0.0, 1.0, 2, 0, 0, 0, 0)
     assert lib._lib.tgrad_set_options(lib._h, ctypes.byref(o)) == tg.EINVAL
-    o = tg.Options(0.0, 1.0, 0, 2, 0)
+    o = tg.Options(0.0, 1.0, 0, 2, 0, 0, 0)
+    assert lib._lib.tgrad_set_options(lib._h, ctypes.byref(o)) == tg.EINVAL
+    o = tg.Options(0.0, 1.0, 0, 0, 0, 2, 0)
     assert lib._lib.tgrad_set_options(lib._h, ctypes.byref(o)) == tg.EINVAL
     assert lib.get_options()["selection"] == "topk"
 
@@ -289,3 +292,109 @@ def test_step_many_rejects_a_repeated_handle():
     with pytest.raises(tg.TGradError, match="invalid argument"):
         tg.step_many([lib, lib], [W, W], [G, G])
     assert lib.t == 0
+
+
+# --------------------------------------------------------------------------- low-rank first
+
+LRF_CASES = [
+    ("bf16-slab-48x25", custom((6, 5, 48, 25), "bf16", (3, 3, 24, 13), 0.05, T=3)),
+    ("config1", CONFIGS[1]),
+    ("c64-small", custom((12, 10, 9), "c64", (5, 4, 3), 0.05, T=3)),
+    ("f16-5mode", custom((9, 7, 5, 11, 4), "f16", (4, 3, 5, 2, 3), 0.05, T=3)),
+]
+
+
+def _residual32(orc, g):
+    """The oracle's fp32 residual G - L for its current factors (flattened)."""
+    G32 = O.decode(g, orc.dtype)
+    return (G32 - orc.lowrank_part(G32)).reshape(-1)
+
+
+def _mag(R):
+    return np.abs(R.astype(np.complex128 if np.iscomplexobj(R) else np.float64))
+
+
+@pytest.mark.parametrize("case", LRF_CASES, ids=lambda c: c[0])
+def test_lowrank_first_refresh(case):
+    """Low-rank-first refresh: factors (HOSVD of G itself) within the projector bar;
+    Omega is a top-k of the oracle's fp32 residual G - L up to the residual's rounding:
+    the library computes L with another fp32 summation order, so an element may trade
+    places with another only where their |G - L| lie within 1e-5 of max |G - L| of the
+    k-th largest. Agreement must cover at least 99.9% of Omega."""
+    name, wl = case
+    lib = lib_for(wl, T=3, order="lowrank_first")
+    orc = oracle_for(wl, T=3, order="lowrank_first")
+    g = GradStream(wl, seed=7).next()
+    lib.refresh(dev(g, wl.dtype))
+    orc.refresh(g)
+    torch.cuda.synchronize()
+    factor_check(lib, orc)
+    om = lib.get_omega().astype(np.int64)
+    assert om.size == orc.k and np.all(np.diff(om) > 0)
+    mag = _mag(_residual32(orc, g))
+    tau = np.sort(mag)[::-1][orc.k - 1]
+    tol = 1e-5 * mag.max()
+    sel = np.zeros(mag.size, bool)
+    sel[om] = True
+    assert mag[sel].min() >= tau - tol, (name, mag[sel].min(), tau)
+    if (~sel).any():
+        assert mag[~sel].max() <= tau + tol, (name, mag[~sel].max(), tau)
+    same = np.intersect1d(om, orc.omega.astype(np.int64)).size
+    assert same >= 0.999 * orc.k, (name, same, orc.k)
+
+
+@pytest.mark.parametrize("fused", [1, 2, 0], ids=["fused", "fused-tiles", "one-mode"])
+@pytest.mark.parametrize("case", LRF_CASES, ids=lambda c: c[0])
+def test_lowrank_first_steps_with_pinned_omega_and_factors(case, fused):
+    """Low-rank-first steps with the oracle's Omega and factors injected: S = (G - L)[Omega]
+    and the update on every launch plan, weights within the bar, sparse moments to fp32
+    rounding of L (relative 1e-5 of max |m_S|), the gradient only read."""
+    name, wl = case
+    lib = lib_for(wl, T=10 ** 6, order="lowrank_first")
+    orc = oracle_for(wl, T=10 ** 6, order="lowrank_first")
+    if not lib.set_fusion(fused):
+        pytest.skip("the two trailing modes are not both compressed")
+    gs = GradStream(wl, seed=8)
+    W0 = init_weights(wl, seed=8)
+    g = gs.next()
+    orc.refresh(g)
+    lib.set_omega(orc.omega)
+    for n, U in enumerate(orc.factors):
+        if U is not None:
+            lib.set_factor(n, U)
+    lib.mark_refreshed()
+    W, Wo = dev(W0, wl.dtype), W0
+    for step in range(4):
+        G = dev(g, wl.dtype)
+        lib.step(W, G)
+        Wo = orc.step(Wo, g)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(G, wl.dtype).view(np.uint8), np.ascontiguousarray(g).view(np.uint8))
+        weight_check(host(W, wl.dtype), Wo, wl.dtype, f"{name} step {step + 1}")
+        g = gs.next()
+    _, _, ms, vs = lib.get_moments()
+    assert np.abs(ms - orc.mS).max() <= 1e-5 * np.abs(orc.mS).max()
+
+
+def test_lowrank_first_independent_run():
+    """A run that refreshes on its own: the library's Omega and factors feed its own
+    steps; weights stay within the bar of an oracle run whose Omega is set to the
+    library's at each refresh (the refresh-time choice near the top-k threshold is the
+    only freedom)."""
+    wl = custom((6, 5, 48, 25), "bf16", (3, 3, 24, 13), 0.05, T=3)
+    lib = lib_for(wl, T=3, order="lowrank_first")
+    orc = oracle_for(wl, T=3, order="lowrank_first")
+    gs = GradStream(wl, seed=12)
+    W0 = init_weights(wl, seed=12)
+    W, Wo = dev(W0, wl.dtype), W0
+    for t in range(1, 8):
+        g = gs.next()
+        if (t - 1) % 3 == 0:
+            lib.refresh(dev(g, wl.dtype))
+            orc.refresh(g, t)
+            torch.cuda.synchronize()
+            orc.omega = lib.get_omega().copy()
+        lib.step(W, dev(g, wl.dtype))
+        Wo = orc.step(Wo, g)
+    torch.cuda.synchronize()
+    weight_check(host(W, wl.dtype), Wo, wl.dtype, "lowrank-first run")

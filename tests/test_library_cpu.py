@@ -94,12 +94,12 @@ def test_null_handle_calls_are_einval(lib):
 
 def test_default_options_are_the_plain_method(lib):
     """tgrad_default_options is host-only; the ctypes layout matches the C struct
-    (two doubles, two int32, one uint64: 32 bytes)."""
-    assert ctypes.sizeof(tg.Options) == 32
-    o = tg.Options(7.0, 7.0, 5, 5, 5)
+    (two doubles, two int32, one uint64, two int32: 40 bytes)."""
+    assert ctypes.sizeof(tg.Options) == 40
+    o = tg.Options(7.0, 7.0, 5, 5, 5, 5, 5)
     lib.tgrad_default_options(ctypes.byref(o))
-    assert (o.weight_decay, o.sparse_scale, o.selection, o.remap_moments, o.seed) == \
-        (0.0, 1.0, tg.SELECT_TOPK, 0, 0)
+    assert (o.weight_decay, o.sparse_scale, o.selection, o.remap_moments, o.seed, o.order,
+            o.reserved) == (0.0, 1.0, tg.SELECT_TOPK, 0, 0, 0, 0)
     assert lib.tgrad_set_options(None, ctypes.byref(o)) == tg.EINVAL
     assert lib.tgrad_get_options(None, ctypes.byref(o)) == tg.EINVAL
 
