@@ -492,6 +492,8 @@ Geo geometry(const ModeProd& mp) {
   return geometry_for(mp, 1);
 }
 
+// `grid` is the number of CUs; the launch puts one resident round of workgroups on
+// each (as many as the kernel's registers and LDS let a CU hold), capped by the tiles.
 template <typename XT, int P, int NRB, int NCB, int EPI, typename WT>
 hipError_t go(const MPK& k, size_t lds, unsigned grid, hipStream_t s) {
   auto fn = k_modeprod<XT, P, NRB, NCB, EPI, WT>;
@@ -500,7 +502,13 @@ hipError_t go(const MPK& k, size_t lds, unsigned grid, hipStream_t s) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(NTH), lds, s, k);
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NTH, lds);
+  if (e != hipSuccess) return e;
+  uint64_t g = (uint64_t)grid * (uint64_t)(per_cu > 0 ? per_cu : 1);
+  if (g > k.ntiles) g = k.ntiles;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL(fn, dim3((unsigned)g), dim3(NTH), lds, s, k);
   return hipGetLastError();
 }
 
@@ -565,13 +573,8 @@ hipError_t launch_modeprod(const ModeProd& mp, int num_cu, hipStream_t s) {
   k.lr = mp.lr;
   k.decay = mp.decay;
   k.has_sparse = mp.has_sparse;
-  // persistent grid: every CU filled several times over
-  const size_t per_cu = g.lds ? (160 * 1024) / g.lds : 8;
-  uint64_t occ = per_cu < 1 ? 1 : (per_cu > 8 ? 8 : per_cu);
-  uint64_t grid = (uint64_t)(num_cu > 0 ? num_cu : 256) * occ;
-  if (grid > g.ntiles) grid = g.ntiles;
-  if (grid < 1) grid = 1;
-  const unsigned gr = (unsigned)grid;
+  // persistent grid: one resident round per CU (sized in go())
+  const unsigned gr = (unsigned)(num_cu > 0 ? num_cu : 256);
   const uint32_t ncb = g.ncb;
   if (!mp.apply) {
     if (mp.P == 2) return pick_ncb<float, 2, 0, float>(k, ncb, g.lds, gr, s);

@@ -440,6 +440,8 @@ Geo2 plan(const ModeProd2& mp, uint32_t TA) {
   return g;
 }
 
+// `grid` is the number of CUs; the launch puts one resident round of workgroups on
+// each (as many as the kernel's registers and LDS let a CU hold), capped by the tiles.
 template <typename XT, int P, int REC, int EPI, typename WT>
 hipError_t go2(const MP2K& k, size_t lds, unsigned grid, hipStream_t s) {
   auto fn = k_modeprod2<XT, P, REC, EPI, WT>;
@@ -448,7 +450,13 @@ hipError_t go2(const MP2K& k, size_t lds, unsigned grid, hipStream_t s) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(NTH), lds, s, k);
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NTH, lds);
+  if (e != hipSuccess) return e;
+  uint64_t g = (uint64_t)grid * (uint64_t)(per_cu > 0 ? per_cu : 1);
+  if (g > k.ntiles) g = k.ntiles;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL(fn, dim3((unsigned)g), dim3(NTH), lds, s, k);
   return hipGetLastError();
 }
 
@@ -512,12 +520,8 @@ hipError_t launch_modeprod2(const ModeProd2& mp, int num_cu, hipStream_t s) {
   k.decay = mp.decay;
   k.has_sparse = mp.has_sparse;
   k.gS = mp.recon ? nullptr : mp.gather_S;
-  const size_t per_cu = g.lds ? (160 * 1024) / g.lds : 8;
-  uint64_t occ = per_cu < 1 ? 1 : (per_cu > 8 ? 8 : per_cu);
-  uint64_t grid = (uint64_t)(num_cu > 0 ? num_cu : 256) * occ;
-  if (grid > k.ntiles) grid = k.ntiles;
-  if (grid < 1) grid = 1;
-  const unsigned gr = (unsigned)grid;
+  // persistent grid: one resident round per CU (sized in go2())
+  const unsigned gr = (unsigned)(num_cu > 0 ? num_cu : 256);
   if (!mp.recon) {
     if (mp.P == 2) return go2<float, 2, 0, 0, float>(k, g.lds, gr, s);
     switch (mp.in_dt) {
