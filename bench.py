@@ -41,8 +41,9 @@ def esize(dtype):
     return {"f32": 4, "f16": 2, "bf16": 2, "c64": 8}[dtype]
 
 
-def kernel_bytes(wl):
-    """Algorithmic HBM bytes per launch of every step kernel, keyed by kernel name.
+def kernel_bytes(wl, proj3=False):
+    """Algorithmic HBM bytes per launch of every step kernel, keyed by kernel name
+    (proj3: the projection's first launch takes the last three modes).
     Mode products: the input tile read once and the output written once (the operand
     matrix is negligible); apply: + W read and written, membership bitmask (N/8 B),
     per-word ranks (N/16 B) and the k sparse updates. Gather: k indices, k gradient
@@ -82,6 +83,10 @@ def kernel_bytes(wl):
     I1, I2, R1, R2 = wl.shape[d - 2], wl.shape[d - 1], wl.ranks[d - 2], wl.ranks[d - 1]
     A = N // (I1 * I2)
     proj2 = A * I1 * I2 * P * es + A * R1 * R2 * P * 4 + k * (4 + 4 * P)
+    # three trailing modes: the same, with the output R0 R1 R2 per index of the leading modes
+    R0 = wl.ranks[d - 3] if d >= 3 else 1
+    U = A // wl.shape[d - 3] if d >= 3 else A
+    proj3_b = A * I1 * I2 * P * es + U * R0 * R1 * R2 * P * 4 + k * (4 + 4 * P)
     rec2 = A * R1 * R2 * P * 4 + 2 * N * es + N // 8 + N // 16 + k * P * 4 + k * 4
     flops_proj = []
     size = N
@@ -93,11 +98,12 @@ def kernel_bytes(wl):
     return {
         "gather_residual": [k * (4 + es + 4 * P + es)],
         "modeprod_project_first": proj[:1],
-        "modeprod_project": proj[1:],
+        "modeprod_project": proj[2:] if proj3 else proj[1:],
         "adam_fused": [(ncore + k) * P * 24],
         "modeprod_reconstruct": rec[:-1],
         "modeprod_reconstruct_apply": rec[-1:],
         "modeprod2_project_first": [proj2],
+        "modeprod3_project_first": [proj3_b],
         "modeprod2_reconstruct_apply": [rec2],
         "_flops_project": flops_proj,
         "_ncore": ncore,
@@ -265,7 +271,7 @@ def main():
     lib.timing_enable(False, 0)
     refresh_ms = float(np.median(rt))
 
-    kb = kernel_bytes(wl)
+    kb = kernel_bytes(wl, proj3="modeprod3_project_first" in rec)
     kernels = {}
     for name, (n, ms) in rec.items():
         per_step = n // K if n % K == 0 else n / K

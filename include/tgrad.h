@@ -170,12 +170,15 @@ int tgrad_mark_refreshed(tgrad_t *h);
  * them fits in LDS, the projection's first two mode products and the reconstruction's
  * last two run as one launch each (the default). For bf16/fp16 tensors with small
  * enough slabs those launches use one wave per slab on bf16 MFMAs (exact bf16 splits of
- * the fp32 operands), otherwise workgroup-wide fp32 MFMA tiles. enable = 0 selects one
- * launch per mode; 1 the fused form (default choice of kernel); 2 the fused form with
- * the workgroup-tile kernel only. enable = 1 or 2 returns TGRAD_EINVAL where the fused
- * form does not apply. The unfused plan projects a residual copy of grad, so enable = 0
- * allocates an N-element workspace the first time (TGRAD_ENOMEM if that fails). Results
- * agree to fp32 rounding; takes effect at the next step. */
+ * the fp32 operands), otherwise workgroup-wide fp32 MFMA tiles; where mode d-3 is also
+ * compressed (I(d-3) a multiple of 16 up to 64, rank <= 32), the projection's first
+ * launch takes mode d-3 as well (one workgroup per index of the leading modes). enable = 0 selects one launch per mode; 1 the fused form
+ * (default choice of kernels); 2 the fused two-mode form with the workgroup-tile kernel
+ * only; 3 the fused two-mode form with the slab kernels, without the three-mode
+ * projection. enable = 1, 2 or 3 returns TGRAD_EINVAL where the fused form does not
+ * apply. The unfused plan projects a residual copy of grad, so enable = 0 allocates an
+ * N-element workspace the first time (TGRAD_ENOMEM if that fails). Results agree to
+ * fp32 rounding; takes effect at the next step. */
 int tgrad_set_fusion(tgrad_t *h, int enable);
 
 /* ---------------------------------------------------------------- variants.

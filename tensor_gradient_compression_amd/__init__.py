@@ -266,9 +266,10 @@ class TGrad:
                     remap_moments=bool(o.remap_moments), seed=o.seed, order=order)
 
     def set_fusion(self, enable) -> bool:
-        """Select fused two-mode launches (True or 1: default kernel choice; 2: workgroup
-        tiles only) or one launch per mode (False or 0); returns False when the fused form
-        does not apply to this shape."""
+        """Select fused multi-mode launches (True or 1: default kernel choice; 2: two-mode
+        workgroup tiles only; 3: two-mode slab kernels without the three-mode projection)
+        or one launch per mode (False or 0); returns False when the fused form does not
+        apply to this shape."""
         rc = self._lib.tgrad_set_fusion(self._h, int(enable))
         if rc == EINVAL and enable:
             return False

@@ -534,6 +534,30 @@ struct G16Geo {
   uint32_t grid;
 };
 
+// Workgroups of k_gram16<BF, NB> a CU holds with `lds` bytes of LDS each (0 on error).
+template <bool BF, int NB>
+int g16_occ(size_t lds) {
+  auto fn = k_gram16<BF, NB>;
+  if (lds > 64 * 1024 &&
+      hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)lds) != hipSuccess)
+    return 0;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, G16_NTH, lds) != hipSuccess)
+    return 0;
+  return per_cu;
+}
+template <bool BF>
+int g16_occ_nb(uint32_t I, size_t lds) {
+  switch ((I + 15) / 16) {
+    case 1: return g16_occ<BF, 1>(lds);
+    case 2: return g16_occ<BF, 2>(lds);
+    case 3: return g16_occ<BF, 3>(lds);
+    case 4: return g16_occ<BF, 4>(lds);
+  }
+  return 0;
+}
+
 G16Geo g16geo(const GramArgs& g, int num_cu) {
   G16Geo r{};
   r.ok = false;
@@ -572,7 +596,14 @@ G16Geo g16geo(const GramArgs& g, int num_cu) {
   const uint32_t nb = (g.I + 15) / 16;
   const size_t red = (size_t)nb * (nb + 1) / 2 * 4 * 64 * sizeof(double);   // block sums
   r.lds = std::max((size_t)2 * k.buf_bytes, red);
-  uint64_t grid = (uint64_t)(num_cu > 0 ? num_cu : 256) * G16_WGS_PER_CU;
+  // a persistent grid of one resident round (a second, partial round would run alone at
+  // the end): as many workgroups as a CU holds with this kernel's registers and LDS, at
+  // most G16_WGS_PER_CU (each workgroup writes an I x I fp64 partial)
+  const int occ = g.dt == DT_BF16 ? g16_occ_nb<true>(g.I, r.lds)
+                                  : g16_occ_nb<false>(g.I, r.lds);
+  if (occ < 1) return r;
+  const int per_cu = occ < G16_WGS_PER_CU ? occ : G16_WGS_PER_CU;
+  uint64_t grid = (uint64_t)(num_cu > 0 ? num_cu : 256) * (uint64_t)per_cu;
   if (grid > k.ntiles) grid = k.ntiles;
   if (grid < 1) grid = 1;
   r.grid = (uint32_t)grid;
@@ -582,12 +613,8 @@ G16Geo g16geo(const GramArgs& g, int num_cu) {
 
 template <bool BF, int NB>
 hipError_t go16(const G16Geo& g, hipStream_t s) {
+  // g16geo has raised the kernel's LDS limit where it needs more than 64 KiB
   auto fn = k_gram16<BF, NB>;
-  if (g.lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)fn,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)g.lds);
-    if (e != hipSuccess) return e;
-  }
   hipLaunchKernelGGL(fn, dim3(g.grid), dim3(G16_NTH), g.lds, s, g.k);
   return hipGetLastError();
 }

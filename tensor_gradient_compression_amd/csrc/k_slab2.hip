@@ -30,6 +30,8 @@
 // orders sum above 2 (each below 2^-24 of the full product) are dropped, so the result
 // agrees with an fp32 GEMM to the level of fp32 rounding. Every other product takes fp32
 // operands as they are, on v_mfma_f32_16x16x4_f32. Accumulation is fp32 throughout.
+#include <type_traits>
+
 #include "tg_common.h"
 
 namespace tg {
@@ -153,13 +155,18 @@ template <> struct Bits16<_Float16> {
 // bound the slab after it; entries past NOM * 64 in one slab are read directly.
 constexpr int NOM = 3;
 
+// Two slots, used alternately by consecutive slabs of a wave; the slab loops are unrolled
+// by two so that a slot index is a compile-time constant and the prefetched entries are
+// never copied between registers (a copy would have to wait for every load in flight,
+// the next slab's transfer included).
 struct OmegaPipe {
-  uint64_t jlo = 0, jhi = 0;      // current slab
-  uint64_t nlo = 0, nhi = 0;      // next slab
+  uint64_t lo[2] = {0, 0}, hi[2] = {0, 0};   // Omega ranges of the slabs in the two slots
   uint64_t bw[4] = {0, 0, 0, 0};  // the slab after: mask, rank at its start; mask, rank at its end
-  uint32_t om_c[NOM], om_n[NOM];
-  float us_c[NOM], us_n[NOM];
+  uint32_t om[2][NOM];
+  float us[2][NOM];
 };
+template <int V>
+using Slot = std::integral_constant<int, V>;
 
 // ------------------------------------------------------------------ projection
 // NRB1: 16-row blocks of I1 (I1 <= 16 NRB1 <= 64); NRB2: 16-row blocks of R1 (<= 32).
@@ -235,11 +242,11 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
   if (sparse) {
     uint64_t w[4];
     bounds(gw, w);
-    range(gw, w, op.jlo, op.jhi);
+    range(gw, w, op.lo[0], op.hi[0]);
 #pragma unroll
     for (int i = 0; i < NOM; ++i) {
-      const uint64_t j = op.jlo + lane + 64 * i;
-      op.om_c[i] = k.omega[j < kS ? j : kS - 1];
+      const uint64_t j = op.lo[0] + lane + 64 * i;
+      op.om[0][i] = k.omega[j < kS ? j : kS - 1];
     }
     if (cnt > 1) bounds(gw + TW, op.bw);
   }
@@ -247,12 +254,13 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
 
   uint32_t nq_prev = 0;
   uint64_t out_prev = 0;
-  for (uint32_t i = 0; i < cnt; ++i) {
+  // slab i of this wave, in slot `cur` (= i % 2)
+  auto slab = [&](uint32_t i, auto slot) {
+    constexpr int cur = decltype(slot)::value, nxt = cur ^ 1;
     const uint32_t n = gw + i * TW;   // this slab
-    const int cur = i & 1;
     wait_vm0();   // slab n, its Omega indices and the next slab's bounds have landed
     wave_fence();
-    if (sparse && i + 1 < cnt) range(n + TW, op.bw, op.nlo, op.nhi);
+    if (sparse && i + 1 < cnt) range(n + TW, op.bw, op.lo[nxt], op.hi[nxt]);
     // the previous slab's output leaves (waited for at the next slab)
     for (uint32_t q = lane; q < nq_prev; q += 64)
       *(f4*)(k.Y + out_prev + 4 * q) = *(const LDS f4*)(So + 4 * q);
@@ -264,8 +272,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
       if (sparse) {
 #pragma unroll
         for (int q = 0; q < NOM; ++q) {
-          const uint64_t j = op.nlo + lane + 64 * q;
-          op.om_n[q] = k.omega[j < kS ? j : kS - 1];
+          const uint64_t j = op.lo[nxt] + lane + 64 * q;
+          op.om[nxt][q] = k.omega[j < kS ? j : kS - 1];
         }
         if (i + 2 < cnt) bounds(n + 2 * TW, op.bw);
       }
@@ -282,21 +290,22 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
         xs[loc] = 0;
       };
       // the prefetched entries: every value read before any is cleared
+      const uint64_t jlo = op.lo[cur], jhi = op.hi[cur];
       float sv[NOM];
 #pragma unroll
-      for (int i = 0; i < NOM; ++i) {
-        const uint64_t j = op.jlo + lane + 64 * i;
-        sv[i] = j < op.jhi ? Bits16<XT>::value(xs[(uint32_t)(op.om_c[i] - e_lo)]) : 0.0f;
+      for (int q = 0; q < NOM; ++q) {
+        const uint64_t j = jlo + lane + 64 * q;
+        sv[q] = j < jhi ? Bits16<XT>::value(xs[(uint32_t)(op.om[cur][q] - e_lo)]) : 0.0f;
       }
 #pragma unroll
-      for (int i = 0; i < NOM; ++i) {
-        const uint64_t j = op.jlo + lane + 64 * i;
-        if (j < op.jhi) {
-          k.S[j] = sv[i];
-          xs[(uint32_t)(op.om_c[i] - e_lo)] = 0;
+      for (int q = 0; q < NOM; ++q) {
+        const uint64_t j = jlo + lane + 64 * q;
+        if (j < jhi) {
+          k.S[j] = sv[q];
+          xs[(uint32_t)(op.om[cur][q] - e_lo)] = 0;
         }
       }
-      for (uint64_t j = op.jlo + 64 * NOM + lane; j < op.jhi; j += 64) take(j, k.omega[j]);
+      for (uint64_t j = jlo + 64 * NOM + lane; j < jhi; j += 64) take(j, k.omega[j]);
       wave_fence();
     }
 
@@ -351,10 +360,10 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
     wave_fence();
     nq_prev = R1 * R2 / 4;
     out_prev = (uint64_t)n * R1 * R2;
-    op.jlo = op.nlo;
-    op.jhi = op.nhi;
-#pragma unroll
-    for (int q = 0; q < NOM; ++q) op.om_c[q] = op.om_n[q];
+  };
+  for (uint32_t i = 0; i < cnt; i += 2) {
+    slab(i, Slot<0>{});
+    if (i + 1 < cnt) slab(i + 1, Slot<1>{});
   }
   // the last slab's output
   wait_lgkm0();
@@ -370,7 +379,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
 // operands stay in registers, and pass 1's row blocks are independent accumulation
 // chains interleaved step by step.
 template <typename WT, int NRB1, int NCB2, int KS1>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8))) k_rec2s(S2K k) {
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) k_rec2s(S2K k) {
   extern __shared__ float smem[];
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -437,13 +446,13 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
   if (sparse) {
     uint64_t w[4];
     bounds(gw, w);
-    range(gw, w, op.jlo, op.jhi);
+    range(gw, w, op.lo[0], op.hi[0]);
 #pragma unroll
     for (int i = 0; i < NOM; ++i) {
-      const uint64_t j = op.jlo + lane + 64 * i;
+      const uint64_t j = op.lo[0] + lane + 64 * i;
       const uint64_t jc = j < kS ? j : kS - 1;
-      op.om_c[i] = k.omega[jc];
-      op.us_c[i] = k.S[jc];
+      op.om[0][i] = k.omega[jc];
+      op.us[0][i] = k.S[jc];
     }
     if (cnt > 1) bounds(gw + TW, op.bw);
   }
@@ -451,12 +460,14 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
 
   uint32_t nq_prev = 0;
   uint64_t out_prev = 0;
-  for (uint32_t i = 0; i <= cnt; ++i) {
+  // slab i of this wave (i < cnt), in slot `cur` (= i % 2), after the previous slab's
+  // weights have been written; i == cnt writes the last slab's weights and returns true
+  auto slab = [&](uint32_t i, auto slot) -> bool {
+    constexpr int cur = decltype(slot)::value, nxt = cur ^ 1;
     const uint32_t n = gw + i * TW;   // this slab (i < cnt)
-    const int cur = i & 1;
     wait_vm0();   // Z of this slab, W of the previous one, Omega data; older stores
     wave_fence();
-    if (sparse && i + 1 < cnt) range(n + TW, op.bw, op.nlo, op.nhi);
+    if (sparse && i + 1 < cnt) range(n + TW, op.bw, op.lo[nxt], op.hi[nxt]);
     // the previous slab: W <- round(W * decay - lr * O), 16-byte pieces (the stores are
     // waited for at the next slab)
     for (uint32_t q = lane; q < nq_prev; q += 64) {
@@ -481,7 +492,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
       }
       *(uint4*)((WT*)k.W + out_prev + 8 * q) = *(const uint4*)o;
     }
-    if (i == cnt) break;
+    if (i == cnt) return true;
     wait_lgkm0();
     wave_fence();
     // this slab's W (used at the next slab), the next slab's Z and Omega data
@@ -491,10 +502,10 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
       if (sparse) {
 #pragma unroll
         for (int q = 0; q < NOM; ++q) {
-          const uint64_t j = op.nlo + lane + 64 * q;
+          const uint64_t j = op.lo[nxt] + lane + 64 * q;
           const uint64_t jc = j < kS ? j : kS - 1;
-          op.om_n[q] = k.omega[jc];
-          op.us_n[q] = k.S[jc];
+          op.om[nxt][q] = k.omega[jc];
+          op.us[nxt][q] = k.S[jc];
         }
         if (i + 2 < cnt) bounds(n + 2 * TW, op.bw);
       }
@@ -548,18 +559,19 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
       const uint64_t e_lo = (uint64_t)n * slab_e;
       // the prefetched entries: all reads, then all writes (distinct elements; lanes
       // past the range use their trash slot)
+      const uint64_t jlo = op.lo[cur], jhi = op.hi[cur];
       uint32_t loc[NOM];
       float cv[NOM];
 #pragma unroll
-      for (int i = 0; i < NOM; ++i) {
-        const uint64_t j = op.jlo + lane + 64 * i;
-        loc[i] = j < op.jhi ? (uint32_t)(op.om_c[i] - e_lo) : k.trash + lane;
+      for (int q = 0; q < NOM; ++q) {
+        const uint64_t j = jlo + lane + 64 * q;
+        loc[q] = j < jhi ? (uint32_t)(op.om[cur][q] - e_lo) : k.trash + lane;
       }
 #pragma unroll
-      for (int i = 0; i < NOM; ++i) cv[i] = Ob[loc[i]];
+      for (int q = 0; q < NOM; ++q) cv[q] = Ob[loc[q]];
 #pragma unroll
-      for (int i = 0; i < NOM; ++i) Ob[loc[i]] = cv[i] + op.us_c[i];
-      for (uint64_t j = op.jlo + 64 * NOM + lane; j < op.jhi; j += 64) {
+      for (int q = 0; q < NOM; ++q) Ob[loc[q]] = cv[q] + op.us[cur][q];
+      for (uint64_t j = jlo + 64 * NOM + lane; j < jhi; j += 64) {
         const uint32_t loc = (uint32_t)(k.omega[j] - e_lo);
         Ob[loc] = Ob[loc] + k.S[j];
       }
@@ -567,13 +579,394 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
     }
     nq_prev = slab_e / 8;
     out_prev = (uint64_t)n * slab_e;
-    op.jlo = op.nlo;
-    op.jhi = op.nhi;
+    return false;
+  };
+  for (uint32_t i = 0;; i += 2) {
+    if (slab(i, Slot<0>{})) break;
+    if (slab(i + 1, Slot<1>{})) break;
+  }
+}
+
+// ------------------------------------------------------------------ three-mode projection
+// The last three modes in one launch. A unit is one index of the leading modes: I0 slabs
+// of I1 x I2 (contiguous). A workgroup of WPB3 waves takes one unit at a time (units
+// strided over the grid) in rounds of WPB3 slabs: in round c wave w projects slab
+// WPB3 c + w over modes d and d-1 exactly as the two-mode kernel does (Omega gathered and
+// zeroed in its staged copy) and leaves the R1 x R2 result as row w of a round stack in
+// LDS; after one barrier every wave adds the round's share of the mode d-2 product,
+// Y[u] (R0 x R1 R2) += M0[:, round] x stack, to the output tiles it owns (fp32
+// accumulators on v_mfma_f32_16x16x4_f32), and writes them after the unit's last round.
+// Two round stacks alternate with the workgroup's round count (across units too), so one
+// barrier per round suffices. Pass 1's accumulators
+// feed pass 2 directly: the 16x16 MFMA result layout (rows 4 (lane / 16) + v, column
+// lane % 16) is pass 2's B-operand layout when its k index runs over rows in the order
+// (block, v, lane / 16).
+#ifndef TG_WPB3
+#define TG_WPB3 16
+#endif
+constexpr int WPB3 = TG_WPB3;
+constexpr int NT3 = WPB3 * 64;
+
+struct S3K {
+  const void* X;        // the gradient (U, I0, I1, I2), only read
+  float* Y;             // fp32 output (U, R0, R1, R2)
+  const float* M0;      // R0 x I0 (row-major fp32)
+  const float* M1;      // R1 x I1
+  const float* M2;      // R2 x I2
+  const uint64_t* mask;
+  const uint32_t* rank;
+  const uint32_t* omega;
+  float* S;             // gathered S (written)
+  uint64_t kS;          // |Omega|; 0: no sparse part
+  uint32_t U, I0, I1, I2, R0, R1, R2;
+  uint32_t slab_e;      // I1 * I2
+  uint32_t lds_wave;    // bytes per wave (two slab buffers)
+  uint32_t off_x1;      // second buffer, within a wave's bytes
+  uint32_t off_stack;   // two round stacks of WPB3 rows of R1 R2 floats + 64 trash slots
+  uint32_t stack_fl;    // floats per round stack
+  uint32_t off_m0;      // M0 copy
+  uint32_t off_fac;     // per-lane operand tables of passes 1 and 2 (see k_proj3s)
+};
+
+// NTW: output tiles (16 x 16) per wave, at most
+template <typename XT, int NRB1, int NRB2, int NTW>
+__global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))) k_proj3s(S3K k) {
+  extern __shared__ float smem[];
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  LDS unsigned char* const lds = (LDS unsigned char*)smem;
+  LDS unsigned char* const xb0 = lds + wv * k.lds_wave;
+  LDS unsigned char* const xb1 = xb0 + k.off_x1;
+  LDS float* const stacks = (LDS float*)(lds + k.off_stack);
+  LDS float* const m0s = (LDS float*)(lds + k.off_m0);
+  const uint32_t li = lane & 15, lg = lane >> 4;
+  const uint32_t I0 = k.I0, I1 = k.I1, I2 = k.I2, R0 = k.R0, R1 = k.R1, R2 = k.R2;
+  const uint32_t RC = R1 * R2;                 // stack row length
+  const uint32_t trash = WPB3 * RC;            // float offset of a stack's trash slots
+  const uint32_t SF = k.stack_fl;
+  const uint32_t slab_e = k.slab_e;
+  const uint64_t N = (uint64_t)k.U * I0 * slab_e;
+  const uint64_t kS = k.kS;
+  const bool sparse = kS > 0;
+  const uint32_t nct = (RC + 15) / 16, ntile = ((R0 + 15) / 16) * nct;
+
+  // The factor operands, as every lane supplies them, in LDS tables shared by the
+  // workgroup (registers would not leave room for the mode d-2 accumulators):
+  //   b1t[part][lane]: pass 1 B[k = i2][col = r2] = M2[r2][i2], i2 = 8 (lane / 16) + e,
+  //                    r2 = lane % 16, in three bf16 parts (16 bytes a lane);
+  //   a2t[r2][rb][lane]: pass 2 A[row = j1][k] = M1[j1][i1], j1 = 16 r2 + lane % 16,
+  //                    i1 = 16 rb + 4 (lane / 16) + v for v = 0..3 (16 bytes a lane).
+  LDS u16x8* const b1t = (LDS u16x8*)(lds + k.off_fac);
+  LDS f4* const a2t = (LDS f4*)(lds + k.off_fac + 3 * 64 * 16);
+  for (uint32_t q = threadIdx.x; q < R0 * I0; q += NT3) m0s[q] = k.M0[q];
+  if (wv == 0) {
+    u16x8 b1[3];
 #pragma unroll
-    for (int q = 0; q < NOM; ++q) {
-      op.om_c[q] = op.om_n[q];
-      op.us_c[q] = op.us_n[q];
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t i2 = 8 * lg + e;
+      const float v = (li < R2 && i2 < I2) ? k.M2[li * I2 + i2] : 0.0f;
+      unsigned short a, b, c;
+      split3(v, a, b, c);
+      b1[0][e] = a; b1[1][e] = b; b1[2][e] = c;
     }
+#pragma unroll
+    for (int h = 0; h < 3; ++h) b1t[h * 64 + lane] = b1[h];
+  } else if (wv == 1) {
+#pragma unroll
+    for (int r2 = 0; r2 < NRB2; ++r2)
+#pragma unroll
+      for (int rb = 0; rb < NRB1; ++rb) {
+        f4 a;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t j1 = 16 * r2 + li, i1 = 16 * rb + 4 * lg + v;
+          a[v] = (j1 < R1 && i1 < I1) ? k.M1[j1 * I1 + i1] : 0.0f;
+        }
+        a2t[(r2 * NRB1 + rb) * 64 + lane] = a;
+      }
+  }
+  wait_lgkm0();
+  wave_fence();
+  __builtin_amdgcn_s_barrier();
+  wave_fence();
+
+  // this wave's slabs: round c of unit r (unit blockIdx.x + r * gridDim.x) is slab
+  // WPB3 c + wv of the unit; g = r * nch + c
+  const uint32_t G = gridDim.x;
+  const uint32_t nu = (k.U - 1 - blockIdx.x) / G + 1;
+  const uint32_t nch = I0 / WPB3;
+  const uint32_t cnt = nu * nch;
+  auto slab_of = [&](uint32_t g) -> uint32_t {
+    const uint32_t r = g / nch, c = g - r * nch;
+    return (blockIdx.x + r * G) * I0 + WPB3 * c + wv;
+  };
+  const XT* X = (const XT*)k.X;
+  const uint32_t xchunks = slab_e * 2 / 16;
+  auto bounds = [&](uint32_t s, uint64_t* w) {
+    const uint64_t elo = (uint64_t)s * slab_e, ehi = elo + slab_e;
+    const uint64_t wl = elo >> 6, wh = ehi < N ? ehi >> 6 : 0;
+    const __attribute__((address_space(4))) uint64_t* m =
+        (const __attribute__((address_space(4))) uint64_t*)k.mask;
+    const __attribute__((address_space(4))) uint32_t* r =
+        (const __attribute__((address_space(4))) uint32_t*)k.rank;
+    w[0] = m[wl];
+    w[1] = r[wl];
+    w[2] = m[wh];
+    w[3] = r[wh];
+  };
+  auto range = [&](uint32_t s, const uint64_t* w, uint64_t& lo, uint64_t& hi) {
+    lo = rank_at(w[0], (uint32_t)w[1], (uint64_t)s * slab_e, N, kS);
+    hi = rank_at(w[2], (uint32_t)w[3], (uint64_t)(s + 1) * slab_e, N, kS);
+  };
+  OmegaPipe op;
+  {
+    const uint32_t s0 = slab_of(0);
+    if (sparse) {
+      uint64_t w[4];
+      bounds(s0, w);
+      range(s0, w, op.lo[0], op.hi[0]);
+#pragma unroll
+      for (int q = 0; q < NOM; ++q) {
+        const uint64_t j = op.lo[0] + lane + 64 * q;
+        op.om[0][q] = k.omega[j < kS ? j : kS - 1];
+      }
+      if (cnt > 1) bounds(slab_of(1), op.bw);
+    }
+    wave_dma(X + (uint64_t)s0 * slab_e, xchunks, xb0, lane);
+  }
+
+  f4 acc3[NTW];
+#pragma unroll
+  for (int m = 0; m < NTW; ++m) acc3[m] = f4{0.f, 0.f, 0.f, 0.f};
+  // a finished unit's tiles are written at the start of the next slab, where every
+  // transfer has landed anyway
+  uint32_t pend = 0xFFFFFFFFu;
+  auto write_unit = [&]() {
+    if (pend == 0xFFFFFFFFu) return;
+#pragma unroll
+    for (int m = 0; m < NTW; ++m) {
+      const uint32_t t = wv + WPB3 * m;
+      if (t < ntile) {
+        const uint32_t jb = t / nct, ct = t - jb * nct;
+        const uint32_t col = 16 * ct + li;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t row = 16 * jb + 4 * lg + v;
+          if (row < R0 && col < RC) k.Y[((uint64_t)pend * R0 + row) * RC + col] = acc3[m][v];
+        }
+      }
+      acc3[m] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+    pend = 0xFFFFFFFFu;
+  };
+
+  auto slab = [&](uint32_t g, auto slot) {
+    constexpr int cur = decltype(slot)::value, nxt = cur ^ 1;
+    const uint32_t n = slab_of(g);
+    const uint32_t r = g / nch, c = g - r * nch;
+    wait_vm0();   // slab n, its Omega indices and the next slab's bounds have landed
+    wave_fence();
+    write_unit();
+    if (g + 1 < cnt) {
+      const uint32_t n1 = slab_of(g + 1);
+      if (sparse) range(n1, op.bw, op.lo[nxt], op.hi[nxt]);
+      wave_dma(X + (uint64_t)n1 * slab_e, xchunks, cur ? xb0 : xb1, lane);
+      if (sparse) {
+#pragma unroll
+        for (int q = 0; q < NOM; ++q) {
+          const uint64_t j = op.lo[nxt] + lane + 64 * q;
+          op.om[nxt][q] = k.omega[j < kS ? j : kS - 1];
+        }
+        if (g + 2 < cnt) bounds(slab_of(g + 2), op.bw);
+      }
+    }
+
+    LDS unsigned short* const xs = (LDS unsigned short*)(cur ? xb1 : xb0);
+    const uint64_t e_lo = (uint64_t)n * slab_e;
+    if (sparse) {
+      // S[j] = X[omega[j]] and X[omega[j]] <- 0 in the LDS copy (+0 is the zero bit
+      // pattern of both 16-bit formats); the gradient in HBM is only read
+      const uint64_t jlo = op.lo[cur], jhi = op.hi[cur];
+      float sv[NOM];
+#pragma unroll
+      for (int q = 0; q < NOM; ++q) {
+        const uint64_t j = jlo + lane + 64 * q;
+        sv[q] = j < jhi ? Bits16<XT>::value(xs[(uint32_t)(op.om[cur][q] - e_lo)]) : 0.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < NOM; ++q) {
+        const uint64_t j = jlo + lane + 64 * q;
+        if (j < jhi) {
+          k.S[j] = sv[q];
+          xs[(uint32_t)(op.om[cur][q] - e_lo)] = 0;
+        }
+      }
+      for (uint64_t j = jlo + 64 * NOM + lane; j < jhi; j += 64) {
+        const uint32_t loc = (uint32_t)(k.omega[j] - e_lo);
+        k.S[j] = Bits16<XT>::value(xs[loc]);
+        xs[loc] = 0;
+      }
+      wave_fence();
+    }
+
+    // pass 1 (mode d): rows i1, k = i2, columns r2, one 16-row block at a time, and
+    // the block's terms of pass 2 (mode d-1: rows j1, k = i1, columns r2) straight from
+    // its registers
+    f4 acc2[NRB2];
+#pragma unroll
+    for (int r2 = 0; r2 < NRB2; ++r2) acc2[r2] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rb = 0; rb < NRB1; ++rb) {
+      const uint32_t i1 = 16 * rb + li;
+      u16x8 xp[Bits16<XT>::NP];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t i2 = 8 * lg + e;
+        const unsigned short raw =
+            (i1 < I1 && i2 < I2) ? xs[i1 * I2 + i2] : (unsigned short)0;
+        unsigned short p[2];
+        Bits16<XT>::parts(raw, p);
+#pragma unroll
+        for (int h = 0; h < Bits16<XT>::NP; ++h) xp[h][e] = p[h];
+      }
+      u16x8 b1[3];
+#pragma unroll
+      for (int h = 0; h < 3; ++h) b1[h] = b1t[h * 64 + lane];
+      f4 acc1 = f4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (Bits16<XT>::NP == 1) {
+        acc1 = mma(xp[0], b1[2], acc1);
+        acc1 = mma(xp[0], b1[1], acc1);
+        acc1 = mma(xp[0], b1[0], acc1);
+      } else {
+        acc1 = mma_2x3(xp[0], xp[1], b1, acc1);
+      }
+#pragma unroll
+      for (int r2 = 0; r2 < NRB2; ++r2) {
+        const f4 a = a2t[(r2 * NRB1 + rb) * 64 + lane];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          acc2[r2] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[v], acc1[v], acc2[r2], 0, 0, 0);
+      }
+    }
+    // round g of the workgroup (every wave is in the same round) uses stack g % 2
+    LDS float* const st = stacks + cur * SF;
+#pragma unroll
+    for (int r2 = 0; r2 < NRB2; ++r2)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t j1 = 16 * r2 + 4 * lg + v;
+        st[(j1 < R1 && li < R2) ? wv * RC + j1 * R2 + li : trash + lane] = acc2[r2][v];
+      }
+
+    // the round's stack is complete; its share of the mode d-2 product (the other stack
+    // is written only after the next barrier, which follows these reads)
+    wait_lgkm0();
+    wave_fence();
+    __builtin_amdgcn_s_barrier();
+    wave_fence();
+#pragma unroll
+    for (int h = 0; h < WPB3 / 4; ++h) {
+      const uint32_t i0l = 4 * h + lg;               // row of the stack
+      const uint32_t i0 = WPB3 * c + i0l;            // mode d-2 index
+      float bv[NTW], av[NTW];
+#pragma unroll
+      for (int m = 0; m < NTW; ++m) {
+        const uint32_t t = wv + WPB3 * m;
+        const uint32_t tt = t < ntile ? t : 0;
+        const uint32_t jb = tt / nct, ct = tt - jb * nct;
+        const uint32_t j0 = 16 * jb + li;
+        // columns >= RC read into the next row or the trash slots; they only reach
+        // outputs that are not stored
+        bv[m] = st[i0l * RC + 16 * ct + li];
+        av[m] = j0 < R0 ? m0s[j0 * I0 + i0] : 0.0f;
+      }
+#pragma unroll
+      for (int m = 0; m < NTW; ++m)
+        acc3[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[m], bv[m], acc3[m], 0, 0, 0);
+    }
+    if (c == nch - 1) pend = blockIdx.x + r * G;
+  };
+  for (uint32_t g = 0; g < cnt; g += 2) {
+    slab(g, Slot<0>{});
+    if (g + 1 < cnt) slab(g + 1, Slot<1>{});
+  }
+  write_unit();
+}
+
+struct Plan3s {
+  S3K k;
+  size_t lds;
+  int nrb1, nrb2, ntw;
+  bool ok;
+};
+
+uint32_t al16(uint32_t x) { return (x + 15u) & ~15u; }
+
+Plan3s plan3s(const ModeProd2& mp) {
+  Plan3s p{};
+  S3K& k = p.k;
+  p.ok = false;
+  if (mp.P != 1 || mp.recon) return p;
+  if (mp.in_dt != DT_BF16 && mp.in_dt != DT_F16) return p;
+  const uint32_t I0 = mp.I0, I1 = mp.I1, I2 = mp.I2, R0 = mp.R0, R1 = mp.R1, R2 = mp.R2;
+  if (I0 < (uint32_t)WPB3 || I0 > 64 || I0 % WPB3 != 0 || R0 == 0 || R0 > 32) return p;
+  if (I1 > 64 || I2 > 32 || R1 > 32 || R2 > 16 || I1 == 0 || I2 == 0 || R1 == 0 || R2 == 0)
+    return p;
+  const uint32_t slab_e = I1 * I2;
+  if (slab_e % 8 != 0 || mp.A == 0 || mp.A % I0 != 0) return p;
+  if ((uintptr_t)mp.X % 16) return p;
+  const uint32_t ntile = ((R0 + 15) / 16) * ((R1 * R2 + 15) / 16);
+  const uint32_t ntw = (ntile + WPB3 - 1) / WPB3;
+  p.ntw = ntw <= 2 ? 2 : ntw <= 3 ? 3 : ntw <= 5 ? 5 : ntw <= 8 ? 8 : 0;
+  if (!p.ntw) return p;
+  k.U = mp.A / I0;
+  k.I0 = I0; k.I1 = I1; k.I2 = I2; k.R0 = R0; k.R1 = R1; k.R2 = R2;
+  k.slab_e = slab_e;
+  p.nrb1 = (int)((I1 + 15) / 16);
+  p.nrb2 = (int)((R1 + 15) / 16);
+  k.off_x1 = al16(slab_e * 2);
+  k.lds_wave = 2 * k.off_x1;
+  k.off_stack = WPB3 * k.lds_wave;
+  k.stack_fl = al16((WPB3 * R1 * R2 + 64) * 4) / 4;
+  k.off_m0 = k.off_stack + 2 * k.stack_fl * 4;
+  k.off_fac = k.off_m0 + al16(R0 * I0 * 4);
+  p.lds = k.off_fac + 3 * 64 * 16 + (size_t)p.nrb2 * p.nrb1 * 64 * 16;
+  p.ok = p.lds <= 160 * 1024;
+  return p;
+}
+
+template <typename XT, int NRB1, int NRB2>
+hipError_t proj3_ntw(const Plan3s& p, int num_cu, hipStream_t s) {
+  auto fn = p.ntw == 2   ? k_proj3s<XT, NRB1, NRB2, 2>
+            : p.ntw == 3 ? k_proj3s<XT, NRB1, NRB2, 3>
+            : p.ntw == 5 ? k_proj3s<XT, NRB1, NRB2, 5>
+                         : k_proj3s<XT, NRB1, NRB2, 8>;
+  if (p.lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)fn,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
+    if (e != hipSuccess) return e;
+  }
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT3, p.lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidValue;
+  uint64_t grid = (uint64_t)(num_cu > 0 ? num_cu : 256) * (uint64_t)per_cu;
+  if (grid > p.k.U) grid = p.k.U;
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(NT3), p.lds, s, p.k);
+  return hipGetLastError();
+}
+template <typename XT, int NRB1>
+hipError_t proj3_nrb2(const Plan3s& p, int num_cu, hipStream_t s) {
+  if (p.nrb2 == 1) return proj3_ntw<XT, NRB1, 1>(p, num_cu, s);
+  return proj3_ntw<XT, NRB1, 2>(p, num_cu, s);
+}
+template <typename XT>
+hipError_t proj3_go(const Plan3s& p, int num_cu, hipStream_t s) {
+  switch (p.nrb1) {
+    case 1: return proj3_nrb2<XT, 1>(p, num_cu, s);
+    case 2: return proj3_nrb2<XT, 2>(p, num_cu, s);
+    case 3: return proj3_nrb2<XT, 3>(p, num_cu, s);
+    default: return proj3_nrb2<XT, 4>(p, num_cu, s);
   }
 }
 
@@ -584,8 +977,6 @@ struct Plan2s {
   int nrb1, nrb2;   // projection: (NRB1, NRB2); reconstruction: (NRB1, NCB2)
   bool ok;
 };
-
-uint32_t al16(uint32_t x) { return (x + 15u) & ~15u; }
 
 Plan2s plan2s(const ModeProd2& mp, int num_cu) {
   Plan2s p{};
@@ -704,6 +1095,25 @@ hipError_t rec_go(const Plan2s& p, hipStream_t s) {
 }  // namespace
 
 bool slab2_supported(const ModeProd2& mp, int num_cu) { return plan2s(mp, num_cu).ok; }
+
+bool slab3_supported(const ModeProd2& mp) { return plan3s(mp).ok; }
+
+hipError_t launch_slab3(const ModeProd2& mp, int num_cu, hipStream_t s) {
+  Plan3s p = plan3s(mp);
+  if (!p.ok) return hipErrorInvalidValue;
+  S3K& k = p.k;
+  k.X = mp.X;
+  k.Y = mp.Y;
+  k.M0 = mp.M0;
+  k.M1 = mp.M1;
+  k.M2 = mp.M2;
+  k.mask = mp.mask;
+  k.rank = mp.rank;
+  k.omega = mp.omega;
+  k.S = mp.gather_S;
+  k.kS = mp.gather_S ? mp.kS : 0;
+  return mp.in_dt == DT_BF16 ? proj3_go<bf16_t>(p, num_cu, s) : proj3_go<_Float16>(p, num_cu, s);
+}
 
 hipError_t launch_slab2(const ModeProd2& mp, int num_cu, hipStream_t s) {
   Plan2s p = plan2s(mp, num_cu);

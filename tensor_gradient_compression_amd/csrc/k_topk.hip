@@ -278,12 +278,14 @@ __global__ void __launch_bounds__(256) k_topk_count(const void* __restrict__ G, 
   }
 }
 
-// One block of 1024 threads: exclusive scan of the (gt, eq) unit counts, in chunks of
-// 1024 x SCAN_V consecutive units (each thread SCAN_V of them, loaded as 16-byte
-// pieces); the next chunk's counts are loaded before the current chunk is scanned.
+// Exclusive scan of the (gt, eq) unit counts in chunks of 1024 x SCAN_V consecutive units
+// (each thread SCAN_V of them, loaded as 16-byte pieces), one block of 1024 threads per
+// chunk: k_topk_chunk_tot sums each chunk, k_topk_scan adds the totals of the chunks
+// before its own and scans it.
 // uoff[2u] = selected elements before unit u = gt before + min(eq before, need);
 // uoff[2u + 1] = ties before unit u. (N < 2^32, so every count fits in 32 bits.)
 constexpr int SCAN_V = 8;
+constexpr uint32_t SCAN_CH = 1024u * SCAN_V;
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sw, uint32_t& total) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   uint32_t x = v;
@@ -306,63 +308,89 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sw, ui
   return before + x - v;
 }
 
+// this thread's SCAN_V unit counts of the chunk at unit c0 (zeros past the end)
+__device__ __forceinline__ void scan_load(const uint32_t* __restrict__ ucount, uint32_t nu,
+                                          uint32_t c0, uint4* v) {
+  const uint32_t u0 = c0 + (uint32_t)threadIdx.x * SCAN_V;
+#pragma unroll
+  for (int q = 0; q < SCAN_V / 2; ++q) {
+    const uint32_t u = u0 + 2 * q;
+    if (u + 2 <= nu) {
+      v[q] = *(const uint4*)(ucount + 2 * (uint64_t)u);
+    } else {
+      v[q] = make_uint4(u < nu ? ucount[2 * (uint64_t)u] : 0u,
+                        u < nu ? ucount[2 * (uint64_t)u + 1] : 0u, 0u, 0u);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(1024) k_topk_chunk_tot(const uint32_t* __restrict__ ucount,
+                                                         uint64_t nunits,
+                                                         uint32_t* __restrict__ ctot) {
+  __shared__ uint32_t sw[16];
+  uint4 cur[SCAN_V / 2];
+  scan_load(ucount, (uint32_t)nunits, blockIdx.x * SCAN_CH, cur);
+  uint32_t g = 0, q = 0;
+#pragma unroll
+  for (int i = 0; i < SCAN_V / 2; ++i) {
+    g += cur[i].x + cur[i].z;
+    q += cur[i].y + cur[i].w;
+  }
+  uint32_t gt_tot, eq_tot;
+  block_excl_scan(g, sw, gt_tot);
+  block_excl_scan(q, sw, eq_tot);
+  if (threadIdx.x == 0) {
+    ctot[2 * blockIdx.x] = gt_tot;
+    ctot[2 * blockIdx.x + 1] = eq_tot;
+  }
+}
+
 __global__ void __launch_bounds__(1024) k_topk_scan(const uint32_t* __restrict__ ucount,
                                                     uint64_t nunits,
+                                                    const uint32_t* __restrict__ ctot,
                                                     const uint64_t* __restrict__ state,
                                                     uint32_t* __restrict__ uoff) {
   __shared__ uint32_t sw[16];
   const int t = threadIdx.x;
   const uint32_t need = (uint32_t)state[1];
   const uint32_t nu = (uint32_t)nunits;
-  constexpr uint32_t CH = 1024u * SCAN_V;
-  auto load = [&](uint32_t c0, uint4* v) {
-    const uint32_t u0 = c0 + (uint32_t)t * SCAN_V;
+  const uint32_t c0 = blockIdx.x * SCAN_CH;
+  uint4 cur[SCAN_V / 2];
+  scan_load(ucount, nu, c0, cur);
+  // the counts of every earlier chunk
+  uint32_t gb = 0, qb = 0;
+  for (uint32_t c = t; c < blockIdx.x; c += 1024) {
+    gb += ctot[2 * c];
+    qb += ctot[2 * c + 1];
+  }
+  uint32_t gbase, qbase;
+  block_excl_scan(gb, sw, gbase);
+  block_excl_scan(qb, sw, qbase);
+  uint32_t g = 0, q = 0;
 #pragma unroll
-    for (int q = 0; q < SCAN_V / 2; ++q) {
-      const uint32_t u = u0 + 2 * q;
-      if (u + 2 <= nu) {
-        v[q] = *(const uint4*)(ucount + 2 * (uint64_t)u);
-      } else {
-        v[q] = make_uint4(u < nu ? ucount[2 * (uint64_t)u] : 0u,
-                          u < nu ? ucount[2 * (uint64_t)u + 1] : 0u, 0u, 0u);
-      }
+  for (int i = 0; i < SCAN_V / 2; ++i) {
+    g += cur[i].x + cur[i].z;
+    q += cur[i].y + cur[i].w;
+  }
+  uint32_t gt_tot, eq_tot;
+  uint32_t gp = gbase + block_excl_scan(g, sw, gt_tot);
+  uint32_t qp = qbase + block_excl_scan(q, sw, eq_tot);
+  const uint32_t u0 = c0 + (uint32_t)t * SCAN_V;
+#pragma unroll
+  for (int i = 0; i < SCAN_V / 2; ++i) {
+    const uint32_t u = u0 + 2 * i;
+    const uint32_t o0 = gp + (qp < need ? qp : need), e0 = qp;
+    gp += cur[i].x;
+    qp += cur[i].y;
+    const uint32_t o1 = gp + (qp < need ? qp : need), e1 = qp;
+    gp += cur[i].z;
+    qp += cur[i].w;
+    if (u + 2 <= nu) {
+      *(uint4*)(uoff + 2 * (uint64_t)u) = make_uint4(o0, e0, o1, e1);
+    } else if (u < nu) {
+      uoff[2 * (uint64_t)u] = o0;
+      uoff[2 * (uint64_t)u + 1] = e0;
     }
-  };
-  uint4 cur[SCAN_V / 2], nxt[SCAN_V / 2];
-  load(0, cur);
-  uint32_t gbase = 0, qbase = 0;
-  for (uint32_t c0 = 0; c0 < nu; c0 += CH) {
-    if (c0 + CH < nu) load(c0 + CH, nxt);
-    uint32_t g = 0, q = 0;
-#pragma unroll
-    for (int i = 0; i < SCAN_V / 2; ++i) {
-      g += cur[i].x + cur[i].z;
-      q += cur[i].y + cur[i].w;
-    }
-    uint32_t gt_tot, eq_tot;
-    uint32_t gp = gbase + block_excl_scan(g, sw, gt_tot);
-    uint32_t qp = qbase + block_excl_scan(q, sw, eq_tot);
-    const uint32_t u0 = c0 + (uint32_t)t * SCAN_V;
-#pragma unroll
-    for (int i = 0; i < SCAN_V / 2; ++i) {
-      const uint32_t u = u0 + 2 * i;
-      const uint32_t o0 = gp + (qp < need ? qp : need), e0 = qp;
-      gp += cur[i].x;
-      qp += cur[i].y;
-      const uint32_t o1 = gp + (qp < need ? qp : need), e1 = qp;
-      gp += cur[i].z;
-      qp += cur[i].w;
-      if (u + 2 <= nu) {
-        *(uint4*)(uoff + 2 * (uint64_t)u) = make_uint4(o0, e0, o1, e1);
-      } else if (u < nu) {
-        uoff[2 * (uint64_t)u] = o0;
-        uoff[2 * (uint64_t)u + 1] = e0;
-      }
-    }
-    gbase += gt_tot;
-    qbase += eq_tot;
-#pragma unroll
-    for (int i = 0; i < SCAN_V / 2; ++i) cur[i] = nxt[i];
   }
 }
 
@@ -487,8 +515,11 @@ hipError_t run_topk(const void* G, uint64_t N, uint32_t k, const TopkWs& ws, uin
   k_topk_count<K, RK><<<ub, 256, 0, s>>>(G, N, ws.state, ws.ucount, nunits, rk_base);
   M(KID_TOPK_COUNT, false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  const unsigned nch = (unsigned)topk_chunks(N);
   M(KID_TOPK_SCAN, true);
-  k_topk_scan<<<1, 1024, 0, s>>>(ws.ucount, nunits, ws.state, ws.uoff);
+  k_topk_chunk_tot<<<nch, 1024, 0, s>>>(ws.ucount, nunits, ws.ctot);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  k_topk_scan<<<nch, 1024, 0, s>>>(ws.ucount, nunits, ws.ctot, ws.state, ws.uoff);
   M(KID_TOPK_SCAN, false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   M(KID_TOPK_COMPACT, true);
@@ -557,6 +588,7 @@ unsigned fill_blocks(uint64_t n) {
 }  // namespace
 
 uint64_t topk_units(uint64_t N) { return (N + UNIT - 1) / UNIT; }
+uint64_t topk_chunks(uint64_t N) { return (topk_units(N) + SCAN_CH - 1) / SCAN_CH; }
 
 template <class K>
 hipError_t topk_dispatch(const void* G, uint64_t N, uint32_t k, const TopkWs& ws,

@@ -60,7 +60,7 @@ enum KernelId {
   KID_TOPK_COMPACT, KID_MASK_FROM_OMEGA, KID_GATHER, KID_PROJECT, KID_ADAM,
   KID_RECONSTRUCT, KID_RECON_APPLY, KID_APPLY_DENSE, KID_GRAM, KID_GRAM_REDUCE,
   KID_EIG, KID_FILL, KID_PROJECT_FIRST, KID_PROJECT_FUSED2, KID_RECON_FUSED2_APPLY,
-  KID_RECON_FUSED2, KID_REMAP, KID_COUNT_
+  KID_RECON_FUSED2, KID_REMAP, KID_PROJECT_FUSED3, KID_COUNT_
 };
 
 // ---------------------------------------------------------------- launchers
@@ -71,8 +71,10 @@ struct TopkWs {
   uint64_t* state;      // TopkState (4 x u64)
   uint32_t* ucount;     // 2 per unit
   uint32_t* uoff;       // 2 per unit
+  uint32_t* ctot;       // 2 per scan chunk of 8192 units
 };
 uint64_t topk_units(uint64_t N);
+uint64_t topk_chunks(uint64_t N);
 // Omega = the k largest keys, ties to the lowest index. randk == 0: magnitude keys of G;
 // randk != 0: element e's key is the top 31 bits of SplitMix64's output for the state
 // rk_base + 0x9E3779B97F4A7C15 * e (G is then read only for the residual).
@@ -161,6 +163,10 @@ struct ModeProd2 {
   // projection only: also perform the COO gather on the staged input, S[j] = X[omega[j]]
   // (fp32), and project the staged input with Omega zeroed (X itself is only read)
   float* gather_S;
+  // three-mode projection: the mode before the two (full size I0, rank R0, operand M0);
+  // A then counts (unit, i0) slabs
+  uint32_t I0, R0;
+  const float* M0;
 };
 uint32_t modeprod2_tile(const ModeProd2& mp);   // 0: does not fit
 hipError_t launch_modeprod2(const ModeProd2& mp, int num_cu, hipStream_t s);
@@ -170,6 +176,12 @@ hipError_t launch_modeprod2(const ModeProd2& mp, int num_cu, hipStream_t s);
 // R1 <= 32, R2 <= 16) and the buffers are 16-byte aligned.
 bool slab2_supported(const ModeProd2& mp, int num_cu);
 hipError_t launch_slab2(const ModeProd2& mp, int num_cu, hipStream_t s);
+// Projection over the last three modes in one launch (16-bit data, gather folded in as
+// above): one workgroup of 16 waves per index of the leading modes at a time, supported
+// when I0 is a multiple of 16 up to 64, R0 <= 32 and the two trailing modes fit the slab
+// kernel.
+bool slab3_supported(const ModeProd2& mp);
+hipError_t launch_slab3(const ModeProd2& mp, int num_cu, hipStream_t s);
 
 // Gram of the (A, I, B, P) view with Omega entries treated as zero:
 // out[x, y] (fp64, (I*P) x (I*P)) = sum over (a, b) of X[a, x, b] X[a, y, b].

@@ -50,6 +50,8 @@ struct tgrad_handle {
   bool can_fuse = false;     // last two modes compressed and a slab fits in LDS
   bool fuse = false;         // use the two-mode launches
   bool slab2 = true;         // 16-bit data: the wave-per-slab two-mode kernels where they fit
+  bool can_slab3 = false;    // the projection's first launch can also take mode d-3
+  bool slab3 = true;         // use it
 
   uint32_t* omega = nullptr;
   uint64_t* mask = nullptr;
@@ -250,16 +252,20 @@ void host_operands(uint32_t I, uint32_t r, uint32_t P, const float* U, float* Mp
 
 // Launch groups of the projection (applied in order) and the reconstruction: each group
 // is one launch, one mode or the two trailing modes together.
-void build_chain(const tgrad_t* h, bool fuse, std::vector<std::vector<int>>& proj,
+// Launch groups of the two chains. fuse: the two trailing modes run as one launch in
+// each direction; proj3 (with fuse): the projection's first launch also takes mode d-3.
+void build_chain(const tgrad_t* h, bool fuse, bool proj3, std::vector<std::vector<int>>& proj,
                  std::vector<std::vector<int>>& rec) {
   proj.clear();
   rec.clear();
   const int nf = (int)h->fmodes.size();
   const int d = h->d;
-  if (fuse) proj.push_back({d - 1, d - 2});
+  proj3 = proj3 && fuse;
+  if (proj3) proj.push_back({d - 1, d - 2, d - 3});
+  else if (fuse) proj.push_back({d - 1, d - 2});
   for (int j = nf - 1; j >= 0; --j) {
     const int n = h->fmodes[j];
-    if (fuse && n >= d - 2) continue;
+    if ((fuse && n >= d - 2) || (proj3 && n == d - 3)) continue;
     proj.push_back({n});
   }
   for (int j = 0; j < nf; ++j) {
@@ -268,6 +274,11 @@ void build_chain(const tgrad_t* h, bool fuse, std::vector<std::vector<int>>& pro
     rec.push_back({n});
   }
   if (fuse) rec.push_back({d - 2, d - 1});
+}
+
+// The three-mode projection launch for input X0 (16-byte aligned for its transfers).
+bool use_proj3(const tgrad_t* h, const void* X0) {
+  return h->fuse && h->slab2 && h->slab3 && h->can_slab3 && ((uintptr_t)X0 % 16) == 0;
 }
 
 int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s);
@@ -380,7 +391,7 @@ const char* tgrad_kernel_name(int id) {
       "modeprod_reconstruct", "modeprod_reconstruct_apply", "apply_dense", "gram",
       "gram_reduce", "eig_jacobi", "fill", "modeprod_project_first",
       "modeprod2_project_first", "modeprod2_reconstruct_apply", "modeprod2_reconstruct",
-      "remap_moments"};
+      "remap_moments", "modeprod3_project_first"};
   if (id < 0 || id >= KID_COUNT_) return "";
   return names[id];
 }
@@ -457,6 +468,13 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
       std::swap(rr.I2, rr.R2);
       h->can_fuse = modeprod2_tile(pp) > 0 && modeprod2_tile(rr) > 0;
       h->fuse = h->can_fuse;
+      if (h->can_fuse && d >= 3 && tucker_ranks[d - 3] < shape[d - 3]) {
+        ModeProd2 p3 = pp;
+        p3.X = (const void*)(uintptr_t)256;   // transfers need a 16-byte aligned input
+        p3.I0 = (uint32_t)shape[d - 3];
+        p3.R0 = (uint32_t)tucker_ranks[d - 3];
+        h->can_slab3 = slab3_supported(p3);
+      }
     }
   }
   // Largest intermediate of the projection and reconstruction chains (either plan).
@@ -467,7 +485,7 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
     int64_t cur[TGRAD_MAX_NDIM];
     for (int i = 0; i < ndim; ++i) cur[i] = shape[i];
     std::vector<std::vector<int>> proj, rec;
-    build_chain(h, fz, proj, rec);
+    build_chain(h, fz, false, proj, rec);
     uint64_t size = N;
     for (size_t j = 0; j < proj.size(); ++j) {
       for (int n : proj[j]) {
@@ -545,6 +563,7 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
   ok = ok && dalloc(h, &h->tw.state, 4, false);
   ok = ok && dalloc(h, &h->tw.ucount, 2 * units, false);
   ok = ok && dalloc(h, &h->tw.uoff, 2 * units, false);
+  ok = ok && dalloc(h, &h->tw.ctot, 2 * topk_chunks(N), false);
   if (!ok) {
     free_all(h);
     delete h;
@@ -639,7 +658,7 @@ namespace {
 int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s) {
   const uint32_t P = h->P;
   std::vector<std::vector<int>> proj, rec;
-  build_chain(h, h->fuse, proj, rec);
+  build_chain(h, h->fuse, use_proj3(h, X0), proj, rec);
   int64_t cur[TGRAD_MAX_NDIM];
   for (int i = 0; i < h->d; ++i) cur[i] = h->shape[i];
   const void* X = X0;
@@ -647,7 +666,40 @@ int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s) {
   int which = 0;
   for (size_t j = 0; j < proj.size(); ++j) {
     float* Y = (j + 1 == proj.size()) ? h->core : h->buf[which];
-    if (proj[j].size() == 2) {
+    if (proj[j].size() == 3) {
+      const int d = h->d;
+      ModeProd2 mp{};
+      mp.X = X;
+      mp.in_dt = xdt;
+      mp.P = P;
+      uint32_t A, I, B;
+      view(cur, d, d - 2, &A, &I, &B);
+      mp.A = A;
+      mp.I0 = (uint32_t)cur[d - 3];
+      mp.I1 = (uint32_t)cur[d - 2];
+      mp.I2 = (uint32_t)cur[d - 1];
+      mp.R0 = (uint32_t)h->ranks[d - 3];
+      mp.R1 = (uint32_t)h->ranks[d - 2];
+      mp.R2 = (uint32_t)h->ranks[d - 1];
+      mp.recon = 0;
+      mp.M0 = h->Mp[d - 3];
+      mp.M1 = h->Mp[d - 2];
+      mp.M2 = h->Mp[d - 1];
+      mp.Y = Y;
+      if (j == 0 && gather) {
+        mp.gather_S = h->S;
+        mp.mask = h->mask;
+        mp.rank = h->rank;
+        mp.omega = h->omega;
+        mp.kS = h->k;
+        mp.has_sparse = 1;
+      }
+      Mark m(h, KID_PROJECT_FUSED3);
+      HIPCHK(h, launch_slab3(mp, h->num_cu, s));
+      cur[d - 3] = h->ranks[d - 3];
+      cur[d - 2] = h->ranks[d - 2];
+      cur[d - 1] = h->ranks[d - 1];
+    } else if (proj[j].size() == 2) {
       const int d = h->d;
       ModeProd2 mp{};
       mp.X = X;
@@ -708,7 +760,7 @@ int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, fl
                        hipStream_t s) {
   const uint32_t P = h->P;
   std::vector<std::vector<int>> proj, rec;
-  build_chain(h, h->fuse, proj, rec);
+  build_chain(h, h->fuse, false, proj, rec);
   int64_t cur[TGRAD_MAX_NDIM];
   for (int i = 0; i < h->d; ++i) cur[i] = h->shape[i];
   for (int n : h->fmodes) cur[n] = h->ranks[n];
@@ -822,10 +874,10 @@ int tgrad_step(tgrad_t* h, void* weight, const void* grad, void* stream) {
     }
   } else {
     std::vector<std::vector<int>> proj, rec;
-    build_chain(h, h->fuse, proj, rec);
-    // the COO gather runs on its own unless the first projection launch is the fused
-    // two-mode one, which takes S and zeroes Omega on its staged input
-    const bool gather_fused = h->k > 0 && !proj.empty() && proj[0].size() == 2;
+    build_chain(h, h->fuse, use_proj3(h, grad), proj, rec);
+    // the COO gather runs on its own unless the first projection launch is a fused
+    // multi-mode one, which takes S and zeroes Omega on its staged input
+    const bool gather_fused = h->k > 0 && !proj.empty() && proj[0].size() >= 2;
     // the first projection's input: grad itself, or (when the gather is not folded into
     // it) a copy of grad that the gather turns into the residual; grad is only read
     if (h->k > 0 && !gather_fused) {
@@ -1147,7 +1199,7 @@ int tgrad_set_options(tgrad_t* h, const tgrad_options* o) {
 }
 
 int tgrad_set_fusion(tgrad_t* h, int enable) {
-  if (!h || enable < 0 || enable > 2) return TGRAD_EINVAL;
+  if (!h || enable < 0 || enable > 3) return TGRAD_EINVAL;
   if (enable && !h->can_fuse) return TGRAD_EINVAL;
   if (!enable && h->k > 0 && !h->gcopy) {
     DevGuard g(h->device);
@@ -1157,6 +1209,7 @@ int tgrad_set_fusion(tgrad_t* h, int enable) {
   }
   h->fuse = enable != 0;
   h->slab2 = enable != 2;
+  h->slab3 = enable == 1;
   return TGRAD_OK;
 }
 

@@ -102,6 +102,14 @@ FACTOR_CASES = [
     ("f16-slab-40x17", custom((9, 40, 17), "f16", (5, 20, 9), 0.05)),
     ("bf16-slab-ragged", custom((7, 33, 24), "bf16", (4, 17, 12), 0.05)),
     ("bf16-slab-k0", custom((5, 16, 8), "bf16", (3, 8, 4), 0.0)),
+    # ... and whose mode d-3 joins them in the projection's first launch (a workgroup
+    # of 16 waves per leading index, in rounds of 16 slabs: three rounds a unit; two
+    # rounds with ragged slab blocks; one round a unit without a sparse part; more
+    # leading indices than the grid has workgroups)
+    ("bf16-slab3-48x48x25", custom((3, 48, 48, 25), "bf16", (2, 24, 24, 13), 0.05)),
+    ("f16-slab3-ragged", custom((2, 32, 40, 17), "f16", (2, 9, 20, 9), 0.05)),
+    ("bf16-slab3-k0", custom((2, 16, 16, 8), "bf16", (1, 8, 8, 4), 0.0)),
+    ("bf16-slab3-300-units", custom((300, 16, 8, 8), "bf16", (300, 8, 4, 4), 0.05)),
     ("f16-64", custom((64, 20, 9), "f16", (32, 7, 4), 0.05)),
     ("c64-small", custom((12, 10, 9), "c64", (5, 4, 3), 0.05)),
     ("c64-64", custom((64, 6, 33), "c64", (32, 6, 16), 0.05)),
@@ -137,13 +145,14 @@ STEP_CASES = FACTOR_CASES + [
 ]
 
 
-@pytest.mark.parametrize("fused", [1, 2, 0], ids=["fused", "fused-tiles", "one-mode"])
+@pytest.mark.parametrize("fused", [1, 3, 2, 0], ids=["fused", "fused-two-mode-slabs", "fused-tiles",
+                                                 "one-mode"])
 @pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: c[0])
 def test_steps_with_pinned_omega_and_factors(case, fused):
     """Omega and U(n) injected from the oracle, so only the step kernels are compared;
-    every launch plan (two trailing modes per launch with the default kernel choice, which
-    is one wave per slab for small 16-bit slabs; the same with workgroup tiles only; one
-    mode per launch)."""
+    every launch plan (trailing modes per launch with the default kernel choice, which is
+    one wave per slab for small 16-bit slabs and a three-mode first projection where it
+    applies; the two-mode slab kernels only; workgroup tiles only; one mode per launch)."""
     name, wl = case
     gs = GradStream(wl, seed=8)
     W0 = init_weights(wl, seed=8)
