@@ -159,9 +159,35 @@ constexpr int NOM = 3;
 // by two so that a slot index is a compile-time constant and the prefetched entries are
 // never copied between registers (a copy would have to wait for every load in flight,
 // the next slab's transfer included).
+// Bitmask words and word ranks at the start (lane 0) and the end (lane 1) of a slab,
+// fetched with vector loads: they retire on vmcnt with the slab transfers (scalar loads
+// would retire on lgkmcnt, out of order, so every wait on LDS traffic after them would
+// also wait for their memory round trip). Read out with lane_u64 / readlane after the
+// next vmcnt wait.
+struct BoundsV {
+  uint64_t m = 0;
+  uint32_t r = 0;
+};
+__device__ __forceinline__ BoundsV load_bounds(const uint64_t* mask, const uint32_t* rank,
+                                               uint64_t elo, uint64_t slab_e, uint64_t N,
+                                               uint32_t lane) {
+  const uint64_t ehi = elo + slab_e;
+  const uint64_t wl = elo >> 6, wh = ehi < N ? ehi >> 6 : 0;
+  const uint64_t idx = lane == 0 ? wl : wh;
+  BoundsV b;
+  b.m = mask[idx];
+  b.r = rank[idx];
+  return b;
+}
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 struct OmegaPipe {
   uint64_t lo[2] = {0, 0}, hi[2] = {0, 0};   // Omega ranges of the slabs in the two slots
-  uint64_t bw[4] = {0, 0, 0, 0};  // the slab after: mask, rank at its start; mask, rank at its end
+  BoundsV bw;                     // the slab after: bounds (lane 0: start, lane 1: end)
   uint32_t om[2][NOM];
   float us[2][NOM];
 };
@@ -220,28 +246,20 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
   const XT* X = (const XT*)k.X;
   const uint32_t xchunks = slab_e * 2 / 16;
   // bitmask words and ranks at the start and the end of slab s, and its Omega range
-  // (uniform over the wave and read-only here: scalar loads, which retire on lgkmcnt and
-  // leave the vector memory queue to the slab transfers)
-  auto bounds = [&](uint32_t s, uint64_t* w) {
-    const uint64_t elo = (uint64_t)s * slab_e, ehi = elo + slab_e;
-    const uint64_t wl = elo >> 6, wh = ehi < N ? ehi >> 6 : 0;
-    const __attribute__((address_space(4))) uint64_t* m =
-        (const __attribute__((address_space(4))) uint64_t*)k.mask;
-    const __attribute__((address_space(4))) uint32_t* r =
-        (const __attribute__((address_space(4))) uint32_t*)k.rank;
-    w[0] = m[wl];
-    w[1] = r[wl];
-    w[2] = m[wh];
-    w[3] = r[wh];
+  auto bounds = [&](uint32_t s, BoundsV& b) {
+    b = load_bounds(k.mask, k.rank, (uint64_t)s * slab_e, slab_e, N, lane);
   };
-  auto range = [&](uint32_t s, const uint64_t* w, uint64_t& lo, uint64_t& hi) {
-    lo = rank_at(w[0], (uint32_t)w[1], (uint64_t)s * slab_e, N, kS);
-    hi = rank_at(w[2], (uint32_t)w[3], (uint64_t)(s + 1) * slab_e, N, kS);
+  auto range = [&](uint32_t s, const BoundsV& b, uint64_t& lo, uint64_t& hi) {
+    lo = rank_at(lane_u64(b.m, 0), (uint32_t)__builtin_amdgcn_readlane((int)b.r, 0),
+                 (uint64_t)s * slab_e, N, kS);
+    hi = rank_at(lane_u64(b.m, 1), (uint32_t)__builtin_amdgcn_readlane((int)b.r, 1),
+                 (uint64_t)(s + 1) * slab_e, N, kS);
   };
   OmegaPipe op;
   if (sparse) {
-    uint64_t w[4];
+    BoundsV w;
     bounds(gw, w);
+    wait_vm0();
     range(gw, w, op.lo[0], op.hi[0]);
 #pragma unroll
     for (int i = 0; i < NOM; ++i) {
@@ -424,8 +442,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   const WT* Wg = (const WT*)k.W;
   const uint32_t zchunks = slab_z * 4 / 16, wchunks = slab_e * 2 / 16;
   // bitmask words and ranks at the start and the end of slab s, and its Omega range
-  // (uniform over the wave and read-only here: scalar loads, which retire on lgkmcnt and
-  // leave the vector memory queue to the slab transfers)
+  // (scalar loads here: this kernel has no register room for the vector form, and none
+  // of its LDS waits falls between a fetch and its use a slab later)
   auto bounds = [&](uint32_t s, uint64_t* w) {
     const uint64_t elo = (uint64_t)s * slab_e, ehi = elo + slab_e;
     const uint64_t wl = elo >> 6, wh = ehi < N ? ehi >> 6 : 0;
@@ -442,6 +460,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
     lo = rank_at(w[0], (uint32_t)w[1], (uint64_t)s * slab_e, N, kS);
     hi = rank_at(w[2], (uint32_t)w[3], (uint64_t)(s + 1) * slab_e, N, kS);
   };
+  uint64_t bws[4] = {0, 0, 0, 0};   // the slab after: mask, rank at its start; at its end
   OmegaPipe op;
   if (sparse) {
     uint64_t w[4];
@@ -454,20 +473,23 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
       op.om[0][i] = k.omega[jc];
       op.us[0][i] = k.S[jc];
     }
-    if (cnt > 1) bounds(gw + TW, op.bw);
+    if (cnt > 1) bounds(gw + TW, bws);
   }
   wave_dma(k.Zin + (uint64_t)gw * slab_z, zchunks, zb0, lane);
 
   uint32_t nq_prev = 0;
   uint64_t out_prev = 0;
-  // slab i of this wave (i < cnt), in slot `cur` (= i % 2), after the previous slab's
-  // weights have been written; i == cnt writes the last slab's weights and returns true
-  auto slab = [&](uint32_t i, auto slot) -> bool {
-    constexpr int cur = decltype(slot)::value, nxt = cur ^ 1;
+  // slab i of this wave (i < cnt) after the previous slab's weights have been written;
+  // i == cnt writes the last slab's weights and returns true. Omega data of this slab in
+  // slot 0, of the next in slot 1 (moved to slot 0 after the slab: unrolling this loop to
+  // alternate the slots would cost the registers that keep it at four waves per SIMD).
+  auto slab = [&](uint32_t i) -> bool {
+    constexpr int cur = 0, nxt = 1;
+    const int par = i & 1;            // LDS buffer of this slab's Z
     const uint32_t n = gw + i * TW;   // this slab (i < cnt)
     wait_vm0();   // Z of this slab, W of the previous one, Omega data; older stores
     wave_fence();
-    if (sparse && i + 1 < cnt) range(n + TW, op.bw, op.lo[nxt], op.hi[nxt]);
+    if (sparse && i + 1 < cnt) range(n + TW, bws, op.lo[nxt], op.hi[nxt]);
     // the previous slab: W <- round(W * decay - lr * O), 16-byte pieces (the stores are
     // waited for at the next slab)
     for (uint32_t q = lane; q < nq_prev; q += 64) {
@@ -498,7 +520,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
     // this slab's W (used at the next slab), the next slab's Z and Omega data
     wave_dma(Wg + (uint64_t)n * slab_e, wchunks, wb, lane);
     if (i + 1 < cnt) {
-      wave_dma(k.Zin + (uint64_t)(n + TW) * slab_z, zchunks, cur ? zb0 : zb1, lane);
+      wave_dma(k.Zin + (uint64_t)(n + TW) * slab_z, zchunks, par ? zb0 : zb1, lane);
       if (sparse) {
 #pragma unroll
         for (int q = 0; q < NOM; ++q) {
@@ -507,11 +529,11 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
           op.om[nxt][q] = k.omega[jc];
           op.us[nxt][q] = k.S[jc];
         }
-        if (i + 2 < cnt) bounds(n + 2 * TW, op.bw);
+        if (i + 2 < cnt) bounds(n + 2 * TW, bws);
       }
     }
 
-    const LDS float* const zs = (const LDS float*)(cur ? zb1 : zb0);
+    const LDS float* const zs = (const LDS float*)(par ? zb1 : zb0);
     // pass 1 (mode d-1): rows i1, k = j1, columns j2
     float zv[KS1];
 #pragma unroll
@@ -581,9 +603,15 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
     out_prev = (uint64_t)n * slab_e;
     return false;
   };
-  for (uint32_t i = 0;; i += 2) {
-    if (slab(i, Slot<0>{})) break;
-    if (slab(i + 1, Slot<1>{})) break;
+  for (uint32_t i = 0;; ++i) {
+    if (slab(i)) break;
+    op.lo[0] = op.lo[1];
+    op.hi[0] = op.hi[1];
+#pragma unroll
+    for (int q = 0; q < NOM; ++q) {
+      op.om[0][q] = op.om[1][q];
+      op.us[0][q] = op.us[1][q];
+    }
   }
 }
 
@@ -654,10 +682,13 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
   // workgroup (registers would not leave room for the mode d-2 accumulators):
   //   b1t[part][lane]: pass 1 B[k = i2][col = r2] = M2[r2][i2], i2 = 8 (lane / 16) + e,
   //                    r2 = lane % 16, in three bf16 parts (16 bytes a lane);
-  //   a2t[r2][rb][lane]: pass 2 A[row = j1][k] = M1[j1][i1], j1 = 16 r2 + lane % 16,
-  //                    i1 = 16 rb + 4 (lane / 16) + v for v = 0..3 (16 bytes a lane).
+  //   a2t[r2][kc][part][lane]: pass 2 A[row = j1][k] = M1[j1][i1] in three bf16 parts,
+  //                    j1 = 16 r2 + lane % 16, k chunk kc of 32: lane / 16 and e = 0..7
+  //                    stand for i1 = 16 (2 kc + e / 4) + 4 (lane / 16) + e % 4, the rows
+  //                    that pass 1 leaves in this lane's registers (16 bytes a lane).
+  constexpr int NKC = (NRB1 + 1) / 2;
   LDS u16x8* const b1t = (LDS u16x8*)(lds + k.off_fac);
-  LDS f4* const a2t = (LDS f4*)(lds + k.off_fac + 3 * 64 * 16);
+  LDS u16x8* const a2t = b1t + 3 * 64;
   for (uint32_t q = threadIdx.x; q < R0 * I0; q += NT3) m0s[q] = k.M0[q];
   if (wv == 0) {
     u16x8 b1[3];
@@ -675,14 +706,19 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
 #pragma unroll
     for (int r2 = 0; r2 < NRB2; ++r2)
 #pragma unroll
-      for (int rb = 0; rb < NRB1; ++rb) {
-        f4 a;
+      for (int kc = 0; kc < NKC; ++kc) {
+        u16x8 a[3];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint32_t j1 = 16 * r2 + li, i1 = 16 * rb + 4 * lg + v;
-          a[v] = (j1 < R1 && i1 < I1) ? k.M1[j1 * I1 + i1] : 0.0f;
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t rb = 2 * kc + e / 4;
+          const uint32_t j1 = 16 * r2 + li, i1 = 16 * rb + 4 * lg + e % 4;
+          const float v = (rb < (uint32_t)NRB1 && j1 < R1 && i1 < I1) ? k.M1[j1 * I1 + i1] : 0.0f;
+          unsigned short x, y, z;
+          split3(v, x, y, z);
+          a[0][e] = x; a[1][e] = y; a[2][e] = z;
         }
-        a2t[(r2 * NRB1 + rb) * 64 + lane] = a;
+#pragma unroll
+        for (int h = 0; h < 3; ++h) a2t[((r2 * NKC + kc) * 3 + h) * 64 + lane] = a[h];
       }
   }
   wait_lgkm0();
@@ -702,28 +738,22 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
   };
   const XT* X = (const XT*)k.X;
   const uint32_t xchunks = slab_e * 2 / 16;
-  auto bounds = [&](uint32_t s, uint64_t* w) {
-    const uint64_t elo = (uint64_t)s * slab_e, ehi = elo + slab_e;
-    const uint64_t wl = elo >> 6, wh = ehi < N ? ehi >> 6 : 0;
-    const __attribute__((address_space(4))) uint64_t* m =
-        (const __attribute__((address_space(4))) uint64_t*)k.mask;
-    const __attribute__((address_space(4))) uint32_t* r =
-        (const __attribute__((address_space(4))) uint32_t*)k.rank;
-    w[0] = m[wl];
-    w[1] = r[wl];
-    w[2] = m[wh];
-    w[3] = r[wh];
+  auto bounds = [&](uint32_t s, BoundsV& b) {
+    b = load_bounds(k.mask, k.rank, (uint64_t)s * slab_e, slab_e, N, lane);
   };
-  auto range = [&](uint32_t s, const uint64_t* w, uint64_t& lo, uint64_t& hi) {
-    lo = rank_at(w[0], (uint32_t)w[1], (uint64_t)s * slab_e, N, kS);
-    hi = rank_at(w[2], (uint32_t)w[3], (uint64_t)(s + 1) * slab_e, N, kS);
+  auto range = [&](uint32_t s, const BoundsV& b, uint64_t& lo, uint64_t& hi) {
+    lo = rank_at(lane_u64(b.m, 0), (uint32_t)__builtin_amdgcn_readlane((int)b.r, 0),
+                 (uint64_t)s * slab_e, N, kS);
+    hi = rank_at(lane_u64(b.m, 1), (uint32_t)__builtin_amdgcn_readlane((int)b.r, 1),
+                 (uint64_t)(s + 1) * slab_e, N, kS);
   };
   OmegaPipe op;
   {
     const uint32_t s0 = slab_of(0);
     if (sparse) {
-      uint64_t w[4];
+      BoundsV w;
       bounds(s0, w);
+      wait_vm0();
       range(s0, w, op.lo[0], op.hi[0]);
 #pragma unroll
       for (int q = 0; q < NOM; ++q) {
@@ -809,14 +839,28 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
       wave_fence();
     }
 
-    // pass 1 (mode d): rows i1, k = i2, columns r2, one 16-row block at a time, and
-    // the block's terms of pass 2 (mode d-1: rows j1, k = i1, columns r2) straight from
-    // its registers
+    // pass 1 (mode d): rows i1, k = i2, columns r2, two 16-row blocks at a time; their
+    // results, split in three bf16 parts in the registers that hold them, are one
+    // 32-deep k chunk of pass 2 (mode d-1: rows j1, k = i1, columns r2), which takes the
+    // six part products of order <= 2 on v_mfma_f32_16x16x32_bf16
     f4 acc2[NRB2];
 #pragma unroll
     for (int r2 = 0; r2 < NRB2; ++r2) acc2[r2] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int rb = 0; rb < NRB1; ++rb) {
+    for (int kc = 0; kc < NKC; ++kc) {
+    u16x8 bp[3];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int rb = 2 * kc + hh;
+      if (rb >= NRB1) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          bp[0][4 * hh + v] = 0;
+          bp[1][4 * hh + v] = 0;
+          bp[2][4 * hh + v] = 0;
+        }
+        continue;
+      }
       const uint32_t i1 = 16 * rb + li;
       u16x8 xp[Bits16<XT>::NP];
 #pragma unroll
@@ -841,12 +885,26 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
         acc1 = mma_2x3(xp[0], xp[1], b1, acc1);
       }
 #pragma unroll
-      for (int r2 = 0; r2 < NRB2; ++r2) {
-        const f4 a = a2t[(r2 * NRB1 + rb) * 64 + lane];
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          acc2[r2] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[v], acc1[v], acc2[r2], 0, 0, 0);
+      for (int v = 0; v < 4; ++v) {
+        unsigned short x, y, z;
+        split3(acc1[v], x, y, z);
+        bp[0][4 * hh + v] = x;
+        bp[1][4 * hh + v] = y;
+        bp[2][4 * hh + v] = z;
       }
+    }
+#pragma unroll
+    for (int r2 = 0; r2 < NRB2; ++r2) {
+      const LDS u16x8* const ap = a2t + (r2 * NKC + kc) * 3 * 64 + lane;
+      const u16x8 a0 = ap[0], a1 = ap[64], a2 = ap[128];
+      f4 c = acc2[r2];
+      c = mma(a2, bp[0], c);
+      c = mma(a1, bp[1], c);
+      c = mma(a0, bp[2], c);
+      c = mma(a1, bp[0], c);
+      c = mma(a0, bp[1], c);
+      acc2[r2] = mma(a0, bp[0], c);
+    }
     }
     // round g of the workgroup (every wave is in the same round) uses stack g % 2
     LDS float* const st = stacks + cur * SF;
@@ -930,7 +988,7 @@ Plan3s plan3s(const ModeProd2& mp) {
   k.stack_fl = al16((WPB3 * R1 * R2 + 64) * 4) / 4;
   k.off_m0 = k.off_stack + 2 * k.stack_fl * 4;
   k.off_fac = k.off_m0 + al16(R0 * I0 * 4);
-  p.lds = k.off_fac + 3 * 64 * 16 + (size_t)p.nrb2 * p.nrb1 * 64 * 16;
+  p.lds = k.off_fac + 3 * 64 * 16 + (size_t)p.nrb2 * ((p.nrb1 + 1) / 2) * 3 * 64 * 16;
   p.ok = p.lds <= 160 * 1024;
   return p;
 }
