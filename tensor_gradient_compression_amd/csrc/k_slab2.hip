@@ -676,19 +676,21 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
   const uint64_t N = (uint64_t)k.U * I0 * slab_e;
   const uint64_t kS = k.kS;
   const bool sparse = kS > 0;
-  const uint32_t nct = (RC + 15) / 16, ntile = ((R0 + 15) / 16) * nct;
+  // mode d-2 output tiles of this wave: row block jb = wv / (WPB3 / 2), column blocks
+  // ct0 + (WPB3 / 2) m, ct0 = wv % (WPB3 / 2)
+  const uint32_t nct = (RC + 15) / 16, njb = (R0 + 15) / 16;
+  const uint32_t jb = wv / (WPB3 / 2), ct0 = wv % (WPB3 / 2);
+  const uint32_t j0 = 16 * jb + li;
+  const bool jok = jb < njb && j0 < R0;
 
   // The factor operands, as every lane supplies them, in LDS tables shared by the
   // workgroup (registers would not leave room for the mode d-2 accumulators):
   //   b1t[part][lane]: pass 1 B[k = i2][col = r2] = M2[r2][i2], i2 = 8 (lane / 16) + e,
   //                    r2 = lane % 16, in three bf16 parts (16 bytes a lane);
-  //   a2t[r2][kc][part][lane]: pass 2 A[row = j1][k] = M1[j1][i1] in three bf16 parts,
-  //                    j1 = 16 r2 + lane % 16, k chunk kc of 32: lane / 16 and e = 0..7
-  //                    stand for i1 = 16 (2 kc + e / 4) + 4 (lane / 16) + e % 4, the rows
-  //                    that pass 1 leaves in this lane's registers (16 bytes a lane).
-  constexpr int NKC = (NRB1 + 1) / 2;
+  //   a2t[r2][rb][lane]: pass 2 A[row = j1][k] = M1[j1][i1], j1 = 16 r2 + lane % 16,
+  //                    i1 = 16 rb + 4 (lane / 16) + v for v = 0..3 (16 bytes a lane).
   LDS u16x8* const b1t = (LDS u16x8*)(lds + k.off_fac);
-  LDS u16x8* const a2t = b1t + 3 * 64;
+  LDS f4* const a2t = (LDS f4*)(lds + k.off_fac + 3 * 64 * 16);
   for (uint32_t q = threadIdx.x; q < R0 * I0; q += NT3) m0s[q] = k.M0[q];
   if (wv == 0) {
     u16x8 b1[3];
@@ -706,19 +708,14 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
 #pragma unroll
     for (int r2 = 0; r2 < NRB2; ++r2)
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        u16x8 a[3];
+      for (int rb = 0; rb < NRB1; ++rb) {
+        f4 a;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t rb = 2 * kc + e / 4;
-          const uint32_t j1 = 16 * r2 + li, i1 = 16 * rb + 4 * lg + e % 4;
-          const float v = (rb < (uint32_t)NRB1 && j1 < R1 && i1 < I1) ? k.M1[j1 * I1 + i1] : 0.0f;
-          unsigned short x, y, z;
-          split3(v, x, y, z);
-          a[0][e] = x; a[1][e] = y; a[2][e] = z;
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t j1 = 16 * r2 + li, i1 = 16 * rb + 4 * lg + v;
+          a[v] = (j1 < R1 && i1 < I1) ? k.M1[j1 * I1 + i1] : 0.0f;
         }
-#pragma unroll
-        for (int h = 0; h < 3; ++h) a2t[((r2 * NKC + kc) * 3 + h) * 64 + lane] = a[h];
+        a2t[(r2 * NRB1 + rb) * 64 + lane] = a;
       }
   }
   wait_lgkm0();
@@ -732,9 +729,14 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
   const uint32_t nu = (k.U - 1 - blockIdx.x) / G + 1;
   const uint32_t nch = I0 / WPB3;
   const uint32_t cnt = nu * nch;
-  auto slab_of = [&](uint32_t g) -> uint32_t {
-    const uint32_t r = g / nch, c = g - r * nch;
+  auto slab_at = [&](uint32_t r, uint32_t c) -> uint32_t {
     return (blockIdx.x + r * G) * I0 + WPB3 * c + wv;
+  };
+  auto step = [&](uint32_t& r, uint32_t& c) {
+    if (++c == nch) {
+      c = 0;
+      ++r;
+    }
   };
   const XT* X = (const XT*)k.X;
   const uint32_t xchunks = slab_e * 2 / 16;
@@ -749,7 +751,7 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
   };
   OmegaPipe op;
   {
-    const uint32_t s0 = slab_of(0);
+    const uint32_t s0 = slab_at(0, 0);
     if (sparse) {
       BoundsV w;
       bounds(s0, w);
@@ -760,7 +762,9 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
         const uint64_t j = op.lo[0] + lane + 64 * q;
         op.om[0][q] = k.omega[j < kS ? j : kS - 1];
       }
-      if (cnt > 1) bounds(slab_of(1), op.bw);
+      uint32_t r1 = 0, c1 = 0;
+      step(r1, c1);
+      if (cnt > 1) bounds(slab_at(r1, c1), op.bw);
     }
     wave_dma(X + (uint64_t)s0 * slab_e, xchunks, xb0, lane);
   }
@@ -775,9 +779,8 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
     if (pend == 0xFFFFFFFFu) return;
 #pragma unroll
     for (int m = 0; m < NTW; ++m) {
-      const uint32_t t = wv + WPB3 * m;
-      if (t < ntile) {
-        const uint32_t jb = t / nct, ct = t - jb * nct;
+      const uint32_t ct = ct0 + (WPB3 / 2) * m;
+      if (jb < njb && ct < nct) {
         const uint32_t col = 16 * ct + li;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -790,15 +793,17 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
     pend = 0xFFFFFFFFu;
   };
 
+  uint32_t r = 0, c = 0;   // the current slab's unit (of this workgroup) and round
   auto slab = [&](uint32_t g, auto slot) {
     constexpr int cur = decltype(slot)::value, nxt = cur ^ 1;
-    const uint32_t n = slab_of(g);
-    const uint32_t r = g / nch, c = g - r * nch;
+    const uint32_t n = slab_at(r, c);
+    uint32_t r1 = r, c1 = c;
+    step(r1, c1);
     wait_vm0();   // slab n, its Omega indices and the next slab's bounds have landed
     wave_fence();
     write_unit();
     if (g + 1 < cnt) {
-      const uint32_t n1 = slab_of(g + 1);
+      const uint32_t n1 = slab_at(r1, c1);
       if (sparse) range(n1, op.bw, op.lo[nxt], op.hi[nxt]);
       wave_dma(X + (uint64_t)n1 * slab_e, xchunks, cur ? xb0 : xb1, lane);
       if (sparse) {
@@ -807,7 +812,9 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
           const uint64_t j = op.lo[nxt] + lane + 64 * q;
           op.om[nxt][q] = k.omega[j < kS ? j : kS - 1];
         }
-        if (g + 2 < cnt) bounds(slab_of(g + 2), op.bw);
+        uint32_t r2 = r1, c2 = c1;
+        step(r2, c2);
+        if (g + 2 < cnt) bounds(slab_at(r2, c2), op.bw);
       }
     }
 
@@ -839,28 +846,14 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
       wave_fence();
     }
 
-    // pass 1 (mode d): rows i1, k = i2, columns r2, two 16-row blocks at a time; their
-    // results, split in three bf16 parts in the registers that hold them, are one
-    // 32-deep k chunk of pass 2 (mode d-1: rows j1, k = i1, columns r2), which takes the
-    // six part products of order <= 2 on v_mfma_f32_16x16x32_bf16
+    // pass 1 (mode d): rows i1, k = i2, columns r2, one 16-row block at a time, and
+    // the block's terms of pass 2 (mode d-1: rows j1, k = i1, columns r2) straight from
+    // its registers
     f4 acc2[NRB2];
 #pragma unroll
     for (int r2 = 0; r2 < NRB2; ++r2) acc2[r2] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-    u16x8 bp[3];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int rb = 2 * kc + hh;
-      if (rb >= NRB1) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          bp[0][4 * hh + v] = 0;
-          bp[1][4 * hh + v] = 0;
-          bp[2][4 * hh + v] = 0;
-        }
-        continue;
-      }
+    for (int rb = 0; rb < NRB1; ++rb) {
       const uint32_t i1 = 16 * rb + li;
       u16x8 xp[Bits16<XT>::NP];
 #pragma unroll
@@ -885,26 +878,12 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
         acc1 = mma_2x3(xp[0], xp[1], b1, acc1);
       }
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        unsigned short x, y, z;
-        split3(acc1[v], x, y, z);
-        bp[0][4 * hh + v] = x;
-        bp[1][4 * hh + v] = y;
-        bp[2][4 * hh + v] = z;
-      }
-    }
+      for (int r2 = 0; r2 < NRB2; ++r2) {
+        const f4 a = a2t[(r2 * NRB1 + rb) * 64 + lane];
 #pragma unroll
-    for (int r2 = 0; r2 < NRB2; ++r2) {
-      const LDS u16x8* const ap = a2t + (r2 * NKC + kc) * 3 * 64 + lane;
-      const u16x8 a0 = ap[0], a1 = ap[64], a2 = ap[128];
-      f4 c = acc2[r2];
-      c = mma(a2, bp[0], c);
-      c = mma(a1, bp[1], c);
-      c = mma(a0, bp[2], c);
-      c = mma(a1, bp[0], c);
-      c = mma(a0, bp[1], c);
-      acc2[r2] = mma(a0, bp[0], c);
-    }
+        for (int v = 0; v < 4; ++v)
+          acc2[r2] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[v], acc1[v], acc2[r2], 0, 0, 0);
+      }
     }
     // round g of the workgroup (every wave is in the same round) uses stack g % 2
     LDS float* const st = stacks + cur * SF;
@@ -926,23 +905,19 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
     for (int h = 0; h < WPB3 / 4; ++h) {
       const uint32_t i0l = 4 * h + lg;               // row of the stack
       const uint32_t i0 = WPB3 * c + i0l;            // mode d-2 index
-      float bv[NTW], av[NTW];
+      const float av = jok ? m0s[j0 * I0 + i0] : 0.0f;
+      // columns RC .. 16 nct - 1 read into the next row or the trash slots; they only
+      // reach outputs that are not stored
+      const LDS float* const brow = st + i0l * RC + 16 * ct0 + li;
 #pragma unroll
       for (int m = 0; m < NTW; ++m) {
-        const uint32_t t = wv + WPB3 * m;
-        const uint32_t tt = t < ntile ? t : 0;
-        const uint32_t jb = tt / nct, ct = tt - jb * nct;
-        const uint32_t j0 = 16 * jb + li;
-        // columns >= RC read into the next row or the trash slots; they only reach
-        // outputs that are not stored
-        bv[m] = st[i0l * RC + 16 * ct + li];
-        av[m] = j0 < R0 ? m0s[j0 * I0 + i0] : 0.0f;
+        const bool ok = ct0 + (WPB3 / 2) * m < nct;
+        const float bv = ok ? brow[16 * (WPB3 / 2) * m] : 0.0f;
+        acc3[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc3[m], 0, 0, 0);
       }
-#pragma unroll
-      for (int m = 0; m < NTW; ++m)
-        acc3[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[m], bv[m], acc3[m], 0, 0, 0);
     }
     if (c == nch - 1) pend = blockIdx.x + r * G;
+    step(r, c);
   };
   for (uint32_t g = 0; g < cnt; g += 2) {
     slab(g, Slot<0>{});
@@ -973,9 +948,9 @@ Plan3s plan3s(const ModeProd2& mp) {
   const uint32_t slab_e = I1 * I2;
   if (slab_e % 8 != 0 || mp.A == 0 || mp.A % I0 != 0) return p;
   if ((uintptr_t)mp.X % 16) return p;
-  const uint32_t ntile = ((R0 + 15) / 16) * ((R1 * R2 + 15) / 16);
-  const uint32_t ntw = (ntile + WPB3 - 1) / WPB3;
-  p.ntw = ntw <= 2 ? 2 : ntw <= 3 ? 3 : ntw <= 5 ? 5 : ntw <= 8 ? 8 : 0;
+  // column blocks per wave (WPB3 / 2 waves per 16-row block of R0 <= 32)
+  const uint32_t ntw = ((R1 * R2 + 15) / 16 + WPB3 / 2 - 1) / (WPB3 / 2);
+  p.ntw = ntw <= 2 ? 2 : ntw <= 3 ? 3 : ntw <= 4 ? 4 : 0;
   if (!p.ntw) return p;
   k.U = mp.A / I0;
   k.I0 = I0; k.I1 = I1; k.I2 = I2; k.R0 = R0; k.R1 = R1; k.R2 = R2;
@@ -988,7 +963,7 @@ Plan3s plan3s(const ModeProd2& mp) {
   k.stack_fl = al16((WPB3 * R1 * R2 + 64) * 4) / 4;
   k.off_m0 = k.off_stack + 2 * k.stack_fl * 4;
   k.off_fac = k.off_m0 + al16(R0 * I0 * 4);
-  p.lds = k.off_fac + 3 * 64 * 16 + (size_t)p.nrb2 * ((p.nrb1 + 1) / 2) * 3 * 64 * 16;
+  p.lds = k.off_fac + 3 * 64 * 16 + (size_t)p.nrb2 * p.nrb1 * 64 * 16;
   p.ok = p.lds <= 160 * 1024;
   return p;
 }
@@ -997,8 +972,7 @@ template <typename XT, int NRB1, int NRB2>
 hipError_t proj3_ntw(const Plan3s& p, int num_cu, hipStream_t s) {
   auto fn = p.ntw == 2   ? k_proj3s<XT, NRB1, NRB2, 2>
             : p.ntw == 3 ? k_proj3s<XT, NRB1, NRB2, 3>
-            : p.ntw == 5 ? k_proj3s<XT, NRB1, NRB2, 5>
-                         : k_proj3s<XT, NRB1, NRB2, 8>;
+                         : k_proj3s<XT, NRB1, NRB2, 4>;
   if (p.lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)fn,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
