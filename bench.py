@@ -271,6 +271,22 @@ def main():
     lib.timing_enable(False, 0)
     refresh_ms = float(np.median(rt))
 
+    # the rate of a plain 1 GiB device copy on this machine (read + write bytes): what a pure
+    # streaming kernel reaches, beside the 8 TB/s peak
+    ncp = (1 << 30) // 4
+    ca = torch.empty(ncp, dtype=torch.float32, device=dev).fill_(1.0)
+    cb = torch.empty_like(ca)
+    cb.copy_(ca)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(5):
+        cb.copy_(ca)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * ncp * 4 * 5 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del ca, cb
+
     kb = kernel_bytes(wl, proj3="modeprod3_project_first" in rec)
     kernels = {}
     for name, (n, ms) in rec.items():
@@ -335,6 +351,7 @@ def main():
         "step_moved_bytes": int(moved_bytes),
         "step_moved_hbm_frac": round(moved_frac, 4),
         "roofline": roofline,
+        "hbm_copy_GBs": round(copy_gbs, 1),
         "kernels": kernels,
         "refresh_kernels": refresh_kernels,
         "multi_tensor": multi,
