@@ -110,6 +110,9 @@ FACTOR_CASES = [
     ("f16-slab3-ragged", custom((2, 32, 40, 17), "f16", (2, 9, 20, 9), 0.05)),
     ("bf16-slab3-k0", custom((2, 16, 16, 8), "bf16", (1, 8, 8, 4), 0.0)),
     ("bf16-slab3-300-units", custom((300, 16, 8, 8), "bf16", (300, 8, 4, 4), 0.05)),
+    # four output column blocks per wave (R1 R2 = 512); R0 = 32 over four rounds
+    ("bf16-slab3-wide-core", custom((2, 16, 40, 17), "bf16", (1, 8, 32, 16), 0.05)),
+    ("bf16-slab3-r0-32", custom((2, 64, 16, 8), "bf16", (1, 32, 8, 4), 0.05)),
     ("f16-64", custom((64, 20, 9), "f16", (32, 7, 4), 0.05)),
     ("c64-small", custom((12, 10, 9), "c64", (5, 4, 3), 0.05)),
     ("c64-64", custom((64, 6, 33), "c64", (32, 6, 16), 0.05)),
