@@ -287,6 +287,19 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
+// 1/x (normal x) and 1/sqrt(x) (positive normal x): v_rcp_f64 / v_rsq_f64 and two Newton
+// steps
+__device__ __forceinline__ double rcp64(double x) {
+  double y = __builtin_amdgcn_rcp(x);
+  y = fma(y, fma(-x, y, 1.0), y);
+  return fma(y, fma(-x, y, 1.0), y);
+}
+__device__ __forceinline__ double rsq64(double x) {
+  double y = __builtin_amdgcn_rsq(x);
+  y = fma(0.5 * y, fma(-x * y, y, 1.0), y);
+  return fma(0.5 * y, fma(-x * y, y, 1.0), y);
+}
+
 __global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
   extern __shared__ double sm[];
   const EK1& k = kk.m[blockIdx.x];
@@ -296,12 +309,9 @@ __global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
   const uint32_t nn = n * LD;
   double* A = sm;
   double* V = A + nn;
-  double* rc = V + nn;        // 32 rotations: cos, sin (sign of a_pq folded in)
-  double* rs = rc + 32;
-  double* red = rs + 32;      // 2 x 16 wave partials
-  int* rp = (int*)(red + 32);
-  int* rq = rp + 32;
-  int* order = rq + 32;       // 64
+  double2* cs = (double2*)(V + nn);   // 32 rotations: (cos, sin), the sign of a_pq folded in
+  double* red = (double*)(cs + 32);   // 2 x 16 wave partials
+  int* order = (int*)(red + 32);      // 64
 
   for (uint32_t idx0 = tid; idx0 < n * n; idx0 += NTS) {
     const uint32_t i = idx0 / n, j = idx0 - i * n;
@@ -312,6 +322,18 @@ __global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
 
   const uint32_t m = n + (n & 1u);   // even number of players; player n is a bye
   const uint32_t half = m / 2;
+  // this thread's share of every round (n <= 64, so half * half <= NTS and n * half <=
+  // 2 NTS): the 2 x 2 block (blk_a, blk_b) of A and rows vi[h] of V's column pair vb[h]
+  const int blk_a = tid < half * half ? (int)(tid / half) : -1;
+  const int blk_b = tid < half * half ? (int)(tid - (tid / half) * half) : -1;
+  int vb[2];
+  uint32_t vi[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t t = tid + (uint32_t)h * NTS;
+    vb[h] = t < n * half ? (int)(t / n) : -1;
+    vi[h] = t < n * half ? t - (t / n) * n : 0u;
+  }
   for (int sweep = 0; sweep < 40; ++sweep) {
     double off = 0.0, tot = 0.0;
     for (uint32_t idx0 = tid; idx0 < n * n; idx0 += NTS) {
@@ -336,44 +358,60 @@ __global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
     if (!(off > 1e-26 * tot)) break;
 
     for (uint32_t round = 0; round + 1 < m; ++round) {
-      if (tid < half) {
+      // pair j of this round: the players at positions j and m - 1 - j of the round-robin
+      // (position 0 fixed, the others rotated by `round`); q = -1 for a bye
+      auto pair = [&](uint32_t j, int& p, int& q) {
         auto player = [&](uint32_t pos) -> uint32_t {
-          return pos == 0 ? 0u : 1u + (pos - 1u + round) % (m - 1u);
+          if (pos == 0) return 0u;
+          uint32_t x = pos - 1u + round;   // < 2 (m - 1)
+          if (x >= m - 1u) x -= m - 1u;
+          return 1u + x;
         };
-        uint32_t p = player(tid), q = player(m - 1 - tid);
-        if (p > q) { uint32_t t = p; p = q; q = t; }
+        const uint32_t x = player(j), y = player(m - 1 - j);
+        const uint32_t lo = x < y ? x : y, hi = x < y ? y : x;
+        p = (int)lo;
+        q = hi < n ? (int)hi : -1;
+      };
+      if (tid < half) {
+        int p, q;
+        pair(tid, p, q);
         double c = 1.0, ss = 0.0;
-        if (q < n) {
+        if (q >= 0) {
           const double app = A[p * LD + p], aqq = A[q * LD + q];
           const double xr = A[p * LD + q];
           const double rr = fabs(xr);
           if (rr > 0.0) {
-            const double theta = (aqq - app) / (2.0 * rr);
+            // theta, t and c from the hardware reciprocal and reciprocal square root,
+            // each refined by two Newton steps: the angle is as good as a divided one,
+            // and c, s are orthogonal to fp64 rounding (both come from the same t)
+            const double d = 2.0 * rr;
+            const double theta = d >= 2.2250738585072014e-308 ? (aqq - app) * rcp64(d)
+                                                             : (aqq - app) / d;
             double t;
             if (fabs(theta) > 1e100) {
-              t = 0.5 / theta;
+              t = 0.5 * rcp64(theta);
             } else {
-              t = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+              const double u = theta * theta + 1.0;
+              t = (theta >= 0.0 ? 1.0 : -1.0) * rcp64(fabs(theta) + u * rsq64(u));
             }
-            c = 1.0 / sqrt(t * t + 1.0);
+            c = rsq64(t * t + 1.0);
             ss = (t * c) * (xr >= 0.0 ? 1.0 : -1.0);
           }
         }
-        rc[tid] = c;
-        rs[tid] = ss;
-        rp[tid] = (int)p;
-        rq[tid] = (q < n) ? (int)q : -1;
+        cs[tid] = make_double2(c, ss);
       }
       __syncthreads();
       // A: block (pair a rows) x (pair b columns); a bye or an unrotated pair acts as
       // the identity on its index
-      for (uint32_t t = tid; t < half * half; t += NTS) {
-        const uint32_t a = t / half, b = t - a * half;
-        const int qa = rq[a], qb = rq[b];
-        const bool ra = qa >= 0 && rs[a] != 0.0, rb = qb >= 0 && rs[b] != 0.0;
-        if (!ra && !rb) continue;
-        const int pa = rp[a], pb = rp[b];
-        const double ca = rc[a], sa = rs[a], cb = rc[b], sb = rs[b];
+      if (blk_a >= 0) {
+        const uint32_t a = (uint32_t)blk_a, b = (uint32_t)blk_b;
+        int pa, qa, pb, qb;
+        pair(a, pa, qa);
+        pair(b, pb, qb);
+        const double2 csa = cs[a], csb = cs[b];
+        const double ca = csa.x, sa = csa.y, cb = csb.x, sb = csb.y;
+        const bool ra = qa >= 0 && sa != 0.0, rb = qb >= 0 && sb != 0.0;
+        if (ra || rb) {
         double x00 = A[pa * LD + pb];
         double x01 = qb >= 0 ? A[pa * LD + qb] : 0.0;
         double x10 = qa >= 0 ? A[qa * LD + pb] : 0.0;
@@ -392,14 +430,18 @@ __global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
         if (qb >= 0) A[pa * LD + qb] = x01;
         if (qa >= 0) A[qa * LD + pb] = x10;
         if (qa >= 0 && qb >= 0) A[qa * LD + qb] = x11;
+        }
       }
       // V <- V J (columns)
-      for (uint32_t t = tid; t < n * half; t += NTS) {
-        const uint32_t b = t / n, i = t - b * n;
-        const int qb = rq[b];
-        if (qb < 0 || rs[b] == 0.0) continue;
-        const int pb = rp[b];
-        const double cb = rc[b], sb = rs[b];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (vb[h] < 0) continue;
+        const uint32_t b = (uint32_t)vb[h], i = vi[h];
+        int pb, qb;
+        pair(b, pb, qb);
+        const double2 csb = cs[b];
+        const double cb = csb.x, sb = csb.y;
+        if (qb < 0 || sb == 0.0) continue;
         const double vx = V[i * LD + pb], vy = V[i * LD + qb];
         V[i * LD + pb] = cb * vx - sb * vy;
         V[i * LD + qb] = sb * vx + cb * vy;
