@@ -9,7 +9,8 @@
 // matrix, then all column updates (A <- A J, V <- V J) and all row updates
 // (A <- J^H A) are applied. Hermitian rotations first turn a_pq real with a phase on
 // column q, then apply the real rotation. Sweeps stop when the off-diagonal energy is
-// below 1e-26 of the total, or after 40 sweeps.
+// below 1e-20 of the total (an off-diagonal norm of 1e-10 of the matrix norm, so an
+// eigenvector errs by about 1e-10 over its relative eigengap), or after 40 sweeps.
 //
 // Outputs (pages silent on eigenvector order, sign and phase): eigenvalues descending
 // (equal values keep index order); each selected column scaled by a unit scalar so its
@@ -106,7 +107,7 @@ __global__ void __launch_bounds__(NTH) k_eig(EK kk) {
     }
     off = block_sum(off, red);
     tot = block_sum(tot, red);
-    if (!(off > 1e-26 * tot)) break;
+    if (!(off > 1e-20 * tot)) break;
 
     for (uint32_t round = 0; round + 1 < m; ++round) {
       if ((uint32_t)tid < half) {
@@ -355,7 +356,7 @@ __global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
       off += red[w];
       tot += red[16 + w];
     }
-    if (!(off > 1e-26 * tot)) break;
+    if (!(off > 1e-20 * tot)) break;
 
     for (uint32_t round = 0; round + 1 < m; ++round) {
       // pair j of this round: the players at positions j and m - 1 - j of the round-robin
