@@ -109,6 +109,8 @@ RUNS = [
     ("config1", CONFIGS[1], 12),
     ("bf16-odd", custom((33, 17, 60), "bf16", (13, 8, 31), 0.05, T=4, steps=9), 9),
     ("c64-small", custom((12, 10, 9), "c64", (5, 4, 3), 0.05, T=3, steps=7), 7),
+    # the three trailing modes in the first projection launch
+    ("bf16-slab3", custom((2, 16, 48, 25), "bf16", (1, 8, 24, 13), 0.05, T=3, steps=7), 7),
 ]
 
 
@@ -301,6 +303,7 @@ LRF_CASES = [
     ("config1", CONFIGS[1]),
     ("c64-small", custom((12, 10, 9), "c64", (5, 4, 3), 0.05, T=3)),
     ("f16-5mode", custom((9, 7, 5, 11, 4), "f16", (4, 3, 5, 2, 3), 0.05, T=3)),
+    ("bf16-slab3", custom((2, 16, 48, 25), "bf16", (1, 8, 24, 13), 0.05, T=3)),
 ]
 
 
