@@ -192,10 +192,23 @@ def cpu_baseline(wl, seed=0):
     orc.step(W, g)
     dt = time.perf_counter() - t0
     threads = len(os.sched_getaffinity(0))
+    cpu_model, blas = None, None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"].get("name")
+    except Exception:
+        pass
     return {"value": wl.numel / dt, "unit": "grad elems/s", "cores": threads, "kind": "oracle",
             "sample": f"1 non-refresh step of the full workload ({wl.numel} elements), "
                       f"{dt:.1f} s; numpy BLAS threads = available cores; refresh excluded",
-            "seconds": dt}
+            "seconds": dt, "cpu_model": cpu_model, "blas": blas}
 
 
 def main():
