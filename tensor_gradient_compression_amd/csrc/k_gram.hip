@@ -293,13 +293,16 @@ __host__ __device__ constexpr int blk_cb(int NB, int q) {
   return rb + q;
 }
 
-// Work split of the four waves: with at most 3 blocks (NB <= 2) every wave forms all
-// blocks over every fourth k-step; otherwise wave W forms blocks W, W + 4, ... (at most
-// 3) over every k-step. Either way a wave holds at most 3 fp32 and 3 fp64 block sums.
-template <int NB>
+// Work split of the four waves. KS: every wave forms all blocks over every fourth
+// k-step (used for NB <= 2, and for NB = 3 on slab tiles, whose fragments are read 16
+// bits at a time: the four waves then read each fragment once instead of each reading
+// the rows of its own blocks; measured 270 -> 119 us for (48 x 25) slabs). Otherwise
+// wave W forms blocks W, W + 4, ... (at most 3) over every k-step, which needs fewer
+// registers (three workgroups per CU on the wide tiles).
+template <int NB, bool KS>
 struct G16Split {
   static constexpr int NBLK = NB * (NB + 1) / 2;
-  static constexpr bool KSPLIT = NB <= 2;
+  static constexpr bool KSPLIT = KS;
   static constexpr int MAXB = KSPLIT ? NBLK : (NBLK + 3) / 4;
   __host__ __device__ static constexpr int count(int W) {
     return KSPLIT ? NBLK : (NBLK > W ? (NBLK - W + 3) / 4 : 0);
@@ -307,9 +310,9 @@ struct G16Split {
   __host__ __device__ static constexpr int q(int W, int m) { return KSPLIT ? m : W + 4 * m; }
 };
 
-template <int NB>
+template <int NB, bool KS>
 __host__ __device__ constexpr bool row_used(int W, int rb) {
-  using S = G16Split<NB>;
+  using S = G16Split<NB, KS>;
   for (int m = 0; m < S::count(W); ++m)
     if (blk_rb(NB, S::q(W, m)) == rb || blk_cb(NB, S::q(W, m)) == rb) return true;
   return false;
@@ -317,34 +320,34 @@ __host__ __device__ constexpr bool row_used(int W, int rb) {
 
 // One k-step of wave W: read the fragments its blocks use, then one MFMA per block.
 // Template recursion keeps every block and fragment index a compile-time constant.
-template <int NB, int W, int RB, class LD>
+template <int NB, bool KS, int W, int RB, class LD>
 __device__ __forceinline__ void g16_load(u16x8* fr, LD& ld) {
   if constexpr (RB < NB) {
-    if constexpr (row_used<NB>(W, RB)) fr[RB] = ld(RB);
-    g16_load<NB, W, RB + 1>(fr, ld);
+    if constexpr (row_used<NB, KS>(W, RB)) fr[RB] = ld(RB);
+    g16_load<NB, KS, W, RB + 1>(fr, ld);
   }
 }
-template <bool BF, int NB, int W, int M>
+template <bool BF, int NB, bool KS, int W, int M>
 __device__ __forceinline__ void g16_mfma(f4* acc, const u16x8* fr) {
-  if constexpr (M < G16Split<NB>::count(W)) {
-    constexpr int qq = G16Split<NB>::q(W, M);
+  if constexpr (M < G16Split<NB, KS>::count(W)) {
+    constexpr int qq = G16Split<NB, KS>::q(W, M);
     constexpr int rb = blk_rb(NB, qq), cb = blk_cb(NB, qq);
     acc[M] = mfma32<BF>(fr[rb], fr[cb], acc[M]);
-    g16_mfma<BF, NB, W, M + 1>(acc, fr);
+    g16_mfma<BF, NB, KS, W, M + 1>(acc, fr);
   }
 }
-template <bool BF, int NB, int W, class LD>
+template <bool BF, int NB, bool KS, int W, class LD>
 __device__ __forceinline__ void g16_step(f4* acc, LD&& ld) {
   u16x8 fr[NB];
-  g16_load<NB, W, 0>(fr, ld);
-  g16_mfma<BF, NB, W, 0>(acc, fr);
+  g16_load<NB, KS, W, 0>(fr, ld);
+  g16_mfma<BF, NB, KS, W, 0>(acc, fr);
 }
 
-template <bool BF, int NB>
+template <bool BF, int NB, bool KS>
 __global__ void __launch_bounds__(G16_NTH) k_gram16(G16K k) {
   extern __shared__ uint4 smem16[];
   unsigned char* lds = (unsigned char*)smem16;
-  using S = G16Split<NB>;
+  using S = G16Split<NB, KS>;
   constexpr int NBLK = S::NBLK, MAXB = S::MAXB;
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -370,13 +373,13 @@ __global__ void __launch_bounds__(G16_NTH) k_gram16(G16K k) {
   };
   auto step = [&](auto&& ld) {
     if (S::KSPLIT) {
-      g16_step<BF, NB, 0>(acc, ld);
+      g16_step<BF, NB, KS, 0>(acc, ld);
     } else {
       switch (wave) {
-        case 0: g16_step<BF, NB, 0>(acc, ld); break;
-        case 1: g16_step<BF, NB, 1>(acc, ld); break;
-        case 2: g16_step<BF, NB, 2>(acc, ld); break;
-        default: g16_step<BF, NB, 3>(acc, ld); break;
+        case 0: g16_step<BF, NB, KS, 0>(acc, ld); break;
+        case 1: g16_step<BF, NB, KS, 1>(acc, ld); break;
+        case 2: g16_step<BF, NB, KS, 2>(acc, ld); break;
+        default: g16_step<BF, NB, KS, 3>(acc, ld); break;
       }
     }
   };
@@ -534,10 +537,13 @@ struct G16Geo {
   uint32_t grid;
 };
 
-// Workgroups of k_gram16<BF, NB> a CU holds with `lds` bytes of LDS each (0 on error).
-template <bool BF, int NB>
+// The work split for NB row blocks on wide or slab tiles.
+constexpr bool g16_ks(int NB, bool wide) { return NB <= 2 || (!wide && NB <= 3); }
+
+// Workgroups of k_gram16<BF, NB, KS> a CU holds with `lds` bytes of LDS each (0 on error).
+template <bool BF, int NB, bool KS>
 int g16_occ(size_t lds) {
-  auto fn = k_gram16<BF, NB>;
+  auto fn = k_gram16<BF, NB, KS>;
   if (lds > 64 * 1024 &&
       hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)lds) != hipSuccess)
@@ -548,12 +554,13 @@ int g16_occ(size_t lds) {
   return per_cu;
 }
 template <bool BF>
-int g16_occ_nb(uint32_t I, size_t lds) {
+int g16_occ_nb(uint32_t I, bool wide, size_t lds) {
   switch ((I + 15) / 16) {
-    case 1: return g16_occ<BF, 1>(lds);
-    case 2: return g16_occ<BF, 2>(lds);
-    case 3: return g16_occ<BF, 3>(lds);
-    case 4: return g16_occ<BF, 4>(lds);
+    case 1: return g16_occ<BF, 1, g16_ks(1, false)>(lds);
+    case 2: return g16_occ<BF, 2, g16_ks(2, false)>(lds);
+    case 3: return wide ? g16_occ<BF, 3, g16_ks(3, true)>(lds)
+                        : g16_occ<BF, 3, g16_ks(3, false)>(lds);
+    case 4: return g16_occ<BF, 4, g16_ks(4, false)>(lds);
   }
   return 0;
 }
@@ -599,8 +606,8 @@ G16Geo g16geo(const GramArgs& g, int num_cu) {
   // a persistent grid of one resident round (a second, partial round would run alone at
   // the end): as many workgroups as a CU holds with this kernel's registers and LDS, at
   // most G16_WGS_PER_CU (each workgroup writes an I x I fp64 partial)
-  const int occ = g.dt == DT_BF16 ? g16_occ_nb<true>(g.I, r.lds)
-                                  : g16_occ_nb<false>(g.I, r.lds);
+  const int occ = g.dt == DT_BF16 ? g16_occ_nb<true>(g.I, k.wide != 0, r.lds)
+                                  : g16_occ_nb<false>(g.I, k.wide != 0, r.lds);
   if (occ < 1) return r;
   const int per_cu = occ < G16_WGS_PER_CU ? occ : G16_WGS_PER_CU;
   uint64_t grid = (uint64_t)(num_cu > 0 ? num_cu : 256) * (uint64_t)per_cu;
@@ -611,10 +618,10 @@ G16Geo g16geo(const GramArgs& g, int num_cu) {
   return r;
 }
 
-template <bool BF, int NB>
+template <bool BF, int NB, bool KS>
 hipError_t go16(const G16Geo& g, hipStream_t s) {
   // g16geo has raised the kernel's LDS limit where it needs more than 64 KiB
-  auto fn = k_gram16<BF, NB>;
+  auto fn = k_gram16<BF, NB, KS>;
   hipLaunchKernelGGL(fn, dim3(g.grid), dim3(G16_NTH), g.lds, s, g.k);
   return hipGetLastError();
 }
@@ -622,10 +629,11 @@ hipError_t go16(const G16Geo& g, hipStream_t s) {
 template <bool BF>
 hipError_t pick16(const G16Geo& g, hipStream_t s) {
   switch ((g.k.I + 15) / 16) {
-    case 1: return go16<BF, 1>(g, s);
-    case 2: return go16<BF, 2>(g, s);
-    case 3: return go16<BF, 3>(g, s);
-    case 4: return go16<BF, 4>(g, s);
+    case 1: return go16<BF, 1, g16_ks(1, false)>(g, s);
+    case 2: return go16<BF, 2, g16_ks(2, false)>(g, s);
+    case 3: return g.k.wide ? go16<BF, 3, g16_ks(3, true)>(g, s)
+                            : go16<BF, 3, g16_ks(3, false)>(g, s);
+    case 4: return go16<BF, 4, g16_ks(4, false)>(g, s);
   }
   return hipErrorInvalidValue;
 }
