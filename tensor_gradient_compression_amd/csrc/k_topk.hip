@@ -491,7 +491,7 @@ hipError_t run_topk(const void* G, uint64_t N, uint32_t k, const TopkWs& ws, uin
   M(KID_TOPK_INIT, false);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   uint64_t hb = (N + 256ull * 16 - 1) / (256ull * 16);
-  if (hb > 4096) hb = 4096;
+  if (hb > 1024) hb = 1024;
   if (hb < 1) hb = 1;
   for (int pass = 0;; ++pass) {
     constexpr int BITS = RK ? 31 : K::BITS;
