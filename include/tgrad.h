@@ -181,6 +181,18 @@ int tgrad_mark_refreshed(tgrad_t *h);
  * fp32 rounding; takes effect at the next step. */
 int tgrad_set_fusion(tgrad_t *h, int enable);
 
+/* Test / benchmark hook: in a bf16/fp16 tensor whose last three modes are all
+ * compressed, a refresh forms their three Grams in one launch that reads the residual
+ * once (pith.science "What carries the argument": every factor comes from the Gram of
+ * its mode's unfolding, and each Gram is a sum over slabs of the last three modes, so
+ * one staged slab serves all three). It applies when the two modes before the last are
+ * at most 64, the last at most 32, and one slab of the three modes is a multiple of 8
+ * elements and at most 128 KiB; the input must be 16-byte aligned (otherwise one launch
+ * per mode is used). enable = 1 selects it (the default; TGRAD_EINVAL where it does not
+ * apply), 0 one Gram launch per mode. Results agree to fp32 rounding of the partial
+ * sums; takes effect at the next refresh. */
+int tgrad_set_gram_fusion(tgrad_t *h, int enable);
+
 /* ---------------------------------------------------------------- variants.
  * Choices the method leaves open, as options of a handle (defaults: the plain method,
  * bit for bit):

@@ -74,6 +74,7 @@ SIGNATURES = [
     ("tgrad_set_factor", ctypes.c_int, [_P, ctypes.c_int, _P, _I64]),
     ("tgrad_mark_refreshed", ctypes.c_int, [_P]),
     ("tgrad_set_fusion", ctypes.c_int, [_P, ctypes.c_int]),
+    ("tgrad_set_gram_fusion", ctypes.c_int, [_P, ctypes.c_int]),
     ("tgrad_default_options", None, [ctypes.POINTER(Options)]),
     ("tgrad_set_options", ctypes.c_int, [_P, ctypes.POINTER(Options)]),
     ("tgrad_get_options", ctypes.c_int, [_P, ctypes.POINTER(Options)]),
@@ -274,6 +275,16 @@ class TGrad:
         if rc == EINVAL and enable:
             return False
         self._check(rc, "tgrad_set_fusion")
+        return True
+
+    def set_gram_fusion(self, enable) -> bool:
+        """Select the one-read Gram launch of the last three modes at a refresh (True)
+        or one Gram launch per mode (False); returns False when the one-read launch does
+        not apply to this shape and dtype."""
+        rc = self._lib.tgrad_set_gram_fusion(self._h, int(bool(enable)))
+        if rc == EINVAL and enable:
+            return False
+        self._check(rc, "tgrad_set_gram_fusion")
         return True
 
     def save_state(self) -> bytes:

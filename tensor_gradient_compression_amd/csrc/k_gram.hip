@@ -641,8 +641,8 @@ hipError_t pick16(const G16Geo& g, hipStream_t s) {
 }  // namespace
 
 // Sum nblk partials of n2 values (stored after them: RGROUPS stage rows) into out.
-static hipError_t reduce_partials(double* partial, uint32_t nblk, uint32_t n2, double* out,
-                           hipStream_t s, void (*mark)(void*, int, bool), void* mctx) {
+hipError_t gram_reduce(double* partial, uint32_t nblk, uint32_t n2, double* out, hipStream_t s,
+                       void (*mark)(void*, int, bool), void* mctx) {
   double* stage = partial + (uint64_t)nblk * n2;
   if (mark) mark(mctx, KID_GRAM_REDUCE, true);
   k_gram_reduce1<<<dim3((n2 + 255) / 256, RGROUPS), 256, 0, s>>>(partial, nblk, n2, stage);
@@ -680,7 +680,7 @@ hipError_t launch_gram(const GramArgs& g, int num_cu, hipStream_t s,
     const hipError_t e = g.dt == DT_BF16 ? pick16<true>(ff, s) : pick16<false>(ff, s);
     if (mark) mark(mctx, KID_GRAM, false);
     if (e != hipSuccess) return e;
-    return reduce_partials(g.partial, nblk, r.Kin * r.Kin, g.out, s, mark, mctx);
+    return gram_reduce(g.partial, nblk, r.Kin * r.Kin, g.out, s, mark, mctx);
   }
   GK k;
   k.X = g.X;
@@ -710,7 +710,7 @@ hipError_t launch_gram(const GramArgs& g, int num_cu, hipStream_t s,
   }
   if (mark) mark(mctx, KID_GRAM, false);
   if (e != hipSuccess) return e;
-  return reduce_partials(g.partial, nblk, r.Kin * r.Kin, g.out, s, mark, mctx);
+  return gram_reduce(g.partial, nblk, r.Kin * r.Kin, g.out, s, mark, mctx);
 }
 
 }  // namespace tg

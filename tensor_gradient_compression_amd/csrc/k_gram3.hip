@@ -1,0 +1,591 @@
+// Gram matrices of the last three modes from a single read of the residual.
+//
+// The HOSVD factors are the leading eigenvectors of the mode-n Grams of the residual
+// (pith.science "What carries the argument": Tucker (higher-order SVD) factors;
+// nullthought summary section 3: the low-rank part is fitted to what the sparse part
+// leaves). View the 16-bit tensor as A slabs S = X[s] of its last three modes
+// (a, b, c) = (d-3, d-2, d-1), each slab Ia x Ib x Ic and contiguous. Every one of the
+// three Grams is a sum over slabs of a product that needs that slab alone:
+//   Gram_a[z, z'] = sum_s sum_{y,x} S[z,y,x] S[z',y,x]   rows z (Ib Ic contiguous values)
+//   Gram_b[y, y'] = sum_s sum_{z,x} S[z,y,x] S[z,y',x]   one Ib x Ic piece per z
+//   Gram_c[x, x'] = sum_s sum_{z,y} S[z,y,x] S[z,y,x']   rows (z, y) of Ic values
+// so a workgroup that holds a whole slab in LDS forms its share of all three, and the
+// residual crosses HBM once for the three modes instead of once per mode. (The leading
+// modes cannot join: a tile that serves the Grams of two modes must hold full fibres of
+// both, and for two leading modes of this size that is most of the tensor.)
+//
+// Organisation. One workgroup per CU takes slabs blockIdx.x, + grid, ... It has 12 waves,
+// or 8 where the first mode's fragments need 16-bit reads (more registers), so that
+// neither form spills. The slab sits in LDS in its natural layout, followed by zeros.
+// The next slab is loaded into registers while the waves work on the current one, then
+// written to LDS after a barrier. The loads go through a buffer resource in 16-byte
+// pieces, and pieces past the slab read as zero. Each wave has one role: a mode, a
+// group of that mode's 16 x 16 output blocks of the upper triangle (all of them for a
+// mode of at most 48), and a residue class of the k-steps (a k-split). The host plans
+// the split so that the three modes finish together. A role reads the fragments of its
+// next k-step before the MFMAs of the current one. Operands come straight from the slab:
+//   mode a: row z, k = the next 32 values of the row (16-byte reads when Ib Ic % 8 == 0);
+//   mode b: row y of piece z, k = x (one k-step per piece, Ic <= 32, zero-padded): five
+//           aligned dwords and a funnel shift per 16-byte run, or one 16-byte read when
+//           Ic % 8 == 0;
+//   mode c: row x, k = 32 slab rows (z, y), one 16-bit value each.
+// Arithmetic as in the single-mode 16-bit Gram: bf16/fp16 products are exact in fp32
+// (v_mfma_f32_16x16x32_bf16 / _f16), each wave adds at most 8 k-steps (256 products) in
+// fp32 before adding into fp64, and the waves' fp64 sums are combined in a fixed order,
+// so the result is deterministic run to run. Workgroup partials are summed by the same
+// two-stage reduction as the single-mode Grams.
+#include <algorithm>
+#include <type_traits>
+
+#include "tg_common.h"
+
+namespace tg {
+
+namespace {
+
+// Threads of a workgroup: 12 waves where the first mode's fragments are 16-byte reads,
+// 8 where they are 16-bit reads (which need more registers), so that neither spills.
+__host__ __device__ constexpr int g3_nt(bool av) { return av ? 768 : 512; }
+constexpr uint32_t G3_MAX_SLAB = 65536;      // elements (128 KiB)
+// 16-byte slab pieces a thread stages
+__host__ __device__ constexpr int g3_cpt(int nt) { return (int)((G3_MAX_SLAB / 8 + nt - 1) / nt); }
+constexpr uint32_t G3_FLUSH = 8;             // k-steps per fp32 partial sum
+constexpr size_t G3_LDS_MAX = 160 * 1024;
+// Fourth word of a raw buffer resource on gfx9-family targets (no format conversion,
+// byte-granular range check: loads past num_records return zero).
+constexpr int G3_RSRC_W3 = 0x00020000;
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#define LDS __attribute__((address_space(3)))
+
+struct G3K {
+  const u32x4* X;          // the tensor as 16-byte pieces
+  double* part[3];         // per mode: gridDim.x partials of I_m^2 fp64 values
+  uint32_t A, Ia, Ib, Ic;
+  uint32_t slab_q;         // 16-byte pieces per slab
+  uint32_t IBC, RAB;       // Ib Ic, Ia Ib
+  uint32_t a_vec, b_vec;   // mode a (b) fragments are aligned 16-byte runs
+  uint32_t nb[3];          // 16-row blocks of each mode
+  uint32_t ns[3];          // k-splits of each mode
+  uint32_t w0[3];          // first wave of each mode
+  uint32_t steps[3];       // k-steps per slab
+  uint32_t red[3];         // each mode's LDS reduction area (doubles)
+};
+
+template <bool BF>
+__device__ __forceinline__ f4 mfma32(const u16x8& a, const u16x8& b, const f4& c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Upper-triangle block q (row-major: (0,0), (0,1), ..., (1,1), ...) of an NB x NB grid.
+__host__ __device__ constexpr int tri_rb(int NB, int q) {
+  int rb = 0;
+  while (q >= NB - rb) {
+    q -= NB - rb;
+    ++rb;
+  }
+  return rb;
+}
+__host__ __device__ constexpr int tri_cb(int NB, int q) {
+  int rb = 0;
+  while (q >= NB - rb) {
+    q -= NB - rb;
+    ++rb;
+  }
+  return rb + q;
+}
+
+// Block groups, consecutive in that order, of at most 6 blocks:
+//   NB 1: {0}; NB 2: {0..2}; NB 3: {0..5}; NB 4: {0..4} {5..9}.
+// A group's blocks share fragment reads within a k-step.
+constexpr int G3_MAXQ = 6;
+__host__ __device__ constexpr int g3_groups(int NB) { return NB <= 3 ? 1 : 2; }
+__host__ __device__ constexpr int g3_q0(int NB, int g) { return NB <= 3 ? 0 : 5 * g; }
+__host__ __device__ constexpr int g3_q1(int NB, int g) {
+  return NB == 1 ? 1 : NB == 2 ? 3 : NB == 3 ? 6 : 5 * g + 5;
+}
+__host__ __device__ constexpr bool g3_used(int NB, int g, int f) {
+  for (int q = g3_q0(NB, g); q < g3_q1(NB, g); ++q)
+    if (tri_rb(NB, q) == f || tri_cb(NB, q) == f) return true;
+  return false;
+}
+// Fragments one k-step of group g reads.
+__host__ constexpr int g3_nfrags(int NB, int g) {
+  int n = 0;
+  for (int f = 0; f < NB; ++f) n += g3_used(NB, g, f) ? 1 : 0;
+  return n;
+}
+
+template <int B, int E, class F>
+__device__ __forceinline__ void sfor(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    sfor<B + 1, E>(f);
+  }
+}
+
+struct Acc {
+  f4 s[G3_MAXQ];          // fp32 sums of the current k-steps
+  double d[G3_MAXQ][4];   // fp64 totals
+  uint32_t since;
+};
+
+template <int NQ>
+__device__ __forceinline__ void flush(Acc& a) {
+#pragma unroll
+  for (int m = 0; m < NQ; ++m) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) a.d[m][v] += (double)a.s[m][v];
+    a.s[m] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Per-lane addressing of one wave's role, formed once per slab (byte offsets into LDS).
+template <int MODE, int NB>
+struct G3Lane {
+  uint32_t a[MODE == 2 ? 8 : NB];   // a, b: each fragment's row; c: the lane's 8 rows
+  u32x4 keep;                       // b: the lane's k = x < Ic, as a mask on the packed values
+};
+
+// mode b: zero the packed values of x >= Ic (they would come from the next row)
+template <int MODE, int NB>
+__device__ __forceinline__ G3Lane<MODE, NB> g3_lane(const G3K& k, uint32_t li, uint32_t kg) {
+  G3Lane<MODE, NB> L;
+  if constexpr (MODE == 0) {
+#pragma unroll
+    for (int f = 0; f < NB; ++f) L.a[f] = min(16u * f + li, k.Ia - 1) * k.IBC * 2;
+  } else if constexpr (MODE == 1) {
+#pragma unroll
+    for (int f = 0; f < NB; ++f) L.a[f] = (min(16u * f + li, k.Ib - 1) * k.Ic + 8 * kg) * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t x = 8 * kg + 2 * i;
+      L.keep[i] = (x < k.Ic ? 0x0000FFFFu : 0u) | (x + 1 < k.Ic ? 0xFFFF0000u : 0u);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) L.a[j] = ((16 * kg + j) * k.Ic + li) * 2;
+  }
+  return L;
+}
+
+// Two 16-bit values (each zero-extended in a register) packed into one dword, low first.
+__device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) {
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// The fragments of k-step st that block group G reads, as 4 dwords (8 packed 16-bit
+// values) a lane. VEC: the 8 values of a lane are an aligned 16-byte run (mode a:
+// Ib Ic % 8 == 0; mode b: Ic % 8 == 0).
+//   mode a: row z = 16 f + li, k = 32 st + 8 kg + j of the row (k >= Ib Ic read as zero);
+//   mode b: piece z = st, row y = 16 f + li, k = x = 8 kg + j (x >= Ic masked to zero);
+//   mode c: row x = 16 f + li, k = slab row r = 64 (st / 2) + 8 (st % 2) + 16 kg + j
+//           (each row once; the lane groups' rows lie 16 apart, so their 32-byte spans
+//           fall in different LDS banks). No guard: rows past the slab read the zeros
+//           staged after it, and x >= Ic only reaches Gram entries that are not stored.
+// Masks apply to whole dwords, so no value is handled 16 bits at a time.
+template <int MODE, int NB, int G, bool VEC>
+__device__ __forceinline__ void g3_frags(const G3K& k, const LDS unsigned char* lds,
+                                         const G3Lane<MODE, NB>& L, uint32_t kg, uint32_t st,
+                                         u32x4* fr) {
+  if constexpr (MODE == 0) {
+    const uint32_t k0 = 32 * st + 8 * kg;
+    sfor<0, NB>([&](auto F) {
+      constexpr int f = decltype(F)::value;
+      if constexpr (g3_used(NB, G, f)) {
+        if constexpr (VEC) {
+          const bool ok = k0 < k.IBC;
+          const u32x4 v = *(const LDS u32x4*)(lds + L.a[f] + (ok ? k0 : 0) * 2);
+          fr[f] = v & (ok ? ~0u : 0u);
+        } else {
+          const LDS unsigned short* const row = (const LDS unsigned short*)(lds + L.a[f]);
+          uint32_t e[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const bool ok = k0 + j < k.IBC;
+            e[j] = ok ? (uint32_t)row[ok ? k0 + j : 0] : 0u;
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) fr[f][i] = pack2(e[2 * i], e[2 * i + 1]);
+        }
+      }
+    });
+  } else if constexpr (MODE == 1) {
+    const uint32_t off = st * k.IBC * 2;
+    sfor<0, NB>([&](auto F) {
+      constexpr int f = decltype(F)::value;
+      if constexpr (g3_used(NB, G, f)) {
+        if constexpr (VEC) {
+          const bool ok = 8 * kg < k.Ic;
+          const u32x4 v = *(const LDS u32x4*)(lds + (ok ? L.a[f] + off : 0));
+          fr[f] = v & (ok ? ~0u : 0u);
+        } else {
+          // the 16-byte run starts on a 2-byte boundary: five aligned dwords around it,
+          // then a funnel shift by 0 or 16 bits (the fifth may read the zeros after
+          // the slab)
+          const uint32_t a = L.a[f] + off;
+          const LDS uint32_t* const p = (const LDS uint32_t*)(lds + (a & ~3u));
+          const uint32_t sh = (a & 2u) * 8;
+          uint32_t d[5];
+#pragma unroll
+          for (int i = 0; i < 5; ++i) d[i] = p[i];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            fr[f][i] = __builtin_amdgcn_alignbit(d[i + 1], d[i], sh) & L.keep[i];
+        }
+      }
+    });
+  } else {
+    const LDS unsigned char* const b = lds + ((st >> 1) * 64 + (st & 1) * 8) * k.Ic * 2;
+    uint32_t e[NB][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const LDS unsigned short* const p = (const LDS unsigned short*)(b + L.a[j]);
+#pragma unroll
+      for (int f = 0; f < NB; ++f) e[f][j] = p[16 * f];
+    }
+#pragma unroll
+    for (int f = 0; f < NB; ++f)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fr[f][i] = pack2(e[f][2 * i], e[f][2 * i + 1]);
+  }
+}
+
+// The k-steps st0, st0 + dst, ... of one block group on the slab in LDS, software
+// pipelined: the reads of the next step are issued before the MFMAs of this one (two
+// fragment sets used in turn; the last pass re-reads the final step and drops it).
+template <bool BF, int MODE, int NB, int G, bool VEC>
+__device__ __forceinline__ void g3_steps(const G3K& k, const LDS unsigned char* lds,
+                                         uint32_t st0, uint32_t dst, uint32_t li,
+                                         uint32_t kg, Acc& acc) {
+  constexpr int Q0 = g3_q0(NB, G), Q1 = g3_q1(NB, G);
+  const uint32_t nst = k.steps[MODE];
+  if (st0 >= nst) return;
+  // The lane index passes through an empty asm statement so that the addresses derived
+  // from it are formed here, once per slab, rather than hoisted out of the slab loop
+  // where they would hold registers throughout.
+  __asm__ volatile("" : "+v"(li), "+v"(kg));
+  const G3Lane<MODE, NB> L = g3_lane<MODE, NB>(k, li, kg);
+  auto mfmas = [&](const u32x4* fr) {
+    sfor<Q0, Q1>([&](auto Q) {
+      constexpr int q = decltype(Q)::value;
+      constexpr int rb = tri_rb(NB, q), cb = tri_cb(NB, q);
+      acc.s[q - Q0] = mfma32<BF>(__builtin_bit_cast(u16x8, fr[rb]),
+                                 __builtin_bit_cast(u16x8, fr[cb]), acc.s[q - Q0]);
+    });
+    if (++acc.since == G3_FLUSH) {
+      flush<Q1 - Q0>(acc);
+      acc.since = 0;
+    }
+  };
+  u32x4 fa[NB], fb[NB];
+  g3_frags<MODE, NB, G, VEC>(k, lds, L, kg, st0, fa);
+  for (uint32_t st = st0;;) {
+    const uint32_t s1 = st + dst;
+    g3_frags<MODE, NB, G, VEC>(k, lds, L, kg, s1 < nst ? s1 : nst - 1, fb);
+    mfmas(fa);
+    if (s1 >= nst) break;
+    const uint32_t s2 = s1 + dst;
+    g3_frags<MODE, NB, G, VEC>(k, lds, L, kg, s2 < nst ? s2 : nst - 1, fa);
+    mfmas(fb);
+    if (s2 >= nst) break;
+    st = s2;
+  }
+}
+
+// This wave's fp64 block totals into the mode's LDS reduction area:
+// red[((q * ns + split) * 4 + v) * 64 + lane].
+template <int NB, int G>
+__device__ __forceinline__ void g3_park(Acc& acc, LDS double* red, uint32_t split,
+                                        uint32_t ns, uint32_t lane) {
+  constexpr int Q0 = g3_q0(NB, G), Q1 = g3_q1(NB, G);
+  flush<Q1 - Q0>(acc);
+#pragma unroll
+  for (int q = Q0; q < Q1; ++q)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[((q * ns + split) * 4 + v) * 64 + lane] = acc.d[q - Q0][v];
+}
+
+// The slab loop of one wave: slab blockIdx.x + i * gridDim.x sits in LDS while the next
+// one is loaded into registers (16-byte pieces q = tid + NT m through a buffer
+// resource that spans the slab, so pieces past its end read as zero without a branch),
+// then staged after a barrier. LDS holds CPT * NT pieces, so every register is
+// stored unconditionally (pieces past the slab land after it and are never read). Every
+// load of the loop is consumed by the stage of the same pass, so no wait for it is
+// needed before the next pass reuses its registers.
+template <int NT, class Work>
+__device__ __forceinline__ void g3_loop(const G3K& k, LDS unsigned char* lds, uint32_t tid,
+                                        Work&& work) {
+  constexpr int CPT = g3_cpt(NT);
+  u32x4 pf[CPT];
+  LDS u32x4* const dst = (LDS u32x4*)lds + tid;
+  auto fetch = [&](uint32_t s) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(k.X + (uint64_t)s * k.slab_q), (short)0, (int)(k.slab_q * 16), G3_RSRC_W3);
+#pragma unroll
+    for (int m = 0; m < CPT; ++m)
+      pf[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(tid * 16), NT * 16 * m, 0);
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) dst[NT * m] = pf[m];
+  };
+  const uint32_t G = gridDim.x;
+  uint32_t s = blockIdx.x;
+  fetch(s);
+  stage();
+  lds_barrier();
+  for (; s + G < k.A; s += G) {
+    fetch(s + G);   // in flight while the slab in LDS is worked on
+    work();
+    lds_barrier();  // every wave is done with the slab
+    stage();
+    lds_barrier();
+  }
+  work();
+  lds_barrier();
+}
+
+// Role ids: mode a and mode b take 0..4 and 5..9 for (NB, group) in the order
+// (1,0) (2,0) (3,0) (4,0) (4,1); mode c takes 10 (NB 1) and 11 (NB 2).
+__host__ __device__ constexpr int g3_role(int mode, int NB, int g) {
+  return mode == 2 ? 10 + (NB - 1) : 5 * mode + (NB - 1) + g;
+}
+
+#define G3_ROLES(X)                                                                    \
+  X(0, 0, 1, 0) X(1, 0, 2, 0) X(2, 0, 3, 0) X(3, 0, 4, 0) X(4, 0, 4, 1) X(5, 1, 1, 0) \
+  X(6, 1, 2, 0) X(7, 1, 3, 0) X(8, 1, 4, 0) X(9, 1, 4, 1) X(10, 2, 1, 0) X(11, 2, 2, 0)
+
+// AV, BV: the fragments of mode a (b) are aligned 16-byte runs (Ib Ic % 8 == 0; Ic % 8 == 0)
+template <bool BF, bool AV, bool BV>
+__global__ void __launch_bounds__(g3_nt(AV)) k_gram3(G3K k) {
+  constexpr int NT = g3_nt(AV);
+  extern __shared__ u32x4 smem3[];
+  LDS unsigned char* const lds = (LDS unsigned char*)smem3;
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t li = lane & 15, kg = lane >> 4;
+
+  // this wave's role (waves past the plan only load and stage slabs)
+  int role = -1;
+  uint32_t split = 0, ns = 1;
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    const uint32_t ng = (uint32_t)g3_groups((int)k.nb[m]);
+    if (wv >= k.w0[m] && wv < k.w0[m] + ng * k.ns[m]) {
+      const uint32_t j = wv - k.w0[m];
+      role = g3_role(m, (int)k.nb[m], (int)(j % ng));
+      split = j / ng;
+      ns = k.ns[m];
+    }
+  }
+  role = __builtin_amdgcn_readfirstlane(role);
+  split = __builtin_amdgcn_readfirstlane(split);
+  ns = __builtin_amdgcn_readfirstlane(ns);
+
+  Acc acc;
+#pragma unroll
+  for (int m = 0; m < G3_MAXQ; ++m) {
+    acc.s[m] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc.d[m][v] = 0.0;
+  }
+  acc.since = 0;
+
+  // each role runs its own copy of the slab loop, so the values one role keeps across
+  // slabs are not live in the others
+  LDS double* const red = (LDS double*)lds;
+  switch (role) {
+#define G3_CASE(ID, M, NB, GR)                                                      \
+  case ID:                                                                          \
+    g3_loop<NT>(k, lds, tid, [&]() {                                                \
+      g3_steps<BF, M, NB, GR, (M == 0 && AV) || (M == 1 && BV)>(k, lds, split, ns, li, kg, \
+                                                                 acc);              \
+    });                                                                             \
+    g3_park<NB, GR>(acc, red + k.red[M], split, ns, lane);                          \
+    break;
+    G3_ROLES(G3_CASE)
+#undef G3_CASE
+    default: g3_loop<NT>(k, lds, tid, []() {}); break;
+  }
+  lds_barrier();
+#pragma unroll 1
+  for (int m = 0; m < 3; ++m) {
+    const uint32_t I = m == 0 ? k.Ia : m == 1 ? k.Ib : k.Ic;
+    const int NB = (int)k.nb[m];
+    const uint32_t nsm = k.ns[m];
+    const uint32_t nblk = (uint32_t)(NB * (NB + 1) / 2);
+    const LDS double* const r = red + k.red[m];
+    double* const out = k.part[m] + (uint64_t)blockIdx.x * I * I;
+    for (uint32_t idx = tid; idx < nblk * 256; idx += NT) {
+      const uint32_t q = idx >> 8, v = (idx >> 6) & 3, l = idx & 63;
+      double t = 0.0;
+      for (uint32_t sp = 0; sp < nsm; ++sp) t += r[((q * nsm + sp) * 4 + v) * 64 + l];
+      const uint32_t rb = (uint32_t)tri_rb(NB, (int)q), cb = (uint32_t)tri_cb(NB, (int)q);
+      const uint32_t row = 16 * rb + 4 * (l >> 4) + v, col = 16 * cb + (l & 15);
+      if (row < I && col < I) {
+        out[(size_t)row * I + col] = t;
+        if (rb != cb) out[(size_t)col * I + row] = t;
+      }
+    }
+  }
+}
+
+struct G3Plan {
+  bool ok;
+  G3K k;
+  size_t lds;
+  uint32_t grid, nt;
+};
+
+typedef void (*G3Fn)(G3K);
+// The instantiation for the data type and the two fragment read forms.
+G3Fn g3_kernel(bool bf, bool av, bool bv) {
+  if (bf)
+    return av ? (bv ? k_gram3<true, true, true> : k_gram3<true, true, false>)
+              : (bv ? k_gram3<true, false, true> : k_gram3<true, false, false>);
+  return av ? (bv ? k_gram3<false, true, true> : k_gram3<false, true, false>)
+            : (bv ? k_gram3<false, false, true> : k_gram3<false, false, false>);
+}
+
+int g3_occupancy(G3Fn fn, int nt, size_t lds) {
+  if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)lds) != hipSuccess)
+    return 0;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, nt, lds) != hipSuccess)
+    return 0;
+  return per_cu;
+}
+
+// Shape checks, the k-split plan and the LDS size; `probe` also asks the runtime whether
+// a workgroup fits a CU.
+G3Plan g3plan(const Gram3Args& g, int num_cu, bool probe) {
+  G3Plan p{};
+  p.ok = false;
+  if (g.dt != DT_BF16 && g.dt != DT_F16) return p;
+  if (g.A == 0 || g.Ia == 0 || g.Ib == 0 || g.Ic == 0) return p;
+  if (g.Ia > 64 || g.Ib > 64 || g.Ic > 32) return p;
+  const uint64_t slab_e = (uint64_t)g.Ia * g.Ib * g.Ic;
+  // mode b's dword reads run up to 68 bytes past the slab, into the staged zeros
+  if (slab_e % 8 != 0 || slab_e * 2 + 80 > (uint64_t)G3_MAX_SLAB * 2) return p;
+  if (((uintptr_t)g.X) % 16 != 0) return p;
+  G3K& k = p.k;
+  k.X = (const u32x4*)g.X;
+  k.A = g.A;
+  k.Ia = g.Ia;
+  k.Ib = g.Ib;
+  k.Ic = g.Ic;
+  k.slab_q = (uint32_t)(slab_e / 8);
+  k.IBC = g.Ib * g.Ic;
+  k.RAB = g.Ia * g.Ib;
+  k.a_vec = k.IBC % 8 == 0;
+  k.b_vec = g.Ic % 8 == 0;
+  const uint32_t I[3] = {g.Ia, g.Ib, g.Ic};
+  k.steps[0] = (k.IBC + 31) / 32;
+  k.steps[1] = g.Ia;
+  k.steps[2] = 2 * ((k.RAB + 63) / 64);   // whole pairs of steps (see g3_frags)
+  // mode c takes its rows in pairs of steps (64 rows) and reads up to 31 values past the
+  // start of each row, the last of them among the zeros staged after the slab
+  const int nt = g3_nt(k.a_vec != 0);
+  const uint64_t staged = (uint64_t)g3_cpt(nt) * nt * 8;   // elements of staged LDS
+  if ((uint64_t)(64 * ((k.steps[2] + 1) / 2)) * g.Ic + 32 > staged)
+    return p;
+  // cost of one k-step of a mode's largest group: its MFMAs (16 cycles each) and its
+  // fragment reads (a 16-byte read ~8 cycles, eight 16-bit reads ~24)
+  uint32_t cost[3], ng[3];
+  for (int m = 0; m < 3; ++m) {
+    const int NB = (int)((I[m] + 15) / 16);
+    k.nb[m] = (uint32_t)NB;
+    ng[m] = (uint32_t)g3_groups(NB);
+    int maxq = 0, maxf = 0;
+    for (int gi = 0; gi < g3_groups(NB); ++gi) {
+      maxq = std::max(maxq, g3_q1(NB, gi) - g3_q0(NB, gi));
+      maxf = std::max(maxf, g3_nfrags(NB, gi));
+    }
+    const bool vec = m == 0 ? k.a_vec != 0 : m == 1 ? k.b_vec != 0 : false;
+    cost[m] = (uint32_t)maxq * 16 + (uint32_t)maxf * (vec ? 8 : 24);
+    k.ns[m] = 1;
+  }
+  // more k-splits for the mode that would finish last, while waves remain
+  auto span = [&](int m) { return (k.steps[m] + k.ns[m] - 1) / k.ns[m] * cost[m]; };
+  uint32_t used = ng[0] + ng[1] + ng[2];
+  for (;;) {
+    int worst = -1;
+    for (int m = 0; m < 3; ++m)
+      if (used + ng[m] <= (uint32_t)(nt / 64) && k.ns[m] < k.steps[m] &&
+          (worst < 0 || span(m) > span(worst)))
+        worst = m;
+    if (worst < 0) break;
+    ++k.ns[worst];
+    used += ng[worst];
+  }
+  k.w0[0] = 0;
+  k.w0[1] = ng[0] * k.ns[0];
+  k.w0[2] = k.w0[1] + ng[1] * k.ns[1];
+  uint32_t red = 0;
+  for (int m = 0; m < 3; ++m) {
+    k.red[m] = red;
+    red += k.nb[m] * (k.nb[m] + 1) / 2 * k.ns[m] * 4 * 64;
+  }
+  // every staged piece (see g3_loop), or the block totals
+  p.lds = std::max<size_t>((size_t)staged * 2, (size_t)red * sizeof(double));
+  p.nt = (uint32_t)nt;
+  if (p.lds > G3_LDS_MAX) return p;
+  if (probe) {
+    const int occ =
+        g3_occupancy(g3_kernel(g.dt == DT_BF16, k.a_vec != 0, k.b_vec != 0), nt, p.lds);
+    if (occ < 1) return p;
+  }
+  uint64_t grid = (uint64_t)(num_cu > 0 ? num_cu : 256);
+  if (grid > g.A) grid = g.A;
+  p.grid = (uint32_t)grid;
+  p.ok = true;
+  return p;
+}
+
+}  // namespace
+
+bool gram3_supported(const Gram3Args& g, int num_cu) { return g3plan(g, num_cu, true).ok; }
+
+uint64_t gram3_partial_doubles(const Gram3Args& g, int num_cu) {
+  const G3Plan p = g3plan(g, num_cu, false);
+  if (!p.ok) return 0;
+  const uint64_t rows = (uint64_t)p.grid + gram_reduce_groups();
+  return rows * ((uint64_t)g.Ia * g.Ia + (uint64_t)g.Ib * g.Ib + (uint64_t)g.Ic * g.Ic);
+}
+
+hipError_t launch_gram3(const Gram3Args& g, int num_cu, hipStream_t s,
+                        void (*mark)(void*, int, bool), void* mctx) {
+  G3Plan p = g3plan(g, num_cu, true);
+  if (!p.ok) return hipErrorInvalidValue;
+  const uint32_t I[3] = {g.Ia, g.Ib, g.Ic};
+  const uint64_t rows = (uint64_t)p.grid + gram_reduce_groups();
+  double* part = g.partial;
+  for (int m = 0; m < 3; ++m) {
+    p.k.part[m] = part;
+    part += rows * I[m] * I[m];
+  }
+  if (mark) mark(mctx, KID_GRAM3, true);
+  hipLaunchKernelGGL(g3_kernel(g.dt == DT_BF16, p.k.a_vec != 0, p.k.b_vec != 0), dim3(p.grid),
+                     dim3(p.nt), p.lds, s, p.k);
+  if (mark) mark(mctx, KID_GRAM3, false);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  for (int m = 0; m < 3; ++m) {
+    e = gram_reduce(p.k.part[m], p.grid, I[m] * I[m], g.out[m], s, mark, mctx);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace tg

@@ -60,7 +60,7 @@ enum KernelId {
   KID_TOPK_COMPACT, KID_MASK_FROM_OMEGA, KID_GATHER, KID_PROJECT, KID_ADAM,
   KID_RECONSTRUCT, KID_RECON_APPLY, KID_APPLY_DENSE, KID_GRAM, KID_GRAM_REDUCE,
   KID_EIG, KID_FILL, KID_PROJECT_FIRST, KID_PROJECT_FUSED2, KID_RECON_FUSED2_APPLY,
-  KID_RECON_FUSED2, KID_REMAP, KID_PROJECT_FUSED3, KID_COUNT_
+  KID_RECON_FUSED2, KID_REMAP, KID_PROJECT_FUSED3, KID_GRAM3, KID_COUNT_
 };
 
 // ---------------------------------------------------------------- launchers
@@ -198,6 +198,26 @@ uint32_t gram_reduce_groups();   // partial buffer holds (blocks + groups) * (I*
 size_t gram_lds_bytes(const GramArgs& g);
 hipError_t launch_gram(const GramArgs& g, int num_cu, hipStream_t s,
                        void (*mark)(void*, int, bool), void* mctx);
+// Sum nblk partials of n2 fp64 values (RGROUPS stage rows follow them) into out.
+hipError_t gram_reduce(double* partial, uint32_t nblk, uint32_t n2, double* out, hipStream_t s,
+                       void (*mark)(void*, int, bool), void* mctx);
+
+// Grams of the last three modes (a, b, c) of a 16-bit tensor viewed as A contiguous
+// slabs of Ia x Ib x Ic, from one read: out[m] (fp64, I_m x I_m) as launch_gram gives
+// for each of the three modes. Supported for bf16/fp16 when Ia, Ib <= 64, Ic <= 32, a
+// slab is a multiple of 8 elements and at most 128 KiB, and X is 16-byte aligned.
+// `partial` holds gram3_partial_doubles() values.
+struct Gram3Args {
+  const void* X;
+  int dt;
+  uint32_t A, Ia, Ib, Ic;
+  double* partial;
+  double* out[3];
+};
+bool gram3_supported(const Gram3Args& g, int num_cu);
+uint64_t gram3_partial_doubles(const Gram3Args& g, int num_cu);
+hipError_t launch_gram3(const Gram3Args& g, int num_cu, hipStream_t s,
+                        void (*mark)(void*, int, bool), void* mctx);
 
 // Eigen-decomposition of the Gram (stacked real (I*P)^2 fp64) and factor outputs.
 struct EigArgs {

@@ -52,6 +52,8 @@ struct tgrad_handle {
   bool slab2 = true;         // 16-bit data: the wave-per-slab two-mode kernels where they fit
   bool can_slab3 = false;    // the projection's first launch can also take mode d-3
   bool slab3 = true;         // use it
+  bool can_gram3 = false;    // refresh: the last three modes' Grams from one read
+  bool gram3 = true;         // use it
 
   uint32_t* omega = nullptr;
   uint64_t* mask = nullptr;
@@ -309,6 +311,26 @@ int select_omega(tgrad_t* h, const void* src, int dt, void* resid, hipStream_t s
   return TGRAD_OK;
 }
 
+// The one-read Gram launch of the last three modes over X, where all three are
+// compressed in a real 16-bit tensor (the caller still asks gram3_supported).
+bool gram3_args(const tgrad_t* h, const void* X, Gram3Args* g) {
+  const int d = h->d;
+  if (d < 3 || h->P != 1 || (h->dtype != TGRAD_BF16 && h->dtype != TGRAD_F16)) return false;
+  for (int i = d - 3; i < d; ++i)
+    if (h->ranks[i] >= h->shape[i]) return false;
+  uint64_t A = 1;
+  for (int i = 0; i < d - 3; ++i) A *= (uint64_t)h->shape[i];
+  *g = Gram3Args{};
+  g->X = X;
+  g->dt = h->dtype;
+  g->A = (uint32_t)A;
+  g->Ia = (uint32_t)h->shape[d - 3];
+  g->Ib = (uint32_t)h->shape[d - 2];
+  g->Ic = (uint32_t)h->shape[d - 1];
+  g->partial = h->gram_part;
+  return true;
+}
+
 int do_refresh(tgrad_t* h, const void* grad, hipStream_t s) {
   // sparse first: Omega from G, then the Grams of the residual (G itself when k = 0,
   // else the copy with Omega zeroed that the top-k compaction writes). Low-rank first:
@@ -325,18 +347,28 @@ int do_refresh(tgrad_t* h, const void* grad, hipStream_t s) {
   const int gdt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
   EigArgs eig[TGRAD_MAX_NDIM];
   int ne = 0;
+  // the last three modes' Grams from one read of R where that launch applies, the other
+  // modes one launch each
+  Gram3Args g3;
+  const bool tail3 = h->gram3 && h->can_gram3 && gram3_args(h, R, &g3) &&
+                     gram3_supported(g3, h->num_cu);
   for (int n : h->fmodes) {
-    GramArgs g;
-    g.X = R;
-    g.dt = gdt;
-    view(h->shape, h->d, n, &g.A, &g.I, &g.B);
-    g.P = h->P;
-    g.mask = nullptr;
-    g.partial = h->gram_part;
-    g.out = h->gram + (size_t)ne * h->gram_stride;
-    HIPCHK(h, launch_gram(g, h->num_cu, s, mark_cb, h));
+    double* const out = h->gram + (size_t)ne * h->gram_stride;
+    if (tail3 && n >= h->d - 3) {
+      g3.out[n - (h->d - 3)] = out;
+    } else {
+      GramArgs g;
+      g.X = R;
+      g.dt = gdt;
+      view(h->shape, h->d, n, &g.A, &g.I, &g.B);
+      g.P = h->P;
+      g.mask = nullptr;
+      g.partial = h->gram_part;
+      g.out = out;
+      HIPCHK(h, launch_gram(g, h->num_cu, s, mark_cb, h));
+    }
     EigArgs& e = eig[ne++];
-    e.gram = g.out;
+    e.gram = out;
     e.I = (uint32_t)h->shape[n];
     e.r = (uint32_t)h->ranks[n];
     e.P = h->P;
@@ -345,6 +377,7 @@ int do_refresh(tgrad_t* h, const void* grad, hipStream_t s) {
     e.Mrec = h->Mr[n];
     e.eigvals = h->eig[n];
   }
+  if (tail3) HIPCHK(h, launch_gram3(g3, h->num_cu, s, mark_cb, h));
   if (ne) {
     Mark m(h, KID_EIG);
     HIPCHK(h, launch_eig(eig, ne, s));
@@ -391,7 +424,7 @@ const char* tgrad_kernel_name(int id) {
       "modeprod_reconstruct", "modeprod_reconstruct_apply", "apply_dense", "gram",
       "gram_reduce", "eig_jacobi", "fill", "modeprod_project_first",
       "modeprod2_project_first", "modeprod2_reconstruct_apply", "modeprod2_reconstruct",
-      "remap_moments", "modeprod3_project_first"};
+      "remap_moments", "modeprod3_project_first", "gram3_tail"};
   if (id < 0 || id >= KID_COUNT_) return "";
   return names[id];
 }
@@ -547,6 +580,13 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
     nb = std::max<uint64_t>(nb, gram_blocks(g, h->num_cu)) + gram_reduce_groups();
     if (nb * K2 > gpart) gpart = nb * K2;
     if (K2 > gmax) gmax = K2;
+  }
+  {
+    Gram3Args g3;
+    if (gram3_args(h, (const void*)(uintptr_t)256, &g3) && gram3_supported(g3, h->num_cu)) {
+      h->can_gram3 = true;
+      gpart = std::max<uint64_t>(gpart, gram3_partial_doubles(g3, h->num_cu));
+    }
   }
   ok = ok && dalloc(h, &h->gram_part, gpart, false);
   // the unfused launch plan projects a residual copy of grad (the fused one zeroes Omega
@@ -1210,6 +1250,13 @@ int tgrad_set_fusion(tgrad_t* h, int enable) {
   h->fuse = enable != 0;
   h->slab2 = enable != 2;
   h->slab3 = enable == 1;
+  return TGRAD_OK;
+}
+
+int tgrad_set_gram_fusion(tgrad_t* h, int enable) {
+  if (!h || enable < 0 || enable > 1) return TGRAD_EINVAL;
+  if (enable && !h->can_gram3) return TGRAD_EINVAL;
+  h->gram3 = enable != 0;
   return TGRAD_OK;
 }
 
