@@ -44,6 +44,7 @@ constexpr int NT = WPB * 64;
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 // LDS-qualified pointers: accesses through them compile to ds_* instructions (a
 // generic pointer would give flat accesses, which also count against vmcnt)
@@ -102,6 +103,33 @@ __device__ __forceinline__ f4 mma_2x3(const u16x8& a0, const u16x8& a1, const u1
   c = mma(a1, b[0], c);
   return mma(a0, b[0], c);
 }
+// Eight consecutive 16-bit values at a 2-byte aligned LDS address, as four packed dwords:
+// five aligned dword reads and a funnel shift by 0 or 16 bits (eight 16-bit reads
+// otherwise). The last read may reach up to 18 bytes past the run; callers keep that
+// inside their LDS and mask what lies outside the row.
+__device__ __forceinline__ u32x4 lds_run8(const LDS unsigned char* p) {
+  const uint32_t a = (uint32_t)(uintptr_t)p;
+  const LDS uint32_t* const d = (const LDS uint32_t*)(p - (a & 2u));
+  const uint32_t sh = (a & 2u) * 8;
+  uint32_t w[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) w[i] = d[i];
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], sh);
+  return r;
+}
+// Per-lane mask keeping values 8 lg + 2 i (+1) < n of a run, packed as lds_run8 gives them.
+__device__ __forceinline__ u32x4 run_keep(uint32_t lg, uint32_t n) {
+  u32x4 m;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = 8 * lg + 2 * i;
+    m[i] = (x < n ? 0x0000FFFFu : 0u) | (x + 1 < n ? 0xFFFF0000u : 0u);
+  }
+  return m;
+}
+
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 __device__ __forceinline__ void wave_fence() {
@@ -222,6 +250,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
   const uint64_t N = (uint64_t)k.A * slab_e;
   const uint64_t kS = k.kS;
   const bool sparse = kS > 0;
+  const u32x4 keep1 = run_keep(lg, I2);   // pass 1: i2 = 8 lg + e < I2
 
   // pass 1 B[k = i2][col = r2] = M2[r2][i2] in three bf16 parts
   u16x8 b1[3];
@@ -332,16 +361,22 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
     for (int rb = 0; rb < NRB1; ++rb) {
       const uint32_t i1 = 16 * rb + li;
       u16x8 xp[Bits16<XT>::NP];
+      if constexpr (Bits16<XT>::NP == 1) {
+        // row i1 (rows past I1 read row I1 - 1 and are masked to zero), i2 = 8 lg + e
+        const u32x4 w = lds_run8((const LDS unsigned char*)xs + (min(i1, I1 - 1) * I2 + 8 * lg) * 2);
+        xp[0] = __builtin_bit_cast(u16x8, w & (i1 < I1 ? keep1 : u32x4{0u, 0u, 0u, 0u}));
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t i2 = 8 * lg + e;
-        const unsigned short raw =
-            (i1 < I1 && i2 < I2) ? xs[i1 * I2 + i2]
-                                 : (unsigned short)0;
-        unsigned short p[2];
-        Bits16<XT>::parts(raw, p);
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t i2 = 8 * lg + e;
+          const unsigned short raw =
+              (i1 < I1 && i2 < I2) ? xs[i1 * I2 + i2]
+                                   : (unsigned short)0;
+          unsigned short p[2];
+          Bits16<XT>::parts(raw, p);
 #pragma unroll
-        for (int h = 0; h < Bits16<XT>::NP; ++h) xp[h][e] = p[h];
+          for (int h = 0; h < Bits16<XT>::NP; ++h) xp[h][e] = p[h];
+        }
       }
       f4 acc = f4{0.f, 0.f, 0.f, 0.f};
       if constexpr (Bits16<XT>::NP == 1) {
@@ -669,6 +704,7 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
   LDS float* const m0s = (LDS float*)(lds + k.off_m0);
   const uint32_t li = lane & 15, lg = lane >> 4;
   const uint32_t I0 = k.I0, I1 = k.I1, I2 = k.I2, R0 = k.R0, R1 = k.R1, R2 = k.R2;
+  const u32x4 keep1 = run_keep(lg, I2);   // pass 1: i2 = 8 lg + e < I2
   const uint32_t RC = R1 * R2;                 // stack row length
   const uint32_t trash = WPB3 * RC;            // float offset of a stack's trash slots
   const uint32_t SF = k.stack_fl;
@@ -856,15 +892,23 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
     for (int rb = 0; rb < NRB1; ++rb) {
       const uint32_t i1 = 16 * rb + li;
       u16x8 xp[Bits16<XT>::NP];
+      // (the largest tile shapes keep 16-bit reads: the dword form's registers would spill)
+      if constexpr (Bits16<XT>::NP == 1 && NRB1 + NRB2 + NTW <= 8) {
+        // row i1 (rows past I1 read row I1 - 1 and are masked to zero), i2 = 8 lg + e;
+        // past the last wave's buffers lie the round stacks
+        const u32x4 w = lds_run8((const LDS unsigned char*)xs + (min(i1, I1 - 1) * I2 + 8 * lg) * 2);
+        xp[0] = __builtin_bit_cast(u16x8, w & (i1 < I1 ? keep1 : u32x4{0u, 0u, 0u, 0u}));
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t i2 = 8 * lg + e;
-        const unsigned short raw =
-            (i1 < I1 && i2 < I2) ? xs[i1 * I2 + i2] : (unsigned short)0;
-        unsigned short p[2];
-        Bits16<XT>::parts(raw, p);
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t i2 = 8 * lg + e;
+          const unsigned short raw =
+              (i1 < I1 && i2 < I2) ? xs[i1 * I2 + i2] : (unsigned short)0;
+          unsigned short p[2];
+          Bits16<XT>::parts(raw, p);
 #pragma unroll
-        for (int h = 0; h < Bits16<XT>::NP; ++h) xp[h][e] = p[h];
+          for (int h = 0; h < Bits16<XT>::NP; ++h) xp[h][e] = p[h];
+        }
       }
       u16x8 b1[3];
 #pragma unroll
