@@ -193,6 +193,17 @@ int tgrad_set_fusion(tgrad_t *h, int enable);
  * sums; takes effect at the next refresh. */
 int tgrad_set_gram_fusion(tgrad_t *h, int enable);
 
+/* Test / benchmark hook: with the fused launch plan, two neighbouring compressed modes
+ * ahead of the trailing ones (the projection's last two products, the reconstruction's
+ * first two) run as one launch. The tensor between the two products is never written
+ * (pith.science "What carries the argument": the projection and reconstruction are
+ * chains of mode-wise products, so any two neighbours may be contracted together).
+ * It applies to real tensors when the product of the sizes after the two modes is a
+ * multiple of 16 and both modes' sizes on each side are multiples of 4 up to 64.
+ * enable = 1 selects it (the default; TGRAD_EINVAL where it does not apply), 0 one
+ * launch per mode. Results agree to fp32 rounding; takes effect at the next step. */
+int tgrad_set_pair_fusion(tgrad_t *h, int enable);
+
 /* ---------------------------------------------------------------- variants.
  * Choices the method leaves open, as options of a handle (defaults: the plain method,
  * bit for bit):

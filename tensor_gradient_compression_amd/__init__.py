@@ -75,6 +75,7 @@ SIGNATURES = [
     ("tgrad_mark_refreshed", ctypes.c_int, [_P]),
     ("tgrad_set_fusion", ctypes.c_int, [_P, ctypes.c_int]),
     ("tgrad_set_gram_fusion", ctypes.c_int, [_P, ctypes.c_int]),
+    ("tgrad_set_pair_fusion", ctypes.c_int, [_P, ctypes.c_int]),
     ("tgrad_default_options", None, [ctypes.POINTER(Options)]),
     ("tgrad_set_options", ctypes.c_int, [_P, ctypes.POINTER(Options)]),
     ("tgrad_get_options", ctypes.c_int, [_P, ctypes.POINTER(Options)]),
@@ -285,6 +286,15 @@ class TGrad:
         if rc == EINVAL and enable:
             return False
         self._check(rc, "tgrad_set_gram_fusion")
+        return True
+
+    def set_pair_fusion(self, enable) -> bool:
+        """Select one launch for two neighbouring leading modes of the fused plan (True)
+        or one launch per mode (False); returns False when no such pair applies."""
+        rc = self._lib.tgrad_set_pair_fusion(self._h, int(bool(enable)))
+        if rc == EINVAL and enable:
+            return False
+        self._check(rc, "tgrad_set_pair_fusion")
         return True
 
     def save_state(self) -> bytes:

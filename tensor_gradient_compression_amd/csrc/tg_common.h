@@ -60,7 +60,7 @@ enum KernelId {
   KID_TOPK_COMPACT, KID_MASK_FROM_OMEGA, KID_GATHER, KID_PROJECT, KID_ADAM,
   KID_RECONSTRUCT, KID_RECON_APPLY, KID_APPLY_DENSE, KID_GRAM, KID_GRAM_REDUCE,
   KID_EIG, KID_FILL, KID_PROJECT_FIRST, KID_PROJECT_FUSED2, KID_RECON_FUSED2_APPLY,
-  KID_RECON_FUSED2, KID_REMAP, KID_PROJECT_FUSED3, KID_GRAM3, KID_COUNT_
+  KID_RECON_FUSED2, KID_REMAP, KID_PROJECT_FUSED3, KID_GRAM3, KID_PROJECT_PAIR, KID_RECON_PAIR, KID_COUNT_
 };
 
 // ---------------------------------------------------------------- launchers
@@ -182,6 +182,21 @@ hipError_t launch_slab2(const ModeProd2& mp, int num_cu, hipStream_t s);
 // kernel.
 bool slab3_supported(const ModeProd2& mp);
 hipError_t launch_slab3(const ModeProd2& mp, int num_cu, hipStream_t s);
+
+// Two neighbouring mode products (n, n+1) of a real fp32 tensor viewed as (A, I0, I1, C)
+// in one launch: Y[a, j0, j1, c] = sum_i0 M0[j0, i0] sum_i1 M1[j1, i1] X[a, i0, i1, c]
+// (M0 J0 x I0, M1 J1 x I1, row-major). Supported when C % 16 == 0, I0 is a multiple of
+// 4 up to 64, I1 is one of 16, 24, 32, 48, 64, J0, J1 <= 64 and X is 16-byte aligned.
+struct ModePair {
+  const float* X;
+  float* Y;
+  const float* M0;
+  const float* M1;
+  uint32_t A, I0, I1, J0, J1;
+  uint64_t C;
+};
+bool pair_supported(const ModePair& mp);
+hipError_t launch_pair(const ModePair& mp, hipStream_t s);
 
 // Gram of the (A, I, B, P) view with Omega entries treated as zero:
 // out[x, y] (fp64, (I*P) x (I*P)) = sum over (a, b) of X[a, x, b] X[a, y, b].

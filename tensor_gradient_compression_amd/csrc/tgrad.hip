@@ -54,6 +54,8 @@ struct tgrad_handle {
   bool slab3 = true;         // use it
   bool can_gram3 = false;    // refresh: the last three modes' Grams from one read
   bool gram3 = true;         // use it
+  bool can_pair = false;     // the fused chains hold two neighbouring leading modes
+  bool pairs = true;         // launch those as one (k_pair)
 
   uint32_t* omega = nullptr;
   uint64_t* mask = nullptr;
@@ -256,8 +258,24 @@ void host_operands(uint32_t I, uint32_t r, uint32_t P, const float* U, float* Mp
 // is one launch, one mode or the two trailing modes together.
 // Launch groups of the two chains. fuse: the two trailing modes run as one launch in
 // each direction; proj3 (with fuse): the projection's first launch also takes mode d-3.
+// The (A, I0, I1, C) view of modes n, n + 1 of a tensor whose sizes are cur.
+void pair_view(const int64_t* cur, int d, int n, ModePair* mp) {
+  uint64_t A = 1, C = 1;
+  for (int i = 0; i < n; ++i) A *= (uint64_t)cur[i];
+  for (int i = n + 2; i < d; ++i) C *= (uint64_t)cur[i];
+  mp->A = (uint32_t)A;
+  mp->I0 = (uint32_t)cur[n];
+  mp->I1 = (uint32_t)cur[n + 1];
+  mp->C = C;
+}
+
+// A group of two modes that is not the trailing pair: a k_pair launch.
+bool is_lead_pair(const tgrad_t* h, const std::vector<int>& g) {
+  return g.size() == 2 && std::min(g[0], g[1]) < h->d - 2;
+}
+
 void build_chain(const tgrad_t* h, bool fuse, bool proj3, std::vector<std::vector<int>>& proj,
-                 std::vector<std::vector<int>>& rec) {
+                 std::vector<std::vector<int>>& rec, bool pairs = true) {
   proj.clear();
   rec.clear();
   const int nf = (int)h->fmodes.size();
@@ -276,6 +294,42 @@ void build_chain(const tgrad_t* h, bool fuse, bool proj3, std::vector<std::vecto
     rec.push_back({n});
   }
   if (fuse) rec.push_back({d - 2, d - 1});
+  if (!(fuse && pairs && h->pairs && h->P == 1)) return;
+  // neighbouring single modes after the first group (projection) and before the last
+  // (reconstruction) become one k_pair launch where it applies to their sizes there
+  auto merge = [&](std::vector<std::vector<int>>& chain, bool projection) {
+    int64_t cur[TGRAD_MAX_NDIM];
+    for (int i = 0; i < d; ++i) cur[i] = h->shape[i];
+    if (!projection)
+      for (int n : h->fmodes) cur[n] = h->ranks[n];
+    std::vector<std::vector<int>> out;
+    for (size_t j = 0; j < chain.size(); ++j) {
+      const bool inner = projection ? j > 0 : j + 1 < chain.size();
+      if (inner && j + 1 < chain.size() && (projection || j + 2 < chain.size()) &&
+          chain[j].size() == 1 && chain[j + 1].size() == 1 &&
+          chain[j + 1][0] == chain[j][0] + (projection ? -1 : 1)) {
+        const int n0 = std::min(chain[j][0], chain[j + 1][0]);
+        ModePair mp{};
+        pair_view(cur, d, n0, &mp);
+        mp.J0 = (uint32_t)(projection ? h->ranks[n0] : h->shape[n0]);
+        mp.J1 = (uint32_t)(projection ? h->ranks[n0 + 1] : h->shape[n0 + 1]);
+        mp.X = (const float*)(uintptr_t)256;
+        mp.Y = (float*)(uintptr_t)256;
+        if (pair_supported(mp)) {
+          out.push_back({chain[j][0], chain[j + 1][0]});
+          cur[n0] = mp.J0;
+          cur[n0 + 1] = mp.J1;
+          ++j;
+          continue;
+        }
+      }
+      for (int n : chain[j]) cur[n] = projection ? h->ranks[n] : h->shape[n];
+      out.push_back(chain[j]);
+    }
+    chain = out;
+  };
+  merge(proj, true);
+  merge(rec, false);
 }
 
 // The three-mode projection launch for input X0 (16-byte aligned for its transfers).
@@ -424,7 +478,8 @@ const char* tgrad_kernel_name(int id) {
       "modeprod_reconstruct", "modeprod_reconstruct_apply", "apply_dense", "gram",
       "gram_reduce", "eig_jacobi", "fill", "modeprod_project_first",
       "modeprod2_project_first", "modeprod2_reconstruct_apply", "modeprod2_reconstruct",
-      "remap_moments", "modeprod3_project_first", "gram3_tail"};
+      "remap_moments", "modeprod3_project_first", "gram3_tail", "modeprod_pair_project",
+      "modeprod_pair_reconstruct"};
   if (id < 0 || id >= KID_COUNT_) return "";
   return names[id];
 }
@@ -518,7 +573,7 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
     int64_t cur[TGRAD_MAX_NDIM];
     for (int i = 0; i < ndim; ++i) cur[i] = shape[i];
     std::vector<std::vector<int>> proj, rec;
-    build_chain(h, fz, false, proj, rec);
+    build_chain(h, fz, false, proj, rec, false);   // pairs only drop intermediates
     uint64_t size = N;
     for (size_t j = 0; j < proj.size(); ++j) {
       for (int n : proj[j]) {
@@ -589,6 +644,12 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
     }
   }
   ok = ok && dalloc(h, &h->gram_part, gpart, false);
+  if (h->can_fuse) {
+    std::vector<std::vector<int>> pp, rr;
+    build_chain(h, true, false, pp, rr);
+    for (const auto& g : pp) h->can_pair = h->can_pair || is_lead_pair(h, g);
+    for (const auto& g : rr) h->can_pair = h->can_pair || is_lead_pair(h, g);
+  }
   // the unfused launch plan projects a residual copy of grad (the fused one zeroes Omega
   // in its staged tiles)
   if (h->k > 0 && !h->can_fuse) {
@@ -739,6 +800,20 @@ int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s) {
       cur[d - 3] = h->ranks[d - 3];
       cur[d - 2] = h->ranks[d - 2];
       cur[d - 1] = h->ranks[d - 1];
+    } else if (is_lead_pair(h, proj[j])) {
+      const int n0 = std::min(proj[j][0], proj[j][1]);
+      ModePair mp{};
+      pair_view(cur, h->d, n0, &mp);
+      mp.X = (const float*)X;
+      mp.Y = Y;
+      mp.M0 = h->Mp[n0];
+      mp.M1 = h->Mp[n0 + 1];
+      mp.J0 = (uint32_t)h->ranks[n0];
+      mp.J1 = (uint32_t)h->ranks[n0 + 1];
+      Mark m(h, KID_PROJECT_PAIR);
+      HIPCHK(h, launch_pair(mp, s));
+      cur[n0] = h->ranks[n0];
+      cur[n0 + 1] = h->ranks[n0 + 1];
     } else if (proj[j].size() == 2) {
       const int d = h->d;
       ModeProd2 mp{};
@@ -812,7 +887,21 @@ int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, fl
     const bool last = (j + 1 == rec.size());
     const bool app = last && apply;
     float* Y = last ? (apply ? nullptr : out) : h->buf[which];
-    if (rec[j].size() == 2) {
+    if (is_lead_pair(h, rec[j])) {
+      const int n0 = std::min(rec[j][0], rec[j][1]);
+      ModePair mp{};
+      pair_view(cur, h->d, n0, &mp);
+      mp.X = (const float*)X;
+      mp.Y = Y;
+      mp.M0 = h->Mr[n0];
+      mp.M1 = h->Mr[n0 + 1];
+      mp.J0 = (uint32_t)h->shape[n0];
+      mp.J1 = (uint32_t)h->shape[n0 + 1];
+      Mark m(h, KID_RECON_PAIR);
+      HIPCHK(h, launch_pair(mp, s));
+      cur[n0] = h->shape[n0];
+      cur[n0 + 1] = h->shape[n0 + 1];
+    } else if (rec[j].size() == 2) {
       const int d = h->d;
       ModeProd2 mp{};
       mp.X = X;
@@ -1250,6 +1339,13 @@ int tgrad_set_fusion(tgrad_t* h, int enable) {
   h->fuse = enable != 0;
   h->slab2 = enable != 2;
   h->slab3 = enable == 1;
+  return TGRAD_OK;
+}
+
+int tgrad_set_pair_fusion(tgrad_t* h, int enable) {
+  if (!h || enable < 0 || enable > 1) return TGRAD_EINVAL;
+  if (enable && !h->can_pair) return TGRAD_EINVAL;
+  h->pairs = enable != 0;
   return TGRAD_OK;
 }
 

@@ -348,13 +348,19 @@ def test_timing_records_every_kernel():
         lib.step(W, dev(gs.next(), wl.dtype))
     rec = lib.timing_read()
     for name in ("topk_hist", "topk_compact", "modeprod2_project_first",
-                 "modeprod_project", "adam_fused", "modeprod_reconstruct",
+                 "modeprod_pair_project", "adam_fused", "modeprod_pair_reconstruct",
                  "modeprod2_reconstruct_apply", "gram", "eig_jacobi"):
         assert name in rec, name
     assert "gather_residual" not in rec        # folded into the fused first projection
+    assert "modeprod_project" not in rec       # modes 1 and 0 in one launch
     assert rec["adam_fused"][0] == 3
     assert rec["modeprod2_project_first"][0] == 3
-    assert rec["modeprod_project"][0] == 6
+    assert rec["modeprod_pair_project"][0] == 3 and rec["modeprod_pair_reconstruct"][0] == 3
+    assert lib.set_pair_fusion(False)
+    lib.step(W, dev(gs.next(), wl.dtype))
+    rec = lib.timing_read()
+    assert rec["modeprod_project"][0] == 2 and rec["modeprod_reconstruct"][0] == 2
+    assert "modeprod_pair_project" not in rec
     assert lib.set_fusion(False)
     lib.step(W, dev(gs.next(), wl.dtype))
     rec = lib.timing_read()
