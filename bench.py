@@ -55,6 +55,7 @@ def kernel_bytes(wl, proj3=False):
     fmodes = [n for n, (I, r) in enumerate(zip(wl.shape, wl.ranks)) if r < I]
     cur = list(wl.shape)
     proj, rec = [], []
+    psizes = [N]        # tensor size after each projection mode
     size = N
     for j, n in enumerate(reversed(fmodes)):
         out = size // cur[n] * wl.ranks[n]
@@ -62,7 +63,9 @@ def kernel_bytes(wl, proj3=False):
         proj.append(inb + out * P * 4)
         cur[n] = wl.ranks[n]
         size = out
+        psizes.append(size)
     ncore = size
+    rsizes = [ncore]    # tensor size after each reconstruction mode
     for j, n in enumerate(fmodes):
         out = size // cur[n] * wl.shape[n]
         b = size * P * 4
@@ -75,6 +78,7 @@ def kernel_bytes(wl, proj3=False):
         rec.append(b)
         cur[n] = wl.shape[n]
         size = out
+        rsizes.append(size)
     # two trailing modes per launch: input read once, output written once; the first
     # projection launch also performs the COO gather (k indices read and k fp32 values
     # written; the gradient values come with the input tile, which is zeroed at Omega in
@@ -105,6 +109,10 @@ def kernel_bytes(wl, proj3=False):
         "modeprod2_project_first": [proj2],
         "modeprod3_project_first": [proj3_b],
         "modeprod2_reconstruct_apply": [rec2],
+        # the projection's last two modes in one launch (fp32 in, core out), and the
+        # reconstruction's first two
+        "modeprod_pair_project": [(psizes[-3] + ncore) * P * 4] if len(psizes) >= 3 else [],
+        "modeprod_pair_reconstruct": [(ncore + rsizes[2]) * P * 4] if len(rsizes) >= 3 else [],
         "_flops_project": flops_proj,
         "_ncore": ncore,
         # the step's work as one launch per kernel of the path, fp32 intermediates and no
