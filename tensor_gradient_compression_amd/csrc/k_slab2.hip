@@ -717,7 +717,7 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
   const uint32_t nct = (RC + 15) / 16, njb = (R0 + 15) / 16;
   const uint32_t jb = wv / (WPB3 / 2), ct0 = wv % (WPB3 / 2);
   const uint32_t j0 = 16 * jb + li;
-  const bool jok = jb < njb && j0 < R0;
+  const uint32_t jc = jb < njb && j0 < R0 ? j0 : R0 - 1;   // M0 row this lane reads
 
   // The factor operands, as every lane supplies them, in LDS tables shared by the
   // workgroup (registers would not leave room for the mode d-2 accumulators):
@@ -945,20 +945,22 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
     wave_fence();
     __builtin_amdgcn_s_barrier();
     wave_fence();
+    // Every operand read is unconditional and at a fixed offset, so the compiler can
+    // issue them without a branch or a register per address (reads under a branch each
+    // waited for their own LDS round trip). Rows j0 >= R0 read row R0 - 1 (jc), and
+    // tiles past the last column block, like columns RC .. 16 nct - 1, read on into the
+    // next rows, the other round stack, the M0 copy or the factor tables (all inside the
+    // workgroup's LDS); all of these only reach outputs that are not stored.
 #pragma unroll
     for (int h = 0; h < WPB3 / 4; ++h) {
       const uint32_t i0l = 4 * h + lg;               // row of the stack
       const uint32_t i0 = WPB3 * c + i0l;            // mode d-2 index
-      const float av = jok ? m0s[j0 * I0 + i0] : 0.0f;
-      // columns RC .. 16 nct - 1 read into the next row or the trash slots; they only
-      // reach outputs that are not stored
+      const float av = m0s[jc * I0 + i0];
       const LDS float* const brow = st + i0l * RC + 16 * ct0 + li;
 #pragma unroll
-      for (int m = 0; m < NTW; ++m) {
-        const bool ok = ct0 + (WPB3 / 2) * m < nct;
-        const float bv = ok ? brow[16 * (WPB3 / 2) * m] : 0.0f;
-        acc3[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc3[m], 0, 0, 0);
-      }
+      for (int m = 0; m < NTW; ++m)
+        acc3[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, brow[16 * (WPB3 / 2) * m], acc3[m], 0,
+                                                       0, 0);
     }
     if (c == nch - 1) pend = blockIdx.x + r * G;
     step(r, c);
