@@ -273,6 +273,11 @@ int tgrad_load_state(tgrad_t *h, const void *buf, int64_t size);
 #define TGRAD_MAX_KERNEL_IDS 32
 int tgrad_timing_enable(tgrad_t *h, int enable, int max_records);
 int tgrad_timing_read(tgrad_t *h, int64_t *launches, double *ms, int n_ids);
+/* Restricts the timing above to the launches of kernel id (0 <= id <
+ * TGRAD_MAX_KERNEL_IDS, see tgrad_kernel_name), so that a timed run carries one event
+ * pair per launch of that kernel and none around the others; id = -1 times every launch
+ * again (the default). Errors: TGRAD_EINVAL (NULL handle, id out of range). */
+int tgrad_timing_only(tgrad_t *h, int id);
 const char *tgrad_kernel_name(int id);
 
 #ifdef __cplusplus

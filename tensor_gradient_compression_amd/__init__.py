@@ -84,6 +84,7 @@ SIGNATURES = [
     ("tgrad_load_state", ctypes.c_int, [_P, _P, _I64]),
     ("tgrad_timing_enable", ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int]),
     ("tgrad_timing_read", ctypes.c_int, [_P, _P, _P, ctypes.c_int]),
+    ("tgrad_timing_only", ctypes.c_int, [_P, ctypes.c_int]),
     ("tgrad_kernel_name", ctypes.c_char_p, [ctypes.c_int]),
 ]
 
@@ -316,6 +317,16 @@ class TGrad:
     def timing_enable(self, enable: bool = True, max_records: int = 100000):
         self._check(self._lib.tgrad_timing_enable(self._h, int(enable), int(max_records)),
                     "tgrad_timing_enable")
+
+    def timing_only(self, name=None):
+        """Time only the launches of the kernel called name (None: every launch)."""
+        kid = -1
+        if name is not None:
+            ids = [i for i in range(MAX_KERNEL_IDS) if kernel_name(i) == name]
+            if not ids:
+                raise ValueError(f"no kernel called {name!r}")
+            kid = ids[0]
+        self._check(self._lib.tgrad_timing_only(self._h, kid), "tgrad_timing_only")
 
     def timing_read(self):
         """{kernel name: (launches, total ms)} since the last read."""

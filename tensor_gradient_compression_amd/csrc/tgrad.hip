@@ -92,6 +92,7 @@ struct tgrad_handle {
   std::string err;
 
   bool timing = false;
+  int timing_only = -1;   // >= 0: only launches of this kernel id are timed
   int max_rec = 0;
   std::vector<Rec> recs;
   std::vector<hipEvent_t> pool;
@@ -206,6 +207,7 @@ hipEvent_t take_event(tgrad_t* h) {
 void mark_cb(void* ctx, int id, bool begin) {
   tgrad_t* h = (tgrad_t*)ctx;
   if (!h->timing) return;
+  if (h->timing_only >= 0 && id != h->timing_only) return;
   if (begin) {
     if ((int)h->recs.size() >= h->max_rec) return;
     Rec r;
@@ -1366,6 +1368,12 @@ int tgrad_timing_enable(tgrad_t* h, int enable, int max_records) {
   if (!h || max_records < 0) return TGRAD_EINVAL;
   h->timing = enable != 0;
   h->max_rec = max_records;
+  return TGRAD_OK;
+}
+
+int tgrad_timing_only(tgrad_t* h, int id) {
+  if (!h || id < -1 || id >= TGRAD_MAX_KERNEL_IDS) return TGRAD_EINVAL;
+  h->timing_only = id;
   return TGRAD_OK;
 }
 

@@ -368,6 +368,27 @@ def test_timing_records_every_kernel():
     assert rec["gather_residual"][0] == 1
 
 
+def test_timing_only_one_kernel():
+    wl = CONFIGS[1]
+    lib = make_lib(wl)
+    gs = GradStream(wl)
+    W = dev(init_weights(wl), wl.dtype)
+    lib.step(W, dev(gs.next(), wl.dtype))          # the refresh step, untimed
+    lib.timing_only("adam_fused")
+    lib.timing_enable(True)
+    for _ in range(2):
+        lib.step(W, dev(gs.next(), wl.dtype))
+    rec = lib.timing_read()
+    assert list(rec) == ["adam_fused"] and rec["adam_fused"][0] == 2
+    assert rec["adam_fused"][1] > 0.0
+    lib.timing_only(None)
+    lib.step(W, dev(gs.next(), wl.dtype))
+    rec = lib.timing_read()
+    assert "adam_fused" in rec and "modeprod2_reconstruct_apply" in rec
+    with pytest.raises(ValueError):
+        lib.timing_only("no_such_kernel")
+
+
 # --------------------------------------------------------------------------- full size, config 4
 
 @pytest.mark.timeout(900)
