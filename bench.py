@@ -34,7 +34,6 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_MFMA_PEAK_TFS = 157.3     # MI355X dense fp32 matrix
-WORKLOAD = 4
 
 
 def esize(dtype):
@@ -149,8 +148,9 @@ def multi_tensor(dev, stream, steps=10, warmup=3):
     step, after the warm-up steps (step 1 refreshes every layer)."""
     import torch
     import tensor_gradient_compression_amd as tg
-    from synth import CONFIGS, GradStream, init_weights
-    wl = CONFIGS[2]
+    from synth import (TINY_F32, F32_32x32x16x16, F16_4x64x64x64x64, C64_64x64x64x33, BF16_64x64x48x48x25,
+                   GradStream, init_weights)
+    wl = F16_4x64x64x64x64
     L = wl.layers
     out = {"workload": f"fp16 {L} x (64,64,64,64), Tucker ranks (32,32,32,32), 5% sparse"}
     for mode in ("sequential", "step_many"):
@@ -238,9 +238,10 @@ def main():
 
     import torch
     import tensor_gradient_compression_amd as tg
-    from synth import CONFIGS, GradStream, init_weights
+    from synth import (TINY_F32, F32_32x32x16x16, F16_4x64x64x64x64, C64_64x64x64x33, BF16_64x64x48x48x25,
+                   GradStream, init_weights)
 
-    wl = CONFIGS[WORKLOAD]
+    wl = BF16_64x64x48x48x25
     assert torch.cuda.is_available(), "bench needs a GPU"
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)

@@ -60,18 +60,20 @@ class Workload:
         return int(math.floor(self.sparse_ratio * self.numel))
 
 
-CONFIGS = {
-    0: Workload("tiny-fp32-(8,8,6,6)", (8, 8, 6, 6), "f32", (4, 4, 3, 3), (3, 3, 2, 2),
-                0.05, T=5, steps=10),
-    1: Workload("fp32-(32,32,16,16)", (32, 32, 16, 16), "f32", (16, 16, 8, 8), (8, 8, 4, 4),
-                0.05, T=10, steps=50, outlier_random=0.002),
-    2: Workload("fp16-4x(64,64,64,64)", (64, 64, 64, 64), "f16", (32, 32, 32, 32),
-                (16, 16, 16, 16), 0.05, T=100, steps=200, layers=4),
-    3: Workload("c64-(64,64,64,33)", (64, 64, 64, 33), "c64", (32, 32, 32, 16), (16, 16, 16, 8),
-                0.05, T=100, steps=100, outlier_random=0.002),
-    4: Workload("bf16-(64,64,48,48,25)", (64, 64, 48, 48, 25), "bf16", (32, 32, 24, 24, 13),
-                (16, 16, 12, 12, 6), 0.05, T=200, steps=400),
-}
+TINY_F32 = Workload("tiny-fp32-(8,8,6,6)", (8, 8, 6, 6), "f32", (4, 4, 3, 3), (3, 3, 2, 2),
+                    0.05, T=5, steps=10)
+F32_32x32x16x16 = Workload("fp32-(32,32,16,16)", (32, 32, 16, 16), "f32", (16, 16, 8, 8), (8, 8, 4, 4),
+                           0.05, T=10, steps=50, outlier_random=0.002)
+F16_4x64x64x64x64 = Workload("fp16-4x(64,64,64,64)", (64, 64, 64, 64), "f16", (32, 32, 32, 32),
+                             (16, 16, 16, 16), 0.05, T=100, steps=200, layers=4)
+C64_64x64x64x33 = Workload("c64-(64,64,64,33)", (64, 64, 64, 33), "c64", (32, 32, 32, 16), (16, 16, 16, 8),
+                           0.05, T=100, steps=100, outlier_random=0.002)
+BF16_64x64x48x48x25 = Workload("bf16-(64,64,48,48,25)", (64, 64, 48, 48, 25), "bf16", (32, 32, 24, 24, 13),
+                               (16, 16, 12, 12, 6), 0.05, T=200, steps=400)
+
+# every workload by its own name
+WORKLOADS = {w.name: w for w in (TINY_F32, F32_32x32x16x16, F16_4x64x64x64x64,
+                                  C64_64x64x64x33, BF16_64x64x48x48x25)}
 
 # Seed offsets for independent streams of one workload.
 LAYER_SEED_STRIDE = 1000

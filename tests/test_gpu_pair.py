@@ -14,7 +14,8 @@ import pytest
 
 import tensor_gradient_compression_amd as tg
 from gpu_helpers import make_lib, make_oracle, weight_check
-from synth import CONFIGS, GradStream, init_weights
+from synth import (TINY_F32, F32_32x32x16x16, F16_4x64x64x64x64, C64_64x64x64x33, BF16_64x64x48x48x25,
+                   GradStream, init_weights)
 from synth.gen import custom
 
 torch = pytest.importorskip("torch")
@@ -30,7 +31,7 @@ def _gpu():
 # (name, workload, pair launches per step in the projection, in the reconstruction)
 CASES = [
     # modes 1, 0 after the trailing pair and 0, 1 before it; 32 and 16 values of k
-    ("config1-f32", CONFIGS[1], 1, 1),
+    ("fp32-32x32x16x16", F32_32x32x16x16, 1, 1),
     # a pair behind a full-rank leading mode (A = 3); the reconstruction's I1 = 8 is too
     # narrow, so it runs one launch per mode
     ("f32-5mode-behind-full-rank", custom((3, 32, 16, 16, 8), "f32", (3, 16, 8, 8, 4), 0.05), 1, 0),

@@ -8,7 +8,8 @@ import pytest
 import oracle as O
 import tensor_gradient_compression_amd as tg
 from gpu_helpers import factor_check, make_lib, make_oracle, omega_properties, weight_check
-from synth import CONFIGS, GradStream, init_weights
+from synth import (TINY_F32, F32_32x32x16x16, F16_4x64x64x64x64, C64_64x64x64x33, BF16_64x64x48x48x25,
+                   GradStream, init_weights)
 from synth.gen import custom
 
 torch = pytest.importorskip("torch")
@@ -51,8 +52,8 @@ def _topk_inputs():
     z[9, 1] = -1e-42
     z[11, 11] = 3e-39
     cases.append(("f32-signed-zeros-subnormals", z.shape, "f32", 0.01, z))
-    wl1 = CONFIGS[1]
-    cases.append(("config1", wl1.shape, "f32", 0.05, GradStream(wl1).next()))
+    wl1 = F32_32x32x16x16
+    cases.append(("fp32-32x32x16x16", wl1.shape, "f32", 0.05, GradStream(wl1).next()))
     big = r.standard_normal((4099, 1031)).astype(np.float32)
     cases.append(("f32-ragged-4M", big.shape, "f32", 0.05, big))
     cz = (r.standard_normal((301, 77)) + 1j * r.standard_normal((301, 77))).astype(np.complex64)
@@ -76,9 +77,8 @@ def test_topk_bit_exact(case):
     assert np.array_equal(host(G, dtype).view(np.uint8), before.view(np.uint8)), "refresh modified grad"
 
 
-def test_topk_config2_and_config3_sizes():
-    for idx in (2, 3):
-        wl = CONFIGS[idx]
+def test_topk_fp16_and_complex64_full_sizes():
+    for wl in (F16_4x64x64x64x64, C64_64x64x64x33):
         g = GradStream(wl).next()
         lib = tg.TGrad(wl.shape, wl.shape, wl.dtype, wl.sparse_ratio, 1000)
         lib.refresh(dev(g, wl.dtype))
@@ -92,8 +92,8 @@ def test_topk_config2_and_config3_sizes():
 # leaves core entries that are zero up to rounding, and Adam's m / (sqrt(v) + eps)
 # turns that rounding noise into O(1) updates on which no two implementations agree.
 FACTOR_CASES = [
-    ("config0", CONFIGS[0]),
-    ("config1", CONFIGS[1]),
+    ("tiny-fp32-8x8x6x6", TINY_F32),
+    ("fp32-32x32x16x16", F32_32x32x16x16),
     ("odd-5mode", custom((9, 7, 5, 11, 3), "f32", (4, 3, 5, 2, 1), 0.05)),
     ("narrow-lastmode-64", custom((3, 5, 64), "f32", (2, 5, 12), 0.1)),
     ("bf16-odd", custom((33, 17, 60), "bf16", (13, 8, 31), 0.05)),
@@ -192,12 +192,12 @@ def test_steps_with_pinned_omega_and_factors(case, fused):
 # --------------------------------------------------------------------------- independent runs
 
 RUN_CASES = [
-    ("config0", CONFIGS[0], None),
-    ("config1", CONFIGS[1], None),
+    ("tiny-fp32-8x8x6x6", TINY_F32, None),
+    ("fp32-32x32x16x16", F32_32x32x16x16, None),
     ("bf16-odd", custom((33, 17, 60), "bf16", (13, 8, 31), 0.05, T=4, steps=9), None),
     ("c64-small", custom((12, 10, 9), "c64", (5, 4, 3), 0.05, T=3, steps=7), None),
-    ("config2-one-layer-3-steps", CONFIGS[2], 3),
-    ("config3-3-steps", CONFIGS[3], 3),
+    ("fp16-64x64x64x64-one-layer-3-steps", F16_4x64x64x64x64, 3),
+    ("c64-64x64x64x33-3-steps", C64_64x64x64x33, 3),
 ]
 
 
@@ -262,7 +262,7 @@ def test_rho_one_is_bitwise_oracle(dtype):
 
 
 def test_deterministic_rerun():
-    wl = CONFIGS[1]
+    wl = F32_32x32x16x16
     outs = []
     for _ in range(2):
         gs = GradStream(wl, seed=2)
@@ -298,7 +298,7 @@ def test_misaligned_grad_is_rejected():
     assert lib.t == 1
 
 
-@pytest.mark.parametrize("name,wl", [("config1", CONFIGS[1]),
+@pytest.mark.parametrize("name,wl", [("fp32-32x32x16x16", F32_32x32x16x16),
                                      ("c64-small", custom((12, 10, 9), "c64", (5, 4, 3), 0.05, T=3, steps=7))],
                          ids=lambda x: x if isinstance(x, str) else "")
 def test_checkpoint_resume_is_exact(name, wl):
@@ -339,7 +339,7 @@ def test_checkpoint_resume_is_exact(name, wl):
 
 
 def test_timing_records_every_kernel():
-    wl = CONFIGS[1]
+    wl = F32_32x32x16x16
     lib = make_lib(wl)
     lib.timing_enable(True)
     gs = GradStream(wl)
@@ -369,7 +369,7 @@ def test_timing_records_every_kernel():
 
 
 def test_timing_only_one_kernel():
-    wl = CONFIGS[1]
+    wl = F32_32x32x16x16
     lib = make_lib(wl)
     gs = GradStream(wl)
     W = dev(init_weights(wl), wl.dtype)
@@ -389,15 +389,15 @@ def test_timing_only_one_kernel():
         lib.timing_only("no_such_kernel")
 
 
-# --------------------------------------------------------------------------- full size, config 4
+# --------------------------------------------------------------------------- full size, bf16 (64,64,48,48,25)
 
 @pytest.mark.timeout(900)
-def test_config4_full_size_refresh_and_step():
+def test_bf16_64x64x48x48x25_full_size_refresh_and_step():
     """bf16 (64,64,48,48,25): Omega checked by its complete characterisation (no sort of
     236M keys), factor projectors against the oracle's fp64 Gram eigenvectors, and the
     stepped weights at a sampled sub-grid of 4^5 positions against the oracle's step
     computed with the library's own Omega and factors."""
-    wl = CONFIGS[4]
+    wl = BF16_64x64x48x48x25
     g = GradStream(wl, seed=0).next()
     W0 = init_weights(wl, seed=0)
     lib = make_lib(wl)
@@ -437,4 +437,4 @@ def test_config4_full_size_refresh_and_step():
     hit = (pos < om.size) & (om[np.minimum(pos, om.size - 1)] == idx)
     D[hit] = D[hit] + uS[pos[hit]]
     Wexp = O.encode(O.decode(W0.reshape(-1)[idx], wl.dtype) - np.float32(wl.lr) * D, wl.dtype)
-    weight_check(Wg.reshape(-1)[idx], Wexp, wl.dtype, "config4 sampled")
+    weight_check(Wg.reshape(-1)[idx], Wexp, wl.dtype, "bf16-(64,64,48,48,25) sampled")

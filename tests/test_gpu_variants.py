@@ -11,7 +11,8 @@ import pytest
 import oracle as O
 import tensor_gradient_compression_amd as tg
 from gpu_helpers import factor_check, make_lib, weight_check
-from synth import CONFIGS, GradStream, init_weights
+from synth import (TINY_F32, F32_32x32x16x16, F16_4x64x64x64x64, C64_64x64x64x33, BF16_64x64x48x48x25,
+                   GradStream, init_weights)
 from synth.gen import custom
 
 torch = pytest.importorskip("torch")
@@ -84,7 +85,7 @@ def test_randk_omega_bit_exact(case):
 
 def test_randk_factors_are_those_of_its_residual():
     """The Gram after a rand-k selection is taken over G with the random Omega zeroed."""
-    wl = CONFIGS[1]
+    wl = F32_32x32x16x16
     lib = lib_for(wl, selection="randk", seed=5)
     orc = oracle_for(wl, selection="randk", seed=5)
     g = GradStream(wl, seed=3).next()
@@ -106,7 +107,7 @@ VARIANTS = [
                  remap_moments=True)),
 ]
 RUNS = [
-    ("config1", CONFIGS[1], 12),
+    ("fp32-32x32x16x16", F32_32x32x16x16, 12),
     ("bf16-odd", custom((33, 17, 60), "bf16", (13, 8, 31), 0.05, T=4, steps=9), 9),
     ("c64-small", custom((12, 10, 9), "c64", (5, 4, 3), 0.05, T=3, steps=7), 7),
     # the three trailing modes in the first projection launch
@@ -123,7 +124,7 @@ def test_variant_runs_match_oracle(run, variant, fused):
     the weight bar, with each variant on both launch plans."""
     name, wl, nsteps = run
     vname, opts = variant
-    T = 4 if name == "config1" else wl.T
+    T = 4 if name == "fp32-32x32x16x16" else wl.T
     lib, orc = lib_for(wl, T=T, **opts), oracle_for(wl, T=T, **opts)
     if not lib.set_fusion(fused):
         pytest.skip("the two trailing modes are not both compressed")
@@ -183,7 +184,7 @@ def test_rho_one_lambda_decay_is_bitwise_oracle(dtype, selection):
 
 
 def test_default_options_leave_the_step_unchanged():
-    wl = CONFIGS[1]
+    wl = F32_32x32x16x16
     outs = []
     for set_defaults in (False, True):
         lib = make_lib(wl, T=4)
@@ -204,7 +205,7 @@ def test_default_options_leave_the_step_unchanged():
 
 
 def test_invalid_options_are_rejected():
-    wl = CONFIGS[0]
+    wl = TINY_F32
     lib = make_lib(wl)
     for bad in (dict(weight_decay=-1e-3), dict(weight_decay=float("nan")),
                 dict(sparse_scale=float("inf"))):
@@ -253,7 +254,7 @@ def test_step_many_matches_separate_steps():
     across a refresh give, per tensor, bit for bit the weights, moments, Omega and
     factors of stepping each alone; the caller's stream sees the updates."""
     wls = [custom((6, 5, 48, 25), "bf16", (3, 3, 24, 13), 0.05, T=3),
-           CONFIGS[1],
+           F32_32x32x16x16,
            custom((12, 10, 9), "c64", (5, 4, 3), 0.05, T=3)]
     nsteps = 5
     grads = []
@@ -287,7 +288,7 @@ def test_step_many_matches_separate_steps():
 
 
 def test_step_many_rejects_a_repeated_handle():
-    wl = CONFIGS[0]
+    wl = TINY_F32
     lib = make_lib(wl)
     W = dev(init_weights(wl), wl.dtype)
     G = dev(GradStream(wl).next(), wl.dtype)
@@ -300,7 +301,7 @@ def test_step_many_rejects_a_repeated_handle():
 
 LRF_CASES = [
     ("bf16-slab-48x25", custom((6, 5, 48, 25), "bf16", (3, 3, 24, 13), 0.05, T=3)),
-    ("config1", CONFIGS[1]),
+    ("fp32-32x32x16x16", F32_32x32x16x16),
     ("c64-small", custom((12, 10, 9), "c64", (5, 4, 3), 0.05, T=3)),
     ("f16-5mode", custom((9, 7, 5, 11, 4), "f16", (4, 3, 5, 2, 3), 0.05, T=3)),
     ("bf16-slab3", custom((2, 16, 48, 25), "bf16", (1, 8, 24, 13), 0.05, T=3)),

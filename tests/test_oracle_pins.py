@@ -14,7 +14,8 @@ import pytest
 import torch
 
 import oracle as O
-from synth import CONFIGS, GradStream, init_weights
+from synth import (TINY_F32, F32_32x32x16x16, F16_4x64x64x64x64, C64_64x64x64x33, BF16_64x64x48x48x25,
+                   GradStream, init_weights)
 from synth.gen import custom
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
