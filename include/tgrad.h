@@ -2,13 +2,13 @@
  * tgrad.h - C ABI of the TensorGRaD optimizer step on AMD MI355X (gfx950).
  *
  * One handle optimises one weight tensor W of shape (I_1, ..., I_d) with the
- * TensorGRaD step: the gradient G is split into a sparse part S on an index set
- * Omega (the k = floor(rho * N) largest |G| entries, extracted first) and a Tucker
- * low-rank part of the residual R = G - scatter(S); Adam runs on the Tucker core and
- * on the sparse values; the update is reconstructed by mode-wise products with the
- * sparse update scatter-added into the same buffer, and W is updated in place.
- * Omega and the Tucker factors are refreshed every T steps (top-k by magnitude,
- * HOSVD from mode-n Gram matrices).
+ * TensorGRaD step. The gradient G splits into a sparse part S, held on an index set
+ * Omega (the k = floor(rho * N) entries of largest |G|, taken out first), and a Tucker
+ * low-rank part of what remains, R = G - scatter(S). Adam keeps its moments on the
+ * small Tucker core and on the k sparse values. The full-size update comes back
+ * through one factor product per mode; the sparse update is added into that same
+ * buffer, and W is then updated in place. Omega and the factors are recomputed every
+ * T steps: a top-k by magnitude, and an HOSVD from each mode's Gram matrix.
  *
  * Sources (no code exists on them): the nullthought.net summary of "TensorGRaD:
  * Tensor Gradient Robust Decomposition for Memory-Efficient Neural Operator
@@ -65,7 +65,8 @@ enum tgrad_status {
  *   ndim            number of modes d, 1..8
  *   shape[d]        I_n >= 1; N = prod I_n must be < 2^32
  *   tucker_ranks[d] r_n in [1, I_n]. r_n == I_n keeps mode n uncompressed (identity
- *                   factor, no mode product); r_n < I_n needs I_n <= 64.
+ *                   factor, no mode product); r_n < I_n needs I_n <= 64 and
+ *                   r_n <= N / I_n (the rank of the mode-n unfolding).
  *   dtype           enum tgrad_dtype of W and G
  *   sparse_ratio    rho in [0, 1]; k = floor(rho * N) computed in IEEE double
  *   T               refresh period >= 1: a refresh runs before every step t with
@@ -91,6 +92,7 @@ int tgrad_init(tgrad_t **out, int ndim, const int64_t *shape, const int64_t *tuc
  *   order; pith.science Theorem 2).
  * Both buffers must stay valid until the work on `stream` completes.
  * Errors: TGRAD_EINVAL (null handle/pointer, grad not 16-byte aligned), TGRAD_EHIP.
+ * On an error t is not advanced (a refresh that completed for this t stays valid).
  */
 int tgrad_step(tgrad_t *h, void *weight, const void *grad, void *stream);
 
@@ -140,8 +142,15 @@ typedef struct tgrad_info {
   int64_t ranks[TGRAD_MAX_NDIM];
   int64_t state_bytes;      /* moments, core, factors, Omega (optimizer state) */
   int64_t workspace_bytes;  /* transient buffers owned by the handle */
+  /* The eigensolver at the last refresh (0 before any): the most Jacobi sweeps any mode
+   * took to reach its off-diagonal bound, and the number of modes that reached the
+   * sweep cap first (their factors are then less accurate than the bound promises). */
+  int64_t eig_sweeps_max;
+  int64_t eig_unconverged;
 } tgrad_info;
 
+/* Synchronises the device once the handle has refreshed (to read the eigensolver
+ * report). Errors: TGRAD_EINVAL, TGRAD_EHIP. */
 int tgrad_get_info(const tgrad_t *h, tgrad_info *out);
 
 /* Omega, k uint32 linear indices ascending. cap = capacity of out (elements). */
@@ -165,6 +174,15 @@ int tgrad_get_moments(tgrad_t *h, float *m_core, float *v_core, float *m_sparse,
 int tgrad_set_omega(tgrad_t *h, const uint32_t *omega, int64_t k);
 int tgrad_set_factor(tgrad_t *h, int mode, const float *U, int64_t n_floats);
 int tgrad_mark_refreshed(tgrad_t *h);
+
+/* Test hook: while `delta` is set, every step also writes its fp32 update before the
+ * weight rounding, Delta = Delta_L + lambda N_S at Omega (the value W * decay - lr * Delta
+ * is rounded from), into `delta`: a caller-owned device buffer of N * P floats (P = 2
+ * for complex64, interleaved), 16-byte aligned, valid until the stream's work is done.
+ * The kernels that write it are separate instantiations of the weight-update launches,
+ * with the same arithmetic; W is updated as usual. NULL turns the capture off.
+ * Errors: TGRAD_EINVAL (NULL handle, misaligned buffer). */
+int tgrad_debug_capture_delta(tgrad_t *h, float *delta);
 
 /* Test / benchmark hook: when the last two modes are both compressed and a slab of
  * them fits in LDS, the projection's first two mode products and the reconstruction's
@@ -256,11 +274,13 @@ int tgrad_get_options(const tgrad_t *h, tgrad_options *out);
  * count and refresh mark, Omega, every U(n) with its Gram eigenvalues, and the core and
  * sparse Adam moments. tgrad_state_size gives its length (-1 for a NULL handle).
  * tgrad_save_state writes it into `buf` (cap >= that size, host memory).
+ * The header also records T, lr, betas, eps and every tgrad_options field.
  * tgrad_load_state restores it into a handle created with the same shape, Tucker ranks,
- * dtype and sparse_ratio (hyper-parameters lr, betas, eps, T are the new handle's), after
- * which steps continue exactly as they would have in the saved handle.
+ * dtype, sparse_ratio, T, betas and eps, and set to the same options; only the learning
+ * rate may differ (the loading handle's lr is used, as a schedule would change it).
+ * Steps then continue exactly as they would have in the saved handle.
  * Both synchronise the device. Errors: TGRAD_EINVAL (NULL, too small a buffer, a size,
- * header, shape or Omega that does not match), TGRAD_EHIP. */
+ * header, shape, hyper-parameter, option or Omega that does not match), TGRAD_EHIP. */
 int64_t tgrad_state_size(tgrad_t *h);
 int tgrad_save_state(tgrad_t *h, void *buf, int64_t cap);
 int tgrad_load_state(tgrad_t *h, const void *buf, int64_t size);

@@ -34,7 +34,8 @@ class Info(ctypes.Structure):
                 ("k", ctypes.c_int64), ("core_numel", ctypes.c_int64), ("T", ctypes.c_int64),
                 ("t", ctypes.c_int64), ("shape", ctypes.c_int64 * MAX_NDIM),
                 ("ranks", ctypes.c_int64 * MAX_NDIM), ("state_bytes", ctypes.c_int64),
-                ("workspace_bytes", ctypes.c_int64)]
+                ("workspace_bytes", ctypes.c_int64), ("eig_sweeps_max", ctypes.c_int64),
+                ("eig_unconverged", ctypes.c_int64)]
 
 
 SELECT_TOPK, SELECT_RANDK = 0, 1
@@ -73,6 +74,7 @@ SIGNATURES = [
     ("tgrad_set_omega", ctypes.c_int, [_P, _P, _I64]),
     ("tgrad_set_factor", ctypes.c_int, [_P, ctypes.c_int, _P, _I64]),
     ("tgrad_mark_refreshed", ctypes.c_int, [_P]),
+    ("tgrad_debug_capture_delta", ctypes.c_int, [_P, _P]),
     ("tgrad_set_fusion", ctypes.c_int, [_P, ctypes.c_int]),
     ("tgrad_set_gram_fusion", ctypes.c_int, [_P, ctypes.c_int]),
     ("tgrad_set_pair_fusion", ctypes.c_int, [_P, ctypes.c_int]),
@@ -119,6 +121,9 @@ def step_many(handles, weights, grads, stream=None):
     n = len(handles)
     if len(weights) != n or len(grads) != n:
         raise ValueError("handles, weights and grads differ in length")
+    for h, w, g in zip(handles, weights, grads):
+        h._check_tensor(w, "weight")
+        h._check_tensor(g, "grad")
     lib = load_library()
     hs = (_P * max(n, 1))(*[h._h.value for h in handles])
     ws = (_P * max(n, 1))(*[w.data_ptr() for w in weights])
@@ -158,6 +163,8 @@ class TGrad:
             raise TGradError(f"tgrad_init: {self._lib.tgrad_status_string(rc).decode()}")
         self._h = h
         self.info = self.get_info()
+        import torch
+        self.device_index = torch.cuda.current_device() if torch.cuda.is_available() else -1
 
     # ---------------------------------------------------------------- lifecycle
     def close(self):
@@ -186,15 +193,54 @@ class TGrad:
             return ctypes.c_void_p(stream)
         return ctypes.c_void_p(stream.cuda_stream)
 
+    def _check_tensor(self, x, what: str):
+        """The library reads and writes N elements of the handle's dtype at x's address:
+        refuse anything that is not exactly such a buffer on the handle's device."""
+        import torch
+        if not isinstance(x, torch.Tensor):
+            raise ValueError(f"{what}: expected a torch.Tensor, got {type(x).__name__}")
+        if not x.is_cuda:
+            raise ValueError(f"{what}: must be a GPU tensor")
+        if x.device.index != self.device_index:
+            raise ValueError(f"{what}: on cuda:{x.device.index}, the handle is on cuda:{self.device_index}")
+        if x.dtype != torch_dtype(self.dtype):
+            raise ValueError(f"{what}: dtype {x.dtype}, the handle expects {torch_dtype(self.dtype)}")
+        n = int(np.prod(self.shape, dtype=np.int64))
+        if x.numel() != n:
+            raise ValueError(f"{what}: {x.numel()} elements, the handle expects {n}")
+        if not x.is_contiguous():
+            raise ValueError(f"{what}: must be contiguous")
+
     # ---------------------------------------------------------------- hot path
     def step(self, weight, grad, stream=None):
+        self._check_tensor(weight, "weight")
+        self._check_tensor(grad, "grad")
         self._check(self._lib.tgrad_step(self._h, ctypes.c_void_p(weight.data_ptr()),
                                          ctypes.c_void_p(grad.data_ptr()), self._stream(stream)),
                     "tgrad_step")
 
     def refresh(self, grad, stream=None):
+        self._check_tensor(grad, "grad")
         self._check(self._lib.tgrad_refresh(self._h, ctypes.c_void_p(grad.data_ptr()),
                                             self._stream(stream)), "tgrad_refresh")
+
+    def capture_delta(self, delta):
+        """Test hook (tgrad_debug_capture_delta): while set, every step also writes its
+        fp32 update before the weight rounding into `delta` (an fp32 GPU tensor of N * P
+        values); None turns it off. The tensor must outlive the steps that write it."""
+        import torch
+        if delta is None:
+            self._check(self._lib.tgrad_debug_capture_delta(self._h, None), "tgrad_debug_capture_delta")
+            self._delta = None
+            return
+        n = int(np.prod(self.shape, dtype=np.int64)) * self.P
+        if (not isinstance(delta, torch.Tensor) or not delta.is_cuda or delta.dtype != torch.float32
+                or delta.numel() != n or not delta.is_contiguous()
+                or delta.device.index != self.device_index):
+            raise ValueError(f"delta: needs a contiguous float32 GPU tensor of {n} values")
+        self._check(self._lib.tgrad_debug_capture_delta(self._h, ctypes.c_void_p(delta.data_ptr())),
+                    "tgrad_debug_capture_delta")
+        self._delta = delta     # kept alive while the library may write it
 
     # ---------------------------------------------------------------- introspection
     def get_info(self) -> Info:

@@ -10,7 +10,8 @@
 // (A <- J^H A) are applied. Hermitian rotations first turn a_pq real with a phase on
 // column q, then apply the real rotation. Sweeps stop when the off-diagonal energy is
 // below 1e-20 of the total (an off-diagonal norm of 1e-10 of the matrix norm, so an
-// eigenvector errs by about 1e-10 over its relative eigengap), or after 40 sweeps.
+// eigenvector errs by about 1e-10 over its relative eigengap), or after MAX_SWEEPS
+// sweeps; each matrix reports the sweeps it took, or -1 when the cap came first.
 //
 // Outputs (pages silent on eigenvector order, sign and phase): eigenvalues descending
 // (equal values keep index order); each selected column scaled by a unit scalar so its
@@ -24,6 +25,7 @@ namespace tg {
 namespace {
 
 constexpr int NTH = 256;
+constexpr int MAX_SWEEPS = 40;
 
 struct EK1 {
   const double* gram;
@@ -31,6 +33,7 @@ struct EK1 {
   float* Mproj;
   float* Mrec;
   double* eigvals;
+  int* status;
   uint32_t n, r;
 };
 // One workgroup per matrix; up to 8 matrices (one per compressed mode) per launch.
@@ -96,7 +99,8 @@ __global__ void __launch_bounds__(NTH) k_eig(EK kk) {
 
   const uint32_t m = n + (n & 1u);   // even number of players; player n is a bye
   const uint32_t half = m / 2;
-  for (int sweep = 0; sweep < 40; ++sweep) {
+  int sweeps = -1;
+  for (int sweep = 0;; ++sweep) {
     double off = 0.0, tot = 0.0;
     for (uint32_t idx0 = tid; idx0 < n * n; idx0 += NTH) {
       const uint32_t i = idx0 / n, j = idx0 - i * n;
@@ -107,7 +111,11 @@ __global__ void __launch_bounds__(NTH) k_eig(EK kk) {
     }
     off = block_sum(off, red);
     tot = block_sum(tot, red);
-    if (!(off > 1e-20 * tot)) break;
+    if (!(off > 1e-20 * tot)) {
+      sweeps = sweep;
+      break;
+    }
+    if (sweep == MAX_SWEEPS) break;
 
     for (uint32_t round = 0; round + 1 < m; ++round) {
       if ((uint32_t)tid < half) {
@@ -214,6 +222,7 @@ __global__ void __launch_bounds__(NTH) k_eig(EK kk) {
     }
   }
 
+  if (tid == 0) *k.status = sweeps;
   // Descending order of the diagonal, equal values in index order.
   if (tid == 0) {
     uint64_t used = 0;
@@ -335,7 +344,8 @@ __global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
     vb[h] = t < n * half ? (int)(t / n) : -1;
     vi[h] = t < n * half ? t - (t / n) * n : 0u;
   }
-  for (int sweep = 0; sweep < 40; ++sweep) {
+  int sweeps = -1;
+  for (int sweep = 0;; ++sweep) {
     double off = 0.0, tot = 0.0;
     for (uint32_t idx0 = tid; idx0 < n * n; idx0 += NTS) {
       const uint32_t i = idx0 / n, j = idx0 - i * n;
@@ -356,7 +366,11 @@ __global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
       off += red[w];
       tot += red[16 + w];
     }
-    if (!(off > 1e-20 * tot)) break;
+    if (!(off > 1e-20 * tot)) {
+      sweeps = sweep;
+      break;
+    }
+    if (sweep == MAX_SWEEPS) break;
 
     for (uint32_t round = 0; round + 1 < m; ++round) {
       // pair j of this round: the players at positions j and m - 1 - j of the round-robin
@@ -451,6 +465,7 @@ __global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
     }
   }
 
+  if (tid == 0) *k.status = sweeps;
   // Descending order of the diagonal, equal values in index order: rank of each entry.
   if (tid < n) {
     const double d = A[tid * LD + tid];
@@ -510,6 +525,7 @@ hipError_t launch_eig(const EigArgs* e, int count, hipStream_t s) {
     k.m[i].Mproj = e[i].Mproj;
     k.m[i].Mrec = e[i].Mrec;
     k.m[i].eigvals = e[i].eigvals;
+    k.m[i].status = e[i].status;
     k.m[i].n = e[i].I;
     k.m[i].r = e[i].r;
     const size_t b = eig_lds_bytes(e[i].I, e[i].P);

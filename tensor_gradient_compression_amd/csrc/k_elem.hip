@@ -112,7 +112,7 @@ __global__ void __launch_bounds__(256) k_apply_dense(WT* __restrict__ W,
                                                      const uint32_t* __restrict__ rank,
                                                      const float* __restrict__ us, uint64_t N,
                                                      float lr, float decay,
-                                                     int has_sparse) {
+                                                     int has_sparse, float* __restrict__ delta) {
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   for (uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; e < N; e += stride) {
     float d[P];
@@ -130,6 +130,7 @@ __global__ void __launch_bounds__(256) k_apply_dense(WT* __restrict__ W,
     for (int p = 0; p < P; ++p) {
       const float w = to_f32(W[e * P + p]);
       W[e * P + p] = from_f32<WT>(w * decay - lr * d[p]);
+      if (delta) delta[e * P + p] = d[p];   // test capture of the fp32 update
     }
   }
 }
@@ -204,24 +205,24 @@ hipError_t launch_adam(int core_dt, const void* g_core, float* u_core, float* m_
 
 hipError_t launch_apply_dense(int dt, void* W, const float* u_core, const uint64_t* mask,
                               const uint32_t* rank, const float* u_s, uint64_t N, float lr,
-                              float decay, int has_sparse, hipStream_t s) {
+                              float decay, int has_sparse, float* delta, hipStream_t s) {
   const unsigned b = grid_for(N, 256, 8192);
   switch (dt) {
     case DT_F32:
       k_apply_dense<float, 1><<<b, 256, 0, s>>>((float*)W, u_core, mask, rank, u_s, N, lr,
-                                                decay, has_sparse);
+                                                decay, has_sparse, delta);
       break;
     case DT_F16:
       k_apply_dense<_Float16, 1><<<b, 256, 0, s>>>((_Float16*)W, u_core, mask, rank, u_s, N, lr,
-                                                   decay, has_sparse);
+                                                   decay, has_sparse, delta);
       break;
     case DT_BF16:
       k_apply_dense<bf16_t, 1><<<b, 256, 0, s>>>((bf16_t*)W, u_core, mask, rank, u_s, N, lr,
-                                                 decay, has_sparse);
+                                                 decay, has_sparse, delta);
       break;
     case DT_C64:
       k_apply_dense<float, 2><<<b, 256, 0, s>>>((float*)W, u_core, mask, rank, u_s, N, lr,
-                                                decay, has_sparse);
+                                                decay, has_sparse, delta);
       break;
     default: return hipErrorInvalidValue;
   }

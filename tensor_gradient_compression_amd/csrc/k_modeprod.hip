@@ -31,6 +31,8 @@
 // output looks up its membership bit and rank (nullthought summary section 3: the
 // sparse update is scatter-added after the low-rank reconstruction so that two full
 // tensors never coexist; here the full Delta never exists at all).
+// EPI: 0 stores, 1 applies, 2 applies and also stores the fp32 update Delta (after the
+// sparse merge, before the weight rounding) to a test buffer.
 // Tiles whose transfer is not 16-byte aligned fall back to plain loads and stores.
 #include <algorithm>
 
@@ -55,6 +57,7 @@ struct MPK {
   const uint32_t* rank;
   const float* uS;
   const uint32_t* omega;   // Omega ascending (contiguous-range merge)
+  float* delta;            // EPI == 2: the fp32 update (after the sparse merge) is also stored here
   uint64_t kS;             // |Omega|
   uint64_t N;              // elements of the output tensor (apply)
   uint64_t ntiles;
@@ -170,7 +173,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod(MPK k) {
     return k.dma_in && (g.len_in * sizeof(XT)) % 16 == 0;
   };
   auto can_dma_w = [&](const TileGeo& g) {
-    return EPI == 1 && k.dma_w && (g.len_out * sizeof(WT)) % 16 == 0;
+    return EPI >= 1 && k.dma_w && (g.len_out * sizeof(WT)) % 16 == 0;
   };
   auto issue = [&](const TileGeo& g, int buf) {
     unsigned char* dx = lds + (buf ? k.off_x1 : k.off_x0);
@@ -180,7 +183,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod(MPK k) {
       else
         dma_tile<XT, 0>(X + g.base_in, 1, 0, g.len_in, dx);
     }
-    if (EPI == 1 && can_dma_w(g)) {
+    if (EPI >= 1 && can_dma_w(g)) {
       unsigned char* dw = lds + (buf ? k.off_w1 : k.off_w0);
       const WT* W = (const WT*)k.W;
       if (k.wide)
@@ -194,7 +197,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod(MPK k) {
   // entries are one contiguous range [j0, j1) of the sorted list. The range of the next
   // tile is looked up when its transfer is issued, and the current tile's (index,
   // update) pairs are loaded into registers before the multiply.
-  const bool merged = (EPI == 1) && k.has_sparse && !k.wide;
+  const bool merged = (EPI >= 1) && k.has_sparse && !k.wide;
   constexpr int NSR = 2;                         // Omega entries per thread in registers
   // Omega rank of element e (how many Omega entries lie below e). e is uniform over the
   // workgroup and mask/rank are read-only here, so the words come in by scalar loads:
@@ -265,7 +268,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod(MPK k) {
       }
       filled = true;
     }
-    if (EPI == 1 && !can_dma_w(gc)) {
+    if (EPI >= 1 && !can_dma_w(gc)) {
       WT* d = (WT*)bw;
       const WT* W = (const WT*)k.W;
       if (k.wide) {
@@ -357,7 +360,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod(MPK k) {
     __builtin_amdgcn_s_waitcnt(0);
 
     // stream the output tile out in memory order
-    auto finish = [&](uint64_t gi, float d, float w) -> float {
+    auto merge = [&](uint64_t gi, float d) -> float {
       if (k.has_sparse && !merged) {
         const uint64_t e = gi / P;
         const uint64_t word = k.mask[e >> 6];
@@ -366,7 +369,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod(MPK k) {
           d = d + k.uS[jpos * P + (gi % P)];
         }
       }
-      return w * k.decay - k.lr * d;
+      return d;
     };
     const uint32_t nseg_o = k.wide ? k.R : 1u;
     const uint32_t seg_o = k.wide ? TW : gc.len_out;          // values per segment slot
@@ -395,8 +398,16 @@ __global__ void __launch_bounds__(NTH) k_modeprod(MPK k) {
           const WT* wsrc = (const WT*)&wraw;
           WT wv[VO];
 #pragma unroll
-          for (int e = 0; e < VO; ++e) wv[e] = from_f32<WT>(finish(g0 + e, d[e], to_f32(wsrc[e])));
+          for (int e = 0; e < VO; ++e) {
+            d[e] = merge(g0 + e, d[e]);
+            wv[e] = from_f32<WT>(to_f32(wsrc[e]) * k.decay - k.lr * d[e]);
+          }
           *(uint4*)((WT*)k.W + g0) = *(const uint4*)wv;
+          if (EPI == 2) {
+#pragma unroll
+            for (int e = 0; e < VO; e += 4)
+              *(float4*)&k.delta[g0 + e] = make_float4(d[e], d[e + 1], d[e + 2], d[e + 3]);
+          }
         }
       }
     } else {
@@ -409,7 +420,9 @@ __global__ void __launch_bounds__(NTH) k_modeprod(MPK k) {
           k.Y[gi] = d;
         } else {
           const float w = lds_ld<WT>(bw, seg * rs_w + e);
-          ((WT*)k.W)[gi] = from_f32<WT>(finish(gi, d, w));
+          const float dm = merge(gi, d);
+          ((WT*)k.W)[gi] = from_f32<WT>(w * k.decay - k.lr * dm);
+          if (EPI == 2) k.delta[gi] = dm;
         }
       }
     }
@@ -548,6 +561,7 @@ hipError_t launch_modeprod(const ModeProd& mp, int num_cu, hipStream_t s) {
   k.rank = mp.rank;
   k.uS = mp.uS;
   k.omega = mp.omega;
+  k.delta = mp.delta;
   k.kS = mp.kS;
   k.N = (uint64_t)mp.A * mp.R * mp.B;
   k.ntiles = g.ntiles;
@@ -582,6 +596,15 @@ hipError_t launch_modeprod(const ModeProd& mp, int num_cu, hipStream_t s) {
       case DT_F32: return pick_ncb<float, 1, 0, float>(k, ncb, g.lds, gr, s);
       case DT_F16: return pick_ncb<_Float16, 1, 0, float>(k, ncb, g.lds, gr, s);
       case DT_BF16: return pick_ncb<bf16_t, 1, 0, float>(k, ncb, g.lds, gr, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (mp.delta) {
+    if (mp.P == 2) return pick_ncb<float, 2, 2, float>(k, ncb, g.lds, gr, s);
+    switch (mp.w_dt) {
+      case DT_F32: return pick_ncb<float, 1, 2, float>(k, ncb, g.lds, gr, s);
+      case DT_F16: return pick_ncb<float, 1, 2, _Float16>(k, ncb, g.lds, gr, s);
+      case DT_BF16: return pick_ncb<float, 1, 2, bf16_t>(k, ncb, g.lds, gr, s);
     }
     return hipErrorInvalidValue;
   }

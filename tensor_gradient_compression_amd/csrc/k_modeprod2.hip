@@ -44,6 +44,7 @@ struct MP2K {
   const uint32_t* rank;
   const float* uS;
   const uint32_t* omega;
+  float* delta;           // EPI == 2: the fp32 update after the sparse merge, stored too
   uint64_t kS, N;
   uint64_t ntiles;
   uint32_t A, TA;
@@ -188,7 +189,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
 
   auto can_dma_in = [&](uint32_t nta) { return k.dma_in && (nta * slab_in * sizeof(XT)) % 16 == 0; };
   auto can_dma_w = [&](uint32_t nta) {
-    return EPI == 1 && k.dma_w && (nta * slab_out * sizeof(WT)) % 16 == 0;
+    return EPI >= 1 && k.dma_w && (nta * slab_out * sizeof(WT)) % 16 == 0;
   };
   auto nta_of = [&](uint64_t tile) -> uint32_t {
     const uint64_t a0 = tile * k.TA;
@@ -199,7 +200,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
     const uint64_t a0 = tile * k.TA;
     if (can_dma_in(nta))
       dma_block<XT>(X + a0 * slab_in, nta * slab_in, lds + (buf ? k.off_x1 : k.off_x0));
-    if (EPI == 1 && can_dma_w(nta))
+    if (EPI >= 1 && can_dma_w(nta))
       dma_block<WT>((const WT*)k.W + a0 * slab_out, nta * slab_out,
                     lds + (buf ? k.off_w1 : k.off_w0));
   };
@@ -230,7 +231,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
     const uint64_t word = (uint64_t)r[0] | ((uint64_t)r[1] << 32);
     return r[2] + (uint64_t)__popcll(word & ((1ull << (e & 63)) - 1ull));
   };
-  const bool merged = (EPI == 1) && k.has_sparse;
+  const bool merged = (EPI >= 1) && k.has_sparse;
   // projection: the sparse part leaves the staged input before the first product
   const bool gath = !REC && k.gS != nullptr;
   const bool ranged = merged || gath;
@@ -281,7 +282,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
       for (uint32_t idx = tid; idx < nta * slab_in; idx += NTH) d[idx] = X[a0 * slab_in + idx];
       filled = true;
     }
-    if (EPI == 1 && !can_dma_w(nta)) {
+    if (EPI >= 1 && !can_dma_w(nta)) {
       WT* d = (WT*)bw;
       const WT* W = (const WT*)k.W;
       for (uint32_t idx = tid; idx < nta * slab_out; idx += NTH) d[idx] = W[a0 * slab_out + idx];
@@ -370,6 +371,11 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
 #pragma unroll
           for (int e = 0; e < VO; ++e) wv[e] = from_f32<WT>(to_f32(ws[e]) * k.decay - k.lr * d[e]);
           *(uint4*)((WT*)k.W + gbase + off) = *(const uint4*)wv;
+          if (EPI == 2) {
+#pragma unroll
+            for (int e = 0; e < VO; e += 4)
+              *(float4*)&k.delta[gbase + off + e] = make_float4(d[e], d[e + 1], d[e + 2], d[e + 3]);
+          }
         }
       }
     } else {
@@ -379,6 +385,7 @@ __global__ void __launch_bounds__(NTH) k_modeprod2(MP2K k) {
         } else {
           const float w = to_f32(((const WT*)bw)[q]);
           ((WT*)k.W)[gbase + q] = from_f32<WT>(w * k.decay - k.lr * sO[q]);
+          if (EPI == 2) k.delta[gbase + q] = sO[q];
         }
       }
     }
@@ -513,6 +520,7 @@ hipError_t launch_modeprod2(const ModeProd2& mp, int num_cu, hipStream_t s) {
   k.rank = mp.rank;
   k.uS = mp.uS;
   k.omega = mp.omega;
+  k.delta = mp.delta;
   k.kS = mp.kS;
   // elements the Omega ranks count over: the output (reconstruction), the input (projection)
   k.N = (uint64_t)mp.A * (mp.recon ? (uint64_t)mp.R1 * mp.R2 : (uint64_t)mp.I1 * mp.I2);
@@ -535,6 +543,15 @@ hipError_t launch_modeprod2(const ModeProd2& mp, int num_cu, hipStream_t s) {
   if (!mp.apply)
     return mp.P == 2 ? go2<float, 2, 1, 0, float>(k, g.lds, gr, s)
                      : go2<float, 1, 1, 0, float>(k, g.lds, gr, s);
+  if (mp.delta) {
+    if (mp.P == 2) return go2<float, 2, 1, 2, float>(k, g.lds, gr, s);
+    switch (mp.w_dt) {
+      case DT_F32: return go2<float, 1, 1, 2, float>(k, g.lds, gr, s);
+      case DT_F16: return go2<float, 1, 1, 2, _Float16>(k, g.lds, gr, s);
+      case DT_BF16: return go2<float, 1, 1, 2, bf16_t>(k, g.lds, gr, s);
+    }
+    return hipErrorInvalidValue;
+  }
   if (mp.P == 2) return go2<float, 2, 1, 1, float>(k, g.lds, gr, s);
   switch (mp.w_dt) {
     case DT_F32: return go2<float, 1, 1, 1, float>(k, g.lds, gr, s);

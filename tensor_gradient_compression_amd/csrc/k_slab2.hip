@@ -61,6 +61,7 @@ struct S2K {
   const uint32_t* rank;
   const uint32_t* omega;
   float* S;             // projection: gathered S (written); reconstruction: N_S (read)
+  float* delta;         // reconstruction with CAP: the fp32 update O is stored here too
   uint64_t kS;          // |Omega|; 0: no sparse part
   uint32_t A, I1, I2, R1, R2;
   uint32_t slab_e;      // I1 * I2
@@ -430,8 +431,9 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 8)))
 // v_mfma_f32_16x16x4_f32 straight from fp32 data: pass 1 (mode d-1) with k index
 // j1 = KS1 (lane / 16) + step, pass 2 (mode d) with j2 = 4 (lane / 16) + step; the factor
 // operands stay in registers, and pass 1's row blocks are independent accumulation
-// chains interleaved step by step.
-template <typename WT, int NRB1, int NCB2, int KS1>
+// chains interleaved step by step. CAP (a test instantiation) also stores the fp32
+// update O (after the sparse merge, before the weight rounding) to k.delta.
+template <typename WT, int NRB1, int NCB2, int KS1, bool CAP>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) k_rec2s(S2K k) {
   extern __shared__ float smem[];
   const uint32_t lane = threadIdx.x & 63;
@@ -548,6 +550,10 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
         }
       }
       *(uint4*)((WT*)k.W + out_prev + 8 * q) = *(const uint4*)o;
+      if constexpr (CAP) {
+        *(f4*)(k.delta + out_prev + 8 * q) = o0;
+        *(f4*)(k.delta + out_prev + 8 * q + 4) = o1;
+      }
     }
     if (i == cnt) return true;
     wait_lgkm0();
@@ -664,10 +670,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 // feed pass 2 directly: the 16x16 MFMA result layout (rows 4 (lane / 16) + v, column
 // lane % 16) is pass 2's B-operand layout when its k index runs over rows in the order
 // (block, v, lane / 16).
-#ifndef TG_WPB3
-#define TG_WPB3 16
-#endif
-constexpr int WPB3 = TG_WPB3;
+constexpr int WPB3 = 16;
 constexpr int NT3 = WPB3 * 64;
 
 struct S3K {
@@ -1143,30 +1146,30 @@ hipError_t proj_go(const Plan2s& p, hipStream_t s) {
     default: return proj_nrb2<XT, 4>(p, s);
   }
 }
-template <typename WT, int NRB1, int NCB2>
+template <typename WT, int NRB1, int NCB2, bool CAP>
 hipError_t rec_ks(const Plan2s& p, hipStream_t s) {
   switch ((p.k.R1 + 3) / 4) {
     case 1:
-    case 2: return launch2s(k_rec2s<WT, NRB1, NCB2, 2>, p, s);
+    case 2: return launch2s(k_rec2s<WT, NRB1, NCB2, 2, CAP>, p, s);
     case 3:
-    case 4: return launch2s(k_rec2s<WT, NRB1, NCB2, 4>, p, s);
+    case 4: return launch2s(k_rec2s<WT, NRB1, NCB2, 4, CAP>, p, s);
     case 5:
-    case 6: return launch2s(k_rec2s<WT, NRB1, NCB2, 6>, p, s);
-    default: return launch2s(k_rec2s<WT, NRB1, NCB2, 8>, p, s);
+    case 6: return launch2s(k_rec2s<WT, NRB1, NCB2, 6, CAP>, p, s);
+    default: return launch2s(k_rec2s<WT, NRB1, NCB2, 8, CAP>, p, s);
   }
 }
-template <typename WT, int NRB1>
+template <typename WT, int NRB1, bool CAP>
 hipError_t rec_ncb(const Plan2s& p, hipStream_t s) {
-  if (p.nrb2 == 1) return rec_ks<WT, NRB1, 1>(p, s);
-  return rec_ks<WT, NRB1, 2>(p, s);
+  if (p.nrb2 == 1) return rec_ks<WT, NRB1, 1, CAP>(p, s);
+  return rec_ks<WT, NRB1, 2, CAP>(p, s);
 }
-template <typename WT>
+template <typename WT, bool CAP>
 hipError_t rec_go(const Plan2s& p, hipStream_t s) {
   switch (p.nrb1) {
-    case 1: return rec_ncb<WT, 1>(p, s);
-    case 2: return rec_ncb<WT, 2>(p, s);
-    case 3: return rec_ncb<WT, 3>(p, s);
-    default: return rec_ncb<WT, 4>(p, s);
+    case 1: return rec_ncb<WT, 1, CAP>(p, s);
+    case 2: return rec_ncb<WT, 2, CAP>(p, s);
+    case 3: return rec_ncb<WT, 3, CAP>(p, s);
+    default: return rec_ncb<WT, 4, CAP>(p, s);
   }
 }
 
@@ -1216,7 +1219,10 @@ hipError_t launch_slab2(const ModeProd2& mp, int num_cu, hipStream_t s) {
   k.W = mp.W;
   k.S = const_cast<float*>(mp.uS);
   k.kS = mp.has_sparse ? mp.kS : 0;
-  return mp.w_dt == DT_BF16 ? rec_go<bf16_t>(p, s) : rec_go<_Float16>(p, s);
+  k.delta = mp.delta;
+  if (mp.delta)
+    return mp.w_dt == DT_BF16 ? rec_go<bf16_t, true>(p, s) : rec_go<_Float16, true>(p, s);
+  return mp.w_dt == DT_BF16 ? rec_go<bf16_t, false>(p, s) : rec_go<_Float16, false>(p, s);
 }
 
 }  // namespace tg

@@ -108,9 +108,11 @@ hipError_t launch_adam(int core_dt, const void* g_core, float* u_core, float* m_
                        uint64_t n_s, AdamK a, hipStream_t s);
 // W <- round(fp32(W) * decay - lr * Delta) (decay = fp32(1 - lr * weight_decay); 1 exactly
 // without decay)
+// delta != NULL (a test capture): Delta, the fp32 update after the sparse merge, is
+// also written there (N * P floats).
 hipError_t launch_apply_dense(int dt, void* W, const float* u_core, const uint64_t* mask,
                               const uint32_t* rank, const float* u_s, uint64_t N, float lr,
-                              float decay, int has_sparse, hipStream_t s);
+                              float decay, int has_sparse, float* delta, hipStream_t s);
 
 // Mode product Y[a, jj, b] = sum_kk M[jj, kk] X[a, kk, b] over the (A, I, B, P) view.
 struct ModeProd {
@@ -133,6 +135,9 @@ struct ModeProd {
   float decay;
   int has_sparse;
   int force_ncb;           // 0: choose the tile width automatically
+  // apply only, a test capture: when not NULL the fp32 update (acc + uS@Omega) is also
+  // stored here, one float per output value (a separate kernel instantiation)
+  float* delta;
 };
 size_t modeprod_lds_bytes(const ModeProd& mp);
 hipError_t launch_modeprod(const ModeProd& mp, int num_cu, hipStream_t s);
@@ -167,6 +172,9 @@ struct ModeProd2 {
   // A then counts (unit, i0) slabs
   uint32_t I0, R0;
   const float* M0;
+  // reconstruction with apply, a test capture: when not NULL the fp32 update after the
+  // sparse merge is also stored here (N * P floats; a separate kernel instantiation)
+  float* delta;
 };
 uint32_t modeprod2_tile(const ModeProd2& mp);   // 0: does not fit
 hipError_t launch_modeprod2(const ModeProd2& mp, int num_cu, hipStream_t s);
@@ -242,6 +250,7 @@ struct EigArgs {
   float* Mproj;  // (r*P) x (I*P)
   float* Mrec;   // (I*P) x (r*P)
   double* eigvals;  // I
+  int* status;      // written: sweeps taken, or -1 if the sweep cap came first
 };
 size_t eig_lds_bytes(uint32_t I, uint32_t P);
 hipError_t launch_eig(const EigArgs* e, int count, hipStream_t s);   // one workgroup each

@@ -86,6 +86,13 @@ struct tgrad_handle {
   uint64_t* mask_prev = nullptr;
   uint32_t* rank_prev = nullptr;
   float *mS_alt = nullptr, *vS_alt = nullptr;
+  // test capture (tgrad_debug_capture_delta): the fp32 update of every step is also
+  // written here (caller's device buffer, N * P floats) while it is set
+  float* delta_cap = nullptr;
+  // eigensolver report of the last refresh: per compressed mode, the sweeps it took, or
+  // -1 when the sweep cap was reached before the off-diagonal bound (device, 8 ints)
+  int* eig_status = nullptr;
+  bool refreshed_once = false;
 
   std::vector<void*> allocs;
   int64_t state_bytes = 0, ws_bytes = 0;
@@ -342,6 +349,7 @@ bool use_proj3(const tgrad_t* h, const void* X0) {
 int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s);
 int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, float* out,
                        hipStream_t s);
+int step_body(tgrad_t* h, void* weight, const void* grad, int64_t t, hipStream_t s);
 
 // Omega (+ bitmask, ranks) as the k largest keys of `src` (storage type dt), or a random
 // k-subset; optionally the residual (src with Omega zeroed) written to `resid`. With
@@ -423,7 +431,9 @@ int do_refresh(tgrad_t* h, const void* grad, hipStream_t s) {
       g.out = out;
       HIPCHK(h, launch_gram(g, h->num_cu, s, mark_cb, h));
     }
-    EigArgs& e = eig[ne++];
+    EigArgs& e = eig[ne];
+    e.status = h->eig_status + ne;
+    ++ne;
     e.gram = out;
     e.I = (uint32_t)h->shape[n];
     e.r = (uint32_t)h->ranks[n];
@@ -454,6 +464,7 @@ int do_refresh(tgrad_t* h, const void* grad, hipStream_t s) {
     }
   }
   h->refreshed_for = h->t + 1;
+  h->refreshed_once = true;
   return TGRAD_OK;
 }
 }  // namespace
@@ -505,6 +516,12 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
     ncore *= (uint64_t)tucker_ranks[i];
     if (N >= (1ull << 32)) return TGRAD_EINVAL;
   }
+  // a compressed mode's rank cannot exceed the rank of its unfolding, N / I_n: the extra
+  // core entries would be zero up to rounding, and Adam turns rounding noise into O(1)
+  // updates there
+  for (int i = 0; i < ndim; ++i)
+    if (tucker_ranks[i] < shape[i] && (uint64_t)tucker_ranks[i] > N / (uint64_t)shape[i])
+      return TGRAD_EINVAL;
   tgrad_t* h = new (std::nothrow) tgrad_t();
   if (!h) return TGRAD_ENOMEM;
   if (hipGetDevice(&h->device) != hipSuccess) {
@@ -661,6 +678,7 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
   }
   h->gram_stride = gmax;
   ok = ok && dalloc(h, &h->gram, gmax * h->fmodes.size(), false);
+  ok = ok && dalloc(h, &h->eig_status, TGRAD_MAX_NDIM, false);
   const uint64_t units = topk_units(N);
   ok = ok && dalloc(h, &h->tw.hist, 2048, false);
   ok = ok && dalloc(h, &h->tw.state, 4, false);
@@ -683,6 +701,7 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
   zero(h->mask, h->nwords * 8);
   zero(h->rank, h->nwords * 4);
   zero(h->omega, h->k * 4);
+  zero(h->eig_status, TGRAD_MAX_NDIM * sizeof(int));
   for (int n : h->fmodes) {
     const uint64_t I = (uint64_t)shape[n], r = (uint64_t)tucker_ranks[n];
     zero(h->U[n], I * r * P * 4);
@@ -931,6 +950,7 @@ int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, fl
       mp.lr = lr;
       mp.decay = decay;
       mp.has_sparse = app && h->k > 0;
+      mp.delta = app ? h->delta_cap : nullptr;
       Mark m(h, app ? KID_RECON_FUSED2_APPLY : KID_RECON_FUSED2);
       if (h->slab2 && slab2_supported(mp, h->num_cu))
         HIPCHK(h, launch_slab2(mp, h->num_cu, s));
@@ -959,6 +979,7 @@ int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, fl
       mp.lr = lr;
       mp.decay = decay;
       mp.has_sparse = app && h->k > 0;
+      mp.delta = app ? h->delta_cap : nullptr;
       Mark m(h, app ? KID_RECON_APPLY : KID_RECONSTRUCT);
       HIPCHK(h, launch_modeprod(mp, h->num_cu, s));
       cur[n] = h->shape[n];
@@ -978,14 +999,23 @@ int tgrad_step(tgrad_t* h, void* weight, const void* grad, void* stream) {
   DevGuard gd(h->device);
   hipStream_t s = (hipStream_t)stream;
   h->cur_stream = s;
-  h->t += 1;
-  const int64_t t = h->t;
+  // the step count advances only when every launch of the step has been enqueued, so a
+  // failed call can be repeated (the refresh it needs is then still due)
+  const int64_t t = h->t + 1;
   if ((t - 1) % h->T == 0 && h->refreshed_for != t) {
-    h->t -= 1;                       // the refresh serves step t = (current t) + 1
-    int rc = do_refresh(h, grad, s);
-    h->t += 1;
+    const int rc = do_refresh(h, grad, s);   // serves step h->t + 1 = t
     if (rc != TGRAD_OK) return rc;
   }
+  const int rc = step_body(h, weight, grad, t, s);
+  if (rc == TGRAD_OK) h->t = t;
+  return rc;
+}
+
+}  // extern "C"
+
+namespace {
+
+int step_body(tgrad_t* h, void* weight, const void* grad, int64_t t, hipStream_t s) {
   const uint32_t P = h->P;
   const size_t nf = h->fmodes.size();
   const bool lowrank_first = h->order == TGRAD_ORDER_LOWRANK_FIRST && h->k > 0;
@@ -1045,15 +1075,38 @@ int tgrad_step(tgrad_t* h, void* weight, const void* grad, void* stream) {
     const float decay = (float)(1.0 - h->lr * h->wd);
     Mark m(h, KID_APPLY_DENSE);
     HIPCHK(h, launch_apply_dense(h->dtype, weight, h->ucore, h->mask, h->rank, h->S, h->N, lr,
-                                 decay, h->k > 0, s));
+                                 decay, h->k > 0, h->delta_cap, s));
     return TGRAD_OK;
   }
   return run_reconstruction(h, h->ucore, true, weight, nullptr, s);
 }
 
+}  // namespace
+
+extern "C" {
+
+int tgrad_debug_capture_delta(tgrad_t* h, float* delta) {
+  if (!h) return TGRAD_EINVAL;
+  if (delta && ((uintptr_t)delta & 15u) != 0) return TGRAD_EINVAL;
+  h->delta_cap = delta;
+  return TGRAD_OK;
+}
+
 int tgrad_get_info(const tgrad_t* h, tgrad_info* out) {
   if (!h || !out) return TGRAD_EINVAL;
+  int st[TGRAD_MAX_NDIM] = {0};
+  const int nf = (int)h->fmodes.size();
+  if (h->refreshed_once && nf) {
+    DevGuard g(h->device);
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpy(st, h->eig_status, nf * sizeof(int), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail_hip(const_cast<tgrad_t*>(h), e, "tgrad_get_info");
+  }
   std::memset(out, 0, sizeof(*out));
+  for (int i = 0; i < nf; ++i) {
+    if (st[i] < 0) out->eig_unconverged += 1;
+    else if (st[i] > out->eig_sweeps_max) out->eig_sweeps_max = st[i];
+  }
   out->ndim = h->d;
   out->dtype = h->dtype;
   out->numel = (int64_t)h->N;
@@ -1153,13 +1206,20 @@ struct CkptHeader {
   int64_t ranks[TGRAD_MAX_NDIM];
   uint64_t k, ncore;
   int64_t t, refreshed_for;
+  // hyper-parameters and options of the saved run (version 2)
+  int64_t T;
+  double lr, beta1, beta2, eps;
+  double weight_decay, sparse_scale;
+  uint64_t seed;
+  int32_t selection, remap, order, pad;
 };
 constexpr char kCkptMagic[8] = {'T', 'G', 'R', 'A', 'D', 'C', 'K', '1'};
+constexpr uint32_t kCkptVersion = 2;
 
 void ckpt_header(const tgrad_t* h, CkptHeader* c) {
   std::memset(c, 0, sizeof(*c));
   std::memcpy(c->magic, kCkptMagic, 8);
-  c->version = 1;
+  c->version = kCkptVersion;
   c->dtype = (uint32_t)h->dtype;
   c->ndim = h->d;
   for (int i = 0; i < h->d; ++i) {
@@ -1170,6 +1230,31 @@ void ckpt_header(const tgrad_t* h, CkptHeader* c) {
   c->ncore = h->ncore;
   c->t = h->t;
   c->refreshed_for = h->refreshed_for;
+  c->T = h->T;
+  c->lr = h->lr;
+  c->beta1 = h->b1;
+  c->beta2 = h->b2;
+  c->eps = h->eps;
+  c->weight_decay = h->wd;
+  c->sparse_scale = h->lam;
+  c->seed = h->seed;
+  c->selection = h->selection;
+  c->remap = h->remap ? 1 : 0;
+  c->order = h->order;
+}
+
+// The saved run and this handle agree on everything that shapes the steps after the
+// resume: tensor layout, Omega size, refresh period, Adam's betas and eps, and every
+// option. The learning rate may differ (a schedule may change it between runs).
+bool ckpt_compatible(const CkptHeader& a, const CkptHeader& b) {
+  return std::memcmp(a.magic, b.magic, 8) == 0 && a.version == b.version && a.dtype == b.dtype &&
+         a.ndim == b.ndim && a.k == b.k && a.ncore == b.ncore &&
+         std::memcmp(a.shape, b.shape, sizeof(a.shape)) == 0 &&
+         std::memcmp(a.ranks, b.ranks, sizeof(a.ranks)) == 0 && a.T == b.T &&
+         a.beta1 == b.beta1 && a.beta2 == b.beta2 && a.eps == b.eps &&
+         a.weight_decay == b.weight_decay && a.sparse_scale == b.sparse_scale &&
+         a.seed == b.seed && a.selection == b.selection && a.remap == b.remap &&
+         a.order == b.order;
 }
 
 // (device pointer, bytes) of every state array in checkpoint order
@@ -1217,12 +1302,7 @@ int tgrad_load_state(tgrad_t* h, const void* buf, int64_t size) {
   CkptHeader mine, theirs;
   ckpt_header(h, &mine);
   std::memcpy(&theirs, buf, sizeof(theirs));
-  if (std::memcmp(theirs.magic, mine.magic, 8) != 0 || theirs.version != mine.version ||
-      theirs.dtype != mine.dtype || theirs.ndim != mine.ndim || theirs.k != mine.k ||
-      theirs.ncore != mine.ncore ||
-      std::memcmp(theirs.shape, mine.shape, sizeof(mine.shape)) != 0 ||
-      std::memcmp(theirs.ranks, mine.ranks, sizeof(mine.ranks)) != 0 || theirs.t < 0)
-    return TGRAD_EINVAL;
+  if (!ckpt_compatible(theirs, mine) || theirs.t < 0) return TGRAD_EINVAL;
   const unsigned char* p = (const unsigned char*)buf + sizeof(CkptHeader);
   // Omega must be ascending and in range, as tgrad_set_omega requires
   const uint32_t* om = (const uint32_t*)p;

@@ -2,8 +2,8 @@
 
 Omega and U(n) come from the oracle, so only the step kernels are compared. Each case
 runs the fused plan with the pair launch and with one launch per mode. Both must meet
-the parity bar of gpu_helpers.weight_check over four steps, and so must the core
-moments. The timing records must show which launches ran. The shapes cover:
+the parity bar of gpu_helpers.weight_check over four steps, with every step's fp32
+update checked (gpu_helpers.checked_step), and so must the core moments. The timing records must show which launches ran. The shapes cover:
 * a pair after the trailing two-mode launch and after the three-mode projection;
 * a pair behind a full-rank leading mode (A > 1);
 * 1 to 4 row blocks of the first product, with 16 to 64 values in its k;
@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import tensor_gradient_compression_amd as tg
-from gpu_helpers import make_lib, make_oracle, weight_check
+from gpu_helpers import CoreSplit, DeltaCapture, checked_step, make_lib, make_oracle, weight_check
 from synth import (TINY_F32, F32_32x32x16x16, F16_4x64x64x64x64, C64_64x64x64x33, BF16_64x64x48x48x25,
                    GradStream, init_weights)
 from synth.gen import custom
@@ -62,14 +62,17 @@ def test_pair_steps_match_oracle(case, pairs):
             lib.set_factor(n, U)
     lib.mark_refreshed()
     lib.timing_enable(True)
+    cap = DeltaCapture(lib, wl)
+    split = CoreSplit(orc)
     W = tg.to_device(W0, wl.dtype)
     Wo = W0
     g = g1
+    slack = 0.0
     for step in range(4):
-        lib.step(W, tg.to_device(g, wl.dtype))
-        Wo = orc.step(Wo, g)
-        torch.cuda.synchronize()
-        weight_check(tg.to_host(W, wl.dtype), Wo, wl.dtype, f"{name} step {step + 1}")
+        what = f"{name}/{'pair' if pairs else 'per-mode'} step {step + 1}"
+        Wo, _ = checked_step(lib, orc, cap, W, Wo, g, wl, what, align=split)
+        slack += wl.lr * 1e-5 * np.abs(orc.last["delta"]).max()
+        weight_check(tg.to_host(W, wl.dtype), Wo, wl.dtype, what, delta_backed=True, slack=slack)
         g = gs.next()
     rec = lib.timing_read()
     got = (rec.get("modeprod_pair_project", (0,))[0], rec.get("modeprod_pair_reconstruct", (0,))[0])

@@ -7,7 +7,8 @@ import pytest
 
 import oracle as O
 import tensor_gradient_compression_amd as tg
-from gpu_helpers import factor_check, make_lib, make_oracle, omega_properties, weight_check
+from gpu_helpers import (DeltaCapture, CoreSplit, apply_check, checked_step, delta_rel, factor_check,
+                         make_lib, make_oracle, omega_properties, weight_check)
 from synth import (TINY_F32, F32_32x32x16x16, F16_4x64x64x64x64, C64_64x64x64x33, BF16_64x64x48x48x25,
                    GradStream, init_weights)
 from synth.gen import custom
@@ -60,6 +61,37 @@ def _topk_inputs():
     cz[3, 3] = cz[0, 0]
     cz[5, 5] = np.conj(cz[0, 0])
     cases.append(("c64-dup-magnitudes", cz.shape, "c64", 0.2, cz))
+    # non-finite values: NaN (several payloads and signs) ranks above +-Inf, which rank
+    # above every finite value; ties among them go to the lowest index
+    for dtype in ("f32", "f16", "bf16"):
+        x = r.standard_normal((13, 11, 7)).astype(np.float32)
+        x.reshape(-1)[[5, 77, 300, 811]] = np.inf
+        x.reshape(-1)[[9, 500]] = -np.inf
+        x.reshape(-1)[[40, 41, 900]] = 1e30 if dtype != "f16" else 6e4
+        enc = O.encode(x, dtype).reshape(-1)
+        bits = enc.view(np.uint32 if dtype == "f32" else np.uint16)
+        if dtype == "f32":
+            nan_bits = [0x7FC00000, 0xFFC00001, 0x7F800001, 0x7FFFFFFF]
+        elif dtype == "f16":
+            nan_bits = [0x7E00, 0xFE01, 0x7C01, 0x7FFF]
+        else:
+            nan_bits = [0x7FC0, 0xFFC1, 0x7F81, 0x7FFF]
+        for pos, nb in zip((3, 150, 151, 1000), nan_bits):
+            bits[pos] = nb
+        enc = enc.reshape(x.shape)
+        for k in (1, 4, 9, 12, 200):
+            cases.append((f"{dtype}-nonfinite-k{k}", x.shape, dtype, k / x.size + 1e-12, enc))
+    zc = (r.standard_normal((17, 19)) + 1j * r.standard_normal((17, 19))).astype(np.complex64)
+    f = zc.reshape(-1)
+    f[2] = complex(np.nan, 0.0)
+    f[30] = complex(1.0, np.nan)
+    f[31] = complex(np.inf, np.nan)
+    f[60] = complex(np.inf, 0.0)
+    f[61] = complex(0.0, -np.inf)
+    f[90] = complex(-np.inf, np.inf)
+    f[100] = complex(3e38, 3e38)      # |z|^2 overflows fp32 but not fp64
+    for k in (1, 3, 6, 8, 40):
+        cases.append((f"c64-nonfinite-k{k}", zc.shape, "c64", k / zc.size + 1e-12, zc))
     return cases
 
 
@@ -169,18 +201,22 @@ def test_steps_with_pinned_omega_and_factors(case, fused):
         if U is not None:
             lib.set_factor(n, U)
     lib.mark_refreshed()
+    cap = DeltaCapture(lib, wl)
+    align = CoreSplit(orc)
     W = dev(W0, wl.dtype)
     Wo = W0
     g = g1
+    slack = 0.0
     for step in range(4):
         G = dev(g, wl.dtype)
-        lib.step(W, G)
-        Wo = orc.step(Wo, g)
-        torch.cuda.synchronize()
+        what = f"{name}/plan{fused} step {step + 1}"
+        Wo, _ = checked_step(lib, orc, cap, W, Wo, g, wl, what, G=G, align=align)
+        slack += wl.lr * 1e-5 * np.abs(orc.last["delta"]).max()
         # the gradient is only read
         assert np.array_equal(host(G, wl.dtype).view(np.uint8), np.ascontiguousarray(g).view(np.uint8)), \
             f"{name}: the step wrote to grad at step {step + 1}"
-        weight_check(host(W, wl.dtype), Wo, wl.dtype, f"{name} step {step + 1}")
+        crit = weight_check(host(W, wl.dtype), Wo, wl.dtype, what, delta_backed=True, slack=slack)
+        print(f"WEIGHTS {what}: {crit}")
         g = gs.next()
     mc, vc, ms, vs = lib.get_moments()
     np.testing.assert_allclose(ms, orc.mS, rtol=1e-6, atol=1e-7)      # sparse path: same inputs
@@ -304,11 +340,17 @@ def test_misaligned_grad_is_rejected():
 def test_checkpoint_resume_is_exact(name, wl):
     """Save after n1 steps, restore into a fresh handle, continue across a refresh:
     weights, moments, Omega, factors and the step count match an uninterrupted run bit
-    for bit. A state for another shape is refused."""
+    for bit, and the resumed run matches the oracle run through all n1 + n2 steps (Omega
+    bit for bit at every refresh, factors within the projector bar, weights within the
+    weight bar). A state for another shape is refused."""
     n1, n2 = 4, 5
     gs = GradStream(wl, seed=5)
     grads = [gs.next() for _ in range(n1 + n2)]
     W0 = init_weights(wl, seed=5)
+    orc = make_oracle(wl, T=4)
+    Wo = W0
+    for g in grads[:n1]:
+        Wo = orc.step(Wo, g)
     a = make_lib(wl, T=4)
     Wa = dev(W0, wl.dtype)
     for g in grads:
@@ -322,9 +364,15 @@ def test_checkpoint_resume_is_exact(name, wl):
     c = make_lib(wl, T=4)
     c.load_state(state)
     assert c.t == n1
-    for g in grads[n1:]:
+    for i, g in enumerate(grads[n1:]):
         c.step(Wb, dev(g, wl.dtype))
+        Wo = orc.step(Wo, g)
+        if (n1 + i) % 4 == 0:     # step n1 + i + 1 refreshed
+            torch.cuda.synchronize()
+            assert np.array_equal(c.get_omega(), orc.omega)
+            factor_check(c, orc)
     torch.cuda.synchronize()
+    weight_check(host(Wb, wl.dtype), Wo, wl.dtype, f"{name} resumed run")
     assert np.array_equal(host(Wa, wl.dtype).view(np.uint8), host(Wb, wl.dtype).view(np.uint8))
     for x, y in zip(a.get_moments(), c.get_moments()):
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
@@ -336,6 +384,33 @@ def test_checkpoint_resume_is_exact(name, wl):
     other = tg.TGrad(tuple(x + 1 for x in wl.shape), wl.ranks, wl.dtype, wl.sparse_ratio, 4)
     with pytest.raises(tg.TGradError, match="invalid argument"):
         other.load_state(state)
+
+
+def test_checkpoint_refuses_other_hyperparameters():
+    """A saved state resumes only into a handle with the same refresh period, Adam betas
+    and eps, and options; a different learning rate (a schedule) is accepted."""
+    wl = F32_32x32x16x16
+    a = make_lib(wl, T=4)
+    W = dev(init_weights(wl, seed=1), wl.dtype)
+    a.step(W, dev(GradStream(wl, seed=1).next(), wl.dtype))
+    state = a.save_state()
+
+    def fresh(T=4, lr=wl.lr, betas=wl.betas, eps=wl.eps, **opts):
+        h = tg.TGrad(wl.shape, wl.ranks, wl.dtype, wl.sparse_ratio, T, lr, betas, eps)
+        if opts:
+            h.set_options(**opts)
+        return h
+
+    for bad in (dict(T=5), dict(betas=(0.8, 0.999)), dict(betas=(0.9, 0.99)), dict(eps=1e-6),
+                dict(selection="randk"), dict(seed=3), dict(weight_decay=1e-4),
+                dict(sparse_scale=0.5), dict(remap_moments=True), dict(order="lowrank_first")):
+        h = fresh(**bad)
+        with pytest.raises(tg.TGradError, match="invalid argument"):
+            h.load_state(state)
+        assert h.t == 0, bad
+    h = fresh(lr=3e-4)
+    h.load_state(state)
+    assert h.t == 1
 
 
 def test_timing_records_every_kernel():
@@ -392,23 +467,31 @@ def test_timing_only_one_kernel():
 # --------------------------------------------------------------------------- full size, bf16 (64,64,48,48,25)
 
 @pytest.mark.timeout(900)
-def test_bf16_64x64x48x48x25_full_size_refresh_and_step():
-    """bf16 (64,64,48,48,25): Omega checked by its complete characterisation (no sort of
-    236M keys), factor projectors against the oracle's fp64 Gram eigenvectors, and the
-    stepped weights at a sampled sub-grid of 4^5 positions against the oracle's step
-    computed with the library's own Omega and factors."""
+def test_bf16_64x64x48x48x25_full_size_two_steps():
+    """bf16 (64,64,48,48,25), the full tensor, two steps in the bench's launch plan.
+
+    Step 1 refreshes: Omega is checked by its complete characterisation (no sort of 236M
+    keys), each factor's projector against the fp64 Gram eigenvectors of the residual.
+    Then the oracle steps with the library's Omega and factors (set into it, as they came
+    from the refresh), and both steps are compared in full (CoreSplit): the core Adam
+    moments (1e-5 of the largest), the fp32 update Delta of every element against the
+    oracle's reconstruction of the library's core update plus its own sparse update
+    (relative max-norm 1e-5), the weight update as the exact rounding of W - lr Delta,
+    all 235.9M weights against the oracle's update of the same W, and the sparse
+    moments."""
     wl = BF16_64x64x48x48x25
-    g = GradStream(wl, seed=0).next()
+    gs = GradStream(wl, seed=0)
+    g = gs.next()
     W0 = init_weights(wl, seed=0)
     lib = make_lib(wl)
+    cap = DeltaCapture(lib, wl)
     G = dev(g, wl.dtype)
     W = dev(W0, wl.dtype)
+    print("CASE bf16-(64,64,48,48,25) step 1 (refresh)", flush=True)
     lib.step(W, G)          # t = 1: refresh, then the step
     torch.cuda.synchronize()
-    Wg = host(W, wl.dtype)
     om = lib.get_omega()
-    keys = O.topk_keys(g, wl.dtype)
-    omega_properties(keys, om, wl.k)
+    omega_properties(O.topk_keys(g, wl.dtype), om, wl.k)
     assert np.array_equal(host(G, wl.dtype).view(np.uint8), g.view(np.uint8))   # only read
     R32 = O.decode(g, wl.dtype).reshape(-1).copy()
     R32[om] = 0
@@ -422,19 +505,46 @@ def test_bf16_64x64x48x48x25_full_size_refresh_and_step():
                      - Uo.astype(np.float64) @ Uo.T.astype(np.float64)).max()
         assert err <= 1e-4, (n, err, gap)
         Us.append(Ug)
-    # oracle step with the library's Omega and factors
-    C = O.project(R, Us).astype(np.float32)
-    uC, _, _ = O.adam(C.reshape(-1), np.zeros(C.size, np.float32), np.zeros(C.size, np.float32), 1,
-                      *wl.betas, wl.eps)
-    S = O.decode(g, wl.dtype).reshape(-1)[om]
-    uS, _, _ = O.adam(S, np.zeros_like(S), np.zeros_like(S), 1, *wl.betas, wl.eps)
-    rng = np.random.default_rng(1)
-    sub = [np.sort(rng.choice(I, 4, replace=False)) for I in wl.shape]
-    DL = O.reconstruct(uC.reshape(wl.ranks), [U[s] for U, s in zip(Us, sub)]).astype(np.float32)
-    idx = np.ravel_multi_index(np.meshgrid(*sub, indexing="ij"), wl.shape).reshape(-1)
-    D = DL.reshape(-1).copy()
-    pos = np.searchsorted(om, idx)
-    hit = (pos < om.size) & (om[np.minimum(pos, om.size - 1)] == idx)
-    D[hit] = D[hit] + uS[pos[hit]]
-    Wexp = O.encode(O.decode(W0.reshape(-1)[idx], wl.dtype) - np.float32(wl.lr) * D, wl.dtype)
-    weight_check(Wg.reshape(-1)[idx], Wexp, wl.dtype, "bf16-(64,64,48,48,25) sampled")
+    del R
+    assert lib.get_info().eig_unconverged == 0
+    # the oracle, stepped with the library's refresh outcome
+    orc = make_oracle(wl)
+    orc.omega = om.copy()
+    orc.factors = Us
+    orc.refreshed_for = 1
+    align = CoreSplit(orc)
+    Wprev, Wo = W0, W0
+    for t in (1, 2):
+        if t == 2:
+            g = gs.next()
+            print("CASE bf16-(64,64,48,48,25) step 2", flush=True)
+            Wprev = host(W, wl.dtype)
+            lib.step(W, dev(g, wl.dtype))
+            torch.cuda.synchronize()
+        Wo = orc.step(Wo, g)
+        dg = cap.host()
+        Wg = host(W, wl.dtype)
+        apply_check(Wprev, Wg, dg, wl.dtype, wl.lr, what=f"step {t}")
+        expected, n_steep, du = align.expected_delta(lib, t)
+        rel = delta_rel(dg, expected)
+        print(f"DELTA bf16-(64,64,48,48,25) step {t}: rel {rel:.3e} (against the oracle's own "
+              f"Delta: {delta_rel(dg, orc.last['delta']):.3e}; steep core entries {n_steep}, "
+              f"max |du| {du:.2e})", flush=True)
+        assert n_steep <= 1e-4 * orc.mC.size, n_steep
+        assert rel <= 1e-5, (t, rel)
+        # every weight against the oracle's update of the same W: the rounding of
+        # W - lr Delta with the oracle's Delta (reconstructed from the library's core
+        # update, as above); at most one bf16 ulp apart where the two fp32 values straddle
+        # a rounding boundary
+        w32 = O.real_view(O.decode(Wprev, wl.dtype))
+        Wexp = O.encode((w32 - np.float32(wl.lr) * expected.astype(np.float32)).reshape(wl.shape),
+                        wl.dtype)
+        slack = wl.lr * 1e-5 * np.abs(expected).max()
+        crit = weight_check(Wg, Wexp, wl.dtype, f"bf16-(64,64,48,48,25) step {t}", delta_backed=True,
+                            slack=slack)
+        print(f"WEIGHTS bf16-(64,64,48,48,25) step {t}: {crit}", flush=True)
+        del expected, w32, Wexp
+        _, _, ms, vs = lib.get_moments()
+        np.testing.assert_allclose(ms, orc.mS, rtol=1e-6, atol=1e-7)
+        np.testing.assert_allclose(vs, orc.vS, rtol=1e-6, atol=1e-12)
+        del dg, Wg, ms, vs

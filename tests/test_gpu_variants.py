@@ -10,7 +10,8 @@ import pytest
 
 import oracle as O
 import tensor_gradient_compression_amd as tg
-from gpu_helpers import factor_check, make_lib, weight_check
+from gpu_helpers import (CoreSplit, DeltaCapture, apply_check, checked_step, delta_rel, factor_check,
+                         make_lib, weight_check)
 from synth import (TINY_F32, F32_32x32x16x16, F16_4x64x64x64x64, C64_64x64x64x33, BF16_64x64x48x48x25,
                    GradStream, init_weights)
 from synth.gen import custom
@@ -287,6 +288,55 @@ def test_step_many_matches_separate_steps():
         assert solo[i].t == many[i].t == nsteps
 
 
+@pytest.mark.timeout(600)
+def test_step_many_four_fp16_layers_match_oracle():
+    """The 4-layer fp16 (64,64,64,64) workload, Tucker ranks (32,32,32,32), 5% sparse,
+    stepped as one tgrad_step_many call per step across two refreshes (T = 2, three
+    steps). Per layer and refresh: Omega bit for bit against the oracle's own refresh and
+    each factor within the projector bar. The oracle then takes the library's factors (as
+    a pinned-factor run), so every step's fp32 update Delta is compared at 1e-5 relative
+    max-norm, the weight update checked as the exact rounding of W - lr Delta, and the
+    weights after the run within the fp16 bar."""
+    wl = F16_4x64x64x64x64
+    L, T, nsteps = wl.layers, 2, 3
+    libs = [make_lib(wl, T=T) for _ in range(L)]
+    orcs = [O.TGradOracle(wl.shape, wl.ranks, wl.dtype, wl.sparse_ratio, T, wl.lr, *wl.betas,
+                          wl.eps) for _ in range(L)]
+    caps = [DeltaCapture(lib, wl) for lib in libs]
+    aligns = [CoreSplit(orc) for orc in orcs]
+    streams = [GradStream(wl, seed=0, layer=l) for l in range(L)]
+    W0s = [init_weights(wl, seed=0, layer=l) for l in range(L)]
+    Ws = [dev(w, wl.dtype) for w in W0s]
+    Wos = list(W0s)
+    for t in range(1, nsteps + 1):
+        gs = [s_.next() for s_ in streams]
+        Wprev = [host(w, wl.dtype) for w in Ws]
+        print(f"CASE step_many 4 x fp16 (64,64,64,64) t={t}", flush=True)
+        tg.step_many(libs, Ws, [dev(g, wl.dtype) for g in gs])
+        torch.cuda.synchronize()
+        for l in range(L):
+            orc, lib = orcs[l], libs[l]
+            if (t - 1) % T == 0:
+                orc.refresh(gs[l], t)
+                assert np.array_equal(lib.get_omega(), orc.omega), (l, t)
+                factor_check(lib, orc)
+                orc.factors = [lib.get_factor(n) for n in range(4)]
+            Wos[l] = orc.step(Wos[l], gs[l])
+            dg = caps[l].host()
+            Wg = host(Ws[l], wl.dtype)
+            apply_check(Wprev[l], Wg, dg, wl.dtype, wl.lr, what=f"layer {l} t={t}")
+            expected, n_steep, du = aligns[l].expected_delta(lib, t)
+            rel = delta_rel(dg, expected)
+            print(f"DELTA step_many layer {l} t={t}: rel {rel:.3e} (against the oracle's own "
+                  f"Delta: {delta_rel(dg, orc.last['delta']):.3e}; steep core entries {n_steep}, "
+                  f"max |du| {du:.2e})", flush=True)
+            assert n_steep <= 1e-4 * orc.mC.size, n_steep
+            assert rel <= 1e-5, (l, t, rel)
+    for l in range(L):
+        weight_check(host(Ws[l], wl.dtype), Wos[l], wl.dtype, f"layer {l}", delta_backed=True)
+        assert libs[l].t == nsteps
+
+
 def test_step_many_rejects_a_repeated_handle():
     wl = TINY_F32
     lib = make_lib(wl)
@@ -367,14 +417,17 @@ def test_lowrank_first_steps_with_pinned_omega_and_factors(case, fused):
         if U is not None:
             lib.set_factor(n, U)
     lib.mark_refreshed()
+    cap = DeltaCapture(lib, wl)
+    split = CoreSplit(orc)
     W, Wo = dev(W0, wl.dtype), W0
+    slack = 0.0
     for step in range(4):
         G = dev(g, wl.dtype)
-        lib.step(W, G)
-        Wo = orc.step(Wo, g)
-        torch.cuda.synchronize()
+        what = f"lowrank-first {name}/plan{fused} step {step + 1}"
+        Wo, _ = checked_step(lib, orc, cap, W, Wo, g, wl, what, G=G, align=split)
+        slack += wl.lr * 1e-5 * np.abs(orc.last["delta"]).max()
         assert np.array_equal(host(G, wl.dtype).view(np.uint8), np.ascontiguousarray(g).view(np.uint8))
-        weight_check(host(W, wl.dtype), Wo, wl.dtype, f"{name} step {step + 1}")
+        weight_check(host(W, wl.dtype), Wo, wl.dtype, what, delta_backed=True, slack=slack)
         g = gs.next()
     _, _, ms, vs = lib.get_moments()
     assert np.abs(ms - orc.mS).max() <= 1e-5 * np.abs(orc.mS).max()

@@ -77,6 +77,9 @@ def _init(lib, shape, ranks, dtype=0, rho=0.05, T=10, lr=1e-3, b1=0.9, b2=0.999,
     dict(shape=(4, 4), ranks=(2, 2), eps=-1.0),
     dict(shape=(4, 4), ranks=(2, 2), lr=-1.0),
     dict(shape=(65536, 65536), ranks=(65536, 65536)),       # N = 2^32
+    dict(shape=(3, 5, 64), ranks=(3, 5, 16)),               # r_n > N / I_n = 15
+    dict(shape=(50,), ranks=(2,)),                          # one mode: N / I_n = 1
+    dict(shape=(2, 40), ranks=(2, 3)),                      # 3 > 80 / 40
 ])
 def test_init_rejects_invalid_arguments(lib, kw):
     rc, h = _init(lib, **kw)
@@ -84,7 +87,28 @@ def test_init_rejects_invalid_arguments(lib, kw):
     assert not h.value
 
 
+@pytest.mark.parametrize("kw", [
+    dict(shape=(3, 5, 64), ranks=(3, 5, 15)),               # r_n = N / I_n
+    dict(shape=(50,), ranks=(1,)),
+    dict(shape=(2, 40), ranks=(1, 2)),
+])
+def test_rank_bound_is_inclusive(lib, kw):
+    """r_n up to the rank of the mode-n unfolding, N / I_n, passes argument validation:
+    without a device the call then fails at the device query (TGRAD_EHIP), never with
+    TGRAD_EINVAL; on a machine with a GPU it succeeds."""
+    rc, h = _init(lib, **kw)
+    assert rc in (tg.OK, tg.EHIP), rc
+    if h.value:
+        lib.tgrad_destroy(h)
+
+
+def test_info_layout():
+    """tgrad_info: 7 + 2 * 8 + 2 + 2 int64 fields, matching the ctypes mirror."""
+    assert ctypes.sizeof(tg.Info) == (7 + 2 * tg.MAX_NDIM + 4) * 8
+
+
 def test_null_handle_calls_are_einval(lib):
+    assert lib.tgrad_debug_capture_delta(None, None) == tg.EINVAL
     assert lib.tgrad_step(None, None, None, None) == tg.EINVAL
     assert lib.tgrad_refresh(None, None, None) == tg.EINVAL
     assert lib.tgrad_get_omega(None, None, 0) == tg.EINVAL
