@@ -206,9 +206,12 @@ int tgrad_set_fusion(tgrad_t *h, int enable);
  * one staged slab serves all three). It applies when the two modes before the last are
  * at most 64, the last at most 32, and one slab of the three modes is a multiple of 8
  * elements and at most 128 KiB; the input must be 16-byte aligned (otherwise one launch
- * per mode is used). enable = 1 selects it (the default; TGRAD_EINVAL where it does not
- * apply), 0 one Gram launch per mode. Results agree to fp32 rounding of the partial
- * sums; takes effect at the next refresh. */
+ * per mode is used). Bit 0 of enable = 1 selects it (the default; TGRAD_EINVAL where it
+ * does not apply), 0 one Gram launch per mode. Bit 1 (enable = 2 or 3) makes every Gram
+ * launch read the gradient itself and clear Omega's entries in its staged tiles through
+ * the membership bitmask, instead of reading the residual copy the top-k pass writes
+ * (the default, enable 0 or 1). Results agree to fp32 rounding of the partial sums;
+ * takes effect at the next refresh. */
 int tgrad_set_gram_fusion(tgrad_t *h, int enable);
 
 /* Test / benchmark hook: with the fused launch plan, two neighbouring compressed modes

@@ -325,11 +325,14 @@ class TGrad:
         self._check(rc, "tgrad_set_fusion")
         return True
 
-    def set_gram_fusion(self, enable) -> bool:
+    def set_gram_fusion(self, enable, masked: bool = False) -> bool:
         """Select the one-read Gram launch of the last three modes at a refresh (True)
-        or one Gram launch per mode (False); returns False when the one-read launch does
-        not apply to this shape and dtype."""
-        rc = self._lib.tgrad_set_gram_fusion(self._h, int(bool(enable)))
+        or one Gram launch per mode (False); masked: the Gram launches read the gradient
+        and clear Omega's entries through its bitmask instead of reading the residual
+        copy. Returns False when the one-read launch does not apply to this shape and
+        dtype."""
+        code = int(bool(enable)) | (2 if masked else 0)
+        rc = self._lib.tgrad_set_gram_fusion(self._h, code)
         if rc == EINVAL and enable:
             return False
         self._check(rc, "tgrad_set_gram_fusion")

@@ -239,6 +239,12 @@ hipError_t pick_nob(const GK& k, size_t lds, unsigned grid, hipStream_t s) {
 //          in its slot) and the 16 rows a fragment read touches fall in distinct banks.
 //   narrow (I * B small): TA whole slabs, contiguous. K runs over (a, b), element
 //          offset a * I * B + r * B + b; fragments are read 16 bits at a time.
+// Both forms move 16-byte pieces that start on a multiple of 8 elements, so each piece
+// has one byte of Omega's membership bitmask. With a mask, the wave that transfers a
+// piece also transfers the dwords holding its byte into LDS; once both have landed the
+// thread clears the piece's Omega entries (+0 is the zero pattern of both formats),
+// before the barrier that publishes the tile, so the Gram is that of the residual while
+// the gradient is only read.
 // Each wave sums 8 k-steps in fp32 (at most 256 exact products per sum) before adding
 // into fp64; at the end the waves' fp64 sums are combined in wave order, so results are
 // deterministic run to run.
@@ -247,6 +253,11 @@ constexpr uint32_t G16_TB = 128;           // wide tiles: columns (b) per tile
 constexpr uint32_t G16_NARROW = 16384;     // narrow tiles: at most this many elements
 constexpr uint32_t G16_FLUSH = 8;          // k-steps per fp32 partial sum
 constexpr int G16_WGS_PER_CU = 3;
+// transfer instructions per thread and tile, at most: wide tiles 64 rows x 16 pieces,
+// narrow tiles G16_NARROW / 8 pieces, over G16_NTH threads
+constexpr int G16_PIECES = (int)(G16_NARROW / 8 / G16_NTH);
+constexpr uint32_t G16_MREG = 80;   // bytes of mask dwords per (instruction, wave)
+static_assert(64 * (G16_TB / 8) <= G16_PIECES * G16_NTH, "wide tile pieces");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -255,6 +266,8 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 struct G16K {
   const uint16_t* X;
+  const uint8_t* mask8;   // Omega's bitmask as bytes (element e: bit e % 8 of byte e / 8), or NULL
+  uint32_t mask_off;      // LDS byte offset of the two buffers' mask-byte areas
   double* partial;
   uint64_t ntiles;
   uint32_t A, I, B;
@@ -343,6 +356,18 @@ __device__ __forceinline__ void g16_step(f4* acc, LD&& ld) {
   g16_mfma<BF, NB, KS, W, 0>(acc, fr);
 }
 
+// Clear the elements of a staged 16-byte piece (8 16-bit values) whose bits are set in
+// its mask byte b.
+__device__ __forceinline__ void clear_piece(unsigned char* piece, uint32_t b) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  u32x4_t keep;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    keep[i] = (((b >> (2 * i)) & 1u) ? 0u : 0x0000FFFFu) |
+              (((b >> (2 * i + 1)) & 1u) ? 0u : 0xFFFF0000u);
+  *(u32x4_t*)piece = *(const u32x4_t*)piece & keep;
+}
+
 template <bool BF, int NB, bool KS>
 __global__ void __launch_bounds__(G16_NTH) k_gram16(G16K k) {
   extern __shared__ uint4 smem16[];
@@ -384,6 +409,17 @@ __global__ void __launch_bounds__(G16_NTH) k_gram16(G16K k) {
     }
   };
 
+  // The transfers of a tile. With a mask, each wave also transfers, per instruction j of
+  // its piece transfers, the mask bytes of those 64 pieces: as whole dwords (4-byte
+  // transfers land at 4-byte steps per lane) into its own 80-byte region of the
+  // buffer's mask area. Narrow tiles: the 64 pieces' bytes are consecutive, 17 dwords
+  // cover them from the dword below; wide tiles: 4 rows of 16 consecutive bytes, 5
+  // dwords each. The bytes are read back only by lanes of the same wave, after the vmcnt
+  // wait that also covers the pieces.
+  auto mregion = [&](int buf, uint32_t j) -> unsigned char* {
+    return lds + k.mask_off + ((size_t)(buf * G16_PIECES + j) * 4 + wave) * G16_MREG;
+  };
+  const uint32_t* const mask32 = (const uint32_t*)k.mask8;
   auto issue = [&](uint64_t tile, int buf) {
     unsigned char* dst = lds + (size_t)buf * k.buf_bytes;
     if (k.wide) {
@@ -391,27 +427,84 @@ __global__ void __launch_bounds__(G16_NTH) k_gram16(G16K k) {
       const uint32_t b0 = (uint32_t)(tile - a * k.tiles_per_a) * G16_TB;
       const uint32_t lenc = (k.B - b0 < G16_TB ? k.B - b0 : G16_TB) / 8;
       const uint32_t nchunk = k.I * (G16_TB / 8);
-      for (uint32_t q0 = wave * 64; q0 < nchunk; q0 += G16_NTH) {
+      uint32_t j = 0;
+      for (uint32_t q0 = wave * 64; q0 < nchunk; q0 += G16_NTH, ++j) {
         const uint32_t p = q0 + lane;
         const uint32_t r = p >> 4, c = (p & 15) ^ (r & 15);
         if (p < nchunk && c < lenc)
-          __builtin_amdgcn_global_load_lds(
-              (const void*)(k.X + ((a * k.I + r) * k.B + b0 + c * 8)),
-              (lds_void_t*)(dst + (size_t)q0 * 16), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const void*)(k.X + ((a * k.I + r) * k.B + b0 + c * 8)),
+                                           (lds_void_t*)(dst + (size_t)q0 * 16), 16, 0, 0);
+        if (k.mask8 && lane < 20) {
+          const uint32_t rr = (q0 >> 4) + lane / 5;   // row of this dword
+          if (rr < k.I) {
+            // clamped to the tensor's last mask dword (bytes past a row are not used)
+            const uint64_t byte0 = ((a * k.I + rr) * k.B + b0) >> 3;
+            const uint64_t d = (byte0 >> 2) + lane % 5;
+            const uint64_t dlast = ((uint64_t)k.A * IB / 8 - 1) >> 2;
+            __builtin_amdgcn_global_load_lds((const void*)(mask32 + (d < dlast ? d : dlast)),
+                                             (lds_void_t*)mregion(buf, j), 4, 0, 0);
+          }
+        }
       }
     } else {
       const uint64_t a0 = tile * k.TA;
       const uint32_t nta = (uint64_t)k.A - a0 < k.TA ? (uint32_t)((uint64_t)k.A - a0) : k.TA;
       const uint32_t len = nta * IB;
       const uint32_t n16 = len / 8;
-      const uint16_t* src = k.X + a0 * IB;
-      for (uint32_t q0 = wave * 64; q0 < n16; q0 += G16_NTH) {
+      const uint64_t e0 = a0 * IB;
+      const uint16_t* src = k.X + e0;
+      uint32_t j = 0;
+      for (uint32_t q0 = wave * 64; q0 < n16; q0 += G16_NTH, ++j) {
         if (q0 + lane < n16)
           __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)(q0 + lane) * 8),
                                            (lds_void_t*)(dst + (size_t)q0 * 16), 16, 0, 0);
+        if (k.mask8 && lane < 17) {
+          // dwords of the bytes of pieces q0 .. q0 + 63, clamped to the tile's last byte
+          const uint64_t first = (e0 >> 3) + q0, last = (e0 >> 3) + n16 - 1;
+          const uint64_t d = (first >> 2) + lane;
+          __builtin_amdgcn_global_load_lds((const void*)(mask32 + (d < (last >> 2) ? d : (last >> 2))),
+                                           (lds_void_t*)mregion(buf, j), 4, 0, 0);
+        }
       }
       // the last tile may end inside a 16-byte piece
-      if (tid < len - n16 * 8) ((uint16_t*)dst)[n16 * 8 + tid] = src[n16 * 8 + tid];
+      if (tid < len - n16 * 8) {
+        const uint64_t e = e0 + n16 * 8 + tid;
+        const bool om = k.mask8 && ((k.mask8[e >> 3] >> (e & 7)) & 1u);
+        ((uint16_t*)dst)[n16 * 8 + tid] = om ? (uint16_t)0 : src[n16 * 8 + tid];
+      }
+    }
+  };
+  // clear the Omega entries of this thread's pieces of the tile in `buf` (their transfers
+  // and mask bytes have landed: called after a vmcnt wait)
+  auto clear = [&](uint64_t tile, int buf) {
+    unsigned char* dst = lds + (size_t)buf * k.buf_bytes;
+    if (k.wide) {
+      const uint64_t a = tile / k.tiles_per_a;
+      const uint32_t b0 = (uint32_t)(tile - a * k.tiles_per_a) * G16_TB;
+      const uint32_t lenc = (k.B - b0 < G16_TB ? k.B - b0 : G16_TB) / 8;
+      const uint32_t nchunk = k.I * (G16_TB / 8);
+      uint32_t j = 0;
+      for (uint32_t q0 = wave * 64; q0 < nchunk; q0 += G16_NTH, ++j) {
+        const uint32_t p = q0 + lane;
+        const uint32_t r = p >> 4, c = (p & 15) ^ (r & 15);
+        if (p < nchunk && c < lenc) {
+          const uint32_t mis = (uint32_t)((((a * k.I + r) * k.B + b0) >> 3) & 3u);
+          const uint32_t b = mregion(buf, j)[20 * (lane >> 4) + mis + c];
+          if (b) clear_piece(dst + (size_t)p * 16, b);
+        }
+      }
+    } else {
+      const uint64_t a0 = tile * k.TA;
+      const uint32_t nta = (uint64_t)k.A - a0 < k.TA ? (uint32_t)((uint64_t)k.A - a0) : k.TA;
+      const uint32_t n16 = nta * IB / 8;
+      const uint32_t mis = (uint32_t)(((a0 * IB) >> 3) & 3u);
+      uint32_t j = 0;
+      for (uint32_t q0 = wave * 64; q0 < n16; q0 += G16_NTH, ++j) {
+        if (q0 + lane < n16) {
+          const uint32_t b = mregion(buf, j)[((mis + q0) & 3u) + lane];
+          if (b) clear_piece(dst + (size_t)(q0 + lane) * 16, b);
+        }
+      }
     }
   };
 
@@ -420,9 +513,10 @@ __global__ void __launch_bounds__(G16_NTH) k_gram16(G16K k) {
   int cur = 0;
   if (tile < k.ntiles) issue(tile, cur);
   __builtin_amdgcn_s_waitcnt(0);
+  if (k.mask8 && tile < k.ntiles) clear(tile, cur);
   for (; tile < k.ntiles; tile += gridDim.x) {
     const uint64_t next = tile + gridDim.x;
-    lds_barrier();                  // tile `cur` landed everywhere; `cur ^ 1` free
+    lds_barrier();                  // tile `cur` landed (Omega cleared) everywhere; `cur ^ 1` free
     if (next < k.ntiles) issue(next, cur ^ 1);
     const unsigned char* buf = lds + (size_t)cur * k.buf_bytes;
     if (k.wide) {
@@ -483,6 +577,7 @@ __global__ void __launch_bounds__(G16_NTH) k_gram16(G16K k) {
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this thread's part of the next tile landed
+    if (k.mask8 && next < k.ntiles) clear(next, cur ^ 1);
     cur ^= 1;
   }
   flush();
@@ -569,9 +664,10 @@ G16Geo g16geo(const GramArgs& g, int num_cu) {
   G16Geo r{};
   r.ok = false;
   if (g.P != 1 || (g.dt != DT_BF16 && g.dt != DT_F16) || g.I > 64 || g.I == 0) return r;
-  if (((uintptr_t)g.X) % 16 != 0 || g.mask) return r;
+  if (((uintptr_t)g.X) % 16 != 0) return r;
   G16K& k = r.k;
   k.X = (const uint16_t*)g.X;
+  k.mask8 = (const uint8_t*)g.mask;
   k.A = g.A;
   k.I = g.I;
   k.B = g.B;
@@ -602,7 +698,10 @@ G16Geo g16geo(const GramArgs& g, int num_cu) {
   }
   const uint32_t nb = (g.I + 15) / 16;
   const size_t red = (size_t)nb * (nb + 1) / 2 * 4 * 64 * sizeof(double);   // block sums
-  r.lds = std::max((size_t)2 * k.buf_bytes, red);
+  // masked: per tile buffer, an 80-byte region per (transfer instruction, wave)
+  k.mask_off = 2 * k.buf_bytes;
+  const size_t mask_area = g.mask ? (size_t)2 * G16_PIECES * 4 * G16_MREG : 0;
+  r.lds = std::max((size_t)2 * k.buf_bytes + mask_area, red);
   // a persistent grid of one resident round (a second, partial round would run alone at
   // the end): as many workgroups as a CU holds with this kernel's registers and LDS, at
   // most G16_WGS_PER_CU (each workgroup writes an I x I fp64 partial)
@@ -612,6 +711,7 @@ G16Geo g16geo(const GramArgs& g, int num_cu) {
   const int per_cu = occ < G16_WGS_PER_CU ? occ : G16_WGS_PER_CU;
   uint64_t grid = (uint64_t)(num_cu > 0 ? num_cu : 256) * (uint64_t)per_cu;
   if (grid > k.ntiles) grid = k.ntiles;
+  if (g.max_blocks && grid > g.max_blocks) grid = g.max_blocks;
   if (grid < 1) grid = 1;
   r.grid = (uint32_t)grid;
   r.ok = true;
@@ -659,6 +759,7 @@ uint32_t gram_blocks(const GramArgs& g, int num_cu) {
   const GGeo r = ggeo(g);
   uint64_t nb = (uint64_t)(num_cu > 0 ? num_cu : 256) * 4;
   if (nb > r.ntiles) nb = r.ntiles;
+  if (g.max_blocks && nb > g.max_blocks) nb = g.max_blocks;
   if (nb < 1) nb = 1;
   // every block gets at least one tile: recompute from tiles per block
   const uint64_t tpb = (r.ntiles + nb - 1) / nb;

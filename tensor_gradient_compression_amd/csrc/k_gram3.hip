@@ -29,6 +29,11 @@
 //           aligned dwords and a funnel shift per 16-byte run, or one 16-byte read when
 //           Ic % 8 == 0;
 //   mode c: row x, k = 32 slab rows (z, y), one 16-bit value each.
+// With Omega's bitmask the Grams are those of the residual while the gradient is only
+// read: each 16-byte piece of a slab (8 elements, starting on a multiple of 8) has one
+// mask byte; the wave that loads a group of pieces transfers the dwords holding their
+// bytes into LDS, and after staging a piece its thread clears the piece's Omega entries
+// there (+0 is the zero pattern of both formats).
 // Arithmetic as in the single-mode 16-bit Gram: bf16/fp16 products are exact in fp32
 // (v_mfma_f32_16x16x32_bf16 / _f16), each wave adds at most 8 k-steps (256 products) in
 // fp32 before adding into fp64, and the waves' fp64 sums are combined in a fixed order,
@@ -51,6 +56,7 @@ constexpr uint32_t G3_MAX_SLAB = 65536;      // elements (128 KiB)
 __host__ __device__ constexpr int g3_cpt(int nt) { return (int)((G3_MAX_SLAB / 8 + nt - 1) / nt); }
 constexpr uint32_t G3_FLUSH = 8;             // k-steps per fp32 partial sum
 constexpr size_t G3_LDS_MAX = 160 * 1024;
+constexpr uint32_t G3_MREG = 80;             // bytes of mask dwords per (load, wave)
 // Fourth word of a raw buffer resource on gfx9-family targets (no format conversion,
 // byte-granular range check: loads past num_records return zero).
 constexpr int G3_RSRC_W3 = 0x00020000;
@@ -64,6 +70,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct G3K {
   const u32x4* X;          // the tensor as 16-byte pieces
+  const uint8_t* mask8;    // Omega's bitmask as bytes (one per 16-byte piece), or NULL
+  uint32_t mask_off;       // LDS byte offset of the staged mask bytes of a slab
   double* part[3];         // per mode: gridDim.x partials of I_m^2 fp64 values
   uint32_t A, Ia, Ib, Ic;
   uint32_t slab_q;         // 16-byte pieces per slab
@@ -328,6 +336,8 @@ __device__ __forceinline__ void g3_loop(const G3K& k, LDS unsigned char* lds, ui
   constexpr int CPT = g3_cpt(NT);
   u32x4 pf[CPT];
   LDS u32x4* const dst = (LDS u32x4*)lds + tid;
+  LDS unsigned char* const mbuf = lds + k.mask_off;
+  const bool masked = k.mask8 != nullptr;
   auto fetch = [&](uint32_t s) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(k.X + (uint64_t)s * k.slab_q), (short)0, (int)(k.slab_q * 16), G3_RSRC_W3);
@@ -335,20 +345,66 @@ __device__ __forceinline__ void g3_loop(const G3K& k, LDS unsigned char* lds, ui
     for (int m = 0; m < CPT; ++m)
       pf[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(tid * 16), NT * 16 * m, 0);
   };
-  auto stage = [&]() {
+  // The mask bytes of slab s's pieces q0 .. q0 + 63 (q0 = NT m + 64 wave: this wave's
+  // m-th load) are consecutive: 17 dwords from the one that holds the first cover them,
+  // transferred (4-byte transfers land at 4-byte steps per lane) into the wave's own
+  // G3_MREG-byte region for m. Dwords past the slab repeat its last one (those pieces
+  // stage zeros). The bytes are read back only by lanes of the same wave.
+  const uint32_t wv64 = tid & ~63u;
+  const uint32_t* const mask32 = (const uint32_t*)k.mask8;
+  auto mregion = [&](int m) -> LDS unsigned char* {
+    return mbuf + ((uint32_t)m * (NT / 64) + (wv64 >> 6)) * G3_MREG;
+  };
+  auto fetch_mask = [&](uint32_t s) {
+    const uint32_t b0 = s * k.slab_q, dlast = (b0 + k.slab_q - 1) >> 2;
+    const uint32_t l = tid & 63u;
+#pragma unroll 1
+    for (int m = 0; m < CPT; ++m) {
+      const uint32_t d = (b0 >> 2) + (NT * (uint32_t)m + wv64) / 4 + l;
+      if (l < 17)
+        __builtin_amdgcn_global_load_lds((const void*)(mask32 + (d < dlast ? d : dlast)),
+                                         (__attribute__((address_space(3))) void*)mregion(m),
+                                         4, 0, 0);
+    }
+  };
+  // The pieces go to LDS as loaded. Masked, each thread then clears the Omega entries of
+  // its own pieces from its own mask bytes (their transfers were issued before the
+  // slab's loads: vmcnt), and then transfers its mask bytes of the slab after (`nxt`,
+  // if any) into the same slots, which only it reads.
+  auto stage = [&](uint32_t cur_slab, bool more, uint32_t nxt) {
 #pragma unroll
     for (int m = 0; m < CPT; ++m) dst[NT * m] = pf[m];
+    if (masked) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+      const uint32_t mis = (cur_slab * k.slab_q) & 3u;
+#pragma unroll 1
+      for (int m = 0; m < CPT; ++m) {
+        // NT m + 64 wave is a multiple of 4, so the first byte sits at offset mis
+        const uint32_t b = mregion(m)[mis + (tid & 63u)];
+        if (b) {
+          u32x4 keep;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            keep[i] = (((b >> (2 * i)) & 1u) ? 0u : 0x0000FFFFu) |
+                      (((b >> (2 * i + 1)) & 1u) ? 0u : 0xFFFF0000u);
+          dst[NT * m] = dst[NT * m] & keep;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the slots are read
+      if (more) fetch_mask(nxt);
+    }
   };
   const uint32_t G = gridDim.x;
   uint32_t s = blockIdx.x;
+  if (masked) fetch_mask(s);
   fetch(s);
-  stage();
+  stage(s, s + G < k.A, s + G);
   lds_barrier();
   for (; s + G < k.A; s += G) {
     fetch(s + G);   // in flight while the slab in LDS is worked on
     work();
     lds_barrier();  // every wave is done with the slab
-    stage();
+    stage(s + G, s + 2 * G < k.A, s + 2 * G);
     lds_barrier();
   }
   work();
@@ -481,6 +537,7 @@ G3Plan g3plan(const Gram3Args& g, int num_cu, bool probe) {
   if (((uintptr_t)g.X) % 16 != 0) return p;
   G3K& k = p.k;
   k.X = (const u32x4*)g.X;
+  k.mask8 = (const uint8_t*)g.mask;
   k.A = g.A;
   k.Ia = g.Ia;
   k.Ib = g.Ib;
@@ -537,8 +594,11 @@ G3Plan g3plan(const Gram3Args& g, int num_cu, bool probe) {
     k.red[m] = red;
     red += k.nb[m] * (k.nb[m] + 1) / 2 * k.ns[m] * 4 * 64;
   }
-  // every staged piece (see g3_loop), or the block totals
-  p.lds = std::max<size_t>((size_t)staged * 2, (size_t)red * sizeof(double));
+  // every staged piece (see g3_loop) and, masked, one mask byte per staged piece; or
+  // the block totals
+  k.mask_off = (uint32_t)(staged * 2);
+  const size_t mask_bytes = g.mask ? (size_t)g3_cpt(nt) * (nt / 64) * G3_MREG : 0;
+  p.lds = std::max<size_t>((size_t)staged * 2 + mask_bytes, (size_t)red * sizeof(double));
   p.nt = (uint32_t)nt;
   if (p.lds > G3_LDS_MAX) return p;
   if (probe) {

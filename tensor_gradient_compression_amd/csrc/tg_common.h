@@ -215,6 +215,7 @@ struct GramArgs {
   const uint64_t* mask;  // NULL -> no masking
   double* partial;       // nblk * (I*P)^2
   double* out;           // (I*P)^2
+  uint32_t max_blocks;   // 0: as many workgroups (partial sums) as fill the GPU; else at most this
 };
 uint32_t gram_blocks(const GramArgs& g, int num_cu);
 uint32_t gram_reduce_groups();   // partial buffer holds (blocks + groups) * (I*P)^2
@@ -234,6 +235,7 @@ struct Gram3Args {
   const void* X;
   int dt;
   uint32_t A, Ia, Ib, Ic;
+  const uint64_t* mask;  // Omega's membership bitmask: entries in it read as zero; NULL: none
   double* partial;
   double* out[3];
 };

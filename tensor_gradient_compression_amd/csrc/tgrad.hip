@@ -9,7 +9,8 @@
 //   reconstruction, one mode product per compressed mode (first mode first), the last
 //   one applying W <- round(W * decay - lr * (Delta_L + lambda N_S at Omega)).
 // Refresh: top-k -> Omega (+ bitmask, ranks) -> per compressed mode: Gram of the
-//   residual (Omega masked on load) -> Jacobi eigensolver -> U(n) and operand matrices.
+//   residual (the gradient read with Omega's entries cleared in the staged tiles) ->
+//   Jacobi eigensolver -> U(n) and operand matrices.
 #include <algorithm>
 #include <cmath>
 #include <mutex>
@@ -30,6 +31,18 @@ namespace {
 struct Rec {
   int id;
   hipEvent_t a, b;
+};
+
+// The scratch buffers of a refresh's kernels: the top-k workspace, the Gram partial sums
+// and the Gram matrices (one gram_stride-double matrix per compressed mode); `masked`:
+// the Gram launches read the gradient with Omega cleared through the bitmask rather than
+// a residual copy.
+struct RefreshWs {
+  tg::TopkWs tw;
+  double* gram_part;
+  double* gram;
+  bool masked;
+  uint32_t max_gram_blocks;   // 0: no cap on a Gram launch's partial sums
 };
 
 }  // namespace
@@ -54,6 +67,12 @@ struct tgrad_handle {
   bool slab3 = true;         // use it
   bool can_gram3 = false;    // refresh: the last three modes' Grams from one read
   bool gram3 = true;         // use it
+  // refresh: the Gram kernels read the gradient and clear Omega's entries in their staged
+  // tiles through the bitmask, instead of reading a residual copy that the top-k pass
+  // writes (the copy is the faster default: 0.10 ms per refresh on the bf16
+  // (64,64,48,48,25) tensor)
+  bool gram_masked = false;
+  void* resid = nullptr;     // refresh: G with Omega zeroed (shares buf's memory)
   bool can_pair = false;     // the fused chains hold two neighbouring leading modes
   bool pairs = true;         // launch those as one (k_pair)
 
@@ -63,7 +82,6 @@ struct tgrad_handle {
   float *S = nullptr, *mS = nullptr, *vS = nullptr;
   float *core = nullptr, *ucore = nullptr, *mC = nullptr, *vC = nullptr;
   float* buf[2] = {nullptr, nullptr};
-  void* resid = nullptr;         // refresh: G with Omega zeroed (shares buf's memory)
   void* gcopy = nullptr;         // step without the folded gather: the residual (N elements)
   float* U[TGRAD_MAX_NDIM] = {nullptr};
   float* Mp[TGRAD_MAX_NDIM] = {nullptr};
@@ -355,7 +373,8 @@ int step_body(tgrad_t* h, void* weight, const void* grad, int64_t t, hipStream_t
 // k-subset; optionally the residual (src with Omega zeroed) written to `resid`. With
 // remapped moments the new bitmask goes to the other buffer, so the old one still
 // locates each element's previous moments, which then follow their element.
-int select_omega(tgrad_t* h, const void* src, int dt, void* resid, hipStream_t s) {
+int select_omega(tgrad_t* h, const TopkWs& tw, const void* src, int dt, void* resid,
+                 hipStream_t s) {
   if (h->remap) {
     std::swap(h->mask, h->mask_prev);
     std::swap(h->rank, h->rank_prev);
@@ -363,7 +382,7 @@ int select_omega(tgrad_t* h, const void* src, int dt, void* resid, hipStream_t s
   const uint64_t gamma = 0x9E3779B97F4A7C15ull;
   const uint64_t serves = (uint64_t)(h->t + 1);
   const uint64_t rk_base = h->seed + gamma * ((serves << 32) + 1ull);
-  HIPCHK(h, launch_topk(dt, src, h->N, (uint32_t)h->k, h->tw, h->omega, h->mask, h->rank, resid,
+  HIPCHK(h, launch_topk(dt, src, h->N, (uint32_t)h->k, tw, h->omega, h->mask, h->rank, resid,
                         h->selection == TGRAD_SELECT_RANDK, rk_base, s, mark_cb, h));
   if (h->remap) {
     Mark m(h, KID_REMAP);
@@ -375,9 +394,11 @@ int select_omega(tgrad_t* h, const void* src, int dt, void* resid, hipStream_t s
   return TGRAD_OK;
 }
 
-// The one-read Gram launch of the last three modes over X, where all three are
-// compressed in a real 16-bit tensor (the caller still asks gram3_supported).
-bool gram3_args(const tgrad_t* h, const void* X, Gram3Args* g) {
+// The one-read Gram launch of the last three modes over X (entries in `mask` read as
+// zero), where all three are compressed in a real 16-bit tensor (the caller still asks
+// gram3_supported).
+bool gram3_args(const tgrad_t* h, const void* X, const uint64_t* mask, double* partial,
+                Gram3Args* g) {
   const int d = h->d;
   if (d < 3 || h->P != 1 || (h->dtype != TGRAD_BF16 && h->dtype != TGRAD_F16)) return false;
   for (int i = d - 3; i < d; ++i)
@@ -391,22 +412,36 @@ bool gram3_args(const tgrad_t* h, const void* X, Gram3Args* g) {
   g->Ia = (uint32_t)h->shape[d - 3];
   g->Ib = (uint32_t)h->shape[d - 2];
   g->Ic = (uint32_t)h->shape[d - 1];
-  g->partial = h->gram_part;
+  g->mask = mask;
+  g->partial = partial;
   return true;
 }
 
-int do_refresh(tgrad_t* h, const void* grad, hipStream_t s) {
-  // sparse first: Omega from G, then the Grams of the residual (G itself when k = 0,
-  // else the copy with Omega zeroed that the top-k compaction writes). Low-rank first:
-  // the Grams of G, then Omega from the residual G - L of the new factors.
+RefreshWs handle_ws(const tgrad_t* h) {
+  RefreshWs ws;
+  ws.tw = h->tw;
+  ws.gram_part = h->gram_part;
+  ws.gram = h->gram;
+  ws.masked = h->gram_masked;
+  ws.max_gram_blocks = 0;
+  return ws;
+}
+
+int do_refresh(tgrad_t* h, const void* grad, hipStream_t s, const RefreshWs& ws) {
+  // sparse first: Omega from G, then the Grams of the residual (G itself when k = 0):
+  // the copy with Omega zeroed that the top-k compaction writes, or (gram_masked) G read
+  // with Omega's entries cleared through its bitmask. Low-rank first: the Grams of G,
+  // then Omega from the residual G - L of the new factors.
   const bool lowrank_first =
       h->order == TGRAD_ORDER_LOWRANK_FIRST && h->k > 0 && !h->fmodes.empty();
   const void* R = grad;
+  const uint64_t* rmask = nullptr;
   int rc;
   if (h->k > 0 && !lowrank_first) {
-    void* rw = h->fmodes.empty() ? nullptr : h->resid;
-    if ((rc = select_omega(h, grad, h->dtype, rw, s)) != TGRAD_OK) return rc;
+    void* rw = (h->fmodes.empty() || ws.masked) ? nullptr : h->resid;
+    if ((rc = select_omega(h, ws.tw, grad, h->dtype, rw, s)) != TGRAD_OK) return rc;
     if (rw) R = rw;
+    else rmask = h->mask;
   }
   const int gdt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
   EigArgs eig[TGRAD_MAX_NDIM];
@@ -414,20 +449,21 @@ int do_refresh(tgrad_t* h, const void* grad, hipStream_t s) {
   // the last three modes' Grams from one read of R where that launch applies, the other
   // modes one launch each
   Gram3Args g3;
-  const bool tail3 = h->gram3 && h->can_gram3 && gram3_args(h, R, &g3) &&
+  const bool tail3 = h->gram3 && h->can_gram3 && gram3_args(h, R, rmask, ws.gram_part, &g3) &&
                      gram3_supported(g3, h->num_cu);
   for (int n : h->fmodes) {
-    double* const out = h->gram + (size_t)ne * h->gram_stride;
+    double* const out = ws.gram + (size_t)ne * h->gram_stride;
     if (tail3 && n >= h->d - 3) {
       g3.out[n - (h->d - 3)] = out;
     } else {
-      GramArgs g;
+      GramArgs g{};
       g.X = R;
+      g.max_blocks = ws.max_gram_blocks;
       g.dt = gdt;
       view(h->shape, h->d, n, &g.A, &g.I, &g.B);
       g.P = h->P;
-      g.mask = nullptr;
-      g.partial = h->gram_part;
+      g.mask = rmask;
+      g.partial = ws.gram_part;
       g.out = out;
       HIPCHK(h, launch_gram(g, h->num_cu, s, mark_cb, h));
     }
@@ -450,7 +486,7 @@ int do_refresh(tgrad_t* h, const void* grad, hipStream_t s) {
   }
   if (lowrank_first) {
     if (h->selection == TGRAD_SELECT_RANDK) {
-      if ((rc = select_omega(h, grad, h->dtype, nullptr, s)) != TGRAD_OK) return rc;
+      if ((rc = select_omega(h, ws.tw, grad, h->dtype, nullptr, s)) != TGRAD_OK) return rc;
     } else {
       // R = G - (G x_n Un^H ...) x_n Un ... in fp32, then its k largest entries
       if ((rc = run_projection(h, grad, false, s)) != TGRAD_OK) return rc;
@@ -459,7 +495,8 @@ int do_refresh(tgrad_t* h, const void* grad, hipStream_t s) {
         Mark m(h, KID_GATHER);
         HIPCHK(h, launch_resid_sub(h->dtype, grad, h->lbuf, h->N * h->P, s));
       }
-      if ((rc = select_omega(h, h->lbuf, h->P == 2 ? DT_C64 : DT_F32, nullptr, s)) != TGRAD_OK)
+      if ((rc = select_omega(h, ws.tw, h->lbuf, h->P == 2 ? DT_C64 : DT_F32, nullptr, s)) !=
+          TGRAD_OK)
         return rc;
     }
   }
@@ -657,7 +694,10 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
   }
   {
     Gram3Args g3;
-    if (gram3_args(h, (const void*)(uintptr_t)256, &g3) && gram3_supported(g3, h->num_cu)) {
+    // with the mask a refresh will pass (the launch then stages mask bytes too)
+    const uint64_t* m3 = h->k > 0 ? h->mask : nullptr;
+    if (gram3_args(h, (const void*)(uintptr_t)256, m3, nullptr, &g3) &&
+        gram3_supported(g3, h->num_cu)) {
       h->can_gram3 = true;
       gpart = std::max<uint64_t>(gpart, gram3_partial_doubles(g3, h->num_cu));
     }
@@ -767,7 +807,7 @@ int tgrad_refresh(tgrad_t* h, const void* grad, void* stream) {
   if (!h || !grad || ((uintptr_t)grad & 15u) != 0) return TGRAD_EINVAL;
   DevGuard g(h->device);
   h->cur_stream = (hipStream_t)stream;
-  return do_refresh(h, grad, (hipStream_t)stream);
+  return do_refresh(h, grad, (hipStream_t)stream, handle_ws(h));
 }
 
 }  // extern "C"
@@ -1003,7 +1043,7 @@ int tgrad_step(tgrad_t* h, void* weight, const void* grad, void* stream) {
   // failed call can be repeated (the refresh it needs is then still due)
   const int64_t t = h->t + 1;
   if ((t - 1) % h->T == 0 && h->refreshed_for != t) {
-    const int rc = do_refresh(h, grad, s);   // serves step h->t + 1 = t
+    const int rc = do_refresh(h, grad, s, handle_ws(h));   // serves step h->t + 1 = t
     if (rc != TGRAD_OK) return rc;
   }
   const int rc = step_body(h, weight, grad, t, s);
@@ -1432,9 +1472,10 @@ int tgrad_set_pair_fusion(tgrad_t* h, int enable) {
 }
 
 int tgrad_set_gram_fusion(tgrad_t* h, int enable) {
-  if (!h || enable < 0 || enable > 1) return TGRAD_EINVAL;
-  if (enable && !h->can_gram3) return TGRAD_EINVAL;
-  h->gram3 = enable != 0;
+  if (!h || enable < 0 || enable > 3) return TGRAD_EINVAL;
+  if ((enable & 1) && !h->can_gram3) return TGRAD_EINVAL;
+  h->gram3 = (enable & 1) != 0;
+  h->gram_masked = (enable & 2) != 0;
   return TGRAD_OK;
 }
 

@@ -44,14 +44,18 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("masked", [False, True], ids=["residual-copy", "masked-read"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
-def test_one_read_gram_matches_oracle_and_per_mode(case):
+def test_one_read_gram_matches_oracle_and_per_mode(case, masked):
+    """Both ways of reading the residual: the copy the top-k pass writes, and the
+    gradient itself with Omega's entries cleared in the staged tiles through the bitmask
+    (every Gram launch, the one-read and the per-mode ones)."""
     name, wl = case
     g = GradStream(wl, seed=11).next()
     G = tg.to_device(g, wl.dtype)
     fused, single = make_lib(wl), make_lib(wl)
-    assert fused.set_gram_fusion(True)
-    assert single.set_gram_fusion(False)
+    assert fused.set_gram_fusion(True, masked=masked)
+    assert single.set_gram_fusion(False, masked=masked)
     fused.timing_enable(True)
     single.timing_enable(True)
     fused.refresh(G)

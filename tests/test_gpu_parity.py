@@ -152,11 +152,16 @@ FACTOR_CASES = [
 ]
 
 
+@pytest.mark.parametrize("masked", [False, True], ids=["residual-copy", "masked-read"])
 @pytest.mark.parametrize("case", FACTOR_CASES, ids=lambda c: c[0])
-def test_refresh_factors_match_oracle(case):
+def test_refresh_factors_match_oracle(case, masked):
+    """The refresh against the oracle, with the Grams reading the residual copy that the
+    top-k pass writes or the gradient with Omega cleared through the bitmask."""
     name, wl = case
     g = GradStream(wl, seed=5).next()
     lib, orc = make_lib(wl), make_oracle(wl)
+    if masked:
+        lib.set_gram_fusion(lib.set_gram_fusion(True), masked=True)
     G = dev(g, wl.dtype)
     before = host(G, wl.dtype).copy()
     lib.refresh(G)
