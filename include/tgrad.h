@@ -288,6 +288,28 @@ int64_t tgrad_state_size(tgrad_t *h);
 int tgrad_save_state(tgrad_t *h, void *buf, int64_t cap);
 int tgrad_load_state(tgrad_t *h, const void *buf, int64_t size);
 
+/* ---------------------------------------------------------------- without allocation.
+ * For callers that cannot allocate device memory while they run: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * tgrad_refresh_noalloc is tgrad_refresh (same kernels and results: Omega bit for bit,
+ * factors to fp32 rounding of the Gram partial sums) with every scratch buffer its
+ * kernels use -- the top-k workspace, the Gram partial sums and the Gram matrices -- in
+ * one file-scope device array of the library, TGRAD_NOALLOC_SCRATCH_BYTES per GPU, held
+ * until the process ends, instead of the handle's workspace. Its Gram launches read
+ * `grad` with Omega's entries cleared through the membership bitmask, so no residual
+ * copy is written, and where the partial sums would not fit they use fewer workgroups.
+ * It calls no hipMalloc or hipFree (the array's address is looked up once per GPU).
+ * Every call on one GPU uses that GPU's array, which keeps the last call's contents (the
+ * kernels clear what must start at zero): calls that overlap on one GPU, from several
+ * threads or streams, race. Per-launch timing is not recorded during the call.
+ * Errors: as tgrad_refresh; TGRAD_EINVAL also when the refresh needs more than the array
+ * holds (the top-k workspace grows as 16 N / 1024 bytes, so N up to about 2.9e9 fits; a
+ * Gram partial sum needs 8 (I_n P)^2 bytes per workgroup) or the handle uses the
+ * low-rank-first order (which needs full-size intermediates); TGRAD_EHIP when the
+ * array's address cannot be obtained. */
+#define TGRAD_NOALLOC_SCRATCH_BYTES (48ull << 20)
+int tgrad_refresh_noalloc(tgrad_t *h, const void *grad, void *stream);
+
 /* ---------------------------------------------------------------- timing.
  * When enabled, every kernel launch of step/refresh is bracketed by HIP events on
  * the launch stream (at most max_records launches are kept). tgrad_timing_read

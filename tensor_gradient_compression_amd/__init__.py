@@ -61,6 +61,7 @@ SIGNATURES = [
                                   ctypes.c_double]),
     ("tgrad_step", ctypes.c_int, [_P, _P, _P, _P]),
     ("tgrad_refresh", ctypes.c_int, [_P, _P, _P]),
+    ("tgrad_refresh_noalloc", ctypes.c_int, [_P, _P, _P]),
     ("tgrad_step_many", ctypes.c_int, [ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P),
                                        ctypes.c_int, _P]),
     ("tgrad_destroy", ctypes.c_int, [_P]),
@@ -223,6 +224,13 @@ class TGrad:
         self._check_tensor(grad, "grad")
         self._check(self._lib.tgrad_refresh(self._h, ctypes.c_void_p(grad.data_ptr()),
                                             self._stream(stream)), "tgrad_refresh")
+
+    def refresh_noalloc(self, grad, stream=None):
+        """tgrad_refresh_noalloc: the refresh with its scratch in the library's static
+        device array (no allocation during the call)."""
+        self._check_tensor(grad, "grad")
+        self._check(self._lib.tgrad_refresh_noalloc(self._h, ctypes.c_void_p(grad.data_ptr()),
+                                                    self._stream(stream)), "tgrad_refresh_noalloc")
 
     def capture_delta(self, delta):
         """Test hook (tgrad_debug_capture_delta): while set, every step also writes its

@@ -1498,6 +1498,111 @@ int tgrad_timing_only(tgrad_t* h, int id) {
   return TGRAD_OK;
 }
 
+// ---------------------------------------------------------------- refresh without allocation
+}  // extern "C"
+
+// The scratch of tgrad_refresh_noalloc: one array per GPU for the life of the process. In
+// host code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, once per device (g_scratch_ptr), and only that address is passed on.
+static __device__ __align__(256) unsigned char scratch[TGRAD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::vector<unsigned char*> g_scratch_ptr;   // per device: scratch's device address
+
+// The device address of this device's scratch array (the device is current).
+int scratch_address(tgrad_t* h, unsigned char** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= h->device) g_scratch_ptr.resize(h->device + 1, nullptr);
+  if (!g_scratch_ptr[h->device]) {
+    void* p = nullptr;
+    HIPCHK(h, hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) {
+      h->err = "tgrad_refresh_noalloc: no device address for the scratch array";
+      return TGRAD_EHIP;
+    }
+    g_scratch_ptr[h->device] = (unsigned char*)p;
+  }
+  *out = g_scratch_ptr[h->device];
+  return TGRAD_OK;
+}
+
+// The refresh's scratch carved from the array at `base`: top-k workspace, Gram matrices,
+// then the Gram partial sums with each launch's workgroups capped so that they fit.
+// Returns false (with h->err set) when the refresh needs more than the array holds.
+bool noalloc_ws(tgrad_t* h, unsigned char* base, RefreshWs* ws) {
+  const size_t cap = TGRAD_NOALLOC_SCRATCH_BYTES;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const uint64_t units = topk_units(h->N), chunks = topk_chunks(h->N);
+  size_t off = 0;
+  const size_t o_hist = off;   off += up(2048 * 4);
+  const size_t o_state = off;  off += up(4 * 8);
+  const size_t o_ucount = off; off += up(2 * units * 4);
+  const size_t o_uoff = off;   off += up(2 * units * 4);
+  const size_t o_ctot = off;   off += up(2 * chunks * 4);
+  const size_t o_gram = off;   off += up((size_t)h->gram_stride * h->fmodes.size() * 8);
+  const size_t o_part = off;
+  if (off >= cap) {
+    h->err = "tgrad_refresh_noalloc: the top-k workspace for this N exceeds the scratch array";
+    return false;
+  }
+  const size_t avail = (cap - off) / 8;   // doubles for the partial sums
+  const uint64_t groups = gram_reduce_groups();
+  uint64_t blocks = UINT32_MAX;
+  for (int n : h->fmodes) {
+    const uint64_t K2 = (uint64_t)h->shape[n] * h->P * h->shape[n] * h->P;
+    const uint64_t fit = avail / K2;
+    if (fit <= groups) {
+      h->err = "tgrad_refresh_noalloc: a Gram partial sum exceeds the scratch array";
+      return false;
+    }
+    blocks = std::min<uint64_t>(blocks, fit - groups);
+  }
+  Gram3Args g3;
+  if (h->gram3 && h->can_gram3 && h->k > 0 &&
+      gram3_args(h, (const void*)(uintptr_t)256, h->mask, nullptr, &g3) &&
+      gram3_supported(g3, h->num_cu) && gram3_partial_doubles(g3, h->num_cu) > avail) {
+    h->err = "tgrad_refresh_noalloc: the three-mode Gram partial sums exceed the scratch array";
+    return false;
+  }
+  ws->tw.hist = (uint32_t*)(base + o_hist);
+  ws->tw.state = (uint64_t*)(base + o_state);
+  ws->tw.ucount = (uint32_t*)(base + o_ucount);
+  ws->tw.uoff = (uint32_t*)(base + o_uoff);
+  ws->tw.ctot = (uint32_t*)(base + o_ctot);
+  ws->gram = (double*)(base + o_gram);
+  ws->gram_part = (double*)(base + o_part);
+  ws->masked = true;
+  ws->max_gram_blocks = (uint32_t)std::min<uint64_t>(blocks, UINT32_MAX);
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tgrad_refresh_noalloc(tgrad_t* h, const void* grad, void* stream) {
+  if (!h || !grad || ((uintptr_t)grad & 15u) != 0) return TGRAD_EINVAL;
+  if (h->order == TGRAD_ORDER_LOWRANK_FIRST && h->k > 0 && !h->fmodes.empty()) {
+    h->err = "tgrad_refresh_noalloc: the low-rank-first order needs full-size intermediates";
+    return TGRAD_EINVAL;
+  }
+  DevGuard g(h->device);
+  unsigned char* base = nullptr;
+  int rc = scratch_address(h, &base);
+  if (rc != TGRAD_OK) return rc;
+  RefreshWs ws{};
+  if (!noalloc_ws(h, base, &ws)) return TGRAD_EINVAL;
+  h->cur_stream = (hipStream_t)stream;
+  // per-launch timing would create events: off for this call
+  const bool timing = h->timing;
+  h->timing = false;
+  rc = do_refresh(h, grad, (hipStream_t)stream, ws);
+  h->timing = timing;
+  return rc;
+}
+
 int tgrad_timing_read(tgrad_t* h, int64_t* launches, double* ms, int n_ids) {
   if (!h || n_ids < 0 || n_ids > TGRAD_MAX_KERNEL_IDS) return TGRAD_EINVAL;
   DevGuard g(h->device);
