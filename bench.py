@@ -40,85 +40,42 @@ def esize(dtype):
     return {"f32": 4, "f16": 2, "bf16": 2, "c64": 8}[dtype]
 
 
-def kernel_bytes(wl, proj3=False):
-    """Algorithmic HBM bytes per launch of every step kernel, keyed by kernel name
-    (proj3: the projection's first launch takes the last three modes).
-    Mode products: the input tile read once and the output written once (the operand
-    matrix is negligible); apply: + W read and written, membership bitmask (N/8 B),
-    per-word ranks (N/16 B) and the k sparse updates. Gather: k indices, k gradient
-    values read, k fp32 values written, k zeros written. Adam: g, m, v read and m, v, u
-    written, 4 B each, over core + k values."""
+def unfused_step_bytes(wl):
+    """The step's algorithmic bytes with one launch per kernel of the path and fp32
+    intermediates, no fusion (the whole-step roofline's definition): the COO gather (k
+    indices, k values read, k fp32 values written, k zeros written), one mode product per
+    compressed mode in each chain (input read once, output written once), Adam over core
+    and sparse values (24 B a value), and the last reconstruction's weight update (W read
+    and written, the k indices and k sparse updates read)."""
     P = 2 if wl.dtype == "c64" else 1
     es = esize(wl.dtype)
     N, k = wl.numel, wl.k
     fmodes = [n for n, (I, r) in enumerate(zip(wl.shape, wl.ranks)) if r < I]
     cur = list(wl.shape)
-    proj, rec = [], []
-    psizes = [N]        # tensor size after each projection mode
-    size = N
+    size, total = N, 0
     for j, n in enumerate(reversed(fmodes)):
         out = size // cur[n] * wl.ranks[n]
-        inb = size * P * (es if j == 0 else 4)
-        proj.append(inb + out * P * 4)
+        total += size * P * (es if j == 0 else 4) + out * P * 4
         cur[n] = wl.ranks[n]
         size = out
-        psizes.append(size)
     ncore = size
-    rsizes = [ncore]    # tensor size after each reconstruction mode
     for j, n in enumerate(fmodes):
         out = size // cur[n] * wl.shape[n]
-        b = size * P * 4
-        if j + 1 == len(fmodes):
-            # W read + written, membership mask, per-word ranks, the k sparse updates and
-            # (contiguous output tiles) their k Omega indices
-            b += 2 * N * es + N // 8 + N // 16 + k * P * 4 + k * 4
-        else:
-            b += out * P * 4
-        rec.append(b)
+        total += size * P * 4
+        total += (2 * N * es + k * 4 + k * P * 4) if j + 1 == len(fmodes) else out * P * 4
         cur[n] = wl.shape[n]
         size = out
-        rsizes.append(size)
-    # two trailing modes per launch: input read once, output written once; the first
-    # projection launch also performs the COO gather (k indices read and k fp32 values
-    # written; the gradient values come with the input tile, which is zeroed at Omega in
-    # LDS only)
-    d = len(wl.shape)
-    I1, I2, R1, R2 = wl.shape[d - 2], wl.shape[d - 1], wl.ranks[d - 2], wl.ranks[d - 1]
-    A = N // (I1 * I2)
-    proj2 = A * I1 * I2 * P * es + A * R1 * R2 * P * 4 + k * (4 + 4 * P)
-    # three trailing modes: the same, with the output R0 R1 R2 per index of the leading modes
-    R0 = wl.ranks[d - 3] if d >= 3 else 1
-    U = A // wl.shape[d - 3] if d >= 3 else A
-    proj3_b = A * I1 * I2 * P * es + U * R0 * R1 * R2 * P * 4 + k * (4 + 4 * P)
-    rec2 = A * R1 * R2 * P * 4 + 2 * N * es + N // 8 + N // 16 + k * P * 4 + k * 4
-    flops_proj = []
-    size = N
-    cur = list(wl.shape)
-    for n in reversed(fmodes):
-        flops_proj.append(2 * size * P * wl.ranks[n] * P)
-        size = size // cur[n] * wl.ranks[n]
-        cur[n] = wl.ranks[n]
-    return {
-        "gather_residual": [k * (4 + es + 4 * P + es)],
-        "modeprod_project_first": proj[:1],
-        "modeprod_project": proj[2:] if proj3 else proj[1:],
-        "adam_fused": [(ncore + k) * P * 24],
-        "modeprod_reconstruct": rec[:-1],
-        "modeprod_reconstruct_apply": rec[-1:],
-        "modeprod2_project_first": [proj2],
-        "modeprod3_project_first": [proj3_b],
-        "modeprod2_reconstruct_apply": [rec2],
-        # the projection's last two modes in one launch (fp32 in, core out), and the
-        # reconstruction's first two
-        "modeprod_pair_project": [(psizes[-3] + ncore) * P * 4] if len(psizes) >= 3 else [],
-        "modeprod_pair_reconstruct": [(ncore + rsizes[2]) * P * 4] if len(rsizes) >= 3 else [],
-        "_flops_project": flops_proj,
-        "_ncore": ncore,
-        # the step's work as one launch per kernel of the path, fp32 intermediates and no
-        # fusion: gather, projection chain, Adam, reconstruction chain with the apply
-        "_unfused_step": k * (4 + es + 4 * P + es) * (1 if k else 0) + sum(proj)
-                         + (ncore + k) * P * 24 + sum(rec),
-    }
+    gather = k * (4 + es + 4 * P + es) if k else 0
+    return total + gather + (ncore + k) * P * 24, ncore
+
+
+def by_kernel(launches):
+    """{kernel name: (launches, bytes read + written, flops)} from a launch record."""
+    out = {}
+    for name, _modes, br, bw, fl in launches:
+        n, b, f = out.get(name, (0, 0, 0))
+        out[name] = (n + 1, b + br + bw, f + fl)
+    return out
 
 
 def counter_traffic(kernel):
@@ -271,16 +228,19 @@ def main():
     torch.cuda.synchronize()
 
     # per-kernel breakdown: K steps with every launch bracketed by HIP events (an event
-    # pair per launch lengthens the step, so these steps are not the timed ones)
+    # pair per launch lengthens the step, so these steps are not the timed ones); the
+    # algorithmic bytes and flops of each launch come from the library's record of the
+    # launches the step made
     lib.timing_enable(True, 100000)
     for i in range(K):
         lib.step(W, grads[Wm + i], stream)
     torch.cuda.synchronize()
     rec = lib.timing_read()
-    kb = kernel_bytes(wl, proj3="modeprod3_project_first" in rec)
+    step_launches = lib.last_launches()
+    kb = by_kernel(step_launches)
     # the dominant kernel: the largest share of the step among kernels with one launch
-    # per step (a unique symbol for the profiler) and a byte count
-    single = {n: ms for n, (c, ms) in rec.items() if c == K and n in kb and kb[n]}
+    # per step (a unique symbol for the profiler)
+    single = {n: ms for n, (c, ms) in rec.items() if c == K and n in kb and kb[n][0] == 1}
     dom = max(single, key=single.get)
 
     # the timed steps: events around the dominant kernel's launches only
@@ -306,6 +266,7 @@ def main():
         torch.cuda.synchronize()
         rt.append((time.perf_counter() - r0) * 1e3)
     rrec = lib.timing_read()
+    refresh_launches = by_kernel(lib.last_launches())
     lib.timing_enable(False, 0)
     refresh_ms = float(np.median(rt))
 
@@ -325,35 +286,39 @@ def main():
     copy_gbs = 2.0 * ncp * 4 * 5 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
     del ca, cb
 
-    kernels = {}
-    for name, (n, ms) in rec.items():
-        per_step = n // K if n % K == 0 else n / K
-        avg_ms = ms / n
-        entry = {"launches_per_step": per_step, "avg_ms": round(avg_ms, 5),
-                 "ms_per_step": round(ms / K, 5)}
-        if name in kb and kb[name]:
-            byts = sum(kb[name]) / len(kb[name])           # mean algorithmic bytes per launch
-            gbs = byts / (avg_ms * 1e-3) / 1e9
-            entry.update({"alg_bytes_per_launch": int(byts), "achieved_GBs": round(gbs, 1),
-                          "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
-        kernels[name] = entry
-    refresh_kernels = {name: {"launches": n, "ms": round(ms / args.refresh_reps, 4)}
-                       for name, (n, ms) in rrec.items()}
+    def table(timed, work, reps):
+        """Per kernel: launches, ms, and from the launch record its algorithmic bytes,
+        flops, achieved GB/s and TFLOP/s (bytes and flops of all its launches in one
+        step or refresh over their total time)."""
+        out = {}
+        for name, (n, ms) in timed.items():
+            per = n // reps if n % reps == 0 else n / reps
+            entry = {"launches": per, "avg_ms": round(ms / n, 5), "ms": round(ms / reps, 5)}
+            if name in work:
+                _, byts, fl = work[name]
+                t = ms / reps * 1e-3
+                entry.update({"alg_bytes": int(byts), "achieved_GBs": round(byts / t / 1e9, 1),
+                              "hbm_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4)})
+                if fl:
+                    entry.update({"flops": int(fl), "achieved_TFs": round(fl / t / 1e12, 2)})
+            out[name] = entry
+        return out
+    kernels = table(rec, kb, K)
+    refresh_kernels = table(rrec, refresh_launches, args.refresh_reps)
 
     # the dominant kernel's launches inside the timed steps
     dn, dms = drec[dom]
-    dom_bytes = sum(kb[dom]) / len(kb[dom])
+    dom_bytes = kb[dom][1]
     dom_gbs = dom_bytes / (dms / dn * 1e-3) / 1e9
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                 "traffic": counter_traffic(dom), "avg_ms": round(dms / dn, 5),
-                "launches": dn}
+                "launches": dn, "alg_bytes": int(dom_bytes)}
     # whole-step roofline: the step's algorithmic bytes counted kernel by kernel without
-    # fusion, over the measured step time; the bytes the launched (fused) kernels move
-    # are reported beside it
-    moved_bytes = sum(sum(kb[name]) / len(kb[name]) * v["launches_per_step"]
-                      for name, v in kernels.items() if name in kb and kb[name])
-    step_bytes = kb["_unfused_step"]
+    # fusion, over the measured step time; beside it the bytes the launched (fused)
+    # kernels move by their own algorithmic count
+    moved_bytes = sum(b for _, b, _ in kb.values())
+    step_bytes, ncore = unfused_step_bytes(wl)
     step_frac = step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS
     moved_frac = moved_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS
 
@@ -381,7 +346,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "bf16 FNO spectral-weight gradient (64,64,48,48,25), Tucker ranks "
                                "(32,32,24,24,13), 5% top-k sparse, T=200",
-                   "numel": wl.numel, "k": wl.k, "core_numel": kb["_ncore"],
+                   "numel": wl.numel, "k": wl.k, "core_numel": ncore,
                    "parallelism": "single GPU"},
         "refresh_ms": round(refresh_ms, 3),
         "step_alg_bytes": int(step_bytes),
@@ -391,7 +356,8 @@ def main():
         "roofline": roofline,
         "hbm_copy_GBs": round(copy_gbs, 1),
         "kernels": kernels,
-        "kernels_note": "per-kernel table from K extra steps with every launch timed; the "
+        "kernels_note": "per-kernel table from K extra steps with every launch timed (bytes "
+                        "and flops: the library's record of the launches one step made); the "
                         "timed steps carry events around the roofline kernel only",
         "refresh_kernels": refresh_kernels,
         "multi_tensor": multi,

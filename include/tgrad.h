@@ -310,6 +310,24 @@ int tgrad_load_state(tgrad_t *h, const void *buf, int64_t size);
 #define TGRAD_NOALLOC_SCRATCH_BYTES (48ull << 20)
 int tgrad_refresh_noalloc(tgrad_t *h, const void *grad, void *stream);
 
+/* ---------------------------------------------------------------- launch record.
+ * The kernel launches of the last tgrad_step, tgrad_refresh or tgrad_refresh_noalloc call
+ * on the handle, in issue order (a step that refreshed lists the refresh's first), with
+ * the algorithmic work of each: bytes_read and bytes_written count once every gradient,
+ * weight, intermediate, index, moment and sparse value the launch's part of the method
+ * needs (the membership bitmask and word ranks are counted only where a top-k pass
+ * produces them or a masked Gram reads them); flops are 2 K M per column of each mode
+ * product and Gram (K, M the real sizes of the contracted and produced mode). modes: bit
+ * n set when the launch contracts mode n. Host memory; no device work.
+ * Returns the number of launches (the first min(cap, number) are written to out), or
+ * -1 for a NULL handle, cap < 0 or out NULL with cap > 0. */
+typedef struct tgrad_launch {
+  int32_t kernel;   /* kernel id, see tgrad_kernel_name */
+  int32_t modes;
+  int64_t bytes_read, bytes_written, flops;
+} tgrad_launch;
+int tgrad_last_launches(const tgrad_t *h, tgrad_launch *out, int cap);
+
 /* ---------------------------------------------------------------- timing.
  * When enabled, every kernel launch of step/refresh is bracketed by HIP events on
  * the launch stream (at most max_records launches are kept). tgrad_timing_read

@@ -38,6 +38,12 @@ class Info(ctypes.Structure):
                 ("eig_unconverged", ctypes.c_int64)]
 
 
+class Launch(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("modes", ctypes.c_int32),
+                ("bytes_read", ctypes.c_int64), ("bytes_written", ctypes.c_int64),
+                ("flops", ctypes.c_int64)]
+
+
 SELECT_TOPK, SELECT_RANDK = 0, 1
 SELECTIONS = {"topk": SELECT_TOPK, "randk": SELECT_RANDK}
 
@@ -85,6 +91,7 @@ SIGNATURES = [
     ("tgrad_state_size", _I64, [_P]),
     ("tgrad_save_state", ctypes.c_int, [_P, _P, _I64]),
     ("tgrad_load_state", ctypes.c_int, [_P, _P, _I64]),
+    ("tgrad_last_launches", ctypes.c_int, [_P, ctypes.POINTER(Launch), ctypes.c_int]),
     ("tgrad_timing_enable", ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int]),
     ("tgrad_timing_read", ctypes.c_int, [_P, _P, _P, ctypes.c_int]),
     ("tgrad_timing_only", ctypes.c_int, [_P, ctypes.c_int]),
@@ -369,6 +376,17 @@ class TGrad:
 
     def mark_refreshed(self):
         self._check(self._lib.tgrad_mark_refreshed(self._h), "tgrad_mark_refreshed")
+
+    def last_launches(self):
+        """[(kernel name, modes, bytes read, bytes written, flops)] of the last step or
+        refresh call, in issue order (tgrad_last_launches)."""
+        n = self._lib.tgrad_last_launches(self._h, None, 0)
+        if n < 0:
+            raise TGradError("tgrad_last_launches: invalid handle")
+        arr = (Launch * max(n, 1))()
+        self._lib.tgrad_last_launches(self._h, arr, n)
+        return [(kernel_name(l.kernel), [m for m in range(MAX_NDIM) if (l.modes >> m) & 1],
+                 int(l.bytes_read), int(l.bytes_written), int(l.flops)) for l in arr[:n]]
 
     # ---------------------------------------------------------------- timing
     def timing_enable(self, enable: bool = True, max_records: int = 100000):

@@ -116,6 +116,9 @@ struct tgrad_handle {
   int64_t state_bytes = 0, ws_bytes = 0;
   std::string err;
 
+  // the launches of the last step or refresh call with their algorithmic work
+  std::vector<tgrad_launch> launches;
+
   bool timing = false;
   int timing_only = -1;   // >= 0: only launches of this kernel id are timed
   int max_rec = 0;
@@ -257,6 +260,54 @@ struct Mark {
   ~Mark() { mark_cb(h, id, false); }
 };
 
+void record(tgrad_t* h, int kid, int modes, uint64_t br, uint64_t bw, uint64_t fl) {
+  tgrad_launch l;
+  l.kernel = kid;
+  l.modes = modes;
+  l.bytes_read = (int64_t)br;
+  l.bytes_written = (int64_t)bw;
+  l.flops = (int64_t)fl;
+  h->launches.push_back(l);
+}
+
+// Record a mode-product launch that contracts `modes` (in order) of a tensor whose
+// current sizes are `cur`: towards the ranks (projection) or the full sizes
+// (reconstruction). Its algorithmic bytes: the input once (es_in bytes a value) and the
+// fp32 output once; with `gather`, the k Omega indices read and the k sparse values
+// written; with `apply`, the weights read and written (instead of an output), the k
+// indices and k sparse updates read. Flops: 2 K M per column of each product, K and M
+// the real sizes (times P) of the contracted and produced mode.
+void account_chain(tgrad_t* h, int kid, const int64_t* cur, const std::vector<int>& modes,
+                   bool projection, uint64_t es_in, bool gather, bool apply) {
+  const uint64_t P = h->P;
+  int64_t c[TGRAD_MAX_NDIM];
+  uint64_t in = 1;
+  for (int i = 0; i < h->d; ++i) {
+    c[i] = cur[i];
+    in *= (uint64_t)cur[i];
+  }
+  uint64_t fl = 0, size = in;
+  int mbits = 0;
+  for (int n : modes) {
+    const uint64_t tgt = (uint64_t)(projection ? h->ranks[n] : h->shape[n]);
+    fl += 2 * (size / (uint64_t)c[n]) * ((uint64_t)c[n] * P) * (tgt * P);
+    size = size / (uint64_t)c[n] * tgt;
+    c[n] = (int64_t)tgt;
+    mbits |= 1 << n;
+  }
+  uint64_t br = in * P * es_in, bw = apply ? 0 : size * P * 4;
+  if (gather) {
+    br += h->k * 4;
+    bw += h->k * P * 4;
+  }
+  if (apply) {
+    const uint64_t esw = h->dtype == TGRAD_C64 ? 4 : dt_bytes(h->dtype);
+    br += h->N * P * esw + h->k * 4 + h->k * P * 4;
+    bw += h->N * P * esw;
+  }
+  record(h, kid, mbits, br, bw, fl);
+}
+
 void host_operands(uint32_t I, uint32_t r, uint32_t P, const float* U, float* Mp, float* Mr) {
   if (P == 1) {
     for (uint32_t i = 0; i < I; ++i)
@@ -384,6 +435,20 @@ int select_omega(tgrad_t* h, const TopkWs& tw, const void* src, int dt, void* re
   const uint64_t rk_base = h->seed + gamma * ((serves << 32) + 1ull);
   HIPCHK(h, launch_topk(dt, src, h->N, (uint32_t)h->k, tw, h->omega, h->mask, h->rank, resid,
                         h->selection == TGRAD_SELECT_RANDK, rk_base, s, mark_cb, h));
+  {
+    // the radix passes read the keys' source (magnitudes: 11 bits a pass), the count pass
+    // once more, the compaction once more (rand-k keys need no read, except for the
+    // residual); the compaction writes Omega, its bitmask and word ranks, and the residual
+    const bool rk = h->selection == TGRAD_SELECT_RANDK;
+    const uint64_t es = dt == DT_C64 ? 8 : (dt == DT_F32 ? 4 : 2);
+    const int bits = rk ? 31 : (dt == DT_C64 ? 63 : (dt == DT_F32 ? 31 : 15));
+    const uint64_t passes = (uint64_t)((bits + 10) / 11);
+    const uint64_t src_b = rk ? 0 : h->N * es;
+    record(h, KID_TOPK_HIST, 0, passes * src_b, 0, 0);
+    record(h, KID_TOPK_COUNT, 0, src_b, 0, 0);
+    record(h, KID_TOPK_COMPACT, 0, (rk && !resid) ? 0 : h->N * es,
+           h->k * 4 + h->N / 8 + h->N / 16 + (resid ? h->N * es : 0), 0);
+  }
   if (h->remap) {
     Mark m(h, KID_REMAP);
     HIPCHK(h, launch_remap_moments(h->mask_prev, h->rank_prev, h->omega, (uint32_t)h->k,
@@ -466,6 +531,8 @@ int do_refresh(tgrad_t* h, const void* grad, hipStream_t s, const RefreshWs& ws)
       g.partial = ws.gram_part;
       g.out = out;
       HIPCHK(h, launch_gram(g, h->num_cu, s, mark_cb, h));
+      record(h, KID_GRAM, 1 << n, h->N * dt_bytes(h->dtype) + (rmask ? h->N / 8 : 0), 0,
+             2 * (h->N / g.I) * ((uint64_t)g.I * h->P) * ((uint64_t)g.I * h->P));
     }
     EigArgs& e = eig[ne];
     e.status = h->eig_status + ne;
@@ -479,10 +546,18 @@ int do_refresh(tgrad_t* h, const void* grad, hipStream_t s, const RefreshWs& ws)
     e.Mrec = h->Mr[n];
     e.eigvals = h->eig[n];
   }
-  if (tail3) HIPCHK(h, launch_gram3(g3, h->num_cu, s, mark_cb, h));
+  if (tail3) {
+    HIPCHK(h, launch_gram3(g3, h->num_cu, s, mark_cb, h));
+    const uint64_t I3[3] = {g3.Ia, g3.Ib, g3.Ic};
+    uint64_t fl = 0;
+    for (int m = 0; m < 3; ++m) fl += 2 * (h->N / I3[m]) * I3[m] * I3[m];
+    record(h, KID_GRAM3, 7 << (h->d - 3), h->N * dt_bytes(h->dtype) + (rmask ? h->N / 8 : 0), 0,
+           fl);
+  }
   if (ne) {
     Mark m(h, KID_EIG);
     HIPCHK(h, launch_eig(eig, ne, s));
+    record(h, KID_EIG, 0, 0, 0, 0);
   }
   if (lowrank_first) {
     if (h->selection == TGRAD_SELECT_RANDK) {
@@ -807,6 +882,7 @@ int tgrad_refresh(tgrad_t* h, const void* grad, void* stream) {
   if (!h || !grad || ((uintptr_t)grad & 15u) != 0) return TGRAD_EINVAL;
   DevGuard g(h->device);
   h->cur_stream = (hipStream_t)stream;
+  h->launches.clear();
   return do_refresh(h, grad, (hipStream_t)stream, handle_ws(h));
 }
 
@@ -858,6 +934,8 @@ int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s) {
       }
       Mark m(h, KID_PROJECT_FUSED3);
       HIPCHK(h, launch_slab3(mp, h->num_cu, s));
+      account_chain(h, KID_PROJECT_FUSED3, cur, proj[j], true, xdt == DT_F32 ? 4 : 2,
+                    j == 0 && gather, false);
       cur[d - 3] = h->ranks[d - 3];
       cur[d - 2] = h->ranks[d - 2];
       cur[d - 1] = h->ranks[d - 1];
@@ -873,6 +951,7 @@ int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s) {
       mp.J1 = (uint32_t)h->ranks[n0 + 1];
       Mark m(h, KID_PROJECT_PAIR);
       HIPCHK(h, launch_pair(mp, s));
+      account_chain(h, KID_PROJECT_PAIR, cur, proj[j], true, 4, false, false);
       cur[n0] = h->ranks[n0];
       cur[n0 + 1] = h->ranks[n0 + 1];
     } else if (proj[j].size() == 2) {
@@ -905,6 +984,8 @@ int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s) {
         HIPCHK(h, launch_slab2(mp, h->num_cu, s));
       else
         HIPCHK(h, launch_modeprod2(mp, h->num_cu, s));
+      account_chain(h, KID_PROJECT_FUSED2, cur, proj[j], true, xdt == DT_F32 ? 4 : 2,
+                    j == 0 && gather, false);
       cur[d - 2] = h->ranks[d - 2];
       cur[d - 1] = h->ranks[d - 1];
     } else {
@@ -920,6 +1001,8 @@ int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s) {
       mp.Y = Y;
       Mark m(h, j == 0 ? KID_PROJECT_FIRST : KID_PROJECT);
       HIPCHK(h, launch_modeprod(mp, h->num_cu, s));
+      account_chain(h, j == 0 ? KID_PROJECT_FIRST : KID_PROJECT, cur, proj[j], true,
+                    xdt == DT_F32 ? 4 : 2, false, false);
       cur[n] = h->ranks[n];
     }
     X = Y;
@@ -960,6 +1043,7 @@ int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, fl
       mp.J1 = (uint32_t)h->shape[n0 + 1];
       Mark m(h, KID_RECON_PAIR);
       HIPCHK(h, launch_pair(mp, s));
+      account_chain(h, KID_RECON_PAIR, cur, rec[j], false, 4, false, false);
       cur[n0] = h->shape[n0];
       cur[n0 + 1] = h->shape[n0 + 1];
     } else if (rec[j].size() == 2) {
@@ -996,6 +1080,8 @@ int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, fl
         HIPCHK(h, launch_slab2(mp, h->num_cu, s));
       else
         HIPCHK(h, launch_modeprod2(mp, h->num_cu, s));
+      account_chain(h, app ? KID_RECON_FUSED2_APPLY : KID_RECON_FUSED2, cur, rec[j], false, 4,
+                    false, app);
       cur[d - 2] = h->shape[d - 2];
       cur[d - 1] = h->shape[d - 1];
     } else {
@@ -1022,6 +1108,8 @@ int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, fl
       mp.delta = app ? h->delta_cap : nullptr;
       Mark m(h, app ? KID_RECON_APPLY : KID_RECONSTRUCT);
       HIPCHK(h, launch_modeprod(mp, h->num_cu, s));
+      account_chain(h, app ? KID_RECON_APPLY : KID_RECONSTRUCT, cur, rec[j], false, 4, false,
+                    app);
       cur[n] = h->shape[n];
     }
     X = Y;
@@ -1039,6 +1127,7 @@ int tgrad_step(tgrad_t* h, void* weight, const void* grad, void* stream) {
   DevGuard gd(h->device);
   hipStream_t s = (hipStream_t)stream;
   h->cur_stream = s;
+  h->launches.clear();
   // the step count advances only when every launch of the step has been enqueued, so a
   // failed call can be repeated (the refresh it needs is then still due)
   const int64_t t = h->t + 1;
@@ -1069,6 +1158,8 @@ int step_body(tgrad_t* h, void* weight, const void* grad, int64_t t, hipStream_t
       if ((rc = run_reconstruction(h, h->core, false, nullptr, h->lbuf, s)) != TGRAD_OK) return rc;
       Mark m(h, KID_GATHER);
       HIPCHK(h, launch_gather_sub(h->dtype, grad, h->lbuf, h->omega, (uint32_t)h->k, h->S, s));
+      // k indices, k values of G and of L read; k fp32 values written
+      record(h, KID_GATHER, 0, h->k * (4 + dt_bytes(h->dtype) + 4 * P), h->k * P * 4, 0);
     } else {
       // every mode full rank: L = G, so S = 0
       HIPCHK(h, launch_fill_u32((uint32_t*)h->S, h->k * P, 0u, s));
@@ -1090,6 +1181,10 @@ int step_body(tgrad_t* h, void* weight, const void* grad, int64_t t, hipStream_t
                                hipMemcpyDeviceToDevice, s));
       Mark m(h, KID_GATHER);
       HIPCHK(h, launch_gather(h->dtype, h->gcopy, h->omega, (uint32_t)h->k, h->S, s));
+      // k indices and values read, k fp32 values written and k values zeroed (on the
+      // copy of grad, whose device copy is not a kernel launch)
+      record(h, KID_GATHER, 0, h->k * (4 + dt_bytes(h->dtype)), h->k * (P * 4 + dt_bytes(h->dtype)),
+             0);
       G0 = h->gcopy;
     }
     if (nf && (rc = run_projection(h, G0, gather_fused, s)) != TGRAD_OK) return rc;
@@ -1109,6 +1204,11 @@ int step_body(tgrad_t* h, void* weight, const void* grad, int64_t t, hipStream_t
     const int cdt = nf ? DT_F32 : h->dtype;
     HIPCHK(h, launch_adam(cdt, gcore, h->ucore, h->mC, h->vC, h->ncore * P, h->S, h->mS, h->vS,
                           h->k * P, a, s));
+    // g, m, v read and u, m, v written, fp32, over the core and the k sparse values (the
+    // dense case reads g in its storage type)
+    const uint64_t nc = h->ncore * P, nsv = h->k * P;
+    record(h, KID_ADAM, 0, nc * (nf ? 4 : dt_bytes(h->dtype) / P) + nc * 8 + nsv * 12,
+           (nc + nsv) * 12, 0);
   }
   if (nf == 0) {
     const float lr = (float)h->lr;
@@ -1116,6 +1216,8 @@ int step_body(tgrad_t* h, void* weight, const void* grad, int64_t t, hipStream_t
     Mark m(h, KID_APPLY_DENSE);
     HIPCHK(h, launch_apply_dense(h->dtype, weight, h->ucore, h->mask, h->rank, h->S, h->N, lr,
                                  decay, h->k > 0, h->delta_cap, s));
+    record(h, KID_APPLY_DENSE, 0, h->N * (dt_bytes(h->dtype) + P * 4) + h->k * P * 4,
+           h->N * dt_bytes(h->dtype), 0);
     return TGRAD_OK;
   }
   return run_reconstruction(h, h->ucore, true, weight, nullptr, s);
@@ -1485,6 +1587,13 @@ int tgrad_mark_refreshed(tgrad_t* h) {
   return TGRAD_OK;
 }
 
+int tgrad_last_launches(const tgrad_t* h, tgrad_launch* out, int cap) {
+  if (!h || cap < 0 || (cap > 0 && !out)) return -1;
+  const int n = (int)h->launches.size();
+  for (int i = 0; i < n && i < cap; ++i) out[i] = h->launches[i];
+  return n;
+}
+
 int tgrad_timing_enable(tgrad_t* h, int enable, int max_records) {
   if (!h || max_records < 0) return TGRAD_EINVAL;
   h->timing = enable != 0;
@@ -1595,6 +1704,7 @@ int tgrad_refresh_noalloc(tgrad_t* h, const void* grad, void* stream) {
   RefreshWs ws{};
   if (!noalloc_ws(h, base, &ws)) return TGRAD_EINVAL;
   h->cur_stream = (hipStream_t)stream;
+  h->launches.clear();
   // per-launch timing would create events: off for this call
   const bool timing = h->timing;
   h->timing = false;

@@ -448,6 +448,52 @@ def test_timing_records_every_kernel():
     assert rec["gather_residual"][0] == 1
 
 
+def test_launch_record_matches_the_launches():
+    """tgrad_last_launches lists exactly the launches the timing records see, and on the
+    one-mode-per-launch plan its algorithmic bytes and flops are the hand count: each
+    mode product reads its input once and writes its output once (fp32), the gather reads
+    k indices and k values and writes k fp32 values and k zeros, Adam moves 24 B per core
+    and sparse value, the last product also reads and writes W and reads the k indices
+    and sparse updates."""
+    wl = F32_32x32x16x16
+    lib = make_lib(wl)
+    assert lib.set_fusion(False)
+    gs = GradStream(wl)
+    W = dev(init_weights(wl), wl.dtype)
+    lib.step(W, dev(gs.next(), wl.dtype))          # t = 1 refreshes
+    names = [n for n, *_ in lib.last_launches()]
+    assert names[:3] == ["topk_hist", "topk_count", "topk_compact"] and "eig_jacobi" in names
+    lib.timing_enable(True)
+    lib.step(W, dev(gs.next(), wl.dtype))
+    rec = lib.timing_read()
+    got = lib.last_launches()
+    counts = {}
+    for n, *_ in got:
+        counts[n] = counts.get(n, 0) + 1
+    assert counts == {n: c for n, (c, _) in rec.items()}
+    N, k, es = wl.numel, wl.k, 4
+    shape, ranks = list(wl.shape), list(wl.ranks)
+    exp = [("gather_residual", k * (4 + es) + k * (4 + es), 0)]
+    cur, size = list(shape), N
+    for j, n in enumerate([3, 2, 1, 0]):
+        out = size // cur[n] * ranks[n]
+        exp.append(("modeprod_project_first" if j == 0 else "modeprod_project",
+                    size * 4 + out * 4, 2 * (size // cur[n]) * cur[n] * ranks[n]))
+        cur[n] = ranks[n]
+        size = out
+    ncore = size
+    exp.append(("adam_fused", (ncore + k) * 24, 0))
+    for j, n in enumerate([0, 1, 2, 3]):
+        out = size // cur[n] * shape[n]
+        last = j == 3
+        b = size * 4 + ((2 * N * es + 8 * k) if last else out * 4)
+        exp.append(("modeprod_reconstruct_apply" if last else "modeprod_reconstruct", b,
+                    2 * (size // cur[n]) * cur[n] * shape[n]))
+        cur[n] = shape[n]
+        size = out
+    assert [(n, br + bw, fl) for n, _m, br, bw, fl in got] == exp
+
+
 def test_timing_only_one_kernel():
     wl = F32_32x32x16x16
     lib = make_lib(wl)
