@@ -185,6 +185,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-multi-tensor", action="store_true",
                     help="skip the 4-layer fp16 sequential vs tgrad_step_many measurement")
+    ap.add_argument("--plan", type=int, default=None,
+                    help="launch plan (tgrad_set_fusion value); default: the library's")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -214,6 +216,8 @@ def main():
     torch.cuda.synchronize()
 
     lib = tg.TGrad(wl.shape, wl.ranks, wl.dtype, wl.sparse_ratio, wl.T, wl.lr, wl.betas, wl.eps)
+    if args.plan is not None and not lib.set_fusion(args.plan):
+        raise SystemExit(f"launch plan {args.plan} does not apply to this workload")
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -347,6 +351,7 @@ def main():
         "config": {"workload": "bf16 FNO spectral-weight gradient (64,64,48,48,25), Tucker ranks "
                                "(32,32,24,24,13), 5% top-k sparse, T=200",
                    "numel": wl.numel, "k": wl.k, "core_numel": ncore,
+                   "launch_plan": "library default" if args.plan is None else args.plan,
                    "parallelism": "single GPU"},
         "refresh_ms": round(refresh_ms, 3),
         "step_alg_bytes": int(step_bytes),

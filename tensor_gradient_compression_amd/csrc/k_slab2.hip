@@ -33,6 +33,7 @@
 #include <type_traits>
 
 #include "tg_common.h"
+#include "k_slab_common.h"
 
 namespace tg {
 
@@ -41,14 +42,6 @@ namespace {
 constexpr int WPB = 4;            // waves per workgroup
 constexpr int NT = WPB * 64;
 
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-// LDS-qualified pointers: accesses through them compile to ds_* instructions (a
-// generic pointer would give flat accesses, which also count against vmcnt)
-#define LDS __attribute__((address_space(3)))
 
 struct S2K {
   const void* X;        // projection: the gradient (A, I1, I2), only read
@@ -131,33 +124,11 @@ __device__ __forceinline__ u32x4 run_keep(uint32_t lg, uint32_t n) {
   return m;
 }
 
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-__device__ __forceinline__ void wave_fence() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_wave_barrier();
-  __asm__ volatile("" ::: "memory");
-}
-
-// nchunks 16-byte pieces from src to dst (wave-uniform), one per lane per instruction
-__device__ __forceinline__ void wave_dma(const void* src, uint32_t nchunks, LDS unsigned char* dst,
-                                        uint32_t lane) {
-  for (uint32_t q0 = 0; q0 < nchunks; q0 += 64)
-    if (q0 + lane < nchunks)
-      __builtin_amdgcn_global_load_lds((const unsigned char*)src + (size_t)(q0 + lane) * 16,
-                                       (lds_void*)(dst + (size_t)q0 * 16), 16, 0, 0);
-}
 
 // Wave w takes slabs w, w + TW, w + 2 TW, ... (TW = waves in the grid), so the whole
 // grid streams through one moving window of the tensor.
 __device__ __forceinline__ uint32_t total_waves() { return gridDim.x * (uint32_t)WPB; }
 
-// Omega rank of element e from its bitmask word and word rank; kS past the end
-__device__ __forceinline__ uint64_t rank_at(uint64_t word, uint32_t wr, uint64_t e, uint64_t N,
-                                            uint64_t kS) {
-  if (e >= N) return kS;
-  return wr + (uint64_t)__popcll(word & ((1ull << (e & 63)) - 1ull));
-}
 
 // 16-bit storage types seen as their bit patterns (LDS holds raw 16-bit words)
 template <typename T> struct Bits16;
@@ -178,50 +149,6 @@ template <> struct Bits16<_Float16> {
   }
 };
 
-// Omega range of slab s: [J(s), J(s + 1)) with J(s) = Omega rank of element s * slab_e.
-// A wave keeps the current slab's range, the next slab's range, the first NOM * 64
-// indices (and N_S) of the next slab's range, and the bitmask words and ranks that
-// bound the slab after it; entries past NOM * 64 in one slab are read directly.
-constexpr int NOM = 3;
-
-// Two slots, used alternately by consecutive slabs of a wave; the slab loops are unrolled
-// by two so that a slot index is a compile-time constant and the prefetched entries are
-// never copied between registers (a copy would have to wait for every load in flight,
-// the next slab's transfer included).
-// Bitmask words and word ranks at the start (lane 0) and the end (lane 1) of a slab,
-// fetched with vector loads: they retire on vmcnt with the slab transfers (scalar loads
-// would retire on lgkmcnt, out of order, so every wait on LDS traffic after them would
-// also wait for their memory round trip). Read out with lane_u64 / readlane after the
-// next vmcnt wait.
-struct BoundsV {
-  uint64_t m = 0;
-  uint32_t r = 0;
-};
-__device__ __forceinline__ BoundsV load_bounds(const uint64_t* mask, const uint32_t* rank,
-                                               uint64_t elo, uint64_t slab_e, uint64_t N,
-                                               uint32_t lane) {
-  const uint64_t ehi = elo + slab_e;
-  const uint64_t wl = elo >> 6, wh = ehi < N ? ehi >> 6 : 0;
-  const uint64_t idx = lane == 0 ? wl : wh;
-  BoundsV b;
-  b.m = mask[idx];
-  b.r = rank[idx];
-  return b;
-}
-__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-struct OmegaPipe {
-  uint64_t lo[2] = {0, 0}, hi[2] = {0, 0};   // Omega ranges of the slabs in the two slots
-  BoundsV bw;                     // the slab after: bounds (lane 0: start, lane 1: end)
-  uint32_t om[2][NOM];
-  float us[2][NOM];
-};
-template <int V>
-using Slot = std::integral_constant<int, V>;
 
 // ------------------------------------------------------------------ projection
 // NRB1: 16-row blocks of I1 (I1 <= 16 NRB1 <= 64); NRB2: 16-row blocks of R1 (<= 32).
@@ -975,14 +902,14 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
   write_unit();
 }
 
+uint32_t al16(uint32_t x) { return (x + 15u) & ~15u; }
+
 struct Plan3s {
   S3K k;
   size_t lds;
   int nrb1, nrb2, ntw;
   bool ok;
 };
-
-uint32_t al16(uint32_t x) { return (x + 15u) & ~15u; }
 
 Plan3s plan3s(const ModeProd2& mp) {
   Plan3s p{};
@@ -1178,6 +1105,8 @@ hipError_t rec_go(const Plan2s& p, hipStream_t s) {
 bool slab2_supported(const ModeProd2& mp, int num_cu) { return plan2s(mp, num_cu).ok; }
 
 bool slab3_supported(const ModeProd2& mp) { return plan3s(mp).ok; }
+
+
 
 hipError_t launch_slab3(const ModeProd2& mp, int num_cu, hipStream_t s) {
   Plan3s p = plan3s(mp);

@@ -60,7 +60,8 @@ enum KernelId {
   KID_TOPK_COMPACT, KID_MASK_FROM_OMEGA, KID_GATHER, KID_PROJECT, KID_ADAM,
   KID_RECONSTRUCT, KID_RECON_APPLY, KID_APPLY_DENSE, KID_GRAM, KID_GRAM_REDUCE,
   KID_EIG, KID_FILL, KID_PROJECT_FIRST, KID_PROJECT_FUSED2, KID_RECON_FUSED2_APPLY,
-  KID_RECON_FUSED2, KID_REMAP, KID_PROJECT_FUSED3, KID_GRAM3, KID_PROJECT_PAIR, KID_RECON_PAIR, KID_COUNT_
+  KID_RECON_FUSED2, KID_REMAP, KID_PROJECT_FUSED3, KID_GRAM3, KID_PROJECT_PAIR, KID_RECON_PAIR,
+  KID_RECON_FUSED3_APPLY, KID_COUNT_
 };
 
 // ---------------------------------------------------------------- launchers
@@ -190,6 +191,15 @@ hipError_t launch_slab2(const ModeProd2& mp, int num_cu, hipStream_t s);
 // kernel.
 bool slab3_supported(const ModeProd2& mp);
 hipError_t launch_slab3(const ModeProd2& mp, int num_cu, hipStream_t s);
+// The reconstruction's last three modes with the sparse merge and the weight update in
+// one launch (16-bit weights): a workgroup of 12 waves per index of the leading modes at
+// a time. mp: recon = 1, apply = 1, I0..I2 the core-side and R0..R2 the full sizes of the
+// three modes, A counts (unit, core-side index of mode d-2) blocks, M0..M2 the
+// reconstruction operands (full x core). Supported when the full size of mode d-2 is a
+// multiple of 12 up to 64, its rank is at most 32, the two trailing modes fit the slab
+// kernel, and the buffers are 16-byte aligned.
+bool rec3_supported(const ModeProd2& mp);
+hipError_t launch_rec3(const ModeProd2& mp, int num_cu, hipStream_t s);
 
 // Two neighbouring mode products (n, n+1) of a real fp32 tensor viewed as (A, I0, I1, C)
 // in one launch: Y[a, j0, j1, c] = sum_i0 M0[j0, i0] sum_i1 M1[j1, i1] X[a, i0, i1, c]

@@ -65,6 +65,8 @@ struct tgrad_handle {
   bool slab2 = true;         // 16-bit data: the wave-per-slab two-mode kernels where they fit
   bool can_slab3 = false;    // the projection's first launch can also take mode d-3
   bool slab3 = true;         // use it
+  bool can_rec3 = false;     // the reconstruction's last launch can also take mode d-3
+  bool rec3 = false;         // use it (set_fusion 4)
   bool can_gram3 = false;    // refresh: the last three modes' Grams from one read
   bool gram3 = true;         // use it
   // refresh: the Gram kernels read the gradient and clear Omega's entries in their staged
@@ -353,12 +355,13 @@ bool is_lead_pair(const tgrad_t* h, const std::vector<int>& g) {
 }
 
 void build_chain(const tgrad_t* h, bool fuse, bool proj3, std::vector<std::vector<int>>& proj,
-                 std::vector<std::vector<int>>& rec, bool pairs = true) {
+                 std::vector<std::vector<int>>& rec, bool pairs = true, bool rec3 = false) {
   proj.clear();
   rec.clear();
   const int nf = (int)h->fmodes.size();
   const int d = h->d;
   proj3 = proj3 && fuse;
+  rec3 = rec3 && fuse;
   if (proj3) proj.push_back({d - 1, d - 2, d - 3});
   else if (fuse) proj.push_back({d - 1, d - 2});
   for (int j = nf - 1; j >= 0; --j) {
@@ -368,10 +371,11 @@ void build_chain(const tgrad_t* h, bool fuse, bool proj3, std::vector<std::vecto
   }
   for (int j = 0; j < nf; ++j) {
     const int n = h->fmodes[j];
-    if (fuse && n >= d - 2) continue;
+    if ((fuse && n >= d - 2) || (rec3 && n == d - 3)) continue;
     rec.push_back({n});
   }
-  if (fuse) rec.push_back({d - 2, d - 1});
+  if (rec3) rec.push_back({d - 3, d - 2, d - 1});
+  else if (fuse) rec.push_back({d - 2, d - 1});
   if (!(fuse && pairs && h->pairs && h->P == 1)) return;
   // neighbouring single modes after the first group (projection) and before the last
   // (reconstruction) become one k_pair launch where it applies to their sizes there
@@ -413,6 +417,10 @@ void build_chain(const tgrad_t* h, bool fuse, bool proj3, std::vector<std::vecto
 // The three-mode projection launch for input X0 (16-byte aligned for its transfers).
 bool use_proj3(const tgrad_t* h, const void* X0) {
   return h->fuse && h->slab2 && h->slab3 && h->can_slab3 && ((uintptr_t)X0 % 16) == 0;
+}
+// The three-mode reconstruction + apply launch for the weights W (16-byte aligned).
+bool use_rec3(const tgrad_t* h, bool apply, const void* W) {
+  return apply && h->fuse && h->slab2 && h->rec3 && h->can_rec3 && ((uintptr_t)W % 16) == 0;
 }
 
 int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s);
@@ -604,7 +612,7 @@ const char* tgrad_kernel_name(int id) {
       "gram_reduce", "eig_jacobi", "fill", "modeprod_project_first",
       "modeprod2_project_first", "modeprod2_reconstruct_apply", "modeprod2_reconstruct",
       "remap_moments", "modeprod3_project_first", "gram3_tail", "modeprod_pair_project",
-      "modeprod_pair_reconstruct"};
+      "modeprod_pair_reconstruct", "modeprod3_reconstruct_apply"};
   if (id < 0 || id >= KID_COUNT_) return "";
   return names[id];
 }
@@ -693,6 +701,23 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
         p3.I0 = (uint32_t)shape[d - 3];
         p3.R0 = (uint32_t)tucker_ranks[d - 3];
         h->can_slab3 = slab3_supported(p3);
+        // the reconstruction's last three modes (core-side sizes in I, full in R)
+        ModeProd2 r3{};
+        r3.X = (const void*)(uintptr_t)256;
+        r3.W = (void*)(uintptr_t)256;
+        r3.in_dt = DT_F32;
+        r3.w_dt = pp.in_dt;
+        r3.P = h->P;
+        r3.recon = 1;
+        r3.apply = 1;
+        r3.A = (uint32_t)(A / shape[d - 3] * tucker_ranks[d - 3]);
+        r3.I0 = (uint32_t)tucker_ranks[d - 3];
+        r3.I1 = (uint32_t)tucker_ranks[d - 2];
+        r3.I2 = (uint32_t)tucker_ranks[d - 1];
+        r3.R0 = (uint32_t)shape[d - 3];
+        r3.R1 = (uint32_t)shape[d - 2];
+        r3.R2 = (uint32_t)shape[d - 1];
+        h->can_rec3 = rec3_supported(r3);
       }
     }
   }
@@ -1019,7 +1044,7 @@ int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, fl
                        hipStream_t s) {
   const uint32_t P = h->P;
   std::vector<std::vector<int>> proj, rec;
-  build_chain(h, h->fuse, false, proj, rec);
+  build_chain(h, h->fuse, false, proj, rec, true, use_rec3(h, apply, weight));
   int64_t cur[TGRAD_MAX_NDIM];
   for (int i = 0; i < h->d; ++i) cur[i] = h->shape[i];
   for (int n : h->fmodes) cur[n] = h->ranks[n];
@@ -1031,7 +1056,45 @@ int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, fl
     const bool last = (j + 1 == rec.size());
     const bool app = last && apply;
     float* Y = last ? (apply ? nullptr : out) : h->buf[which];
-    if (is_lead_pair(h, rec[j])) {
+    if (rec[j].size() == 3) {
+      // the last three modes with the merge and the weight update (last launch, apply)
+      const int d = h->d;
+      ModeProd2 mp{};
+      mp.X = X;
+      mp.in_dt = DT_F32;
+      mp.P = P;
+      uint32_t A, I, B;
+      view(cur, d, d - 2, &A, &I, &B);
+      mp.A = A;
+      mp.I0 = (uint32_t)cur[d - 3];
+      mp.I1 = (uint32_t)cur[d - 2];
+      mp.I2 = (uint32_t)cur[d - 1];
+      mp.R0 = (uint32_t)h->shape[d - 3];
+      mp.R1 = (uint32_t)h->shape[d - 2];
+      mp.R2 = (uint32_t)h->shape[d - 1];
+      mp.recon = 1;
+      mp.M0 = h->Mr[d - 3];
+      mp.M1 = h->Mr[d - 2];
+      mp.M2 = h->Mr[d - 1];
+      mp.apply = 1;
+      mp.W = weight;
+      mp.w_dt = h->dtype;
+      mp.mask = h->mask;
+      mp.rank = h->rank;
+      mp.uS = h->S;
+      mp.omega = h->omega;
+      mp.kS = h->k;
+      mp.lr = lr;
+      mp.decay = decay;
+      mp.has_sparse = h->k > 0;
+      mp.delta = h->delta_cap;
+      Mark m(h, KID_RECON_FUSED3_APPLY);
+      HIPCHK(h, launch_rec3(mp, h->num_cu, s));
+      account_chain(h, KID_RECON_FUSED3_APPLY, cur, rec[j], false, 4, false, true);
+      cur[d - 3] = h->shape[d - 3];
+      cur[d - 2] = h->shape[d - 2];
+      cur[d - 1] = h->shape[d - 1];
+    } else if (is_lead_pair(h, rec[j])) {
       const int n0 = std::min(rec[j][0], rec[j][1]);
       ModePair mp{};
       pair_view(cur, h->d, n0, &mp);
@@ -1552,7 +1615,7 @@ int tgrad_set_options(tgrad_t* h, const tgrad_options* o) {
 }
 
 int tgrad_set_fusion(tgrad_t* h, int enable) {
-  if (!h || enable < 0 || enable > 3) return TGRAD_EINVAL;
+  if (!h || enable < 0 || enable > 4) return TGRAD_EINVAL;
   if (enable && !h->can_fuse) return TGRAD_EINVAL;
   if (!enable && h->k > 0 && !h->gcopy) {
     DevGuard g(h->device);
@@ -1562,7 +1625,8 @@ int tgrad_set_fusion(tgrad_t* h, int enable) {
   }
   h->fuse = enable != 0;
   h->slab2 = enable != 2;
-  h->slab3 = enable == 1;
+  h->slab3 = enable == 1 || enable == 4;
+  h->rec3 = enable == 4;
   return TGRAD_OK;
 }
 

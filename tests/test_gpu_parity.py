@@ -145,6 +145,13 @@ FACTOR_CASES = [
     # four output column blocks per wave (R1 R2 = 512); R0 = 32 over four rounds
     ("bf16-slab3-wide-core", custom((2, 16, 40, 17), "bf16", (1, 8, 32, 16), 0.05)),
     ("bf16-slab3-r0-32", custom((2, 64, 16, 8), "bf16", (1, 32, 8, 4), 0.05)),
+    # ... and whose mode d-2 (I0 a multiple of 12) joins the reconstruction's last launch
+    # (12 waves a unit, rounds of 12 slabs): 3 rounds a unit with ragged row and column
+    # blocks; one round a unit; k = 0; more units than the grid has workgroups
+    ("bf16-rec3-36x40x17", custom((3, 36, 40, 17), "bf16", (2, 18, 20, 9), 0.05)),
+    ("f16-rec3-12x24x16", custom((5, 12, 24, 16), "f16", (3, 6, 12, 8), 0.05)),
+    ("bf16-rec3-k0", custom((2, 24, 32, 8), "bf16", (1, 12, 16, 4), 0.0)),
+    ("bf16-rec3-300-units", custom((300, 12, 24, 8), "bf16", (300, 6, 12, 4), 0.05)),
     ("f16-64", custom((64, 20, 9), "f16", (32, 7, 4), 0.05)),
     ("c64-small", custom((12, 10, 9), "c64", (5, 4, 3), 0.05)),
     ("c64-64", custom((64, 6, 33), "c64", (32, 6, 16), 0.05)),
@@ -185,14 +192,15 @@ STEP_CASES = FACTOR_CASES + [
 ]
 
 
-@pytest.mark.parametrize("fused", [1, 3, 2, 0], ids=["fused", "fused-two-mode-slabs", "fused-tiles",
-                                                 "one-mode"])
+@pytest.mark.parametrize("fused", [1, 4, 3, 2, 0], ids=["fused", "fused-rec3", "fused-two-mode-slabs",
+                                                    "fused-tiles", "one-mode"])
 @pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: c[0])
 def test_steps_with_pinned_omega_and_factors(case, fused):
     """Omega and U(n) injected from the oracle, so only the step kernels are compared;
     every launch plan (trailing modes per launch with the default kernel choice, which is
     one wave per slab for small 16-bit slabs and a three-mode first projection where it
-    applies; the two-mode slab kernels only; workgroup tiles only; one mode per launch)."""
+    applies; the same with the three-mode reconstruction where it applies; the two-mode
+    slab kernels only; workgroup tiles only; one mode per launch)."""
     name, wl = case
     gs = GradStream(wl, seed=8)
     W0 = init_weights(wl, seed=8)
@@ -519,7 +527,8 @@ def test_timing_only_one_kernel():
 
 @pytest.mark.timeout(900)
 def test_bf16_64x64x48x48x25_full_size_two_steps():
-    """bf16 (64,64,48,48,25), the full tensor, two steps in the bench's launch plan.
+    """bf16 (64,64,48,48,25), the full tensor, two steps: the first in the bench's launch
+    plan, the second with the three-mode reconstruction.
 
     Step 1 refreshes: Omega is checked by its complete characterisation (no sort of 236M
     keys), each factor's projector against the fp64 Gram eigenvectors of the residual.
@@ -567,8 +576,10 @@ def test_bf16_64x64x48x48x25_full_size_two_steps():
     Wprev, Wo = W0, W0
     for t in (1, 2):
         if t == 2:
+            # the second step in the plan with the three-mode reconstruction
+            assert lib.set_fusion(4)
             g = gs.next()
-            print("CASE bf16-(64,64,48,48,25) step 2", flush=True)
+            print("CASE bf16-(64,64,48,48,25) step 2 (three-mode reconstruction)", flush=True)
             Wprev = host(W, wl.dtype)
             lib.step(W, dev(g, wl.dtype))
             torch.cuda.synchronize()
