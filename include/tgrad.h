@@ -228,6 +228,19 @@ int tgrad_set_gram_fusion(tgrad_t *h, int enable);
  * launch per mode. Results agree to fp32 rounding; takes effect at the next step. */
 int tgrad_set_pair_fusion(tgrad_t *h, int enable);
 
+/* Test / benchmark hook: a single mode product on fp32 data (the projection's later
+ * modes, the reconstruction's leading ones) runs on a streaming kernel where it applies:
+ * every wave owns all output rows of 64 consecutive trailing columns and loads the next
+ * such tile while it multiplies the current one, without LDS staging or workgroup
+ * barriers (pith.science "What carries the argument": projection and reconstruction are
+ * chains of mode-wise products). It applies when the mode has at most 32 values on the
+ * input side and 64 on the output side and the trailing part is at least 64 values and a
+ * multiple of 4. enable = 1 selects it (the default), 0 the tiled kernel for every
+ * single mode product; enable = n >= 2 selects it with at most n - 1 workgroups of 4
+ * waves (so that small tensors exercise a wave's walk over several tiles). Negative enable:
+ * TGRAD_EINVAL. Results agree to fp32 rounding; takes effect at the next step. */
+int tgrad_set_stream_products(tgrad_t *h, int enable);
+
 /* ---------------------------------------------------------------- variants.
  * Choices the method leaves open, as options of a handle (defaults: the plain method,
  * bit for bit):

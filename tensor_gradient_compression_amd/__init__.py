@@ -85,6 +85,7 @@ SIGNATURES = [
     ("tgrad_set_fusion", ctypes.c_int, [_P, ctypes.c_int]),
     ("tgrad_set_gram_fusion", ctypes.c_int, [_P, ctypes.c_int]),
     ("tgrad_set_pair_fusion", ctypes.c_int, [_P, ctypes.c_int]),
+    ("tgrad_set_stream_products", ctypes.c_int, [_P, ctypes.c_int]),
     ("tgrad_default_options", None, [ctypes.POINTER(Options)]),
     ("tgrad_set_options", ctypes.c_int, [_P, ctypes.POINTER(Options)]),
     ("tgrad_get_options", ctypes.c_int, [_P, ctypes.POINTER(Options)]),
@@ -361,6 +362,17 @@ class TGrad:
             return False
         self._check(rc, "tgrad_set_pair_fusion")
         return True
+
+    def set_stream_products(self, enable, max_workgroups: int = 0) -> None:
+        """Single fp32 mode products on the streaming kernel where it applies (True, the
+        default) or on the tiled kernel always (False); max_workgroups > 0 caps the
+        streaming kernel's grid (a test hook)."""
+        v = int(bool(enable))
+        if v and max_workgroups:
+            if max_workgroups < 0:
+                raise ValueError("max_workgroups must be >= 0")
+            v = int(max_workgroups) + 1
+        self._check(self._lib.tgrad_set_stream_products(self._h, v), "tgrad_set_stream_products")
 
     def save_state(self) -> bytes:
         """The optimizer state as bytes (see tgrad_save_state)."""

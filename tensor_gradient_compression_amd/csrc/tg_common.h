@@ -61,7 +61,7 @@ enum KernelId {
   KID_RECONSTRUCT, KID_RECON_APPLY, KID_APPLY_DENSE, KID_GRAM, KID_GRAM_REDUCE,
   KID_EIG, KID_FILL, KID_PROJECT_FIRST, KID_PROJECT_FUSED2, KID_RECON_FUSED2_APPLY,
   KID_RECON_FUSED2, KID_REMAP, KID_PROJECT_FUSED3, KID_GRAM3, KID_PROJECT_PAIR, KID_RECON_PAIR,
-  KID_RECON_FUSED3_APPLY, KID_COUNT_
+  KID_RECON_FUSED3_APPLY, KID_STREAM_PROJECT, KID_STREAM_RECONSTRUCT, KID_COUNT_
 };
 
 // ---------------------------------------------------------------- launchers
@@ -136,12 +136,18 @@ struct ModeProd {
   float decay;
   int has_sparse;
   int force_ncb;           // 0: choose the tile width automatically
+  int max_wg;              // streaming kernel: at most this many workgroups (0: no cap)
   // apply only, a test capture: when not NULL the fp32 update (acc + uS@Omega) is also
   // stored here, one float per output value (a separate kernel instantiation)
   float* delta;
 };
 size_t modeprod_lds_bytes(const ModeProd& mp);
 hipError_t launch_modeprod(const ModeProd& mp, int num_cu, hipStream_t s);
+// The same product streamed by independent waves (k_streamprod.hip): real fp32 input and
+// output (store epilogue), I <= 32, R <= 64, B >= 64 and a multiple of 4, X and Y
+// 16-byte aligned.
+bool streamprod_supported(const ModeProd& mp);
+hipError_t launch_streamprod(const ModeProd& mp, int num_cu, hipStream_t s);
 
 // Two trailing mode products in one launch over slabs (A, I1, I2, P) -> (A, R1, R2, P).
 // M1 is (R1*P) x (I1*P) (mode d-1), M2 is (R2*P) x (I2*P) (mode d). recon = 0: mode d

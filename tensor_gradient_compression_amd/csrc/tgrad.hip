@@ -77,6 +77,8 @@ struct tgrad_handle {
   void* resid = nullptr;     // refresh: G with Omega zeroed (shares buf's memory)
   bool can_pair = false;     // the fused chains hold two neighbouring leading modes
   bool pairs = true;         // launch those as one (k_pair)
+  bool stream = true;        // single fp32 mode products on k_streamprod where it applies
+  int stream_wg = 0;         // test hook: cap on its workgroups (0: none)
 
   uint32_t* omega = nullptr;
   uint64_t* mask = nullptr;
@@ -349,6 +351,20 @@ void pair_view(const int64_t* cur, int d, int n, ModePair* mp) {
   mp->C = C;
 }
 
+// One mode product runs on the streaming kernel where it applies (and is enabled), else
+// on the tiled one; the launch is recorded under the kernel id of the kernel that ran.
+bool use_stream(const tgrad_t* h, const ModeProd& mp) {
+  return h->stream && streamprod_supported(mp);
+}
+hipError_t mode_product(const tgrad_t* h, const ModeProd& mp, hipStream_t s) {
+  if (use_stream(h, mp)) {
+    ModeProd m = mp;
+    m.max_wg = h->stream_wg;
+    return launch_streamprod(m, h->num_cu, s);
+  }
+  return launch_modeprod(mp, h->num_cu, s);
+}
+
 // A group of two modes that is not the trailing pair: a k_pair launch.
 bool is_lead_pair(const tgrad_t* h, const std::vector<int>& g) {
   return g.size() == 2 && std::min(g[0], g[1]) < h->d - 2;
@@ -612,7 +628,8 @@ const char* tgrad_kernel_name(int id) {
       "gram_reduce", "eig_jacobi", "fill", "modeprod_project_first",
       "modeprod2_project_first", "modeprod2_reconstruct_apply", "modeprod2_reconstruct",
       "remap_moments", "modeprod3_project_first", "gram3_tail", "modeprod_pair_project",
-      "modeprod_pair_reconstruct", "modeprod3_reconstruct_apply"};
+      "modeprod_pair_reconstruct", "modeprod3_reconstruct_apply", "streamprod_project",
+      "streamprod_reconstruct"};
   if (id < 0 || id >= KID_COUNT_) return "";
   return names[id];
 }
@@ -1024,10 +1041,11 @@ int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s) {
       mp.P = P;
       mp.apply = 0;
       mp.Y = Y;
-      Mark m(h, j == 0 ? KID_PROJECT_FIRST : KID_PROJECT);
-      HIPCHK(h, launch_modeprod(mp, h->num_cu, s));
-      account_chain(h, j == 0 ? KID_PROJECT_FIRST : KID_PROJECT, cur, proj[j], true,
-                    xdt == DT_F32 ? 4 : 2, false, false);
+      const int kid =
+          use_stream(h, mp) ? KID_STREAM_PROJECT : j == 0 ? KID_PROJECT_FIRST : KID_PROJECT;
+      Mark m(h, kid);
+      HIPCHK(h, mode_product(h, mp, s));
+      account_chain(h, kid, cur, proj[j], true, xdt == DT_F32 ? 4 : 2, false, false);
       cur[n] = h->ranks[n];
     }
     X = Y;
@@ -1169,10 +1187,11 @@ int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, fl
       mp.decay = decay;
       mp.has_sparse = app && h->k > 0;
       mp.delta = app ? h->delta_cap : nullptr;
-      Mark m(h, app ? KID_RECON_APPLY : KID_RECONSTRUCT);
-      HIPCHK(h, launch_modeprod(mp, h->num_cu, s));
-      account_chain(h, app ? KID_RECON_APPLY : KID_RECONSTRUCT, cur, rec[j], false, 4, false,
-                    app);
+      const int kid =
+          use_stream(h, mp) ? KID_STREAM_RECONSTRUCT : app ? KID_RECON_APPLY : KID_RECONSTRUCT;
+      Mark m(h, kid);
+      HIPCHK(h, mode_product(h, mp, s));
+      account_chain(h, kid, cur, rec[j], false, 4, false, app);
       cur[n] = h->shape[n];
     }
     X = Y;
@@ -1627,6 +1646,13 @@ int tgrad_set_fusion(tgrad_t* h, int enable) {
   h->slab2 = enable != 2;
   h->slab3 = enable == 1 || enable == 4;
   h->rec3 = enable == 4;
+  return TGRAD_OK;
+}
+
+int tgrad_set_stream_products(tgrad_t* h, int enable) {
+  if (!h || enable < 0) return TGRAD_EINVAL;
+  h->stream = enable != 0;
+  h->stream_wg = enable > 1 ? enable - 1 : 0;
   return TGRAD_OK;
 }
 

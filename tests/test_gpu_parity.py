@@ -238,6 +238,66 @@ def test_steps_with_pinned_omega_and_factors(case, fused):
     assert np.abs(mc - orc.mC).max() <= 1e-4 * scale
 
 
+# Single fp32 mode products on the streaming kernel: every tile of 64 trailing columns
+# owned by one wave, loads a tile ahead. Cases: ragged last tiles (B not a multiple of
+# 64), R not a multiple of 16, I not a multiple of 4, several leading indices, and more
+# tiles than waves in the grid.
+STREAM_CASES = [
+    ("f32-40x60", custom((4, 40, 60, 12), "f32", (3, 20, 30, 6), 0.05), 0),
+    ("bf16-64x30", custom((2, 64, 24, 16), "bf16", (2, 30, 12, 8), 0.05), 0),
+    ("f16-tall-ragged", custom((3, 50, 7, 20), "f16", (2, 13, 5, 12), 0.05), 0),
+    # 65 and 96 tiles for 8 and for 4 waves: each wave walks 8 to 24 tiles, ending after
+    # either of its two register sets
+    ("f32-many-tiles-2-wg", custom((24, 40, 52, 16), "f32", (12, 20, 26, 8), 0.02), 2),
+    ("f32-many-tiles-1-wg", custom((24, 40, 52, 16), "f32", (12, 20, 26, 8), 0.02), 1),
+]
+
+
+@pytest.mark.parametrize("fused", [1, 0], ids=["fused", "one-mode"])
+@pytest.mark.parametrize("case", STREAM_CASES, ids=lambda c: c[0])
+def test_stream_products_match_tiled_and_oracle(case, fused):
+    """Two libraries with the oracle's Omega and factors, one with the streaming kernel
+    for its single fp32 mode products and one with the tiled kernel only: the same fp32
+    update Delta bit for bit (both accumulate the same fp32 MFMA steps in the same k
+    order), and Delta against the oracle's at the parity bar, over two steps."""
+    name, wl, wg = case
+    gs = GradStream(wl, seed=5)
+    W0 = init_weights(wl, seed=5)
+    libs = [make_lib(wl, T=10 ** 6), make_lib(wl, T=10 ** 6)]
+    if wg:
+        libs[0].set_stream_products(True, max_workgroups=wg)
+    orc = make_oracle(wl, T=10 ** 6)
+    for lib in libs:
+        if not lib.set_fusion(fused):
+            pytest.skip("the two trailing modes are not both compressed")
+        lib.set_pair_fusion(False)
+    libs[1].set_stream_products(False)
+    g = gs.next()
+    orc.refresh(g)
+    caps = []
+    for lib in libs:
+        lib.set_omega(orc.omega)
+        for n, U in enumerate(orc.factors):
+            if U is not None:
+                lib.set_factor(n, U)
+        lib.mark_refreshed()
+        caps.append(DeltaCapture(lib, wl))
+    align = CoreSplit(orc)
+    Ws = [dev(W0, wl.dtype), dev(W0, wl.dtype)]
+    Wo = W0
+    for step in range(2):
+        what = f"{name}/plan{fused} step {step + 1}"
+        libs[0].timing_enable(True)
+        libs[1].step(Ws[1], dev(g, wl.dtype))
+        Wo, _ = checked_step(libs[0], orc, caps[0], Ws[0], Wo, g, wl, what, align=align)
+        rec = libs[0].timing_read()
+        assert "streamprod_reconstruct" in rec, (what, sorted(rec))
+        assert np.array_equal(caps[0].host(), caps[1].host()), f"{what}: streamed Delta differs"
+        assert np.array_equal(host(Ws[0], wl.dtype).view(np.uint8),
+                              host(Ws[1], wl.dtype).view(np.uint8))
+        g = gs.next()
+
+
 # --------------------------------------------------------------------------- independent runs
 
 RUN_CASES = [
@@ -447,8 +507,14 @@ def test_timing_records_every_kernel():
     assert lib.set_pair_fusion(False)
     lib.step(W, dev(gs.next(), wl.dtype))
     rec = lib.timing_read()
-    assert rec["modeprod_project"][0] == 2 and rec["modeprod_reconstruct"][0] == 2
+    # modes 1 and 0 one by one, on the streaming kernel (trailing parts of 64 and 1024)
+    assert rec["streamprod_project"][0] == 2 and rec["streamprod_reconstruct"][0] == 2
     assert "modeprod_pair_project" not in rec
+    lib.set_stream_products(False)
+    lib.step(W, dev(gs.next(), wl.dtype))
+    rec = lib.timing_read()
+    assert rec["modeprod_project"][0] == 2 and rec["modeprod_reconstruct"][0] == 2
+    assert "streamprod_project" not in rec and "streamprod_reconstruct" not in rec
     assert lib.set_fusion(False)
     lib.step(W, dev(gs.next(), wl.dtype))
     rec = lib.timing_read()
@@ -481,12 +547,20 @@ def test_launch_record_matches_the_launches():
     assert counts == {n: c for n, (c, _) in rec.items()}
     N, k, es = wl.numel, wl.k, 4
     shape, ranks = list(wl.shape), list(wl.ranks)
+
+    def streams(cur, n, I, R):
+        # the streaming kernel's documented conditions (fp32 in and out, no apply)
+        B = int(np.prod(cur[n + 1:], dtype=np.int64))
+        return I <= 32 and R <= 64 and B >= 64 and B % 4 == 0
+
     exp = [("gather_residual", k * (4 + es) + k * (4 + es), 0)]
     cur, size = list(shape), N
     for j, n in enumerate([3, 2, 1, 0]):
         out = size // cur[n] * ranks[n]
-        exp.append(("modeprod_project_first" if j == 0 else "modeprod_project",
-                    size * 4 + out * 4, 2 * (size // cur[n]) * cur[n] * ranks[n]))
+        name = "modeprod_project_first" if j == 0 else "modeprod_project"
+        if streams(cur, n, cur[n], ranks[n]):
+            name = "streamprod_project"
+        exp.append((name, size * 4 + out * 4, 2 * (size // cur[n]) * cur[n] * ranks[n]))
         cur[n] = ranks[n]
         size = out
     ncore = size
@@ -495,10 +569,13 @@ def test_launch_record_matches_the_launches():
         out = size // cur[n] * shape[n]
         last = j == 3
         b = size * 4 + ((2 * N * es + 8 * k) if last else out * 4)
-        exp.append(("modeprod_reconstruct_apply" if last else "modeprod_reconstruct", b,
-                    2 * (size // cur[n]) * cur[n] * shape[n]))
+        name = "modeprod_reconstruct_apply" if last else "modeprod_reconstruct"
+        if not last and streams(cur, n, cur[n], shape[n]):
+            name = "streamprod_reconstruct"
+        exp.append((name, b, 2 * (size // cur[n]) * cur[n] * shape[n]))
         cur[n] = shape[n]
         size = out
+    assert sum(n.startswith("streamprod") for n, *_ in exp) == 4   # modes 1 and 0 both ways
     assert [(n, br + bw, fl) for n, _m, br, bw, fl in got] == exp
 
 
