@@ -190,13 +190,13 @@ int tgrad_debug_capture_delta(tgrad_t *h, float *delta);
  * enough slabs those launches use one wave per slab on bf16 MFMAs (exact bf16 splits of
  * the fp32 operands), otherwise workgroup-wide fp32 MFMA tiles; where mode d-3 is also
  * compressed (I(d-3) a multiple of 16 up to 64, rank <= 32), the projection's first
- * launch takes mode d-3 as well (one workgroup per index of the leading modes). enable
- * = 0 selects one launch per mode; 1 the fused form (default choice of kernels); 2 the
- * fused two-mode form with the workgroup-tile kernel only; 3 the fused two-mode form with
- * the slab kernels, without the three-mode projection; 4 as 1, and where I(d-3) is a
- * multiple of 12 up to 64 (16-bit weights, 16-byte aligned) the reconstruction's last
- * launch takes mode d-3 as well, with the merge and the weight update (one workgroup per
- * index of the leading modes; the mode d-2 tensor stays on chip). enable = 1 to 4 returns
+ * launch takes mode d-3 as well (one workgroup per index of the leading modes), and,
+ * where I(d-3) is a multiple of 12 up to 64 (16-bit weights, 16-byte aligned), so does
+ * the reconstruction's last launch, with the merge and the weight update (the mode d-2
+ * tensor stays on chip). enable = 0 selects one launch per mode; 1 the fused form
+ * (default choice of kernels); 2 the fused two-mode form with the workgroup-tile kernel
+ * only; 3 the fused two-mode form with the slab kernels, without the three-mode
+ * launches; 4 as 1 but with the two-mode reconstruction. enable = 1 to 4 returns
  * TGRAD_EINVAL where the fused form does not apply. The unfused plan projects a residual copy of grad, so enable = 0 allocates an
  * N-element workspace the first time (TGRAD_ENOMEM if that fails). Results agree to
  * fp32 rounding; takes effect at the next step. */

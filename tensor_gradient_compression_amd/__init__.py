@@ -332,8 +332,8 @@ class TGrad:
 
     def set_fusion(self, enable) -> bool:
         """Select fused multi-mode launches (True or 1: default kernel choice; 2: two-mode
-        workgroup tiles only; 3: two-mode slab kernels without the three-mode projection;
-        4: as 1 with the three-mode reconstruction where it applies) or one launch per mode (False or 0);
+        workgroup tiles only; 3: two-mode slab kernels without the three-mode launches;
+        4: as 1 with the two-mode reconstruction) or one launch per mode (False or 0);
         returns False when the fused form does not apply to this shape."""
         rc = self._lib.tgrad_set_fusion(self._h, int(enable))
         if rc == EINVAL and enable:

@@ -60,8 +60,11 @@ struct R3K {
 };
 
 // NRB1: 16-row blocks of I1 (<= 64); NCB2: 16-column blocks of I2 (<= 32); KS1: fp32
-// MFMA k-steps of the mode d-1 product (R1 <= 4 KS1 <= 32); R2 <= 16.
-template <typename WT, int NRB1, int NCB2, int KS1>
+// MFMA k-steps of the mode d-1 product (R1 <= 4 KS1 <= 32); R2 <= 16. FULL: I1 = 16 NRB1
+// and R1 = 4 KS1, so that only the last column block of a slab and the columns past R2
+// of the stack rows need lane tests (every lane test is a mask the compiler keeps in
+// scalar registers across the slab loop).
+template <typename WT, int NRB1, int NCB2, int KS1, bool FULL>
 __global__ void __launch_bounds__(NTR) __attribute__((amdgpu_waves_per_eu(3, 8))) k_rec3s(R3K k) {
   // 16-byte weight pieces a lane holds: a slab has at most 16 NRB1 x 16 NCB2 values
   constexpr int WQ = (NRB1 * NCB2 + 1) / 2;
@@ -87,7 +90,6 @@ __global__ void __launch_bounds__(NTR) __attribute__((amdgpu_waves_per_eu(3, 8))
   const uint64_t kS = k.kS;
   const bool sparse = kS > 0;
   const float lr = k.lr, decay = k.decay;
-  const bool decayed = decay != 1.0f;
   const uint32_t np = slab_e / 8;              // 16-byte weight pieces of a slab
 
   // M0 into LDS (4-byte transfers, I0 R0 <= 2048 values), and the operand tables: every
@@ -157,44 +159,54 @@ __global__ void __launch_bounds__(NTR) __attribute__((amdgpu_waves_per_eu(3, 8))
     hi = rank_at(lane_u64(b.m, 1), (uint32_t)__builtin_amdgcn_readlane((int)b.r, 1),
                  (uint64_t)(s + 1) * slab_e, N, kS);
   };
+  // A slab's weights (and the test capture of its update) are reached through buffer
+  // resources over the slab alone: piece q >= np lies past the extent, so its load
+  // reads zero and its store is dropped, without a per-lane branch (each per-lane branch
+  // is a mask the compiler keeps in scalar registers across the loop).
+  auto wres = [&](uint32_t s) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(Wg + (uint64_t)s * slab_e), 0,
+                                             (int)(slab_e * 2), 0x00020000);
+  };
   // the weights of slab s into registers (pieces lane + 64 j), kept as loaded: unpacking
   // them here would make the wave wait for the loads at once; they are used a slab later
+  const uint32_t vq = lane * 16;   // byte offset of piece lane; piece lane + 64 j adds 1024 j
   u32x4 wr[WQ];
   auto wload = [&](uint32_t s) {
+    const __amdgpu_buffer_rsrc_t rw = wres(s);
 #pragma unroll
-    for (int j = 0; j < WQ; ++j) {
-      const uint32_t q = lane + 64 * j;
-      if (q < np) wr[j] = *(const u32x4*)(Wg + (uint64_t)s * slab_e + 8 * q);
-    }
+    for (int j = 0; j < WQ; ++j)
+      wr[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(vq + 1024 * j), 0, 0);
   };
   // W <- round(W * decay - lr * O) for slab s from the staged O and the loaded weights,
   // one piece at a time (a scheduling barrier keeps the pieces' LDS reads from being
-  // hoisted together, which would hold all of them in registers at once)
+  // hoisted together, which would hold all of them in registers at once). decay is 1
+  // exactly without weight decay, and W * 1 is W: one expression serves both. A piece
+  // past the slab reads O slots past this wave's region (the allocation extends far
+  // enough for the last wave) and its store is dropped. The test capture of the fp32
+  // update goes through a resource of extent zero when it is off.
   auto epilogue = [&](uint32_t s) {
+    const __amdgpu_buffer_rsrc_t rw = wres(s);
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(k.delta ? k.delta + (uint64_t)s * slab_e : (float*)k.W), 0,
+        k.delta ? (int)(slab_e * 4) : 0, 0x00020000);
 #pragma unroll
     for (int j = 0; j < WQ; ++j) {
-      const uint32_t q = lane + 64 * j;
-      if (q < np) {
-        const f4 o0 = *(const LDS f4*)(Ob + 8 * q);
-        const f4 o1 = *(const LDS f4*)(Ob + 8 * q + 4);
-        const float ov[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
-        u32x4 out;
+      const LDS float* const ob = Ob + 8 * (lane + 64 * j);
+      const f4 o0 = *(const LDS f4*)ob;
+      const f4 o1 = *(const LDS f4*)(ob + 4);
+      const float ov[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
+      u32x4 out;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t w = wr[j][e];
-          float lo = wlo<WT>(w), hi = whi<WT>(w);
-          if (decayed) {
-            lo = lo * decay;
-            hi = hi * decay;
-          }
-          out[e] = wpack<WT>(lo - lr * ov[2 * e], hi - lr * ov[2 * e + 1]);
-        }
-        *(u32x4*)((WT*)k.W + (uint64_t)s * slab_e + 8 * q) = out;
-        if (k.delta) {
-          *(f4*)(k.delta + (uint64_t)s * slab_e + 8 * q) = o0;
-          *(f4*)(k.delta + (uint64_t)s * slab_e + 8 * q + 4) = o1;
-        }
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = wr[j][e];
+        const float lo = wlo<WT>(w) * decay, hi = whi<WT>(w) * decay;
+        out[e] = wpack<WT>(lo - lr * ov[2 * e], hi - lr * ov[2 * e + 1]);
       }
+      __builtin_amdgcn_raw_buffer_store_b128(out, rw, (int)(vq + 1024 * j), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o0), rd,
+                                             (int)(2 * vq + 2048 * j), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o1), rd,
+                                             (int)(2 * vq + 2048 * j + 16), 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -299,10 +311,19 @@ __global__ void __launch_bounds__(NTR) __attribute__((amdgpu_waves_per_eu(3, 8))
     // 3. modes d-1 and d of row i0 of the stack, then the Omega merge
     const LDS float* const zr = st + (spw * wv + c) * RC;
     float zv[KS1];
+    if constexpr (FULL) {
+      const bool okc = li < R2;
 #pragma unroll
-    for (int t = 0; t < KS1; ++t) {
-      const uint32_t j1 = KS1 * lg + t;
-      zv[t] = (j1 < R1 && li < R2) ? zr[j1 * R2 + li] : 0.0f;
+      for (int t = 0; t < KS1; ++t) {
+        const float z = zr[okc ? (KS1 * lg + t) * R2 + li : 0];
+        zv[t] = okc ? z : 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < KS1; ++t) {
+        const uint32_t j1 = KS1 * lg + t;
+        zv[t] = (j1 < R1 && li < R2) ? zr[j1 * R2 + li] : 0.0f;
+      }
     }
     f4 acc1[NRB1];
 #pragma unroll
@@ -342,7 +363,14 @@ __global__ void __launch_bounds__(NTR) __attribute__((amdgpu_waves_per_eu(3, 8))
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const uint32_t i1 = 16 * rb + 4 * lg + v, i2 = 16 * cb + li;
-          Ob[(i1 < I1 && i2 < I2) ? i1 * I2 + i2 : k.trash + lane] = acc[cb][v];
+          if constexpr (FULL) {
+            if (cb + 1 < NCB2)
+              Ob[i1 * I2 + i2] = acc[cb][v];
+            else
+              Ob[i2 < I2 ? i1 * I2 + i2 : k.trash + lane] = acc[cb][v];
+          } else {
+            Ob[(i1 < I1 && i2 < I2) ? i1 * I2 + i2 : k.trash + lane] = acc[cb][v];
+          }
         }
     }
     wave_fence();
@@ -441,13 +469,18 @@ Plan3r plan3r(const ModeProd2& mp) {
   k.off_fac = k.off_m0 + al16(I0 * R0 * 4);
   k.off_o = k.off_fac + (uint32_t)(p.nrb1 * p.ks1 + p.ncb2 * 4) * 64 * 4;
   p.lds = (size_t)k.off_o + (size_t)WPR * k.o_wave;
+  // the epilogue of the last wave reads up to 8 * 64 WQ floats from its region's start
+  const uint32_t wq = (uint32_t)(p.nrb1 * p.ncb2 + 1) / 2;
+  const size_t rd_end = (size_t)k.off_o + (size_t)(WPR - 1) * k.o_wave + (size_t)512 * wq * 4;
+  if (rd_end > p.lds) p.lds = rd_end;
   p.ok = p.lds <= 160 * 1024;
   return p;
 }
 
 template <typename WT, int NRB1, int NCB2, int KS1>
 hipError_t rec3_launch(const Plan3r& p, int num_cu, hipStream_t s) {
-  auto fn = k_rec3s<WT, NRB1, NCB2, KS1>;
+  const bool full = p.k.I1 == 16u * NRB1 && p.k.R1 == 4u * KS1;
+  auto fn = full ? k_rec3s<WT, NRB1, NCB2, KS1, true> : k_rec3s<WT, NRB1, NCB2, KS1, false>;
   if (p.lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)fn,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);

@@ -42,12 +42,15 @@ template <> __device__ __forceinline__ float wlo<_Float16>(uint32_t w) {
 template <> __device__ __forceinline__ float whi<_Float16>(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
 }
+// (round to nearest even, as from_f32; one v_cvt_pk_bf16_f32 for bf16)
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
 template <> __device__ __forceinline__ uint32_t wpack<bf16_t>(float lo, float hi) {
-  return (uint32_t)from_f32<bf16_t>(lo).b | ((uint32_t)from_f32<bf16_t>(hi).b << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){lo, hi}, bf16x2v));
 }
 template <> __device__ __forceinline__ uint32_t wpack<_Float16>(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(unsigned short, from_f32<_Float16>(lo)) |
-         ((uint32_t)__builtin_bit_cast(unsigned short, from_f32<_Float16>(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){lo, hi}, f16x2v));
 }
 
 // nchunks 16-byte pieces from src to dst (wave-uniform), one per lane per instruction

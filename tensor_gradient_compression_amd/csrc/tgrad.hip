@@ -66,7 +66,7 @@ struct tgrad_handle {
   bool can_slab3 = false;    // the projection's first launch can also take mode d-3
   bool slab3 = true;         // use it
   bool can_rec3 = false;     // the reconstruction's last launch can also take mode d-3
-  bool rec3 = false;         // use it (set_fusion 4)
+  bool rec3 = true;          // use it (not under set_fusion 4)
   bool can_gram3 = false;    // refresh: the last three modes' Grams from one read
   bool gram3 = true;         // use it
   // refresh: the Gram kernels read the gradient and clear Omega's entries in their staged
@@ -1645,7 +1645,7 @@ int tgrad_set_fusion(tgrad_t* h, int enable) {
   h->fuse = enable != 0;
   h->slab2 = enable != 2;
   h->slab3 = enable == 1 || enable == 4;
-  h->rec3 = enable == 4;
+  h->rec3 = enable == 1;
   return TGRAD_OK;
 }
 

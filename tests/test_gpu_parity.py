@@ -192,15 +192,15 @@ STEP_CASES = FACTOR_CASES + [
 ]
 
 
-@pytest.mark.parametrize("fused", [1, 4, 3, 2, 0], ids=["fused", "fused-rec3", "fused-two-mode-slabs",
+@pytest.mark.parametrize("fused", [1, 4, 3, 2, 0], ids=["fused", "fused-rec2", "fused-two-mode-slabs",
                                                     "fused-tiles", "one-mode"])
 @pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: c[0])
 def test_steps_with_pinned_omega_and_factors(case, fused):
     """Omega and U(n) injected from the oracle, so only the step kernels are compared;
     every launch plan (trailing modes per launch with the default kernel choice, which is
-    one wave per slab for small 16-bit slabs and a three-mode first projection where it
-    applies; the same with the three-mode reconstruction where it applies; the two-mode
-    slab kernels only; workgroup tiles only; one mode per launch)."""
+    one wave per slab for small 16-bit slabs and three-mode first projection and last
+    reconstruction launches where they apply; the same with the two-mode reconstruction;
+    the two-mode slab kernels only; workgroup tiles only; one mode per launch)."""
     name, wl = case
     gs = GradStream(wl, seed=8)
     W0 = init_weights(wl, seed=8)
@@ -605,7 +605,7 @@ def test_timing_only_one_kernel():
 @pytest.mark.timeout(900)
 def test_bf16_64x64x48x48x25_full_size_two_steps():
     """bf16 (64,64,48,48,25), the full tensor, two steps: the first in the bench's launch
-    plan, the second with the three-mode reconstruction.
+    plan (three-mode reconstruction), the second with the two-mode reconstruction.
 
     Step 1 refreshes: Omega is checked by its complete characterisation (no sort of 236M
     keys), each factor's projector against the fp64 Gram eigenvectors of the residual.
@@ -653,10 +653,10 @@ def test_bf16_64x64x48x48x25_full_size_two_steps():
     Wprev, Wo = W0, W0
     for t in (1, 2):
         if t == 2:
-            # the second step in the plan with the three-mode reconstruction
+            # the second step in the plan with the two-mode reconstruction
             assert lib.set_fusion(4)
             g = gs.next()
-            print("CASE bf16-(64,64,48,48,25) step 2 (three-mode reconstruction)", flush=True)
+            print("CASE bf16-(64,64,48,48,25) step 2 (two-mode reconstruction)", flush=True)
             Wprev = host(W, wl.dtype)
             lib.step(W, dev(g, wl.dtype))
             torch.cuda.synchronize()

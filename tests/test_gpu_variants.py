@@ -118,7 +118,7 @@ RUNS = [
 ]
 
 
-@pytest.mark.parametrize("fused", [1, 4, 0], ids=["fused", "fused-rec3", "one-mode"])
+@pytest.mark.parametrize("fused", [1, 4, 0], ids=["fused", "fused-rec2", "one-mode"])
 @pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: v[0])
 @pytest.mark.parametrize("run", RUNS, ids=lambda r: r[0])
 def test_variant_runs_match_oracle(run, variant, fused):
@@ -402,7 +402,7 @@ def test_lowrank_first_refresh(case):
     assert same >= 0.999 * orc.k, (name, same, orc.k)
 
 
-@pytest.mark.parametrize("fused", [1, 4, 2, 0], ids=["fused", "fused-rec3", "fused-tiles", "one-mode"])
+@pytest.mark.parametrize("fused", [1, 4, 2, 0], ids=["fused", "fused-rec2", "fused-tiles", "one-mode"])
 @pytest.mark.parametrize("case", LRF_CASES, ids=lambda c: c[0])
 def test_lowrank_first_steps_with_pinned_omega_and_factors(case, fused):
     """Low-rank-first steps with the oracle's Omega and factors injected: S = (G - L)[Omega]
