@@ -137,25 +137,60 @@ def multi_tensor(dev, stream, steps=10, warmup=3):
 
 
 def cpu_baseline(wl, seed=0):
-    """The oracle (numpy, fp64 contractions) timed on this host on a bounded sample: one
-    non-refresh step of the full workload, with Omega a seeded random index set of size
-    k and seeded random orthonormal factors (the step's cost does not depend on which
-    indices or which subspace it uses). The refresh (a 236M-key sort and fp64 Grams)
-    is left out of the sample."""
+    """The oracle (numpy, fp64 contractions) timed on this host on bounded samples:
+    * one non-refresh step of the full workload on all available cores, with Omega a
+      seeded random index set of size k and seeded random orthonormal factors (the
+      step's cost does not depend on which indices or which subspace it uses) -- the
+      reported value;
+    * the same step with numpy's BLAS held to one thread, on the first 8 of the 64
+      leading indices (1/8 of the elements, ranks capped at the slice's sizes);
+    * one refresh (top-k by a full sort of the keys, five fp64 Grams, eigh) on the first
+      4 leading indices (1/16 of the elements), all cores.
+    Each figure is scaled to gradient elements per second of its own sample."""
     import oracle as O
     from synth import GradStream, init_weights
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
     g = GradStream(wl, seed=seed).next()
     W = init_weights(wl, seed=seed)
-    orc = O.TGradOracle(wl.shape, wl.ranks, wl.dtype, wl.sparse_ratio, wl.T, wl.lr, *wl.betas, wl.eps)
-    rng = np.random.default_rng(seed + 99)
-    orc.omega = np.sort(rng.choice(wl.numel, wl.k, replace=False)).astype(np.uint32)
-    orc.factors = [np.linalg.qr(rng.standard_normal((I, r)))[0].astype(np.float32) if r < I else None
-                   for I, r in zip(wl.shape, wl.ranks)]
-    orc.t = 1
-    orc.refreshed_for = 2
+
+    def timed_step(shape, gs, Ws):
+        ranks = tuple(min(r, I) for I, r in zip(shape, wl.ranks))
+        n = int(np.prod(shape, dtype=np.int64))
+        k = int(np.floor(wl.sparse_ratio * n))
+        orc = O.TGradOracle(shape, ranks, wl.dtype, wl.sparse_ratio, wl.T, wl.lr, *wl.betas, wl.eps)
+        rng = np.random.default_rng(seed + 99)
+        orc.omega = np.sort(rng.choice(n, k, replace=False)).astype(np.uint32)
+        orc.factors = [np.linalg.qr(rng.standard_normal((I, r)))[0].astype(np.float32) if r < I else None
+                       for I, r in zip(shape, ranks)]
+        orc.t = 1
+        orc.refreshed_for = 2
+        t0 = time.perf_counter()
+        orc.step(np.ascontiguousarray(Ws), np.ascontiguousarray(gs))
+        return n, time.perf_counter() - t0
+
+    n_all, dt = timed_step(wl.shape, g, W)
+    one = None
+    if threadpool_limits is not None:
+        sl = (8,) + tuple(wl.shape[1:])
+        with threadpool_limits(limits=1):
+            n1, dt1 = timed_step(sl, g[:8], W[:8])
+        one = {"value": n1 / dt1, "unit": "grad elems/s", "cores": 1, "seconds": dt1,
+               "sample": f"1 non-refresh step on the first 8 leading indices {sl} ({n1} elements), "
+                         f"numpy BLAS held to one thread"}
+    sr = (4,) + tuple(wl.shape[1:])
+    ranks_r = tuple(min(r, I) for I, r in zip(sr, wl.ranks))
+    orc = O.TGradOracle(sr, ranks_r, wl.dtype, wl.sparse_ratio, wl.T, wl.lr, *wl.betas, wl.eps)
+    gr = np.ascontiguousarray(g[:4])
     t0 = time.perf_counter()
-    orc.step(W, g)
-    dt = time.perf_counter() - t0
+    orc.refresh(gr, 1)
+    dtr = time.perf_counter() - t0
+    nr = int(np.prod(sr, dtype=np.int64))
+    refresh = {"value": nr / dtr, "unit": "grad elems/s", "seconds": dtr,
+               "sample": f"1 refresh (sort-based top-k, fp64 Grams, eigh) on the first 4 leading "
+                         f"indices {sr} ({nr} elements), all cores"}
     threads = len(os.sched_getaffinity(0))
     cpu_model, blas = None, None
     try:
@@ -170,10 +205,88 @@ def cpu_baseline(wl, seed=0):
         blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"].get("name")
     except Exception:
         pass
-    return {"value": wl.numel / dt, "unit": "grad elems/s", "cores": threads, "kind": "oracle",
-            "sample": f"1 non-refresh step of the full workload ({wl.numel} elements), "
-                      f"{dt:.1f} s; numpy BLAS threads = available cores; refresh excluded",
-            "seconds": dt, "cpu_model": cpu_model, "blas": blas}
+    return {"value": n_all / dt, "unit": "grad elems/s", "cores": threads, "kind": "oracle",
+            "sample": f"1 non-refresh step of the full workload ({n_all} elements), "
+                      f"{dt:.1f} s; numpy BLAS threads = available cores",
+            "seconds": dt, "one_thread": one, "refresh": refresh,
+            "cpu_model": cpu_model, "blas": blas}
+
+
+def kernel_table(timed, work, reps):
+    """Per kernel: launches, ms, and from the launch record its algorithmic bytes, flops,
+    achieved GB/s and TFLOP/s (bytes and flops of all its launches in one step or refresh
+    over their total time)."""
+    out = {}
+    for name, (n, ms) in timed.items():
+        per = n // reps if n % reps == 0 else n / reps
+        entry = {"launches": per, "avg_ms": round(ms / n, 5), "ms": round(ms / reps, 5)}
+        if name in work:
+            _, byts, fl = work[name]
+            t = ms / reps * 1e-3
+            entry.update({"alg_bytes": int(byts), "achieved_GBs": round(byts / t / 1e9, 1),
+                          "hbm_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4)})
+            if fl:
+                entry.update({"flops": int(fl), "achieved_TFs": round(fl / t / 1e12, 2)})
+        out[name] = entry
+    return out
+
+
+def other_configs(dev, stream, steps=10, warmup=3, refresh_reps=3):
+    """The other workloads, one tensor each: ms per step (K steps, no events inside), the
+    per-kernel table (K more steps with an event pair around every launch, bytes and
+    flops from the launch record), and the refresh alone (median of refresh_reps) with
+    its per-kernel table."""
+    import torch
+    import tensor_gradient_compression_amd as tg
+    from synth import F32_32x32x16x16, F16_4x64x64x64x64, C64_64x64x64x33, GradStream, init_weights
+    out = {}
+    for key, wl, desc in (
+            ("fp16_64x64x64x64", F16_4x64x64x64x64,
+             "fp16 (64,64,64,64), Tucker ranks (32,32,32,32), 5% sparse (one of the 4 layers)"),
+            ("c64_64x64x64x33", C64_64x64x64x33,
+             "complex64 (64,64,64,33), Tucker ranks (32,32,32,16), 5% sparse"),
+            ("fp32_32x32x16x16", F32_32x32x16x16,
+             "fp32 (32,32,16,16), Tucker ranks (16,16,8,8), 5% sparse")):
+        # refresh period beyond the run: the steps timed are plain steps (step 1 refreshes)
+        lib = tg.TGrad(wl.shape, wl.ranks, wl.dtype, wl.sparse_ratio, 10 ** 6, wl.lr, wl.betas,
+                       wl.eps)
+        gs = GradStream(wl, seed=0)
+        G = [tg.to_device(gs.next(), wl.dtype, dev) for _ in range(2)]
+        W = tg.to_device(init_weights(wl, seed=0), wl.dtype, dev)
+        for i in range(warmup):
+            lib.step(W, G[i % 2], stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            lib.step(W, G[i % 2], stream)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        lib.timing_enable(True, 100000)
+        for i in range(steps):
+            lib.step(W, G[i % 2], stream)
+        rec = lib.timing_read()
+        kb = by_kernel(lib.last_launches())
+        rt = []
+        for _ in range(refresh_reps):
+            torch.cuda.synchronize()
+            r0 = time.perf_counter()
+            lib.refresh(G[0], stream)
+            torch.cuda.synchronize()
+            rt.append((time.perf_counter() - r0) * 1e3)
+        rrec = lib.timing_read()
+        rkb = by_kernel(lib.last_launches())
+        lib.timing_enable(False, 0)
+        step_bytes, _ = unfused_step_bytes(wl)
+        out[key] = {"workload": desc, "numel": wl.numel, "ms_per_step": round(ms, 4),
+                    "grad_elems_per_s": wl.numel / (ms * 1e-3),
+                    "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "kernels": kernel_table(rec, kb, steps),
+                    "refresh_ms": round(float(np.median(rt)), 3),
+                    "refresh_kernels": kernel_table(rrec, rkb, refresh_reps)}
+        lib.close()
+        del G, W
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -183,6 +296,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--refresh-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the per-kernel measurement of the other workloads")
     ap.add_argument("--no-multi-tensor", action="store_true",
                     help="skip the 4-layer fp16 sequential vs tgrad_step_many measurement")
     ap.add_argument("--plan", type=int, default=None,
@@ -290,25 +405,8 @@ def main():
     copy_gbs = 2.0 * ncp * 4 * 5 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
     del ca, cb
 
-    def table(timed, work, reps):
-        """Per kernel: launches, ms, and from the launch record its algorithmic bytes,
-        flops, achieved GB/s and TFLOP/s (bytes and flops of all its launches in one
-        step or refresh over their total time)."""
-        out = {}
-        for name, (n, ms) in timed.items():
-            per = n // reps if n % reps == 0 else n / reps
-            entry = {"launches": per, "avg_ms": round(ms / n, 5), "ms": round(ms / reps, 5)}
-            if name in work:
-                _, byts, fl = work[name]
-                t = ms / reps * 1e-3
-                entry.update({"alg_bytes": int(byts), "achieved_GBs": round(byts / t / 1e9, 1),
-                              "hbm_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4)})
-                if fl:
-                    entry.update({"flops": int(fl), "achieved_TFs": round(fl / t / 1e12, 2)})
-            out[name] = entry
-        return out
-    kernels = table(rec, kb, K)
-    refresh_kernels = table(rrec, refresh_launches, args.refresh_reps)
+    kernels = kernel_table(rec, kb, K)
+    refresh_kernels = kernel_table(rrec, refresh_launches, args.refresh_reps)
 
     # the dominant kernel's launches inside the timed steps
     dn, dms = drec[dom]
@@ -329,6 +427,7 @@ def main():
     del grads
     torch.cuda.empty_cache()
     multi = None if args.no_multi_tensor else multi_tensor(dev, stream)
+    others = None if args.no_other_configs else other_configs(dev, stream)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -366,6 +465,7 @@ def main():
                         "timed steps carry events around the roofline kernel only",
         "refresh_kernels": refresh_kernels,
         "multi_tensor": multi,
+        "other_configs": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
