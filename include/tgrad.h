@@ -58,14 +58,14 @@ enum tgrad_status {
 };
 
 #define TGRAD_MAX_NDIM 8
-#define TGRAD_MAX_FACTOR_DIM 64   /* largest I_n of a mode with r_n < I_n */
+#define TGRAD_MAX_FACTOR_DIM 128  /* largest I_n of a mode with r_n < I_n */
 
 /*
  * Create a handle on the current HIP device and allocate all optimizer state.
  *   ndim            number of modes d, 1..8
  *   shape[d]        I_n >= 1; N = prod I_n must be < 2^32
  *   tucker_ranks[d] r_n in [1, I_n]. r_n == I_n keeps mode n uncompressed (identity
- *                   factor, no mode product); r_n < I_n needs I_n <= 64 and
+ *                   factor, no mode product); r_n < I_n needs I_n <= 128 and
  *                   r_n <= N / I_n (the rank of the mode-n unfolding).
  *   dtype           enum tgrad_dtype of W and G
  *   sparse_ratio    rho in [0, 1]; k = floor(rho * N) computed in IEEE double

@@ -506,6 +506,375 @@ __global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
   }
 }
 
+// ---------------------------------------------------------------- 64 < I <= 128
+// The same parallel cyclic Jacobi (round-robin pairs, rotations formed from one matrix
+// per round, A <- J^H A J with the column rotation then the row rotation, the Hermitian
+// phase on column q), for matrices too large to hold A and V in LDS in fp64: A is kept
+// as its packed upper triangle (row i holds a_ii .. a_in; a_ji = conj(a_ij)), and V in
+// registers, in round-robin position order: lane j of a wave holds, for 8 of V's rows,
+// the two columns that pair j of the current round joins, so a round's column rotation
+// is local to the lane; between rounds the players move one position on, which moves
+// each held column to a neighbouring lane (two shuffles). 1024 threads: 16 waves of
+// V rows; the A update visits the pair blocks (a <= b), the block (b, a) being its
+// conjugate transpose. Eigenvector columns are gathered through LDS (the packed A's
+// space, 64 columns at a time) for the canonical sign / phase and the outputs.
+constexpr int NTB = 1024;
+constexpr int RPW = 8;   // V rows a wave holds (I <= 16 RPW)
+
+__device__ __forceinline__ uint32_t tri(uint32_t n, uint32_t i, uint32_t j) {   // i <= j
+  return i * n - (i * (i - 1u)) / 2u + (j - i);
+}
+
+template <bool CPLX>
+__global__ void __launch_bounds__(NTB) k_eig_big(EK kk) {
+  extern __shared__ double sm[];
+  const EK1& k = kk.m[blockIdx.x];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t n = k.n;
+  const uint32_t npk = n * (n + 1) / 2;
+  const uint32_t area = npk > 64u * n ? npk : 64u * n;   // A, later 64 columns of V
+  double* Ar = sm;
+  double* Ai = CPLX ? Ar + area : nullptr;
+  double* rot = (CPLX ? Ai : Ar) + area;   // pair j: c, s, Re e^{i phi}, Im e^{i phi}
+  double* red = rot + 4 * 64;              // 2 x 16 wave partials
+  double* diag = red + 32;                 // 128
+  int* rpq = (int*)(diag + 128);           // pair j: p, q (q = -1 for a bye)
+  int* order = rpq + 128;                  // 128
+
+  const uint32_t m = n + (n & 1u);
+  const uint32_t half = m / 2;
+  auto player = [&](uint32_t pos, uint32_t g) -> uint32_t {
+    if (pos == 0) return 0u;
+    uint32_t x = pos - 1u + g;
+    if (x >= m - 1u) x -= m - 1u;
+    return 1u + x;
+  };
+  auto pair = [&](uint32_t j, uint32_t g, int& p, int& q) {
+    const uint32_t x = player(j, g), y = player(m - 1 - j, g);
+    const uint32_t lo = x < y ? x : y, hi = x < y ? y : x;
+    p = (int)lo;
+    q = hi < n ? (int)hi : -1;
+  };
+
+  // A from the Gram (symmetrised; complex: the Hermitian matrix of the stacked real Gram)
+  const uint32_t K = CPLX ? 2 * n : n;
+  for (uint32_t idx0 = tid; idx0 < n * n; idx0 += NTB) {
+    const uint32_t i = idx0 / n, j = idx0 - i * n;
+    if (i > j) continue;
+    const uint32_t t = tri(n, i, j);
+    if (CPLX) {
+      auto G = [&](uint32_t a, uint32_t b) { return k.gram[(uint64_t)a * K + b]; };
+      const double re1 = G(2 * i, 2 * j) + G(2 * i + 1, 2 * j + 1);
+      const double im1 = G(2 * i + 1, 2 * j) - G(2 * i, 2 * j + 1);
+      const double re2 = G(2 * j, 2 * i) + G(2 * j + 1, 2 * i + 1);
+      const double im2 = G(2 * j + 1, 2 * i) - G(2 * j, 2 * i + 1);
+      Ar[t] = 0.5 * (re1 + re2);
+      Ai[t] = 0.5 * (im1 - im2);
+    } else {
+      Ar[t] = 0.5 * (k.gram[(uint64_t)i * n + j] + k.gram[(uint64_t)j * n + i]);
+    }
+  }
+  // V = I in the positions of round 0: slot `lane`, rows wave + 16 r
+  double fr[RPW], sr[RPW], fi[RPW], si[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const uint32_t i = wave + 16u * r;
+    fr[r] = (lane < half && player(lane, 0) == i) ? 1.0 : 0.0;
+    sr[r] = (lane < half && player(m - 1 - lane, 0) == i) ? 1.0 : 0.0;
+    fi[r] = 0.0;
+    si[r] = 0.0;
+  }
+
+  auto getA = [&](int r, int c, double& xr, double& xi) {
+    if (r < 0 || c < 0) { xr = 0.0; xi = 0.0; return; }
+    if (r <= c) {
+      const uint32_t t = tri(n, (uint32_t)r, (uint32_t)c);
+      xr = Ar[t];
+      xi = CPLX ? Ai[t] : 0.0;
+    } else {
+      const uint32_t t = tri(n, (uint32_t)c, (uint32_t)r);
+      xr = Ar[t];
+      xi = CPLX ? -Ai[t] : 0.0;
+    }
+  };
+  auto putA = [&](int r, int c, double xr, double xi) {
+    if (r < 0 || c < 0) return;
+    if (r <= c) {
+      const uint32_t t = tri(n, (uint32_t)r, (uint32_t)c);
+      Ar[t] = xr;
+      if (CPLX) Ai[t] = xi;
+    } else {
+      const uint32_t t = tri(n, (uint32_t)c, (uint32_t)r);
+      Ar[t] = xr;
+      if (CPLX) Ai[t] = -xi;
+    }
+  };
+
+  int sweeps = -1;
+  for (int sweep = 0;; ++sweep) {
+    __syncthreads();   // A complete (set-up or the last round)
+    double off = 0.0, tot = 0.0;
+    for (uint32_t idx0 = tid; idx0 < n * n; idx0 += NTB) {
+      const uint32_t i = idx0 / n, j = idx0 - i * n;
+      if (i > j) continue;
+      const uint32_t t = tri(n, i, j);
+      const double a2 = Ar[t] * Ar[t] + (CPLX ? Ai[t] * Ai[t] : 0.0);
+      if (i == j) {
+        tot += a2;
+      } else {
+        off += 2.0 * a2;
+        tot += 2.0 * a2;
+      }
+    }
+    off = wave_sum(off);
+    tot = wave_sum(tot);
+    if (lane == 0) {
+      red[wave] = off;
+      red[16 + wave] = tot;
+    }
+    __syncthreads();
+    off = 0.0;
+    tot = 0.0;
+    for (int w = 0; w < NTB / 64; ++w) {
+      off += red[w];
+      tot += red[16 + w];
+    }
+    if (!(off > 1e-20 * tot)) {
+      sweeps = sweep;
+      break;
+    }
+    if (sweep == MAX_SWEEPS) break;
+
+    for (uint32_t round = 0; round + 1 < m; ++round) {
+      // 1. the round's rotations (pair tid), from the matrix as the last round left it
+      if (tid < half) {
+        int p, q;
+        pair(tid, round, p, q);
+        double c = 1.0, s = 0.0, pr = 1.0, pi = 0.0;
+        if (q >= 0) {
+          const double app = Ar[tri(n, p, p)], aqq = Ar[tri(n, q, q)];
+          const uint32_t t = tri(n, p, q);
+          const double xr = Ar[t], xi = CPLX ? Ai[t] : 0.0;
+          const double rr = CPLX ? sqrt(xr * xr + xi * xi) : fabs(xr);
+          if (rr > 0.0) {
+            const double d = 2.0 * rr;
+            const double theta = d >= 2.2250738585072014e-308 ? (aqq - app) * rcp64(d)
+                                                             : (aqq - app) / d;
+            double tt;
+            if (fabs(theta) > 1e100) {
+              tt = 0.5 * rcp64(theta);
+            } else {
+              const double u = theta * theta + 1.0;
+              tt = (theta >= 0.0 ? 1.0 : -1.0) * rcp64(fabs(theta) + u * rsq64(u));
+            }
+            c = rsq64(tt * tt + 1.0);
+            s = tt * c;
+            if (CPLX) {
+              pr = xr / rr;
+              pi = xi / rr;
+            } else {
+              pr = xr >= 0.0 ? 1.0 : -1.0;
+            }
+          }
+        }
+        rot[4 * tid + 0] = c;
+        rot[4 * tid + 1] = s;
+        rot[4 * tid + 2] = pr;
+        rot[4 * tid + 3] = pi;
+        rpq[2 * tid] = p;
+        rpq[2 * tid + 1] = q;
+      }
+      __syncthreads();
+      // 2. A <- J^H A J on the pair blocks (a <= b)
+      for (uint32_t bi = tid; bi < half * half; bi += NTB) {
+        const uint32_t a = bi / half, b = bi - a * half;
+        if (a > b) continue;
+        const int pa = rpq[2 * a], qa = rpq[2 * a + 1], pb = rpq[2 * b], qb = rpq[2 * b + 1];
+        const double ca = rot[4 * a], sa = rot[4 * a + 1], par = rot[4 * a + 2], pai = rot[4 * a + 3];
+        const double cb = rot[4 * b], sb = rot[4 * b + 1], pbr = rot[4 * b + 2], pbi = rot[4 * b + 3];
+        const bool ra = qa >= 0 && sa != 0.0, rb = qb >= 0 && sb != 0.0;
+        if (!ra && !rb) continue;
+        double x00r, x00i, x01r, x01i, x10r, x10i, x11r, x11i;
+        getA(pa, pb, x00r, x00i);
+        getA(pa, qb, x01r, x01i);
+        getA(qa, pb, x10r, x10i);
+        getA(qa, qb, x11r, x11i);
+        if (rb) {   // columns pb, qb: y' = conj(ph_b) y; x <- c x - s y', y <- s x + c y'
+          auto col = [&](double& xr, double& xi, double& yr, double& yi) {
+            const double ur = pbr * yr + pbi * yi, ui = pbr * yi - pbi * yr;
+            const double nxr = cb * xr - sb * ur, nxi = cb * xi - sb * ui;
+            const double nyr = sb * xr + cb * ur, nyi = sb * xi + cb * ui;
+            xr = nxr; xi = nxi; yr = nyr; yi = nyi;
+          };
+          col(x00r, x00i, x01r, x01i);
+          col(x10r, x10i, x11r, x11i);
+        }
+        if (ra) {   // rows pa, qa: y' = ph_a y; x <- c x - s y', y <- s x + c y'
+          auto row = [&](double& xr, double& xi, double& yr, double& yi) {
+            const double ur = par * yr - pai * yi, ui = par * yi + pai * yr;
+            const double nxr = ca * xr - sa * ur, nxi = ca * xi - sa * ui;
+            const double nyr = sa * xr + ca * ur, nyi = sa * xi + ca * ui;
+            xr = nxr; xi = nxi; yr = nyr; yi = nyi;
+          };
+          row(x00r, x00i, x10r, x10i);
+          row(x01r, x01i, x11r, x11i);
+        }
+        if (a == b) {   // pa < qa: the upper entries of the diagonal block
+          putA(pa, pa, x00r, CPLX ? 0.0 : x00i);
+          putA(pa, qa, x01r, x01i);
+          putA(qa, qa, x11r, CPLX ? 0.0 : x11i);
+        } else {
+          putA(pa, pb, x00r, x00i);
+          putA(pa, qb, x01r, x01i);
+          putA(qa, pb, x10r, x10i);
+          putA(qa, qb, x11r, x11i);
+        }
+      }
+      // 3. V <- V J on the lane's pair, then every held column moves one position on
+      if (lane < half) {
+        int p, q;
+        pair(lane, round, p, q);
+        const double c = rot[4 * lane], s = rot[4 * lane + 1];
+        const double phr = rot[4 * lane + 2], phi = rot[4 * lane + 3];
+        if (q >= 0 && s != 0.0) {
+          const bool fp = player(lane, round) == (uint32_t)p;   // the first slot holds p
+#pragma unroll
+          for (int r = 0; r < RPW; ++r) {
+            const double vpr = fp ? fr[r] : sr[r], vpi = fp ? fi[r] : si[r];
+            const double vqr = fp ? sr[r] : fr[r], vqi = fp ? si[r] : fi[r];
+            const double yr = phr * vqr + phi * vqi, yi = phr * vqi - phi * vqr;   // conj(ph) vq
+            const double npr = c * vpr - s * yr, npi = c * vpi - s * yi;
+            const double nqr = s * vpr + c * yr, nqi = s * vpi + c * yi;
+            if (fp) {
+              fr[r] = npr; fi[r] = npi; sr[r] = nqr; si[r] = nqi;
+            } else {
+              sr[r] = npr; si[r] = npi; fr[r] = nqr; fi[r] = nqi;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const double fnr = __shfl(fr[r], (int)lane + 1, 64), snr = __shfl(sr[r], (int)lane - 1, 64);
+        const double f1r = __shfl(fr[r], 1, 64);
+        double fni = 0.0, sni = 0.0, f1i = 0.0;
+        if (CPLX) {
+          fni = __shfl(fi[r], (int)lane + 1, 64);
+          sni = __shfl(si[r], (int)lane - 1, 64);
+          f1i = __shfl(fi[r], 1, 64);
+        }
+        if (lane == 0) {
+          sr[r] = f1r;
+          si[r] = f1i;
+        } else if (lane < half) {
+          const double nfr = lane + 1 == half ? sr[r] : fnr;
+          const double nfi = lane + 1 == half ? si[r] : fni;
+          sr[r] = snr;
+          si[r] = sni;
+          fr[r] = nfr;
+          fi[r] = nfi;
+        }
+        __builtin_amdgcn_sched_barrier(0);   // one row's shuffles in flight at a time
+      }
+      __syncthreads();   // the rotations and A are rewritten next round
+    }
+  }
+  __syncthreads();
+  if (tid == 0) *k.status = sweeps;
+  if (tid < n) diag[tid] = Ar[tri(n, tid, tid)];
+  __syncthreads();
+  // descending order of the diagonal, equal values in index order
+  if (tid < n) {
+    const double d = diag[tid];
+    uint32_t rank = 0;
+    for (uint32_t j = 0; j < n; ++j) {
+      const double e = diag[j];
+      rank += (e > d || (e == d && j < tid)) ? 1u : 0u;
+    }
+    order[rank] = (int)tid;
+  }
+  __syncthreads();
+  if (tid < n) k.eigvals[tid] = diag[order[tid]];
+
+  // columns of V through LDS, 64 players at a time (column-major, n rows each); one wave
+  // per selected column: largest |entry| (lowest row on ties) made real positive
+  const uint32_t r = k.r;
+  for (uint32_t cb = 0; cb < n; cb += 64) {
+    __syncthreads();
+    if (lane < half) {
+      const uint32_t xs[2] = {player(lane, 0), player(m - 1 - lane, 0)};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t x = xs[h];
+        if (x >= n || x < cb || x >= cb + 64) continue;
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) {
+          const uint32_t i = wave + 16u * rr;
+          if (i >= n) continue;
+          Ar[(x - cb) * n + i] = h == 0 ? fr[rr] : sr[rr];
+          if (CPLX) Ai[(x - cb) * n + i] = h == 0 ? fi[rr] : si[rr];
+        }
+      }
+    }
+    __syncthreads();
+    for (uint32_t c = wave; c < r; c += NTB / 64) {
+      const uint32_t src = (uint32_t)order[c];
+      if (src < cb || src >= cb + 64) continue;
+      const double* colr = Ar + (src - cb) * n;
+      const double* coli = CPLX ? Ai + (src - cb) * n : nullptr;
+      double best = -1.0;
+      uint32_t bi = 0;
+      for (uint32_t i = lane; i < n; i += 64) {
+        const double vr = colr[i], vi = CPLX ? coli[i] : 0.0;
+        const double a2 = vr * vr + vi * vi;
+        if (a2 > best) { best = a2; bi = i; }
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const double ob = __shfl_xor(best, off, 64);
+        const uint32_t oi = __shfl_xor(bi, off, 64);
+        if (ob > best || (ob == best && oi < bi)) {
+          best = ob;
+          bi = oi;
+        }
+      }
+      const double mr = colr[bi], mi = CPLX ? coli[bi] : 0.0;
+      const double mag = sqrt(mr * mr + mi * mi);
+      const double scr = mag > 0.0 ? mr / mag : 1.0;   // scale = conj(phase)
+      const double sci = mag > 0.0 ? -mi / mag : 0.0;
+      for (uint32_t i = lane; i < n; i += 64) {
+        const double xr = colr[i], xi = CPLX ? coli[i] : 0.0;
+        const float ur = (float)(xr * scr - xi * sci);
+        const float ui = (float)(xr * sci + xi * scr);
+        if (CPLX) {
+          k.U[((uint64_t)i * r + c) * 2] = ur;
+          k.U[((uint64_t)i * r + c) * 2 + 1] = ui;
+          const uint64_t KP = 2ull * n, RP = 2ull * r;
+          k.Mproj[(2 * c) * KP + 2 * i] = ur;
+          k.Mproj[(2 * c) * KP + 2 * i + 1] = ui;
+          k.Mproj[(2 * c + 1) * KP + 2 * i] = -ui;
+          k.Mproj[(2 * c + 1) * KP + 2 * i + 1] = ur;
+          k.Mrec[(2 * i) * RP + 2 * c] = ur;
+          k.Mrec[(2 * i) * RP + 2 * c + 1] = -ui;
+          k.Mrec[(2 * i + 1) * RP + 2 * c] = ui;
+          k.Mrec[(2 * i + 1) * RP + 2 * c + 1] = ur;
+        } else {
+          k.U[(uint64_t)i * r + c] = ur;
+          k.Mproj[(uint64_t)c * n + i] = ur;
+          k.Mrec[(uint64_t)i * r + c] = ur;
+        }
+      }
+    }
+  }
+}
+
+size_t eig_big_lds(uint32_t I, uint32_t P) {
+  const size_t npk = (size_t)I * (I + 1) / 2;
+  const size_t area = npk > 64u * (size_t)I ? npk : 64u * (size_t)I;
+  return (area * P + 4 * 64 + 32 + 128) * sizeof(double) + (128 + 128) * sizeof(int);
+}
+
 }  // namespace
 
 size_t eig_lds_bytes(uint32_t I, uint32_t P) {
@@ -516,30 +885,50 @@ size_t eig_lds_bytes(uint32_t I, uint32_t P) {
 
 hipError_t launch_eig(const EigArgs* e, int count, hipStream_t s) {
   if (count < 1 || count > 8) return hipErrorInvalidValue;
-  EK k;
-  size_t lds = 0;
-  for (int i = 0; i < count; ++i) {
-    if (e[i].I > 64 || e[i].r > e[i].I || e[i].r < 1 || e[i].P != e[0].P) return hipErrorInvalidValue;
-    k.m[i].gram = e[i].gram;
-    k.m[i].U = e[i].U;
-    k.m[i].Mproj = e[i].Mproj;
-    k.m[i].Mrec = e[i].Mrec;
-    k.m[i].eigvals = e[i].eigvals;
-    k.m[i].status = e[i].status;
-    k.m[i].n = e[i].I;
-    k.m[i].r = e[i].r;
-    const size_t b = eig_lds_bytes(e[i].I, e[i].P);
-    if (b > lds) lds = b;
-  }
   const bool cplx = e[0].P == 2;
-  auto fn = cplx ? k_eig<true> : k_eig_sym;
-  if (lds > 64 * 1024) {
-    hipError_t err = hipFuncSetAttribute((const void*)fn,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // matrices up to 64 on the LDS-resident kernels, larger ones (up to 128) on k_eig_big
+  EK ks, kb;
+  int ns = 0, nb = 0;
+  size_t lds_s = 0, lds_b = 0;
+  for (int i = 0; i < count; ++i) {
+    if (e[i].I > 128 || e[i].r > e[i].I || e[i].r < 1 || e[i].P != e[0].P) return hipErrorInvalidValue;
+    const bool big = e[i].I > 64;
+    EK1& m = big ? kb.m[nb++] : ks.m[ns++];
+    m.gram = e[i].gram;
+    m.U = e[i].U;
+    m.Mproj = e[i].Mproj;
+    m.Mrec = e[i].Mrec;
+    m.eigvals = e[i].eigvals;
+    m.status = e[i].status;
+    m.n = e[i].I;
+    m.r = e[i].r;
+    const size_t b = big ? eig_big_lds(e[i].I, e[i].P) : eig_lds_bytes(e[i].I, e[i].P);
+    size_t& l = big ? lds_b : lds_s;
+    if (b > l) l = b;
+  }
+  if (ns) {
+    auto fn = cplx ? k_eig<true> : k_eig_sym;
+    if (lds_s > 64 * 1024) {
+      hipError_t err = hipFuncSetAttribute((const void*)fn,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_s);
+      if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(fn, dim3(ns), dim3(cplx ? NTH : NTS), lds_s, s, ks);
+    hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(fn, dim3(count), dim3(cplx ? NTH : NTS), lds, s, k);
-  return hipGetLastError();
+  if (nb) {
+    auto fn = cplx ? k_eig_big<true> : k_eig_big<false>;
+    if (lds_b > 64 * 1024) {
+      hipError_t err = hipFuncSetAttribute((const void*)fn,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_b);
+      if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(fn, dim3(nb), dim3(NTB), lds_b, s, kb);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace tg

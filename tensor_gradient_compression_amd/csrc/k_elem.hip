@@ -16,6 +16,11 @@
 //   apply_dense:  the update when no mode is compressed (every r_n = I_n): Delta =
 //                 N_C, plus N_S at Omega, W <- round(W * decay - lr * Delta), decay =
 //                 fp32(1 - lr * weight_decay) (decoupled decay, exactly 1 without it).
+//   csplit:       complex mode products wider than the tiled kernel's 128 real rows
+//                 and columns run as two real products on the interleaved (re, im)
+//                 view of the tensor, one with Re M and one with Im M;
+//                 split_operand takes those two parts out of the real-block operand
+//                 and combine forms (Re M) x + i (Im M) x from the two outputs.
 #include "tg_common.h"
 
 namespace tg {
@@ -226,6 +231,73 @@ hipError_t launch_apply_dense(int dt, void* W, const float* u_core, const uint64
       break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+namespace {
+
+// re[r, c] = M[2r, 2c] and im[r, c] = M[2r + 1, 2c] of the (2 rows) x (2 cols) real-block
+// form of a complex matrix (each entry a + ib stored as the block [[a, -b], [b, a]])
+__global__ void __launch_bounds__(256) k_split_operand(const float* __restrict__ M,
+                                                       uint32_t rows, uint32_t cols,
+                                                       float* __restrict__ re,
+                                                       float* __restrict__ im) {
+  const uint64_t n = (uint64_t)rows * cols;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n; j += stride) {
+    const uint64_t r = j / cols, c = j % cols;
+    re[j] = M[(2 * r) * (2 * (uint64_t)cols) + 2 * c];
+    im[j] = M[(2 * r + 1) * (2 * (uint64_t)cols) + 2 * c];
+  }
+}
+
+// y1 holds (Re M) x and y2 (Im M) x, both as (re, im) pairs; y1 <- M x:
+// re = y1.re - y2.im, im = y1.im + y2.re. VEC (both buffers 16-byte aligned): two
+// complex values (16 bytes) per thread and pass, and an odd count leaves one pair, done
+// on its own; otherwise one pair per thread and pass.
+template <bool VEC>
+__global__ void __launch_bounds__(256) k_csplit_combine(float* __restrict__ y1,
+                                                        const float* __restrict__ y2,
+                                                        uint64_t npairs) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  const uint64_t t0 = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (!VEC) {
+    for (uint64_t q = t0; q < npairs; q += stride) {
+      const float ar = y1[2 * q], ai = y1[2 * q + 1], br = y2[2 * q], bi = y2[2 * q + 1];
+      y1[2 * q] = ar - bi;
+      y1[2 * q + 1] = ai + br;
+    }
+    return;
+  }
+  const uint64_t nq = npairs / 2;
+  for (uint64_t q = t0; q < nq; q += stride) {
+    const float4 a = reinterpret_cast<const float4*>(y1)[q];
+    const float4 b = reinterpret_cast<const float4*>(y2)[q];
+    reinterpret_cast<float4*>(y1)[q] = make_float4(a.x - b.y, a.y + b.x, a.z - b.w, a.w + b.z);
+  }
+  if ((npairs & 1) && t0 == 0) {
+    const uint64_t e = 2 * (npairs - 1);
+    const float ar = y1[e], ai = y1[e + 1], br = y2[e], bi = y2[e + 1];
+    y1[e] = ar - bi;
+    y1[e + 1] = ai + br;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_split_operand(const float* M, uint32_t rows, uint32_t cols, float* re,
+                                float* im, hipStream_t s) {
+  k_split_operand<<<grid_for((uint64_t)rows * cols, 256, 1024), 256, 0, s>>>(M, rows, cols, re,
+                                                                            im);
+  return hipGetLastError();
+}
+
+hipError_t launch_csplit_combine(float* y1, const float* y2, uint64_t npairs, hipStream_t s) {
+  if (!npairs) return hipSuccess;
+  if ((((uintptr_t)y1) | ((uintptr_t)y2)) % 16 == 0)
+    k_csplit_combine<true><<<grid_for(npairs / 2 + 1, 256, 8192), 256, 0, s>>>(y1, y2, npairs);
+  else
+    k_csplit_combine<false><<<grid_for(npairs, 256, 8192), 256, 0, s>>>(y1, y2, npairs);
   return hipGetLastError();
 }
 

@@ -39,6 +39,7 @@ struct GK {
   uint32_t A, I, B;
   uint32_t Kin, nb;   // Kin = I*P; nb = ceil(Kin / 16)
   uint32_t TA, wide;
+  uint32_t ob0, ob1;  // the output blocks of this launch: ob0 <= block < ob1 (of nb * nb)
 };
 
 // NOB = output 16x16 blocks per wave (nb*nb blocks over 4 waves).
@@ -55,8 +56,6 @@ __global__ void __launch_bounds__(NTH) k_gram(GK k) {
   constexpr uint32_t TWSH = (P == 1) ? 6 : 7;
   const uint32_t rs = k.wide ? TW + PADW : k.B * P;
   const uint32_t blk = k.I * k.B * P;
-  const uint32_t nblocks = k.nb * k.nb;
-
   f4 acc[NOB];
   double dacc[NOB][4];
 #pragma unroll
@@ -122,8 +121,8 @@ __global__ void __launch_bounds__(NTH) k_gram(GK k) {
       const uint32_t cbase = scol[c];
 #pragma unroll
       for (int q = 0; q < NOB; ++q) {
-        const uint32_t ob = wave + 4 * q;
-        if (ob < nblocks) {
+        const uint32_t ob = k.ob0 + wave + 4 * q;
+        if (ob < k.ob1) {
           const uint32_t rb = ob / k.nb, cb = ob - rb * k.nb;
           const uint32_t ka = rb * 16 + (lane & 15), kb = cb * 16 + (lane & 15);
           float av = 0.0f, bv = 0.0f;
@@ -143,8 +142,8 @@ __global__ void __launch_bounds__(NTH) k_gram(GK k) {
   double* out = k.partial + (uint64_t)blockIdx.x * k.Kin * k.Kin;
 #pragma unroll
   for (int q = 0; q < NOB; ++q) {
-    const uint32_t ob = wave + 4 * q;
-    if (ob < nblocks) {
+    const uint32_t ob = k.ob0 + wave + 4 * q;
+    if (ob < k.ob1) {
       const uint32_t rb = ob / k.nb, cb = ob - rb * k.nb;
       const uint32_t colj = cb * 16 + (lane & 15);
       for (int v = 0; v < 4; ++v) {
@@ -215,13 +214,24 @@ hipError_t gogram(const GK& k, size_t lds, unsigned grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+// More than 64 output blocks (I P > 128): launches of 64 blocks each (16 a wave), every
+// one re-reading the tiles; each writes its own entries of the same partial sums.
 template <typename XT, int P>
 hipError_t pick_nob(const GK& k, size_t lds, unsigned grid, hipStream_t s) {
-  const uint32_t per_wave = (k.nb * k.nb + 3) / 4;
-  if (per_wave <= 1) return gogram<XT, P, 1>(k, lds, grid, s);
-  if (per_wave <= 4) return gogram<XT, P, 4>(k, lds, grid, s);
-  if (per_wave <= 16) return gogram<XT, P, 16>(k, lds, grid, s);
-  return hipErrorInvalidValue;
+  const uint32_t nblocks = k.nb * k.nb;
+  const uint32_t per_wave = (nblocks + 3) / 4;
+  GK kk = k;
+  kk.ob0 = 0;
+  kk.ob1 = nblocks;
+  if (per_wave <= 1) return gogram<XT, P, 1>(kk, lds, grid, s);
+  if (per_wave <= 4) return gogram<XT, P, 4>(kk, lds, grid, s);
+  for (uint32_t b0 = 0; b0 < nblocks; b0 += 64) {
+    kk.ob0 = b0;
+    kk.ob1 = b0 + 64 < nblocks ? b0 + 64 : nblocks;
+    const hipError_t e = gogram<XT, P, 16>(kk, lds, grid, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------- 16-bit real data
@@ -759,6 +769,9 @@ uint32_t gram_blocks(const GramArgs& g, int num_cu) {
   const GGeo r = ggeo(g);
   uint64_t nb = (uint64_t)(num_cu > 0 ? num_cu : 256) * 4;
   if (nb > r.ntiles) nb = r.ntiles;
+  // at most 2^24 doubles (128 MB) of partial sums
+  const uint64_t k2 = (uint64_t)r.Kin * r.Kin;
+  if (nb * k2 > (1ull << 24)) nb = std::max<uint64_t>(1, (1ull << 24) / k2);
   if (g.max_blocks && nb > g.max_blocks) nb = g.max_blocks;
   if (nb < 1) nb = 1;
   // every block gets at least one tile: recompute from tiles per block
@@ -771,7 +784,7 @@ size_t gram_lds_bytes(const GramArgs& g) { return ggeo(g).lds; }
 hipError_t launch_gram(const GramArgs& g, int num_cu, hipStream_t s,
                        void (*mark)(void*, int, bool), void* mctx) {
   const GGeo r = ggeo(g);
-  if (r.Kin > 128) return hipErrorInvalidValue;
+  if (r.Kin > 256) return hipErrorInvalidValue;
   const uint32_t nblk = gram_blocks(g, num_cu);
   const G16Geo f = g16geo(g, num_cu);
   if (f.ok) {

@@ -61,7 +61,8 @@ enum KernelId {
   KID_RECONSTRUCT, KID_RECON_APPLY, KID_APPLY_DENSE, KID_GRAM, KID_GRAM_REDUCE,
   KID_EIG, KID_FILL, KID_PROJECT_FIRST, KID_PROJECT_FUSED2, KID_RECON_FUSED2_APPLY,
   KID_RECON_FUSED2, KID_REMAP, KID_PROJECT_FUSED3, KID_GRAM3, KID_PROJECT_PAIR, KID_RECON_PAIR,
-  KID_RECON_FUSED3_APPLY, KID_STREAM_PROJECT, KID_STREAM_RECONSTRUCT, KID_COUNT_
+  KID_RECON_FUSED3_APPLY, KID_STREAM_PROJECT, KID_STREAM_RECONSTRUCT, KID_CSPLIT_OPERAND,
+  KID_CSPLIT_COMBINE, KID_COUNT_
 };
 
 // ---------------------------------------------------------------- launchers
@@ -114,6 +115,14 @@ hipError_t launch_adam(int core_dt, const void* g_core, float* u_core, float* m_
 hipError_t launch_apply_dense(int dt, void* W, const float* u_core, const uint64_t* mask,
                               const uint32_t* rank, const float* u_s, uint64_t N, float lr,
                               float decay, int has_sparse, float* delta, hipStream_t s);
+
+// Complex mode products too wide for one real-block product: Re M and Im M as (rows x
+// cols) fp32 matrices from the (2 rows) x (2 cols) real-block operand M, and the
+// combination y1 <- y1 + i y2 of the two real products' outputs (y1 = (Re M) x and
+// y2 = (Im M) x on the interleaved view; npairs complex values).
+hipError_t launch_split_operand(const float* M, uint32_t rows, uint32_t cols, float* re,
+                                float* im, hipStream_t s);
+hipError_t launch_csplit_combine(float* y1, const float* y2, uint64_t npairs, hipStream_t s);
 
 // Mode product Y[a, jj, b] = sum_kk M[jj, kk] X[a, kk, b] over the (A, I, B, P) view.
 struct ModeProd {

@@ -90,6 +90,16 @@ struct tgrad_handle {
   float* U[TGRAD_MAX_NDIM] = {nullptr};
   float* Mp[TGRAD_MAX_NDIM] = {nullptr};
   float* Mr[TGRAD_MAX_NDIM] = {nullptr};
+  // complex modes wider than 64 (their real-block operands exceed the tiled product's
+  // 128 rows or columns): each product runs as two real products on the interleaved
+  // (re, im) view, one with Re M and one with Im M, and a combine pass. Mps: Re, Im of
+  // the projection operand (r x I each); Mrs: of the reconstruction operand (I x r
+  // each); ctmp: the Im M product's output (N P floats), then, when the reconstruction's
+  // last launch is such a mode, its full update before the dense apply (N P floats)
+  bool csplit[TGRAD_MAX_NDIM] = {false};
+  float* Mps[TGRAD_MAX_NDIM] = {nullptr};
+  float* Mrs[TGRAD_MAX_NDIM] = {nullptr};
+  float* ctmp = nullptr;
   double* eig[TGRAD_MAX_NDIM] = {nullptr};
   double* gram_part = nullptr;
   double* gram = nullptr;        // one (I*P)^2 matrix per compressed mode
@@ -365,6 +375,47 @@ hipError_t mode_product(const tgrad_t* h, const ModeProd& mp, hipStream_t s) {
   return launch_modeprod(mp, h->num_cu, s);
 }
 
+// Re and Im parts of mode n's operands (a wide complex mode), from its real-block ones.
+hipError_t split_operands(const tgrad_t* h, int n, hipStream_t s) {
+  const uint32_t I = (uint32_t)h->shape[n], r = (uint32_t)h->ranks[n];
+  const size_t ri = (size_t)r * I;
+  hipError_t e = launch_split_operand(h->Mp[n], r, I, h->Mps[n], h->Mps[n] + ri, s);
+  if (e == hipSuccess) e = launch_split_operand(h->Mr[n], I, r, h->Mrs[n], h->Mrs[n] + ri, s);
+  return e;
+}
+
+// A single-mode product of a wide complex mode n: mp describes it in the real-block form
+// (P = 2, operand (R P) x (I P)); Ms holds Re M then Im M (R x I each). The interleaved
+// view of X is a real (A, I, 2B) tensor, so (Re M) X lands in Y and (Im M) X in ctmp as
+// (re, im) pairs, and the combine pass leaves M X = (Re M) X + i (Im M) X in Y.
+int split_product(tgrad_t* h, const ModeProd& mp, const float* Ms, int n, int kid,
+                  int kid_stream, float* Y, hipStream_t s) {
+  ModeProd m{};
+  m.X = mp.X;
+  m.in_dt = DT_F32;
+  m.A = mp.A;
+  m.I = mp.I;
+  m.B = 2 * mp.B;
+  m.R = mp.R;
+  m.P = 1;
+  m.apply = 0;
+  const uint64_t in = (uint64_t)mp.A * mp.I * mp.B * 2, out = (uint64_t)mp.A * mp.R * mp.B * 2;
+  const uint64_t fl = 2 * ((uint64_t)mp.A * 2 * mp.B) * mp.I * mp.R;
+  float* parts[2] = {Y, h->ctmp};
+  for (int p = 0; p < 2; ++p) {
+    m.M = Ms + (size_t)p * mp.R * mp.I;
+    m.Y = parts[p];
+    const int k = use_stream(h, m) ? kid_stream : kid;
+    Mark mk(h, k);
+    HIPCHK(h, mode_product(h, m, s));
+    record(h, k, 1 << n, in * 4, out * 4, fl);
+  }
+  Mark mk(h, KID_CSPLIT_COMBINE);
+  HIPCHK(h, launch_csplit_combine(Y, h->ctmp, out / 2, s));
+  record(h, KID_CSPLIT_COMBINE, 1 << n, out * 8, out * 4, 2 * out);
+  return TGRAD_OK;
+}
+
 // A group of two modes that is not the trailing pair: a k_pair launch.
 bool is_lead_pair(const tgrad_t* h, const std::vector<int>& g) {
   return g.size() == 2 && std::min(g[0], g[1]) < h->d - 2;
@@ -583,6 +634,13 @@ int do_refresh(tgrad_t* h, const void* grad, hipStream_t s, const RefreshWs& ws)
     HIPCHK(h, launch_eig(eig, ne, s));
     record(h, KID_EIG, 0, 0, 0, 0);
   }
+  for (int n : h->fmodes)
+    if (h->csplit[n]) {
+      Mark m(h, KID_CSPLIT_OPERAND);
+      HIPCHK(h, split_operands(h, n, s));
+      const uint64_t ri = (uint64_t)h->shape[n] * h->ranks[n];
+      record(h, KID_CSPLIT_OPERAND, 1 << n, 2 * ri * 4, 4 * ri * 4, 0);
+    }
   if (lowrank_first) {
     if (h->selection == TGRAD_SELECT_RANDK) {
       if ((rc = select_omega(h, ws.tw, grad, h->dtype, nullptr, s)) != TGRAD_OK) return rc;
@@ -629,7 +687,7 @@ const char* tgrad_kernel_name(int id) {
       "modeprod2_project_first", "modeprod2_reconstruct_apply", "modeprod2_reconstruct",
       "remap_moments", "modeprod3_project_first", "gram3_tail", "modeprod_pair_project",
       "modeprod_pair_reconstruct", "modeprod3_reconstruct_apply", "streamprod_project",
-      "streamprod_reconstruct"};
+      "streamprod_reconstruct", "complex_split_operand", "complex_split_combine"};
   if (id < 0 || id >= KID_COUNT_) return "";
   return names[id];
 }
@@ -796,6 +854,12 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
     ok = ok && dalloc(h, &h->Mp[n], I * r * P * P, false);
     ok = ok && dalloc(h, &h->Mr[n], I * r * P * P, false);
     ok = ok && dalloc(h, &h->eig[n], I, false);
+    if (P == 2 && I > 64) {
+      h->csplit[n] = true;
+      ok = ok && dalloc(h, &h->Mps[n], 2 * I * r, false);
+      ok = ok && dalloc(h, &h->Mrs[n], 2 * I * r, false);
+      if (!h->ctmp) ok = ok && dalloc(h, &h->ctmp, 2 * N * P, false);
+    }
     GramArgs g{};
     view(shape, ndim, n, &g.A, &g.I, &g.B);
     g.P = (uint32_t)P;
@@ -1041,11 +1105,18 @@ int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s) {
       mp.P = P;
       mp.apply = 0;
       mp.Y = Y;
-      const int kid =
-          use_stream(h, mp) ? KID_STREAM_PROJECT : j == 0 ? KID_PROJECT_FIRST : KID_PROJECT;
-      Mark m(h, kid);
-      HIPCHK(h, mode_product(h, mp, s));
-      account_chain(h, kid, cur, proj[j], true, xdt == DT_F32 ? 4 : 2, false, false);
+      if (h->csplit[n]) {
+        const int rc = split_product(h, mp, h->Mps[n], n,
+                                     j == 0 ? KID_PROJECT_FIRST : KID_PROJECT,
+                                     KID_STREAM_PROJECT, Y, s);
+        if (rc != TGRAD_OK) return rc;
+      } else {
+        const int kid =
+            use_stream(h, mp) ? KID_STREAM_PROJECT : j == 0 ? KID_PROJECT_FIRST : KID_PROJECT;
+        Mark m(h, kid);
+        HIPCHK(h, mode_product(h, mp, s));
+        account_chain(h, kid, cur, proj[j], true, xdt == DT_F32 ? 4 : 2, false, false);
+      }
       cur[n] = h->ranks[n];
     }
     X = Y;
@@ -1187,11 +1258,26 @@ int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, fl
       mp.decay = decay;
       mp.has_sparse = app && h->k > 0;
       mp.delta = app ? h->delta_cap : nullptr;
-      const int kid =
-          use_stream(h, mp) ? KID_STREAM_RECONSTRUCT : app ? KID_RECON_APPLY : KID_RECONSTRUCT;
-      Mark m(h, kid);
-      HIPCHK(h, mode_product(h, mp, s));
-      account_chain(h, kid, cur, rec[j], false, 4, false, app);
+      if (h->csplit[n]) {
+        // with apply: the full update goes to ctmp's second half, then the dense apply
+        float* dst = app ? h->ctmp + h->N * P : Y;
+        const int rc = split_product(h, mp, h->Mrs[n], n, KID_RECONSTRUCT,
+                                     KID_STREAM_RECONSTRUCT, dst, s);
+        if (rc != TGRAD_OK) return rc;
+        if (app) {
+          Mark m(h, KID_APPLY_DENSE);
+          HIPCHK(h, launch_apply_dense(h->dtype, weight, dst, h->mask, h->rank, h->S, h->N, lr,
+                                       decay, h->k > 0, h->delta_cap, s));
+          record(h, KID_APPLY_DENSE, 0, h->N * (dt_bytes(h->dtype) + P * 4) + h->k * P * 4,
+                 h->N * dt_bytes(h->dtype), 0);
+        }
+      } else {
+        const int kid =
+            use_stream(h, mp) ? KID_STREAM_RECONSTRUCT : app ? KID_RECON_APPLY : KID_RECONSTRUCT;
+        Mark m(h, kid);
+        HIPCHK(h, mode_product(h, mp, s));
+        account_chain(h, kid, cur, rec[j], false, 4, false, app);
+      }
       cur[n] = h->shape[n];
     }
     X = Y;
@@ -1413,6 +1499,10 @@ int tgrad_set_factor(tgrad_t* h, int mode, const float* U, int64_t n_floats) {
   HIPCHK(h, hipMemcpy(h->U[mode], U, n * 4, hipMemcpyHostToDevice));
   HIPCHK(h, hipMemcpy(h->Mp[mode], mp.data(), mp.size() * 4, hipMemcpyHostToDevice));
   HIPCHK(h, hipMemcpy(h->Mr[mode], mr.data(), mr.size() * 4, hipMemcpyHostToDevice));
+  if (h->csplit[mode]) {
+    HIPCHK(h, split_operands(h, mode, nullptr));
+    HIPCHK(h, hipDeviceSynchronize());
+  }
   return TGRAD_OK;
 }
 
@@ -1553,6 +1643,7 @@ int tgrad_load_state(tgrad_t* h, const void* buf, int64_t size) {
     host_operands(I, r, h->P, U.data(), mp.data(), mr.data());
     HIPCHK(h, hipMemcpy(h->Mp[n], mp.data(), mp.size() * 4, hipMemcpyHostToDevice));
     HIPCHK(h, hipMemcpy(h->Mr[n], mr.data(), mr.size() * 4, hipMemcpyHostToDevice));
+    if (h->csplit[n]) HIPCHK(h, split_operands(h, n, nullptr));
   }
   HIPCHK(h, hipDeviceSynchronize());
   h->t = theirs.t;

@@ -145,6 +145,19 @@ FACTOR_CASES = [
     # four output column blocks per wave (R1 R2 = 512); R0 = 32 over four rounds
     ("bf16-slab3-wide-core", custom((2, 16, 40, 17), "bf16", (1, 8, 32, 16), 0.05)),
     ("bf16-slab3-r0-32", custom((2, 64, 16, 8), "bf16", (1, 32, 8, 4), 0.05)),
+    # compressed modes wider than 64 (the eigensolver for 64 < I <= 128 keeps A packed in
+    # LDS and V in registers): 128 real, an odd width with a bye in every round, and the
+    # narrowest; complex ones (the complex Gram has 256 stacked rows, four launches of 64
+    # output blocks; each mode product runs as two real ones and a combine pass): a
+    # leading 128, a last mode of 100 (its update goes through the dense apply), and two
+    # leading 128s with small trailing modes, the shape of a spectral layer's weights
+    ("f32-128", custom((128, 20, 6), "f32", (40, 10, 3), 0.05)),
+    ("bf16-128x24", custom((128, 24, 8), "bf16", (48, 12, 4), 0.05)),
+    ("c64-128", custom((128, 12, 6), "c64", (30, 6, 3), 0.05)),
+    ("c64-last-100", custom((10, 6, 100), "c64", (4, 3, 20), 0.05)),
+    ("c64-128x128x6x4", custom((128, 128, 6, 4), "c64", (24, 24, 4, 3), 0.05)),
+    ("f32-127-odd", custom((127, 16, 5), "f32", (31, 8, 2), 0.05)),
+    ("f16-65", custom((65, 30, 4), "f16", (16, 10, 2), 0.05)),
     # ... and whose mode d-2 (I0 a multiple of 12) joins the reconstruction's last launch
     # (12 waves a unit, rounds of 12 slabs): 3 rounds a unit with ragged row and column
     # blocks; one round a unit; k = 0; more units than the grid has workgroups

@@ -68,7 +68,7 @@ def _init(lib, shape, ranks, dtype=0, rho=0.05, T=10, lr=1e-3, b1=0.9, b2=0.999,
     dict(shape=(2,) * 9, ranks=(1,) * 9),                   # ndim 9
     dict(shape=(4, 4), ranks=(5, 4)),                       # rank > size
     dict(shape=(4, 4), ranks=(0, 4)),                       # rank 0
-    dict(shape=(65, 4), ranks=(8, 4)),                      # factor mode too large
+    dict(shape=(129, 4), ranks=(8, 4)),                     # factor mode too large
     dict(shape=(4, 4), ranks=(2, 2), dtype=7),              # dtype
     dict(shape=(4, 4), ranks=(2, 2), rho=1.5),              # rho > 1
     dict(shape=(4, 4), ranks=(2, 2), rho=-0.1),
@@ -91,6 +91,8 @@ def test_init_rejects_invalid_arguments(lib, kw):
     dict(shape=(3, 5, 64), ranks=(3, 5, 15)),               # r_n = N / I_n
     dict(shape=(50,), ranks=(1,)),
     dict(shape=(2, 40), ranks=(1, 2)),
+    dict(shape=(128, 4), ranks=(4, 4)),                     # a factor mode of 128
+    dict(shape=(128, 4), ranks=(4, 4), dtype=3),            # a complex factor mode of 128
 ])
 def test_rank_bound_is_inclusive(lib, kw):
     """r_n up to the rank of the mode-n unfolding, N / I_n, passes argument validation:
