@@ -621,8 +621,9 @@ struct S3K {
   uint32_t off_fac;     // per-lane operand tables of passes 1 and 2 (see k_proj3s)
 };
 
-// NTW: output tiles (16 x 16) per wave, at most
-template <typename XT, int NRB1, int NRB2, int NTW>
+// NTW: output tiles (16 x 16) per wave, at most; ND: loads a slab transfer issues
+// ((slab bytes / 16 + 63) / 64)
+template <typename XT, int NRB1, int NRB2, int NTW, int ND>
 __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))) k_proj3s(S3K k) {
   extern __shared__ float smem[];
   const uint32_t lane = threadIdx.x & 63;
@@ -706,6 +707,11 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
   };
   const XT* X = (const XT*)k.X;
   const uint32_t xchunks = slab_e * 2 / 16;
+  // (the slab index is wave-uniform; readfirstlane keeps the base in scalar registers)
+  auto dma = [&](uint32_t s, LDS unsigned char* b) {
+    const uint32_t su = __builtin_amdgcn_readfirstlane(s);
+    wave_dma_n<ND>(X + (uint64_t)su * slab_e, xchunks, b, lane);
+  };
   auto bounds = [&](uint32_t s, BoundsV& b) {
     b = load_bounds(k.mask, k.rank, (uint64_t)s * slab_e, slab_e, N, lane);
   };
@@ -732,7 +738,12 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
       step(r1, c1);
       if (cnt > 1) bounds(slab_at(r1, c1), op.bw);
     }
-    wave_dma(X + (uint64_t)s0 * slab_e, xchunks, xb0, lane);
+    dma(s0, xb0);
+    // every slab is followed by exactly one transfer (a copy of slab 0 when there is no
+    // second slab), so the waits below can count on it
+    uint32_t r1 = 0, c1 = 0;
+    step(r1, c1);
+    dma(cnt > 1 ? slab_at(r1, c1) : s0, xb1);
   }
 
   f4 acc3[NTW];
@@ -765,23 +776,21 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
     const uint32_t n = slab_at(r, c);
     uint32_t r1 = r, c1 = c;
     step(r1, c1);
-    wait_vm0();   // slab n, its Omega indices and the next slab's bounds have landed
+    uint32_t rn2 = r1, cn2 = c1;   // the slab after the next one
+    step(rn2, cn2);
+    // slab n, its Omega indices and the next slab's bounds have landed; the next slab's
+    // transfer, the last ND operations issued, may still be in flight
+    __builtin_amdgcn_s_waitcnt(0x0F70 | ND);   // vmcnt(ND)
     wave_fence();
     write_unit();
-    if (g + 1 < cnt) {
-      const uint32_t n1 = slab_at(r1, c1);
-      if (sparse) range(n1, op.bw, op.lo[nxt], op.hi[nxt]);
-      wave_dma(X + (uint64_t)n1 * slab_e, xchunks, cur ? xb0 : xb1, lane);
-      if (sparse) {
+    if (g + 1 < cnt && sparse) {
+      range(slab_at(r1, c1), op.bw, op.lo[nxt], op.hi[nxt]);
 #pragma unroll
-        for (int q = 0; q < NOM; ++q) {
-          const uint64_t j = op.lo[nxt] + lane + 64 * q;
-          op.om[nxt][q] = k.omega[j < kS ? j : kS - 1];
-        }
-        uint32_t r2 = r1, c2 = c1;
-        step(r2, c2);
-        if (g + 2 < cnt) bounds(slab_at(r2, c2), op.bw);
+      for (int q = 0; q < NOM; ++q) {
+        const uint64_t j = op.lo[nxt] + lane + 64 * q;
+        op.om[nxt][q] = k.omega[j < kS ? j : kS - 1];
       }
+      if (g + 2 < cnt) bounds(slab_at(rn2, cn2), op.bw);
     }
 
     LDS unsigned short* const xs = (LDS unsigned short*)(cur ? xb1 : xb0);
@@ -859,6 +868,11 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
           acc2[r2] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[v], acc1[v], acc2[r2], 0, 0, 0);
       }
     }
+    // this slab's buffer has been read: the slab after the next one goes into it, so two
+    // transfers are in flight through the stack write, the barrier and the mode d-2 share
+    // (past the last slab, a copy of this one that nothing reads keeps the count fixed)
+    wave_fence();
+    dma(g + 2 < cnt ? slab_at(rn2, cn2) : n, cur ? xb1 : xb0);
     // round g of the workgroup (every wave is in the same round) uses stack g % 2
     LDS float* const st = stacks + cur * SF;
 #pragma unroll
@@ -899,6 +913,7 @@ __global__ void __launch_bounds__(NT3) __attribute__((amdgpu_waves_per_eu(4, 8))
     slab(g, Slot<0>{});
     if (g + 1 < cnt) slab(g + 1, Slot<1>{});
   }
+  wait_vm0();   // the trailing copies have landed before the workgroup's LDS is released
   write_unit();
 }
 
@@ -944,11 +959,21 @@ Plan3s plan3s(const ModeProd2& mp) {
   return p;
 }
 
+template <typename XT, int NRB1, int NRB2, int NTW>
+auto proj3_fn(uint32_t nd) {
+  // a slab of at most 16 NRB1 rows of at most 32 values needs at most NRB1 loads
+  return nd <= 1 || NRB1 == 1   ? k_proj3s<XT, NRB1, NRB2, NTW, 1>
+         : nd == 2 || NRB1 == 2 ? k_proj3s<XT, NRB1, NRB2, NTW, (NRB1 >= 2 ? 2 : 1)>
+         : nd == 3 || NRB1 == 3 ? k_proj3s<XT, NRB1, NRB2, NTW, (NRB1 >= 3 ? 3 : 1)>
+                                : k_proj3s<XT, NRB1, NRB2, NTW, (NRB1 >= 4 ? 4 : 1)>;
+}
 template <typename XT, int NRB1, int NRB2>
 hipError_t proj3_ntw(const Plan3s& p, int num_cu, hipStream_t s) {
-  auto fn = p.ntw == 2   ? k_proj3s<XT, NRB1, NRB2, 2>
-            : p.ntw == 3 ? k_proj3s<XT, NRB1, NRB2, 3>
-                         : k_proj3s<XT, NRB1, NRB2, 4>;
+  const uint32_t nd = (p.k.slab_e * 2 / 16 + 63) / 64;
+  if (nd > (uint32_t)NRB1) return hipErrorInvalidValue;
+  auto fn = p.ntw == 2   ? proj3_fn<XT, NRB1, NRB2, 2>(nd)
+            : p.ntw == 3 ? proj3_fn<XT, NRB1, NRB2, 3>(nd)
+                         : proj3_fn<XT, NRB1, NRB2, 4>(nd);
   if (p.lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)fn,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);

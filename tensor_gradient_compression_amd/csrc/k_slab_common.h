@@ -62,6 +62,31 @@ __device__ __forceinline__ void wave_dma(const void* src, uint32_t nchunks, LDS 
                                        (lds_void*)(dst + (size_t)q0 * 16), 16, 0, 0);
 }
 
+// A slab transfer of exactly ND loads a wave, nchunks in (64 (ND - 1), 64 ND], through a
+// buffer resource over the slab: the lane's byte offset is the one vector operand and
+// each group's base a scalar one, so the transfer needs no 64-bit address registers.
+// With nchunks >= 64 every lane is active: the last group of 64 chunks is shifted back
+// to end at the slab's end, so it writes some chunks the group before it wrote, with
+// the same data. A fixed count lets the caller wait for all but the last transfer with
+// one immediate wait count, and lets the compiler see that count too.
+template <int ND>
+__device__ __forceinline__ void wave_dma_n(const void* src, uint32_t nchunks,
+                                          LDS unsigned char* dst, uint32_t lane) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, (int)(nchunks * 16u), 0x00020000);
+  const uint32_t lo = lane * 16u;
+  if (ND > 1 || nchunks == 64) {
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      const uint32_t b = i + 1 < ND ? 64u * i : nchunks - 64;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + b * 16u), 16, lo,
+                                               (int)(b * 16u), 0, 0);
+    }
+  } else if (lane < nchunks) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, lo, 0, 0, 0);
+  }
+}
+
 // Omega rank of element e from its bitmask word and word rank; kS past the end
 __device__ __forceinline__ uint64_t rank_at(uint64_t word, uint32_t wr, uint64_t e, uint64_t N,
                                             uint64_t kS) {
