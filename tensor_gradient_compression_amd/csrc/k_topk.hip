@@ -23,6 +23,9 @@
 //      equal the prefix found so far, and adds it to a global histogram; a one-block
 //      kernel walks the bins from the top and fixes the next digit. After the last
 //      digit: tau = the k-th largest key, need = how many keys equal to tau are taken.
+//      16-bit magnitude keys (15 bits) take one pass instead of two: one workgroup per
+//      CU holds the histogram of the whole key (32768 bins, 128 KB of LDS) and adds its
+//      nonzero bins to the global one.
 //   2. count pass: each wave counts (key > tau, key == tau) over a unit of 1024
 //      consecutive elements.
 //   3. scan: one block turns unit counts into each unit's output offset and its
@@ -42,6 +45,9 @@ namespace {
 
 constexpr int DIGIT = 11;
 constexpr int NBINS = 1 << DIGIT;
+constexpr int NB15 = 1 << 15;                // whole 16-bit magnitude keys
+constexpr int NT15 = 1024;                   // threads of the one-pass histogram
+static_assert(NB15 <= TOPK_HIST_BINS, "the global histogram holds every 15-bit key");
 constexpr int UNIT_ITERS = 2;                // 2 x 64 lanes x 8 = 1024 elements per wave unit
 constexpr uint64_t UNIT = 512ull * UNIT_ITERS;
 
@@ -141,7 +147,7 @@ __device__ __forceinline__ void load_group(const void* G, uint64_t N, uint64_t e
 }
 
 __global__ void k_topk_init(uint64_t* state, uint32_t* hist, uint32_t k) {
-  for (int i = threadIdx.x; i < NBINS; i += blockDim.x) hist[i] = 0;
+  for (int i = threadIdx.x; i < TOPK_HIST_BINS; i += blockDim.x) hist[i] = 0;
   if (threadIdx.x == 0) {
     state[0] = 0;
     state[1] = k;
@@ -181,43 +187,100 @@ __global__ void __launch_bounds__(256) k_topk_hist(const void* __restrict__ G, u
     if (h[i]) atomicAdd(&ghist[i], h[i]);
 }
 
-// Fix the next digit and clear the histogram for the next pass. The digit is the
-// highest bin b whose count, added to the counts of all higher bins, reaches the number
-// of keys still to take (bin 0 if none does); 256 threads own 8 consecutive bins each
-// and a suffix scan over the threads locates that bin.
-__global__ void __launch_bounds__(256) k_topk_select(uint32_t* hist, int shift, int width,
-                                                     uint64_t* state) {
-  __shared__ uint64_t suf[257];
-  __shared__ int found_b;
-  __shared__ uint64_t found_cum;
-  const int t = threadIdx.x;
-  const int nb = 1 << width;
-  constexpr int PER = NBINS / 256;
-  const int b0 = t * PER;
-  uint32_t c[PER];
-  uint64_t mine = 0;
+// The whole 15-bit key of every element in one pass (K = KeyH16): the LDS histogram of
+// a workgroup per CU, whose nonzero bins are added to the global one. Two groups of 8
+// elements per iteration, both loaded before the first LDS atomic (four measured
+// slower).
+template <class K>
+__global__ void __launch_bounds__(NT15) k_topk_hist15(const void* __restrict__ G, uint64_t N,
+                                                      uint32_t* __restrict__ ghist) {
+  extern __shared__ uint32_t h15[];
+  for (int i = threadIdx.x; i < NB15; i += NT15) h15[i] = 0;
+  __syncthreads();
+  const uint64_t stride = (uint64_t)gridDim.x * NT15;
+  const uint64_t ngroups = (N + 7) / 8;
+  uint64_t gi = (uint64_t)blockIdx.x * NT15 + threadIdx.x;
+  auto add = [&](uint64_t g, const typename K::Raw* x) {
+    if (g * 8 + 8 <= N) {
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    c[i] = b0 + i < nb ? hist[b0 + i] : 0u;
-    mine += c[i];
+      for (int j = 0; j < 8; ++j) atomicAdd(&h15[K::key_of(x[j])], 1u);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (g * 8 + j < N) atomicAdd(&h15[K::key_of(x[j])], 1u);
+    }
+  };
+  for (; gi + stride < ngroups; gi += 2 * stride) {
+    typename K::Raw x[8], y[8];
+    load_group<K>(G, N, gi * 8, x);
+    load_group<K>(G, N, (gi + stride) * 8, y);
+    add(gi, x);
+    add(gi + stride, y);
   }
-  suf[t] = mine;
-  if (t == 0) {
-    suf[256] = 0;
-    found_b = -1;
+  if (gi < ngroups) {
+    typename K::Raw x[8];
+    load_group<K>(G, N, gi * 8, x);
+    add(gi, x);
   }
   __syncthreads();
-  // inclusive suffix sums: suf[t] = sum over threads >= t
-  for (int off = 1; off < 256; off <<= 1) {
-    const uint64_t y = t + off < 256 ? suf[t + off] : 0;
-    __syncthreads();
-    suf[t] += y;
-    __syncthreads();
+  for (int i = threadIdx.x; i < NB15; i += NT15)
+    if (h15[i]) atomicAdd(&ghist[i], h15[i]);
+}
+
+// Fix the next digit and (CLEAR) clear the histogram for the next pass. The digit is
+// the highest bin b whose count, added to the counts of all higher bins, reaches the
+// number of keys still to take (bin 0 if none does); NT threads own NB / NT consecutive
+// bins each and a suffix scan over the threads (shuffles within a wave, then over the
+// waves' totals) locates that bin. Counts fit 32 bits: N < 2^32.
+template <int NT, int NB, bool CLEAR>
+__global__ void __launch_bounds__(NT) k_topk_select(uint32_t* hist, int shift, int width,
+                                                    uint64_t* state) {
+  constexpr int NW = NT / 64;
+  __shared__ uint32_t wsum[NW + 1];
+  __shared__ int found_b;
+  __shared__ uint32_t found_cum;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int nb = 1 << width;
+  constexpr int PER = NB / NT;
+  const int b0 = t * PER;
+  static_assert(PER % 4 == 0, "bins are read four at a time");
+  uint32_t c[PER];
+  uint32_t mine = 0;
+  if (b0 + PER <= nb) {
+#pragma unroll
+    for (int i = 0; i < PER; i += 4) {
+      const uint4 v = *(const uint4*)(hist + b0 + i);   // 16-byte aligned: PER % 4 == 0
+      c[i] = v.x; c[i + 1] = v.y; c[i + 2] = v.z; c[i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) c[i] = b0 + i < nb ? hist[b0 + i] : 0u;
   }
-  const uint64_t rem = state[1];
-  const uint64_t above = suf[t + 1];        // bins owned by higher threads
+#pragma unroll
+  for (int i = 0; i < PER; ++i) mine += c[i];
+  // x: the sum over the lanes >= lane of this wave
+  uint32_t x = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_down(x, off, 64);
+    if (lane + off < 64) x += y;
+  }
+  if (lane == 0) wsum[w] = x;
+  if (t == 0) found_b = -1;
+  __syncthreads();
+  if (t == 0) {
+    uint32_t acc = 0;
+    wsum[NW] = 0;
+    for (int v = NW - 1; v >= 0; --v) {
+      acc += wsum[v];
+      wsum[v] = acc;            // the sum over waves >= v
+    }
+  }
+  __syncthreads();
+  const uint32_t rem = (uint32_t)state[1];
+  const uint32_t above = x - mine + wsum[w + 1];   // bins owned by higher threads
   if (above < rem && above + mine >= rem) {
-    uint64_t cum = above;
+    uint32_t cum = above;
     for (int i = PER - 1; i >= 0; --i) {
       const int b = b0 + i;
       if (b == 0 || cum + c[i] >= rem) {
@@ -231,16 +294,32 @@ __global__ void __launch_bounds__(256) k_topk_select(uint32_t* hist, int shift, 
   __syncthreads();
   if (t == 0) {
     int b = found_b;
-    uint64_t cum = found_cum;
+    uint32_t cum = found_cum;
     if (b < 0) {             // never reached: bin 0, with every higher bin counted
       b = 0;
-      cum = suf[0] - (nb > 0 ? (uint64_t)hist[0] : 0);
+      cum = wsum[0] - (nb > 0 ? hist[0] : 0u);
     }
     state[0] |= ((uint64_t)b) << shift;
     state[1] = rem - cum;
   }
-  __syncthreads();
-  for (int i = t; i < NBINS; i += blockDim.x) hist[i] = 0;
+  if constexpr (CLEAR) {
+    __syncthreads();
+    for (int i = t; i < NB; i += NT) hist[i] = 0;
+  }
+}
+
+int cu_count() {
+  static int n = 0;
+  if (!n) {
+    int dev = 0, c = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        c > 0)
+      n = c;
+    else
+      return 256;
+  }
+  return n;
 }
 
 template <class K, bool RK>
@@ -493,7 +572,24 @@ hipError_t run_topk(const void* G, uint64_t N, uint32_t k, const TopkWs& ws, uin
   uint64_t hb = (N + 256ull * 16 - 1) / (256ull * 16);
   if (hb > 1024) hb = 1024;
   if (hb < 1) hb = 1;
-  for (int pass = 0;; ++pass) {
+  if constexpr (!RK && K::BITS == 15) {
+    // the whole key in one pass
+    err = hipFuncSetAttribute((const void*)k_topk_hist15<K>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, NB15 * 4);
+    if (err != hipSuccess) return err;
+    uint64_t g15 = ((N + 7) / 8 + NT15 - 1) / NT15;
+    if (g15 > (uint64_t)cu_count()) g15 = (uint64_t)cu_count();
+    if (g15 < 1) g15 = 1;
+    M(KID_TOPK_HIST, true);
+    k_topk_hist15<K><<<(unsigned)g15, NT15, NB15 * 4, s>>>(G, N, ws.hist);
+    M(KID_TOPK_HIST, false);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    M(KID_TOPK_SELECT, true);
+    k_topk_select<1024, NB15, false><<<1, 1024, 0, s>>>(ws.hist, 0, 15, ws.state);
+    M(KID_TOPK_SELECT, false);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  for (int pass = 0; RK || K::BITS != 15; ++pass) {
     constexpr int BITS = RK ? 31 : K::BITS;
     int top = BITS - DIGIT * pass;            // bits above this digit already fixed
     if (top <= 0) break;
@@ -505,7 +601,7 @@ hipError_t run_topk(const void* G, uint64_t N, uint32_t k, const TopkWs& ws, uin
     M(KID_TOPK_HIST, false);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     M(KID_TOPK_SELECT, true);
-    k_topk_select<<<1, 256, 0, s>>>(ws.hist, shift, width, ws.state);
+    k_topk_select<256, NBINS, true><<<1, 256, 0, s>>>(ws.hist, shift, width, ws.state);
     M(KID_TOPK_SELECT, false);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }

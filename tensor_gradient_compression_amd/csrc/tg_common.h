@@ -68,8 +68,9 @@ enum KernelId {
 // ---------------------------------------------------------------- launchers
 // Every launcher enqueues on `s` and returns hipGetLastError().
 
+constexpr int TOPK_HIST_BINS = 32768;
 struct TopkWs {
-  uint32_t* hist;       // 2048 bins
+  uint32_t* hist;       // TOPK_HIST_BINS bins
   uint64_t* state;      // TopkState (4 x u64)
   uint32_t* ucount;     // 2 per unit
   uint32_t* uoff;       // 2 per unit

@@ -511,13 +511,14 @@ int select_omega(tgrad_t* h, const TopkWs& tw, const void* src, int dt, void* re
   HIPCHK(h, launch_topk(dt, src, h->N, (uint32_t)h->k, tw, h->omega, h->mask, h->rank, resid,
                         h->selection == TGRAD_SELECT_RANDK, rk_base, s, mark_cb, h));
   {
-    // the radix passes read the keys' source (magnitudes: 11 bits a pass), the count pass
+    // the radix passes read the keys' source (magnitudes: 11 bits a pass, 16-bit
+    // magnitudes all 15 bits in one pass), the count pass
     // once more, the compaction once more (rand-k keys need no read, except for the
     // residual); the compaction writes Omega, its bitmask and word ranks, and the residual
     const bool rk = h->selection == TGRAD_SELECT_RANDK;
     const uint64_t es = dt == DT_C64 ? 8 : (dt == DT_F32 ? 4 : 2);
     const int bits = rk ? 31 : (dt == DT_C64 ? 63 : (dt == DT_F32 ? 31 : 15));
-    const uint64_t passes = (uint64_t)((bits + 10) / 11);
+    const uint64_t passes = bits == 15 ? 1 : (uint64_t)((bits + 10) / 11);
     const uint64_t src_b = rk ? 0 : h->N * es;
     record(h, KID_TOPK_HIST, 0, passes * src_b, 0, 0);
     record(h, KID_TOPK_COUNT, 0, src_b, 0, 0);
@@ -901,7 +902,7 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
   ok = ok && dalloc(h, &h->gram, gmax * h->fmodes.size(), false);
   ok = ok && dalloc(h, &h->eig_status, TGRAD_MAX_NDIM, false);
   const uint64_t units = topk_units(N);
-  ok = ok && dalloc(h, &h->tw.hist, 2048, false);
+  ok = ok && dalloc(h, &h->tw.hist, TOPK_HIST_BINS, false);
   ok = ok && dalloc(h, &h->tw.state, 4, false);
   ok = ok && dalloc(h, &h->tw.ucount, 2 * units, false);
   ok = ok && dalloc(h, &h->tw.uoff, 2 * units, false);
@@ -929,6 +930,8 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
     zero(h->Mp[n], I * r * P * P * 4);
     zero(h->Mr[n], I * r * P * P * 4);
     zero(h->eig[n], I * 8);
+    zero(h->Mps[n], 2 * I * r * 4);
+    zero(h->Mrs[n], 2 * I * r * 4);
   }
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
@@ -1826,7 +1829,7 @@ bool noalloc_ws(tgrad_t* h, unsigned char* base, RefreshWs* ws) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const uint64_t units = topk_units(h->N), chunks = topk_chunks(h->N);
   size_t off = 0;
-  const size_t o_hist = off;   off += up(2048 * 4);
+  const size_t o_hist = off;   off += up(TOPK_HIST_BINS * 4);
   const size_t o_state = off;  off += up(4 * 8);
   const size_t o_ucount = off; off += up(2 * units * 4);
   const size_t o_uoff = off;   off += up(2 * units * 4);
