@@ -1,6 +1,6 @@
 // One fp32 mode product streamed by independent waves: the leading compressed modes of
-// the reconstruction (and any other real fp32 -> fp32 mode product with I <= 32,
-// R <= 64 and a long trailing part).
+// the reconstruction and the projection (any fp32 -> fp32 mode product with I <= 64,
+// R <= 64 and a long trailing part, real or complex).
 //
 // Same product as k_modeprod.hip (pith.science "What carries the argument": projection
 // to the core and reconstruction by mode-wise products; appendix M Theorem 2), on the
@@ -29,6 +29,11 @@
 //    issues the same memory instructions and the wait counts are exact.
 //  * M's A operands come from a per-lane LDS table (one conflict-free read per MFMA),
 //    filled once per workgroup.
+// Complex data (CPLX) is taken as the real tensor (A, I, 2B) of its interleaved
+// (re, im) values, multiplied by Re M and by Im M (two tables, two accumulator sets):
+// a lane's four columns are two complex values, and M X = (Re M) X + i (Im M) X is
+// formed in registers before the store: re = (Re M x)_re - (Im M x)_im, im =
+// (Re M x)_im + (Im M x)_re.
 #include "tg_common.h"
 
 namespace tg {
@@ -44,42 +49,48 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #define LDS __attribute__((address_space(3)))
 
 struct SPK {
-  const float* X;    // (A, I, B)
+  const float* X;    // (A, I, B) (complex: B counts the real values, twice the complex)
   float* Y;          // (A, R, B)
-  const float* M;    // R x I row-major
+  const float* M;    // R x I row-major (complex: Re M)
+  const float* Mi;   // complex: Im M, R x I
   uint64_t ntiles;   // A * tpa
   uint32_t A, I, B, R;
   uint32_t tpa;      // tiles per a
 };
 
-// NRB: 16-row blocks of R (<= 4); NKS: k-steps of 4 (I <= 4 NKS).
-template <int NRB, int NKS>
+// NRB: 16-row blocks of R (<= 4); NKS: k-steps of 4 (I <= 4 NKS); CPLX: complex data.
+template <int NRB, int NKS, bool CPLX>
 __global__ void __launch_bounds__(SP_NT) k_streamprod(SPK k) {
   extern __shared__ float smem[];
-  // at[(rb NKS + ks) 64 + lane] = M[16 rb + lane % 16][4 ks + lane / 16] (zero outside)
+  // at[(rb NKS + ks) 64 + lane] = M[16 rb + lane % 16][4 ks + lane / 16] (zero outside);
+  // complex: the Im M table follows
+  constexpr uint32_t NTAB = NRB * NKS * 64;
   LDS float* const at = (LDS float*)smem;
+  LDS float* const ati = at + NTAB;
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t li = lane & 15, lg = lane >> 4;
   const uint32_t I = k.I, B = k.B, R = k.R;
 
   {
-    constexpr uint32_t NTAB = NRB * NKS * 64;
-    constexpr int IT = (int)((NTAB + SP_NT - 1) / SP_NT);
+    constexpr uint32_t NT2 = CPLX ? 2 * NTAB : NTAB;
+    constexpr int IT = (int)((NT2 + SP_NT - 1) / SP_NT);
     float tv[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const uint32_t q = threadIdx.x + it * SP_NT;
+      const uint32_t q2 = threadIdx.x + it * SP_NT;
+      const bool im = CPLX && q2 >= NTAB;
+      const uint32_t q = im ? q2 - NTAB : q2;
       const uint32_t rk = q >> 6, rb = rk / NKS, ks = rk - rb * NKS;
       const uint32_t row = 16 * rb + (q & 15), kk = 4 * ks + ((q & 63) >> 4);
-      const bool ok = q < NTAB && row < R && kk < I;
-      const float v = k.M[ok ? row * I + kk : 0];
+      const bool ok = q2 < NT2 && row < R && kk < I;
+      const float v = (im ? k.Mi : k.M)[ok ? row * I + kk : 0];
       tv[it] = ok ? v : 0.0f;
     }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const uint32_t q = threadIdx.x + it * SP_NT;
-      if (q < NTAB) at[q] = tv[it];
+      if (q < NT2) at[q] = tv[it];   // the Im table follows the Re one
     }
   }
   __syncthreads();
@@ -108,10 +119,12 @@ __global__ void __launch_bounds__(SP_NT) k_streamprod(SPK k) {
     for (int ks = 0; ks < NKS; ++ks)
       b[ks] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(off + 16 * ks * B), 0, 0);
   };
-  // acc[j][rb]: rows 16 rb + 4 lg + v, column b0 + 4 li + j
-  auto multiply = [&](const u32x4 (&b)[NKS], f4 (&acc)[4][NRB]) {
+  // acc[j][rb]: rows 16 rb + 4 lg + v, column b0 + 4 li + j (complex: acc[j + 4][rb]
+  // the same with Im M)
+  constexpr int NJ = CPLX ? 8 : 4;
+  auto multiply = [&](const u32x4 (&b)[NKS], f4 (&acc)[NJ][NRB]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) acc[j][rb] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -125,9 +138,19 @@ __global__ void __launch_bounds__(SP_NT) k_streamprod(SPK k) {
         for (int rb = 0; rb < NRB; ++rb)
           acc[j][rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rb], __uint_as_float(b[ks][j]),
                                                            acc[j][rb], 0, 0, 0);
+      if constexpr (CPLX) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) a[rb] = ati[(rb * NKS + ks) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb)
+            acc[j + 4][rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                a[rb], __uint_as_float(b[ks][j]), acc[j + 4][rb], 0, 0, 0);
+      }
     }
   };
-  auto store = [&](uint64_t t, bool valid, const f4 (&acc)[4][NRB]) {
+  auto store = [&](uint64_t t, bool valid, const f4 (&acc)[NJ][NRB]) {
     uint32_t a, b0;
     place(t, valid, a, b0);
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
@@ -138,8 +161,19 @@ __global__ void __launch_bounds__(SP_NT) k_streamprod(SPK k) {
     for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const u32x4 val = {__float_as_uint(acc[0][rb][v]), __float_as_uint(acc[1][rb][v]),
-                           __float_as_uint(acc[2][rb][v]), __float_as_uint(acc[3][rb][v])};
+        float o[4];
+        if constexpr (CPLX) {
+          // columns 4 li, 4 li + 1 and 4 li + 2, 4 li + 3 are two complex values
+          o[0] = acc[0][rb][v] - acc[5][rb][v];
+          o[1] = acc[1][rb][v] + acc[4][rb][v];
+          o[2] = acc[2][rb][v] - acc[7][rb][v];
+          o[3] = acc[3][rb][v] + acc[6][rb][v];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = acc[j][rb][v];
+        }
+        const u32x4 val = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                           __float_as_uint(o[3])};
         __builtin_amdgcn_raw_buffer_store_b128(val, ry, (int)(off + (16 * rb + v) * B * 4), 0, 0);
       }
   };
@@ -149,7 +183,7 @@ __global__ void __launch_bounds__(SP_NT) k_streamprod(SPK k) {
   // has the same memory operations behind it (the loads of the next tile and the
   // stores of the previous one), whichever way the loop was entered. A scheduling
   // barrier keeps the compiler from sinking the loads down to their use.
-  f4 acc[4][NRB];
+  f4 acc[NJ][NRB];
   u32x4 bA[NKS], bB[NKS];
   load(t0, true, bA);
   load(t0 + TW, t0 + TW < k.ntiles, bB);
@@ -173,6 +207,7 @@ __global__ void __launch_bounds__(SP_NT) k_streamprod(SPK k) {
 
 struct PlanS {
   SPK k;
+  bool cplx;
   int nrb, nks;
   int max_wg;
   size_t lds;
@@ -182,34 +217,43 @@ struct PlanS {
 PlanS plan_s(const ModeProd& mp) {
   PlanS p{};
   p.ok = false;
-  if (mp.P != 1 || mp.in_dt != DT_F32 || mp.apply || !mp.Y) return p;
-  if (mp.A == 0 || mp.I == 0 || mp.I > 32 || mp.R == 0 || mp.R > 64 || mp.B < SP_TC) return p;
+  if (mp.in_dt != DT_F32 || mp.apply || !mp.Y) return p;
+  const bool cplx = mp.P == 2;
+  if (mp.P != 1 && !(cplx && mp.Mre && mp.Mim)) return p;
+  // complex: the real view's rows hold 2 B values
+  const uint64_t B = cplx ? 2ull * mp.B : (uint64_t)mp.B;
+  // complex rows of 16 values (32 real) take half a tile: still far ahead of the tiled
+  // kernel's complex form
+  if (mp.A == 0 || mp.I == 0 || mp.I > 64 || mp.R == 0 || mp.R > 64 || B < (cplx ? 32 : SP_TC))
+    return p;
   // 16-byte pieces: rows of whole pieces, 16-byte aligned tensors; 32-bit byte offsets
   // within one a (buffer extents below 2^31)
-  if (mp.B % 4 != 0 || (uintptr_t)mp.X % 16 != 0 || (uintptr_t)mp.Y % 16 != 0) return p;
-  if ((uint64_t)mp.B * 64 * 4 >= 0x7FFFFFFFull) return p;
+  if (B % 4 != 0 || (uintptr_t)mp.X % 16 != 0 || (uintptr_t)mp.Y % 16 != 0) return p;
+  if (B * 64 * 4 >= 0x7FFFFFFFull) return p;
+  p.cplx = cplx;
   p.nrb = (int)((mp.R + 15) / 16);
   const int ks = (int)((mp.I + 3) / 4);
-  p.nks = ks <= 4 ? 4 : ks <= 6 ? 6 : 8;
+  p.nks = ks <= 4 ? 4 : ks <= 6 ? 6 : ks <= 8 ? 8 : ks <= 12 ? 12 : 16;
   SPK& k = p.k;
   k.X = (const float*)mp.X;
   k.Y = mp.Y;
-  k.M = mp.M;
+  k.M = cplx ? mp.Mre : mp.M;
+  k.Mi = cplx ? mp.Mim : nullptr;
   k.A = mp.A;
   k.I = mp.I;
-  k.B = mp.B;
+  k.B = (uint32_t)B;
   k.R = mp.R;
-  k.tpa = (mp.B + SP_TC - 1) / SP_TC;
+  k.tpa = (k.B + SP_TC - 1) / SP_TC;
   k.ntiles = (uint64_t)mp.A * k.tpa;
-  p.lds = (size_t)p.nrb * p.nks * 64 * 4;
+  p.lds = (size_t)p.nrb * p.nks * 64 * 4 * (cplx ? 2 : 1);
   p.max_wg = mp.max_wg;
   p.ok = true;
   return p;
 }
 
-template <int NRB, int NKS>
+template <int NRB, int NKS, bool CPLX>
 hipError_t sp_launch(const PlanS& p, int num_cu, hipStream_t s) {
-  auto fn = k_streamprod<NRB, NKS>;
+  auto fn = k_streamprod<NRB, NKS, CPLX>;
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, SP_NT, p.lds);
   if (e != hipSuccess) return e;
@@ -223,10 +267,21 @@ hipError_t sp_launch(const PlanS& p, int num_cu, hipStream_t s) {
 }
 template <int NRB>
 hipError_t sp_nks(const PlanS& p, int num_cu, hipStream_t s) {
+  if (p.cplx) {
+    switch (p.nks) {
+      case 4: return sp_launch<NRB, 4, true>(p, num_cu, s);
+      case 6: return sp_launch<NRB, 6, true>(p, num_cu, s);
+      case 8: return sp_launch<NRB, 8, true>(p, num_cu, s);
+      case 12: return sp_launch<NRB, 12, true>(p, num_cu, s);
+      default: return sp_launch<NRB, 16, true>(p, num_cu, s);
+    }
+  }
   switch (p.nks) {
-    case 4: return sp_launch<NRB, 4>(p, num_cu, s);
-    case 6: return sp_launch<NRB, 6>(p, num_cu, s);
-    default: return sp_launch<NRB, 8>(p, num_cu, s);
+    case 4: return sp_launch<NRB, 4, false>(p, num_cu, s);
+    case 6: return sp_launch<NRB, 6, false>(p, num_cu, s);
+    case 8: return sp_launch<NRB, 8, false>(p, num_cu, s);
+    case 12: return sp_launch<NRB, 12, false>(p, num_cu, s);
+    default: return sp_launch<NRB, 16, false>(p, num_cu, s);
   }
 }
 

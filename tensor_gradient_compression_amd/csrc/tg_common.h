@@ -147,15 +147,19 @@ struct ModeProd {
   int has_sparse;
   int force_ncb;           // 0: choose the tile width automatically
   int max_wg;              // streaming kernel: at most this many workgroups (0: no cap)
+  // complex (P == 2), streaming kernel only: Re M and Im M as R x I fp32 matrices (the
+  // streaming kernel applies to a complex product only when both are given)
+  const float* Mre;
+  const float* Mim;
   // apply only, a test capture: when not NULL the fp32 update (acc + uS@Omega) is also
   // stored here, one float per output value (a separate kernel instantiation)
   float* delta;
 };
 size_t modeprod_lds_bytes(const ModeProd& mp);
 hipError_t launch_modeprod(const ModeProd& mp, int num_cu, hipStream_t s);
-// The same product streamed by independent waves (k_streamprod.hip): real fp32 input and
-// output (store epilogue), I <= 32, R <= 64, B >= 64 and a multiple of 4, X and Y
-// 16-byte aligned.
+// The same product streamed by independent waves (k_streamprod.hip): fp32 input and
+// output (store epilogue), I <= 64, R <= 64, B >= 64 (complex, with Mre and Mim:
+// 2 B >= 32) and B (complex: 2 B) a multiple of 4, X and Y 16-byte aligned.
 bool streamprod_supported(const ModeProd& mp);
 hipError_t launch_streamprod(const ModeProd& mp, int num_cu, hipStream_t s);
 

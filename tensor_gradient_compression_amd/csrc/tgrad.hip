@@ -90,12 +90,13 @@ struct tgrad_handle {
   float* U[TGRAD_MAX_NDIM] = {nullptr};
   float* Mp[TGRAD_MAX_NDIM] = {nullptr};
   float* Mr[TGRAD_MAX_NDIM] = {nullptr};
-  // complex modes wider than 64 (their real-block operands exceed the tiled product's
-  // 128 rows or columns): each product runs as two real products on the interleaved
-  // (re, im) view, one with Re M and one with Im M, and a combine pass. Mps: Re, Im of
-  // the projection operand (r x I each); Mrs: of the reconstruction operand (I x r
-  // each); ctmp: the Im M product's output (N P floats), then, when the reconstruction's
-  // last launch is such a mode, its full update before the dense apply (N P floats)
+  // complex modes: Mps holds Re, Im of the projection operand (r x I each), Mrs those of
+  // the reconstruction operand (I x r each), for the streaming kernel's complex form.
+  // Modes wider than 64 (csplit: their real-block operands exceed the tiled product's
+  // 128 rows or columns) run each product as two real products on the interleaved
+  // (re, im) view, one with Re M and one with Im M, and a combine pass; ctmp: the Im M
+  // product's output (N P floats), then, when the reconstruction's last launch is such a
+  // mode, its full update before the dense apply (N P floats)
   bool csplit[TGRAD_MAX_NDIM] = {false};
   float* Mps[TGRAD_MAX_NDIM] = {nullptr};
   float* Mrs[TGRAD_MAX_NDIM] = {nullptr};
@@ -636,7 +637,7 @@ int do_refresh(tgrad_t* h, const void* grad, hipStream_t s, const RefreshWs& ws)
     record(h, KID_EIG, 0, 0, 0, 0);
   }
   for (int n : h->fmodes)
-    if (h->csplit[n]) {
+    if (h->Mps[n]) {
       Mark m(h, KID_CSPLIT_OPERAND);
       HIPCHK(h, split_operands(h, n, s));
       const uint64_t ri = (uint64_t)h->shape[n] * h->ranks[n];
@@ -855,11 +856,15 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
     ok = ok && dalloc(h, &h->Mp[n], I * r * P * P, false);
     ok = ok && dalloc(h, &h->Mr[n], I * r * P * P, false);
     ok = ok && dalloc(h, &h->eig[n], I, false);
-    if (P == 2 && I > 64) {
-      h->csplit[n] = true;
+    if (P == 2) {
+      // Re and Im parts of the operands (the streaming kernel's complex form, and the
+      // split products of modes wider than 64)
       ok = ok && dalloc(h, &h->Mps[n], 2 * I * r, false);
       ok = ok && dalloc(h, &h->Mrs[n], 2 * I * r, false);
-      if (!h->ctmp) ok = ok && dalloc(h, &h->ctmp, 2 * N * P, false);
+      if (I > 64) {
+        h->csplit[n] = true;
+        if (!h->ctmp) ok = ok && dalloc(h, &h->ctmp, 2 * N * P, false);
+      }
     }
     GramArgs g{};
     view(shape, ndim, n, &g.A, &g.I, &g.B);
@@ -1108,6 +1113,10 @@ int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s) {
       mp.P = P;
       mp.apply = 0;
       mp.Y = Y;
+      if (h->Mps[n] && !h->csplit[n]) {
+        mp.Mre = h->Mps[n];
+        mp.Mim = h->Mps[n] + (size_t)mp.R * mp.I;
+      }
       if (h->csplit[n]) {
         const int rc = split_product(h, mp, h->Mps[n], n,
                                      j == 0 ? KID_PROJECT_FIRST : KID_PROJECT,
@@ -1261,6 +1270,10 @@ int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, fl
       mp.decay = decay;
       mp.has_sparse = app && h->k > 0;
       mp.delta = app ? h->delta_cap : nullptr;
+      if (h->Mrs[n] && !h->csplit[n]) {
+        mp.Mre = h->Mrs[n];
+        mp.Mim = h->Mrs[n] + (size_t)mp.R * mp.I;
+      }
       if (h->csplit[n]) {
         // with apply: the full update goes to ctmp's second half, then the dense apply
         float* dst = app ? h->ctmp + h->N * P : Y;
@@ -1502,7 +1515,7 @@ int tgrad_set_factor(tgrad_t* h, int mode, const float* U, int64_t n_floats) {
   HIPCHK(h, hipMemcpy(h->U[mode], U, n * 4, hipMemcpyHostToDevice));
   HIPCHK(h, hipMemcpy(h->Mp[mode], mp.data(), mp.size() * 4, hipMemcpyHostToDevice));
   HIPCHK(h, hipMemcpy(h->Mr[mode], mr.data(), mr.size() * 4, hipMemcpyHostToDevice));
-  if (h->csplit[mode]) {
+  if (h->Mps[mode]) {
     HIPCHK(h, split_operands(h, mode, nullptr));
     HIPCHK(h, hipDeviceSynchronize());
   }
@@ -1646,7 +1659,7 @@ int tgrad_load_state(tgrad_t* h, const void* buf, int64_t size) {
     host_operands(I, r, h->P, U.data(), mp.data(), mr.data());
     HIPCHK(h, hipMemcpy(h->Mp[n], mp.data(), mp.size() * 4, hipMemcpyHostToDevice));
     HIPCHK(h, hipMemcpy(h->Mr[n], mr.data(), mr.size() * 4, hipMemcpyHostToDevice));
-    if (h->csplit[n]) HIPCHK(h, split_operands(h, n, nullptr));
+    if (h->Mps[n]) HIPCHK(h, split_operands(h, n, nullptr));
   }
   HIPCHK(h, hipDeviceSynchronize());
   h->t = theirs.t;
