@@ -222,10 +222,8 @@ PlanS plan_s(const ModeProd& mp) {
   if (mp.P != 1 && !(cplx && mp.Mre && mp.Mim)) return p;
   // complex: the real view's rows hold 2 B values
   const uint64_t B = cplx ? 2ull * mp.B : (uint64_t)mp.B;
-  // complex rows of 16 values (32 real) take half a tile: still far ahead of the tiled
-  // kernel's complex form
-  if (mp.A == 0 || mp.I == 0 || mp.I > 64 || mp.R == 0 || mp.R > 64 || B < (cplx ? 32 : SP_TC))
-    return p;
+  // rows of 32 values take half a tile: still ahead of the tiled kernel
+  if (mp.A == 0 || mp.I == 0 || mp.I > 64 || mp.R == 0 || mp.R > 64 || B < SP_TC / 2) return p;
   // 16-byte pieces: rows of whole pieces, 16-byte aligned tensors; 32-bit byte offsets
   // within one a (buffer extents below 2^31)
   if (B % 4 != 0 || (uintptr_t)mp.X % 16 != 0 || (uintptr_t)mp.Y % 16 != 0) return p;

@@ -158,8 +158,8 @@ struct ModeProd {
 size_t modeprod_lds_bytes(const ModeProd& mp);
 hipError_t launch_modeprod(const ModeProd& mp, int num_cu, hipStream_t s);
 // The same product streamed by independent waves (k_streamprod.hip): fp32 input and
-// output (store epilogue), I <= 64, R <= 64, B >= 64 (complex, with Mre and Mim:
-// 2 B >= 32) and B (complex: 2 B) a multiple of 4, X and Y 16-byte aligned.
+// output (store epilogue), I <= 64, R <= 64 (complex with Mre and Mim), B (complex:
+// 2 B) >= 32 and a multiple of 4, X and Y 16-byte aligned.
 bool streamprod_supported(const ModeProd& mp);
 hipError_t launch_streamprod(const ModeProd& mp, int num_cu, hipStream_t s);
 
