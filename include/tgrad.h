@@ -233,12 +233,16 @@ int tgrad_set_pair_fusion(tgrad_t *h, int enable);
  * every wave owns all output rows of 64 consecutive trailing columns and loads the next
  * such tile while it multiplies the current one, without LDS staging or workgroup
  * barriers (pith.science "What carries the argument": projection and reconstruction are
- * chains of mode-wise products). It applies when the mode has at most 32 values on the
- * input side and 64 on the output side and the trailing part is at least 64 values and a
- * multiple of 4. enable = 1 selects it (the default), 0 the tiled kernel for every
- * single mode product; enable = n >= 2 selects it with at most n - 1 workgroups of 4
- * waves (so that small tensors exercise a wave's walk over several tiles). Negative enable:
- * TGRAD_EINVAL. Results agree to fp32 rounding; takes effect at the next step. */
+ * chains of mode-wise products). It applies when the mode has at most 64 values on
+ * either side (complex data: Re and Im of the factor in two accumulator sets) and the
+ * trailing part is at least 32 values (complex: 16) and a multiple of 4 (complex: 2).
+ * Products over the last mode (no trailing part: the one-mode plan's first projection
+ * and its weight-updating last reconstruction) run on a kernel that streams rows of the
+ * tensor with the factor in registers, where the factor fits. enable = 1 selects both
+ * (the default), 0 the tiled kernel for every single mode product; enable = n >= 2
+ * selects them with at most n - 1 workgroups of 4 waves for the first (so that small
+ * tensors exercise a wave's walk over several tiles). Negative enable: TGRAD_EINVAL.
+ * Results agree to fp32 rounding; takes effect at the next step. */
 int tgrad_set_stream_products(tgrad_t *h, int enable);
 
 /* ---------------------------------------------------------------- variants.
@@ -349,7 +353,7 @@ int tgrad_last_launches(const tgrad_t *h, tgrad_launch *out, int cap);
  * the launch stream (at most max_records launches are kept). tgrad_timing_read
  * synchronises, then returns per-kernel-id totals: launches[id] and ms[id] for
  * id < n_ids (n_ids <= TGRAD_MAX_KERNEL_IDS) and resets the records. */
-#define TGRAD_MAX_KERNEL_IDS 32
+#define TGRAD_MAX_KERNEL_IDS 48
 int tgrad_timing_enable(tgrad_t *h, int enable, int max_records);
 int tgrad_timing_read(tgrad_t *h, int64_t *launches, double *ms, int n_ids);
 /* Restricts the timing above to the launches of kernel id (0 <= id <

@@ -20,7 +20,7 @@ F32, F16, BF16, C64 = 0, 1, 2, 3
 DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "c64": C64}
 OK, EINVAL, ENOMEM, EHIP, ESTATE = 0, 1, 2, 3, 4
 MAX_NDIM = 8
-MAX_KERNEL_IDS = 32
+MAX_KERNEL_IDS = 48
 
 _lib = None
 

@@ -62,7 +62,7 @@ enum KernelId {
   KID_EIG, KID_FILL, KID_PROJECT_FIRST, KID_PROJECT_FUSED2, KID_RECON_FUSED2_APPLY,
   KID_RECON_FUSED2, KID_REMAP, KID_PROJECT_FUSED3, KID_GRAM3, KID_PROJECT_PAIR, KID_RECON_PAIR,
   KID_RECON_FUSED3_APPLY, KID_STREAM_PROJECT, KID_STREAM_RECONSTRUCT, KID_CSPLIT_OPERAND,
-  KID_CSPLIT_COMBINE, KID_COUNT_
+  KID_CSPLIT_COMBINE, KID_ROW_PROJECT, KID_ROW_RECON_APPLY, KID_COUNT_
 };
 
 // ---------------------------------------------------------------- launchers
@@ -161,6 +161,12 @@ hipError_t launch_modeprod(const ModeProd& mp, int num_cu, hipStream_t s);
 // output (store epilogue), I <= 64, R <= 64 (complex with Mre and Mim), B (complex:
 // 2 B) >= 32 and a multiple of 4, X and Y 16-byte aligned.
 bool streamprod_supported(const ModeProd& mp);
+// A product over the last mode (B == 1) as a stream of rows (k_rowprod.hip): store form
+// (fp32, f16 or bf16 input; complex as fp32 pairs with the real-block operand) or
+// weight-updating form (fp32 input); K = I P and N = R P small enough for M to sit in
+// registers, the input below 2^31 bytes.
+bool rowprod_supported(const ModeProd& mp);
+hipError_t launch_rowprod(const ModeProd& mp, int num_cu, hipStream_t s);
 hipError_t launch_streamprod(const ModeProd& mp, int num_cu, hipStream_t s);
 
 // Two trailing mode products in one launch over slabs (A, I1, I2, P) -> (A, R1, R2, P).

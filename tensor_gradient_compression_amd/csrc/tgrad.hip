@@ -78,6 +78,7 @@ struct tgrad_handle {
   bool can_pair = false;     // the fused chains hold two neighbouring leading modes
   bool pairs = true;         // launch those as one (k_pair)
   bool stream = true;        // single fp32 mode products on k_streamprod where it applies
+  bool rows = true;          // single last-mode products on k_rowprod where it applies
   int stream_wg = 0;         // test hook: cap on its workgroups (0: none)
 
   uint32_t* omega = nullptr;
@@ -689,7 +690,9 @@ const char* tgrad_kernel_name(int id) {
       "modeprod2_project_first", "modeprod2_reconstruct_apply", "modeprod2_reconstruct",
       "remap_moments", "modeprod3_project_first", "gram3_tail", "modeprod_pair_project",
       "modeprod_pair_reconstruct", "modeprod3_reconstruct_apply", "streamprod_project",
-      "streamprod_reconstruct", "complex_split_operand", "complex_split_combine"};
+      "streamprod_reconstruct", "complex_split_operand", "complex_split_combine",
+      "rowprod_project", "rowprod_reconstruct_apply"};
+  static_assert(KID_COUNT_ <= TGRAD_MAX_KERNEL_IDS, "kernel ids fit the timing arrays");
   if (id < 0 || id >= KID_COUNT_) return "";
   return names[id];
 }
@@ -1122,6 +1125,12 @@ int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s) {
                                      j == 0 ? KID_PROJECT_FIRST : KID_PROJECT,
                                      KID_STREAM_PROJECT, Y, s);
         if (rc != TGRAD_OK) return rc;
+      } else if (h->rows && rowprod_supported(mp)) {
+        // the last mode (B = 1): a stream of rows
+        Mark m(h, KID_ROW_PROJECT);
+        HIPCHK(h, launch_rowprod(mp, h->num_cu, s));
+        account_chain(h, KID_ROW_PROJECT, cur, proj[j], true, xdt == DT_F32 ? 4 : 2, false,
+                      false);
       } else {
         const int kid =
             use_stream(h, mp) ? KID_STREAM_PROJECT : j == 0 ? KID_PROJECT_FIRST : KID_PROJECT;
@@ -1287,6 +1296,11 @@ int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, fl
           record(h, KID_APPLY_DENSE, 0, h->N * (dt_bytes(h->dtype) + P * 4) + h->k * P * 4,
                  h->N * dt_bytes(h->dtype), 0);
         }
+      } else if (app && h->rows && rowprod_supported(mp)) {
+        // the last mode (B = 1) with the weight update: a stream of rows
+        Mark m(h, KID_ROW_RECON_APPLY);
+        HIPCHK(h, launch_rowprod(mp, h->num_cu, s));
+        account_chain(h, KID_ROW_RECON_APPLY, cur, rec[j], false, 4, false, true);
       } else {
         const int kid =
             use_stream(h, mp) ? KID_STREAM_RECONSTRUCT : app ? KID_RECON_APPLY : KID_RECONSTRUCT;
@@ -1759,6 +1773,7 @@ int tgrad_set_fusion(tgrad_t* h, int enable) {
 int tgrad_set_stream_products(tgrad_t* h, int enable) {
   if (!h || enable < 0) return TGRAD_EINVAL;
   h->stream = enable != 0;
+  h->rows = enable != 0;
   h->stream_wg = enable > 1 ? enable - 1 : 0;
   return TGRAD_OK;
 }
