@@ -52,6 +52,8 @@ struct RPK {
   const uint32_t* rank;
   const float* uS;      // N_S, P values per Omega entry
   float* delta;         // test capture of the fp32 update (NULL: off)
+  float* gS;            // store form with the COO gather: S[j] = X[omega[j]] (fp32)
+  uint64_t nwords;      // bitmask words
   uint64_t ntiles;      // ceil(A / 16)
   uint32_t A, K, N, P;
   float lr, decay;
@@ -80,8 +82,11 @@ template <> struct RowIn<bf16_t> {
 
 // NQ: groups of 4 VPL values per row (K <= 4 VPL NQ); NCB: 16-column blocks of N
 // (N <= 16 NCB); EPI 0: store Y; EPI 1: update W (type WT; complex weights as fp32
-// pairs with P = 2).
-template <typename XT, int NQ, int NCB, int EPI, typename WT>
+// pairs with P = 2). GATH (store form): X is the gradient itself; the COO gather
+// S[j] = X[omega[j]] happens on the loaded rows, whose Omega values are then cleared
+// before the product (X is only read): each lane prefetches, with its row groups, the
+// bitmask and rank words of their elements.
+template <typename XT, int NQ, int NCB, int EPI, typename WT, bool GATH>
 __global__ void __launch_bounds__(RP_NT) k_rowprod(RPK k) {
   constexpr int VPL = RowIn<XT>::VPL;
   constexpr int NS = NQ * VPL;   // k-steps
@@ -157,6 +162,70 @@ __global__ void __launch_bounds__(RP_NT) k_rowprod(RPK k) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
       b[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(base + 4 * VPL * q * es), 0, 0);
+  };
+  // GATH: the bitmask and rank words of group q's elements (its first element e0 and
+  // the word after, which the group may reach into)
+  constexpr int NG = GATH ? NQ : 1;
+  struct GW {
+    uint64_t m0[NG], m1[NG];
+    uint32_t r0[NG], r1[NG];
+  };
+  const uint32_t P = k.P;
+  auto gfirst = [&](uint64_t t, int q) -> uint64_t {
+    const uint64_t row = 16 * t + li;
+    const uint32_t k0 = 4 * VPL * q + VPL * lg;
+    return row < k.A && k0 < K ? (row * K + k0) / P : 0;
+  };
+  auto gload = [&](uint64_t t, GW& g) {
+    if constexpr (GATH) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const uint64_t w = gfirst(t, q) >> 6;
+        const uint64_t w1 = w + 1 < k.nwords ? w + 1 : w;
+        g.m0[q] = k.mask[w];
+        g.m1[q] = k.mask[w1];
+        g.r0[q] = k.rank[w];
+        g.r1[q] = k.rank[w1];
+      }
+    }
+  };
+  // GATH: S[j] = X[omega[j]] for the Omega elements among b's values, which are then
+  // cleared (+0 is the zero bit pattern of every input type)
+  auto gather = [&](uint64_t t, u32x4 (&b)[NQ], const GW& g) {
+    if constexpr (GATH) {
+      constexpr uint32_t NEL = VPL;   // values of a group; elements: NEL / P
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const uint64_t row = 16 * t + li;
+        const uint32_t k0 = 4 * VPL * q + VPL * lg;
+        const uint32_t vlive = row < k.A && k0 < K ? (K - k0 < NEL ? K - k0 : NEL) : 0u;
+        const uint32_t nel = vlive / P;   // live elements of the group
+        const uint64_t e0 = gfirst(t, q);
+        const uint32_t sh = (uint32_t)(e0 & 63);
+        const uint64_t win = sh ? (g.m0[q] >> sh) | (g.m1[q] << (64 - sh)) : g.m0[q];
+        const uint32_t bits = (uint32_t)win & ((1u << nel) - 1u);
+        if (!bits) continue;
+        u32x4 zm = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (uint32_t j = 0; j < NEL; ++j) {
+          if (j >= nel || !((bits >> j) & 1u)) continue;
+          const uint32_t lb = sh + j;
+          const uint32_t r = lb < 64
+                                 ? g.r0[q] + (uint32_t)__popcll(g.m0[q] & ((1ull << lb) - 1ull))
+                                 : g.r1[q] +
+                                       (uint32_t)__popcll(g.m1[q] & ((1ull << (lb - 64)) - 1ull));
+          for (uint32_t p = 0; p < P; ++p) {
+            const uint32_t v = j * P + p;
+            k.gS[(uint64_t)r * P + p] = RowIn<XT>::val(b[q], (int)v);
+            if constexpr (VPL == 4)
+              zm[v] = 0xFFFFFFFFu;
+            else
+              zm[v >> 1] |= 0xFFFFu << (16 * (v & 1));
+          }
+        }
+        b[q] = b[q] & ~zm;
+      }
+    }
   };
   // (values past the row's end belong to the next row: masked to +0 before use)
   auto multiply = [&](const u32x4 (&b)[NQ], f4 (&acc)[NCB]) {
@@ -259,19 +328,25 @@ __global__ void __launch_bounds__(RP_NT) k_rowprod(RPK k) {
   f4 acc[NCB];
   u32x4 bA[NQ], bB[NQ];
   u32x4 wA[NR][NW], wB[NR][NW];
+  GW gA, gB;
   load(t0, bA);
   wload(t0, wA);
+  gload(t0, gA);
   const uint64_t t1 = t0 + TW < k.ntiles ? t0 + TW : t0;
   load(t1, bB);
   wload(t1, wB);
+  gload(t1, gB);
   __builtin_amdgcn_sched_barrier(0);
+  gather(t0, bA, gA);
   multiply(bA, acc);
   finish(t0, acc, wA);
   for (uint64_t t = t0 + TW; t < k.ntiles;) {
     const uint64_t tn = t + TW < k.ntiles ? t + TW : t;
     load(tn, bA);
     wload(tn, wA);
+    gload(tn, gA);
     __builtin_amdgcn_sched_barrier(0);
+    gather(t, bB, gB);
     multiply(bB, acc);
     finish(t, acc, wB);
     t += TW;
@@ -279,7 +354,9 @@ __global__ void __launch_bounds__(RP_NT) k_rowprod(RPK k) {
     const uint64_t tm = t + TW < k.ntiles ? t + TW : t;
     load(tm, bB);
     wload(tm, wB);
+    gload(tm, gB);
     __builtin_amdgcn_sched_barrier(0);
+    gather(t, bA, gA);
     multiply(bA, acc);
     finish(t, acc, wA);
     t += TW;
@@ -297,6 +374,7 @@ PlanR plan_r(const ModeProd& mp) {
   p.ok = false;
   if (mp.B != 1 || mp.A == 0 || mp.I == 0 || mp.R == 0) return p;
   if (mp.apply ? (mp.in_dt != DT_F32 || !mp.W) : !mp.Y) return p;
+  if (mp.gather_S && (mp.apply || !mp.mask || !mp.rank)) return p;
   // weight runs of 8 values in 16-byte accesses: W 16-byte aligned, its bytes within
   // one buffer resource
   if (mp.apply && (uintptr_t)mp.W % 16 != 0) return p;
@@ -324,6 +402,8 @@ PlanR plan_r(const ModeProd& mp) {
   k.rank = mp.rank;
   k.uS = mp.uS;
   k.delta = mp.delta;
+  k.gS = mp.gather_S;
+  k.nwords = ((uint64_t)mp.A * mp.I + 63) / 64;
   k.A = mp.A;
   k.K = (uint32_t)K;
   k.N = (uint32_t)N;
@@ -341,7 +421,9 @@ hipError_t rp_launch(const PlanR& p, int num_cu, hipStream_t s) {
   if constexpr (NQ * RowIn<XT>::VPL * NCB > 64) {
     return hipErrorInvalidValue;
   } else {
-    auto fn = k_rowprod<XT, NQ, NCB, EPI, WT>;
+    void (*fn)(RPK) = k_rowprod<XT, NQ, NCB, EPI, WT, false>;
+    if constexpr (EPI == 0)
+      if (p.k.gS) fn = k_rowprod<XT, NQ, NCB, EPI, WT, true>;
     const size_t lds = EPI ? (size_t)RP_WPB * 16 * p.k.N * 4 : 0;
     int per_cu = 0;
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, RP_NT, lds);

@@ -151,6 +151,10 @@ struct ModeProd {
   // streaming kernel applies to a complex product only when both are given)
   const float* Mre;
   const float* Mim;
+  // row kernel only, store form over the gradient: also perform the COO gather,
+  // gather_S[j] = X[omega[j]] (fp32, through mask and rank), and project X with Omega
+  // cleared (X itself is only read)
+  float* gather_S;
   // apply only, a test capture: when not NULL the fp32 update (acc + uS@Omega) is also
   // stored here, one float per output value (a separate kernel instantiation)
   float* delta;

@@ -1125,6 +1125,20 @@ int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s) {
                                      j == 0 ? KID_PROJECT_FIRST : KID_PROJECT,
                                      KID_STREAM_PROJECT, Y, s);
         if (rc != TGRAD_OK) return rc;
+      } else if (j == 0 && gather) {
+        // the last mode (B = 1) with the COO gather: a stream of rows of the gradient
+        mp.gather_S = h->S;
+        mp.mask = h->mask;
+        mp.rank = h->rank;
+        mp.kS = h->k;
+        if (!rowprod_supported(mp)) {
+          h->err = "run_projection: the first single-mode launch cannot take the gather";
+          return TGRAD_EHIP;
+        }
+        Mark m(h, KID_ROW_PROJECT);
+        HIPCHK(h, launch_rowprod(mp, h->num_cu, s));
+        account_chain(h, KID_ROW_PROJECT, cur, proj[j], true, xdt == DT_F32 ? 4 : 2, true,
+                      false);
       } else if (h->rows && rowprod_supported(mp)) {
         // the last mode (B = 1): a stream of rows
         Mark m(h, KID_ROW_PROJECT);
@@ -1342,6 +1356,27 @@ int tgrad_step(tgrad_t* h, void* weight, const void* grad, void* stream) {
 
 namespace {
 
+// The one-mode plan's first projection launch is a row stream over the last mode that
+// can also take the COO gather (the same ModeProd run_projection builds for it).
+bool first_rows_gather(const tgrad_t* h, const void* grad,
+                       const std::vector<std::vector<int>>& proj) {
+  const int d = h->d;
+  if (!h->rows || proj.empty() || proj[0].size() != 1 || proj[0][0] != d - 1) return false;
+  if (h->csplit[d - 1]) return false;
+  ModeProd mp{};
+  mp.X = grad;
+  mp.in_dt = (h->dtype == DT_C64) ? DT_F32 : h->dtype;
+  mp.M = h->Mp[d - 1];
+  view(h->shape, d, d - 1, &mp.A, &mp.I, &mp.B);
+  mp.R = (uint32_t)h->ranks[d - 1];
+  mp.P = h->P;
+  mp.Y = h->core;   // any non-null output: only the shape and alignment are checked
+  mp.gather_S = h->S;
+  mp.mask = h->mask;
+  mp.rank = h->rank;
+  return rowprod_supported(mp);
+}
+
 int step_body(tgrad_t* h, void* weight, const void* grad, int64_t t, hipStream_t s) {
   const uint32_t P = h->P;
   const size_t nf = h->fmodes.size();
@@ -1366,8 +1401,10 @@ int step_body(tgrad_t* h, void* weight, const void* grad, int64_t t, hipStream_t
     std::vector<std::vector<int>> proj, rec;
     build_chain(h, h->fuse, use_proj3(h, grad), proj, rec);
     // the COO gather runs on its own unless the first projection launch is a fused
-    // multi-mode one, which takes S and zeroes Omega on its staged input
-    const bool gather_fused = h->k > 0 && !proj.empty() && proj[0].size() >= 2;
+    // multi-mode one, which takes S and zeroes Omega on its staged input, or a row
+    // stream over the last mode, which does the same on its loaded rows
+    const bool gather_fused =
+        h->k > 0 && !proj.empty() && (proj[0].size() >= 2 || first_rows_gather(h, grad, proj));
     // the first projection's input: grad itself, or (when the gather is not folded into
     // it) a copy of grad that the gather turns into the residual; grad is only read
     if (h->k > 0 && !gather_fused) {

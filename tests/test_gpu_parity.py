@@ -595,7 +595,10 @@ def test_launch_record_matches_the_launches():
         nq, ncb = -(-I // 16), -(-R // 16)
         return nq <= 5 and ncb <= 5 and nq * 4 * ncb <= 64
 
-    exp = [("gather_residual", k * (4 + es) + k * (4 + es), 0)]
+    # the COO gather: its own launch on a copy of G, unless the first projection is the
+    # row stream over the last mode, which takes it (k indices read, k values written)
+    row_gather = rows(shape[3], ranks[3])
+    exp = [] if row_gather else [("gather_residual", k * (4 + es) + k * (4 + es), 0)]
     cur, size = list(shape), N
     for j, n in enumerate([3, 2, 1, 0]):
         out = size // cur[n] * ranks[n]
@@ -604,7 +607,8 @@ def test_launch_record_matches_the_launches():
             name = "streamprod_project"
         if n == 3 and rows(cur[n], ranks[n]):
             name = "rowprod_project"
-        exp.append((name, size * 4 + out * 4, 2 * (size // cur[n]) * cur[n] * ranks[n]))
+        gb = 8 * k if (j == 0 and row_gather) else 0
+        exp.append((name, size * 4 + out * 4 + gb, 2 * (size // cur[n]) * cur[n] * ranks[n]))
         cur[n] = ranks[n]
         size = out
     ncore = size
