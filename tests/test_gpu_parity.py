@@ -335,6 +335,65 @@ def test_stream_products_match_tiled_and_oracle(case, fused):
         g = gs.next()
 
 
+# The row stream over the last mode (one-mode plan: the first projection, with the COO
+# gather on the gradient's rows, and the weight-updating last reconstruction). Cases:
+# a row tail inside the last group of values (K not a multiple of 16 or 32), ragged
+# 16-row tiles, 16-bit and complex rows (complex rows of 62 and 80 fp32 values, the
+# latter five groups), many Omega entries, no sparse part, and a factor too large for
+# registers (the tiled kernel then runs).
+ROW_CASES = [
+    ("f32-tail-23", custom((37, 5, 23), "f32", (20, 5, 11), 0.05), True),
+    ("bf16-tail-46", custom((9, 13, 46), "bf16", (5, 13, 20), 0.05), True),
+    ("f16-64-dense-omega", custom((11, 7, 64), "f16", (6, 7, 32), 0.3), True),
+    ("c64-31", custom((7, 9, 31), "c64", (4, 9, 12), 0.05), True),
+    ("c64-40-five-groups", custom((6, 5, 40), "c64", (3, 5, 8), 0.05), True),
+    ("f32-k0", custom((12, 6, 20), "f32", (6, 6, 10), 0.0), True),
+    ("f32-factor-too-large", custom((8, 10, 80), "f32", (4, 10, 64), 0.05), False),
+]
+
+
+@pytest.mark.parametrize("case", ROW_CASES, ids=lambda c: c[0])
+def test_row_products_match_oracle(case):
+    """The one-mode plan with Omega and factors pinned from the oracle, over two steps:
+    the last mode's products run on the row kernel where the factor fits in registers
+    (else on the tiled kernel), Delta against the oracle's at the parity bar, the
+    weight update bit for bit against the rounding of the library's own Delta, the
+    sparse moments against the oracle's (S comes from the fused gather), and the
+    gradient untouched."""
+    name, wl, rows = case
+    gs = GradStream(wl, seed=3)
+    W0 = init_weights(wl, seed=3)
+    lib, orc = make_lib(wl, T=10 ** 6), make_oracle(wl, T=10 ** 6)
+    assert lib.set_fusion(0)
+    g = gs.next()
+    orc.refresh(g)
+    lib.set_omega(orc.omega)
+    for n, U in enumerate(orc.factors):
+        if U is not None:
+            lib.set_factor(n, U)
+    lib.mark_refreshed()
+    cap = DeltaCapture(lib, wl)
+    align = CoreSplit(orc)
+    W, Wo = dev(W0, wl.dtype), W0
+    for step in range(2):
+        what = f"{name} step {step + 1}"
+        G = dev(g, wl.dtype)
+        before = host(G, wl.dtype).copy()
+        lib.timing_enable(True)
+        Wo, _ = checked_step(lib, orc, cap, W, Wo, g, wl, what, G=G, align=align)
+        rec = lib.timing_read()
+        got = "rowprod_project" in rec and "rowprod_reconstruct_apply" in rec
+        assert got == rows, (what, sorted(rec))
+        if rows and wl.k > 0:
+            assert "gather_residual" not in rec, (what, sorted(rec))
+        if wl.k > 0:
+            mS = lib.get_moments()[2]
+            np.testing.assert_allclose(mS, orc.mS.reshape(-1), rtol=1e-5,
+                                       atol=1e-6 * np.abs(orc.mS).max(), err_msg=what)
+        assert np.array_equal(host(G, wl.dtype).view(np.uint8), before.view(np.uint8)), what
+        g = gs.next()
+
+
 # --------------------------------------------------------------------------- independent runs
 
 RUN_CASES = [
