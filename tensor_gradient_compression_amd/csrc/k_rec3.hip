@@ -64,7 +64,8 @@ struct R3K {
 // and R1 = 4 KS1, so that only the last column block of a slab and the columns past R2
 // of the stack rows need lane tests (every lane test is a mask the compiler keeps in
 // scalar registers across the slab loop).
-template <typename WT, int NRB1, int NCB2, int KS1, bool FULL>
+// CAP: the test capture of the fp32 update is on (its stores are issued only then).
+template <typename WT, int NRB1, int NCB2, int KS1, bool FULL, bool CAP>
 __global__ void __launch_bounds__(NTR) __attribute__((amdgpu_waves_per_eu(3, 8))) k_rec3s(R3K k) {
   // 16-byte weight pieces a lane holds: a slab has at most 16 NRB1 x 16 NCB2 values
   constexpr int WQ = (NRB1 * NCB2 + 1) / 2;
@@ -90,7 +91,6 @@ __global__ void __launch_bounds__(NTR) __attribute__((amdgpu_waves_per_eu(3, 8))
   const uint64_t kS = k.kS;
   const bool sparse = kS > 0;
   const float lr = k.lr, decay = k.decay;
-  const uint32_t np = slab_e / 8;              // 16-byte weight pieces of a slab
 
   // M0 into LDS (4-byte transfers, I0 R0 <= 2048 values), and the operand tables: every
   // load of a thread issued before its first LDS write (one memory latency in all)
@@ -183,12 +183,12 @@ __global__ void __launch_bounds__(NTR) __attribute__((amdgpu_waves_per_eu(3, 8))
   // exactly without weight decay, and W * 1 is W: one expression serves both. A piece
   // past the slab reads O slots past this wave's region (the allocation extends far
   // enough for the last wave) and its store is dropped. The test capture of the fp32
-  // update goes through a resource of extent zero when it is off.
+  // update (CAP) goes through a resource over the slab's capture values.
   auto epilogue = [&](uint32_t s) {
     const __amdgpu_buffer_rsrc_t rw = wres(s);
     const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(k.delta ? k.delta + (uint64_t)s * slab_e : (float*)k.W), 0,
-        k.delta ? (int)(slab_e * 4) : 0, 0x00020000);
+        (void*)(CAP ? k.delta + (uint64_t)s * slab_e : (float*)k.W), 0,
+        CAP ? (int)(slab_e * 4) : 0, 0x00020000);
 #pragma unroll
     for (int j = 0; j < WQ; ++j) {
       const LDS float* const ob = Ob + 8 * (lane + 64 * j);
@@ -203,10 +203,12 @@ __global__ void __launch_bounds__(NTR) __attribute__((amdgpu_waves_per_eu(3, 8))
         out[e] = wpack<WT>(lo - lr * ov[2 * e], hi - lr * ov[2 * e + 1]);
       }
       __builtin_amdgcn_raw_buffer_store_b128(out, rw, (int)(vq + 1024 * j), 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o0), rd,
-                                             (int)(2 * vq + 2048 * j), 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o1), rd,
-                                             (int)(2 * vq + 2048 * j + 16), 0, 0);
+      if constexpr (CAP) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o0), rd,
+                                               (int)(2 * vq + 2048 * j), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o1), rd,
+                                               (int)(2 * vq + 2048 * j + 16), 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -480,7 +482,11 @@ Plan3r plan3r(const ModeProd2& mp) {
 template <typename WT, int NRB1, int NCB2, int KS1>
 hipError_t rec3_launch(const Plan3r& p, int num_cu, hipStream_t s) {
   const bool full = p.k.I1 == 16u * NRB1 && p.k.R1 == 4u * KS1;
-  auto fn = full ? k_rec3s<WT, NRB1, NCB2, KS1, true> : k_rec3s<WT, NRB1, NCB2, KS1, false>;
+  const bool cap = p.k.delta != nullptr;
+  auto fn = full ? (cap ? k_rec3s<WT, NRB1, NCB2, KS1, true, true>
+                        : k_rec3s<WT, NRB1, NCB2, KS1, true, false>)
+                 : (cap ? k_rec3s<WT, NRB1, NCB2, KS1, false, true>
+                        : k_rec3s<WT, NRB1, NCB2, KS1, false, false>);
   if (p.lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)fn,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
