@@ -41,247 +41,6 @@ struct EK {
   EK1 m[8];
 };
 
-__device__ __forceinline__ double block_sum(double v, double* red) {
-  const int tid = threadIdx.x;
-  red[tid] = v;
-  __syncthreads();
-  for (int off = NTH / 2; off > 0; off >>= 1) {
-    if (tid < off) red[tid] += red[tid + off];
-    __syncthreads();
-  }
-  const double s = red[0];
-  __syncthreads();
-  return s;
-}
-
-template <bool CPLX>
-__global__ void __launch_bounds__(NTH) k_eig(EK kk) {
-  extern __shared__ double sm[];
-  const EK1& k = kk.m[blockIdx.x];
-  const int tid = threadIdx.x;
-  const uint32_t n = k.n;
-  const uint32_t LD = n + 1;          // odd row stride: column walks hit distinct banks
-  const uint32_t nn = n * LD;
-  double* Ar = sm;
-  double* Ai = CPLX ? Ar + nn : nullptr;
-  double* Vr = CPLX ? Ai + nn : Ar + nn;
-  double* Vi = CPLX ? Vr + nn : nullptr;
-  double* tail = (CPLX ? Vi : Vr) + nn;
-  double* rc = tail;          // 32 pairs max
-  double* rs = rc + 32;
-  double* rpc = rs + 32;      // cos(phi)
-  double* rps = rpc + 32;     // sin(phi)
-  double* red = rps + 32;     // NTH
-  int* rp = (int*)(red + NTH);
-  int* rq = rp + 32;
-  int* order = rq + 32;       // 64
-
-  // Hermitian (or symmetric) matrix from the stacked real Gram, symmetrised.
-  const uint32_t K = CPLX ? 2 * n : n;
-  for (uint32_t idx0 = tid; idx0 < n * n; idx0 += NTH) {
-    const uint32_t i = idx0 / n, j = idx0 - i * n;
-    const uint32_t idx = i * LD + j;
-    if (CPLX) {
-      auto G = [&](uint32_t a, uint32_t b) { return k.gram[(uint64_t)a * K + b]; };
-      const double re1 = G(2 * i, 2 * j) + G(2 * i + 1, 2 * j + 1);
-      const double im1 = G(2 * i + 1, 2 * j) - G(2 * i, 2 * j + 1);
-      const double re2 = G(2 * j, 2 * i) + G(2 * j + 1, 2 * i + 1);
-      const double im2 = G(2 * j + 1, 2 * i) - G(2 * j, 2 * i + 1);
-      Ar[idx] = 0.5 * (re1 + re2);
-      Ai[idx] = 0.5 * (im1 - im2);
-      Vi[idx] = 0.0;
-    } else {
-      Ar[idx] = 0.5 * (k.gram[(uint64_t)i * K + j] + k.gram[(uint64_t)j * K + i]);
-    }
-    Vr[idx] = (i == j) ? 1.0 : 0.0;
-  }
-  __syncthreads();
-
-  const uint32_t m = n + (n & 1u);   // even number of players; player n is a bye
-  const uint32_t half = m / 2;
-  int sweeps = -1;
-  for (int sweep = 0;; ++sweep) {
-    double off = 0.0, tot = 0.0;
-    for (uint32_t idx0 = tid; idx0 < n * n; idx0 += NTH) {
-      const uint32_t i = idx0 / n, j = idx0 - i * n;
-      const uint32_t idx = i * LD + j;
-      const double a2 = Ar[idx] * Ar[idx] + (CPLX ? Ai[idx] * Ai[idx] : 0.0);
-      tot += a2;
-      if (i != j) off += a2;
-    }
-    off = block_sum(off, red);
-    tot = block_sum(tot, red);
-    if (!(off > 1e-20 * tot)) {
-      sweeps = sweep;
-      break;
-    }
-    if (sweep == MAX_SWEEPS) break;
-
-    for (uint32_t round = 0; round + 1 < m; ++round) {
-      if ((uint32_t)tid < half) {
-        auto player = [&](uint32_t pos) -> uint32_t {
-          return pos == 0 ? 0u : 1u + (pos - 1u + round) % (m - 1u);
-        };
-        uint32_t p = player(tid), q = player(m - 1 - tid);
-        if (p > q) { uint32_t t = p; p = q; q = t; }
-        double c = 1.0, s = 0.0, pc = 1.0, ps = 0.0;
-        if (q < n) {
-          const double app = Ar[p * LD + p], aqq = Ar[q * LD + q];
-          const double xr = Ar[p * LD + q], xi = CPLX ? Ai[p * LD + q] : 0.0;
-          const double rr = CPLX ? sqrt(xr * xr + xi * xi) : fabs(xr);
-          if (rr > 0.0) {
-            const double theta = (aqq - app) / (2.0 * rr);
-            double t;
-            if (fabs(theta) > 1e100) {
-              t = 0.5 / theta;
-            } else {
-              t = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
-            }
-            c = 1.0 / sqrt(t * t + 1.0);
-            s = t * c;
-            if (CPLX) {
-              pc = xr / rr;
-              ps = xi / rr;
-            } else {
-              pc = xr >= 0.0 ? 1.0 : -1.0;
-            }
-          }
-        }
-        rc[tid] = c;
-        rs[tid] = s;
-        rpc[tid] = pc;
-        rps[tid] = ps;
-        rp[tid] = (int)p;
-        rq[tid] = (q < n) ? (int)q : -1;
-      }
-      __syncthreads();
-      // Real case: the phase is the sign of a_pq; folding it into s gives the usual
-      // real rotation (c, s*sign) for the symmetric 2x2 problem.
-      // Column updates: A[:, p], A[:, q] and V[:, p], V[:, q].
-      for (uint32_t idx = tid; idx < n * half; idx += NTH) {
-        const uint32_t j = idx / n, i = idx - j * n;
-        const int q = rq[j];
-        if (q < 0 || rs[j] == 0.0) continue;
-        const int p = rp[j];
-        const double c = rc[j], s = rs[j], pc = rpc[j], ps = rps[j];
-        if (CPLX) {
-          // y' = e^{-i phi} * y
-          {
-            const double xr = Ar[i * LD + p], xi = Ai[i * LD + p];
-            const double yr0 = Ar[i * LD + q], yi0 = Ai[i * LD + q];
-            const double yr = pc * yr0 + ps * yi0, yi = pc * yi0 - ps * yr0;
-            Ar[i * LD + p] = c * xr - s * yr;
-            Ai[i * LD + p] = c * xi - s * yi;
-            Ar[i * LD + q] = s * xr + c * yr;
-            Ai[i * LD + q] = s * xi + c * yi;
-          }
-          {
-            const double xr = Vr[i * LD + p], xi = Vi[i * LD + p];
-            const double yr0 = Vr[i * LD + q], yi0 = Vi[i * LD + q];
-            const double yr = pc * yr0 + ps * yi0, yi = pc * yi0 - ps * yr0;
-            Vr[i * LD + p] = c * xr - s * yr;
-            Vi[i * LD + p] = c * xi - s * yi;
-            Vr[i * LD + q] = s * xr + c * yr;
-            Vi[i * LD + q] = s * xi + c * yi;
-          }
-        } else {
-          const double ss = s * pc;
-          const double x = Ar[i * LD + p], y = Ar[i * LD + q];
-          Ar[i * LD + p] = c * x - ss * y;
-          Ar[i * LD + q] = ss * x + c * y;
-          const double vx = Vr[i * LD + p], vy = Vr[i * LD + q];
-          Vr[i * LD + p] = c * vx - ss * vy;
-          Vr[i * LD + q] = ss * vx + c * vy;
-        }
-      }
-      __syncthreads();
-      // Row updates: A[p, :], A[q, :] <- J^H A.
-      for (uint32_t idx = tid; idx < n * half; idx += NTH) {
-        const uint32_t j = idx / n, col = idx - j * n;
-        const int q = rq[j];
-        if (q < 0 || rs[j] == 0.0) continue;
-        const int p = rp[j];
-        const double c = rc[j], s = rs[j], pc = rpc[j], ps = rps[j];
-        if (CPLX) {
-          // y' = e^{+i phi} * y
-          const double xr = Ar[p * LD + col], xi = Ai[p * LD + col];
-          const double yr0 = Ar[q * LD + col], yi0 = Ai[q * LD + col];
-          const double yr = pc * yr0 - ps * yi0, yi = pc * yi0 + ps * yr0;
-          Ar[p * LD + col] = c * xr - s * yr;
-          Ai[p * LD + col] = c * xi - s * yi;
-          Ar[q * LD + col] = s * xr + c * yr;
-          Ai[q * LD + col] = s * xi + c * yi;
-        } else {
-          const double ss = s * pc;
-          const double x = Ar[p * LD + col], y = Ar[q * LD + col];
-          Ar[p * LD + col] = c * x - ss * y;
-          Ar[q * LD + col] = ss * x + c * y;
-        }
-      }
-      __syncthreads();
-    }
-  }
-
-  if (tid == 0) *k.status = sweeps;
-  // Descending order of the diagonal, equal values in index order.
-  if (tid == 0) {
-    uint64_t used = 0;
-    for (uint32_t pos = 0; pos < n; ++pos) {
-      int best = -1;
-      double bv = 0.0;
-      for (uint32_t i = 0; i < n; ++i) {
-        if ((used >> i) & 1ull) continue;
-        const double d = Ar[i * LD + i];
-        if (best < 0 || d > bv) { best = (int)i; bv = d; }
-      }
-      used |= 1ull << best;
-      order[pos] = best;
-    }
-  }
-  __syncthreads();
-  for (uint32_t i = tid; i < n; i += NTH) k.eigvals[i] = Ar[order[i] * LD + order[i]];
-
-  const uint32_t r = k.r;
-  const uint32_t P = CPLX ? 2 : 1;
-  for (uint32_t c = tid; c < r; c += NTH) {
-    const uint32_t src = (uint32_t)order[c];
-    uint32_t imax = 0;
-    double best = -1.0;
-    for (uint32_t i = 0; i < n; ++i) {
-      const double vr = Vr[i * LD + src], vi = CPLX ? Vi[i * LD + src] : 0.0;
-      const double a2 = vr * vr + vi * vi;
-      if (a2 > best) { best = a2; imax = i; }
-    }
-    const double vr = Vr[imax * LD + src], vi = CPLX ? Vi[imax * LD + src] : 0.0;
-    const double mag = sqrt(vr * vr + vi * vi);
-    const double sr = mag > 0.0 ? vr / mag : 1.0;     // scale = conj(phase)
-    const double si = mag > 0.0 ? -vi / mag : 0.0;
-    for (uint32_t i = 0; i < n; ++i) {
-      const double xr = Vr[i * LD + src], xi = CPLX ? Vi[i * LD + src] : 0.0;
-      const float ur = (float)(xr * sr - xi * si);
-      const float ui = (float)(xr * si + xi * sr);
-      if (CPLX) {
-        k.U[((uint64_t)i * r + c) * 2] = ur;
-        k.U[((uint64_t)i * r + c) * 2 + 1] = ui;
-        const uint64_t KP = 2ull * n, RP = 2ull * r;
-        k.Mproj[(2 * c) * KP + 2 * i] = ur;
-        k.Mproj[(2 * c) * KP + 2 * i + 1] = ui;
-        k.Mproj[(2 * c + 1) * KP + 2 * i] = -ui;
-        k.Mproj[(2 * c + 1) * KP + 2 * i + 1] = ur;
-        k.Mrec[(2 * i) * RP + 2 * c] = ur;
-        k.Mrec[(2 * i) * RP + 2 * c + 1] = -ui;
-        k.Mrec[(2 * i + 1) * RP + 2 * c] = ui;
-        k.Mrec[(2 * i + 1) * RP + 2 * c + 1] = ur;
-      } else {
-        k.U[(uint64_t)i * r + c] = ur;
-        k.Mproj[(uint64_t)c * n + i] = ur;
-        k.Mrec[(uint64_t)i * r + c] = ur;
-      }
-    }
-    (void)P;
-  }
-}
-
 // ---------------------------------------------------------------- real symmetric case
 // Same method and arithmetic as above (parallel cyclic Jacobi in fp64, round-robin
 // pairs, each rotation from the same matrix, A <- J^T A J as the column rotation then
@@ -504,6 +263,257 @@ __global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
       k.Mrec[(uint64_t)lane * r + c] = u;
     }
   }
+}
+
+// ---------------------------------------------------------------- Hermitian, I <= 64
+// The Hermitian form of k_eig_sym: one 1024-thread workgroup per matrix, A and V in LDS
+// as real and imaginary planes (fp64), per round the rotations (c, s and the phase
+// e^{i phi} = a_pq / |a_pq|) formed by one thread per pair, then one pass that applies
+// the two-sided update to every 2 x 2 block (pair a rows, pair b columns) of A and the
+// column update to V. Every element sees the operations of a column pass followed by a
+// row pass in the same order: columns, y' = e^{-i phi} y on column q then the real
+// rotation; rows, y' = e^{+i phi} y on row q then the real rotation.
+__global__ void __launch_bounds__(NTS) k_eig_herm(EK kk) {
+  extern __shared__ double sm[];
+  const EK1& k = kk.m[blockIdx.x];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t n = k.n;
+  const uint32_t LD = n + 1;
+  const uint32_t nn = n * LD;
+  double* Ar = sm;
+  double* Ai = Ar + nn;
+  double* Vr = Ai + nn;
+  double* Vi = Vr + nn;
+  double4* cs = (double4*)(Vi + nn);   // 32 rotations: (c, s, cos phi, sin phi)
+  double* red = (double*)(cs + 32);    // 2 x 16 wave partials
+  int* order = (int*)(red + 32);       // 64
+
+  // the Hermitian matrix from the stacked real Gram (rows and columns i P + p),
+  // symmetrised
+  const uint32_t K = 2 * n;
+  for (uint32_t idx0 = tid; idx0 < n * n; idx0 += NTS) {
+    const uint32_t i = idx0 / n, j = idx0 - i * n;
+    auto G = [&](uint32_t a, uint32_t b) { return k.gram[(uint64_t)a * K + b]; };
+    const double re1 = G(2 * i, 2 * j) + G(2 * i + 1, 2 * j + 1);
+    const double im1 = G(2 * i + 1, 2 * j) - G(2 * i, 2 * j + 1);
+    const double re2 = G(2 * j, 2 * i) + G(2 * j + 1, 2 * i + 1);
+    const double im2 = G(2 * j + 1, 2 * i) - G(2 * j, 2 * i + 1);
+    Ar[i * LD + j] = 0.5 * (re1 + re2);
+    Ai[i * LD + j] = 0.5 * (im1 - im2);
+    Vr[i * LD + j] = (i == j) ? 1.0 : 0.0;
+    Vi[i * LD + j] = 0.0;
+  }
+  __syncthreads();
+
+  const uint32_t m = n + (n & 1u);
+  const uint32_t half = m / 2;
+  const int blk_a = tid < half * half ? (int)(tid / half) : -1;
+  const int blk_b = tid < half * half ? (int)(tid - (tid / half) * half) : -1;
+  int vb[2];
+  uint32_t vi[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t t = tid + (uint32_t)h * NTS;
+    vb[h] = t < n * half ? (int)(t / n) : -1;
+    vi[h] = t < n * half ? t - (t / n) * n : 0u;
+  }
+  int sweeps = -1;
+  for (int sweep = 0;; ++sweep) {
+    double off = 0.0, tot = 0.0;
+    for (uint32_t idx0 = tid; idx0 < n * n; idx0 += NTS) {
+      const uint32_t i = idx0 / n, j = idx0 - i * n;
+      const double a2 = Ar[i * LD + j] * Ar[i * LD + j] + Ai[i * LD + j] * Ai[i * LD + j];
+      tot += a2;
+      if (i != j) off += a2;
+    }
+    off = wave_sum(off);
+    tot = wave_sum(tot);
+    if (lane == 0) {
+      red[wave] = off;
+      red[16 + wave] = tot;
+    }
+    __syncthreads();
+    off = 0.0;
+    tot = 0.0;
+    for (int w = 0; w < NTS / 64; ++w) {
+      off += red[w];
+      tot += red[16 + w];
+    }
+    if (!(off > 1e-20 * tot)) {
+      sweeps = sweep;
+      break;
+    }
+    if (sweep == MAX_SWEEPS) break;
+
+    for (uint32_t round = 0; round + 1 < m; ++round) {
+      auto pair = [&](uint32_t j, int& p, int& q) {
+        auto player = [&](uint32_t pos) -> uint32_t {
+          if (pos == 0) return 0u;
+          uint32_t x = pos - 1u + round;
+          if (x >= m - 1u) x -= m - 1u;
+          return 1u + x;
+        };
+        const uint32_t x = player(j), y = player(m - 1 - j);
+        const uint32_t lo = x < y ? x : y, hi = x < y ? y : x;
+        p = (int)lo;
+        q = hi < n ? (int)hi : -1;
+      };
+      if (tid < half) {
+        int p, q;
+        pair(tid, p, q);
+        double c = 1.0, sn = 0.0, pc = 1.0, ps = 0.0;
+        if (q >= 0) {
+          const double app = Ar[p * LD + p], aqq = Ar[q * LD + q];
+          const double xr = Ar[p * LD + q], xi = Ai[p * LD + q];
+          const double rr = sqrt(xr * xr + xi * xi);
+          if (rr > 0.0) {
+            const double theta = (aqq - app) / (2.0 * rr);
+            double t;
+            if (fabs(theta) > 1e100) {
+              t = 0.5 / theta;
+            } else {
+              t = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+            }
+            c = 1.0 / sqrt(t * t + 1.0);
+            sn = t * c;
+            pc = xr / rr;
+            ps = xi / rr;
+          }
+        }
+        cs[tid] = make_double4(c, sn, pc, ps);
+      }
+      __syncthreads();
+      if (blk_a >= 0) {
+        const uint32_t a = (uint32_t)blk_a, b = (uint32_t)blk_b;
+        int pa, qa, pb, qb;
+        pair(a, pa, qa);
+        pair(b, pb, qb);
+        const double4 ra4 = cs[a], rb4 = cs[b];
+        const bool ra = qa >= 0 && ra4.y != 0.0, rb = qb >= 0 && rb4.y != 0.0;
+        if (ra || rb) {
+          double x00r = Ar[pa * LD + pb], x00i = Ai[pa * LD + pb];
+          double x01r = qb >= 0 ? Ar[pa * LD + qb] : 0.0, x01i = qb >= 0 ? Ai[pa * LD + qb] : 0.0;
+          double x10r = qa >= 0 ? Ar[qa * LD + pb] : 0.0, x10i = qa >= 0 ? Ai[qa * LD + pb] : 0.0;
+          double x11r = (qa >= 0 && qb >= 0) ? Ar[qa * LD + qb] : 0.0;
+          double x11i = (qa >= 0 && qb >= 0) ? Ai[qa * LD + qb] : 0.0;
+          if (rb) {   // columns pb, qb: y' = e^{-i phi} y, then the rotation
+            const double c = rb4.x, sn = rb4.y, pc = rb4.z, ps = rb4.w;
+            const double y0r = pc * x01r + ps * x01i, y0i = pc * x01i - ps * x01r;
+            const double y1r = pc * x11r + ps * x11i, y1i = pc * x11i - ps * x11r;
+            const double n00r = c * x00r - sn * y0r, n00i = c * x00i - sn * y0i;
+            const double n01r = sn * x00r + c * y0r, n01i = sn * x00i + c * y0i;
+            const double n10r = c * x10r - sn * y1r, n10i = c * x10i - sn * y1i;
+            const double n11r = sn * x10r + c * y1r, n11i = sn * x10i + c * y1i;
+            x00r = n00r; x00i = n00i; x01r = n01r; x01i = n01i;
+            x10r = n10r; x10i = n10i; x11r = n11r; x11i = n11i;
+          }
+          if (ra) {   // rows pa, qa: y' = e^{+i phi} y, then the rotation
+            const double c = ra4.x, sn = ra4.y, pc = ra4.z, ps = ra4.w;
+            const double y0r = pc * x10r - ps * x10i, y0i = pc * x10i + ps * x10r;
+            const double y1r = pc * x11r - ps * x11i, y1i = pc * x11i + ps * x11r;
+            const double n00r = c * x00r - sn * y0r, n00i = c * x00i - sn * y0i;
+            const double n10r = sn * x00r + c * y0r, n10i = sn * x00i + c * y0i;
+            const double n01r = c * x01r - sn * y1r, n01i = c * x01i - sn * y1i;
+            const double n11r = sn * x01r + c * y1r, n11i = sn * x01i + c * y1i;
+            x00r = n00r; x00i = n00i; x10r = n10r; x10i = n10i;
+            x01r = n01r; x01i = n01i; x11r = n11r; x11i = n11i;
+          }
+          Ar[pa * LD + pb] = x00r;
+          Ai[pa * LD + pb] = x00i;
+          if (qb >= 0) {
+            Ar[pa * LD + qb] = x01r;
+            Ai[pa * LD + qb] = x01i;
+          }
+          if (qa >= 0) {
+            Ar[qa * LD + pb] = x10r;
+            Ai[qa * LD + pb] = x10i;
+          }
+          if (qa >= 0 && qb >= 0) {
+            Ar[qa * LD + qb] = x11r;
+            Ai[qa * LD + qb] = x11i;
+          }
+        }
+      }
+      // V <- V J (columns)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (vb[h] < 0) continue;
+        const uint32_t b = (uint32_t)vb[h], i = vi[h];
+        int pb, qb;
+        pair(b, pb, qb);
+        const double4 rb4 = cs[b];
+        if (qb < 0 || rb4.y == 0.0) continue;
+        const double c = rb4.x, sn = rb4.y, pc = rb4.z, ps = rb4.w;
+        const double xr = Vr[i * LD + pb], xi = Vi[i * LD + pb];
+        const double y0r = Vr[i * LD + qb], y0i = Vi[i * LD + qb];
+        const double yr = pc * y0r + ps * y0i, yi = pc * y0i - ps * y0r;
+        Vr[i * LD + pb] = c * xr - sn * yr;
+        Vi[i * LD + pb] = c * xi - sn * yi;
+        Vr[i * LD + qb] = sn * xr + c * yr;
+        Vi[i * LD + qb] = sn * xi + c * yi;
+      }
+      __syncthreads();
+    }
+  }
+
+  if (tid == 0) *k.status = sweeps;
+  // descending order of the diagonal, equal values in index order
+  if (tid < n) {
+    const double d = Ar[tid * LD + tid];
+    uint32_t rank = 0;
+    for (uint32_t j = 0; j < n; ++j) {
+      const double e = Ar[j * LD + j];
+      rank += (e > d || (e == d && j < tid)) ? 1u : 0u;
+    }
+    order[rank] = (int)tid;
+  }
+  __syncthreads();
+  if (tid < n) k.eigvals[tid] = Ar[order[tid] * LD + order[tid]];
+
+  // one wave per selected column: its largest-|.| entry (lowest row on ties) made real
+  // positive by a unit scalar, then U, Mproj (the real form of U^H) and Mrec (of U)
+  const uint32_t r = k.r;
+  for (uint32_t cc = wave; cc < r; cc += NTS / 64) {
+    const uint32_t src = (uint32_t)order[cc];
+    const double xr = lane < n ? Vr[lane * LD + src] : 0.0;
+    const double xi = lane < n ? Vi[lane * LD + src] : 0.0;
+    double best = lane < n ? xr * xr + xi * xi : -1.0;
+    uint32_t bi = lane;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const double ob = __shfl_xor(best, o, 64);
+      const uint32_t oi = __shfl_xor(bi, o, 64);
+      if (ob > best || (ob == best && oi < bi)) {
+        best = ob;
+        bi = oi;
+      }
+    }
+    const double vr = __shfl(xr, bi, 64), vim = __shfl(xi, bi, 64);
+    const double mag = sqrt(vr * vr + vim * vim);
+    const double sr = mag > 0.0 ? vr / mag : 1.0;     // scale = conj(phase)
+    const double si = mag > 0.0 ? -vim / mag : 0.0;
+    if (lane < n) {
+      const uint32_t i = lane;
+      const float ur = (float)(xr * sr - xi * si);
+      const float ui = (float)(xr * si + xi * sr);
+      k.U[((uint64_t)i * r + cc) * 2] = ur;
+      k.U[((uint64_t)i * r + cc) * 2 + 1] = ui;
+      const uint64_t KP = 2ull * n, RP = 2ull * r;
+      k.Mproj[(2 * cc) * KP + 2 * i] = ur;
+      k.Mproj[(2 * cc) * KP + 2 * i + 1] = ui;
+      k.Mproj[(2 * cc + 1) * KP + 2 * i] = -ui;
+      k.Mproj[(2 * cc + 1) * KP + 2 * i + 1] = ur;
+      k.Mrec[(2 * i) * RP + 2 * cc] = ur;
+      k.Mrec[(2 * i) * RP + 2 * cc + 1] = -ui;
+      k.Mrec[(2 * i + 1) * RP + 2 * cc] = ui;
+      k.Mrec[(2 * i + 1) * RP + 2 * cc + 1] = ur;
+    }
+  }
+}
+
+size_t eig_herm_lds(uint32_t I) {
+  const size_t nn = (size_t)I * (I + 1);
+  return (4 * nn + 4 * 32 + 32) * sizeof(double) + 64 * sizeof(int);
 }
 
 // ---------------------------------------------------------------- 64 < I <= 128
@@ -902,18 +912,19 @@ hipError_t launch_eig(const EigArgs* e, int count, hipStream_t s) {
     m.status = e[i].status;
     m.n = e[i].I;
     m.r = e[i].r;
-    const size_t b = big ? eig_big_lds(e[i].I, e[i].P) : eig_lds_bytes(e[i].I, e[i].P);
+    const size_t b = big ? eig_big_lds(e[i].I, e[i].P)
+                         : (cplx ? eig_herm_lds(e[i].I) : eig_lds_bytes(e[i].I, e[i].P));
     size_t& l = big ? lds_b : lds_s;
     if (b > l) l = b;
   }
   if (ns) {
-    auto fn = cplx ? k_eig<true> : k_eig_sym;
+    auto fn = cplx ? k_eig_herm : k_eig_sym;
     if (lds_s > 64 * 1024) {
       hipError_t err = hipFuncSetAttribute((const void*)fn,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_s);
       if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(fn, dim3(ns), dim3(cplx ? NTH : NTS), lds_s, s, ks);
+    hipLaunchKernelGGL(fn, dim3(ns), dim3(NTS), lds_s, s, ks);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
