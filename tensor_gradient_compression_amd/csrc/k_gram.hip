@@ -13,9 +13,10 @@
 // Each workgroup owns a contiguous range of 64-column tiles (split-K). A tile is
 // staged in LDS (fp32; entries in Omega read as zero via the membership bitmask, so
 // the gradient is never modified), v_mfma_f32_16x16x4_f32 accumulates the tile's
-// 64-term sums in fp32, and every tile result is added to fp64 accumulators. Each
-// workgroup writes its fp64 partial; a second kernel sums the partials in a fixed
-// order, so the result is deterministic run to run.
+// 64-term sums in fp32 for the upper-triangle 16 x 16 blocks, and every tile result is
+// added to fp64 accumulators. Each workgroup writes its fp64 partial (both triangles);
+// a second kernel sums the partials in a fixed order, so the result is deterministic
+// run to run.
 #include <algorithm>
 
 #include "tg_common.h"
@@ -39,10 +40,11 @@ struct GK {
   uint32_t A, I, B;
   uint32_t Kin, nb;   // Kin = I*P; nb = ceil(Kin / 16)
   uint32_t TA, wide;
-  uint32_t ob0, ob1;  // the output blocks of this launch: ob0 <= block < ob1 (of nb * nb)
+  uint32_t ob0, ob1;  // the output blocks of this launch: ob0 <= block < ob1 of the
+                      // nb (nb + 1) / 2 upper-triangle blocks (row-major)
 };
 
-// NOB = output 16x16 blocks per wave (nb*nb blocks over 4 waves).
+// NOB = output 16x16 blocks per wave (nb (nb + 1) / 2 blocks over 4 waves).
 template <typename XT, int P, int NOB>
 __global__ void __launch_bounds__(NTH) k_gram(GK k) {
   extern __shared__ float smem[];
@@ -58,10 +60,24 @@ __global__ void __launch_bounds__(NTH) k_gram(GK k) {
   const uint32_t blk = k.I * k.B * P;
   f4 acc[NOB];
   double dacc[NOB][4];
+  // this wave's upper-triangle output blocks (rb <= cb); rb = -1: none
+  int brb[NOB], bcb[NOB];
 #pragma unroll
   for (int q = 0; q < NOB; ++q) {
     acc[q] = f4{0.f, 0.f, 0.f, 0.f};
     for (int v = 0; v < 4; ++v) dacc[q][v] = 0.0;
+    const uint32_t ob = k.ob0 + wave + 4 * q;
+    brb[q] = -1;
+    bcb[q] = 0;
+    if (ob < k.ob1) {
+      uint32_t t = ob, rb = 0;
+      while (t >= k.nb - rb) {
+        t -= k.nb - rb;
+        ++rb;
+      }
+      brb[q] = (int)rb;
+      bcb[q] = (int)(rb + t);
+    }
   }
 
   const uint64_t t0 = (uint64_t)blockIdx.x * k.tiles_per_blk;
@@ -121,9 +137,8 @@ __global__ void __launch_bounds__(NTH) k_gram(GK k) {
       const uint32_t cbase = scol[c];
 #pragma unroll
       for (int q = 0; q < NOB; ++q) {
-        const uint32_t ob = k.ob0 + wave + 4 * q;
-        if (ob < k.ob1) {
-          const uint32_t rb = ob / k.nb, cb = ob - rb * k.nb;
+        if (brb[q] >= 0) {
+          const uint32_t rb = (uint32_t)brb[q], cb = (uint32_t)bcb[q];
           const uint32_t ka = rb * 16 + (lane & 15), kb = cb * 16 + (lane & 15);
           float av = 0.0f, bv = 0.0f;
           if (cv && ka < k.Kin) av = sX[cbase + (ka / P) * rs + (ka % P)];
@@ -139,16 +154,19 @@ __global__ void __launch_bounds__(NTH) k_gram(GK k) {
     }
   }
 
+  // the partial is written symmetric: block (rb, cb) and its transpose
   double* out = k.partial + (uint64_t)blockIdx.x * k.Kin * k.Kin;
 #pragma unroll
   for (int q = 0; q < NOB; ++q) {
-    const uint32_t ob = k.ob0 + wave + 4 * q;
-    if (ob < k.ob1) {
-      const uint32_t rb = ob / k.nb, cb = ob - rb * k.nb;
+    if (brb[q] >= 0) {
+      const uint32_t rb = (uint32_t)brb[q], cb = (uint32_t)bcb[q];
       const uint32_t colj = cb * 16 + (lane & 15);
       for (int v = 0; v < 4; ++v) {
         const uint32_t rowi = rb * 16 + 4 * (lane >> 4) + v;
-        if (rowi < k.Kin && colj < k.Kin) out[rowi * k.Kin + colj] = dacc[q][v];
+        if (rowi < k.Kin && colj < k.Kin) {
+          out[rowi * k.Kin + colj] = dacc[q][v];
+          if (rb != cb) out[colj * k.Kin + rowi] = dacc[q][v];
+        }
       }
     }
   }
@@ -218,7 +236,7 @@ hipError_t gogram(const GK& k, size_t lds, unsigned grid, hipStream_t s) {
 // one re-reading the tiles; each writes its own entries of the same partial sums.
 template <typename XT, int P>
 hipError_t pick_nob(const GK& k, size_t lds, unsigned grid, hipStream_t s) {
-  const uint32_t nblocks = k.nb * k.nb;
+  const uint32_t nblocks = k.nb * (k.nb + 1) / 2;   // upper-triangle blocks
   const uint32_t per_wave = (nblocks + 3) / 4;
   GK kk = k;
   kk.ob0 = 0;
