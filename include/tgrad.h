@@ -143,8 +143,9 @@ typedef struct tgrad_info {
   int64_t state_bytes;      /* moments, core, factors, Omega (optimizer state) */
   int64_t workspace_bytes;  /* transient buffers owned by the handle */
   /* The eigensolver at the last refresh (0 before any): the most Jacobi sweeps any mode
-   * took to reach its off-diagonal bound, and the number of modes that reached the
-   * sweep cap first (their factors are then less accurate than the bound promises). */
+   * took to reach its off-diagonal bound (0 for a mode that the tridiagonal route for
+   * real modes up to 64 served), and the number of modes that reached the sweep cap
+   * first (their factors are then less accurate than the bound promises). */
   int64_t eig_sweeps_max;
   int64_t eig_unconverged;
 } tgrad_info;

@@ -3,21 +3,26 @@
 // U(n) = the r_n leading eigenvectors of the mode-n Gram matrix of the residual
 // (pith.science "What carries the argument": Tucker / higher-order SVD factors U^(n);
 // its appendix M excerpt: the factors are orthonormal, P^T P = I). One workgroup
-// diagonalises one I x I matrix (I <= 64) held in LDS in fp64 with the parallel cyclic
-// Jacobi method: each sweep visits every (p, q) pair once, in I - 1 rounds of disjoint
+// diagonalises one I x I matrix held in LDS in fp64. Real matrices up to 64 take the
+// tridiagonal route (k_eig_tri, below); the Jacobi kernels serve complex matrices, modes
+// wider than 64, and the real matrices the tridiagonal route hands over. The parallel
+// cyclic Jacobi method: each sweep visits every (p, q) pair once, in I - 1 rounds of disjoint
 // pairs (round-robin order); within a round every rotation is computed from the same
 // matrix, then all column updates (A <- A J, V <- V J) and all row updates
 // (A <- J^H A) are applied. Hermitian rotations first turn a_pq real with a phase on
 // column q, then apply the real rotation. Sweeps stop when the off-diagonal energy is
 // below 1e-20 of the total (an off-diagonal norm of 1e-10 of the matrix norm, so an
 // eigenvector errs by about 1e-10 over its relative eigengap), or after MAX_SWEEPS
-// sweeps; each matrix reports the sweeps it took, or -1 when the cap came first.
+// sweeps; each matrix reports the sweeps it took, or -1 when the cap came first (0
+// when the tridiagonal route served it).
 //
 // Outputs (pages silent on eigenvector order, sign and phase): eigenvalues descending
 // (equal values keep index order); each selected column scaled by a unit scalar so its
 // largest-magnitude entry (lowest row on ties) is real positive; U stored fp32, and
 // from those fp32 values the two MFMA operand matrices of the mode products: Mproj
 // ((r*P) x (I*P), the real form of U^H) and Mrec ((I*P) x (r*P), the real form of U).
+#include <algorithm>
+
 #include "tg_common.h"
 
 namespace tg {
@@ -26,6 +31,7 @@ namespace {
 
 constexpr int NTH = 256;
 constexpr int MAX_SWEEPS = 40;
+constexpr int EIG_HANDOFF = -2;   // status of a matrix the tridiagonal route leaves to Jacobi
 
 struct EK1 {
   const double* gram;
@@ -37,8 +43,10 @@ struct EK1 {
   uint32_t n, r;
 };
 // One workgroup per matrix; up to 8 matrices (one per compressed mode) per launch.
+// handoff_only: act only on the matrices whose status is EIG_HANDOFF.
 struct EK {
   EK1 m[8];
+  int handoff_only;
 };
 
 // ---------------------------------------------------------------- real symmetric case
@@ -72,6 +80,7 @@ __device__ __forceinline__ double rsq64(double x) {
 __global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
   extern __shared__ double sm[];
   const EK1& k = kk.m[blockIdx.x];
+  if (kk.handoff_only && *k.status != EIG_HANDOFF) return;   // the same for every thread
   const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t n = k.n;
   const uint32_t LD = n + 1;          // odd row stride: column walks hit distinct banks
@@ -243,6 +252,359 @@ __global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
   for (uint32_t c = wave; c < r; c += NTS / 64) {
     const uint32_t src = (uint32_t)order[c];
     const double x = lane < n ? V[lane * LD + src] : 0.0;
+    double best = lane < n ? x * x : -1.0;
+    uint32_t bi = lane;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const double ob = __shfl_xor(best, off, 64);
+      const uint32_t oi = __shfl_xor(bi, off, 64);
+      if (ob > best || (ob == best && oi < bi)) {
+        best = ob;
+        bi = oi;
+      }
+    }
+    const double vmax = __shfl(x, bi, 64);
+    const double sr = vmax != 0.0 ? (vmax > 0.0 ? 1.0 : -1.0) : 1.0;
+    if (lane < n) {
+      const float u = (float)(x * sr);
+      k.U[(uint64_t)lane * r + c] = u;
+      k.Mproj[(uint64_t)c * n + lane] = u;
+      k.Mrec[(uint64_t)lane * r + c] = u;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- real symmetric, I <= 64
+// Tridiagonal route for real matrices, the default for I <= 64: Householder reduction
+// A = Q T Q^T; all eigenvalues of T by multisection on Sturm counts; the r leading
+// eigenvectors of T by inverse iteration; each brought back to A's basis by the
+// reflectors. Jacobi needs I - 1 workgroup-synchronised rounds per sweep and 8-10
+// sweeps; here only the reduction (I - 2 steps of three barriers) is synchronised, and
+// every later stage runs each eigenvalue or vector on its own lanes without a barrier.
+//
+// Reduction step c (column c below the diagonal, length m = I - 1 - c): the reflector
+// H = I - tau v v^T with v_0 = 1 that maps x = A[c+1:, c] to beta e_1, beta = -sign(x_0)
+// ||x||, tau = (beta - x_0) / beta, v = x / (x_0 - beta) past v_0 (tau = 0 and no step
+// when x is already a multiple of e_1); then the trailing block B <- H B H as the
+// symmetric rank-2 update B - v w^T - w v^T with p = tau B v and w = p - (tau / 2)
+// (p^T v) v. The update keeps B exactly symmetric (both triangles add the same two
+// products).
+//
+// Eigenvalues: the number of eigenvalues of T below x is the number of sign changes in
+// the leading principal minors of T - x I, P_0 = 1, P_1 = d_0 - x, P_k = (d_{k-1} - x)
+// P_{k-1} - e_{k-2}^2 P_{k-2} (Sylvester's law of inertia on T - x I = L D L^T; a zero
+// minor counts with the sign opposite to the one before it). The pair (P_k, P_{k-1}) is
+// rescaled by a power of two every four terms, which keeps every sign. Four lanes own
+// eigenvalue j (ascending): each step they count at the four inner points of a fifth
+// split of the bracket [a, b] (count(a) <= j < count(b), from the Gershgorin interval)
+// and keep the fifth that holds it; 24 steps shrink the bracket by 5^24 > 2^55.
+//
+// Eigenvectors: for each of the r largest eigenvalues (one lane each) two rounds of
+// inverse iteration, (T - lambda I) y = z then z = y / ||y||, from a fixed pseudo-random
+// z: Gaussian elimination with partial pivoting between neighbouring rows (a zero pivot
+// replaced by eps ||T||), the factors kept in LDS for the back substitution. An
+// eigenvalue known to about eps ||T|| makes one round converge already. Inverse
+// iteration leaves eigenvectors of eigenvalues closer than its error bound
+// non-orthogonal: when two of the r leading eigenvalues lie within 1e-9 ||T|| of each
+// other (or any eigenvalue is not a number) the matrix is handed to the Jacobi kernel,
+// which runs after this one and acts only on matrices marked so.
+//
+// The matrix is scaled by a power of two first, so that no product overflows or
+// underflows, and the eigenvalues are scaled back exactly. A zero matrix, or one with an
+// infinite entry, goes to the Jacobi kernel as well.
+constexpr int NTQ = 256;
+constexpr int MS_STEPS = 24;
+constexpr uint32_t LDY = 65;      // row stride of the eigenvectors of T in LDS
+
+__device__ __forceinline__ double wave_max(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ double wave_min(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmin(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// eigenvalues of the tridiagonal (d, e) below x
+__device__ uint32_t sturm_count(const double* d, const double* e, uint32_t n, double x) {
+  double p0 = 1.0, p1 = d[0] - x;
+  bool neg = !(p1 > 0.0);
+  uint32_t cnt = neg ? 1u : 0u;
+  for (uint32_t k = 1; k < n; ++k) {
+    const double ek = e[k - 1];
+    const double p2 = (d[k] - x) * p1 - (ek * ek) * p0;
+    const bool ng = p2 < 0.0 || (p2 == 0.0 && !neg);
+    cnt += (ng != neg) ? 1u : 0u;
+    neg = ng;
+    p0 = p1;
+    p1 = p2;
+    if ((k & 3u) == 3u) {
+      const double mg = fmax(fabs(p0), fabs(p1));
+      if (mg > 0.0 && mg <= 1.7976931348623157e308) {
+        int ex;
+        (void)frexp(mg, &ex);
+        p0 = ldexp(p0, -ex);
+        p1 = ldexp(p1, -ex);
+      }
+    }
+  }
+  return cnt;
+}
+
+// a fixed pseudo-random start vector entry in [-1, 1) for row k of solve c
+__device__ __forceinline__ double start_entry(uint32_t k, uint32_t c) {
+  uint32_t h = k * 0x9E3779B1u + c * 0x85EBCA77u + 0x165667B1u;
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  return (double)h * (1.0 / 4294967296.0) * 2.0 - 1.0;
+}
+
+size_t eig_tri_lds(uint32_t I) {
+  const size_t LD = I | 1u;
+  return (I * LD + 64 * LDY + 4 * 64 * 32 + 6 * 64 + 8) * sizeof(double);
+}
+
+__global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
+  extern __shared__ double sm[];
+  const EK1& k = kk.m[blockIdx.x];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t n = k.n, r = k.r;
+  const uint32_t LD = n | 1u;          // odd row stride: column walks hit distinct banks
+  double* A = sm;                      // n x LD; the reflectors end up below its diagonal
+  double* Y = A + n * LD;              // the eigenvectors (columns), rows of LDY
+  double* W = Y + 64 * LDY;            // elimination rows of 32 solves: W[(4 k + a) 32 + s]
+  double* hv = W + 4 * 64 * 32;        // the current reflector
+  double* pw = hv + 64;                // p = tau B v
+  double* dv = pw + 64;                // T's diagonal
+  double* ev = dv + 64;                // T's off-diagonal
+  double* tv = ev + 64;                // the taus
+  double* lam = tv + 64;               // the eigenvalues, ascending
+  double* red = lam + 64;              // partials; [4], [5]: the Gershgorin interval
+
+  // the power-of-two scale that brings the largest |entry| into [0.5, 1)
+  double mx = 0.0;
+  for (uint32_t q = tid; q < n * n; q += NTQ) mx = fmax(mx, fabs(k.gram[q]));
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+  // a zero matrix (every basis is an eigenbasis) and one with an infinite entry go to
+  // Jacobi: after the scaling every other matrix has a largest eigenvalue magnitude of
+  // at least 1/2, which the pivot floor of the inverse iteration relies on
+  if (!(mx > 0.0 && mx <= 1.7976931348623157e308)) {   // the same for every thread
+    if (tid == 0) *k.status = EIG_HANDOFF;
+    return;
+  }
+  int ex = 0;
+  (void)frexp(mx, &ex);
+  const double scale = ldexp(1.0, -ex);
+  for (uint32_t q = tid; q < n * n; q += NTQ) {
+    const uint32_t i = q / n, j = q - i * n;
+    A[i * LD + j] = (0.5 * (k.gram[(uint64_t)i * n + j] + k.gram[(uint64_t)j * n + i])) * scale;
+  }
+  __syncthreads();
+
+  // Householder reduction to tridiagonal form
+  const uint32_t ri = tid >> 2, part = tid & 3;   // row (or column) and its quarter
+  for (uint32_t c = 0; c + 2 < n; ++c) {
+    const uint32_t m = n - 1 - c, b = c + 1;
+    if (wave == 0) {
+      const double x = lane < m ? A[(b + lane) * LD + c] : 0.0;
+      const double sig = wave_sum(lane >= 1 ? x * x : 0.0);
+      const double x0 = __shfl(x, 0, 64);
+      double tau = 0.0, beta = x0, inv = 0.0;
+      if (sig > 0.0) {
+        const double mu = sqrt(x0 * x0 + sig);
+        beta = x0 <= 0.0 ? mu : -mu;
+        tau = (beta - x0) / beta;
+        inv = 1.0 / (x0 - beta);
+      }
+      const double v = lane == 0 ? 1.0 : x * inv;
+      if (lane < m) {
+        hv[lane] = v;
+        A[(b + lane) * LD + c] = v;
+      }
+      if (lane == 0) {
+        tv[c] = tau;
+        ev[c] = beta;
+        dv[c] = A[c * LD + c];
+      }
+    }
+    __syncthreads();
+    const double tau = tv[c];
+    if (tau == 0.0) continue;   // the same for every thread
+    double sp = 0.0;
+    if (ri < m)
+      for (uint32_t j = part; j < m; j += 4) sp += A[(b + ri) * LD + b + j] * hv[j];
+    sp += __shfl_xor(sp, 1, 64);
+    sp += __shfl_xor(sp, 2, 64);
+    if (ri < m && part == 0) pw[ri] = tau * sp;
+    __syncthreads();
+    const double kd = 0.5 * tau * wave_sum(lane < m ? pw[lane] * hv[lane] : 0.0);
+    if (ri < m) {
+      const double vi = hv[ri], wi = pw[ri] - kd * vi;
+      for (uint32_t j = part; j < m; j += 4) {
+        const double vj = hv[j], wj = pw[j] - kd * vj;
+        A[(b + ri) * LD + b + j] -= vi * wj + wi * vj;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    if (n >= 2) {
+      dv[n - 2] = A[(n - 2) * LD + n - 2];
+      ev[n - 2] = A[(n - 1) * LD + n - 2];
+    }
+    dv[n - 1] = A[(n - 1) * LD + n - 1];
+    ev[n - 1] = 0.0;
+  }
+  __syncthreads();
+
+  // the Gershgorin interval, widened a little
+  if (wave == 0) {
+    const double dl = lane < n ? dv[lane] : 0.0;
+    const double eb = lane < n ? fabs(ev[lane]) : 0.0;
+    const double ea = (lane >= 1 && lane < n) ? fabs(ev[lane - 1]) : 0.0;
+    const double lo = wave_min(lane < n ? dl - ea - eb : 1.7976931348623157e308);
+    const double hi = wave_max(lane < n ? dl + ea + eb : -1.7976931348623157e308);
+    const double pad = 8.881784197001252e-16 * fmax(fabs(lo), fabs(hi)) + 1e-300;
+    if (lane == 0) {
+      red[4] = lo - pad;
+      red[5] = hi + pad;
+    }
+  }
+  __syncthreads();
+
+  // multisection: lanes 4 j .. 4 j + 3 bracket eigenvalue j
+  {
+    const uint32_t j = tid >> 2, q = tid & 3;
+    double a = red[4], b = red[5];
+    for (int step = 0; step < MS_STEPS; ++step) {
+      const double w = b - a;
+      const double x0 = a + w * 0.2, x1 = a + w * 0.4, x2 = a + w * 0.6, x3 = a + w * 0.8;
+      const double xq = q == 0 ? x0 : q == 1 ? x1 : q == 2 ? x2 : x3;
+      const uint32_t cq = sturm_count(dv, ev, n, xq);
+      const uint32_t base = lane & ~3u;
+      const uint32_t c0 = (uint32_t)__shfl((int)cq, (int)base, 64);
+      const uint32_t c1 = (uint32_t)__shfl((int)cq, (int)base + 1, 64);
+      const uint32_t c2 = (uint32_t)__shfl((int)cq, (int)base + 2, 64);
+      const uint32_t c3 = (uint32_t)__shfl((int)cq, (int)base + 3, 64);
+      if (c0 > j) {
+        b = x0;
+      } else if (c1 > j) {
+        a = x0;
+        b = x1;
+      } else if (c2 > j) {
+        a = x1;
+        b = x2;
+      } else if (c3 > j) {
+        a = x2;
+        b = x3;
+      } else {
+        a = x3;
+      }
+    }
+    if (q == 0 && j < n) lam[j] = 0.5 * (a + b);
+  }
+  __syncthreads();
+
+  // hand near-degenerate leading eigenvalues (and non-numbers) to the Jacobi kernel
+  const double nrm = fmax(fabs(lam[0]), fabs(lam[n - 1]));
+  {
+    bool bad = lane < n && !(lam[lane] == lam[lane]);
+    if (lane + 1 < r) {
+      const double gap = lam[n - 1 - lane] - lam[n - 2 - lane];
+      bad = bad || !(gap > 1e-9 * nrm);
+    }
+    if (__ballot(bad) != 0) {   // the same in every wave
+      if (tid == 0) *k.status = EIG_HANDOFF;
+      return;
+    }
+  }
+  if (tid < n) k.eigvals[tid] = ldexp(lam[n - 1 - tid], ex);
+  if (tid == 0) *k.status = 0;
+
+  // inverse iteration, one lane per leading eigenvalue, 32 at a time
+  if (wave == 0) {
+    const double tiny = 2.220446049250313e-16 * fmax(nrm, 0.25);
+    for (uint32_t c0 = 0; c0 < r; c0 += 32) {
+      const uint32_t c = c0 + lane;
+      if (lane < 32 && c < r) {
+        const double lm = lam[n - 1 - c];
+        for (uint32_t i = 0; i < n; ++i) Y[i * LDY + c] = start_entry(i, c);
+        for (int round = 0; round < 2; ++round) {
+          // elimination: the current row (u0, u1, u2 | rc) against row k + 1
+          double u0 = dv[0] - lm, u1 = n > 1 ? ev[0] : 0.0, u2 = 0.0, rc = Y[c];
+          for (uint32_t i = 0; i + 1 < n; ++i) {
+            double n0 = ev[i], n1 = dv[i + 1] - lm, n2 = i + 2 < n ? ev[i + 1] : 0.0;
+            double rn = Y[(i + 1) * LDY + c];
+            if (fabs(n0) > fabs(u0)) {
+              double t;
+              t = u0; u0 = n0; n0 = t;
+              t = u1; u1 = n1; n1 = t;
+              t = u2; u2 = n2; n2 = t;
+              t = rc; rc = rn; rn = t;
+            }
+            if (u0 == 0.0) u0 = tiny;
+            const double iv = rcp64(u0);
+            const double l = n0 * iv;
+            W[(4 * i + 0) * 32 + lane] = iv;
+            W[(4 * i + 1) * 32 + lane] = u1;
+            W[(4 * i + 2) * 32 + lane] = u2;
+            W[(4 * i + 3) * 32 + lane] = rc;
+            u0 = n1 - l * u1;
+            u1 = n2 - l * u2;
+            u2 = 0.0;
+            rc = rn - l * rc;
+          }
+          if (fabs(u0) < tiny) u0 = u0 >= 0.0 ? tiny : -tiny;
+          W[(4 * (n - 1) + 0) * 32 + lane] = rcp64(u0);
+          W[(4 * (n - 1) + 1) * 32 + lane] = 0.0;
+          W[(4 * (n - 1) + 2) * 32 + lane] = 0.0;
+          W[(4 * (n - 1) + 3) * 32 + lane] = rc;
+          // back substitution, then y / ||y||
+          double y1 = 0.0, y2 = 0.0, ss = 0.0;
+          for (uint32_t i = n; i-- > 0;) {
+            const double y = (W[(4 * i + 3) * 32 + lane] - W[(4 * i + 1) * 32 + lane] * y1 -
+                              W[(4 * i + 2) * 32 + lane] * y2) * W[(4 * i + 0) * 32 + lane];
+            Y[i * LDY + c] = y;
+            ss += y * y;
+            y2 = y1;
+            y1 = y;
+          }
+          const double is = ss > 0.0 && ss <= 1.7976931348623157e308 ? rsq64(ss) : 1.0;
+          for (uint32_t i = 0; i < n; ++i) Y[i * LDY + c] *= is;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // back to A's basis: X = H_0 H_1 ... H_{I-3} Y, four lanes per column, no barrier
+  {
+    const uint32_t col = tid >> 2;
+    for (int c = (int)n - 3; c >= 0; --c) {
+      const double tau = tv[c];
+      if (tau == 0.0) continue;
+      const uint32_t b = (uint32_t)c + 1, m = n - 1 - (uint32_t)c;
+      double u = 0.0;
+      if (col < r)
+        for (uint32_t i = part; i < m; i += 4) u += A[(b + i) * LD + c] * Y[(b + i) * LDY + col];
+      u += __shfl_xor(u, 1, 64);
+      u += __shfl_xor(u, 2, 64);
+      u *= tau;
+      if (col < r)
+        for (uint32_t i = part; i < m; i += 4) Y[(b + i) * LDY + col] -= A[(b + i) * LD + c] * u;
+    }
+  }
+  __syncthreads();
+
+  // one wave per selected column: largest |entry| (lowest row on ties) made positive
+  for (uint32_t c = wave; c < r; c += NTQ / 64) {
+    const double x = lane < n ? Y[lane * LDY + c] : 0.0;
     double best = lane < n ? x * x : -1.0;
     uint32_t bi = lane;
 #pragma unroll
@@ -897,9 +1259,9 @@ hipError_t launch_eig(const EigArgs* e, int count, hipStream_t s) {
   if (count < 1 || count > 8) return hipErrorInvalidValue;
   const bool cplx = e[0].P == 2;
   // matrices up to 64 on the LDS-resident kernels, larger ones (up to 128) on k_eig_big
-  EK ks, kb;
+  EK ks{}, kb{};
   int ns = 0, nb = 0;
-  size_t lds_s = 0, lds_b = 0;
+  size_t lds_s = 0, lds_b = 0, lds_j = 0;
   for (int i = 0; i < count; ++i) {
     if (e[i].I > 128 || e[i].r > e[i].I || e[i].r < 1 || e[i].P != e[0].P) return hipErrorInvalidValue;
     const bool big = e[i].I > 64;
@@ -913,30 +1275,35 @@ hipError_t launch_eig(const EigArgs* e, int count, hipStream_t s) {
     m.n = e[i].I;
     m.r = e[i].r;
     const size_t b = big ? eig_big_lds(e[i].I, e[i].P)
-                         : (cplx ? eig_herm_lds(e[i].I) : eig_lds_bytes(e[i].I, e[i].P));
+                         : (cplx ? eig_herm_lds(e[i].I) : eig_tri_lds(e[i].I));
     size_t& l = big ? lds_b : lds_s;
     if (b > l) l = b;
+    if (!big && !cplx) lds_j = std::max(lds_j, eig_lds_bytes(e[i].I, 1));
   }
-  if (ns) {
-    auto fn = cplx ? k_eig_herm : k_eig_sym;
-    if (lds_s > 64 * 1024) {
+  auto go = [&](auto fn, int nm, int nt, size_t lds, const EK& args) -> hipError_t {
+    if (lds > 64 * 1024) {
       hipError_t err = hipFuncSetAttribute((const void*)fn,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_s);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(fn, dim3(ns), dim3(NTS), lds_s, s, ks);
-    hipError_t err = hipGetLastError();
+    hipLaunchKernelGGL(fn, dim3(nm), dim3(nt), lds, s, args);
+    return hipGetLastError();
+  };
+  if (ns && cplx) {
+    hipError_t err = go(k_eig_herm, ns, NTS, lds_s, ks);
+    if (err != hipSuccess) return err;
+  } else if (ns) {
+    // the tridiagonal route, then Jacobi on the matrices it handed over
+    hipError_t err = go(k_eig_tri, ns, NTQ, lds_s, ks);
+    if (err != hipSuccess) return err;
+    EK kj = ks;
+    kj.handoff_only = 1;
+    err = go(k_eig_sym, ns, NTS, lds_j, kj);
     if (err != hipSuccess) return err;
   }
   if (nb) {
-    auto fn = cplx ? k_eig_big<true> : k_eig_big<false>;
-    if (lds_b > 64 * 1024) {
-      hipError_t err = hipFuncSetAttribute((const void*)fn,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_b);
-      if (err != hipSuccess) return err;
-    }
-    hipLaunchKernelGGL(fn, dim3(nb), dim3(NTB), lds_b, s, kb);
-    hipError_t err = hipGetLastError();
+    hipError_t err = cplx ? go(k_eig_big<true>, nb, NTB, lds_b, kb)
+                          : go(k_eig_big<false>, nb, NTB, lds_b, kb);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;

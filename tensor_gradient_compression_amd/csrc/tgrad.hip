@@ -10,7 +10,8 @@
 //   one applying W <- round(W * decay - lr * (Delta_L + lambda N_S at Omega)).
 // Refresh: top-k -> Omega (+ bitmask, ranks) -> per compressed mode: Gram of the
 //   residual (the gradient read with Omega's entries cleared in the staged tiles) ->
-//   Jacobi eigensolver -> U(n) and operand matrices.
+//   eigensolver (tridiagonal route for real modes up to 64, else Jacobi) -> U(n) and
+//   operand matrices.
 #include <algorithm>
 #include <cmath>
 #include <mutex>
@@ -686,7 +687,7 @@ const char* tgrad_kernel_name(int id) {
       "topk_init", "topk_hist", "topk_select", "topk_count", "topk_scan", "topk_compact",
       "mask_from_omega", "gather_residual", "modeprod_project", "adam_fused",
       "modeprod_reconstruct", "modeprod_reconstruct_apply", "apply_dense", "gram",
-      "gram_reduce", "eig_jacobi", "fill", "modeprod_project_first",
+      "gram_reduce", "eigensolver", "fill", "modeprod_project_first",
       "modeprod2_project_first", "modeprod2_reconstruct_apply", "modeprod2_reconstruct",
       "remap_moments", "modeprod3_project_first", "gram3_tail", "modeprod_pair_project",
       "modeprod_pair_reconstruct", "modeprod3_reconstruct_apply", "streamprod_project",

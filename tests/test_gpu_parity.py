@@ -593,7 +593,7 @@ def test_timing_records_every_kernel():
     rec = lib.timing_read()
     for name in ("topk_hist", "topk_compact", "modeprod2_project_first",
                  "modeprod_pair_project", "adam_fused", "modeprod_pair_reconstruct",
-                 "modeprod2_reconstruct_apply", "gram", "eig_jacobi"):
+                 "modeprod2_reconstruct_apply", "gram", "eigensolver"):
         assert name in rec, name
     assert "gather_residual" not in rec        # folded into the fused first projection
     assert "modeprod_project" not in rec       # modes 1 and 0 in one launch
@@ -632,7 +632,7 @@ def test_launch_record_matches_the_launches():
     W = dev(init_weights(wl), wl.dtype)
     lib.step(W, dev(gs.next(), wl.dtype))          # t = 1 refreshes
     names = [n for n, *_ in lib.last_launches()]
-    assert names[:3] == ["topk_hist", "topk_count", "topk_compact"] and "eig_jacobi" in names
+    assert names[:3] == ["topk_hist", "topk_count", "topk_compact"] and "eigensolver" in names
     lib.timing_enable(True)
     lib.step(W, dev(gs.next(), wl.dtype))
     rec = lib.timing_read()
