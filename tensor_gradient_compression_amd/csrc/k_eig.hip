@@ -293,11 +293,11 @@ __global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
 // Eigenvalues: the number of eigenvalues of T below x is the number of sign changes in
 // the leading principal minors of T - x I, P_0 = 1, P_1 = d_0 - x, P_k = (d_{k-1} - x)
 // P_{k-1} - e_{k-2}^2 P_{k-2} (Sylvester's law of inertia on T - x I = L D L^T; a zero
-// minor counts with the sign opposite to the one before it). The pair (P_k, P_{k-1}) is
-// rescaled by a power of two every four terms, which keeps every sign. Four lanes own
-// eigenvalue j (ascending): each step they count at the four inner points of a fifth
+// minor is taken as a tiny negative one, a zero pivot counting as negative). The pair
+// (P_k, P_{k-1}) is rescaled by a power of two every four terms, which keeps every sign. Sixteen lanes own
+// eigenvalue j (ascending): each step they count at the sixteen inner points of a 17-part
 // split of the bracket [a, b] (count(a) <= j < count(b), from the Gershgorin interval)
-// and keep the fifth that holds it; 24 steps shrink the bracket by 5^24 > 2^55.
+// and keep the part that holds it; 14 steps shrink the bracket by 17^14 > 2^57.
 //
 // Eigenvectors: for each of the r largest eigenvalues (one lane each) two rounds of
 // inverse iteration, (T - lambda I) y = z then z = y / ||y||, from a fixed pseudo-random
@@ -312,8 +312,9 @@ __global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
 // The matrix is scaled by a power of two first, so that no product overflows or
 // underflows, and the eigenvalues are scaled back exactly. A zero matrix, or one with an
 // infinite entry, goes to the Jacobi kernel as well.
-constexpr int NTQ = 256;
-constexpr int MS_STEPS = 24;
+constexpr int NTQ = 1024;
+constexpr uint32_t QP = NTQ / 64;   // lanes per row, column or eigenvalue
+constexpr int MS_STEPS = 14;        // (QP + 1)^14 > 2^57
 constexpr uint32_t LDY = 65;      // row stride of the eigenvectors of T in LDS
 
 __device__ __forceinline__ double wave_max(double v) {
@@ -327,28 +328,28 @@ __device__ __forceinline__ double wave_min(double v) {
   return v;
 }
 
-// eigenvalues of the tridiagonal (d, e) below x
-__device__ uint32_t sturm_count(const double* d, const double* e, uint32_t n, double x) {
-  double p0 = 1.0, p1 = d[0] - x;
-  bool neg = !(p1 > 0.0);
-  uint32_t cnt = neg ? 1u : 0u;
-  for (uint32_t k = 1; k < n; ++k) {
-    const double ek = e[k - 1];
-    const double p2 = (d[k] - x) * p1 - (ek * ek) * p0;
-    const bool ng = p2 < 0.0 || (p2 == 0.0 && !neg);
-    cnt += (ng != neg) ? 1u : 0u;
-    neg = ng;
-    p0 = p1;
-    p1 = p2;
-    if ((k & 3u) == 3u) {
-      const double mg = fmax(fabs(p0), fabs(p1));
-      if (mg > 0.0 && mg <= 1.7976931348623157e308) {
-        int ex;
-        (void)frexp(mg, &ex);
-        p0 = ldexp(p0, -ex);
-        p1 = ldexp(p1, -ex);
-      }
+// eigenvalues of the tridiagonal (d, e) below x, from de[k] = (d_k, e_{k-1}^2) in LDS,
+// padded past k = I - 1 up to a multiple of four terms with (above the Gershgorin
+// interval, 0), which leave every sign as it is. A zero minor is replaced by -2^-1000
+// (a zero pivot counts as negative), and sign changes are counted from the sign bits.
+__device__ uint32_t sturm_count(const double2* de, uint32_t nt, double x) {
+  double p0 = 1.0, p1 = de[0].x - x;
+  p1 = p1 == 0.0 ? -9.332636185032189e-302 : p1;
+  uint32_t cnt = (uint32_t)(__builtin_bit_cast(uint64_t, p1) >> 63);
+  for (uint32_t k0 = 1; k0 < nt; k0 += 4) {
+#pragma unroll
+    for (uint32_t u = 0; u < 4; ++u) {
+      const double2 t = de[k0 + u];
+      double p2 = (t.x - x) * p1 - t.y * p0;
+      p2 = p2 == 0.0 ? -9.332636185032189e-302 : p2;
+      cnt += (uint32_t)((__builtin_bit_cast(uint64_t, p2) ^ __builtin_bit_cast(uint64_t, p1)) >> 63);
+      p0 = p1;
+      p1 = p2;
     }
+    int ex;
+    (void)frexp(fmax(fabs(p0), fabs(p1)), &ex);
+    p0 = ldexp(p0, -ex);
+    p1 = ldexp(p1, -ex);
   }
   return cnt;
 }
@@ -364,7 +365,7 @@ __device__ __forceinline__ double start_entry(uint32_t k, uint32_t c) {
 
 size_t eig_tri_lds(uint32_t I) {
   const size_t LD = I | 1u;
-  return (I * LD + 64 * LDY + 4 * 64 * 32 + 6 * 64 + 8) * sizeof(double);
+  return (I * LD + 64 * LDY + 4 * 64 * 32 + 6 * 64 + 24 + 2 * 68) * sizeof(double);
 }
 
 __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
@@ -382,7 +383,8 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
   double* ev = dv + 64;                // T's off-diagonal
   double* tv = ev + 64;                // the taus
   double* lam = tv + 64;               // the eigenvalues, ascending
-  double* red = lam + 64;              // partials; [4], [5]: the Gershgorin interval
+  double* red = lam + 64;              // wave partials; [16], [17]: the Gershgorin interval
+  double2* de = (double2*)(red + 24);  // (d_k, e_{k-1}^2), padded to 1 + 4 ceil((I - 1) / 4)
 
   // the power-of-two scale that brings the largest |entry| into [0.5, 1)
   double mx = 0.0;
@@ -390,7 +392,8 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
   mx = wave_max(mx);
   if (lane == 0) red[wave] = mx;
   __syncthreads();
-  mx = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+  mx = red[0];
+  for (uint32_t w = 1; w < NTQ / 64; ++w) mx = fmax(mx, red[w]);
   // a zero matrix (every basis is an eigenbasis) and one with an infinite entry go to
   // Jacobi: after the scaling every other matrix has a largest eigenvalue magnitude of
   // at least 1/2, which the pivot floor of the inverse iteration relies on
@@ -408,7 +411,7 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
   __syncthreads();
 
   // Householder reduction to tridiagonal form
-  const uint32_t ri = tid >> 2, part = tid & 3;   // row (or column) and its quarter
+  const uint32_t ri = tid / QP, part = tid % QP;   // row (or column) and its share
   for (uint32_t c = 0; c + 2 < n; ++c) {
     const uint32_t m = n - 1 - c, b = c + 1;
     if (wave == 0) {
@@ -419,8 +422,8 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
       if (sig > 0.0) {
         const double mu = sqrt(x0 * x0 + sig);
         beta = x0 <= 0.0 ? mu : -mu;
-        tau = (beta - x0) / beta;
-        inv = 1.0 / (x0 - beta);
+        tau = (beta - x0) * rcp64(beta);
+        inv = rcp64(x0 - beta);
       }
       const double v = lane == 0 ? 1.0 : x * inv;
       if (lane < m) {
@@ -438,15 +441,15 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
     if (tau == 0.0) continue;   // the same for every thread
     double sp = 0.0;
     if (ri < m)
-      for (uint32_t j = part; j < m; j += 4) sp += A[(b + ri) * LD + b + j] * hv[j];
-    sp += __shfl_xor(sp, 1, 64);
-    sp += __shfl_xor(sp, 2, 64);
+      for (uint32_t j = part; j < m; j += QP) sp += A[(b + ri) * LD + b + j] * hv[j];
+#pragma unroll
+    for (uint32_t o = 1; o < QP; o <<= 1) sp += __shfl_xor(sp, (int)o, 64);
     if (ri < m && part == 0) pw[ri] = tau * sp;
     __syncthreads();
     const double kd = 0.5 * tau * wave_sum(lane < m ? pw[lane] * hv[lane] : 0.0);
     if (ri < m) {
       const double vi = hv[ri], wi = pw[ri] - kd * vi;
-      for (uint32_t j = part; j < m; j += 4) {
+      for (uint32_t j = part; j < m; j += QP) {
         const double vj = hv[j], wj = pw[j] - kd * vj;
         A[(b + ri) * LD + b + j] -= vi * wj + wi * vj;
       }
@@ -472,40 +475,31 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
     const double hi = wave_max(lane < n ? dl + ea + eb : -1.7976931348623157e308);
     const double pad = 8.881784197001252e-16 * fmax(fabs(lo), fabs(hi)) + 1e-300;
     if (lane == 0) {
-      red[4] = lo - pad;
-      red[5] = hi + pad;
+      red[16] = lo - pad;
+      red[17] = hi + pad;
     }
+    const double ep = (lane >= 1 && lane < n) ? ev[lane - 1] : 0.0;
+    de[lane] = make_double2(lane < n ? dl : hi + pad + 1.0, ep * ep);
+    if (lane < 4) de[64 + lane] = make_double2(hi + pad + 1.0, 0.0);
   }
   __syncthreads();
 
-  // multisection: lanes 4 j .. 4 j + 3 bracket eigenvalue j
+  // multisection: lanes QP j .. QP j + QP - 1 bracket eigenvalue j
   {
-    const uint32_t j = tid >> 2, q = tid & 3;
-    double a = red[4], b = red[5];
-    for (int step = 0; step < MS_STEPS; ++step) {
+    const uint32_t j = tid / QP, q = tid % QP, base = lane & ~(QP - 1);
+    const uint32_t nt = 1 + 4 * ((n + 2) / 4);   // terms: 1, then groups of four
+    const double step = 1.0 / (double)(QP + 1);
+    double a = red[16], b = red[17];
+    for (int it = 0; it < MS_STEPS; ++it) {
       const double w = b - a;
-      const double x0 = a + w * 0.2, x1 = a + w * 0.4, x2 = a + w * 0.6, x3 = a + w * 0.8;
-      const double xq = q == 0 ? x0 : q == 1 ? x1 : q == 2 ? x2 : x3;
-      const uint32_t cq = sturm_count(dv, ev, n, xq);
-      const uint32_t base = lane & ~3u;
-      const uint32_t c0 = (uint32_t)__shfl((int)cq, (int)base, 64);
-      const uint32_t c1 = (uint32_t)__shfl((int)cq, (int)base + 1, 64);
-      const uint32_t c2 = (uint32_t)__shfl((int)cq, (int)base + 2, 64);
-      const uint32_t c3 = (uint32_t)__shfl((int)cq, (int)base + 3, 64);
-      if (c0 > j) {
-        b = x0;
-      } else if (c1 > j) {
-        a = x0;
-        b = x1;
-      } else if (c2 > j) {
-        a = x1;
-        b = x2;
-      } else if (c3 > j) {
-        a = x2;
-        b = x3;
-      } else {
-        a = x3;
-      }
+      const uint32_t cq = sturm_count(de, nt, a + w * ((double)(q + 1) * step));
+      // the first point of the group whose count passes j
+      const uint64_t hit = (__ballot(cq > j) >> base) & ((1ull << QP) - 1);
+      const uint32_t f = hit ? (uint32_t)__builtin_ctzll(hit) : QP;
+      const double na = f == 0 ? a : a + w * ((double)f * step);
+      const double nb = f == QP ? b : a + w * ((double)(f + 1) * step);
+      a = na;
+      b = nb;
     }
     if (q == 0 && j < n) lam[j] = 0.5 * (a + b);
   }
@@ -583,21 +577,41 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
   }
   __syncthreads();
 
-  // back to A's basis: X = H_0 H_1 ... H_{I-3} Y, four lanes per column, no barrier
+  // back to A's basis: X = H_0 H_1 ... H_{I-3} Y, QP lanes per column, no barrier
   {
-    const uint32_t col = tid >> 2;
+    // rows part + QP t of column tid / QP in registers
+    constexpr int NR = 64 / QP;
+    const uint32_t col = tid / QP;
+    const bool act = col < r;
+    double yv[NR];
+#pragma unroll
+    for (int t = 0; t < NR; ++t) {
+      const uint32_t row = part + QP * t;
+      yv[t] = (act && row < n) ? Y[row * LDY + col] : 0.0;
+    }
     for (int c = (int)n - 3; c >= 0; --c) {
       const double tau = tv[c];
-      if (tau == 0.0) continue;
-      const uint32_t b = (uint32_t)c + 1, m = n - 1 - (uint32_t)c;
-      double u = 0.0;
-      if (col < r)
-        for (uint32_t i = part; i < m; i += 4) u += A[(b + i) * LD + c] * Y[(b + i) * LDY + col];
-      u += __shfl_xor(u, 1, 64);
-      u += __shfl_xor(u, 2, 64);
+      if (tau == 0.0) continue;   // the same for every thread
+      const uint32_t b = (uint32_t)c + 1;
+      double vv[NR], u = 0.0;
+#pragma unroll
+      for (int t = 0; t < NR; ++t) {
+        const uint32_t row = part + QP * t;
+        const double v = A[(row < n ? row : n - 1) * LD + c];
+        vv[t] = (row >= b && row < n) ? v : 0.0;
+      }
+#pragma unroll
+      for (int t = 0; t < NR; ++t) u += vv[t] * yv[t];
+#pragma unroll
+      for (uint32_t o = 1; o < QP; o <<= 1) u += __shfl_xor(u, (int)o, 64);
       u *= tau;
-      if (col < r)
-        for (uint32_t i = part; i < m; i += 4) Y[(b + i) * LDY + col] -= A[(b + i) * LD + c] * u;
+#pragma unroll
+      for (int t = 0; t < NR; ++t) yv[t] -= vv[t] * u;
+    }
+#pragma unroll
+    for (int t = 0; t < NR; ++t) {
+      const uint32_t row = part + QP * t;
+      if (act && row < n) Y[row * LDY + col] = yv[t];
     }
   }
   __syncthreads();
