@@ -313,7 +313,8 @@ __global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
 // underflows, and the eigenvalues are scaled back exactly. A zero matrix, or one with an
 // infinite entry, goes to the Jacobi kernel as well.
 constexpr int NTQ = 1024;
-constexpr uint32_t QP = NTQ / 64;   // lanes per row, column or eigenvalue
+constexpr uint32_t QP = NTQ / 64;   // lanes per row, column or eigenvalue (one DPP row)
+static_assert(QP == 16, "the row reductions span 16 lanes");
 constexpr int MS_STEPS = 14;        // (QP + 1)^14 > 2^57
 constexpr uint32_t LDY = 65;      // row stride of the eigenvectors of T in LDS
 
@@ -326,6 +327,35 @@ __device__ __forceinline__ double wave_min(double v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmin(v, __shfl_xor(v, off, 64));
   return v;
+}
+
+// Reductions over a row of 16 lanes by data-parallel-primitive moves (quad butterflies,
+// then the half-row and row mirrors): every lane of the row ends with the same sum, added
+// in the same order. A wave's total adds the four row sums read from lanes 0, 16, 32, 48.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double row16_sum(double v) {
+  v += dpp_f64<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+  v += dpp_f64<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+  v += dpp_f64<0x141>(v);   // row_half_mirror
+  v += dpp_f64<0x140>(v);   // row_mirror
+  return v;
+}
+__device__ __forceinline__ double lane_value(double v, int at) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, at);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), at);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double wave_total(double v) {
+  v = row16_sum(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
 // eigenvalues of the tridiagonal (d, e) below x, from de[k] = (d_k, e_{k-1}^2) in LDS,
@@ -374,7 +404,9 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
   const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t n = k.n, r = k.r;
   const uint32_t LD = n | 1u;          // odd row stride: column walks hit distinct banks
-  double* A = sm;                      // n x LD; the reflectors end up below its diagonal
+  double2* de = (double2*)sm;          // (d_k, e_{k-1}^2), padded to 1 + 4 ceil((I - 1) / 4)
+                                       // (first: 16-byte reads need 16-byte alignment)
+  double* A = sm + 2 * 68;             // n x LD; the reflectors end up below its diagonal
   double* Y = A + n * LD;              // the eigenvectors (columns), rows of LDY
   double* W = Y + 64 * LDY;            // elimination rows of 32 solves: W[(4 k + a) 32 + s]
   double* hv = W + 4 * 64 * 32;        // the current reflector
@@ -384,7 +416,6 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
   double* tv = ev + 64;                // the taus
   double* lam = tv + 64;               // the eigenvalues, ascending
   double* red = lam + 64;              // wave partials; [16], [17]: the Gershgorin interval
-  double2* de = (double2*)(red + 24);  // (d_k, e_{k-1}^2), padded to 1 + 4 ceil((I - 1) / 4)
 
   // the power-of-two scale that brings the largest |entry| into [0.5, 1)
   double mx = 0.0;
@@ -416,8 +447,8 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
     const uint32_t m = n - 1 - c, b = c + 1;
     if (wave == 0) {
       const double x = lane < m ? A[(b + lane) * LD + c] : 0.0;
-      const double sig = wave_sum(lane >= 1 ? x * x : 0.0);
-      const double x0 = __shfl(x, 0, 64);
+      const double sig = wave_total(lane >= 1 ? x * x : 0.0);
+      const double x0 = lane_value(x, 0);
       double tau = 0.0, beta = x0, inv = 0.0;
       if (sig > 0.0) {
         const double mu = sqrt(x0 * x0 + sig);
@@ -442,11 +473,10 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
     double sp = 0.0;
     if (ri < m)
       for (uint32_t j = part; j < m; j += QP) sp += A[(b + ri) * LD + b + j] * hv[j];
-#pragma unroll
-    for (uint32_t o = 1; o < QP; o <<= 1) sp += __shfl_xor(sp, (int)o, 64);
+    sp = row16_sum(sp);
     if (ri < m && part == 0) pw[ri] = tau * sp;
     __syncthreads();
-    const double kd = 0.5 * tau * wave_sum(lane < m ? pw[lane] * hv[lane] : 0.0);
+    const double kd = 0.5 * tau * wave_total(lane < m ? pw[lane] * hv[lane] : 0.0);
     if (ri < m) {
       const double vi = hv[ri], wi = pw[ri] - kd * vi;
       for (uint32_t j = part; j < m; j += QP) {
@@ -602,9 +632,7 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
       }
 #pragma unroll
       for (int t = 0; t < NR; ++t) u += vv[t] * yv[t];
-#pragma unroll
-      for (uint32_t o = 1; o < QP; o <<= 1) u += __shfl_xor(u, (int)o, 64);
-      u *= tau;
+      u = row16_sum(u) * tau;
 #pragma unroll
       for (int t = 0; t < NR; ++t) yv[t] -= vv[t] * u;
     }
