@@ -218,6 +218,20 @@ int tgrad_set_fusion(tgrad_t *h, int enable);
  * takes effect at the next refresh. */
 int tgrad_set_gram_fusion(tgrad_t *h, int enable);
 
+/* Test / benchmark hook: when the COO gather is folded into the first projection launch
+ * and further launches follow it, the Adam update of the k sparse values (the
+ * nullthought summary, section 3: S and the low-rank core keep separate Adam states)
+ * runs on a second stream that the handle owns (created by tgrad_init, default
+ * priority). It waits for the first projection launch, overlaps the projection's later
+ * launches and the core's Adam update, and the caller's stream waits for it before the
+ * reconstruction, so the call stays ordered on the caller's stream. The update is
+ * element-wise: results are bit-identical either way. The fork and the join cost
+ * about 10 us a step, so enable = 1 (the default) selects it only when the sparse part
+ * holds at least 2^22 values (k, times 2 for complex data); 2 selects it whenever it
+ * applies; 0 runs both updates in one launch on the caller's stream. Its launch is
+ * named adam_sparse (tgrad_kernel_name); takes effect at the next step. */
+int tgrad_set_adam_overlap(tgrad_t *h, int enable);
+
 /* Test / benchmark hook: with the fused launch plan, two neighbouring compressed modes
  * ahead of the trailing ones (the projection's last two products, the reconstruction's
  * first two) run as one launch. The tensor between the two products is never written

@@ -85,6 +85,7 @@ SIGNATURES = [
     ("tgrad_set_fusion", ctypes.c_int, [_P, ctypes.c_int]),
     ("tgrad_set_gram_fusion", ctypes.c_int, [_P, ctypes.c_int]),
     ("tgrad_set_pair_fusion", ctypes.c_int, [_P, ctypes.c_int]),
+    ("tgrad_set_adam_overlap", ctypes.c_int, [_P, ctypes.c_int]),
     ("tgrad_set_stream_products", ctypes.c_int, [_P, ctypes.c_int]),
     ("tgrad_default_options", None, [ctypes.POINTER(Options)]),
     ("tgrad_set_options", ctypes.c_int, [_P, ctypes.POINTER(Options)]),
@@ -353,6 +354,14 @@ class TGrad:
             return False
         self._check(rc, "tgrad_set_gram_fusion")
         return True
+
+    def set_adam_overlap(self, enable) -> None:
+        """Where the sparse values' Adam update runs: on the handle's second stream,
+        beside the projection's later launches, when the sparse part is large (1, the
+        default), whenever that applies (2), or in one launch with the core's update on
+        the caller's stream (0). Results are bit-identical."""
+        self._check(self._lib.tgrad_set_adam_overlap(self._h, int(enable)),
+                    "tgrad_set_adam_overlap")
 
     def set_pair_fusion(self, enable) -> bool:
         """Select one launch for two neighbouring leading modes of the fused plan (True)

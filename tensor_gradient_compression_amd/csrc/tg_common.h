@@ -62,7 +62,7 @@ enum KernelId {
   KID_EIG, KID_FILL, KID_PROJECT_FIRST, KID_PROJECT_FUSED2, KID_RECON_FUSED2_APPLY,
   KID_RECON_FUSED2, KID_REMAP, KID_PROJECT_FUSED3, KID_GRAM3, KID_PROJECT_PAIR, KID_RECON_PAIR,
   KID_RECON_FUSED3_APPLY, KID_STREAM_PROJECT, KID_STREAM_RECONSTRUCT, KID_CSPLIT_OPERAND,
-  KID_CSPLIT_COMBINE, KID_ROW_PROJECT, KID_ROW_RECON_APPLY, KID_COUNT_
+  KID_CSPLIT_COMBINE, KID_ROW_PROJECT, KID_ROW_RECON_APPLY, KID_ADAM_SPARSE, KID_COUNT_
 };
 
 // ---------------------------------------------------------------- launchers

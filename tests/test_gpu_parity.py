@@ -624,23 +624,32 @@ def test_launch_record_matches_the_launches():
     mode product reads its input once and writes its output once (fp32), the gather reads
     k indices and k values and writes k fp32 values and k zeros, Adam moves 24 B per core
     and sparse value, the last product also reads and writes W and reads the k indices
-    and sparse updates."""
+    and sparse updates. With the sparse values' Adam update on the second stream (the
+    default, when the first projection takes the gather) it is its own launch,
+    adam_sparse, right after that first projection, and adam_fused covers the core."""
     wl = F32_32x32x16x16
-    lib = make_lib(wl)
-    assert lib.set_fusion(False)
-    gs = GradStream(wl)
-    W = dev(init_weights(wl), wl.dtype)
-    lib.step(W, dev(gs.next(), wl.dtype))          # t = 1 refreshes
-    names = [n for n, *_ in lib.last_launches()]
-    assert names[:3] == ["topk_hist", "topk_count", "topk_compact"] and "eigensolver" in names
-    lib.timing_enable(True)
-    lib.step(W, dev(gs.next(), wl.dtype))
-    rec = lib.timing_read()
-    got = lib.last_launches()
-    counts = {}
-    for n, *_ in got:
-        counts[n] = counts.get(n, 0) + 1
-    assert counts == {n: c for n, (c, _) in rec.items()}
+    for overlap in (2, 0):
+        lib = make_lib(wl)
+        assert lib.set_fusion(False)
+        lib.set_adam_overlap(overlap)
+        gs = GradStream(wl)
+        W = dev(init_weights(wl), wl.dtype)
+        lib.step(W, dev(gs.next(), wl.dtype))          # t = 1 refreshes
+        names = [n for n, *_ in lib.last_launches()]
+        assert names[:3] == ["topk_hist", "topk_count", "topk_compact"] and "eigensolver" in names
+        lib.timing_enable(True)
+        lib.step(W, dev(gs.next(), wl.dtype))
+        rec = lib.timing_read()
+        got = lib.last_launches()
+        counts = {}
+        for n, *_ in got:
+            counts[n] = counts.get(n, 0) + 1
+        assert counts == {n: c for n, (c, _) in rec.items()}
+        _check_launch_record(wl, got, overlap)
+        lib.close()
+
+
+def _check_launch_record(wl, got, overlap):
     N, k, es = wl.numel, wl.k, 4
     shape, ranks = list(wl.shape), list(wl.ranks)
 
@@ -668,10 +677,13 @@ def test_launch_record_matches_the_launches():
             name = "rowprod_project"
         gb = 8 * k if (j == 0 and row_gather) else 0
         exp.append((name, size * 4 + out * 4 + gb, 2 * (size // cur[n]) * cur[n] * ranks[n]))
+        if j == 0 and row_gather and overlap == 2:
+            exp.append(("adam_sparse", k * 24, 0))
         cur[n] = ranks[n]
         size = out
     ncore = size
-    exp.append(("adam_fused", (ncore + k) * 24, 0))
+    forked = row_gather and overlap == 2
+    exp.append(("adam_fused", (ncore + (0 if forked else k)) * 24, 0))
     for j, n in enumerate([0, 1, 2, 3]):
         out = size // cur[n] * shape[n]
         last = j == 3

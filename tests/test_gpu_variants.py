@@ -462,3 +462,47 @@ def test_lowrank_first_independent_run():
         Wo = orc.step(Wo, g)
     torch.cuda.synchronize()
     weight_check(host(W, wl.dtype), Wo, wl.dtype, "lowrank-first run")
+
+
+# --------------------------------------------------------------------------- sparse Adam on a second stream
+
+OVERLAP_CASES = [
+    ("fp32-32x32x16x16", F32_32x32x16x16),
+    ("bf16-slab3", custom((4, 3, 48, 48, 25), "bf16", (3, 2, 24, 24, 13), 0.05,
+                          signal_ranks=(2, 2, 12, 12, 6))),
+    ("c64-small", custom((12, 10, 9), "c64", (5, 4, 3), 0.05)),
+    ("f16-one-mode", custom((16, 24, 64, 64), "f16", (8, 12, 32, 32), 0.05)),
+]
+
+
+@pytest.mark.parametrize("name,wl", OVERLAP_CASES, ids=[c[0] for c in OVERLAP_CASES])
+def test_adam_overlap_is_bitwise_identical(name, wl):
+    """The sparse values' Adam update on the handle's second stream gives
+    the same weights, moments, Omega and factors bit for bit as both updates in one
+    launch on the caller's stream, over steps that cross a refresh; and the run matches
+    the oracle to the weight bar."""
+    gs = GradStream(wl, seed=11)
+    grads = [gs.next() for _ in range(7)]
+    W0 = init_weights(wl, seed=11)
+    runs = []
+    for overlap in (2, 0):
+        lib = make_lib(wl, T=3)
+        lib.set_adam_overlap(overlap)
+        W = dev(W0, wl.dtype)
+        for g in grads:
+            lib.step(W, dev(g, wl.dtype))
+        torch.cuda.synchronize()
+        names = {n for n, *_ in lib.last_launches()}
+        runs.append((host(W, wl.dtype), lib.get_moments(), lib.get_omega(), names))
+        lib.close()
+    (Wa, ma, oa, na), (Wb, mb, ob, nb) = runs
+    assert "adam_sparse" in na and "adam_sparse" not in nb
+    assert np.array_equal(Wa.view(np.uint8), Wb.view(np.uint8))
+    for x, y in zip(ma, mb):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    assert np.array_equal(oa, ob)
+    orc = oracle_for(wl, T=3)
+    Wo = W0
+    for g in grads:
+        Wo = orc.step(Wo, g)
+    weight_check(Wa, Wo, wl.dtype, f"{name} with the sparse Adam update overlapped")
