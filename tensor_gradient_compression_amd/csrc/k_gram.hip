@@ -784,6 +784,8 @@ uint32_t gram_reduce_groups() { return RGROUPS; }
 uint32_t gram_blocks(const GramArgs& g, int num_cu) {
   const G16Geo f = g16geo(g, num_cu);
   if (f.ok) return f.grid;
+  const G32Geo f32 = gram32_geo(g, num_cu);
+  if (f32.ok) return f32.grid;
   const GGeo r = ggeo(g);
   uint64_t nb = (uint64_t)(num_cu > 0 ? num_cu : 256) * 4;
   if (nb > r.ntiles) nb = r.ntiles;
@@ -810,6 +812,14 @@ hipError_t launch_gram(const GramArgs& g, int num_cu, hipStream_t s,
     ff.k.partial = g.partial;
     if (mark) mark(mctx, KID_GRAM, true);
     const hipError_t e = g.dt == DT_BF16 ? pick16<true>(ff, s) : pick16<false>(ff, s);
+    if (mark) mark(mctx, KID_GRAM, false);
+    if (e != hipSuccess) return e;
+    return gram_reduce(g.partial, nblk, r.Kin * r.Kin, g.out, s, mark, mctx);
+  }
+  const G32Geo f32 = gram32_geo(g, num_cu);
+  if (f32.ok) {
+    if (mark) mark(mctx, KID_GRAM, true);
+    const hipError_t e = launch_gram32(f32, g.partial, s);
     if (mark) mark(mctx, KID_GRAM, false);
     if (e != hipSuccess) return e;
     return gram_reduce(g.partial, nblk, r.Kin * r.Kin, g.out, s, mark, mctx);

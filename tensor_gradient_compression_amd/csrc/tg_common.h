@@ -258,6 +258,16 @@ struct GramArgs {
   uint32_t max_blocks;   // 0: as many workgroups (partial sums) as fill the GPU; else at most this
 };
 uint32_t gram_blocks(const GramArgs& g, int num_cu);
+// fp32 / complex64 Grams with I <= 64 and no mask (k_gram32.hip): the launch geometry
+// (ok = false where that kernel does not apply) and the launch into `partial`
+struct G32Geo {
+  bool ok;
+  uint32_t grid, P;
+  size_t lds;
+  alignas(8) unsigned char kbytes[96];
+};
+G32Geo gram32_geo(const GramArgs& g, int num_cu);
+hipError_t launch_gram32(const G32Geo& geo, double* partial, hipStream_t s);
 uint32_t gram_reduce_groups();   // partial buffer holds (blocks + groups) * (I*P)^2
 size_t gram_lds_bytes(const GramArgs& g);
 hipError_t launch_gram(const GramArgs& g, int num_cu, hipStream_t s,

@@ -894,6 +894,12 @@ int tgrad_init(tgrad_t** out, int ndim, const int64_t* shape, const int64_t* tuc
     g.dt = DT_F32;
     uint64_t nb = gram_blocks(g, h->num_cu);
     g.dt = dtype == TGRAD_C64 ? DT_F32 : dtype;
+    nb = std::max<uint64_t>(nb, gram_blocks(g, h->num_cu));
+    // and with a mask (the masked Grams take the general kernels where the unmasked
+    // ones take the fp32 / complex one)
+    g.mask = (const uint64_t*)(uintptr_t)64;
+    nb = std::max<uint64_t>(nb, gram_blocks(g, h->num_cu));
+    g.dt = DT_F32;
     nb = std::max<uint64_t>(nb, gram_blocks(g, h->num_cu)) + gram_reduce_groups();
     if (nb * K2 > gpart) gpart = nb * K2;
     if (K2 > gmax) gmax = K2;

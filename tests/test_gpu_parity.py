@@ -196,6 +196,30 @@ def test_refresh_factors_match_oracle(case, masked):
     assert np.array_equal(host(G, wl.dtype).view(np.uint8), before.view(np.uint8))
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("masked", [False, True], ids=["residual-copy", "masked-read"])
+@pytest.mark.parametrize("name,wl", [("c64-64x64x64x33", C64_64x64x64x33),
+                                     ("f16-64x64x64x64", F16_4x64x64x64x64)],
+                         ids=lambda x: x if isinstance(x, str) else "")
+def test_full_size_refresh_factors_match_oracle(name, wl, masked):
+    """The complex64 (64,64,64,33) and fp16 (64,64,64,64) workloads at full size: one
+    refresh against the oracle's (Omega bit for bit, projectors and eigenvalues), with
+    the Grams reading the residual copy (the complex one on the fp32 / complex Gram
+    kernel) or the gradient through the bitmask (the general kernel)."""
+    g = GradStream(wl, seed=3).next()
+    lib, orc = make_lib(wl), make_oracle(wl)
+    if masked:
+        lib.set_gram_fusion(lib.set_gram_fusion(True), masked=True)
+    lib.refresh(dev(g, wl.dtype))
+    orc.refresh(g)
+    torch.cuda.synchronize()
+    assert np.array_equal(lib.get_omega(), orc.omega)
+    factor_check(lib, orc)
+    for n, w in enumerate(orc.eigvals):
+        if w is not None:
+            np.testing.assert_allclose(lib.get_eigvals(n), w, rtol=1e-4, atol=1e-5 * w[0])
+
+
 # --------------------------------------------------------------------------- steps, pinned factors
 
 STEP_CASES = FACTOR_CASES + [
