@@ -393,33 +393,56 @@ __device__ __forceinline__ double start_entry(uint32_t k, uint32_t c) {
   return (double)h * (1.0 / 4294967296.0) * 2.0 - 1.0;
 }
 
-size_t eig_tri_lds(uint32_t I) {
-  const size_t LD = I | 1u;
-  return (I * LD + 64 * LDY + 4 * 64 * 32 + 6 * 64 + 24 + 2 * 68) * sizeof(double);
-}
+// solves of the inverse iteration per batch (one lane each): 32 for real matrices; 16 for
+// Hermitian ones, whose two planes of A leave less LDS for the elimination rows
+template <int P> constexpr uint32_t tri_batch() { return P == 1 ? 32u : 16u; }
 
+template <int P>
+size_t eig_tri_lds_p(uint32_t I) {
+  const size_t LD = I | 1u;
+  return (P * I * LD + 64 * LDY + 4 * 64 * tri_batch<P>() + (3 * P + 3) * 64 + 24 + 2 * 68) *
+         sizeof(double);
+}
+size_t eig_tri_lds(uint32_t I) { return eig_tri_lds_p<1>(I); }
+size_t eig_trih_lds(uint32_t I) { return eig_tri_lds_p<2>(I); }
+
+// P = 1: real symmetric matrices. P = 2: Hermitian ones, from the stacked real Gram
+// (rows and columns i P + p). The reflectors are then complex, H = I - tau v v^H with
+// v_0 = 1 and a complex tau chosen so that H^H x = beta e_1 with beta real (tau =
+// (beta - x_0) / beta, v = x / (x_0 - beta) past v_0, beta = -sign(Re x_0) ||x||), and the
+// trailing block takes B <- H^H B H as B - v w^H - w v^H with p = tau B v and w = p -
+// (tau / 2) (p^H v) v. Every column, the last included, is reduced, so T is real
+// symmetric tridiagonal and the multisection and inverse iteration are the real ones.
+// The eigenvectors come back as X = H_0 H_1 ... H_{I-2} Y, complex.
+template <int P>
 __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
   extern __shared__ double sm[];
   const EK1& k = kk.m[blockIdx.x];
   const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t n = k.n, r = k.r;
+  constexpr uint32_t SB = tri_batch<P>();
   const uint32_t LD = n | 1u;          // odd row stride: column walks hit distinct banks
   double2* de = (double2*)sm;          // (d_k, e_{k-1}^2), padded to 1 + 4 ceil((I - 1) / 4)
                                        // (first: 16-byte reads need 16-byte alignment)
-  double* A = sm + 2 * 68;             // n x LD; the reflectors end up below its diagonal
-  double* Y = A + n * LD;              // the eigenvectors (columns), rows of LDY
-  double* W = Y + 64 * LDY;            // elimination rows of 32 solves: W[(4 k + a) 32 + s]
-  double* hv = W + 4 * 64 * 32;        // the current reflector
-  double* pw = hv + 64;                // p = tau B v
-  double* dv = pw + 64;                // T's diagonal
+  double* A = sm + 2 * 68;             // n x LD (P = 2: the real plane, then the imaginary
+                                       // one); the reflectors end up below its diagonal
+  double* Ai = A + (P - 1) * n * LD;   // P = 2: the imaginary plane
+  double* Y = A + P * n * LD;          // the eigenvectors of T (columns), rows of LDY
+  double* W = Y + 64 * LDY;            // elimination rows of SB solves: W[(4 k + a) SB + s]
+  double* hv = W + 4 * 64 * SB;        // the current reflector (P = 2: re, then im)
+  double* pw = hv + 64 * P;            // p = tau B v
+  double* dv = pw + 64 * P;            // T's diagonal
   double* ev = dv + 64;                // T's off-diagonal
-  double* tv = ev + 64;                // the taus
-  double* lam = tv + 64;               // the eigenvalues, ascending
+  double* tv = ev + 64;                // the taus (P = 2: re, then im)
+  double* lam = tv + 64 * P;           // the eigenvalues, ascending
   double* red = lam + 64;              // wave partials; [16], [17]: the Gershgorin interval
 
-  // the power-of-two scale that brings the largest |entry| into [0.5, 1)
+  // the power-of-two scale that brings the largest |entry| of the (stacked) Gram into
+  // [0.5, 1); for a Hermitian matrix every diagonal entry is a sum of two diagonal entries
+  // of the stacked Gram, so its largest eigenvalue is at least that largest entry too
+  const uint32_t K = P * n;
   double mx = 0.0;
-  for (uint32_t q = tid; q < n * n; q += NTQ) mx = fmax(mx, fabs(k.gram[q]));
+  for (uint32_t q = tid; q < K * K; q += NTQ) mx = fmax(mx, fabs(k.gram[q]));
   mx = wave_max(mx);
   if (lane == 0) red[wave] = mx;
   __syncthreads();
@@ -437,57 +460,144 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
   const double scale = ldexp(1.0, -ex);
   for (uint32_t q = tid; q < n * n; q += NTQ) {
     const uint32_t i = q / n, j = q - i * n;
-    A[i * LD + j] = (0.5 * (k.gram[(uint64_t)i * n + j] + k.gram[(uint64_t)j * n + i])) * scale;
+    if constexpr (P == 1) {
+      A[i * LD + j] = (0.5 * (k.gram[(uint64_t)i * n + j] + k.gram[(uint64_t)j * n + i])) * scale;
+    } else {
+      // H[i][j] = sum_c x_i conj(x_j): re from the (p, p) blocks, im from the cross ones,
+      // symmetrised as the Jacobi kernel does
+      auto G = [&](uint32_t a, uint32_t b) { return k.gram[(uint64_t)a * K + b]; };
+      const double re1 = G(2 * i, 2 * j) + G(2 * i + 1, 2 * j + 1);
+      const double im1 = G(2 * i + 1, 2 * j) - G(2 * i, 2 * j + 1);
+      const double re2 = G(2 * j, 2 * i) + G(2 * j + 1, 2 * i + 1);
+      const double im2 = G(2 * j + 1, 2 * i) - G(2 * j, 2 * i + 1);
+      A[i * LD + j] = (0.5 * (re1 + re2)) * scale;
+      Ai[i * LD + j] = (0.5 * (im1 - im2)) * scale;
+    }
   }
   __syncthreads();
 
   // Householder reduction to tridiagonal form
   const uint32_t ri = tid / QP, part = tid % QP;   // row (or column) and its share
-  for (uint32_t c = 0; c + 2 < n; ++c) {
+  const uint32_t nred = P == 1 ? (n >= 2 ? n - 2 : 0) : n - 1;   // columns reduced
+  for (uint32_t c = 0; c < nred; ++c) {
     const uint32_t m = n - 1 - c, b = c + 1;
     if (wave == 0) {
-      const double x = lane < m ? A[(b + lane) * LD + c] : 0.0;
-      const double sig = wave_total(lane >= 1 ? x * x : 0.0);
-      const double x0 = lane_value(x, 0);
-      double tau = 0.0, beta = x0, inv = 0.0;
-      if (sig > 0.0) {
-        const double mu = sqrt(x0 * x0 + sig);
-        beta = x0 <= 0.0 ? mu : -mu;
-        tau = (beta - x0) * rcp64(beta);
-        inv = rcp64(x0 - beta);
-      }
-      const double v = lane == 0 ? 1.0 : x * inv;
-      if (lane < m) {
-        hv[lane] = v;
-        A[(b + lane) * LD + c] = v;
-      }
-      if (lane == 0) {
-        tv[c] = tau;
-        ev[c] = beta;
-        dv[c] = A[c * LD + c];
+      if constexpr (P == 1) {
+        const double x = lane < m ? A[(b + lane) * LD + c] : 0.0;
+        const double sig = wave_total(lane >= 1 ? x * x : 0.0);
+        const double x0 = lane_value(x, 0);
+        double tau = 0.0, beta = x0, inv = 0.0;
+        if (sig > 0.0) {
+          const double mu = sqrt(x0 * x0 + sig);
+          beta = x0 <= 0.0 ? mu : -mu;
+          tau = (beta - x0) * rcp64(beta);
+          inv = rcp64(x0 - beta);
+        }
+        const double v = lane == 0 ? 1.0 : x * inv;
+        if (lane < m) {
+          hv[lane] = v;
+          A[(b + lane) * LD + c] = v;
+        }
+        if (lane == 0) {
+          tv[c] = tau;
+          ev[c] = beta;
+          dv[c] = A[c * LD + c];
+        }
+      } else {
+        const double xr = lane < m ? A[(b + lane) * LD + c] : 0.0;
+        const double xi = lane < m ? Ai[(b + lane) * LD + c] : 0.0;
+        const double sig = wave_total(lane >= 1 ? xr * xr + xi * xi : 0.0);
+        const double x0r = lane_value(xr, 0), x0i = lane_value(xi, 0);
+        double tr = 0.0, ti = 0.0, beta = x0r, ir = 0.0, ii = 0.0;
+        if (sig > 0.0 || x0i != 0.0) {
+          const double mu = sqrt(x0r * x0r + x0i * x0i + sig);
+          beta = x0r <= 0.0 ? mu : -mu;
+          const double rb = rcp64(beta);
+          tr = (beta - x0r) * rb;
+          ti = -x0i * rb;
+          // 1 / (x_0 - beta)
+          const double dr = x0r - beta, di = x0i;
+          const double den = rcp64(dr * dr + di * di);
+          ir = dr * den;
+          ii = -di * den;
+        }
+        const double vr = lane == 0 ? 1.0 : xr * ir - xi * ii;
+        const double vi = lane == 0 ? 0.0 : xr * ii + xi * ir;
+        if (lane < m) {
+          hv[lane] = vr;
+          hv[64 + lane] = vi;
+          A[(b + lane) * LD + c] = vr;
+          Ai[(b + lane) * LD + c] = vi;
+        }
+        if (lane == 0) {
+          tv[c] = tr;
+          tv[64 + c] = ti;
+          ev[c] = beta;
+          dv[c] = A[c * LD + c];
+        }
       }
     }
     __syncthreads();
-    const double tau = tv[c];
-    if (tau == 0.0) continue;   // the same for every thread
-    double sp = 0.0;
-    if (ri < m)
-      for (uint32_t j = part; j < m; j += QP) sp += A[(b + ri) * LD + b + j] * hv[j];
-    sp = row16_sum(sp);
-    if (ri < m && part == 0) pw[ri] = tau * sp;
-    __syncthreads();
-    const double kd = 0.5 * tau * wave_total(lane < m ? pw[lane] * hv[lane] : 0.0);
-    if (ri < m) {
-      const double vi = hv[ri], wi = pw[ri] - kd * vi;
-      for (uint32_t j = part; j < m; j += QP) {
-        const double vj = hv[j], wj = pw[j] - kd * vj;
-        A[(b + ri) * LD + b + j] -= vi * wj + wi * vj;
+    if constexpr (P == 1) {
+      const double tau = tv[c];
+      if (tau == 0.0) continue;   // the same for every thread
+      double sp = 0.0;
+      if (ri < m)
+        for (uint32_t j = part; j < m; j += QP) sp += A[(b + ri) * LD + b + j] * hv[j];
+      sp = row16_sum(sp);
+      if (ri < m && part == 0) pw[ri] = tau * sp;
+      __syncthreads();
+      const double kd = 0.5 * tau * wave_total(lane < m ? pw[lane] * hv[lane] : 0.0);
+      if (ri < m) {
+        const double vi = hv[ri], wi = pw[ri] - kd * vi;
+        for (uint32_t j = part; j < m; j += QP) {
+          const double vj = hv[j], wj = pw[j] - kd * vj;
+          A[(b + ri) * LD + b + j] -= vi * wj + wi * vj;
+        }
+      }
+    } else {
+      const double tr = tv[c], ti = tv[64 + c];
+      if (tr == 0.0 && ti == 0.0) continue;   // the same for every thread
+      // sp = (B v)_ri, then p = tau sp
+      double sr = 0.0, si = 0.0;
+      if (ri < m)
+        for (uint32_t j = part; j < m; j += QP) {
+          const double br = A[(b + ri) * LD + b + j], bi = Ai[(b + ri) * LD + b + j];
+          const double vr = hv[j], vi = hv[64 + j];
+          sr += br * vr - bi * vi;
+          si += br * vi + bi * vr;
+        }
+      sr = row16_sum(sr);
+      si = row16_sum(si);
+      if (ri < m && part == 0) {
+        pw[ri] = tr * sr - ti * si;
+        pw[64 + ri] = tr * si + ti * sr;
+      }
+      __syncthreads();
+      // kd = (tau / 2) (p^H v)
+      const double pr = lane < m ? pw[lane] : 0.0, pim = lane < m ? pw[64 + lane] : 0.0;
+      const double hr = lane < m ? hv[lane] : 0.0, him = lane < m ? hv[64 + lane] : 0.0;
+      const double qr = wave_total(pr * hr + pim * him);
+      const double qi = wave_total(pr * him - pim * hr);
+      const double kr = 0.5 * (tr * qr - ti * qi), ki = 0.5 * (tr * qi + ti * qr);
+      if (ri < m) {
+        const double vir = hv[ri], vii = hv[64 + ri];
+        const double wir = pw[ri] - (kr * vir - ki * vii);
+        const double wii = pw[64 + ri] - (kr * vii + ki * vir);
+        for (uint32_t j = part; j < m; j += QP) {
+          const double vjr = hv[j], vji = hv[64 + j];
+          const double wjr = pw[j] - (kr * vjr - ki * vji);
+          const double wji = pw[64 + j] - (kr * vji + ki * vjr);
+          // v_i conj(w_j) + w_i conj(v_j)
+          A[(b + ri) * LD + b + j] -= (vir * wjr + vii * wji) + (wir * vjr + wii * vji);
+          Ai[(b + ri) * LD + b + j] -= (vii * wjr - vir * wji) + (wii * vjr - wir * vji);
+        }
       }
     }
     __syncthreads();
   }
   if (tid == 0) {
-    if (n >= 2) {
+    if (P == 1 && n >= 2) {
       dv[n - 2] = A[(n - 2) * LD + n - 2];
       ev[n - 2] = A[(n - 1) * LD + n - 2];
     }
@@ -551,12 +661,12 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
   if (tid < n) k.eigvals[tid] = ldexp(lam[n - 1 - tid], ex);
   if (tid == 0) *k.status = 0;
 
-  // inverse iteration, one lane per leading eigenvalue, 32 at a time
+  // inverse iteration, one lane per leading eigenvalue, SB at a time
   if (wave == 0) {
     const double tiny = 2.220446049250313e-16 * fmax(nrm, 0.25);
-    for (uint32_t c0 = 0; c0 < r; c0 += 32) {
+    for (uint32_t c0 = 0; c0 < r; c0 += SB) {
       const uint32_t c = c0 + lane;
-      if (lane < 32 && c < r) {
+      if (lane < SB && c < r) {
         const double lm = lam[n - 1 - c];
         for (uint32_t i = 0; i < n; ++i) Y[i * LDY + c] = start_entry(i, c);
         for (int round = 0; round < 2; ++round) {
@@ -575,25 +685,25 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
             if (u0 == 0.0) u0 = tiny;
             const double iv = rcp64(u0);
             const double l = n0 * iv;
-            W[(4 * i + 0) * 32 + lane] = iv;
-            W[(4 * i + 1) * 32 + lane] = u1;
-            W[(4 * i + 2) * 32 + lane] = u2;
-            W[(4 * i + 3) * 32 + lane] = rc;
+            W[(4 * i + 0) * SB + lane] = iv;
+            W[(4 * i + 1) * SB + lane] = u1;
+            W[(4 * i + 2) * SB + lane] = u2;
+            W[(4 * i + 3) * SB + lane] = rc;
             u0 = n1 - l * u1;
             u1 = n2 - l * u2;
             u2 = 0.0;
             rc = rn - l * rc;
           }
           if (fabs(u0) < tiny) u0 = u0 >= 0.0 ? tiny : -tiny;
-          W[(4 * (n - 1) + 0) * 32 + lane] = rcp64(u0);
-          W[(4 * (n - 1) + 1) * 32 + lane] = 0.0;
-          W[(4 * (n - 1) + 2) * 32 + lane] = 0.0;
-          W[(4 * (n - 1) + 3) * 32 + lane] = rc;
+          W[(4 * (n - 1) + 0) * SB + lane] = rcp64(u0);
+          W[(4 * (n - 1) + 1) * SB + lane] = 0.0;
+          W[(4 * (n - 1) + 2) * SB + lane] = 0.0;
+          W[(4 * (n - 1) + 3) * SB + lane] = rc;
           // back substitution, then y / ||y||
           double y1 = 0.0, y2 = 0.0, ss = 0.0;
           for (uint32_t i = n; i-- > 0;) {
-            const double y = (W[(4 * i + 3) * 32 + lane] - W[(4 * i + 1) * 32 + lane] * y1 -
-                              W[(4 * i + 2) * 32 + lane] * y2) * W[(4 * i + 0) * 32 + lane];
+            const double y = (W[(4 * i + 3) * SB + lane] - W[(4 * i + 1) * SB + lane] * y1 -
+                              W[(4 * i + 2) * SB + lane] * y2) * W[(4 * i + 0) * SB + lane];
             Y[i * LDY + c] = y;
             ss += y * y;
             y2 = y1;
@@ -607,19 +717,19 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
   }
   __syncthreads();
 
-  // back to A's basis: X = H_0 H_1 ... H_{I-3} Y, QP lanes per column, no barrier
-  {
+  // back to A's basis: X = H_0 H_1 ... Y, QP lanes per column, no barrier
+  constexpr int NR = 64 / QP;
+  const uint32_t col = tid / QP;
+  const bool act = col < r;
+  if constexpr (P == 1) {
     // rows part + QP t of column tid / QP in registers
-    constexpr int NR = 64 / QP;
-    const uint32_t col = tid / QP;
-    const bool act = col < r;
     double yv[NR];
 #pragma unroll
     for (int t = 0; t < NR; ++t) {
       const uint32_t row = part + QP * t;
       yv[t] = (act && row < n) ? Y[row * LDY + col] : 0.0;
     }
-    for (int c = (int)n - 3; c >= 0; --c) {
+    for (int c = (int)nred - 1; c >= 0; --c) {
       const double tau = tv[c];
       if (tau == 0.0) continue;   // the same for every thread
       const uint32_t b = (uint32_t)c + 1;
@@ -641,16 +751,84 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
       const uint32_t row = part + QP * t;
       if (act && row < n) Y[row * LDY + col] = yv[t];
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // one wave per selected column: largest |entry| (lowest row on ties) made positive
-  for (uint32_t c = wave; c < r; c += NTQ / 64) {
-    const double x = lane < n ? Y[lane * LDY + c] : 0.0;
-    double best = lane < n ? x * x : -1.0;
-    uint32_t bi = lane;
+    // one wave per selected column: largest |entry| (lowest row on ties) made positive
+    for (uint32_t c = wave; c < r; c += NTQ / 64) {
+      const double x = lane < n ? Y[lane * LDY + c] : 0.0;
+      double best = lane < n ? x * x : -1.0;
+      uint32_t bi = lane;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
+      for (int off = 32; off > 0; off >>= 1) {
+        const double ob = __shfl_xor(best, off, 64);
+        const uint32_t oi = __shfl_xor(bi, off, 64);
+        if (ob > best || (ob == best && oi < bi)) {
+          best = ob;
+          bi = oi;
+        }
+      }
+      const double vmax = __shfl(x, bi, 64);
+      const double sr = vmax != 0.0 ? (vmax > 0.0 ? 1.0 : -1.0) : 1.0;
+      if (lane < n) {
+        const float u = (float)(x * sr);
+        k.U[(uint64_t)lane * r + c] = u;
+        k.Mproj[(uint64_t)c * n + lane] = u;
+        k.Mrec[(uint64_t)lane * r + c] = u;
+      }
+    }
+  } else {
+    double yr[NR], yi[NR];
+#pragma unroll
+    for (int t = 0; t < NR; ++t) {
+      const uint32_t row = part + QP * t;
+      yr[t] = (act && row < n) ? Y[row * LDY + col] : 0.0;
+      yi[t] = 0.0;
+    }
+    for (int c = (int)nred - 1; c >= 0; --c) {
+      const double tr = tv[c], ti = tv[64 + c];
+      if (tr == 0.0 && ti == 0.0) continue;   // the same for every thread
+      const uint32_t b = (uint32_t)c + 1;
+      double vr[NR], vi[NR], ur = 0.0, ui = 0.0;
+#pragma unroll
+      for (int t = 0; t < NR; ++t) {
+        const uint32_t row = part + QP * t;
+        const uint32_t rr = row < n ? row : n - 1;
+        const bool in = row >= b && row < n;
+        const double a = A[rr * LD + c], ai = Ai[rr * LD + c];
+        vr[t] = in ? a : 0.0;
+        vi[t] = in ? ai : 0.0;
+      }
+      // u = tau (v^H x)
+#pragma unroll
+      for (int t = 0; t < NR; ++t) {
+        ur += vr[t] * yr[t] + vi[t] * yi[t];
+        ui += vr[t] * yi[t] - vi[t] * yr[t];
+      }
+      ur = row16_sum(ur);
+      ui = row16_sum(ui);
+      const double qr = tr * ur - ti * ui, qi = tr * ui + ti * ur;
+#pragma unroll
+      for (int t = 0; t < NR; ++t) {
+        yr[t] -= vr[t] * qr - vi[t] * qi;
+        yi[t] -= vr[t] * qi + vi[t] * qr;
+      }
+    }
+    // the column's largest-|.| entry (lowest row on ties) made real positive by a unit
+    // scalar, then U, Mproj (the real form of U^H) and Mrec (of U); the QP lanes of a
+    // column are one DPP row
+    double best = -1.0;
+    uint32_t bi = 0;
+#pragma unroll
+    for (int t = 0; t < NR; ++t) {
+      const uint32_t row = part + QP * t;
+      const double m2 = row < n ? yr[t] * yr[t] + yi[t] * yi[t] : -1.0;
+      if (m2 > best) {   // rows ascend with t: the first of equal values is the lowest row
+        best = m2;
+        bi = row;
+      }
+    }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) {
       const double ob = __shfl_xor(best, off, 64);
       const uint32_t oi = __shfl_xor(bi, off, 64);
       if (ob > best || (ob == best && oi < bi)) {
@@ -658,13 +836,39 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
         bi = oi;
       }
     }
-    const double vmax = __shfl(x, bi, 64);
-    const double sr = vmax != 0.0 ? (vmax > 0.0 ? 1.0 : -1.0) : 1.0;
-    if (lane < n) {
-      const float u = (float)(x * sr);
-      k.U[(uint64_t)lane * r + c] = u;
-      k.Mproj[(uint64_t)c * n + lane] = u;
-      k.Mrec[(uint64_t)lane * r + c] = u;
+    // the winning entry: from the lane of the row group that holds row bi
+    const uint32_t owner = (lane & ~(QP - 1)) + (bi % QP);
+    double wr = 0.0, wi = 0.0;
+#pragma unroll
+    for (int t = 0; t < NR; ++t)
+      if (bi / QP == (uint32_t)t) {
+        wr = yr[t];
+        wi = yi[t];
+      }
+    const double vmr = __shfl(wr, owner, 64), vmi = __shfl(wi, owner, 64);
+    const double mag = sqrt(vmr * vmr + vmi * vmi);
+    const double sr = mag > 0.0 ? vmr / mag : 1.0;     // scale = conj(phase)
+    const double si = mag > 0.0 ? -vmi / mag : 0.0;
+    if (act) {
+      const uint64_t KP = 2ull * n, RP = 2ull * r;
+#pragma unroll
+      for (int t = 0; t < NR; ++t) {
+        const uint32_t i = part + QP * t;
+        if (i < n) {
+          const float ur = (float)(yr[t] * sr - yi[t] * si);
+          const float ui = (float)(yr[t] * si + yi[t] * sr);
+          k.U[((uint64_t)i * r + col) * 2] = ur;
+          k.U[((uint64_t)i * r + col) * 2 + 1] = ui;
+          k.Mproj[(2 * col) * KP + 2 * i] = ur;
+          k.Mproj[(2 * col) * KP + 2 * i + 1] = ui;
+          k.Mproj[(2 * col + 1) * KP + 2 * i] = -ui;
+          k.Mproj[(2 * col + 1) * KP + 2 * i + 1] = ur;
+          k.Mrec[(2 * i) * RP + 2 * col] = ur;
+          k.Mrec[(2 * i) * RP + 2 * col + 1] = -ui;
+          k.Mrec[(2 * i + 1) * RP + 2 * col] = ui;
+          k.Mrec[(2 * i + 1) * RP + 2 * col + 1] = ur;
+        }
+      }
     }
   }
 }
@@ -680,6 +884,7 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
 __global__ void __launch_bounds__(NTS) k_eig_herm(EK kk) {
   extern __shared__ double sm[];
   const EK1& k = kk.m[blockIdx.x];
+  if (kk.handoff_only && *k.status != EIG_HANDOFF) return;   // the same for every thread
   const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t n = k.n;
   const uint32_t LD = n + 1;
@@ -1317,10 +1522,10 @@ hipError_t launch_eig(const EigArgs* e, int count, hipStream_t s) {
     m.n = e[i].I;
     m.r = e[i].r;
     const size_t b = big ? eig_big_lds(e[i].I, e[i].P)
-                         : (cplx ? eig_herm_lds(e[i].I) : eig_tri_lds(e[i].I));
+                         : (cplx ? eig_trih_lds(e[i].I) : eig_tri_lds(e[i].I));
     size_t& l = big ? lds_b : lds_s;
     if (b > l) l = b;
-    if (!big && !cplx) lds_j = std::max(lds_j, eig_lds_bytes(e[i].I, 1));
+    if (!big) lds_j = std::max(lds_j, cplx ? eig_herm_lds(e[i].I) : eig_lds_bytes(e[i].I, 1));
   }
   auto go = [&](auto fn, int nm, int nt, size_t lds, const EK& args) -> hipError_t {
     if (lds > 64 * 1024) {
@@ -1331,16 +1536,13 @@ hipError_t launch_eig(const EigArgs* e, int count, hipStream_t s) {
     hipLaunchKernelGGL(fn, dim3(nm), dim3(nt), lds, s, args);
     return hipGetLastError();
   };
-  if (ns && cplx) {
-    hipError_t err = go(k_eig_herm, ns, NTS, lds_s, ks);
-    if (err != hipSuccess) return err;
-  } else if (ns) {
+  if (ns) {
     // the tridiagonal route, then Jacobi on the matrices it handed over
-    hipError_t err = go(k_eig_tri, ns, NTQ, lds_s, ks);
+    hipError_t err = cplx ? go(k_eig_tri<2>, ns, NTQ, lds_s, ks) : go(k_eig_tri<1>, ns, NTQ, lds_s, ks);
     if (err != hipSuccess) return err;
     EK kj = ks;
     kj.handoff_only = 1;
-    err = go(k_eig_sym, ns, NTS, lds_j, kj);
+    err = cplx ? go(k_eig_herm, ns, NTS, lds_j, kj) : go(k_eig_sym, ns, NTS, lds_j, kj);
     if (err != hipSuccess) return err;
   }
   if (nb) {
