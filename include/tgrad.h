@@ -218,19 +218,27 @@ int tgrad_set_fusion(tgrad_t *h, int enable);
  * takes effect at the next refresh. */
 int tgrad_set_gram_fusion(tgrad_t *h, int enable);
 
-/* Test / benchmark hook: when the COO gather is folded into the first projection launch
- * and further launches follow it, the Adam update of the k sparse values (the
- * nullthought summary, section 3: S and the low-rank core keep separate Adam states)
- * runs on a second stream that the handle owns (created by tgrad_init, default
- * priority). It waits for the first projection launch, overlaps the projection's later
- * launches and the core's Adam update, and the caller's stream waits for it before the
- * reconstruction, so the call stays ordered on the caller's stream. The update is
- * element-wise: results are bit-identical either way. The fork and the join cost
- * about 10 us a step, so enable = 1 (the default) selects it only when the sparse part
- * holds at least 2^22 values (k, times 2 for complex data); 2 selects it whenever it
- * applies; 0 runs both updates in one launch on the caller's stream. Its launch is
- * named adam_sparse (tgrad_kernel_name); takes effect at the next step. */
-int tgrad_set_adam_overlap(tgrad_t *h, int enable);
+/* Test / benchmark hook: work that runs on a second stream the handle owns (created by
+ * tgrad_init, default priority), forked from the caller's stream and joined back before
+ * the call's later work, so every call stays ordered on the caller's stream.
+ *  adam: when the COO gather is folded into the first projection launch and further
+ *        launches follow it, the Adam update of the k sparse values (the nullthought
+ *        summary, section 3: S and the low-rank core keep separate Adam states) waits
+ *        for that first launch and overlaps the projection's later launches and the
+ *        core's Adam update; the reconstruction waits for it. The update is element-wise:
+ *        results are bit-identical either way. The fork and the join cost about 10 us a
+ *        step, so adam = 1 (the default) selects it only when the sparse part holds at
+ *        least 2^22 values (k, times 2 for complex data); 2 whenever it applies; 0 runs
+ *        both updates in one launch on the caller's stream. Its launch is named
+ *        adam_sparse (tgrad_kernel_name).
+ *  eig:  at a refresh whose last three modes' Grams come from one launch (see
+ *        tgrad_set_gram_fusion), the eigensolver of the compressed modes before them
+ *        (pith.science "What carries the argument": each factor from its own mode's
+ *        Gram) runs beside that launch, which then leaves one CU per such matrix free.
+ *        1 (default) or 0. With fewer workgroups the three-mode launch sums its partial
+ *        Grams in another grouping, so factors agree to fp64 rounding of the Grams.
+ * Takes effect at the next step or refresh. */
+int tgrad_set_stream_overlap(tgrad_t *h, int adam, int eig);
 
 /* Test / benchmark hook: with the fused launch plan, two neighbouring compressed modes
  * ahead of the trailing ones (the projection's last two products, the reconstruction's

@@ -85,7 +85,7 @@ SIGNATURES = [
     ("tgrad_set_fusion", ctypes.c_int, [_P, ctypes.c_int]),
     ("tgrad_set_gram_fusion", ctypes.c_int, [_P, ctypes.c_int]),
     ("tgrad_set_pair_fusion", ctypes.c_int, [_P, ctypes.c_int]),
-    ("tgrad_set_adam_overlap", ctypes.c_int, [_P, ctypes.c_int]),
+    ("tgrad_set_stream_overlap", ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int]),
     ("tgrad_set_stream_products", ctypes.c_int, [_P, ctypes.c_int]),
     ("tgrad_default_options", None, [ctypes.POINTER(Options)]),
     ("tgrad_set_options", ctypes.c_int, [_P, ctypes.POINTER(Options)]),
@@ -355,13 +355,18 @@ class TGrad:
         self._check(rc, "tgrad_set_gram_fusion")
         return True
 
+    def set_stream_overlap(self, adam=1, eig=True) -> None:
+        """Work on the handle's second stream: the sparse values' Adam update beside the
+        projection's later launches when the sparse part is large (adam=1, the default),
+        whenever that applies (2) or never (0); and at a refresh, the leading modes'
+        eigensolver beside the three-mode Gram launch (eig). Adam results are
+        bit-identical either way; factors agree to fp64 rounding of the Grams."""
+        self._check(self._lib.tgrad_set_stream_overlap(self._h, int(adam), int(bool(eig))),
+                    "tgrad_set_stream_overlap")
+
     def set_adam_overlap(self, enable) -> None:
-        """Where the sparse values' Adam update runs: on the handle's second stream,
-        beside the projection's later launches, when the sparse part is large (1, the
-        default), whenever that applies (2), or in one launch with the core's update on
-        the caller's stream (0). Results are bit-identical."""
-        self._check(self._lib.tgrad_set_adam_overlap(self._h, int(enable)),
-                    "tgrad_set_adam_overlap")
+        """set_stream_overlap with only the Adam choice changed (eig left on)."""
+        self.set_stream_overlap(adam=enable, eig=True)
 
     def set_pair_fusion(self, enable) -> bool:
         """Select one launch for two neighbouring leading modes of the fused plan (True)

@@ -90,7 +90,9 @@ __global__ void __launch_bounds__(NTR) __attribute__((amdgpu_waves_per_eu(3, 8))
   const uint64_t N = (uint64_t)k.U * I0 * slab_e;
   const uint64_t kS = k.kS;
   const bool sparse = kS > 0;
-  const float lr = k.lr, decay = k.decay;
+  // used only by per-lane arithmetic: kept in vector registers
+  const float lr = __builtin_bit_cast(float, in_vgpr(__builtin_bit_cast(uint32_t, k.lr)));
+  const float decay = __builtin_bit_cast(float, in_vgpr(__builtin_bit_cast(uint32_t, k.decay)));
 
   // M0 into LDS (4-byte transfers, I0 R0 <= 2048 values), and the operand tables: every
   // load of a thread issued before its first LDS write (one memory latency in all)
@@ -150,8 +152,14 @@ __global__ void __launch_bounds__(NTR) __attribute__((amdgpu_waves_per_eu(3, 8))
   // 0 and 1: they retire on vmcnt, at the next slab's wait; scalar loads would retire on
   // lgkmcnt, so every wait for an LDS read after them would wait for them too), and
   // slab s's Omega range from them
+  // the Omega structures' addresses are used only by per-lane loads: they live in
+  // vector registers (this kernel runs short of scalar ones)
+  const auto maskv = in_vgpr_ptr(k.mask);
+  const auto rankv = in_vgpr_ptr(k.rank);
+  const auto omegav = in_vgpr_ptr(k.omega);
+  const auto Sv = in_vgpr_ptr(k.S);
   auto bounds = [&](uint32_t s, BoundsV& b) {
-    b = load_bounds(k.mask, k.rank, (uint64_t)s * slab_e, slab_e, N, lane);
+    b = load_bounds(maskv, rankv, (uint64_t)s * slab_e, slab_e, N, lane);
   };
   auto range = [&](uint32_t s, const BoundsV& b, uint64_t& lo, uint64_t& hi) {
     lo = rank_at(lane_u64(b.m, 0), (uint32_t)__builtin_amdgcn_readlane((int)b.r, 0),
@@ -224,8 +232,8 @@ __global__ void __launch_bounds__(NTR) __attribute__((amdgpu_waves_per_eu(3, 8))
     for (int q = 0; q < NOM; ++q) {
       const uint64_t j = op.lo[0] + lane + 64 * q;
       const uint64_t jc = j < kS ? j : kS - 1;
-      op.om[0][q] = k.omega[jc];
-      op.us[0][q] = k.S[jc];
+      op.om[0][q] = omegav[jc];
+      op.us[0][q] = Sv[jc];
     }
     if (cnt > 1) bounds(slab_of(1), op.bw);
   }
@@ -305,8 +313,8 @@ __global__ void __launch_bounds__(NTR) __attribute__((amdgpu_waves_per_eu(3, 8))
       for (int q = 0; q < NOM; ++q) {
         const uint64_t j = op.lo[nxt] + lane + 64 * q;
         const uint64_t jc = j < kS ? j : kS - 1;
-        op.om[nxt][q] = k.omega[jc];
-        op.us[nxt][q] = k.S[jc];
+        op.om[nxt][q] = omegav[jc];
+        op.us[nxt][q] = Sv[jc];
       }
       if (i + 2 < cnt) bounds(slab_of(i + 2), op.bw);
     }
@@ -393,8 +401,8 @@ __global__ void __launch_bounds__(NTR) __attribute__((amdgpu_waves_per_eu(3, 8))
 #pragma unroll
       for (int q = 0; q < NOM; ++q) Ob[loc[q]] = cv[q] + op.us[cur][q];
       for (uint64_t j = jlo + 64 * NOM + lane; j < jhi; j += 64) {
-        const uint32_t l = (uint32_t)(k.omega[j] - e_lo);
-        Ob[l] = Ob[l] + k.S[j];
+        const uint32_t l = (uint32_t)(omegav[j] - e_lo);
+        Ob[l] = Ob[l] + Sv[j];
       }
       wave_fence();
     }

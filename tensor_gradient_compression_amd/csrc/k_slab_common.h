@@ -113,9 +113,9 @@ struct BoundsV {
   uint64_t m = 0;
   uint32_t r = 0;
 };
-__device__ __forceinline__ BoundsV load_bounds(const uint64_t* mask, const uint32_t* rank,
-                                               uint64_t elo, uint64_t slab_e, uint64_t N,
-                                               uint32_t lane) {
+template <typename MaskPtr, typename RankPtr>
+__device__ __forceinline__ BoundsV load_bounds(MaskPtr mask, RankPtr rank, uint64_t elo,
+                                               uint64_t slab_e, uint64_t N, uint32_t lane) {
   const uint64_t ehi = elo + slab_e;
   const uint64_t wl = elo >> 6, wh = ehi < N ? ehi >> 6 : 0;
   const uint64_t idx = lane == 0 ? wl : wh;
@@ -128,6 +128,26 @@ __device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
   return ((uint64_t)hi << 32) | lo;
+}
+
+// A wave-uniform value held in vector registers. The compiler keeps uniform values in
+// scalar registers; where a kernel runs out of those it spills them into lanes of a
+// vector register and reads each one back (v_readlane) at every use. Values whose uses
+// are all vector operations (addresses of per-lane loads, per-lane compares) lose
+// nothing by living in a vector register instead.
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t x) {
+  uint32_t y;
+  __asm__("v_mov_b32 %0, %1" : "=v"(y) : "s"(x));
+  return y;
+}
+__device__ __forceinline__ uint64_t in_vgpr64(uint64_t x) {
+  return ((uint64_t)in_vgpr((uint32_t)(x >> 32)) << 32) | in_vgpr((uint32_t)x);
+}
+// a global-memory pointer held so (its loads stay global loads: a generic pointer's
+// would be flat loads, which also count against the LDS wait counter)
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* in_vgpr_ptr(T* p) {
+  return (__attribute__((address_space(1))) T*)in_vgpr64((uint64_t)(uintptr_t)p);
 }
 
 struct OmegaPipe {

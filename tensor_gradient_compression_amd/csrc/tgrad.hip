@@ -88,6 +88,8 @@ struct tgrad_handle {
   // join cost about 10 us a step, which only a large sparse update repays: bf16
   // (64,64,48,48,25) 0.749 -> 0.740 ms, fp16 (64,64,64,64) 0.179 -> 0.192 ms); 2: always
   int adam_overlap = 1;
+  // refresh: the leading modes' eigensolver beside the three-mode Gram launch
+  bool eig_overlap = true;
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 
@@ -640,19 +642,53 @@ int do_refresh(tgrad_t* h, const void* grad, hipStream_t s, const RefreshWs& ws)
     e.Mrec = h->Mr[n];
     e.eigvals = h->eig[n];
   }
+  // With the last three modes' Grams in one launch, the modes before them have their
+  // Gram matrices before that launch starts: their eigensolver (one workgroup a matrix)
+  // runs on the handle's second stream, on CUs the three-mode launch leaves free (it
+  // takes one workgroup per CU otherwise), and the caller's stream waits for it before
+  // the refresh ends. Results do not depend on the overlap.
+  int nlead = 0;
+  for (int n : h->fmodes)
+    if (tail3 && n < h->d - 3) ++nlead;
+  const bool eig_fork = tail3 && h->eig_overlap && h->side && nlead > 0 && nlead < ne &&
+                        nlead < h->num_cu / 4;
+  if (eig_fork) {
+    HIPCHK(h, hipEventRecord(h->ev_fork, s));
+    HIPCHK(h, hipStreamWaitEvent(h->side, h->ev_fork, 0));
+    hipError_t e;
+    h->cur_stream = h->side;   // the timing events of this launch go on the side stream
+    {
+      Mark m(h, KID_EIG);
+      e = launch_eig(eig, nlead, h->side);
+    }
+    h->cur_stream = s;
+    if (e != hipSuccess) return fail_hip(h, e, "launch_eig (leading modes)");
+    record(h, KID_EIG, 0, 0, 0, 0);
+    HIPCHK(h, hipEventRecord(h->ev_join, h->side));
+  }
   if (tail3) {
-    HIPCHK(h, launch_gram3(g3, h->num_cu, s, mark_cb, h));
+    hipError_t e = launch_gram3(g3, eig_fork ? h->num_cu - nlead : h->num_cu, s, mark_cb, h);
+    if (e != hipSuccess) {
+      if (eig_fork) (void)hipStreamWaitEvent(s, h->ev_join, 0);
+      return fail_hip(h, e, "launch_gram3");
+    }
     const uint64_t I3[3] = {g3.Ia, g3.Ib, g3.Ic};
     uint64_t fl = 0;
     for (int m = 0; m < 3; ++m) fl += 2 * (h->N / I3[m]) * I3[m] * I3[m];
     record(h, KID_GRAM3, 7 << (h->d - 3), h->N * dt_bytes(h->dtype) + (rmask ? h->N / 8 : 0), 0,
            fl);
   }
-  if (ne) {
+  const int e0 = eig_fork ? nlead : 0;
+  if (ne > e0) {
     Mark m(h, KID_EIG);
-    HIPCHK(h, launch_eig(eig, ne, s));
+    const hipError_t e = launch_eig(eig + e0, ne - e0, s);
+    if (e != hipSuccess) {
+      if (eig_fork) (void)hipStreamWaitEvent(s, h->ev_join, 0);
+      return fail_hip(h, e, "launch_eig");
+    }
     record(h, KID_EIG, 0, 0, 0, 0);
   }
+  if (eig_fork) HIPCHK(h, hipStreamWaitEvent(s, h->ev_join, 0));
   for (int n : h->fmodes)
     if (h->Mps[n]) {
       Mark m(h, KID_CSPLIT_OPERAND);
@@ -1881,9 +1917,10 @@ int tgrad_set_stream_products(tgrad_t* h, int enable) {
   return TGRAD_OK;
 }
 
-int tgrad_set_adam_overlap(tgrad_t* h, int enable) {
-  if (!h || enable < 0 || enable > 2) return TGRAD_EINVAL;
-  h->adam_overlap = enable;
+int tgrad_set_stream_overlap(tgrad_t* h, int adam, int eig) {
+  if (!h || adam < 0 || adam > 2 || eig < 0 || eig > 1) return TGRAD_EINVAL;
+  h->adam_overlap = adam;
+  h->eig_overlap = eig != 0;
   return TGRAD_OK;
 }
 
