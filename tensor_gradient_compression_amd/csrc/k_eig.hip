@@ -294,10 +294,12 @@ __global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
 // the leading principal minors of T - x I, P_0 = 1, P_1 = d_0 - x, P_k = (d_{k-1} - x)
 // P_{k-1} - e_{k-2}^2 P_{k-2} (Sylvester's law of inertia on T - x I = L D L^T; a zero
 // minor is taken as a tiny negative one, a zero pivot counting as negative). The pair
-// (P_k, P_{k-1}) is rescaled by a power of two every four terms, which keeps every sign. Sixteen lanes own
-// eigenvalue j (ascending): each step they count at the sixteen inner points of a 17-part
-// split of the bracket [a, b] (count(a) <= j < count(b), from the Gershgorin interval)
-// and keep the part that holds it; 14 steps shrink the bracket by 17^14 > 2^57.
+// (P_k, P_{k-1}) is rescaled by a power of two every four terms, which keeps every sign.
+// Sixteen lanes own eigenvalue j (ascending): each step they count at the sixteen inner
+// points of a 17-part split of the bracket [a, b] (count(a) <= j < count(b), from the
+// Gershgorin interval) and keep the part that holds it; 14 steps shrink the bracket by
+// 17^14 > 2^57 for the r leading eigenvalues, 6 steps by 17^6 for the others, which are
+// only reported.
 //
 // Eigenvectors: for each of the r largest eigenvalues (one lane each) two rounds of
 // inverse iteration, (T - lambda I) y = z then z = y / ||y||, from a fixed pseudo-random
@@ -315,7 +317,11 @@ __global__ void __launch_bounds__(NTS) k_eig_sym(EK kk) {
 constexpr int NTQ = 1024;
 constexpr uint32_t QP = NTQ / 64;   // lanes per row, column or eigenvalue (one DPP row)
 static_assert(QP == 16, "the row reductions span 16 lanes");
-constexpr int MS_STEPS = 14;        // (QP + 1)^14 > 2^57
+// multisection steps: the r leading eigenvalues, which the inverse iteration and the
+// eigengap test use, to (QP + 1)^-14 < 2^-57 of the Gershgorin interval; the others, which
+// are only reported, to (QP + 1)^-6 < 5e-8 of it
+constexpr int MS_STEPS = 14;
+constexpr int MS_STEPS_TAIL = 6;
 constexpr uint32_t LDY = 65;      // row stride of the eigenvectors of T in LDS
 
 __device__ __forceinline__ double wave_max(double v) {
@@ -630,7 +636,9 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
     const uint32_t nt = 1 + 4 * ((n + 2) / 4);   // terms: 1, then groups of four
     const double step = 1.0 / (double)(QP + 1);
     double a = red[16], b = red[17];
-    for (int it = 0; it < MS_STEPS; ++it) {
+    // the same for a lane group; groups past n have no eigenvalue
+    const int steps = j >= n ? 0 : (j + r >= n ? MS_STEPS : MS_STEPS_TAIL);
+    for (int it = 0; it < steps; ++it) {
       const double w = b - a;
       const uint32_t cq = sturm_count(de, nt, a + w * ((double)(q + 1) * step));
       // the first point of the group whose count passes j
@@ -722,16 +730,17 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
   const uint32_t col = tid / QP;
   const bool act = col < r;
   if constexpr (P == 1) {
-    // rows part + QP t of column tid / QP in registers
+    // rows part + QP t of column tid / QP in registers; the lane groups of columns past r
+    // skip the loop (whole waves when r is a multiple of 4)
     double yv[NR];
 #pragma unroll
     for (int t = 0; t < NR; ++t) {
       const uint32_t row = part + QP * t;
       yv[t] = (act && row < n) ? Y[row * LDY + col] : 0.0;
     }
-    for (int c = (int)nred - 1; c >= 0; --c) {
+    for (int c = act ? (int)nred - 1 : -1; c >= 0; --c) {
       const double tau = tv[c];
-      if (tau == 0.0) continue;   // the same for every thread
+      if (tau == 0.0) continue;   // the same for every active thread
       const uint32_t b = (uint32_t)c + 1;
       double vv[NR], u = 0.0;
 #pragma unroll
@@ -784,9 +793,9 @@ __global__ void __launch_bounds__(NTQ) k_eig_tri(EK kk) {
       yr[t] = (act && row < n) ? Y[row * LDY + col] : 0.0;
       yi[t] = 0.0;
     }
-    for (int c = (int)nred - 1; c >= 0; --c) {
+    for (int c = act ? (int)nred - 1 : -1; c >= 0; --c) {
       const double tr = tv[c], ti = tv[64 + c];
-      if (tr == 0.0 && ti == 0.0) continue;   // the same for every thread
+      if (tr == 0.0 && ti == 0.0) continue;   // the same for every active thread
       const uint32_t b = (uint32_t)c + 1;
       double vr[NR], vi[NR], ur = 0.0, ui = 0.0;
 #pragma unroll
