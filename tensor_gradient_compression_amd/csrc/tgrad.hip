@@ -512,7 +512,7 @@ bool use_rec3(const tgrad_t* h, bool apply, const void* W) {
 int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s,
                    const AdamK* fork_adam = nullptr);
 int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, float* out,
-                       hipStream_t s);
+                       hipStream_t s, hipEvent_t wait_last = nullptr);
 int step_body(tgrad_t* h, void* weight, const void* grad, int64_t t, hipStream_t s);
 
 // Omega (+ bitmask, ranks) as the k largest keys of `src` (storage type dt), or a random
@@ -1255,8 +1255,9 @@ int run_projection(tgrad_t* h, const void* X0, bool gather, hipStream_t s,
 // Reconstruction chain X x_1 U1 ... (first compressed mode first) from the core-sized
 // fp32 X. apply: the last launch merges N_S at Omega and updates W; otherwise it
 // writes the full fp32 tensor to out.
+// wait_last: an event the last launch (the one that merges the sparse update) waits for
 int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, float* out,
-                       hipStream_t s) {
+                       hipStream_t s, hipEvent_t wait_last) {
   const uint32_t P = h->P;
   std::vector<std::vector<int>> proj, rec;
   build_chain(h, h->fuse, false, proj, rec, true, use_rec3(h, apply, weight));
@@ -1270,6 +1271,7 @@ int run_reconstruction(tgrad_t* h, const float* X0, bool apply, void* weight, fl
   for (size_t j = 0; j < rec.size(); ++j) {
     const bool last = (j + 1 == rec.size());
     const bool app = last && apply;
+    if (last && wait_last) HIPCHK(h, hipStreamWaitEvent(s, wait_last, 0));
     float* Y = last ? (apply ? nullptr : out) : h->buf[which];
     if (rec[j].size() == 3) {
       // the last three modes with the merge and the weight update (last launch, apply)
@@ -1546,7 +1548,6 @@ int step_body(tgrad_t* h, void* weight, const void* grad, int64_t t, hipStream_t
     record(h, KID_ADAM, 0, nc * (nf ? 4 : dt_bytes(h->dtype) / P) + nc * 8 + nsv * 12,
            (nc + nsv) * 12, 0);
   }
-  if (forked) HIPCHK(h, hipStreamWaitEvent(s, h->ev_join, 0));
   if (nf == 0) {
     const float lr = (float)h->lr;
     const float decay = (float)(1.0 - h->lr * h->wd);
@@ -1557,7 +1558,11 @@ int step_body(tgrad_t* h, void* weight, const void* grad, int64_t t, hipStream_t
            h->N * dt_bytes(h->dtype), 0);
     return TGRAD_OK;
   }
-  return run_reconstruction(h, h->ucore, true, weight, nullptr, s);
+  // the sparse update, forked to the second stream, is joined before the launch that
+  // merges it (the reconstruction's earlier launches overlap it too)
+  rc = run_reconstruction(h, h->ucore, true, weight, nullptr, s, forked ? h->ev_join : nullptr);
+  if (rc != TGRAD_OK && forked) (void)hipStreamWaitEvent(s, h->ev_join, 0);
+  return rc;
 }
 
 }  // namespace
