@@ -15,17 +15,17 @@
 // projection's contracting pairs; an expanding pair would need its rows split over
 // workgroups, each repeating the first product: measured slower than one launch per
 // mode, so that form is not used). It walks i0 in groups of four. The DMA engine brings
-// X[a, i0 .. i0+3, :, c-block] in 16-byte pieces into two LDS buffers, one group ahead.
-// Wave w forms Z[i0 + w] = M1 X[i0 + w] on v_mfma_f32_16x16x4_f32, with M1 held in
-// registers, and leaves it in LDS. After one barrier every wave adds the group's rank-4
-// update Y[j0, (j1, c)] += M0[j0, i0 .. i0+3] Z[.., j1, c] to the 16 x 16 output tiles
-// it owns, one MFMA each. Accumulation is fp32 throughout, as in the single-mode kernel.
-// The output leaves in 64-byte row pieces. Neighbouring column blocks share 128-byte
-// lines and are placed on one XCD (see the block mapping). At 48 KB of LDS and 156
-// VGPRs three workgroups fit a CU. For the largest workload the launch takes 56 us
-// against 104 us for the two single-mode launches. Its transfers alone take 35 us; the
-// fp32 MFMA work (2.9 GFLOP, 19 us at the MFMA peak) runs between two barriers per group
-// and sets the pace.
+// X[a, i0 .. i0+3, :, c-block] in 16-byte pieces into two LDS buffers. Wave w forms
+// Z[i0 + w] = M1 X[i0 + w] on v_mfma_f32_16x16x4_f32, with M1 held in registers, and
+// leaves it in LDS; every wave adds a group's rank-4 update Y[j0, (j1, c)] +=
+// M0[j0, i0 .. i0+3] Z[.., j1, c] to the 16 x 16 output tiles it owns, one MFMA each.
+// The two products are software-pipelined over two Z copies: after the one barrier of
+// group g, the waves form group g + 1's Z and add group g's update while group g + 2
+// arrives. Accumulation is fp32 throughout, as in the single-mode kernel. The output
+// leaves in 64-byte row pieces. Neighbouring column blocks share 128-byte lines and are
+// placed on one XCD (see the block mapping). At 57 KB of LDS and 156 + 88 registers two
+// workgroups fit a CU, which holds the largest workload's 468 in one round. Its
+// transfers alone take 35 us; the fp32 MFMA work is 2.9 GFLOP (19 us at the MFMA peak).
 #include <algorithm>
 
 #include "tg_common.h"
@@ -142,48 +142,62 @@ __global__ void __launch_bounds__(PW_NT) k_pair(PWK k) {
   for (int m = 0; m < PW_TILES; ++m) acc[m] = f4{0.f, 0.f, 0.f, 0.f};
 
   const uint32_t ng = I0 / 4;
-  // the M0 and M1 loads above retire before the first transfer is waited for
-  __builtin_amdgcn_s_waitcnt(0);
-  issue(0, 0);
-  for (uint32_t g = 0; g < ng; ++g) {
-    // this thread's pieces of group g have landed; after the barrier everyone's have, the
-    // other buffer (group g - 1) is free, and every read of group g - 1's Z is done
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-    if (g + 1 < ng) issue(g + 1, (g + 1) & 1);
-    // first product: wave wv forms Z[i0 = 4 g + wv]
-    const LDS float* const xt = (const LDS float*)(lds + (g & 1) * k.xbuf) + wv * I1 * 16;
-    // (even and odd k-steps in separate accumulators: twice the independent MFMA chains)
+  // first product of group gg: wave wv forms Z[i0 = 4 gg + wv] from X buffer xb into Z copy
+  // zb (even and odd k-steps in separate accumulators: twice the independent MFMA chains)
+  auto first = [&](uint32_t xb, uint32_t zb) {
+    const LDS float* const xt = (const LDS float*)(lds + xb * k.xbuf) + wv * I1 * 16;
     f4 z[NRB1], z2[NRB1];
 #pragma unroll
     for (int rb = 0; rb < NRB1; ++rb) z[rb] = z2[rb] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS1; ++s) {
-      const float xb = xt[(4 * s + lg) * 16 + li];
+      const float xb2 = xt[(4 * s + lg) * 16 + li];
 #pragma unroll
       for (int rb = 0; rb < NRB1; ++rb) {
-        if (s & 1) z2[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(m1[rb][s], xb, z2[rb], 0, 0, 0);
-        else z[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(m1[rb][s], xb, z[rb], 0, 0, 0);
+        if (s & 1) z2[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(m1[rb][s], xb2, z2[rb], 0, 0, 0);
+        else z[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(m1[rb][s], xb2, z[rb], 0, 0, 0);
       }
     }
 #pragma unroll
     for (int rb = 0; rb < NRB1; ++rb) z[rb] += z2[rb];
     // Z[t = wv][j1][c]: the result rows are j1 = 16 rb + 4 lg + v, column c = li
-    LDS float* const zw = zs + wv * ZT;
+    LDS float* const zw = zs + zb * 4 * ZT + wv * ZT;
 #pragma unroll
     for (int rb = 0; rb < NRB1; ++rb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) zw[(16 * rb + 4 * lg + v) * ZR + li] = z[rb][v];
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the Z writes are done
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-    // second product: tile (row block r, j1) += M0[16 r + li][4 g + lg] Z[lg][j1][li]
-    const LDS float* const zg = zs + lg * ZT + li;
+  };
+  // second product of group g: tile (row block r, j1) += M0[16 r + li][4 g + lg] Z[lg][j1][li]
+  auto second = [&](uint32_t g, uint32_t zb) {
+    const LDS float* const zg = zs + zb * 4 * ZT + lg * ZT + li;
     const LDS float* const mg = m0s + (4 * g + lg) * MS + li;
 #pragma unroll
     for (int m = 0; m < PW_TILES; ++m)
       acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(mg[t_ab[m]], zg[t_b[m]], acc[m], 0, 0, 0);
+  };
+
+  // Software pipeline, one barrier a group: while the DMA engine brings group g + 2, each
+  // wave forms group g + 1's Z (into the other Z copy) and adds group g's update, so the
+  // two products' MFMAs interleave. The barrier that opens group g follows every read of
+  // X[g] (group g's first product ran a group earlier) and of the Z copy group g + 1
+  // writes (group g - 1's second product).
+  // the M0 and M1 loads above retire before the first transfer is waited for
+  __builtin_amdgcn_s_waitcnt(0);
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+  if (ng > 1) issue(1, 1);
+  first(0, 0);
+  for (uint32_t g = 0; g < ng; ++g) {
+    // this thread's pieces of group g + 1 and its Z writes of group g are done; after the
+    // barrier everyone's are
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    if (g + 2 < ng) issue(g + 2, g & 1);
+    if (g + 1 < ng) first((g + 1) & 1, (g + 1) & 1);
+    second(g, g & 1);
   }
   // Y[a, j0, j1, c0 + li], j0 = j00 + 16 r + 4 lg + v
   float* const Ya = k.Y + (uint64_t)a * J0 * J1 * k.C + c0;
@@ -248,7 +262,7 @@ PairPlan pair_plan(const ModePair& mp) {
   const uint32_t ZT = 16 * (uint32_t)p.nrb1 * 16 + 16;   // floats of one Z slice (k_pair)
   k.xbuf = xbuf;
   k.off_z = 2 * xbuf;
-  k.off_m0 = k.off_z + 4 * ZT * 4;
+  k.off_m0 = k.off_z + 2 * 4 * ZT * 4;   // two copies of the four Z slices
   p.lds = k.off_m0 + (size_t)mp.I0 * k.JB * 4;
   p.ok = p.lds <= 160 * 1024;
   return p;
