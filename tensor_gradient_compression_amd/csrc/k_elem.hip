@@ -110,6 +110,21 @@ __global__ void __launch_bounds__(256) k_adam(const CT* __restrict__ gc, float* 
   }
 }
 
+// The sparse values' update alone (its own symbol, so that a profile tells it apart from
+// the launch that also updates the core)
+__global__ void __launch_bounds__(256) k_adam_sparse(float* __restrict__ S,
+                                                     float* __restrict__ ms,
+                                                     float* __restrict__ vs, uint64_t ns,
+                                                     AdamK a) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < ns; j += stride) {
+    float m = ms[j], v = vs[j];
+    S[j] = a.lam * adam_one(S[j], m, v, a);
+    ms[j] = m;
+    vs[j] = v;
+  }
+}
+
 template <typename WT, int P>
 __global__ void __launch_bounds__(256) k_apply_dense(WT* __restrict__ W,
                                                      const float* __restrict__ uc,
@@ -205,6 +220,14 @@ hipError_t launch_adam(int core_dt, const void* g_core, float* u_core, float* m_
       break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_adam_sparse(float* S, float* m_s, float* v_s, uint64_t n_s, AdamK a,
+                              hipStream_t s) {
+  if (!n_s) return hipSuccess;
+  const unsigned b = grid_for(n_s, 256, 8192);
+  k_adam_sparse<<<b, 256, 0, s>>>(S, m_s, v_s, n_s, a);
   return hipGetLastError();
 }
 

@@ -109,6 +109,9 @@ hipError_t launch_resid_sub(int dt, const void* G, float* L, uint64_t n, hipStre
 hipError_t launch_adam(int core_dt, const void* g_core, float* u_core, float* m_core,
                        float* v_core, uint64_t n_core, float* S, float* m_s, float* v_s,
                        uint64_t n_s, AdamK a, hipStream_t s);
+// the k sparse values' update alone: S <- lam * Adam(S), moments m_s, v_s
+hipError_t launch_adam_sparse(float* S, float* m_s, float* v_s, uint64_t n_s, AdamK a,
+                              hipStream_t s);
 // W <- round(fp32(W) * decay - lr * Delta) (decay = fp32(1 - lr * weight_decay); 1 exactly
 // without decay)
 // delta != NULL (a test capture): Delta, the fp32 update after the sparse merge, is

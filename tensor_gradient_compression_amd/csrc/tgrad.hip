@@ -1082,8 +1082,7 @@ int fork_sparse_adam(tgrad_t* h, const AdamK& a, hipStream_t s) {
   h->cur_stream = h->side;   // the timing events of this launch go on the side stream
   {
     Mark m(h, KID_ADAM_SPARSE);
-    e = launch_adam(DT_F32, nullptr, nullptr, nullptr, nullptr, 0, h->S, h->mS, h->vS, nsv, a,
-                    h->side);
+    e = launch_adam_sparse(h->S, h->mS, h->vS, nsv, a, h->side);
   }
   h->cur_stream = s;
   if (e != hipSuccess) return fail_hip(h, e, "launch_adam (sparse values)");
