@@ -298,6 +298,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the per-kernel measurement of the other workloads")
+    ap.add_argument("--other-configs-only", action="store_true",
+                    help="run only the other workloads' per-kernel measurement (for a profiler "
+                         "run of those kernels) and print their table as one JSON line")
     ap.add_argument("--no-multi-tensor", action="store_true",
                     help="skip the 4-layer fp16 sequential vs tgrad_step_many measurement")
     ap.add_argument("--plan", type=int, default=None,
@@ -319,6 +322,10 @@ def main():
     assert torch.cuda.is_available(), "bench needs a GPU"
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    if args.other_configs_only:
+        print(json.dumps({"other_configs": other_configs(dev, stream, steps=args.steps,
+                                                          refresh_reps=args.refresh_reps)}))
+        return
     K, Wm = args.steps, args.warmup
 
     # inputs: two distinct synthetic gradients, staged into one buffer per step
