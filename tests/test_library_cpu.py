@@ -117,6 +117,9 @@ def test_null_handle_calls_are_einval(lib):
     assert lib.tgrad_mark_refreshed(None) == tg.EINVAL
     assert lib.tgrad_timing_enable(None, 1, 10) == tg.EINVAL
     assert lib.tgrad_set_stream_products(None, 1) == tg.EINVAL
+    assert lib.tgrad_set_stream_overlap(None, 1, 1) == tg.EINVAL
+    assert lib.tgrad_set_pair_fusion(None, 1) == tg.EINVAL
+    assert lib.tgrad_set_gram_fusion(None, 1) == tg.EINVAL
 
 
 def test_default_options_are_the_plain_method(lib):
