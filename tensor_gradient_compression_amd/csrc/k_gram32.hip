@@ -169,24 +169,30 @@ __global__ void __launch_bounds__(G32_NTH) k_gram32(G32K k) {
   auto group = [&](const unsigned char* buf, uint32_t g, uint32_t ncol) {
     float fr[NBK][4];
     if (k.wide) {
+      // one 16-byte read per row block gives a lane its columns 4 kg .. 4 kg + 3 (P = 1),
+      // or two of them, both components (P = 2: two reads)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t c = 16 * g + 4 * kg + t;
-        const bool ok = c < ncol;
-        const uint32_t cp = (c * P) >> 2, w = (c * P) & 3u;
+      for (int rb = 0; rb < NBI; ++rb) {
+        // rows >= I only reach Gram entries that are dropped: read row I - 1 instead
+        const uint32_t r = 16 * rb + li < I ? 16 * rb + li : I - 1;
+        if constexpr (P == 2) {
 #pragma unroll
-        for (int rb = 0; rb < NBI; ++rb) {
-          // rows >= I only reach Gram entries that are dropped: read row I - 1 instead
-          const uint32_t r = 16 * rb + li < I ? 16 * rb + li : I - 1;
-          const uint32_t off = ((r * k.rowq + (cp ^ (r & 15u))) << 4) + (w << 2);
-          if constexpr (P == 2) {
-            const f2 v = *(const f2*)(buf + off);
-            fr[rb][t] = ok ? v[0] : 0.0f;
-            fr[NBI + rb][t] = ok ? v[1] : 0.0f;
-          } else {
-            const float v = *(const float*)(buf + off);
-            fr[rb][t] = ok ? v : 0.0f;
+          for (int h = 0; h < 2; ++h) {
+            // columns c0 = 16 g + 4 kg + 2 h and c0 + 1: floats 2 c0 .. 2 c0 + 3, one piece
+            const uint32_t c0 = 16 * g + 4 * kg + 2 * h;
+            const uint32_t cp = 8 * g + 2 * kg + h;
+            const f4 v = *(const f4*)(buf + ((r * k.rowq + (cp ^ (r & 15u))) << 4));
+            const bool ok0 = c0 < ncol, ok1 = c0 + 1 < ncol;
+            fr[rb][2 * h] = ok0 ? v[0] : 0.0f;
+            fr[NBI + rb][2 * h] = ok0 ? v[1] : 0.0f;
+            fr[rb][2 * h + 1] = ok1 ? v[2] : 0.0f;
+            fr[NBI + rb][2 * h + 1] = ok1 ? v[3] : 0.0f;
           }
+        } else {
+          const uint32_t cp = 4 * g + kg;
+          const f4 v = *(const f4*)(buf + ((r * k.rowq + (cp ^ (r & 15u))) << 4));
+#pragma unroll
+          for (int t = 0; t < 4; ++t) fr[rb][t] = 16 * g + 4 * kg + t < ncol ? v[t] : 0.0f;
         }
       }
     } else {
