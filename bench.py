@@ -15,7 +15,7 @@ that the library records on the launch stream around every launch in the timed r
 Beside the headline it reports, in "multi_tensor", the 4-layer fp16 (64,64,64,64)
 workload stepped layer after layer and as one tgrad_step_many call.
 
-Prints ONE JSON line. --gpus N with N > 1 exits: this build runs on one GPU.
+Prints ONE JSON line. --gpus N with N > 1 exits: the step is measured on one GPU.
 """
 from __future__ import annotations
 
@@ -309,7 +309,7 @@ def main():
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the step is measured on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
