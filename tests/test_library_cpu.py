@@ -143,3 +143,16 @@ def test_step_many_argument_checks_need_no_device(lib):
     assert lib.tgrad_step_many(None, None, None, 2, None) == tg.EINVAL
     hs = (P * 1)(None)
     assert lib.tgrad_step_many(hs, hs, hs, 1, None) == tg.EINVAL
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures the step on one GPU: --gpus 2 prints one JSON error line and
+    exits with status 2 before importing torch or touching a device."""
+    import json
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "one GPU" in line["error"]
